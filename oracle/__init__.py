@@ -1,0 +1,129 @@
+"""fp64 CPU reference for the KLA recurrence (test infrastructure only).
+
+Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of bench.py
+may import this package.  The product library never calls it.
+
+The arithmetic lives in kla_oracle.c (token-by-token definition from the
+KLA technical summary, "Resumo Tecnico: Atencao Linear Kaczmarz (KLA)",
+sections "Derivacao Teorica" and "A Regra de Atualizacao KLA").  This
+module only converts arrays to float64 (exact for bf16/fp32 values) and
+calls it.
+
+Parity pins for every function here are in tests/test_oracle_pins.py.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkla_oracle.so")
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+_libs = {}
+
+
+def _load(path=None):
+    """Load the compiled reference (the default build, or another build of
+    the same source given by path)."""
+    path = path or _LIB_PATH
+    if path in _libs:
+        return _libs[path]
+    if path == _LIB_PATH and not os.path.exists(path):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(path)
+    lib.kla_oracle_fwd.restype = ctypes.c_int
+    lib.kla_oracle_fwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _i64p,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_double, _dp, _dp, _dp]
+    lib.kla_oracle_decode_step.restype = ctypes.c_int
+    lib.kla_oracle_decode_step.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_double, _dp]
+    lib.kla_oracle_num_threads.restype = ctypes.c_int
+    lib.kla_oracle_num_threads.argtypes = []
+    _libs[path] = lib
+    return lib
+
+
+def _f64(x):
+    """Contiguous float64 copy/view of an array-like (torch CPU tensors too)."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        import torch
+        x = x.to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return a.ctypes.data_as(_dp) if a is not None else None
+
+
+def num_threads() -> int:
+    """OpenMP threads the reference will use (OMP_NUM_THREADS)."""
+    return int(_load().kla_oracle_num_threads())
+
+
+def fwd(q, k, v, alpha, eta, cu_seqlens=None, eps=1e-6, initial_state=None, lib_path=None):
+    """Sequential fp64 KLA prefill.
+
+    q, k: [tok, H, dk]; v: [tok, H, dv]; alpha, eta: [tok, H].  Packed
+    sequences are given by cu_seqlens [n_seqs+1]; without it, q/k/v may
+    also be [B, T, H, d] (dense batch, flattened here).  Returns
+    (o [tok, H, dv] float64, final_state [n_seqs, H, dk, dv] float64), with
+    o shaped like v.
+    """
+    lib = _load(lib_path)
+    q, k, v, alpha, eta = (_f64(t) for t in (q, k, v, alpha, eta))
+    out_shape = v.shape
+    if cu_seqlens is None:
+        if q.ndim == 4:
+            B, T = q.shape[0], q.shape[1]
+            cu = np.arange(B + 1, dtype=np.int64) * T
+        else:
+            cu = np.array([0, q.shape[0]], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    dk, dv = q.shape[-1], v.shape[-1]
+    H = q.shape[-2]
+    q = q.reshape(-1, H, dk)
+    k = k.reshape(-1, H, dk)
+    v = v.reshape(-1, H, dv)
+    alpha = alpha.reshape(-1, H)
+    eta = eta.reshape(-1, H)
+    n_seqs = cu.shape[0] - 1
+    tok = q.shape[0]
+    if int(cu[-1]) != tok:
+        raise ValueError("cu_seqlens[-1] must equal the token count")
+    init = None if initial_state is None else _f64(initial_state).reshape(n_seqs, H, dk, dv)
+    o = np.zeros((tok, H, dv), dtype=np.float64)
+    fin = np.zeros((n_seqs, H, dk, dv), dtype=np.float64)
+    rc = lib.kla_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
+                            cu.ctypes.data_as(_i64p), n_seqs, H, dk, dv, float(eps),
+                            _ptr(init), _ptr(o), _ptr(fin))
+    if rc != 0:
+        raise RuntimeError("kla_oracle_fwd failed")
+    return o.reshape(out_shape), fin
+
+
+def decode_step(q, k, v, alpha, eta, state, eps=1e-6, lib_path=None):
+    """One fp64 KLA decode step.
+
+    q, k: [N, H, dk]; v: [N, H, dv]; alpha, eta: [N, H]; state [N, H, dk, dv].
+    Returns (o [N, H, dv], new_state), both float64; the input state is not
+    modified.
+    """
+    lib = _load(lib_path)
+    q, k, v, alpha, eta = (_f64(t) for t in (q, k, v, alpha, eta))
+    S = _f64(state).copy()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((N, H, dv), dtype=np.float64)
+    rc = lib.kla_oracle_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
+                                    _ptr(S), N, H, dk, dv, float(eps), _ptr(o))
+    if rc != 0:
+        raise RuntimeError("kla_oracle_decode_step failed")
+    return o, S

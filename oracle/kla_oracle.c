@@ -1,0 +1,159 @@
+/*
+ * kla_oracle.c -- fp64 reference for the Kaczmarz Linear Attention (KLA)
+ * recurrence.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark call it; the library under
+ * delta_rule_linear_amd/ never does.  It shares no code with the HIP path.
+ *
+ * Source: "Resumo Tecnico: Atencao Linear Kaczmarz (KLA)"
+ * (gist.science/pt/paper/2605.08587), sections "Derivacao Teorica" and
+ * "A Regra de Atualizacao KLA".  Per head, with state S in R^{dk x dv}:
+ *
+ *   beta_t  = eta_t / (k_t^T k_t + eps)          (relaxed Kaczmarz step)
+ *   S~      = alpha_t S_{t-1}                     (decayed previous state)
+ *   e_t     = v_t - S~^T k_t                      (residual)
+ *   S_t     = S~ + beta_t k_t e_t^T               (rank-one write)
+ *   o_t     = S_t^T q_t                           (read of the written state)
+ *
+ * The page fixes the first four lines.  The decay alpha_t is the scalar
+ * gate that the page keeps from Gated DeltaNet (section "Implementacao";
+ * the linear-attention survey page, gist.science/pt/paper/2607.07953,
+ * section "Metodologia e Estrutura", describes it as a decay applied to
+ * the memory before the residual).  The read o_t = S_t^T q_t uses the
+ * state after the write; the pages never print the read, so this is a
+ * stated reading.
+ *
+ * This is the plain definition, token by token, in double precision,
+ * with no blocking or chunking: the chunkwise algorithm of the GPU path
+ * reaches the same result up to rounding.  Inputs arrive as doubles that
+ * hold the exact values the GPU reads (bf16 and fp32 convert to fp64
+ * exactly).
+ *
+ * Layouts (all row-major, contiguous):
+ *   q, k      [total_tok][H][dk]
+ *   v, o      [total_tok][H][dv]
+ *   alpha,eta [total_tok][H]
+ *   state     [n_seqs][H][dk][dv]
+ *   cu_seqlens[n_seqs+1], cu_seqlens[0] = 0, non-decreasing.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* One KLA write followed by the read, on one (sequence, head) state. */
+static void kla_token(double *S, double *e, const double *q, const double *k,
+                      const double *v, double alpha, double eta, double eps,
+                      int dk, int dv, double *o)
+{
+    double kk = 0.0;
+    for (int i = 0; i < dk; ++i) kk += k[i] * k[i];
+    const double beta = eta / (kk + eps);
+
+    /* S~ = alpha S */
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= alpha;
+
+    /* e = v - S~^T k */
+    for (int j = 0; j < dv; ++j) e[j] = v[j];
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) e[j] -= S[(size_t)i * dv + j] * k[i];
+
+    /* S = S~ + beta k e^T */
+    for (int i = 0; i < dk; ++i) {
+        const double bk = beta * k[i];
+        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += bk * e[j];
+    }
+
+    /* o = S^T q */
+    if (o) {
+        for (int j = 0; j < dv; ++j) o[j] = 0.0;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) o[j] += S[(size_t)i * dv + j] * q[i];
+    }
+}
+
+int kla_oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Prefill over packed sequences.  The state starts at initial_state[s] (or
+ * zero when initial_state is NULL) at the first token of each sequence and
+ * the final state of each sequence goes to final_state (when not NULL).
+ * Returns 0, or -1 on a malformed argument.
+ */
+int kla_oracle_fwd(const double *q, const double *k, const double *v,
+                   const double *alpha, const double *eta,
+                   const int64_t *cu_seqlens, int n_seqs, int H, int dk, int dv,
+                   double eps, const double *initial_state, double *o,
+                   double *final_state)
+{
+    if (!q || !k || !v || !alpha || !eta || !cu_seqlens || !o) return -1;
+    if (n_seqs <= 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    for (int s = 0; s < n_seqs; ++s)
+        if (cu_seqlens[s + 1] < cu_seqlens[s]) return -1;
+    if (cu_seqlens[0] != 0) return -1;
+
+    const size_t sdim = (size_t)dk * dv;
+    int failed = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int s = 0; s < n_seqs; ++s) {
+        for (int h = 0; h < H; ++h) {
+            double *S = (double *)malloc(sizeof(double) * (sdim + dv));
+            if (!S) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            double *e = S + sdim;
+            const size_t sh = (size_t)s * H + h;
+            if (initial_state)
+                memcpy(S, initial_state + sh * sdim, sizeof(double) * sdim);
+            else
+                memset(S, 0, sizeof(double) * sdim);
+            for (int64_t t = cu_seqlens[s]; t < cu_seqlens[s + 1]; ++t) {
+                const size_t th = (size_t)t * H + h;
+                kla_token(S, e, q + th * dk, k + th * dk, v + th * dv,
+                          alpha[th], eta[th], eps, dk, dv, o + th * dv);
+            }
+            if (final_state) memcpy(final_state + sh * sdim, S, sizeof(double) * sdim);
+            free(S);
+        }
+    }
+    return failed ? -1 : 0;
+}
+
+/*
+ * One decode step: every (sequence, head) state advances by one token in
+ * place and o receives the read of the new state.
+ *   q, k [n_seqs][H][dk], v, o [n_seqs][H][dv], alpha, eta [n_seqs][H]
+ */
+int kla_oracle_decode_step(const double *q, const double *k, const double *v,
+                           const double *alpha, const double *eta, double *state,
+                           int n_seqs, int H, int dk, int dv, double eps, double *o)
+{
+    if (!q || !k || !v || !alpha || !eta || !state || !o) return -1;
+    if (n_seqs <= 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    const size_t sdim = (size_t)dk * dv;
+    int failed = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t sh = 0; sh < (int64_t)n_seqs * H; ++sh) {
+        double *e = (double *)malloc(sizeof(double) * dv);
+        if (!e) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        kla_token(state + sh * sdim, e, q + sh * dk, k + sh * dk, v + sh * dv,
+                  alpha[sh], eta[sh], eps, dk, dv, o + sh * dv);
+        free(e);
+    }
+    return failed ? -1 : 0;
+}

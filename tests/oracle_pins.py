@@ -1,0 +1,286 @@
+"""Pins of the fp64 oracle against facts the KLA pages and the mathematics fix.
+
+Each pin takes the reference under test as two callables,
+  fwd(q, k, v, alpha, eta, cu_seqlens=None, eps=..., initial_state=None)
+      -> (o, final_state)
+  decode(q, k, v, alpha, eta, state, eps=...) -> (o, new_state)
+so the same checks can run against deliberately broken builds of the
+reference (tests/test_oracle_mutants.py) and must fail there.
+
+Sources: the KLA technical summary ("Resumo Tecnico: Atencao Linear
+Kaczmarz (KLA)", gist.science/pt/paper/2605.08587): the constrained write
+and its projection solution (section "Derivacao Teorica"), the relaxed
+coefficient and the update (section "A Regra de Atualizacao KLA"), the
+three properties of the unrelaxed step (section "Propriedades Chave") and
+the drop-in relation to Gated DeltaNet (section "Implementacao").  The
+linear-attention survey page (gist.science/pt/paper/2607.07953, section
+"Metodologia e Estrutura") gives DeltaNet and Gated DeltaNet.
+"""
+import json
+import os
+
+import numpy as np
+
+from chunk_model import chunked
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TIGHT = 1e-12
+
+
+def rel(x, y):
+    """Normwise max relative error max|x-y| / max|y|."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    den = np.max(np.abs(y))
+    return float(np.max(np.abs(x - y)) / (den if den > 0 else 1.0))
+
+
+def _rand_seq(rng, L, H, dk, dv, amin=0.3):
+    q = rng.standard_normal((L, H, dk))
+    k = rng.standard_normal((L, H, dk)) * np.exp(rng.standard_normal((L, H, 1)))
+    v = rng.standard_normal((L, H, dv))
+    alpha = rng.uniform(amin, 1.0, (L, H))
+    eta = rng.uniform(0.05, 1.0, (L, H))
+    return q, k, v, alpha, eta
+
+
+def pin_worked_example(fwd, decode):
+    """Hand-worked two-token example (tests/golden/kla_worked_2x2.json)."""
+    with open(os.path.join(GOLDEN, "kla_worked_2x2.json")) as f:
+        g = json.load(f)
+    o, S = fwd(np.array(g["q"]), np.array(g["k"]), np.array(g["v"]),
+               np.array(g["alpha"]), np.array(g["eta"]), cu_seqlens=[0, 2],
+               eps=g["eps"], initial_state=np.array(g["initial_state"]))
+    assert np.allclose(o, np.array(g["expected_o"]), rtol=0, atol=1e-14), o
+    assert np.allclose(S, np.array(g["expected_final_state"]), rtol=0, atol=1e-14), S
+
+
+def pin_orthogonal_projection(fwd, decode):
+    """eta=1, eps=0: every write satisfies the constraint S_t^T k_t = v_t
+    (projection onto the constraint set).  Reading with q_t = k_t therefore
+    returns v_t exactly, for any decay and any start state."""
+    rng = np.random.default_rng(1)
+    L, H, dk, dv = 40, 3, 8, 5
+    _, k, v, alpha, _ = _rand_seq(rng, L, H, dk, dv)
+    S0 = rng.standard_normal((1, H, dk, dv))
+    o, _ = fwd(k, k, v, alpha, np.ones((L, H)), eps=0.0, initial_state=S0)
+    assert rel(o, v) < TIGHT, rel(o, v)
+
+
+def pin_min_norm_bruteforce(fwd, decode):
+    """Each write is the minimum-Frobenius-norm change that meets S^T k = v,
+    scaled by the relaxation eta |k|^2/(|k|^2+eps).  Solved here directly as
+    a least-norm problem on vec(S) with the Kronecker constraint
+    (I_dv kron k^T) vec(S) = v, token by token, with numpy's lstsq."""
+    rng = np.random.default_rng(2)
+    L, dk, dv, eps = 7, 4, 3, 0.3
+    q, k, v, alpha, eta = _rand_seq(rng, L, 1, dk, dv)
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, S_fin = fwd(q, k, v, alpha, eta, eps=eps, initial_state=S0)
+    S = S0[0, 0].copy()
+    for t in range(L):
+        kt, vt = k[t, 0], v[t, 0]
+        St = alpha[t, 0] * S
+        # vec(S) stacks columns: vec(S)[j*dk + i] = S[i, j]; (S^T k)_j = sum_i S[i,j] k_i
+        Cmat = np.kron(np.eye(dv), kt[None, :])
+        r = vt - Cmat @ St.reshape(-1, order="F")
+        x = np.linalg.lstsq(Cmat, r, rcond=None)[0]
+        kk = float(kt @ kt)
+        S = St + (eta[t, 0] * kk / (kk + eps)) * x.reshape(dk, dv, order="F")
+        assert rel(o[t, 0], S.T @ q[t, 0]) < 1e-11
+    assert rel(S_fin[0, 0], S) < 1e-11
+
+
+def pin_exact_line_search(fwd, decode):
+    """eta=1, eps=0: along the write direction k e^T, the step is the exact
+    minimiser of the per-token loss l(b) = 1/2 |(S~ + b k e^T)^T k - v|^2,
+    found here by a numerical scalar minimiser, and the loss at it is 0."""
+    from scipy.optimize import minimize_scalar
+    rng = np.random.default_rng(3)
+    dk, dv = 6, 4
+    for trial in range(5):
+        k = rng.standard_normal((1, 1, dk)) * np.exp(rng.standard_normal())
+        v = rng.standard_normal((1, 1, dv))
+        a = np.array([[rng.uniform(0.2, 1.0)]])
+        S0 = rng.standard_normal((1, 1, dk, dv))
+        _, S1 = fwd(k, k, v, a, np.ones((1, 1)), eps=0.0, initial_state=S0)
+        St = a[0, 0] * S0[0, 0]
+        kt, vt = k[0, 0], v[0, 0]
+        D = S1[0, 0] - St                         # the write the reference made
+        resid = lambda S: 0.5 * float(np.sum((S.T @ kt - vt) ** 2))
+        # D must be a multiple of a rank-one k e^T: project onto k to get e-direction
+        e_dir = kt @ D                            # = b |k|^2 e, any b
+        ke = np.outer(kt, e_dir)
+        b_ref = float(np.sum(D * ke) / np.sum(ke * ke))
+        assert rel(D, b_ref * ke) < 1e-12         # rank-one along k
+        res = minimize_scalar(lambda b: resid(St + b * ke), bracket=(0.0, 2.0 * abs(b_ref) + 1.0),
+                              tol=1e-14)
+        assert abs(res.x - b_ref) <= 1e-6 * abs(b_ref), (res.x, b_ref)
+        assert resid(S1[0, 0]) < 1e-20 * max(1.0, float(vt @ vt))
+
+
+def pin_normalised_gradient(fwd, decode):
+    """The write equals S~ - eta/(|k|^2+eps) grad l(S~) with
+    l(S) = 1/2 |S^T k - v|^2; the gradient is taken by central differences
+    (exact for this quadratic up to rounding)."""
+    rng = np.random.default_rng(4)
+    dk, dv = 5, 4
+    for trial in range(4):
+        eps = [0.0, 1e-3, 0.5, 2.0][trial]
+        k = rng.standard_normal((1, 1, dk)) * np.exp(rng.standard_normal())
+        v = rng.standard_normal((1, 1, dv))
+        a = np.array([[rng.uniform(0.2, 1.0)]])
+        et = np.array([[rng.uniform(0.1, 1.0)]])
+        S0 = rng.standard_normal((1, 1, dk, dv))
+        _, S1 = fwd(k, k, v, a, et, eps=eps, initial_state=S0)
+        St = a[0, 0] * S0[0, 0]
+        kt, vt = k[0, 0], v[0, 0]
+        loss = lambda S: 0.5 * float(np.sum((S.T @ kt - vt) ** 2))
+        G = np.zeros_like(St)
+        h = 1e-3
+        for i in range(dk):
+            for j in range(dv):
+                E = np.zeros_like(St)
+                E[i, j] = h
+                G[i, j] = (loss(St + E) - loss(St - E)) / (2 * h)
+        step = et[0, 0] / (float(kt @ kt) + eps)
+        assert rel(S1[0, 0], St - step * G) < 1e-9, rel(S1[0, 0], St - step * G)
+
+
+def pin_exact_recall(fwd, decode):
+    """No decay, eta=1, eps=0 and orthonormal keys: after n <= dk writes the
+    state returns every stored value, S^T k_j = v_j for all j (each later
+    write leaves earlier orthogonal constraints intact)."""
+    rng = np.random.default_rng(5)
+    dk, dv = 8, 6
+    for n in (1, 5, 8):
+        Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+        K = Qm[:, :n].T.reshape(n, 1, dk)
+        V = rng.standard_normal((n, 1, dv))
+        S0 = rng.standard_normal((1, 1, dk, dv))
+        _, S = fwd(K, K, V, np.ones((n, 1)), np.ones((n, 1)), eps=0.0, initial_state=S0)
+        assert rel(K[:, 0] @ S[0, 0], V[:, 0]) < 1e-12
+
+
+def pin_eta_zero(fwd, decode):
+    """eta = 0: no write; the state only decays, so
+    o_t = (prod_{i<=t} alpha_i) S0^T q_t."""
+    rng = np.random.default_rng(6)
+    L, H, dk, dv = 30, 2, 5, 7
+    q, k, v, alpha, _ = _rand_seq(rng, L, H, dk, dv, amin=0.8)
+    S0 = rng.standard_normal((1, H, dk, dv))
+    o, S = fwd(q, k, v, alpha, np.zeros((L, H)), eps=1e-6, initial_state=S0)
+    decay = np.cumprod(alpha, axis=0)
+    exp_o = np.einsum("th,hij,thi->thj", decay, S0[0], q)
+    assert rel(o, exp_o) < TIGHT
+    assert rel(S[0], decay[-1][:, None, None] * S0[0]) < TIGHT
+
+
+def pin_scalar_case(fwd, decode):
+    """dk = dv = 1, eta = 1, eps = 0: the write solves s k = v, so
+    s_t = v_t / k_t and o_t = q_t v_t / k_t, whatever the decay."""
+    rng = np.random.default_rng(7)
+    L = 25
+    q = rng.standard_normal((L, 1, 1))
+    k = rng.uniform(0.5, 2.0, (L, 1, 1)) * rng.choice([-1, 1], (L, 1, 1))
+    v = rng.standard_normal((L, 1, 1))
+    o, S = fwd(q, k, v, rng.uniform(0.3, 1, (L, 1)), np.ones((L, 1)), eps=0.0,
+               initial_state=rng.standard_normal((1, 1, 1, 1)))
+    assert rel(o, q * v / k) < TIGHT
+    assert abs(S[0, 0, 0, 0] - v[-1, 0, 0] / k[-1, 0, 0]) < 1e-12
+
+
+def pin_gated_deltanet_form(fwd, decode):
+    """Unit-norm keys: KLA is Gated DeltaNet's product form
+    S_t = alpha_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T with
+    b_t = eta_t/(1+eps); with alpha = 1 it is DeltaNet."""
+    rng = np.random.default_rng(8)
+    L, dk, dv, eps = 20, 6, 4, 0.25
+    q, k, v, alpha, eta = _rand_seq(rng, L, 1, dk, dv)
+    k = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    for a in (alpha, np.ones_like(alpha)):
+        S0 = rng.standard_normal((dk, dv))
+        o, S_fin = fwd(q, k, v, a, eta, eps=eps, initial_state=S0[None, None])
+        S = S0.copy()
+        for t in range(L):
+            kt = k[t, 0]
+            b = eta[t, 0] / (1.0 + eps)
+            S = a[t, 0] * (np.eye(dk) - b * np.outer(kt, kt)) @ S + b * np.outer(kt, v[t, 0])
+            assert rel(o[t, 0], S.T @ q[t, 0]) < 1e-11
+        assert rel(S_fin[0, 0], S) < 1e-11
+
+
+def pin_chunk_form(fwd, decode):
+    """The chunkwise WY/UT form with B = Diag(beta) gives the same result
+    for every chunk size, including ragged last chunks."""
+    rng = np.random.default_rng(9)
+    H, dk, dv = 2, 6, 5
+    cu = np.array([0, 1, 17, 80, 143])
+    L = int(cu[-1])
+    q, k, v, alpha, eta = _rand_seq(rng, L, H, dk, dv)
+    S0 = rng.standard_normal((len(cu) - 1, H, dk, dv))
+    o, S = fwd(q, k, v, alpha, eta, cu_seqlens=cu, eps=1e-3, initial_state=S0)
+    for C in (1, 7, 16, 64):
+        oc, Sc = chunked(q, k, v, alpha, eta, cu, 1e-3, C, S0)
+        assert rel(o, oc) < 1e-11 and rel(S, Sc) < 1e-11, (C, rel(o, oc), rel(S, Sc))
+
+
+def pin_packed_and_resume(fwd, decode):
+    """Packed sequences equal separate runs, and splitting one sequence in two
+    with the first part's final state as the second part's start state
+    equals one run."""
+    rng = np.random.default_rng(10)
+    H, dk, dv = 2, 4, 3
+    cu = np.array([0, 9, 9, 30, 41])   # includes an empty sequence
+    L = int(cu[-1])
+    q, k, v, alpha, eta = _rand_seq(rng, L, H, dk, dv)
+    S0 = rng.standard_normal((4, H, dk, dv))
+    o, S = fwd(q, k, v, alpha, eta, cu_seqlens=cu, eps=1e-6, initial_state=S0)
+    for s in range(4):
+        a, b = cu[s], cu[s + 1]
+        oi, Si = fwd(q[a:b], k[a:b], v[a:b], alpha[a:b], eta[a:b], cu_seqlens=[0, b - a],
+                     eps=1e-6, initial_state=S0[s:s + 1])
+        assert rel(o[a:b], oi) < TIGHT if b > a else True
+        assert rel(S[s], Si[0]) < TIGHT
+    # resume: [0,13) then [13,30) of sequence 2
+    a, m, b = 9, 13, 30
+    o1, S1 = fwd(q[a:m], k[a:m], v[a:m], alpha[a:m], eta[a:m], cu_seqlens=[0, m - a],
+                 eps=1e-6, initial_state=S0[2:3])
+    o2, S2 = fwd(q[m:b], k[m:b], v[m:b], alpha[m:b], eta[m:b], cu_seqlens=[0, b - m],
+                 eps=1e-6, initial_state=S1)
+    assert rel(np.concatenate([o1, o2]), o[a:b]) < TIGHT
+    assert rel(S2[0], S[2]) < TIGHT
+    # an empty sequence returns its start state unchanged
+    assert np.array_equal(S[1], S0[1])
+
+
+def pin_decode_is_one_token(fwd, decode):
+    """A decode step on the state after a prefill equals the prefill that is
+    one token longer (its last output and final state)."""
+    rng = np.random.default_rng(11)
+    L, H, dk, dv = 12, 3, 5, 4
+    q, k, v, alpha, eta = _rand_seq(rng, L + 1, H, dk, dv)
+    _, S = fwd(q[:L], k[:L], v[:L], alpha[:L], eta[:L], eps=1e-4)
+    od, Sd = decode(q[L:], k[L:], v[L:], alpha[L:], eta[L:], S, eps=1e-4)
+    o_all, S_all = fwd(q, k, v, alpha, eta, eps=1e-4)
+    assert rel(od[0], o_all[L]) < TIGHT
+    assert rel(Sd, S_all) < TIGHT
+
+
+def pin_zero_key(fwd, decode):
+    """A zero key with eps > 0 writes nothing: the token only decays the
+    state, and the read is alpha S^T q."""
+    rng = np.random.default_rng(12)
+    dk, dv = 4, 3
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    q = rng.standard_normal((1, 1, dk))
+    o, S = fwd(q, np.zeros((1, 1, dk)), rng.standard_normal((1, 1, dv)), np.array([[0.7]]),
+               np.array([[0.9]]), eps=1e-6, initial_state=S0)
+    assert np.array_equal(S[0, 0], 0.7 * S0[0, 0])
+    assert rel(o[0, 0], 0.7 * S0[0, 0].T @ q[0, 0]) < TIGHT
+
+
+ALL_PINS = [pin_worked_example, pin_orthogonal_projection, pin_min_norm_bruteforce,
+            pin_exact_line_search, pin_normalised_gradient, pin_exact_recall, pin_eta_zero,
+            pin_scalar_case, pin_gated_deltanet_form, pin_chunk_form, pin_packed_and_resume,
+            pin_decode_is_one_token, pin_zero_key]

@@ -1,0 +1,91 @@
+"""Pin strength: plausible mistakes planted in copies of the oracle source
+must each fail at least one pin of tests/oracle_pins.py.
+
+Each mutant is a textual edit of oracle/kla_oracle.c compiled with gcc into
+a temporary directory and exercised in a child process (a mutant that
+crashes counts as caught).  Nothing here touches a GPU.
+"""
+import os
+import subprocess
+import sys
+import textwrap
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "kla_oracle.c")
+
+W_MARK = "    /* S = S~ + beta k e^T */\n"
+O_MARK = "    /* o = S^T q */\n"
+
+
+def _swap_write_and_read(src):
+    """Read before the write (the pre-write readout reading)."""
+    a = src.index(W_MARK)
+    b = src.index(O_MARK)
+    end = src.index("\n}\n", b) + 1
+    write_blk, read_blk = src[a:b], src[b:end]
+    return src[:a] + read_blk + write_blk + src[end:]
+
+
+MUTANTS = {
+    "no_decay": lambda s: s.replace("S[(size_t)i * dv + j] *= alpha;", "(void)alpha;"),
+    "beta_unnormalised": lambda s: s.replace("eta / (kk + eps)", "eta"),
+    "beta_norm_not_squared": lambda s: s.replace("eta / (kk + eps)", "eta / (__builtin_sqrt(kk) + eps)"),
+    "beta_drops_eps": lambda s: s.replace("eta / (kk + eps)", "eta / kk"),
+    "beta_times_alpha": lambda s: s.replace("eta / (kk + eps)", "alpha * eta / (kk + eps)"),
+    "residual_sign": lambda s: s.replace("e[j] -= S[(size_t)i * dv + j] * k[i];",
+                                         "e[j] += S[(size_t)i * dv + j] * k[i];"),
+    "residual_undecayed": lambda s: s.replace("e[j] -= S[(size_t)i * dv + j] * k[i];",
+                                              "e[j] -= S[(size_t)i * dv + j] * k[i] / alpha;"),
+    "write_uses_v": lambda s: s.replace("S[(size_t)i * dv + j] += bk * e[j];",
+                                        "S[(size_t)i * dv + j] += bk * v[j];"),
+    "read_with_key": lambda s: s.replace("o[j] += S[(size_t)i * dv + j] * q[i];",
+                                         "o[j] += S[(size_t)i * dv + j] * k[i];"),
+    "read_before_write": _swap_write_and_read,
+    "ignores_initial_state": lambda s: s.replace("if (initial_state)\n", "if (0)\n"),
+    "decode_swaps_q_and_k": lambda s: s.replace(
+        "kla_token(state + sh * sdim, e, q + sh * dk, k + sh * dk,",
+        "kla_token(state + sh * sdim, e, k + sh * dk, q + sh * dk,"),
+    "drops_last_token": lambda s: s.replace("t < cu_seqlens[s + 1]; ++t", "t + 1 < cu_seqlens[s + 1]; ++t"),
+    "decay_after_write": lambda s: s.replace(
+        "    for (int i = 0; i < dk; ++i)\n        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= alpha;\n",
+        "").replace("    /* o = S^T q */\n",
+                    "    for (int i = 0; i < dk; ++i)\n        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= alpha;\n    /* o = S^T q */\n"),
+}
+
+RUNNER = textwrap.dedent("""
+    import sys, functools
+    sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+    import oracle
+    from oracle_pins import ALL_PINS
+    fwd = functools.partial(oracle.fwd, lib_path={lib!r})
+    dec = functools.partial(oracle.decode_step, lib_path={lib!r})
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(fwd, dec)
+        except Exception as e:
+            failed.append(pin.__name__)
+    print("FAILED_PINS", ",".join(failed))
+""")
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = open(SRC).read()
+    mutated = MUTANTS[name](src)
+    assert mutated != src, "mutation did not apply"
+    csrc = tmp_path / "mutant.c"
+    csrc.write_text(mutated)
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", str(csrc),
+                    "-o", str(lib)], check=True)
+    code = RUNNER.format(root=ROOT, tests=os.path.join(ROOT, "tests"), lib=str(lib))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       env=dict(os.environ, OMP_NUM_THREADS="2"))
+    if r.returncode != 0:
+        return  # crashed: caught
+    line = [l for l in r.stdout.splitlines() if l.startswith("FAILED_PINS")][0]
+    failed = [x for x in line.split(" ", 1)[1].split(",") if x] if " " in line else []
+    assert failed, f"mutant {name} passed every pin"
