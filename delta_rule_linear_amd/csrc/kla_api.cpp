@@ -1,0 +1,145 @@
+// C-ABI entry points of libkla.so (declared in include/kla.h): argument
+// validation on the host, then one kernel launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/kla.h"
+#include "kla_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range(const void *p, int64_t bytes) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+  return {b, b + static_cast<uintptr_t>(bytes > 0 ? bytes : 0)};
+}
+bool overlap(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool supported_dim(int32_t dk, int32_t dv) { return dk == dv && (dk == 64 || dk == 128); }
+
+}  // namespace
+
+extern "C" {
+
+const char *kla_status_string(kla_status s) {
+  switch (s) {
+    case KLA_OK: return "ok";
+    case KLA_ERR_INVALID_ARG: return "invalid argument";
+    case KLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case KLA_ERR_WORKSPACE: return "workspace too small";
+    case KLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *kla_version(void) { return "0.1.0 gfx950"; }
+
+size_t kla_fwd_chunked_workspace_size(int32_t, int64_t, int32_t, int32_t, int32_t, int32_t) {
+  return 0;
+}
+
+kla_status kla_fwd_chunked(const void *q, const void *k, const void *v, const float *alpha,
+                           const float *eta, const int32_t *cu_seqlens, int32_t n_seqs,
+                           int64_t total_tok, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                           float eps, kla_dtype dtype, const float *initial_state, float *o,
+                           float *final_state, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+  if (n_seqs <= 0 || H <= 0 || total_tok < 0 || !std::isfinite(eps) || eps < 0.f)
+    return KLA_ERR_INVALID_ARG;
+  if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
+  if (!supported_dim(dk, dv) || chunk != 64) return KLA_ERR_UNSUPPORTED;
+  if (!cu_seqlens && total_tok % n_seqs != 0) return KLA_ERR_INVALID_ARG;
+  if (workspace_bytes < kla_fwd_chunked_workspace_size(n_seqs, total_tok, H, dk, dv, chunk))
+    return KLA_ERR_WORKSPACE;
+  (void)workspace;
+  const bool have_tokens = total_tok > 0;
+  if (have_tokens && (!q || !k || !v || !alpha || !eta || !o)) return KLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(initial_state) || !aligned16(final_state))
+    return KLA_ERR_INVALID_ARG;
+
+  const int64_t esz = dtype == KLA_BF16 ? 2 : 4;
+  const int64_t th = total_tok * H;
+  const Range rq = range(q, th * dk * esz), rk = range(k, th * dk * esz),
+              rv = range(v, th * dv * esz), ra = range(alpha, th * 4), re = range(eta, th * 4),
+              ro = range(o, th * dv * 4),
+              rcu = range(cu_seqlens, cu_seqlens ? (int64_t)(n_seqs + 1) * 4 : 0),
+              rs0 = range(initial_state, initial_state ? (int64_t)n_seqs * H * dk * dv * 4 : 0),
+              rs1 = range(final_state, final_state ? (int64_t)n_seqs * H * dk * dv * 4 : 0);
+  for (const Range &in : {rq, rk, rv, ra, re, rcu, rs0, rs1})
+    if (overlap(ro, in)) return KLA_ERR_INVALID_ARG;
+  if (final_state) {
+    for (const Range &in : {rq, rk, rv, ra, re, rcu})
+      if (overlap(rs1, in)) return KLA_ERR_INVALID_ARG;
+    if (initial_state && initial_state != final_state && overlap(rs0, rs1))
+      return KLA_ERR_INVALID_ARG;
+  }
+
+  kla::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.eta = eta;
+  a.cu_seqlens = cu_seqlens;
+  a.n_seqs = n_seqs;
+  a.seq_len_dense = cu_seqlens ? 0 : total_tok / n_seqs;
+  a.H = H;
+  a.D = dk;
+  a.eps = eps;
+  a.initial_state = initial_state;
+  a.o = o;
+  a.final_state = final_state;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      dtype == KLA_BF16 ? kla::launch_prefill_bf16(a, st) : kla::launch_prefill_f32(a, st);
+  return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
+}
+
+kla_status kla_decode_step(const void *q, const void *k, const void *v, const float *alpha,
+                           const float *eta, float *state, float *o, int32_t n_seqs, int32_t H,
+                           int32_t dk, int32_t dv, float eps, kla_dtype dtype, void *stream) {
+  if (n_seqs <= 0 || H <= 0 || !std::isfinite(eps) || eps < 0.f) return KLA_ERR_INVALID_ARG;
+  if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
+  if (!supported_dim(dk, dv)) return KLA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !alpha || !eta || !state || !o) return KLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o))
+    return KLA_ERR_INVALID_ARG;
+  const int64_t esz = dtype == KLA_BF16 ? 2 : 4;
+  const int64_t nh = (int64_t)n_seqs * H;
+  const Range rq = range(q, nh * dk * esz), rk = range(k, nh * dk * esz),
+              rv = range(v, nh * dv * esz), ra = range(alpha, nh * 4), re = range(eta, nh * 4),
+              rs = range(state, nh * dk * dv * 4), ro = range(o, nh * dv * 4);
+  for (const Range &in : {rq, rk, rv, ra, re, rs})
+    if (overlap(ro, in)) return KLA_ERR_INVALID_ARG;
+  for (const Range &in : {rq, rk, rv, ra, re})
+    if (overlap(rs, in)) return KLA_ERR_INVALID_ARG;
+
+  kla::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.eta = eta;
+  a.state = state;
+  a.o = o;
+  a.n_seqs = n_seqs;
+  a.H = H;
+  a.D = dk;
+  a.eps = eps;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      dtype == KLA_BF16 ? kla::launch_decode_bf16(a, st) : kla::launch_decode_f32(a, st);
+  return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// KLA single-token decode step for gfx950.
+//
+// Per (sequence, head) the step is the KLA write followed by the read
+// (KLA technical summary, "Resumo Tecnico: Atencao Linear Kaczmarz (KLA)",
+// section "A Regra de Atualizacao KLA"), regrouped so the fp32 state is read
+// from HBM once and written once:
+//   x = S^T k,  y = S^T q                 (one sweep over S)
+//   beta = eta / (k.k + eps),  e = v - alpha x
+//   o = alpha y + beta (k.q) e            (= S_new^T q)
+//   S_new = alpha S + beta k e^T
+// The kernel is bound by HBM bandwidth (0.75 flop/byte): one workgroup per
+// (sequence, head), each thread holds RPT rows x 4 columns of the state in
+// registers between the read and the write.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kla_internal.h"
+
+namespace kla {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(__bf16 x) { return static_cast<float>(x); }
+
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void decode_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
+    const float *__restrict__ alpha, const float *__restrict__ eta, float *__restrict__ state,
+    float *__restrict__ o, float eps) {
+  constexpr int NQ = D / 4;              // float4 column groups per row
+  constexpr int NRG = kThreads / NQ;     // row groups
+  constexpr int RPT = D / NRG;           // rows per thread
+  static_assert(NQ * NRG == kThreads && RPT * NRG == D, "decode tiling");
+
+  __shared__ float sq[D], sk[D], sv[D], se[D];
+  __shared__ float px[NRG][D], py[NRG][D];
+
+  const int64_t sh = blockIdx.x;  // (sequence, head) pair
+  const int t = threadIdx.x;
+  const int cq = t % NQ, rg = t / NQ;
+  float *Sg = state + sh * (int64_t)(D * D);
+
+  // Issue the state loads first: they carry all the bytes.
+  float4 s[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    s[i] = *reinterpret_cast<const float4 *>(Sg + (rg + NRG * i) * D + 4 * cq);
+
+  if (t < D) {
+    sq[t] = to_f32(q[sh * D + t]);
+    sk[t] = to_f32(k[sh * D + t]);
+    sv[t] = to_f32(v[sh * D + t]);
+  }
+  const float a = alpha[sh];
+  const float et = eta[sh];
+  __syncthreads();
+
+  // k.k and k.q: every wave reduces its own copy (fixed order, no barrier).
+  float kk = 0.f, kq = 0.f;
+  {
+    const int l = t & 63;
+#pragma unroll
+    for (int i = l; i < D; i += 64) {
+      kk += sk[i] * sk[i];
+      kq += sk[i] * sq[i];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      kk += __shfl_xor(kk, off, 64);
+      kq += __shfl_xor(kq, off, 64);
+    }
+  }
+  const float beta = et / (kk + eps);
+
+  float4 xs = {0.f, 0.f, 0.f, 0.f}, ys = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const float kr = sk[rg + NRG * i], qr = sq[rg + NRG * i];
+    xs.x += s[i].x * kr; xs.y += s[i].y * kr; xs.z += s[i].z * kr; xs.w += s[i].w * kr;
+    ys.x += s[i].x * qr; ys.y += s[i].y * qr; ys.z += s[i].z * qr; ys.w += s[i].w * qr;
+  }
+  *reinterpret_cast<float4 *>(&px[rg][4 * cq]) = xs;
+  *reinterpret_cast<float4 *>(&py[rg][4 * cq]) = ys;
+  __syncthreads();
+
+  if (t < D) {
+    float x = 0.f, y = 0.f;
+#pragma unroll
+    for (int r = 0; r < NRG; ++r) {
+      x += px[r][t];
+      y += py[r][t];
+    }
+    const float e = sv[t] - a * x;
+    se[t] = e;
+    o[sh * D + t] = a * y + beta * kq * e;
+  }
+  __syncthreads();
+
+  const float4 e4 = *reinterpret_cast<const float4 *>(&se[4 * cq]);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const float bk = beta * sk[rg + NRG * i];
+    float4 r;
+    r.x = a * s[i].x + bk * e4.x;
+    r.y = a * s[i].y + bk * e4.y;
+    r.z = a * s[i].z + bk * e4.z;
+    r.w = a * s[i].w + bk * e4.w;
+    *reinterpret_cast<float4 *>(Sg + (rg + NRG * i) * D + 4 * cq) = r;
+  }
+}
+
+template <typename E>
+hipError_t launch(const DecodeArgs &a, hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)a.n_seqs * a.H)), block(kThreads);
+  const E *q = static_cast<const E *>(a.q), *k = static_cast<const E *>(a.k),
+          *v = static_cast<const E *>(a.v);
+  if (a.D == 128)
+    hipLaunchKernelGGL((decode_kernel<E, 128>), grid, block, 0, st, q, k, v, a.alpha, a.eta,
+                       a.state, a.o, a.eps);
+  else
+    hipLaunchKernelGGL((decode_kernel<E, 64>), grid, block, 0, st, q, k, v, a.alpha, a.eta,
+                       a.state, a.o, a.eps);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) { return launch<__bf16>(a, s); }
+hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s) { return launch<float>(a, s); }
+
+}  // namespace kla

@@ -1,0 +1,36 @@
+// Internal launcher interface between the C-ABI layer (kla_api.cpp) and the
+// HIP kernel translation units.  Arguments are already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kla {
+
+struct PrefillArgs {
+  const void *q, *k, *v;
+  const float *alpha, *eta;
+  const int32_t *cu_seqlens;  // device, or nullptr for dense
+  int32_t n_seqs;
+  int64_t seq_len_dense;      // tokens per sequence when cu_seqlens == nullptr
+  int32_t H, D;               // D = dk = dv
+  float eps;
+  const float *initial_state; // nullable
+  float *o;
+  float *final_state;         // nullable
+};
+
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const float *alpha, *eta;
+  float *state, *o;
+  int32_t n_seqs, H, D;
+  float eps;
+};
+
+// Each returns the HIP status of the launch.
+hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
+
+}  // namespace kla

@@ -1,0 +1,157 @@
+"""ctypes binding of libkla.so (C ABI in include/kla.h).
+
+Argument marshalling only: shapes are read from the torch tensors, outputs
+are allocated with torch when not given, and every step of the computation
+runs in the library's HIP kernels on torch's current stream.  There is no
+fallback: a missing library raises ImportError here.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libkla.so")
+if not os.path.exists(lib_path):
+    raise ImportError(f"{lib_path} is missing: build it with `python -m delta_rule_linear_amd.build`")
+_lib = ctypes.CDLL(lib_path)
+
+KLA_OK, KLA_ERR_INVALID_ARG, KLA_ERR_UNSUPPORTED, KLA_ERR_WORKSPACE, KLA_ERR_HIP = 0, -1, -2, -3, -4
+KLA_F32, KLA_BF16 = 0, 1
+
+_vp, _fp, _i32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+_lib.kla_fwd_chunked_workspace_size.restype = ctypes.c_size_t
+_lib.kla_fwd_chunked_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+_lib.kla_fwd_chunked.restype = ctypes.c_int
+_lib.kla_fwd_chunked.argtypes = [_vp, _vp, _vp, _fp, _fp, _i32p, ctypes.c_int32, ctypes.c_int64,
+                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_float, ctypes.c_int, _fp, _fp, _fp, _vp, ctypes.c_size_t,
+                                 _vp]
+_lib.kla_decode_step.restype = ctypes.c_int
+_lib.kla_decode_step.argtypes = [_vp, _vp, _vp, _fp, _fp, _fp, _fp, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int, _vp]
+_lib.kla_status_string.restype = ctypes.c_char_p
+_lib.kla_status_string.argtypes = [ctypes.c_int]
+_lib.kla_version.restype = ctypes.c_char_p
+_lib.kla_version.argtypes = []
+
+
+class KLAError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(f"libkla: {kla_status_string(status)} ({status})")
+
+
+def kla_status_string(status: int) -> str:
+    return _lib.kla_status_string(int(status)).decode()
+
+
+def kla_version() -> str:
+    return _lib.kla_version().decode()
+
+
+def kla_fwd_chunked_workspace_size(n_seqs, total_tok, H, dk, dv, chunk=64) -> int:
+    return int(_lib.kla_fwd_chunked_workspace_size(n_seqs, total_tok, H, dk, dv, chunk))
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return KLA_BF16
+    if t.dtype == torch.float32:
+        return KLA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def kla_fwd_chunked(q, k, v, alpha, eta, cu_seqlens=None, initial_state=None, eps=1e-6, chunk=64,
+                    output_final_state=False, o=None, final_state=None, workspace=None,
+                    stream=None):
+    """Chunked KLA prefill (C ABI `kla_fwd_chunked`).
+
+    q, k: [tok, H, dk] (packed, with cu_seqlens int32 [n+1]) or [B, T, H, dk]
+    (dense); v likewise with dv.  alpha, eta: [tok, H] or [B, T, H] fp32.
+    Returns (o fp32 shaped like v, final_state [n, H, dk, dv] fp32 or None).
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    _need(alpha, "alpha", torch.float32)
+    _need(eta, "eta", torch.float32)
+    dk, dv, H = q.shape[-1], v.shape[-1], q.shape[-2]
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        if q.dim() != 3:
+            raise ValueError("packed input (cu_seqlens given) must be [tok, H, d]")
+        n_seqs = cu_seqlens.numel() - 1
+        total = q.shape[0]
+    else:
+        if q.dim() == 4:
+            n_seqs, total = q.shape[0], q.shape[0] * q.shape[1]
+        elif q.dim() == 3:
+            n_seqs, total = 1, q.shape[0]
+        else:
+            raise ValueError("q must be [tok, H, d] or [B, T, H, d]")
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32)
+    if o is None:
+        o = torch.empty(v.shape, dtype=torch.float32, device=v.device)
+    else:
+        _need(o, "o", torch.float32)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n_seqs, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _need(final_state, "final_state", torch.float32)
+    ws_bytes = kla_fwd_chunked_workspace_size(n_seqs, total, H, dk, dv, chunk)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.kla_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(cu_seqlens),
+                              n_seqs, total, H, dk, dv, chunk, float(eps), _dtype_code(q),
+                              _ptr(initial_state), _ptr(o), _ptr(final_state), ws_ptr, ws_len,
+                              _stream(stream))
+    if st != KLA_OK:
+        raise KLAError(st)
+    return o, final_state
+
+
+def kla_decode_step(q, k, v, alpha, eta, state, eps=1e-6, o=None, stream=None):
+    """One KLA decode step (C ABI `kla_decode_step`); `state` is updated in place.
+
+    q, k: [N, H, dk]; v: [N, H, dv]; alpha, eta: [N, H] fp32;
+    state: [N, H, dk, dv] fp32.  Returns o [N, H, dv] fp32.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    _need(alpha, "alpha", torch.float32)
+    _need(eta, "eta", torch.float32)
+    _need(state, "state", torch.float32)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=torch.float32, device=q.device)
+    else:
+        _need(o, "o", torch.float32)
+    st = _lib.kla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(state),
+                              _ptr(o), N, H, dk, dv, float(eps), _dtype_code(q), _stream(stream))
+    if st != KLA_OK:
+        raise KLAError(st)
+    return o

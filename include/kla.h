@@ -1,0 +1,141 @@
+/*
+ * kla.h -- C ABI of libkla.so: Kaczmarz Linear Attention (KLA) prefill and
+ * decode on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (per sequence and per head, state S in R^{dk x dv}) is the
+ * gated delta rule with the Kaczmarz step size from the KLA technical
+ * summary ("Resumo Tecnico: Atencao Linear Kaczmarz (KLA)",
+ * gist.science/pt/paper/2605.08587), sections "Derivacao Teorica" and
+ * "A Regra de Atualizacao KLA":
+ *
+ *     beta_t = eta_t / (k_t^T k_t + eps)
+ *     S~     = alpha_t S_{t-1}
+ *     e_t    = v_t - S~^T k_t
+ *     S_t    = S~ + beta_t k_t e_t^T
+ *     o_t    = S_t^T q_t            (read after the write)
+ *
+ * alpha_t is the scalar decay gate and eta_t the relaxation gate; both are
+ * per (token, head).  No scaling is applied to q (callers pre-scale).
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are DEVICE pointers (HIP device memory) except where
+ *     noted; the caller owns every buffer.  The library never allocates or
+ *     frees memory and keeps no state between calls.
+ *   - Tensors are dense, row-major, with the innermost dimension contiguous.
+ *     Pointers to q, k, v, o and states must be 16-byte aligned.
+ *   - q, k, v share one element type (kla_dtype).  alpha, eta, o and all
+ *     states are fp32.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous and ordered on that stream; nothing synchronises the host.
+ *   - Arguments are checked on the host before any launch.  On an error
+ *     nothing is launched and no output is written.  Launch failures are
+ *     reported as KLA_ERR_HIP.
+ *   - Results are deterministic: repeated calls with the same inputs give
+ *     bitwise identical outputs (no atomics, fixed reduction order).
+ *   - Supported shapes: dk = dv in {64, 128}, chunk = 64.
+ */
+#ifndef KLA_H
+#define KLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KLA_OK = 0,
+    KLA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, aliasing */
+    KLA_ERR_UNSUPPORTED = -2, /* valid but not implemented (dk, dv, chunk, dtype) */
+    KLA_ERR_WORKSPACE = -3,   /* workspace smaller than the query returned */
+    KLA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} kla_status;
+
+typedef enum {
+    KLA_F32 = 0,  /* IEEE binary32 */
+    KLA_BF16 = 1  /* bfloat16 (8-bit exponent, 7-bit mantissa) */
+} kla_dtype;
+
+/*
+ * Bytes of device workspace kla_fwd_chunked needs for these sizes.  The
+ * current kernels need none and this returns 0; callers should still query
+ * it and pass a buffer at least that large.
+ */
+size_t kla_fwd_chunked_workspace_size(int32_t n_seqs, int64_t total_tok, int32_t H,
+                                      int32_t dk, int32_t dv, int32_t chunk);
+
+/*
+ * Chunkwise-parallel prefill over packed sequences.
+ *
+ * The chunked form computes the same result as the token recurrence above
+ * (up to rounding).  The KLA summary, section "Implementacao", keeps Gated
+ * DeltaNet's chunk-parallel algorithm and changes only the diagonal
+ * coefficient matrix B = Diag(beta_1..beta_C) of the chunk solver.
+ *
+ *   q, k        [total_tok, H, dk]   element type `dtype`
+ *   v           [total_tok, H, dv]   element type `dtype`
+ *   alpha, eta  [total_tok, H]       fp32; alpha in (0, 1], eta in [0, 1]
+ *   cu_seqlens  device int32 [n_seqs + 1] with 0 = cu[0] <= cu[1] <= ... <=
+ *               cu[n_seqs] = total_tok: sequence s is tokens [cu[s], cu[s+1]).
+ *               NULL means n_seqs equal sequences of total_tok / n_seqs tokens
+ *               (a dense [B, T, H, d] batch).  The contents are NOT checked on
+ *               the host (that would need a synchronisation); violating the
+ *               ordering above is undefined behaviour.
+ *   chunk       must be 64.
+ *   eps         the stabiliser in beta; eps >= 0.  With eps = 0 a zero key
+ *               gives a non-finite result.
+ *   initial_state [n_seqs, H, dk, dv] fp32 start state of each sequence, or
+ *               NULL for zeros.
+ *   o           [total_tok, H, dv] fp32, written: o_t = S_t^T q_t.
+ *   final_state [n_seqs, H, dk, dv] fp32, written with each sequence's last
+ *               state, or NULL.  It may be the same buffer as initial_state
+ *               (in-place update); any other overlap is an error.
+ *   workspace   device buffer of workspace_bytes >= the size query (may be
+ *               NULL when the query returns 0).
+ *
+ * Errors: KLA_ERR_INVALID_ARG for null required pointers, misalignment,
+ * n_seqs <= 0, H <= 0, total_tok < 0, total_tok not divisible by n_seqs when
+ * cu_seqlens is NULL, eps < 0 or not finite, or `o` overlapping an input;
+ * KLA_ERR_UNSUPPORTED for other dk/dv/chunk/dtype values; KLA_ERR_WORKSPACE
+ * for a short workspace; KLA_ERR_HIP if the launch fails.
+ */
+kla_status kla_fwd_chunked(const void *q, const void *k, const void *v,
+                           const float *alpha, const float *eta,
+                           const int32_t *cu_seqlens, int32_t n_seqs, int64_t total_tok,
+                           int32_t H, int32_t dk, int32_t dv, int32_t chunk, float eps,
+                           kla_dtype dtype, const float *initial_state, float *o,
+                           float *final_state, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * One recurrent decode step for n_seqs independent sequences: every
+ * (sequence, head) state advances by one token IN PLACE, and o receives the
+ * read of the new state.  It is the token recurrence above applied once,
+ * written as a single pass over the state:
+ *   x = S^T k, y = S^T q, e = v - alpha x, o = alpha y + beta (k^T q) e,
+ *   S <- alpha S + beta k e^T.
+ *
+ *   q, k        [n_seqs, H, dk]      element type `dtype`
+ *   v           [n_seqs, H, dv]      element type `dtype`
+ *   alpha, eta  [n_seqs, H]          fp32
+ *   state       [n_seqs, H, dk, dv]  fp32, read and updated in place
+ *   o           [n_seqs, H, dv]      fp32, written
+ *
+ * Errors: as kla_fwd_chunked (o must not overlap state or the inputs).
+ */
+kla_status kla_decode_step(const void *q, const void *k, const void *v,
+                           const float *alpha, const float *eta, float *state, float *o,
+                           int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, float eps,
+                           kla_dtype dtype, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *kla_status_string(kla_status s);
+
+/* Library version string, e.g. "0.1.0 gfx950". */
+const char *kla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KLA_H */

@@ -1,0 +1,132 @@
+"""libkla.so loads, exports every entry point include/kla.h declares, and
+rejects bad arguments on the host before any launch (no GPU needed: every
+call here fails validation, so no HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kla.h")
+LIB = os.path.join(ROOT, "delta_rule_linear_amd", "libkla.so")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kla_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from delta_rule_linear_amd import build
+        build.build()
+    L = ctypes.CDLL(LIB)
+    L.kla_fwd_chunked.restype = ctypes.c_int
+    L.kla_fwd_chunked.argtypes = [ctypes.c_void_p] * 6 + [
+        ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.kla_decode_step.restype = ctypes.c_int
+    L.kla_decode_step.argtypes = [ctypes.c_void_p] * 7 + [
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+        ctypes.c_int, ctypes.c_void_p]
+    L.kla_status_string.restype = ctypes.c_char_p
+    L.kla_status_string.argtypes = [ctypes.c_int]
+    L.kla_version.restype = ctypes.c_char_p
+    L.kla_fwd_chunked_workspace_size.restype = ctypes.c_size_t
+    L.kla_fwd_chunked_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64] + [ctypes.c_int32] * 4
+    return L
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["kla_fwd_chunked", "kla_fwd_chunked_workspace_size",
+                                           "kla_decode_step", "kla_status_string", "kla_version"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, 7):
+        s = lib.kla_status_string(code)
+        assert s and len(s) > 0
+    assert b"gfx950" in lib.kla_version()
+
+
+# Fake, never-dereferenced device addresses (validation fails before use).
+BASE = 1 << 40
+MB = 1 << 20
+
+
+def fwd_args(**over):
+    a = dict(q=BASE, k=BASE + 64 * MB, v=BASE + 128 * MB, alpha=BASE + 192 * MB,
+             eta=BASE + 200 * MB, cu=None, n_seqs=2, tok=128, H=2, dk=64, dv=64, chunk=64,
+             eps=1e-6, dtype=1, s0=None, o=BASE + 256 * MB, s1=None, ws=None, wsb=0, stream=None)
+    a.update(over)
+    return [a[x] for x in ("q", "k", "v", "alpha", "eta", "cu", "n_seqs", "tok", "H", "dk", "dv",
+                           "chunk", "eps", "dtype", "s0", "o", "s1", "ws", "wsb", "stream")]
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(n_seqs=0), INVALID),
+    (dict(H=0), INVALID),
+    (dict(tok=-1), INVALID),
+    (dict(tok=129), INVALID),          # dense batch not divisible by n_seqs
+    (dict(eps=-1.0), INVALID),
+    (dict(eps=float("nan")), INVALID),
+    (dict(q=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(alpha=None), INVALID),
+    (dict(q=BASE + 2), INVALID),       # misaligned
+    (dict(o=BASE + 256 * MB + 4), INVALID),
+    (dict(o=BASE + 8), INVALID),       # o overlaps q
+    (dict(s0=BASE + 300 * MB, s1=BASE + 300 * MB + 16), INVALID),  # partial state overlap
+    (dict(s1=BASE + 64 * MB), INVALID),  # final state overlaps k
+    (dict(dk=96, dv=96), UNSUPPORTED),
+    (dict(dk=64, dv=128), UNSUPPORTED),
+    (dict(chunk=32), UNSUPPORTED),
+    (dict(dtype=5), UNSUPPORTED),
+])
+def test_fwd_rejects(lib, over, code):
+    assert lib.kla_fwd_chunked(*fwd_args(**over)) == code
+
+
+def test_workspace_query(lib):
+    assert lib.kla_fwd_chunked_workspace_size(8, 16384, 16, 128, 128, 64) == 0
+
+
+def dec_args(**over):
+    a = dict(q=BASE, k=BASE + MB, v=BASE + 2 * MB, alpha=BASE + 3 * MB, eta=BASE + 4 * MB,
+             state=BASE + 8 * MB, o=BASE + 64 * MB, N=4, H=2, dk=128, dv=128, eps=1e-6, dtype=1,
+             stream=None)
+    a.update(over)
+    return [a[x] for x in ("q", "k", "v", "alpha", "eta", "state", "o", "N", "H", "dk", "dv",
+                           "eps", "dtype", "stream")]
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(N=0), INVALID),
+    (dict(state=None), INVALID),
+    (dict(o=BASE + 8 * MB + 64), INVALID),   # o inside state
+    (dict(state=BASE + 4), INVALID),         # misaligned
+    (dict(state=BASE + 2 * MB), INVALID),    # state overlaps v
+    (dict(eps=-0.5), INVALID),
+    (dict(dk=32, dv=32), UNSUPPORTED),
+    (dict(dtype=3), UNSUPPORTED),
+])
+def test_decode_rejects(lib, over, code):
+    assert lib.kla_decode_step(*dec_args(**over)) == code
+
+
+def test_binding_names_match_the_abi():
+    import delta_rule_linear_amd as pkg
+    for name in ("kla_fwd_chunked", "kla_decode_step", "kla_fwd_chunked_workspace_size",
+                 "kla_status_string", "kla_version"):
+        assert callable(getattr(pkg, name))
