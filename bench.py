@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""KLA prefill + decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One timed step is one kla_fwd_chunked call over the layer-shaped workload
+(8 sequences x 2048 tokens, 16 heads, dk = dv = 128, chunk 64, bf16 q/k/v,
+fp32 gates, fp32 o and final state), inputs already resident in HBM.  The
+headline value is prefill tokens/s.  The same JSON line also carries the
+decode step (256 sequences x 16 heads, 128 steps, fp32 state updated in
+place) as state GB/s, each kernel's roofline fraction from HIP events on the
+launch stream, and the fp64 reference timed on the host cores.
+
+Algorithmic work counted per token-head (d = 128, C = 64):
+  prefill bytes  q,k,v bf16 3*256 + alpha,eta 2*4 + o fp32 512 = 1288 B,
+                 plus the final state (d*d*4 B) once per (sequence, head)
+  prefill flops  full 16x16-tile MFMA count of the method as implemented:
+                 K K^T, Q K^T, T R, M Delta: 2*C*d each; Q S, K S, K^T Delta:
+                 2*d*d each  ->  8*C*d + 6*d*d = 163,840
+  decode bytes   the fp32 state read and written once: 2*d*d*4 per (seq, head)
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_MFMA_PEAK_TF = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+
+PREFILL_KERNEL = "prefill_kernel"
+DECODE_KERNEL = "decode_kernel"
+
+
+def prefill_work(n_seqs, T, H, d, C=64):
+    th = n_seqs * T * H
+    bytes_ = th * (3 * d * 2 + 2 * 4 + d * 4) + n_seqs * H * d * d * 4
+    flops = th * (8 * C * d + 6 * d * d)
+    return bytes_, flops
+
+
+def time_launches(fn, n, stream):
+    """Run fn n times on `stream`, bracketing every launch with HIP events.
+    Returns (wall seconds for the n launches, mean event ms per launch)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, sum(a.elapsed_time(b) for a, b in ev) / n
+
+
+def bench_prefill(args, torch, kla, workloads):
+    inp = workloads.prefill("layer")
+    B, H, d = inp["n_seqs"], inp["H"], inp["d"]
+    T = inp["lengths"][0]
+    dev = "cuda:0"
+    q = inp["q"].to(dev).view(B, T, H, d)
+    k = inp["k"].to(dev).view(B, T, H, d)
+    v = inp["v"].to(dev).view(B, T, H, d)
+    a = inp["alpha"].to(dev).view(B, T, H)
+    e = inp["eta"].to(dev).view(B, T, H)
+    o = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kla.kla_fwd_chunked(q, k, v, a, e, eps=inp["eps"], o=o, final_state=S)
+
+    for _ in range(args.warmup):
+        step()
+    wall, ev_ms = time_launches(step, args.steps, stream)
+    nbytes, flops = prefill_work(B, T, H, d)
+    return dict(inp=inp, tokens=B * T, wall=wall, ev_ms=ev_ms, bytes=nbytes, flops=flops,
+                shape=(B, T, H, d))
+
+
+def bench_decode(args, torch, kla, workloads):
+    wl = workloads.decode(steps=args.decode_steps)
+    dev = "cuda:0"
+    N, H, d = wl["n_seqs"], wl["H"], wl["d"]
+    state = wl["state"].to(dev)
+    steps = [{n: st[n].to(dev) for n in ("q", "k", "v", "alpha", "eta")} for st in wl["steps"]]
+    o = torch.empty((N, H, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    # warm up on a scratch copy so the timed run starts from the drawn state
+    scratch = state.clone()
+    for st in steps[:4]:
+        kla.kla_decode_step(st["q"], st["k"], st["v"], st["alpha"], st["eta"], scratch,
+                            eps=wl["eps"], o=o)
+    del scratch
+    it = iter(range(len(steps)))
+
+    def one():
+        st = steps[next(it)]
+        kla.kla_decode_step(st["q"], st["k"], st["v"], st["alpha"], st["eta"], state,
+                            eps=wl["eps"], o=o)
+
+    wall, ev_ms = time_launches(one, len(steps), stream)
+    state_bytes = 2 * N * H * d * d * 4
+    return dict(N=N, H=H, d=d, steps=len(steps), wall=wall, ev_ms=ev_ms, state_bytes=state_bytes)
+
+
+def cpu_baseline(pre, oracle):
+    """fp64 reference on the host over the whole layer-shaped prefill."""
+    import numpy as np
+    inp = pre["inp"]
+    B, T, H, d = pre["shape"]
+    cu = np.arange(B + 1, dtype=np.int64) * T
+    t0 = time.perf_counter()
+    oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["eta"], cu_seqlens=cu,
+               eps=float(np.float32(inp["eps"])))
+    dt = time.perf_counter() - t0
+    return dict(value=B * T / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"whole layer-shaped prefill ({B} seqs x {T} tokens x {H} heads, d={d}), "
+                       f"one run, {dt:.2f} s wall including the fp64 conversion of the inputs",
+                seconds=round(dt, 3))
+
+
+def calibrate_copy(torch):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    n = 1 << 28  # 256 Mi floats = 1 GiB read + 1 GiB written
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": 4 * n, "bytes_written": 4 * n,
+                      "launches": 3}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; the multi-GPU layout is a design "
+              "(sequences and heads shard with no communication) and is not measured. "
+              "Run with --gpus 1.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
+    import workloads
+    import delta_rule_linear_amd as kla
+
+    pre = bench_prefill(args, torch, kla, workloads)
+    ms_per_step = pre["wall"] * 1e3 / args.steps
+    value = pre["tokens"] / (pre["wall"] / args.steps)
+    ach_gbs = pre["bytes"] / (pre["ev_ms"] * 1e-3) / 1e9
+    ach_tf = pre["flops"] / (pre["ev_ms"] * 1e-3) / 1e12
+    B, T, H, d = pre["shape"]
+    out = {
+        "metric": "KLA prefill tokens/s (H=16,d=128) + decode state GB/s, % of MI355X roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"layer-shaped KLA prefill: {B} sequences x {T} tokens, H={H}, "
+                               f"dk=dv={d}, chunk 64, bf16 q/k/v, fp32 alpha/eta/o/final state",
+                   "tokens_per_step": pre["tokens"], "token_heads_per_step": B * T * H},
+        "roofline": {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": PREFILL_KERNEL, "avg_launch_us": round(pre["ev_ms"] * 1e3, 2),
+                     "algorithmic_bytes_per_launch": pre["bytes"],
+                     "mfma_tflops": round(ach_tf, 2),
+                     "mfma_frac": round(ach_tf / BF16_MFMA_PEAK_TF, 4),
+                     "algorithmic_flops_per_launch": pre["flops"]},
+    }
+    if not args.skip_decode:
+        dec = bench_decode(args, torch, kla, workloads)
+        dgbs = dec["state_bytes"] / (dec["ev_ms"] * 1e-3) / 1e9
+        out["decode"] = {
+            "workload": f"decode step: {dec['N']} sequences x {dec['H']} heads, dk=dv={dec['d']}, "
+                        f"bf16 q/k/v, fp32 state in place, {dec['steps']} successive steps",
+            "us_per_step": round(dec["wall"] * 1e6 / dec["steps"], 2),
+            "tokens_per_s": round(dec["N"] * dec["steps"] / dec["wall"], 1),
+            "roofline": {"bound": "hbm", "achieved": round(dgbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(dgbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": DECODE_KERNEL, "avg_launch_us": round(dec["ev_ms"] * 1e3, 2),
+                         "algorithmic_bytes_per_launch": dec["state_bytes"]},
+        }
+    if not args.skip_cpu_baseline:
+        import oracle
+        out["cpu_baseline"] = cpu_baseline(pre, oracle)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

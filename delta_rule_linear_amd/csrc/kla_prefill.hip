@@ -16,21 +16,33 @@
 //   S'    = e^{g_n} S + K^T Diag(e^{g_n - g}) Delta
 //
 // This is the WY form U - W S with U = T V, W = T Diag(e^g) K, regrouped so
-// W is never formed (one dk-long contraction less per chunk).
+// W is never formed (one dk-long contraction less per chunk).  T itself is
+// never formed either: with 16-row blocks b, Ahat = K K^T o Gam and
+// Y_bb = (I + Diag(beta_b) Ahat_bb)^{-1} Diag(beta_b) (a 16x16 block inverse),
+// Delta follows by block forward substitution
+//   Delta_b = Y_bb (R_b - sum_{m<b} Ahat_bm Delta_m),
+// which is (I + L) Delta = Diag(beta) R solved blockwise.
 //
 // Mapping.  One workgroup of 4 waves per (sequence, head, 64-column block of
 // dv); each wave owns 16 columns of the state and keeps them in MFMA
-// accumulator registers for the whole sequence.  Per chunk all waves stage
-// K, Q, V and the gates in LDS, compute the Gram tiles on MFMA, solve T in
-// fp32, and then each wave runs the state-dependent chain on its own
-// columns.  A state tile in accumulator layout feeds the next MFMA directly
+// accumulator registers for the whole sequence.  Per chunk:
+//   1. all waves stage K, Q, V in LDS; row norms |k|^2 are reduced on the way
+//      in and wave 0 scans the log-decays;
+//   2. wave 0 computes the diagonal K K^T tiles and inverts the four 16x16
+//      diagonal blocks, while waves 1-3 compute the other Gram tiles; then
+//      every wave forms Q S, K S and R for its columns;
+//   3. every wave runs the substitution for Delta, the output, and the
+//      state update on its own columns.
+// A state (or Delta) tile in accumulator layout feeds the next MFMA directly
 // as its B operand: the contraction index is permuted consistently on the A
-// side, so the state never goes through LDS.
+// side, so those tiles never go through LDS.  K^T for the state update is
+// read from the row-major K tile with the transposing LDS read.
 //
 // Precision.  bf16 inputs enter MFMA exactly.  Every fp32 intermediate
-// (S, T, R, M, Delta) enters as a hi+lo pair of bf16 (x = hi + lo + O(2^-17 x));
-// products of two split operands use hi*hi + hi*lo + lo*hi.  fp32 inputs use
-// the fp32 MFMA (v_mfma_f32_16x16x4_f32) throughout.
+// (S, R, Y, Ahat, M, Delta) enters as a hi+lo pair of bf16
+// (x = hi + lo + O(2^-17 x)); products of two split operands use
+// hi*hi + hi*lo + lo*hi.  fp32 inputs use the fp32 MFMA
+// (v_mfma_f32_16x16x4_f32) throughout.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -44,27 +56,24 @@ namespace {
 typedef __bf16 bf16;
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int C = 64;         // chunk length
+constexpr int C = 64;             // chunk length
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int DVB = 16 * kWaves;  // dv columns per workgroup
-
-// Lower-triangular 16x16 tile list of a 64x64 matrix (row block, col block).
-__constant__ int8_t kTri[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1},
-                                   {2, 2}, {3, 0}, {3, 1}, {3, 2}, {3, 3}};
 
 template <typename E, int D>
 struct Cfg {
   static constexpr bool BF = std::is_same<E, bf16>::value;
   using P = typename std::conditional<BF, bf16, float>::type;  // operand-plane type
-  static constexpr int LDK = D + (BF ? 8 : 4);   // K, Q rows (elements)
-  static constexpr int LDKT = C + 8;             // K^T rows (bf16 only)
-  static constexpr int LDV = DVB + (BF ? 8 : 4); // V rows
-  static constexpr int LDF = C + 4;              // fp32 64x64 work matrices
-  static constexpr int LDP = BF ? C + 8 : C + 4; // T, M operand planes
-  static constexpr int NST = D / 16;             // state tiles per wave (dk direction)
+  static constexpr int LDK = D + (BF ? 8 : 4);    // K, Q rows (elements)
+  static constexpr int LDV = DVB + (BF ? 8 : 4);  // V rows
+  static constexpr int LDP = BF ? C + 8 : C + 4;  // Ahat, M operand planes (64x64)
+  static constexpr int LDY = 20;                  // Y diagonal blocks (16x16)
+  static constexpr int NST = D / 16;              // state tiles per wave (dk direction)
 };
 
 template <typename E, int D>
@@ -74,61 +83,83 @@ struct Smem {
   // Every member starts on a 16-byte boundary (128-bit LDS accesses).
   alignas(16) E Kr[C * CF::LDK];
   alignas(16) E Qr[C * CF::LDK];
-  alignas(16) E Kt[CF::BF ? D * CF::LDKT : 8];
   alignas(16) E Vs[C * CF::LDV];
-  alignas(16) float Lf[C * CF::LDF];
-  alignas(16) float Xf[C * CF::LDF];
-  alignas(16) P Th[C * CF::LDP];
-  alignas(16) P Tl[CF::BF ? C * CF::LDP : 8];
-  alignas(16) P Mh[C * CF::LDP];
+  alignas(16) P Ah[C * CF::LDP];  // -Ahat below the block diagonal
+  alignas(16) P Al[CF::BF ? C * CF::LDP : 8];
+  alignas(16) P Mh[C * CF::LDP];  // M = lower(Q K^T o Gam)
   alignas(16) P Ml[CF::BF ? C * CF::LDP : 8];
-  alignas(16) float tmp[3 * 256];
-  alignas(16) float g[C];
-  alignas(16) float beta[C];
-  alignas(16) float gam[C];
-  alignas(16) float rgam[C];
-  alignas(16) float al[C];
+  alignas(16) P Yh[4 * 16 * CF::LDY];
+  alignas(16) P Yl[CF::BF ? 4 * 16 * CF::LDY : 8];
+  alignas(16) float Ld[4 * 16 * 17];  // Diag(beta) Ahat on the diagonal blocks
+  alignas(16) float kk[C];
   alignas(16) float et[C];
+  alignas(16) float beta[C];
+  alignas(16) float g2[C];    // cumulative log2 decay
+  alignas(16) float gam[C];   // 2^g2
+  alignas(16) float rgam[C];  // 2^(g2_last - g2)
 };
 
 __device__ inline f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ inline f32x4 mma(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 __device__ inline f32x4 mma(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+struct Split4 {
+  bf16x4 hi, lo;
+};
 struct Split8 {
   bf16x8 hi, lo;
 };
 
-// B operand of a 32-deep bf16 MFMA taken from two accumulator tiles that
-// cover contraction rows [0,16) and [16,32): element i of lane-group j holds
-// row 4j+i (i<4) or 16+4j+(i-4) (i>=4).  Each value is split into hi + lo.
-__device__ inline Split8 split_tiles(f32x4 c0, f32x4 c1) {
-  Split8 r;
+// One accumulator tile as the B operand of a 16-deep MFMA (lane-group j
+// holds contraction rows 4j..4j+3, exactly the tile's own rows), split into
+// hi + lo.
+__device__ inline Split4 split4(f32x4 c) {
+  Split4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    bf16 h0 = static_cast<bf16>(c0[i]);
-    bf16 h1 = static_cast<bf16>(c1[i]);
-    r.hi[i] = h0;
-    r.lo[i] = static_cast<bf16>(c0[i] - static_cast<float>(h0));
-    r.hi[4 + i] = h1;
-    r.lo[4 + i] = static_cast<bf16>(c1[i] - static_cast<float>(h1));
+    const bf16 h = static_cast<bf16>(c[i]);
+    r.hi[i] = h;
+    r.lo[i] = static_cast<bf16>(c[i] - static_cast<float>(h));
   }
   return r;
 }
+// Two tiles covering contraction rows [0,16) and [16,32) as the B operand of
+// a 32-deep MFMA: element i of lane-group j holds row 4j+i (i<4) or
+// 16+4j+(i-4) (i>=4).
+__device__ inline Split8 join(const Split4 &a, const Split4 &b) {
+  Split8 r;
+  r.hi = __builtin_shufflevector(a.hi, b.hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  r.lo = __builtin_shufflevector(a.lo, b.lo, 0, 1, 2, 3, 4, 5, 6, 7);
+  return r;
+}
 
-// A operand matching split_tiles' row order: from a row-major source row
+// A operand matching join()'s row order: from a row-major source row
 // (pointer at column kb), columns kb+4j..kb+4j+3 and kb+16+4j..kb+16+4j+3.
 __device__ inline bf16x8 lda_perm(const bf16 *row, int j) {
-  bf16x4 x = *reinterpret_cast<const bf16x4 *>(row + 4 * j);
-  bf16x4 y = *reinterpret_cast<const bf16x4 *>(row + 16 + 4 * j);
+  const bf16x4 x = *reinterpret_cast<const bf16x4 *>(row + 4 * j);
+  const bf16x4 y = *reinterpret_cast<const bf16x4 *>(row + 16 + 4 * j);
   return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ inline bf16x4 lda4(const bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
+// lane i receives element i%4 of the 8-byte chunks addressed by lanes
+// 4e + i/4, e = 0..3.  With lane c addressing row (r0 + c/4), columns
+// c0 + 4(c%4) .. +3 of a row-major tile, lane i gets column c0 + i of rows
+// r0 .. r0+3: a transposed 4-element operand.
+__device__ inline bf16x4 ld_tr(const bf16 *p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+  return __builtin_bit_cast(bf16x4, v);
 }
 
 __device__ inline void store_split(bf16 *h, bf16 *l, int idx, float x) {
-  bf16 hv = static_cast<bf16>(x);
+  const bf16 hv = static_cast<bf16>(x);
   h[idx] = hv;
   l[idx] = static_cast<bf16>(x - static_cast<float>(hv));
 }
@@ -143,6 +174,36 @@ __device__ inline int64_t logical_block() {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + kx;
 }
 
+// Gram jobs of waves 1-3: kind 0 = K K^T block below the diagonal (-> -Ahat),
+// kind 1 = Q K^T block on or below the diagonal (-> M).
+struct Job {
+  int8_t kind, bi, bj;
+};
+__constant__ Job kJobs[16] = {{0, 1, 0}, {0, 2, 0}, {0, 2, 1}, {0, 3, 0}, {0, 3, 1},
+                              {0, 3, 2}, {1, 0, 0}, {1, 1, 0}, {1, 1, 1}, {1, 2, 0},
+                              {1, 2, 1}, {1, 2, 2}, {1, 3, 0}, {1, 3, 1}, {1, 3, 2},
+                              {1, 3, 3}};
+
+// 16x16 Gram tile G[r][s] = sum_d A[r0+r][d] B[s0+s][d] (rows of A, B in LDS).
+template <typename E, int D>
+__device__ inline f32x4 gram_tile(const E *A, const E *B, int r0, int s0, int j, int c16) {
+  using CF = Cfg<E, D>;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (CF::BF) {
+#pragma unroll
+    for (int k0 = 0; k0 < D; k0 += 32) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&A[(r0 + c16) * CF::LDK + k0 + 8 * j]);
+      const bf16x8 b = *reinterpret_cast<const bf16x8 *>(&B[(s0 + c16) * CF::LDK + k0 + 8 * j]);
+      acc = mma(a, b, acc);
+    }
+  } else {
+#pragma unroll
+    for (int k0 = 0; k0 < D; k0 += 4)
+      acc = mma(A[(r0 + c16) * CF::LDK + k0 + j], B[(s0 + c16) * CF::LDK + k0 + j], acc);
+  }
+  return acc;
+}
+
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
@@ -154,15 +215,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   constexpr bool BF = CF::BF;
   constexpr int NB = D / DVB;
   constexpr int NST = CF::NST;
-  constexpr int SEG_EL = 16 / sizeof(E);       // elements per 16-byte segment
-  constexpr int SEG_ROW = D / SEG_EL;          // segments per K/Q row
-  constexpr int SEG_VROW = DVB / SEG_EL;       // segments per V row (this block)
+  constexpr int SEG_EL = 16 / sizeof(E);  // elements per 16-byte segment
+  constexpr int SEG_ROW = D / SEG_EL;     // segments per K/Q row
+  constexpr int SEG_VROW = DVB / SEG_EL;  // segments per V row (this block)
+  static_assert(kThreads % SEG_ROW == 0, "row segments must not straddle waves");
 
   __shared__ Smem<E, D> sm;
 
   const int tid = threadIdx.x;
-  const int w = tid / 64, l = tid % 64;
-  const int j = l / 16, c16 = l % 16;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  const int l = tid & 63;
+  const int j = l >> 4, c16 = l & 15;
 
   const int64_t lb = logical_block();
   const int nb = (int)(lb % NB);
@@ -179,14 +242,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   }
   const int col = nb * DVB + 16 * w + c16;  // this lane's state/output column
 
-  // Planes of T and M above the block diagonal are read as zeros.
+  // M above the block diagonal is read as zero.
   for (int i = tid; i < C * CF::LDP; i += kThreads) {
-    sm.Th[i] = P(0.f);
     sm.Mh[i] = P(0.f);
-    if constexpr (BF) {
-      sm.Tl[i] = P(0.f);
-      sm.Ml[i] = P(0.f);
-    }
+    if constexpr (BF) sm.Ml[i] = P(0.f);
   }
 
   // State tiles: tile t holds rows 16t+4j+i (i<4), column `col`.
@@ -202,8 +261,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   for (int64_t tok0 = bos; tok0 < eos; tok0 += C) {
     const int n = (int)((eos - tok0) < C ? (eos - tok0) : C);
 
-    // ---- stage the chunk in LDS (rows >= n are zero) ----------------------
-    __syncthreads();  // previous chunk's readers are done with LDS
+    // ---- 1. stage the chunk in LDS (rows >= n are zero) -------------------
+    __syncthreads();  // the previous chunk's readers are done with LDS
     for (int sg = tid; sg < C * SEG_ROW; sg += kThreads) {
       const int r = sg / SEG_ROW, cs = sg % SEG_ROW;
       uint4 kv = {0, 0, 0, 0}, qv = {0, 0, 0, 0};
@@ -214,11 +273,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       }
       *reinterpret_cast<uint4 *>(&sm.Kr[r * CF::LDK + cs * SEG_EL]) = kv;
       *reinterpret_cast<uint4 *>(&sm.Qr[r * CF::LDK + cs * SEG_EL]) = qv;
-      if constexpr (BF) {
-        const bf16 *ke = reinterpret_cast<const bf16 *>(&kv);
+      // |k_r|^2: this segment's share, reduced over the SEG_ROW lanes of row r
+      const E *ke = reinterpret_cast<const E *>(&kv);
+      float part = 0.f;
 #pragma unroll
-        for (int e = 0; e < SEG_EL; ++e) sm.Kt[(cs * SEG_EL + e) * CF::LDKT + r] = ke[e];
+      for (int e = 0; e < SEG_EL; ++e) {
+        const float x = static_cast<float>(ke[e]);
+        part += x * x;
       }
+#pragma unroll
+      for (int off = SEG_ROW / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+      if (cs == 0) sm.kk[r] = part;
     }
     for (int sg = tid; sg < C * SEG_VROW; sg += kThreads) {
       const int r = sg / SEG_VROW, cs = sg % SEG_VROW;
@@ -228,73 +293,89 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
                                               nb * DVB + cs * SEG_EL);
       *reinterpret_cast<uint4 *>(&sm.Vs[r * CF::LDV + cs * SEG_EL]) = vv;
     }
-    if (tid < C) {
-      const bool in = tid < n;
-      sm.al[tid] = in ? alpha[(tok0 + tid) * H + h] : 1.f;
-      sm.et[tid] = in ? eta[(tok0 + tid) * H + h] : 0.f;
-    }
-    __syncthreads();
-
-    // ---- gates: beta, cumulative log-decay g (wave 0, one lane per row) ---
     if (w == 0) {
-      float kk = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < D; ++d) {
-        const float x = static_cast<float>(sm.Kr[l * CF::LDK + d]);
-        kk += x * x;
-      }
-      const float b = l < n ? sm.et[l] / (kk + eps) : 0.f;
-      float g = l < n ? logf(sm.al[l]) : 0.f;
+      // cumulative log2-decay over the chunk (rows >= n: alpha = 1, eta = 0)
+      const bool in = l < n;
+      const float a = in ? alpha[(tok0 + l) * H + h] : 1.f;
+      sm.et[l] = in ? eta[(tok0 + l) * H + h] : 0.f;
+      float g = log2f(a);
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(g, off, 64);
         if (l >= off) g += y;
       }
       const float glast = __shfl(g, 63, 64);
-      sm.g[l] = g;
-      sm.beta[l] = b;
-      sm.gam[l] = expf(g);
-      sm.rgam[l] = expf(glast - g);
+      sm.g2[l] = g;
+      sm.gam[l] = exp2f(g);
+      sm.rgam[l] = exp2f(glast - g);
     }
     __syncthreads();
 
-    // ---- Gram tiles on MFMA: L (fp32, for the solve) and M (operand) -----
-    for (int job = w; job < 20; job += kWaves) {
-      const int bi = kTri[job % 10][0], bj = kTri[job % 10][1];
-      const E *A = job < 10 ? sm.Kr : sm.Qr;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (BF) {
+    // ---- 2. Gram tiles, diagonal block inverses, Q S, K S, R --------------
+    if (w == 0) {
+      const float b_l = sm.et[l] / (sm.kk[l] + eps);
+      sm.beta[l] = b_l;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // diagonal K K^T tiles -> Diag(beta) Ahat on the diagonal blocks (strictly lower)
 #pragma unroll
-        for (int k0 = 0; k0 < D; k0 += 32) {
-          bf16x8 a = *reinterpret_cast<const bf16x8 *>(&A[(16 * bi + c16) * CF::LDK + k0 + 8 * j]);
-          bf16x8 b =
-              *reinterpret_cast<const bf16x8 *>(&sm.Kr[(16 * bj + c16) * CF::LDK + k0 + 8 * j]);
-          acc = mma(a, b, acc);
+      for (int b = 0; b < 4; ++b) {
+        const f32x4 acc = gram_tile<E, D>(sm.Kr, sm.Kr, 16 * b, 16 * b, j, c16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * j + i, R = 16 * b + r, Sc = 16 * b + c16;
+          sm.Ld[(b * 16 + r) * 17 + c16] =
+              r > c16 ? sm.beta[R] * acc[i] * exp2f(sm.g2[R] - sm.g2[Sc]) : 0.f;
         }
-      } else {
-#pragma unroll
-        for (int k0 = 0; k0 < D; k0 += 4)
-          acc = mma(A[(16 * bi + c16) * CF::LDK + k0 + j], sm.Kr[(16 * bj + c16) * CF::LDK + k0 + j],
-                    acc);
       }
-      const int sc = 16 * bj + c16;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // lane (block j, column c16): x = (I + L_jj)^{-1} e_c by substitution
+      {
+        const float *Lb = &sm.Ld[j * 16 * 17];
+        float x[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * bi + 4 * j + i;
-        const float dec = expf(fminf(sm.g[r] - sm.g[sc], 0.f));
-        if (job < 10)
-          sm.Lf[r * CF::LDF + sc] = r > sc ? sm.beta[r] * acc[i] * dec : 0.f;
-        else
-          store_split(sm.Mh, sm.Ml, r * CF::LDP + sc, r >= sc ? acc[i] * dec : 0.f);
+        for (int r = 0; r < 16; ++r) {
+          float a0 = (r == c16) ? 1.f : 0.f, a1 = 0.f;
+#pragma unroll
+          for (int t = 0; t < r; t += 2) {
+            a0 -= Lb[r * 17 + t] * x[t];
+            if (t + 1 < r) a1 -= Lb[r * 17 + t + 1] * x[t + 1];
+          }
+          x[r] = a0 + a1;
+        }
+        // Y = X Diag(beta): column c16 scaled by beta of that column
+        const float bc = sm.beta[16 * j + c16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) store_split(sm.Yh, sm.Yl, (j * 16 + r) * CF::LDY + c16, x[r] * bc);
+      }
+    } else {
+      const int q0 = w == 1 ? 0 : (w == 2 ? 5 : 10), q1 = w == 1 ? 5 : (w == 2 ? 10 : 16);
+      for (int qj = q0; qj < q1; ++qj) {
+        const Job jb = kJobs[qj];
+        const f32x4 acc =
+            gram_tile<E, D>(jb.kind ? sm.Qr : sm.Kr, sm.Kr, 16 * jb.bi, 16 * jb.bj, j, c16);
+        const int Sc = 16 * jb.bj + c16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int R = 16 * jb.bi + 4 * j + i;
+          const float dec = exp2f(fminf(sm.g2[R] - sm.g2[Sc], 0.f));
+          if (jb.kind == 0)
+            store_split(sm.Ah, sm.Al, R * CF::LDP + Sc, -acc[i] * dec);
+          else
+            store_split(sm.Mh, sm.Ml, R * CF::LDP + Sc, R >= Sc ? acc[i] * dec : 0.f);
+        }
       }
     }
 
-    // ---- state-dependent products that do not need T: QS, KS, R ---------
+    // Q S and K S for this wave's columns, then R = V - diag(gamma) K S
     f32x4 QS[4], R[4];
     if constexpr (BF) {
       Split8 Sf[NST / 2];
 #pragma unroll
-      for (int kk = 0; kk < NST / 2; ++kk) Sf[kk] = split_tiles(S[2 * kk], S[2 * kk + 1]);
+      for (int kk = 0; kk < NST / 2; ++kk) Sf[kk] = join(split4(S[2 * kk]), split4(S[2 * kk + 1]));
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
         f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
@@ -326,7 +407,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         R[bi] = ak;
       }
     }
-    // R = V - diag(gamma) K S  (rows 16bi+4j+i, local column 16w+c16)
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
@@ -336,80 +416,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       }
     __syncthreads();
 
-    // ---- T = (I + L)^{-1} Diag(beta): blocked forward substitution --------
-    // Diagonal 16x16 blocks: wave 0, lane (block j, column c16) solves
-    // (I + L_jj) x = e_c by substitution down the rows.
-    if (w == 0) {
-      float x[16];
-      const int b0 = 16 * j;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == c16) ? 1.f : 0.f;
-#pragma unroll
-        for (int t = 0; t < r; ++t) acc -= sm.Lf[(b0 + r) * CF::LDF + b0 + t] * x[t];
-        x[r] = acc;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sm.Xf[(b0 + r) * CF::LDF + b0 + c16] = x[r];
-    }
-    __syncthreads();
-    // Off-diagonal blocks by distance d from the diagonal:
-    //   X_ij = -X_ii * sum_{m=j}^{i-1} L_im X_mj,  i - j = d.
-    {
-      const int rr = tid / 16, cc = tid % 16;
-      for (int d = 1; d < 4; ++d) {
-        for (int qb = 0; qb < 4 - d; ++qb) {
-          const int i = d + qb, jb = qb;
-          float acc = 0.f;
-          for (int m = jb; m < i; ++m)
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-              acc += sm.Lf[(16 * i + rr) * CF::LDF + 16 * m + t] *
-                     sm.Xf[(16 * m + t) * CF::LDF + 16 * jb + cc];
-          sm.tmp[qb * 256 + tid] = acc;
-        }
-        __syncthreads();
-        for (int qb = 0; qb < 4 - d; ++qb) {
-          const int i = d + qb, jb = qb;
-          float acc = 0.f;
-#pragma unroll
-          for (int t = 0; t < 16; ++t)
-            acc += sm.Xf[(16 * i + rr) * CF::LDF + 16 * i + t] * sm.tmp[qb * 256 + t * 16 + cc];
-          sm.Xf[(16 * i + rr) * CF::LDF + 16 * jb + cc] = -acc;
-        }
-        __syncthreads();
-      }
-      // T = X Diag(beta) on the lower block triangle, as MFMA operand planes.
-#pragma unroll
-      for (int tt = 0; tt < 10; ++tt) {
-        const int r = 16 * kTri[tt][0] + rr, sc = 16 * kTri[tt][1] + cc;
-        store_split(sm.Th, sm.Tl, r * CF::LDP + sc, sm.Xf[r * CF::LDF + sc] * sm.beta[sc]);
-      }
-    }
-    __syncthreads();
-
-    // ---- chain: Delta = T R, O = diag(gamma) QS + M Delta, state update ---
+    // ---- 3. Delta by block substitution, output, state update -------------
     f32x4 Dl[4];
     if constexpr (BF) {
-      Split8 Rf[2];
-      Rf[0] = split_tiles(R[0], R[1]);
-      Rf[1] = split_tiles(R[2], R[3]);
+      Split4 Ds[4];
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < 4; ++b) {
+        f32x4 acc = R[b];
 #pragma unroll
-        for (int kk = 0; kk <= bi / 2; ++kk) {
-          const int off = (16 * bi + c16) * CF::LDP + 32 * kk;
-          const bf16x8 ah = lda_perm(&sm.Th[off], j), al = lda_perm(&sm.Tl[off], j);
-          acc = mma(ah, Rf[kk].hi, acc);
-          acc = mma(ah, Rf[kk].lo, acc);
-          acc = mma(al, Rf[kk].hi, acc);
+        for (int m = 0; m < b; ++m) {
+          const int off = (16 * b + c16) * CF::LDP + 16 * m + 4 * j;
+          const bf16x4 ah = lda4(&sm.Ah[off]), al = lda4(&sm.Al[off]);
+          acc = mma(ah, Ds[m].hi, acc);
+          acc = mma(ah, Ds[m].lo, acc);
+          acc = mma(al, Ds[m].hi, acc);
         }
-        Dl[bi] = acc;
+        const Split4 as = split4(acc);
+        const int yo = (b * 16 + c16) * CF::LDY + 4 * j;
+        const bf16x4 yh = lda4(&sm.Yh[yo]), yl = lda4(&sm.Yl[yo]);
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        d = mma(yh, as.hi, d);
+        d = mma(yh, as.lo, d);
+        d = mma(yl, as.hi, d);
+        Dl[b] = d;
+        Ds[b] = split4(d);
       }
-      Split8 Df[2];
-      Df[0] = split_tiles(Dl[0], Dl[1]);
-      Df[1] = split_tiles(Dl[2], Dl[3]);
+      const Split8 Df[2] = {join(Ds[0], Ds[1]), join(Ds[2], Ds[3])};
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
         f32x4 acc;
@@ -427,19 +459,24 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       }
     } else {
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int mt = 0; mt <= bi; ++mt)
+      for (int b = 0; b < 4; ++b) {
+        f32x4 acc = R[b];
+#pragma unroll
+        for (int m = 0; m < b; ++m)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            acc = mma(sm.Th[(16 * bi + c16) * CF::LDP + 16 * mt + 4 * j + i], R[mt][i], acc);
-        Dl[bi] = acc;
+            acc = mma(sm.Ah[(16 * b + c16) * CF::LDP + 16 * m + 4 * j + i], Dl[m][i], acc);
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d = mma(sm.Yh[(b * 16 + c16) * CF::LDY + 4 * j + i], acc[i], d);
+        Dl[b] = d;
       }
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
         f32x4 acc;
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = sm.gam[16 * bi + 4 * j + i] * QS[bi][i];
+#pragma unroll
         for (int mt = 0; mt <= bi; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -457,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         if (r < n) o[((tok0 + r) * H + h) * (int64_t)D + col] = QS[bi][i];
       }
 
-    // S' = e^{g_n} S + K^T Diag(e^{g_n - g}) Delta
+    // S' = 2^{g2_last} S + K^T Diag(2^{g2_last - g2}) Delta
     const float glast = sm.gam[C - 1];
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi)
@@ -466,14 +503,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
     for (int t = 0; t < NST; ++t) S[t] *= glast;
     if constexpr (BF) {
-      Split8 Hf[2];
-      Hf[0] = split_tiles(Dl[0], Dl[1]);
-      Hf[1] = split_tiles(Dl[2], Dl[3]);
+      const Split8 Hf[2] = {join(split4(Dl[0]), split4(Dl[1])), join(split4(Dl[2]), split4(Dl[3]))};
 #pragma unroll
       for (int t = 0; t < NST; ++t)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 a = lda_perm(&sm.Kt[(16 * t + c16) * CF::LDKT + 32 * kk], j);
+          // K^T rows 16t.., tokens 32kk+4j+e and 32kk+16+4j+e (join() order)
+          const bf16 *base = &sm.Kr[16 * t + 4 * (c16 & 3)];
+          const bf16x4 x0 = ld_tr(base + (32 * kk + 4 * j + (c16 >> 2)) * CF::LDK);
+          const bf16x4 x1 = ld_tr(base + (32 * kk + 16 + 4 * j + (c16 >> 2)) * CF::LDK);
+          const bf16x8 a = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
           S[t] = mma(a, Hf[kk].hi, S[t]);
           S[t] = mma(a, Hf[kk].lo, S[t]);
         }
