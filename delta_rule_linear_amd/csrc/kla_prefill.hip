@@ -47,6 +47,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "kla_internal.h"
 
@@ -90,7 +91,7 @@ struct Smem {
   alignas(16) P Ml[CF::BF ? C * CF::LDP : 8];
   alignas(16) P Yh[4 * 16 * CF::LDY];
   alignas(16) P Yl[CF::BF ? 4 * 16 * CF::LDY : 8];
-  alignas(16) float Ld[4 * 16 * 17];  // Diag(beta) Ahat on the diagonal blocks
+  alignas(16) float Ld[4 * 16 * 20];  // Diag(beta) Ahat on the diagonal blocks, [block][col][row]
   alignas(16) float kk[C];
   alignas(16) float et[C];
   alignas(16) float beta[C];
@@ -158,6 +159,75 @@ __device__ inline bf16x4 ld_tr(const bf16 *p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// Workgroup barrier that orders LDS traffic only.  __syncthreads() also
+// waits for every outstanding global load, which would expose the latency of
+// the next chunk's prefetch at each barrier.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// DPP lane movement within 16-lane rows (gfx9 controls plus row_share).
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Same, but lanes whose source is outside the row (or rows masked off by
+// ROWS) read zero.
+template <int CTRL, int ROWS = 0xF>
+__device__ inline float dpp0(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;       // quad_perm [1,0,3,2], [2,3,0,1]
+constexpr int kHalfMirror = 0x141, kRowRor4 = 0x124, kRowRor8 = 0x128;
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+constexpr int kRowShare0 = 0x150;                        // + t: lane t of each row
+
+// Sum over aligned groups of N lanes (N = 8, 16 or 32); every lane gets it.
+template <int N>
+__device__ inline float group_sum(float x) {
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  if constexpr (N == 8) {
+    x += dpp<kHalfMirror>(x);
+  } else {
+    x += dpp<kRowRor4>(x);
+    x += dpp<kRowRor8>(x);
+  }
+  if constexpr (N == 32) x += __shfl_xor(x, 16, 64);
+  return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ inline float wave_scan(float x) {
+  x += dpp0<kRowShr1>(x);
+  x += dpp0<kRowShr2>(x);
+  x += dpp0<kRowShr4>(x);
+  x += dpp0<kRowShr8>(x);
+  x += dpp0<kRowBcast15, 0xA>(x);  // rows 1, 3 add the last lane of rows 0, 2
+  x += dpp0<kRowBcast31, 0xC>(x);  // rows 2, 3 add lane 31
+  return x;
+}
+
+// Range-checked buffer access: a load past the descriptor's byte range
+// returns zero and a store past it is dropped, so ragged chunk tails and
+// absent states need no branches (and no conservative waits on the memory
+// counter around them).  Word 3 selects the 32-bit raw data format.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  const int64_t b = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)(uint32_t)b, 0x00020000);
+}
+__device__ inline uint4 buf_ld16(rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return uint4{v.x, v.y, v.z, v.w};
+}
+__device__ inline float buf_ld4(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ inline void buf_st4(rsrc_t r, uint32_t off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)off, 0, 0);
+}
+
 __device__ inline void store_split(bf16 *h, bf16 *l, int idx, float x) {
   const bf16 hv = static_cast<bf16>(x);
   h[idx] = hv;
@@ -174,15 +244,28 @@ __device__ inline int64_t logical_block() {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + kx;
 }
 
-// Gram jobs of waves 1-3: kind 0 = K K^T block below the diagonal (-> -Ahat),
-// kind 1 = Q K^T block on or below the diagonal (-> M).
+// Gram jobs of waves 1-3, numbered 0..15: jobs 0-5 are the K K^T blocks
+// below the diagonal (-> -Ahat), in row order (1,0) (2,0) (2,1) (3,0) (3,1)
+// (3,2); jobs 6-15 are the Q K^T blocks on or below the diagonal (-> M), in
+// row order (0,0) (1,0) (1,1) (2,0) ... (3,3).  Decoded with scalar
+// arithmetic from a wave-uniform job number.
 struct Job {
-  int8_t kind, bi, bj;
+  bool qk;
+  int bi, bj;
 };
-__constant__ Job kJobs[16] = {{0, 1, 0}, {0, 2, 0}, {0, 2, 1}, {0, 3, 0}, {0, 3, 1},
-                              {0, 3, 2}, {1, 0, 0}, {1, 1, 0}, {1, 1, 1}, {1, 2, 0},
-                              {1, 2, 1}, {1, 2, 2}, {1, 3, 0}, {1, 3, 1}, {1, 3, 2},
-                              {1, 3, 3}};
+__device__ inline Job job_of(int qj) {
+  Job jb;
+  jb.qk = qj >= 6;
+  if (!jb.qk) {
+    jb.bi = 1 + (qj >= 1) + (qj >= 3);
+    jb.bj = qj - (jb.bi - 1) * jb.bi / 2;
+  } else {
+    const int p = qj - 6;
+    jb.bi = (p >= 1) + (p >= 3) + (p >= 6);
+    jb.bj = p - jb.bi * (jb.bi + 1) / 2;
+  }
+  return jb;
+}
 
 // 16x16 Gram tile G[r][s] = sum_d A[r0+r][d] B[s0+s][d] (rows of A, B in LDS).
 template <typename E, int D>
@@ -190,18 +273,34 @@ __device__ inline f32x4 gram_tile(const E *A, const E *B, int r0, int s0, int j,
   using CF = Cfg<E, D>;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if constexpr (CF::BF) {
+    // all operands first, then the MFMA chain
+    bf16x8 a[D / 32], b[D / 32];
 #pragma unroll
-    for (int k0 = 0; k0 < D; k0 += 32) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&A[(r0 + c16) * CF::LDK + k0 + 8 * j]);
-      const bf16x8 b = *reinterpret_cast<const bf16x8 *>(&B[(s0 + c16) * CF::LDK + k0 + 8 * j]);
-      acc = mma(a, b, acc);
+    for (int u = 0; u < D / 32; ++u) {
+      a[u] = *reinterpret_cast<const bf16x8 *>(&A[(r0 + c16) * CF::LDK + 32 * u + 8 * j]);
+      b[u] = *reinterpret_cast<const bf16x8 *>(&B[(s0 + c16) * CF::LDK + 32 * u + 8 * j]);
     }
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) acc = mma(a[u], b[u], acc);
   } else {
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += 4)
       acc = mma(A[(r0 + c16) * CF::LDK + k0 + j], B[(s0 + c16) * CF::LDK + k0 + j], acc);
   }
   return acc;
+}
+
+// One column step of the 16x16 unit-lower-triangular substitution:
+// x[r] -= L[r][t] x[t] for r > t, with L[r][t] broadcast from lane t.
+template <int T>
+__device__ inline void solve_step(float (&x)[16], const float (&lc)[16]) {
+#pragma unroll
+  for (int r = T + 1; r < 16; ++r) x[r] -= dpp<kRowShare0 + T>(lc[r]) * x[T];
+}
+template <int... T>
+__device__ inline void solve_steps(float (&x)[16], const float (&lc)[16],
+                                   std::integer_sequence<int, T...>) {
+  (solve_step<T>(x, lc), ...);
 }
 
 template <typename E, int D>
@@ -248,68 +347,94 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     if constexpr (BF) sm.Ml[i] = P(0.f);
   }
 
-  // State tiles: tile t holds rows 16t+4j+i (i<4), column `col`.
+  // State tiles: tile t holds rows 16t+4j+i (i<4), column `col`.  A null
+  // start state is an empty buffer range: every load returns zero.
+  const int64_t sbase = (s * H + h) * (int64_t)D * D;
   f32x4 S[NST];
   {
-    const float *src = S0 ? S0 + ((s * H + h) * (int64_t)D) * D : nullptr;
+    const rsrc_t rs = make_rsrc(S0 ? S0 + sbase : o, S0 ? (int64_t)D * D * 4 : 0);
 #pragma unroll
     for (int t = 0; t < NST; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S[t][i] = src ? src[(16 * t + 4 * j + i) * D + col] : 0.f;
+      for (int i = 0; i < 4; ++i) S[t][i] = buf_ld4(rs, ((16 * t + 4 * j + i) * D + col) * 4);
   }
 
-  for (int64_t tok0 = bos; tok0 < eos; tok0 += C) {
-    const int n = (int)((eos - tok0) < C ? (eos - tok0) : C);
-
-    // ---- 1. stage the chunk in LDS (rows >= n are zero) -------------------
-    __syncthreads();  // the previous chunk's readers are done with LDS
-    for (int sg = tid; sg < C * SEG_ROW; sg += kThreads) {
-      const int r = sg / SEG_ROW, cs = sg % SEG_ROW;
-      uint4 kv = {0, 0, 0, 0}, qv = {0, 0, 0, 0};
-      if (r < n) {
-        const int64_t off = ((tok0 + r) * H + h) * (int64_t)D + cs * SEG_EL;
-        kv = *reinterpret_cast<const uint4 *>(k + off);
-        qv = *reinterpret_cast<const uint4 *>(q + off);
-      }
-      *reinterpret_cast<uint4 *>(&sm.Kr[r * CF::LDK + cs * SEG_EL]) = kv;
-      *reinterpret_cast<uint4 *>(&sm.Qr[r * CF::LDK + cs * SEG_EL]) = qv;
+  // Chunk inputs are loaded one chunk ahead into registers, so their HBM
+  // latency overlaps the previous chunk's compute.
+  constexpr int NSEG = C * SEG_ROW / kThreads;   // K (and Q) segments per thread
+  constexpr int NVSEG = C * SEG_VROW / kThreads; // V segments per thread
+  static_assert(NSEG * kThreads == C * SEG_ROW && NVSEG * kThreads == C * SEG_VROW, "tiling");
+  uint4 kreg[NSEG], qreg[NSEG], vreg[NVSEG];
+  float areg = 1.f, ereg = 0.f;
+  auto fetch = [&](int64_t t0) {
+    // rows past the end of the sequence fall outside the descriptors: zeros
+    const int64_t nn = (eos - t0) < C ? (eos - t0) : C;
+    const int64_t rowb = (int64_t)H * D * sizeof(E);
+    const rsrc_t rk = make_rsrc(k + t0 * H * (int64_t)D, nn * rowb);
+    const rsrc_t rq = make_rsrc(q + t0 * H * (int64_t)D, nn * rowb);
+    const rsrc_t rv = make_rsrc(v + t0 * H * (int64_t)D, nn * rowb);
+#pragma unroll
+    for (int u = 0; u < NSEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+      const uint32_t off = (uint32_t)((r * H + h) * D + cs * SEG_EL) * sizeof(E);
+      kreg[u] = buf_ld16(rk, off);
+      qreg[u] = buf_ld16(rq, off);
+    }
+#pragma unroll
+    for (int u = 0; u < NVSEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
+      vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + nb * DVB + cs * SEG_EL) * sizeof(E));
+    }
+    if (w == 0) {
+      const rsrc_t ra = make_rsrc(alpha + t0 * H, nn * H * 4);
+      const rsrc_t re = make_rsrc(eta + t0 * H, nn * H * 4);
+      areg = buf_ld4(ra, (uint32_t)(l * H + h) * 4);  // zero past the end
+      ereg = buf_ld4(re, (uint32_t)(l * H + h) * 4);
+    }
+  };
+  // Copy the prefetched chunk starting at t0 into LDS, with |k|^2 per row
+  // and (wave 0) the scanned log2-decays.
+  auto stage = [&](int64_t t0) {
+#pragma unroll
+    for (int u = 0; u < NSEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+      *reinterpret_cast<uint4 *>(&sm.Kr[r * CF::LDK + cs * SEG_EL]) = kreg[u];
+      *reinterpret_cast<uint4 *>(&sm.Qr[r * CF::LDK + cs * SEG_EL]) = qreg[u];
       // |k_r|^2: this segment's share, reduced over the SEG_ROW lanes of row r
-      const E *ke = reinterpret_cast<const E *>(&kv);
+      const E *ke = reinterpret_cast<const E *>(&kreg[u]);
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < SEG_EL; ++e) {
         const float x = static_cast<float>(ke[e]);
         part += x * x;
       }
-#pragma unroll
-      for (int off = SEG_ROW / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+      part = group_sum<SEG_ROW>(part);
       if (cs == 0) sm.kk[r] = part;
     }
-    for (int sg = tid; sg < C * SEG_VROW; sg += kThreads) {
-      const int r = sg / SEG_VROW, cs = sg % SEG_VROW;
-      uint4 vv = {0, 0, 0, 0};
-      if (r < n)
-        vv = *reinterpret_cast<const uint4 *>(v + ((tok0 + r) * H + h) * (int64_t)D +
-                                              nb * DVB + cs * SEG_EL);
-      *reinterpret_cast<uint4 *>(&sm.Vs[r * CF::LDV + cs * SEG_EL]) = vv;
+#pragma unroll
+    for (int u = 0; u < NVSEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
+      *reinterpret_cast<uint4 *>(&sm.Vs[r * CF::LDV + cs * SEG_EL]) = vreg[u];
     }
     if (w == 0) {
-      // cumulative log2-decay over the chunk (rows >= n: alpha = 1, eta = 0)
-      const bool in = l < n;
-      const float a = in ? alpha[(tok0 + l) * H + h] : 1.f;
-      sm.et[l] = in ? eta[(tok0 + l) * H + h] : 0.f;
-      float g = log2f(a);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(g, off, 64);
-        if (l >= off) g += y;
-      }
+      // cumulative log2-decay over the chunk (rows past the end: alpha = 1, eta = 0)
+      sm.et[l] = ereg;
+      const float g = wave_scan(l < eos - t0 ? log2f(areg) : 0.f);  // alpha = 1 past the end
       const float glast = __shfl(g, 63, 64);
       sm.g2[l] = g;
       sm.gam[l] = exp2f(g);
       sm.rgam[l] = exp2f(glast - g);
     }
-    __syncthreads();
+  };
+
+  fetch(bos);
+  stage(bos);
+  for (int64_t tok0 = bos; tok0 < eos; tok0 += C) {
+    const int n = (int)((eos - tok0) < C ? (eos - tok0) : C);
+    lds_barrier();  // chunk tok0 is staged
+    // Prefetch the next chunk (past the end the descriptors are empty and the
+    // loads return zeros without touching memory).
+    fetch(tok0 + C);
 
     // ---- 2. Gram tiles, diagonal block inverses, Q S, K S, R --------------
     if (w == 0) {
@@ -322,52 +447,63 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const f32x4 acc = gram_tile<E, D>(sm.Kr, sm.Kr, 16 * b, 16 * b, j, c16);
+        const float gS = sm.g2[16 * b + c16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i, R = 16 * b + r, Sc = 16 * b + c16;
-          sm.Ld[(b * 16 + r) * 17 + c16] =
-              r > c16 ? sm.beta[R] * acc[i] * exp2f(sm.g2[R] - sm.g2[Sc]) : 0.f;
+          const int r = 4 * j + i, R = 16 * b + r;
+          const float v = sm.beta[R] * acc[i] * exp2f(fminf(sm.g2[R] - gS, 0.f));
+          sm.Ld[(b * 16 + c16) * 20 + r] = r > c16 ? v : 0.f;
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // lane (block j, column c16): x = (I + L_jj)^{-1} e_c by substitution
+      // lane (block j, column c16): x = (I + L_jj)^{-1} e_c by substitution,
+      // column-oriented: once x_t is final it is eliminated from every later
+      // row.  Each lane holds column c16 of L_jj; L[r][t] reaches the whole
+      // row of lanes by a DPP broadcast from lane t.
       {
-        const float *Lb = &sm.Ld[j * 16 * 17];
+        float lc[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 v4 = *reinterpret_cast<const float4 *>(&sm.Ld[(j * 16 + c16) * 20 + 4 * q4]);
+          lc[4 * q4] = v4.x;
+          lc[4 * q4 + 1] = v4.y;
+          lc[4 * q4 + 2] = v4.z;
+          lc[4 * q4 + 3] = v4.w;
+        }
         float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float a0 = (r == c16) ? 1.f : 0.f, a1 = 0.f;
-#pragma unroll
-          for (int t = 0; t < r; t += 2) {
-            a0 -= Lb[r * 17 + t] * x[t];
-            if (t + 1 < r) a1 -= Lb[r * 17 + t + 1] * x[t + 1];
-          }
-          x[r] = a0 + a1;
-        }
+        for (int r = 0; r < 16; ++r) x[r] = (r == c16) ? 1.f : 0.f;
+        solve_steps(x, lc, std::make_integer_sequence<int, 15>{});
         // Y = X Diag(beta): column c16 scaled by beta of that column
         const float bc = sm.beta[16 * j + c16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) store_split(sm.Yh, sm.Yl, (j * 16 + r) * CF::LDY + c16, x[r] * bc);
       }
     } else {
-      const int q0 = w == 1 ? 0 : (w == 2 ? 5 : 10), q1 = w == 1 ? 5 : (w == 2 ? 10 : 16);
-      for (int qj = q0; qj < q1; ++qj) {
-        const Job jb = kJobs[qj];
-        const f32x4 acc =
-            gram_tile<E, D>(jb.kind ? sm.Qr : sm.Kr, sm.Kr, 16 * jb.bi, 16 * jb.bj, j, c16);
+      // waves 1, 2, 3 take jobs [0,5), [5,10), [10,16): straight-line code,
+      // plane and mask chosen arithmetically so the jobs can overlap.
+      const int q0 = 5 * (w - 1);
+      auto job = [&](int qj) {
+        const Job jb = job_of(qj);
+        const bool qk = jb.qk;
+        const f32x4 acc = gram_tile<E, D>(qk ? sm.Qr : sm.Kr, sm.Kr, 16 * jb.bi, 16 * jb.bj, j, c16);
+        P *ph = qk ? sm.Mh : sm.Ah;
+        P *pl = qk ? sm.Ml : sm.Al;
+        const float sgn = qk ? 1.f : -1.f;
         const int Sc = 16 * jb.bj + c16;
+        const float gS = sm.g2[Sc];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int R = 16 * jb.bi + 4 * j + i;
-          const float dec = exp2f(fminf(sm.g2[R] - sm.g2[Sc], 0.f));
-          if (jb.kind == 0)
-            store_split(sm.Ah, sm.Al, R * CF::LDP + Sc, -acc[i] * dec);
-          else
-            store_split(sm.Mh, sm.Ml, R * CF::LDP + Sc, R >= Sc ? acc[i] * dec : 0.f);
+          const float v = sgn * acc[i] * exp2f(fminf(sm.g2[R] - gS, 0.f));
+          store_split(ph, pl, R * CF::LDP + Sc, R >= Sc ? v : 0.f);
         }
-      }
+      };
+#pragma unroll
+      for (int u = 0; u < 5; ++u) job(q0 + u);
+      if (w == 3) job(15);
     }
 
     // Q S and K S for this wave's columns, then R = V - diag(gamma) K S
@@ -414,7 +550,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         const int r = 16 * bi + 4 * j + i;
         R[bi][i] = static_cast<float>(sm.Vs[r * CF::LDV + 16 * w + c16]) - sm.gam[r] * R[bi][i];
       }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 3. Delta by block substitution, output, state update -------------
     f32x4 Dl[4];
@@ -485,14 +621,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       }
     }
 
-    // output rows < n
+    // output rows < n (rows past the end fall outside the descriptor)
+    {
+      const rsrc_t ro = make_rsrc(o + tok0 * H * (int64_t)D, (int64_t)n * H * D * 4);
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
+      for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * bi + 4 * j + i;
-        if (r < n) o[((tok0 + r) * H + h) * (int64_t)D + col] = QS[bi][i];
-      }
+        for (int i = 0; i < 4; ++i) {
+          const float val = QS[bi][i];
+          buf_st4(ro, (uint32_t)(((16 * bi + 4 * j + i) * H + h) * D + col) * 4, val);
+        }
+    }
 
     // S' = 2^{g2_last} S + K^T Diag(2^{g2_last - g2}) Delta
     const float glast = sm.gam[C - 1];
@@ -525,14 +664,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
           for (int i = 0; i < 4; ++i)
             S[t] = mma(sm.Kr[(16 * mt + 4 * j + i) * CF::LDK + 16 * t + c16], Dl[mt][i], S[t]);
     }
+    lds_barrier();  // everyone is done with this chunk's LDS
+    stage(tok0 + C);
   }
 
-  if (Sfin) {
-    float *dst = Sfin + ((s * H + h) * (int64_t)D) * D;
+  {
+    const rsrc_t rs = make_rsrc(Sfin ? Sfin + sbase : o, Sfin ? (int64_t)D * D * 4 : 0);
 #pragma unroll
     for (int t = 0; t < NST; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(16 * t + 4 * j + i) * D + col] = S[t][i];
+      for (int i = 0; i < 4; ++i) {
+        const float val = S[t][i];
+        buf_st4(rs, ((16 * t + 4 * j + i) * D + col) * 4, val);
+      }
   }
 }
 
