@@ -33,6 +33,70 @@ BF16_MFMA_PEAK_TF = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 
 PREFILL_KERNEL = "prefill_kernel"
 DECODE_KERNEL = "decode_kernel"
+KERNEL_SOURCES = {PREFILL_KERNEL: "delta_rule_linear_amd/csrc/kla_prefill.hip",
+                  DECODE_KERNEL: "delta_rule_linear_amd/csrc/kla_decode.hip"}
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def source_hash(kernel):
+    import hashlib
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_hash(kernel):
+        return None
+    return rec["bytes_per_launch"]
+
+
+def ingest_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
+    """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) into
+    bytes per launch, scaled by what the same counters read for a plain
+    1 GiB device copy (bench.py --calibrate-copy), and record them with the
+    kernel source hash in profiles/hbm_traffic.json."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        acc = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    def copy_kib(path, counter):
+        vals = [v for k, v in per_kernel(path, counter).items() if "copyBuffer" in k]
+        return vals[0]
+
+    gib_kib = float(1 << 20)  # the calibration copy reads and writes 1 GiB
+    f_scale = gib_kib / copy_kib(cal_fetch_csv, "FETCH_SIZE")
+    w_scale = gib_kib / copy_kib(cal_write_csv, "WRITE_SIZE")
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    out = {}
+    for kernel in KERNEL_SOURCES:
+        fk = [v for k, v in fetch.items() if kernel in k]
+        wk = [v for k, v in write.items() if kernel in k]
+        if not fk or not wk:
+            continue
+        rb, wb = fk[0] * f_scale * 1024, wk[0] * w_scale * 1024
+        out[kernel] = {"source_sha256": source_hash(kernel), "fetch_kib_raw": fk[0],
+                       "write_kib_raw": wk[0], "fetch_scale": round(f_scale, 5),
+                       "write_scale": round(w_scale, 5), "read_bytes": round(rb),
+                       "write_bytes": round(wb), "bytes_per_launch": round(rb + wb)}
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def prefill_work(n_seqs, T, H, d, C=64):
@@ -148,7 +212,13 @@ def main():
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                           "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                    help="record rocprofv3 counter CSVs into profiles/hbm_traffic.json")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -187,8 +257,8 @@ def main():
                                f"dk=dv={d}, chunk 64, bf16 q/k/v, fp32 alpha/eta/o/final state",
                    "tokens_per_step": pre["tokens"], "token_heads_per_step": B * T * H},
         "roofline": {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(ach_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": PREFILL_KERNEL, "avg_launch_us": round(pre["ev_ms"] * 1e3, 2),
+                     "unit": "GB/s", "frac": round(ach_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(PREFILL_KERNEL), "kernel": PREFILL_KERNEL, "avg_launch_us": round(pre["ev_ms"] * 1e3, 2),
                      "algorithmic_bytes_per_launch": pre["bytes"],
                      "mfma_tflops": round(ach_tf, 2),
                      "mfma_frac": round(ach_tf / BF16_MFMA_PEAK_TF, 4),
@@ -203,8 +273,8 @@ def main():
             "us_per_step": round(dec["wall"] * 1e6 / dec["steps"], 2),
             "tokens_per_s": round(dec["N"] * dec["steps"] / dec["wall"], 1),
             "roofline": {"bound": "hbm", "achieved": round(dgbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(dgbs / HBM_PEAK_GBS, 4), "traffic": None,
-                         "kernel": DECODE_KERNEL, "avg_launch_us": round(dec["ev_ms"] * 1e3, 2),
+                         "unit": "GB/s", "frac": round(dgbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(DECODE_KERNEL), "kernel": DECODE_KERNEL, "avg_launch_us": round(dec["ev_ms"] * 1e3, 2),
                          "algorithmic_bytes_per_launch": dec["state_bytes"]},
         }
     if not args.skip_cpu_baseline:
