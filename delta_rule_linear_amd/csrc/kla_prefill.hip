@@ -680,6 +680,387 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   }
 }
 
+// ===========================================================================
+// bf16 prefill with producer and consumer waves.
+//
+// Eight waves per workgroup.  Waves 0-3 (consumers) own 16 state columns
+// each and run the state-dependent chain of chunk c; waves 4-7 (producers)
+// stage chunk c+1 in LDS and compute its Gram tiles and diagonal-block
+// inverses at the same time.  Each SIMD hosts one consumer and one producer,
+// so the two halves of the chunk work overlap instead of running in turn.
+// Chunk data lives in two LDS slots used alternately; per chunk:
+//   segment A: producers stage chunk c+1 (and prefetch c+2 from HBM);
+//              consumers form Q S, K S and R for chunk c;
+//   barrier;
+//   segment B: producers build chunk c+1's operand planes;
+//              consumers run the substitution, output and state update of c;
+//   barrier.
+// ===========================================================================
+
+template <int D>
+struct PSlot {
+  using CF = Cfg<bf16, D>;
+  static constexpr int LDA = 20;  // compact 16x16 blocks of -Ahat and Y
+  alignas(16) bf16 Kr[C * CF::LDK];
+  alignas(16) bf16 Qr[C * CF::LDK];
+  alignas(16) bf16 Vs[C * CF::LDV];
+  alignas(16) bf16 Ah[6 * 16 * LDA];  // -Ahat blocks (b, m), m < b, index b(b-1)/2 + m
+  alignas(16) bf16 Al[6 * 16 * LDA];
+  alignas(16) bf16 Mh[C * CF::LDP];   // M = lower(Q K^T o Gam), zero above the block diagonal
+  alignas(16) bf16 Ml[C * CF::LDP];
+  alignas(16) bf16 Yh[4 * 16 * LDA];  // Y_bb = (I + L_bb)^{-1} Diag(beta_b)
+  alignas(16) bf16 Yl[4 * 16 * LDA];
+  alignas(16) float gam[C];
+  alignas(16) float rgam[C];
+};
+template <int D>
+struct PSmem {
+  PSlot<D> slot[2];
+  // producer scratch for the chunk being prepared
+  alignas(16) float Ld[4 * 16 * 20];  // Diag(beta) Ahat on the diagonal blocks, [block][col][row]
+  alignas(16) float kk[C];
+  alignas(16) float et[C];
+  alignas(16) float beta[C];
+  alignas(16) float g2[C];
+};
+
+template <int D>
+__global__ __launch_bounds__(512) void prefill_pc_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ alpha, const float *__restrict__ eta,
+    const int32_t *__restrict__ cu_seqlens, int64_t seq_len_dense, int H, float eps,
+    const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ Sfin) {
+  using CF = Cfg<bf16, D>;
+  using SL = PSlot<D>;
+  constexpr int LDA = SL::LDA;
+  constexpr int NB = D / DVB;
+  constexpr int NST = CF::NST;
+  constexpr int SEG_EL = 8;               // bf16 per 16-byte segment
+  constexpr int SEG_ROW = D / SEG_EL;     // segments per K/Q row
+  constexpr int SEG_VROW = DVB / SEG_EL;  // segments per V row (this block)
+  constexpr int PT = 256;                 // producer threads
+  constexpr int NSEG = C * SEG_ROW / PT;
+  constexpr int NVSEG = C * SEG_VROW / PT;
+  static_assert(NSEG * PT == C * SEG_ROW && NVSEG * PT == C * SEG_VROW, "tiling");
+
+  __shared__ PSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  const bool producer = w >= 4;
+  const int pw = w - 4;                                    // producer wave 0..3
+  const int ptid = tid - PT;
+  const int l = tid & 63;
+  const int j = l >> 4, c16 = l & 15;
+
+  const int64_t lb = logical_block();
+  const int nb = (int)(lb % NB);
+  const int64_t shi = lb / NB;
+  const int h = (int)(shi % H);
+  const int64_t s = shi / H;
+  int64_t bos, eos;
+  if (cu_seqlens) {
+    bos = cu_seqlens[s];
+    eos = cu_seqlens[s + 1];
+  } else {
+    bos = s * seq_len_dense;
+    eos = bos + seq_len_dense;
+  }
+  const int col = nb * DVB + 16 * w + c16;  // consumer lane's state/output column
+  const int64_t sbase = (s * H + h) * (int64_t)D * D;
+
+  // M above the block diagonal is read as zero (both slots).
+  for (int i = tid; i < C * CF::LDP; i += 512) {
+    sm.slot[0].Mh[i] = bf16(0.f);
+    sm.slot[0].Ml[i] = bf16(0.f);
+    sm.slot[1].Mh[i] = bf16(0.f);
+    sm.slot[1].Ml[i] = bf16(0.f);
+  }
+
+  // ---- producer pieces ------------------------------------------------------
+  uint4 kreg[NSEG], qreg[NSEG], vreg[NVSEG];
+  float areg = 1.f, ereg = 0.f;
+  auto fetch = [&](int64_t t0) {  // HBM -> registers (zeros past the end)
+    const int64_t nn = (eos - t0) < C ? (eos - t0) : C;
+    const int64_t rowb = (int64_t)H * D * 2;
+    const rsrc_t rk = make_rsrc(k + t0 * H * (int64_t)D, nn * rowb);
+    const rsrc_t rq = make_rsrc(q + t0 * H * (int64_t)D, nn * rowb);
+    const rsrc_t rv = make_rsrc(v + t0 * H * (int64_t)D, nn * rowb);
+#pragma unroll
+    for (int u = 0; u < NSEG; ++u) {
+      const int sg = u * PT + ptid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+      const uint32_t off = (uint32_t)((r * H + h) * D + cs * SEG_EL) * 2;
+      kreg[u] = buf_ld16(rk, off);
+      qreg[u] = buf_ld16(rq, off);
+    }
+#pragma unroll
+    for (int u = 0; u < NVSEG; ++u) {
+      const int sg = u * PT + ptid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
+      vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + nb * DVB + cs * SEG_EL) * 2);
+    }
+    if (pw == 0) {
+      const rsrc_t ra = make_rsrc(alpha + t0 * H, nn * H * 4);
+      const rsrc_t re = make_rsrc(eta + t0 * H, nn * H * 4);
+      areg = buf_ld4(ra, (uint32_t)(l * H + h) * 4);  // zero past the end
+      ereg = buf_ld4(re, (uint32_t)(l * H + h) * 4);
+    }
+  };
+  auto stage = [&](SL &sl, int64_t t0) {  // registers -> LDS slot, row norms, decay scan
+#pragma unroll
+    for (int u = 0; u < NSEG; ++u) {
+      const int sg = u * PT + ptid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+      *reinterpret_cast<uint4 *>(&sl.Kr[r * CF::LDK + cs * SEG_EL]) = kreg[u];
+      *reinterpret_cast<uint4 *>(&sl.Qr[r * CF::LDK + cs * SEG_EL]) = qreg[u];
+      const bf16 *ke = reinterpret_cast<const bf16 *>(&kreg[u]);
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < SEG_EL; ++e) {
+        const float x = static_cast<float>(ke[e]);
+        part += x * x;
+      }
+      part = group_sum<SEG_ROW>(part);
+      if (cs == 0) sm.kk[r] = part;
+    }
+#pragma unroll
+    for (int u = 0; u < NVSEG; ++u) {
+      const int sg = u * PT + ptid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
+      *reinterpret_cast<uint4 *>(&sl.Vs[r * CF::LDV + cs * SEG_EL]) = vreg[u];
+    }
+    if (pw == 0) {
+      sm.et[l] = ereg;
+      const float g = wave_scan(l < eos - t0 ? log2f(areg) : 0.f);  // alpha = 1 past the end
+      const float glast = __shfl(g, 63, 64);
+      sm.g2[l] = g;
+      sl.gam[l] = exp2f(g);
+      sl.rgam[l] = exp2f(glast - g);
+    }
+  };
+  auto prepare = [&](SL &sl) {  // Gram tiles, diagonal inverses, operand planes
+    if (pw == 0) {
+      sm.beta[l] = sm.et[l] / (sm.kk[l] + eps);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const f32x4 acc = gram_tile<bf16, D>(sl.Kr, sl.Kr, 16 * b, 16 * b, j, c16);
+        const float gS = sm.g2[16 * b + c16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * j + i, R = 16 * b + r;
+          const float val = sm.beta[R] * acc[i] * exp2f(fminf(sm.g2[R] - gS, 0.f));
+          sm.Ld[(b * 16 + c16) * 20 + r] = r > c16 ? val : 0.f;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // lane (block j, column c16): column c16 of (I + L_jj)^{-1}, DPP substitution
+      float lc[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v4 = *reinterpret_cast<const float4 *>(&sm.Ld[(j * 16 + c16) * 20 + 4 * q4]);
+        lc[4 * q4] = v4.x;
+        lc[4 * q4 + 1] = v4.y;
+        lc[4 * q4 + 2] = v4.z;
+        lc[4 * q4 + 3] = v4.w;
+      }
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = (r == c16) ? 1.f : 0.f;
+      solve_steps(x, lc, std::make_integer_sequence<int, 15>{});
+      const float bc = sm.beta[16 * j + c16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) store_split(sl.Yh, sl.Yl, (j * 16 + r) * LDA + c16, x[r] * bc);
+    } else {
+      // producer waves 1, 2, 3 take Gram jobs [0,5), [5,10), [10,16)
+      const int q0 = 5 * (pw - 1);
+      auto job = [&](int qj) {
+        const Job jb = job_of(qj);
+        const f32x4 acc =
+            gram_tile<bf16, D>(jb.qk ? sl.Qr : sl.Kr, sl.Kr, 16 * jb.bi, 16 * jb.bj, j, c16);
+        const float gS = sm.g2[16 * jb.bj + c16];
+        // -Ahat blocks go to the compact block store, M to its full planes
+        const int aq = jb.bi * (jb.bi - 1) / 2 + jb.bj;
+        bf16 *ph = jb.qk ? sl.Mh : sl.Ah;
+        bf16 *pl = jb.qk ? sl.Ml : sl.Al;
+        const float sgn = jb.qk ? 1.f : -1.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * j + i, R = 16 * jb.bi + r, Sc = 16 * jb.bj + c16;
+          const float val = sgn * acc[i] * exp2f(fminf(sm.g2[R] - gS, 0.f));
+          const int idx = jb.qk ? R * CF::LDP + Sc : (aq * 16 + r) * LDA + c16;
+          store_split(ph, pl, idx, R >= Sc ? val : 0.f);
+        }
+      };
+#pragma unroll
+      for (int u = 0; u < 5; ++u) job(q0 + u);
+      if (pw == 3) job(15);
+    }
+  };
+
+  // The two roles run separate loops with the same number of barriers, so
+  // neither role's loop-carried registers are live in the other's code.
+  if (producer) {
+    // prologue: chunk 0 into slot 0
+    fetch(bos);
+    stage(sm.slot[0], bos);
+    fetch(bos + C);
+    lds_barrier();
+    if (bos < eos) prepare(sm.slot[0]);
+    lds_barrier();
+    int cur = 0;
+    for (int64_t tok0 = bos; tok0 < eos; tok0 += C, cur ^= 1) {
+      SL &nx = sm.slot[cur ^ 1];
+      stage(nx, tok0 + C);       // segment A
+      fetch(tok0 + 2 * C);
+      lds_barrier();
+      if (tok0 + C < eos) prepare(nx);  // segment B
+      lds_barrier();
+    }
+    return;
+  }
+
+  // ---- consumers ---------------------------------------------------------
+  f32x4 S[NST];
+  {
+    const rsrc_t rs = make_rsrc(S0 ? S0 + sbase : o, S0 ? (int64_t)D * D * 4 : 0);
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[t][i] = buf_ld4(rs, ((16 * t + 4 * j + i) * D + col) * 4);
+  }
+  lds_barrier();
+  lds_barrier();
+
+  int cur = 0;
+  for (int64_t tok0 = bos; tok0 < eos; tok0 += C, cur ^= 1) {
+    SL &sl = sm.slot[cur];
+
+    // ---- segment A: Q S, K S, R = V - Diag(gamma) K S -----------------------
+    f32x4 QS[4], R[4];
+    {
+      Split8 Sf[NST / 2];
+#pragma unroll
+      for (int kk = 0; kk < NST / 2; ++kk) Sf[kk] = join(split4(S[2 * kk]), split4(S[2 * kk + 1]));
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NST / 2; ++kk) {
+          const bf16x8 a1 = lda_perm(&sl.Qr[(16 * bi + c16) * CF::LDK + 32 * kk], j);
+          const bf16x8 a2 = lda_perm(&sl.Kr[(16 * bi + c16) * CF::LDK + 32 * kk], j);
+          aq = mma(a1, Sf[kk].hi, aq);
+          aq = mma(a1, Sf[kk].lo, aq);
+          ak = mma(a2, Sf[kk].hi, ak);
+          ak = mma(a2, Sf[kk].lo, ak);
+        }
+        QS[bi] = aq;
+        R[bi] = ak;
+      }
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * bi + 4 * j + i;
+          R[bi][i] = static_cast<float>(sl.Vs[r * CF::LDV + 16 * w + c16]) - sl.gam[r] * R[bi][i];
+        }
+    }
+    lds_barrier();
+
+    // ---- segment B: Delta, output, state update -----------------------------
+    {
+      const int n = (int)((eos - tok0) < C ? (eos - tok0) : C);
+      f32x4 Dl[4];
+      Split4 Ds[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        f32x4 acc = R[b];
+#pragma unroll
+        for (int m = 0; m < b; ++m) {
+          const int off = ((b * (b - 1) / 2 + m) * 16 + c16) * LDA + 4 * j;
+          const bf16x4 ah = lda4(&sl.Ah[off]), al = lda4(&sl.Al[off]);
+          acc = mma(ah, Ds[m].hi, acc);
+          acc = mma(ah, Ds[m].lo, acc);
+          acc = mma(al, Ds[m].hi, acc);
+        }
+        const Split4 as = split4(acc);
+        const int yo = (b * 16 + c16) * LDA + 4 * j;
+        const bf16x4 yh = lda4(&sl.Yh[yo]), yl = lda4(&sl.Yl[yo]);
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        d = mma(yh, as.hi, d);
+        d = mma(yh, as.lo, d);
+        d = mma(yl, as.hi, d);
+        Dl[b] = d;
+        Ds[b] = split4(d);
+      }
+      const Split8 Df[2] = {join(Ds[0], Ds[1]), join(Ds[2], Ds[3])};
+      const rsrc_t ro = make_rsrc(o + tok0 * H * (int64_t)D, (int64_t)n * H * D * 4);
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        f32x4 acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = sl.gam[16 * bi + 4 * j + i] * QS[bi][i];
+#pragma unroll
+        for (int kk = 0; kk <= bi / 2; ++kk) {
+          const int off = (16 * bi + c16) * CF::LDP + 32 * kk;
+          const bf16x8 ah = lda_perm(&sl.Mh[off], j), al = lda_perm(&sl.Ml[off], j);
+          acc = mma(ah, Df[kk].hi, acc);
+          acc = mma(ah, Df[kk].lo, acc);
+          acc = mma(al, Df[kk].hi, acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // rows past the end fall outside the descriptor
+          const float val = acc[i];
+          buf_st4(ro, (uint32_t)(((16 * bi + 4 * j + i) * H + h) * D + col) * 4, val);
+        }
+      }
+      // S' = 2^{g2_last} S + K^T Diag(2^{g2_last - g2}) Delta
+      const float glast = sl.gam[C - 1];
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Dl[bi][i] *= sl.rgam[16 * bi + 4 * j + i];
+#pragma unroll
+      for (int t = 0; t < NST; ++t) S[t] *= glast;
+      const Split8 Hf[2] = {join(split4(Dl[0]), split4(Dl[1])), join(split4(Dl[2]), split4(Dl[3]))};
+#pragma unroll
+      for (int t = 0; t < NST; ++t)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16 *base = &sl.Kr[16 * t + 4 * (c16 & 3)];
+          const bf16x4 x0 = ld_tr(base + (32 * kk + 4 * j + (c16 >> 2)) * CF::LDK);
+          const bf16x4 x1 = ld_tr(base + (32 * kk + 16 + 4 * j + (c16 >> 2)) * CF::LDK);
+          const bf16x8 a = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+          S[t] = mma(a, Hf[kk].hi, S[t]);
+          S[t] = mma(a, Hf[kk].lo, S[t]);
+        }
+    }
+    lds_barrier();
+  }
+
+  {
+    const rsrc_t rs = make_rsrc(Sfin ? Sfin + sbase : o, Sfin ? (int64_t)D * D * 4 : 0);
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float val = S[t][i];
+        buf_st4(rs, ((16 * t + 4 * j + i) * D + col) * 4, val);
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_pc(const PrefillArgs &a, hipStream_t st) {
+  const int64_t grid = (int64_t)a.n_seqs * a.H * (D / DVB);
+  hipLaunchKernelGGL((prefill_pc_kernel<D>), dim3((unsigned)grid), dim3(512), 0, st,
+                     static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
+                     static_cast<const bf16 *>(a.v), a.alpha, a.eta, a.cu_seqlens, a.seq_len_dense,
+                     a.H, a.eps, a.initial_state, a.o, a.final_state);
+  return hipGetLastError();
+}
+
 template <typename E, int D>
 hipError_t launch_d(const PrefillArgs &a, hipStream_t st) {
   const int64_t grid = (int64_t)a.n_seqs * a.H * (D / DVB);
@@ -693,7 +1074,7 @@ hipError_t launch_d(const PrefillArgs &a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s) {
-  return a.D == 128 ? launch_d<bf16, 128>(a, s) : launch_d<bf16, 64>(a, s);
+  return a.D == 128 ? launch_pc<128>(a, s) : launch_pc<64>(a, s);
 }
 hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t s) {
   return a.D == 128 ? launch_d<float, 128>(a, s) : launch_d<float, 64>(a, s);
