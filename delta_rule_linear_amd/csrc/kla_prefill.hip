@@ -164,6 +164,16 @@ __device__ inline bf16x4 ld_tr(const bf16 *p) {
 // the next chunk's prefetch at each barrier.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Hardware base-2 exponential and logarithm (v_exp_f32, v_log_f32, about
+// 1 ulp).  Decay factors are 2^x with x <= 0; results below the normal range
+// flush to zero, which is exact to the precision of the outputs.
+__device__ inline float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float flog2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Keep the instruction scheduler from moving code across this point; used to
+// hold software-pipelined LDS loads ahead of the MFMAs that consume them.
+__device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // DPP lane movement within 16-lane rows (gfx9 controls plus row_share).
 template <int CTRL>
 __device__ inline float dpp(float x) {
@@ -708,8 +718,9 @@ struct PSlot {
   alignas(16) bf16 Al[6 * 16 * LDA];
   alignas(16) bf16 Mh[C * CF::LDP];   // M = lower(Q K^T o Gam), zero above the block diagonal
   alignas(16) bf16 Ml[C * CF::LDP];
-  alignas(16) bf16 Yh[4 * 16 * LDA];  // Y_bb = (I + L_bb)^{-1} Diag(beta_b)
-  alignas(16) bf16 Yl[4 * 16 * LDA];
+  static constexpr int LDYT = 24;     // Y^T rows: 16 values + pad, 16-byte aligned
+  alignas(16) bf16 Yh[4 * 16 * LDYT];  // Y_bb^T, Y_bb = (I + L_bb)^{-1} Diag(beta_b)
+  alignas(16) bf16 Yl[4 * 16 * LDYT];
   alignas(16) float gam[C];
   alignas(16) float rgam[C];
 };
@@ -828,11 +839,11 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
     }
     if (pw == 0) {
       sm.et[l] = ereg;
-      const float g = wave_scan(l < eos - t0 ? log2f(areg) : 0.f);  // alpha = 1 past the end
+      const float g = wave_scan(l < eos - t0 ? flog2(areg) : 0.f);  // alpha = 1 past the end
       const float glast = __shfl(g, 63, 64);
       sm.g2[l] = g;
-      sl.gam[l] = exp2f(g);
-      sl.rgam[l] = exp2f(glast - g);
+      sl.gam[l] = fexp2(g);
+      sl.rgam[l] = fexp2(glast - g);
     }
   };
   auto prepare = [&](SL &sl) {  // Gram tiles, diagonal inverses, operand planes
@@ -848,7 +859,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * j + i, R = 16 * b + r;
-          const float val = sm.beta[R] * acc[i] * exp2f(fminf(sm.g2[R] - gS, 0.f));
+          const float val = sm.beta[R] * acc[i] * fexp2(fminf(sm.g2[R] - gS, 0.f));
           sm.Ld[(b * 16 + c16) * 20 + r] = r > c16 ? val : 0.f;
         }
       }
@@ -870,32 +881,75 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       for (int r = 0; r < 16; ++r) x[r] = (r == c16) ? 1.f : 0.f;
       solve_steps(x, lc, std::make_integer_sequence<int, 15>{});
       const float bc = sm.beta[16 * j + c16];
+      // column c16 of Y_jj, contiguous in Y^T: two 16-byte writes per plane
+      bf16x8 yh0, yh1, yl0, yl1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) store_split(sl.Yh, sl.Yl, (j * 16 + r) * LDA + c16, x[r] * bc);
+      for (int r = 0; r < 8; ++r) {
+        const float y0 = x[r] * bc, y1 = x[r + 8] * bc;
+        const bf16 h0 = static_cast<bf16>(y0), h1 = static_cast<bf16>(y1);
+        yh0[r] = h0;
+        yh1[r] = h1;
+        yl0[r] = static_cast<bf16>(y0 - static_cast<float>(h0));
+        yl1[r] = static_cast<bf16>(y1 - static_cast<float>(h1));
+      }
+      const int yo = (j * 16 + c16) * SL::LDYT;
+      *reinterpret_cast<bf16x8 *>(&sl.Yh[yo]) = yh0;
+      *reinterpret_cast<bf16x8 *>(&sl.Yh[yo + 8]) = yh1;
+      *reinterpret_cast<bf16x8 *>(&sl.Yl[yo]) = yl0;
+      *reinterpret_cast<bf16x8 *>(&sl.Yl[yo + 8]) = yl1;
     } else {
-      // producer waves 1, 2, 3 take Gram jobs [0,5), [5,10), [10,16)
+      // producer waves 1, 2, 3 take Gram jobs [0,5), [5,10), [10,16).  Each
+      // tile is computed transposed, C[s][r] = K[s] . (Q or K)[r], so a lane
+      // holds four consecutive s of one row r and writes them as one 8-byte
+      // store per plane.  Operands of the next job are loaded first.
       const int q0 = 5 * (pw - 1);
-      auto job = [&](int qj) {
-        const Job jb = job_of(qj);
-        const f32x4 acc =
-            gram_tile<bf16, D>(jb.qk ? sl.Qr : sl.Kr, sl.Kr, 16 * jb.bi, 16 * jb.bj, j, c16);
-        const float gS = sm.g2[16 * jb.bj + c16];
-        // -Ahat blocks go to the compact block store, M to its full planes
-        const int aq = jb.bi * (jb.bi - 1) / 2 + jb.bj;
-        bf16 *ph = jb.qk ? sl.Mh : sl.Ah;
-        bf16 *pl = jb.qk ? sl.Ml : sl.Al;
-        const float sgn = jb.qk ? 1.f : -1.f;
+      const int nj = pw == 3 ? 6 : 5;
+      bf16x8 opa[2][D / 32], opb[2][D / 32];
+      auto ldjob = [&](int u) {
+        const Job jb = job_of(q0 + u);
+        const bf16 *B = jb.qk ? sl.Qr : sl.Kr;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i, R = 16 * jb.bi + r, Sc = 16 * jb.bj + c16;
-          const float val = sgn * acc[i] * exp2f(fminf(sm.g2[R] - gS, 0.f));
-          const int idx = jb.qk ? R * CF::LDP + Sc : (aq * 16 + r) * LDA + c16;
-          store_split(ph, pl, idx, R >= Sc ? val : 0.f);
+        for (int t = 0; t < D / 32; ++t) {
+          opa[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&sl.Kr[(16 * jb.bj + c16) * CF::LDK + 32 * t + 8 * j]);
+          opb[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&B[(16 * jb.bi + c16) * CF::LDK + 32 * t + 8 * j]);
         }
       };
+      ldjob(0);
 #pragma unroll
-      for (int u = 0; u < 5; ++u) job(q0 + u);
-      if (pw == 3) job(15);
+      for (int u = 0; u < 6; ++u) {
+        if (u < nj) {
+          if (u + 1 < nj) ldjob(u + 1);
+          sched_fence();
+          const Job jb = job_of(q0 + u);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t) acc = mma(opa[u & 1][t], opb[u & 1][t], acc);
+          sched_fence();
+          const int r = 16 * jb.bi + c16;  // this lane's row
+          const float gr = sm.g2[r];
+          const float4 gs = *reinterpret_cast<const float4 *>(&sm.g2[16 * jb.bj + 4 * j]);
+          const float gsv[4] = {gs.x, gs.y, gs.z, gs.w};
+          bf16x4 vh, vl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int sc = 16 * jb.bj + 4 * j + i;
+            float val = acc[i] * fexp2(fminf(gr - gsv[i], 0.f));
+            val = jb.qk ? (r >= sc ? val : 0.f) : -val;
+            const bf16 hv = static_cast<bf16>(val);
+            vh[i] = hv;
+            vl[i] = static_cast<bf16>(val - static_cast<float>(hv));
+          }
+          if (jb.qk) {
+            const int off = r * CF::LDP + 16 * jb.bj + 4 * j;
+            *reinterpret_cast<bf16x4 *>(&sl.Mh[off]) = vh;
+            *reinterpret_cast<bf16x4 *>(&sl.Ml[off]) = vl;
+          } else {
+            const int off = ((jb.bi * (jb.bi - 1) / 2 + jb.bj) * 16 + c16) * LDA + 4 * j;
+            *reinterpret_cast<bf16x4 *>(&sl.Ah[off]) = vh;
+            *reinterpret_cast<bf16x4 *>(&sl.Al[off]) = vl;
+          }
+        }
+      }
     }
   };
 
@@ -940,23 +994,35 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
     // ---- segment A: Q S, K S, R = V - Diag(gamma) K S -----------------------
     f32x4 QS[4], R[4];
     {
-      Split8 Sf[NST / 2];
+      constexpr int NK = NST / 2, NSTEP = 4 * NK;
+      Split8 Sf[NK];
 #pragma unroll
-      for (int kk = 0; kk < NST / 2; ++kk) Sf[kk] = join(split4(S[2 * kk]), split4(S[2 * kk + 1]));
+      for (int kk = 0; kk < NK; ++kk) Sf[kk] = join(split4(S[2 * kk]), split4(S[2 * kk + 1]));
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
-        f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+        QS[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
+        R[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      // steps run kk-major so consecutive MFMAs update different tiles; the
+      // A operands are loaded two steps ahead
+      bf16x8 qa[3], ka[3];
+      auto ld = [&](int st) {
+        const int kk = st / 4, bi = st % 4;
+        qa[st % 3] = lda_perm(&sl.Qr[(16 * bi + c16) * CF::LDK + 32 * kk], j);
+        ka[st % 3] = lda_perm(&sl.Kr[(16 * bi + c16) * CF::LDK + 32 * kk], j);
+      };
+      ld(0);
+      ld(1);
 #pragma unroll
-        for (int kk = 0; kk < NST / 2; ++kk) {
-          const bf16x8 a1 = lda_perm(&sl.Qr[(16 * bi + c16) * CF::LDK + 32 * kk], j);
-          const bf16x8 a2 = lda_perm(&sl.Kr[(16 * bi + c16) * CF::LDK + 32 * kk], j);
-          aq = mma(a1, Sf[kk].hi, aq);
-          aq = mma(a1, Sf[kk].lo, aq);
-          ak = mma(a2, Sf[kk].hi, ak);
-          ak = mma(a2, Sf[kk].lo, ak);
-        }
-        QS[bi] = aq;
-        R[bi] = ak;
+      for (int st = 0; st < NSTEP; ++st) {
+        if (st + 2 < NSTEP) ld(st + 2);
+        sched_fence();
+        const int kk = st / 4, bi = st % 4;
+        QS[bi] = mma(qa[st % 3], Sf[kk].hi, QS[bi]);
+        R[bi] = mma(ka[st % 3], Sf[kk].hi, R[bi]);
+        QS[bi] = mma(qa[st % 3], Sf[kk].lo, QS[bi]);
+        R[bi] = mma(ka[st % 3], Sf[kk].lo, R[bi]);
+        sched_fence();
       }
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
@@ -971,6 +1037,22 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
     // ---- segment B: Delta, output, state update -----------------------------
     {
       const int n = (int)((eos - tok0) < C ? (eos - tok0) : C);
+      // every operand of the substitution up front: the chain is latency-bound
+      bf16x4 yh[4], yl[4], ah[6], al[6];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        // Y[c16][4j..4j+3] from Y^T (row-major, 16 + pad per row) by the
+        // transposing read: lane c addresses row 4j + c/4, columns 4(c%4)..
+        const int yo = (b * 16 + 4 * j + (c16 >> 2)) * SL::LDYT + 4 * (c16 & 3);
+        yh[b] = ld_tr(&sl.Yh[yo]);
+        yl[b] = ld_tr(&sl.Yl[yo]);
+      }
+#pragma unroll
+      for (int qb = 0; qb < 6; ++qb) {
+        const int off = (qb * 16 + c16) * LDA + 4 * j;
+        ah[qb] = lda4(&sl.Ah[off]);
+        al[qb] = lda4(&sl.Al[off]);
+      }
       f32x4 Dl[4];
       Split4 Ds[4];
 #pragma unroll
@@ -978,43 +1060,55 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
         f32x4 acc = R[b];
 #pragma unroll
         for (int m = 0; m < b; ++m) {
-          const int off = ((b * (b - 1) / 2 + m) * 16 + c16) * LDA + 4 * j;
-          const bf16x4 ah = lda4(&sl.Ah[off]), al = lda4(&sl.Al[off]);
-          acc = mma(ah, Ds[m].hi, acc);
-          acc = mma(ah, Ds[m].lo, acc);
-          acc = mma(al, Ds[m].hi, acc);
+          const int qb = b * (b - 1) / 2 + m;
+          acc = mma(ah[qb], Ds[m].hi, acc);
+          acc = mma(ah[qb], Ds[m].lo, acc);
+          acc = mma(al[qb], Ds[m].hi, acc);
         }
         const Split4 as = split4(acc);
-        const int yo = (b * 16 + c16) * LDA + 4 * j;
-        const bf16x4 yh = lda4(&sl.Yh[yo]), yl = lda4(&sl.Yl[yo]);
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
-        d = mma(yh, as.hi, d);
-        d = mma(yh, as.lo, d);
-        d = mma(yl, as.hi, d);
+        d = mma(yh[b], as.hi, d);
+        d = mma(yh[b], as.lo, d);
+        d = mma(yl[b], as.hi, d);
         Dl[b] = d;
         Ds[b] = split4(d);
       }
       const Split8 Df[2] = {join(Ds[0], Ds[1]), join(Ds[2], Ds[3])};
-      const rsrc_t ro = make_rsrc(o + tok0 * H * (int64_t)D, (int64_t)n * H * D * 4);
+      // O = Diag(gamma) Q S + M Delta: steps (kk, bi), bi >= 2 kk, kk-major
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi) {
-        f32x4 acc;
+      for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = sl.gam[16 * bi + 4 * j + i] * QS[bi][i];
-#pragma unroll
-        for (int kk = 0; kk <= bi / 2; ++kk) {
+        for (int i = 0; i < 4; ++i) QS[bi][i] *= sl.gam[16 * bi + 4 * j + i];
+      {
+        constexpr int NSTEP = 6;
+        bf16x8 mh[3], ml[3];
+        auto ld = [&](int st) {
+          const int kk = st < 4 ? 0 : 1, bi = st < 4 ? st : st - 2;
           const int off = (16 * bi + c16) * CF::LDP + 32 * kk;
-          const bf16x8 ah = lda_perm(&sl.Mh[off], j), al = lda_perm(&sl.Ml[off], j);
-          acc = mma(ah, Df[kk].hi, acc);
-          acc = mma(ah, Df[kk].lo, acc);
-          acc = mma(al, Df[kk].hi, acc);
-        }
+          mh[st % 3] = lda_perm(&sl.Mh[off], j);
+          ml[st % 3] = lda_perm(&sl.Ml[off], j);
+        };
+        ld(0);
+        ld(1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {  // rows past the end fall outside the descriptor
-          const float val = acc[i];
-          buf_st4(ro, (uint32_t)(((16 * bi + 4 * j + i) * H + h) * D + col) * 4, val);
+        for (int st = 0; st < NSTEP; ++st) {
+          if (st + 2 < NSTEP) ld(st + 2);
+          sched_fence();
+          const int kk = st < 4 ? 0 : 1, bi = st < 4 ? st : st - 2;
+          QS[bi] = mma(mh[st % 3], Df[kk].hi, QS[bi]);
+          QS[bi] = mma(mh[st % 3], Df[kk].lo, QS[bi]);
+          QS[bi] = mma(ml[st % 3], Df[kk].hi, QS[bi]);
+          sched_fence();
         }
       }
+      const rsrc_t ro = make_rsrc(o + tok0 * H * (int64_t)D, (int64_t)n * H * D * 4);
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // rows past the end fall outside the descriptor
+          const float val = QS[bi][i];
+          buf_st4(ro, (uint32_t)(((16 * bi + 4 * j + i) * H + h) * D + col) * 4, val);
+        }
       // S' = 2^{g2_last} S + K^T Diag(2^{g2_last - g2}) Delta
       const float glast = sl.gam[C - 1];
 #pragma unroll
@@ -1024,17 +1118,29 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
 #pragma unroll
       for (int t = 0; t < NST; ++t) S[t] *= glast;
       const Split8 Hf[2] = {join(split4(Dl[0]), split4(Dl[1])), join(split4(Dl[2]), split4(Dl[3]))};
-#pragma unroll
-      for (int t = 0; t < NST; ++t)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+      {
+        // steps (kk, t), kk-major; K^T operands by transposing reads, two ahead
+        constexpr int NSTEP = 2 * NST;
+        bf16x8 kt[3];
+        auto ld = [&](int st) {
+          const int kk = st / NST, t = st % NST;
           const bf16 *base = &sl.Kr[16 * t + 4 * (c16 & 3)];
           const bf16x4 x0 = ld_tr(base + (32 * kk + 4 * j + (c16 >> 2)) * CF::LDK);
           const bf16x4 x1 = ld_tr(base + (32 * kk + 16 + 4 * j + (c16 >> 2)) * CF::LDK);
-          const bf16x8 a = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-          S[t] = mma(a, Hf[kk].hi, S[t]);
-          S[t] = mma(a, Hf[kk].lo, S[t]);
+          kt[st % 3] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        ld(0);
+        ld(1);
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+          if (st + 2 < NSTEP) ld(st + 2);
+          sched_fence();
+          const int kk = st / NST, t = st % NST;
+          S[t] = mma(kt[st % 3], Hf[kk].hi, S[t]);
+          S[t] = mma(kt[st % 3], Hf[kk].lo, S[t]);
+          sched_fence();
         }
+      }
     }
     lds_barrier();
   }
