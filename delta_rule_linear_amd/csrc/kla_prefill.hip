@@ -91,7 +91,7 @@ struct Smem {
   alignas(16) P Ml[CF::BF ? C * CF::LDP : 8];
   alignas(16) P Yh[4 * 16 * CF::LDY];
   alignas(16) P Yl[CF::BF ? 4 * 16 * CF::LDY : 8];
-  alignas(16) float Ld[4 * 16 * 20];  // Diag(beta) Ahat on the diagonal blocks, [block][col][row]
+  alignas(16) float Ld[4 * 16 * 20];  // -Diag(beta) Ahat below the diagonal of the diagonal blocks, [block][col][row]
   alignas(16) float kk[C];
   alignas(16) float et[C];
   alignas(16) float beta[C];
@@ -189,7 +189,6 @@ constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;       // quad_perm [1,0,3,2], 
 constexpr int kHalfMirror = 0x141, kRowRor4 = 0x124, kRowRor8 = 0x128;
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
-constexpr int kRowShare0 = 0x150;                        // + t: lane t of each row
 
 // Sum over aligned groups of N lanes (N = 8, 16 or 32); every lane gets it.
 template <int N>
@@ -233,6 +232,9 @@ __device__ inline uint4 buf_ld16(rsrc_t r, uint32_t off) {
 }
 __device__ inline float buf_ld4(rsrc_t r, uint32_t off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ inline void buf_st16(rsrc_t r, uint32_t off, f32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)off, 0, 0);
 }
 __device__ inline void buf_st4(rsrc_t r, uint32_t off, float x) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)off, 0, 0);
@@ -301,11 +303,15 @@ __device__ inline f32x4 gram_tile(const E *A, const E *B, int r0, int s0, int j,
 }
 
 // One column step of the 16x16 unit-lower-triangular substitution:
-// x[r] -= L[r][t] x[t] for r > t, with L[r][t] broadcast from lane t.
+// x[r] += (-L[r][t]) x[t] for r > t, one v_fmac_f32_dpp per row whose first
+// factor is broadcast from lane t of the 16-lane row.  lc holds -L and comes
+// straight from LDS, so no VALU write precedes its DPP read.
 template <int T>
 __device__ inline void solve_step(float (&x)[16], const float (&lc)[16]) {
 #pragma unroll
-  for (int r = T + 1; r < 16; ++r) x[r] -= dpp<kRowShare0 + T>(lc[r]) * x[T];
+  for (int r = T + 1; r < 16; ++r)
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(x[r]) : "v"(lc[r]), "v"(x[T]), "n"(T));
 }
 template <int... T>
 __device__ inline void solve_steps(float (&x)[16], const float (&lc)[16],
@@ -453,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // diagonal K K^T tiles -> Diag(beta) Ahat on the diagonal blocks (strictly lower)
+      // diagonal K K^T tiles -> -Diag(beta) Ahat on the diagonal blocks (strictly lower)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const f32x4 acc = gram_tile<E, D>(sm.Kr, sm.Kr, 16 * b, 16 * b, j, c16);
@@ -461,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * j + i, R = 16 * b + r;
-          const float v = sm.beta[R] * acc[i] * exp2f(fminf(sm.g2[R] - gS, 0.f));
+          const float v = -sm.beta[R] * acc[i] * exp2f(fminf(sm.g2[R] - gS, 0.f));
           sm.Ld[(b * 16 + c16) * 20 + r] = r > c16 ? v : 0.f;
         }
       }
@@ -470,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       // lane (block j, column c16): x = (I + L_jj)^{-1} e_c by substitution,
       // column-oriented: once x_t is final it is eliminated from every later
-      // row.  Each lane holds column c16 of L_jj; L[r][t] reaches the whole
+      // row.  Each lane holds column c16 of -L_jj; -L[r][t] reaches the whole
       // row of lanes by a DPP broadcast from lane t.
       {
         float lc[16];
@@ -728,7 +734,7 @@ template <int D>
 struct PSmem {
   PSlot<D> slot[2];
   // producer scratch for the chunk being prepared
-  alignas(16) float Ld[4 * 16 * 20];  // Diag(beta) Ahat on the diagonal blocks, [block][col][row]
+  alignas(16) float Ld[4 * 16 * 20];  // -Diag(beta) Ahat below the diagonal of the diagonal blocks, [block][col][row]
   alignas(16) float kk[C];
   alignas(16) float et[C];
   alignas(16) float beta[C];
@@ -859,8 +865,8 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * j + i, R = 16 * b + r;
-          const float val = sm.beta[R] * acc[i] * fexp2(fminf(sm.g2[R] - gS, 0.f));
-          sm.Ld[(b * 16 + c16) * 20 + r] = r > c16 ? val : 0.f;
+          const float val = -sm.beta[R] * acc[i] * fexp2(fminf(sm.g2[R] - gS, 0.f));
+          sm.Ld[(b * 16 + c16) * 20 + r] = r > c16 ? val : 0.f;  // -L below the diagonal
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1018,9 +1024,12 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
         if (st + 2 < NSTEP) ld(st + 2);
         sched_fence();
         const int kk = st / 4, bi = st % 4;
-        QS[bi] = mma(qa[st % 3], Sf[kk].hi, QS[bi]);
+        // Q S is formed transposed, (Q S)^T = S^T Q^T: the state fragments
+        // serve as the A operand, so the output tile holds four consecutive
+        // dv values of one token per lane (16-byte stores below)
+        QS[bi] = mma(Sf[kk].hi, qa[st % 3], QS[bi]);
         R[bi] = mma(ka[st % 3], Sf[kk].hi, R[bi]);
-        QS[bi] = mma(qa[st % 3], Sf[kk].lo, QS[bi]);
+        QS[bi] = mma(Sf[kk].lo, qa[st % 3], QS[bi]);
         R[bi] = mma(ka[st % 3], Sf[kk].lo, R[bi]);
         sched_fence();
       }
@@ -1076,9 +1085,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       const Split8 Df[2] = {join(Ds[0], Ds[1]), join(Ds[2], Ds[3])};
       // O = Diag(gamma) Q S + M Delta: steps (kk, bi), bi >= 2 kk, kk-major
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) QS[bi][i] *= sl.gam[16 * bi + 4 * j + i];
+      for (int bi = 0; bi < 4; ++bi) QS[bi] *= sl.gam[16 * bi + c16];  // token column c16
       {
         constexpr int NSTEP = 6;
         bf16x8 mh[3], ml[3];
@@ -1095,20 +1102,17 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
           if (st + 2 < NSTEP) ld(st + 2);
           sched_fence();
           const int kk = st < 4 ? 0 : 1, bi = st < 4 ? st : st - 2;
-          QS[bi] = mma(mh[st % 3], Df[kk].hi, QS[bi]);
-          QS[bi] = mma(mh[st % 3], Df[kk].lo, QS[bi]);
-          QS[bi] = mma(ml[st % 3], Df[kk].hi, QS[bi]);
+          // (M Delta)^T = Delta^T M^T, accumulated into the transposed output
+          QS[bi] = mma(Df[kk].hi, mh[st % 3], QS[bi]);
+          QS[bi] = mma(Df[kk].lo, mh[st % 3], QS[bi]);
+          QS[bi] = mma(Df[kk].hi, ml[st % 3], QS[bi]);
           sched_fence();
         }
       }
       const rsrc_t ro = make_rsrc(o + tok0 * H * (int64_t)D, (int64_t)n * H * D * 4);
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {  // rows past the end fall outside the descriptor
-          const float val = QS[bi][i];
-          buf_st4(ro, (uint32_t)(((16 * bi + 4 * j + i) * H + h) * D + col) * 4, val);
-        }
+      for (int bi = 0; bi < 4; ++bi)  // token 16bi + c16, dv 16w + 4j..+3; rows past the end are dropped
+        buf_st16(ro, (uint32_t)(((16 * bi + c16) * H + h) * D + nb * DVB + 16 * w + 4 * j) * 4, QS[bi]);
       // S' = 2^{g2_last} S + K^T Diag(2^{g2_last - g2}) Delta
       const float glast = sl.gam[C - 1];
 #pragma unroll
