@@ -55,6 +55,7 @@ namespace kla {
 namespace {
 
 typedef __bf16 bf16;
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -119,15 +120,29 @@ struct Split8 {
 
 // One accumulator tile as the B operand of a 16-deep MFMA (lane-group j
 // holds contraction rows 4j..4j+3, exactly the tile's own rows), split into
-// hi + lo.
+// hi = bf16(x) (round to nearest even) + lo = bf16(x - hi).  The residual
+// x - hi is exact in fp32; one v_dot2 of the packed hi pair with (-1, 0) or
+// (0, -1) forms it without unpacking hi.
+// The bf16 pairs (-1, 0) and (0, -1) as opaque scalar values: written by an
+// s_mov the compiler cannot see through, so it never folds them into an
+// inline constant (the inline constant -1.0 reads as the f32 bit pattern,
+// i.e. the pair (0, -1), for packed bf16 operands).
+__device__ inline bf16x2 sgpr_pair(uint32_t bits) {
+  uint32_t r;
+  asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(bits));
+  return __builtin_bit_cast(bf16x2, r);
+}
 __device__ inline Split4 split4(f32x4 c) {
+  const bf16x2 m0 = sgpr_pair(0x0000BF80u), m1 = sgpr_pair(0xBF800000u);
+  const bf16x2 h01 = __builtin_convertvector(__builtin_shufflevector(c, c, 0, 1), bf16x2);
+  const bf16x2 h23 = __builtin_convertvector(__builtin_shufflevector(c, c, 2, 3), bf16x2);
+  const f32x4 res = {__builtin_amdgcn_fdot2_f32_bf16(h01, m0, c[0], false),
+                     __builtin_amdgcn_fdot2_f32_bf16(h01, m1, c[1], false),
+                     __builtin_amdgcn_fdot2_f32_bf16(h23, m0, c[2], false),
+                     __builtin_amdgcn_fdot2_f32_bf16(h23, m1, c[3], false)};
   Split4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16 h = static_cast<bf16>(c[i]);
-    r.hi[i] = h;
-    r.lo[i] = static_cast<bf16>(c[i] - static_cast<float>(h));
-  }
+  r.hi = __builtin_shufflevector(h01, h23, 0, 1, 2, 3);
+  r.lo = __builtin_convertvector(res, bf16x4);
   return r;
 }
 // Two tiles covering contraction rows [0,16) and [16,32) as the B operand of
@@ -888,16 +903,14 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       solve_steps(x, lc, std::make_integer_sequence<int, 15>{});
       const float bc = sm.beta[16 * j + c16];
       // column c16 of Y_jj, contiguous in Y^T: two 16-byte writes per plane
-      bf16x8 yh0, yh1, yl0, yl1;
+      Split4 yq[4];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float y0 = x[r] * bc, y1 = x[r + 8] * bc;
-        const bf16 h0 = static_cast<bf16>(y0), h1 = static_cast<bf16>(y1);
-        yh0[r] = h0;
-        yh1[r] = h1;
-        yl0[r] = static_cast<bf16>(y0 - static_cast<float>(h0));
-        yl1[r] = static_cast<bf16>(y1 - static_cast<float>(h1));
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+        yq[q4] = split4(f32x4{x[4 * q4] * bc, x[4 * q4 + 1] * bc, x[4 * q4 + 2] * bc, x[4 * q4 + 3] * bc});
+      const bf16x8 yh0 = __builtin_shufflevector(yq[0].hi, yq[1].hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 yh1 = __builtin_shufflevector(yq[2].hi, yq[3].hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 yl0 = __builtin_shufflevector(yq[0].lo, yq[1].lo, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 yl1 = __builtin_shufflevector(yq[2].lo, yq[3].lo, 0, 1, 2, 3, 4, 5, 6, 7);
       const int yo = (j * 16 + c16) * SL::LDYT;
       *reinterpret_cast<bf16x8 *>(&sl.Yh[yo]) = yh0;
       *reinterpret_cast<bf16x8 *>(&sl.Yh[yo + 8]) = yh1;
@@ -935,24 +948,22 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
           const float gr = sm.g2[r];
           const float4 gs = *reinterpret_cast<const float4 *>(&sm.g2[16 * jb.bj + 4 * j]);
           const float gsv[4] = {gs.x, gs.y, gs.z, gs.w};
-          bf16x4 vh, vl;
+          f32x4 vals;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int sc = 16 * jb.bj + 4 * j + i;
-            float val = acc[i] * fexp2(fminf(gr - gsv[i], 0.f));
-            val = jb.qk ? (r >= sc ? val : 0.f) : -val;
-            const bf16 hv = static_cast<bf16>(val);
-            vh[i] = hv;
-            vl[i] = static_cast<bf16>(val - static_cast<float>(hv));
+            const float val = acc[i] * fexp2(fminf(gr - gsv[i], 0.f));
+            vals[i] = jb.qk ? (r >= sc ? val : 0.f) : -val;
           }
+          const Split4 sp = split4(vals);
           if (jb.qk) {
             const int off = r * CF::LDP + 16 * jb.bj + 4 * j;
-            *reinterpret_cast<bf16x4 *>(&sl.Mh[off]) = vh;
-            *reinterpret_cast<bf16x4 *>(&sl.Ml[off]) = vl;
+            *reinterpret_cast<bf16x4 *>(&sl.Mh[off]) = sp.hi;
+            *reinterpret_cast<bf16x4 *>(&sl.Ml[off]) = sp.lo;
           } else {
             const int off = ((jb.bi * (jb.bi - 1) / 2 + jb.bj) * 16 + c16) * LDA + 4 * j;
-            *reinterpret_cast<bf16x4 *>(&sl.Ah[off]) = vh;
-            *reinterpret_cast<bf16x4 *>(&sl.Al[off]) = vl;
+            *reinterpret_cast<bf16x4 *>(&sl.Ah[off]) = sp.hi;
+            *reinterpret_cast<bf16x4 *>(&sl.Al[off]) = sp.lo;
           }
         }
       }
