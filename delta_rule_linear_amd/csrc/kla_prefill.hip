@@ -843,15 +843,6 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       const int sg = u * PT + ptid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
       *reinterpret_cast<uint4 *>(&sl.Kr[r * CF::LDK + cs * SEG_EL]) = kreg[u];
       *reinterpret_cast<uint4 *>(&sl.Qr[r * CF::LDK + cs * SEG_EL]) = qreg[u];
-      const bf16 *ke = reinterpret_cast<const bf16 *>(&kreg[u]);
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < SEG_EL; ++e) {
-        const float x = static_cast<float>(ke[e]);
-        part += x * x;
-      }
-      part = group_sum<SEG_ROW>(part);
-      if (cs == 0) sm.kk[r] = part;
     }
 #pragma unroll
     for (int u = 0; u < NVSEG; ++u) {
@@ -867,26 +858,47 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       sl.rgam[l] = fexp2(glast - g);
     }
   };
+  auto wave_sync = [&]() {  // order this wave's LDS writes before its reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
   auto prepare = [&](SL &sl) {  // Gram tiles, diagonal inverses, operand planes
     if (pw == 0) {
+      f32x4 dg[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) dg[b] = gram_tile<bf16, D>(sl.Kr, sl.Kr, 16 * b, 16 * b, j, c16);
+      // |k_r|^2 is the diagonal: row 16b + c16 sits in lane (c16 / 4, c16), element c16 % 4
+      if ((c16 >> 2) == j) {
+        const int e = c16 & 3;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          sm.kk[16 * b + c16] = e == 0 ? dg[b][0] : e == 1 ? dg[b][1] : e == 2 ? dg[b][2] : dg[b][3];
+      }
+      wave_sync();
       sm.beta[l] = sm.et[l] / (sm.kk[l] + eps);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_sync();
+      // every gate and beta this lane needs first, then the 16 values, then
+      // one 16-byte write per block (rows 4j..4j+3 of column c16)
+      f32x4 gr[4], br[4];
+      float gc[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const f32x4 acc = gram_tile<bf16, D>(sl.Kr, sl.Kr, 16 * b, 16 * b, j, c16);
-        const float gS = sm.g2[16 * b + c16];
+        gr[b] = *reinterpret_cast<const f32x4 *>(&sm.g2[16 * b + 4 * j]);
+        br[b] = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * b + 4 * j]);
+        gc[b] = sm.g2[16 * b + c16];
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        f32x4 val;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i, R = 16 * b + r;
-          const float val = -sm.beta[R] * acc[i] * fexp2(fminf(sm.g2[R] - gS, 0.f));
-          sm.Ld[(b * 16 + c16) * 20 + r] = r > c16 ? val : 0.f;  // -L below the diagonal
+          const float x = -br[b][i] * dg[b][i] * fexp2(fminf(gr[b][i] - gc[b], 0.f));
+          val[i] = 4 * j + i > c16 ? x : 0.f;  // -L below the diagonal
         }
+        *reinterpret_cast<f32x4 *>(&sm.Ld[(b * 16 + c16) * 20 + 4 * j]) = val;
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_sync();
       // lane (block j, column c16): column c16 of (I + L_jj)^{-1}, DPP substitution
       float lc[16];
 #pragma unroll
