@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_MFMA_PEAK_TF = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 
-PREFILL_KERNEL = "prefill_kernel"
+PREFILL_KERNEL = "prefill_pc_kernel"  # the bf16 prefill kernel (producer/consumer waves)
 DECODE_KERNEL = "decode_kernel"
 KERNEL_SOURCES = {PREFILL_KERNEL: "delta_rule_linear_amd/csrc/kla_prefill.hip",
                   DECODE_KERNEL: "delta_rule_linear_amd/csrc/kla_decode.hip"}
@@ -107,20 +107,22 @@ def prefill_work(n_seqs, T, H, d, C=64):
 
 
 def time_launches(fn, n, stream):
-    """Run fn n times on `stream`, bracketing every launch with HIP events.
-    Returns (wall seconds for the n launches, mean event ms per launch)."""
+    """Run fn n times back to back on `stream`, with one pair of HIP events
+    around the whole run on that stream.  Returns (wall seconds for the n
+    launches, event ms per launch).  One launch is one kernel, so the event
+    figure is the kernel's average launch duration (the launches queue up
+    faster than they run, so no host gaps fall between them)."""
     import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
+    a.record(stream)
+    for _ in range(n):
         fn()
-        b.record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, sum(a.elapsed_time(b) for a, b in ev) / n
+    return wall, a.elapsed_time(b) / n
 
 
 def bench_prefill(args, torch, kla, workloads):
@@ -205,8 +207,10 @@ def calibrate_copy(torch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The GPU takes some tens of milliseconds of sustained work to reach its
+    # steady clock; 200 warm-up launches (about 30 ms) cover that.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
