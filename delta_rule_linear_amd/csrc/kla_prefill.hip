@@ -928,17 +928,23 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       *reinterpret_cast<bf16x8 *>(&sl.Yh[yo + 8]) = yh1;
       *reinterpret_cast<bf16x8 *>(&sl.Yl[yo]) = yl0;
       *reinterpret_cast<bf16x8 *>(&sl.Yl[yo + 8]) = yl1;
-    } else {
-      // producer waves 1, 2, 3 take Gram jobs [0,5), [5,10), [10,16).  Each
-      // tile is computed transposed, C[s][r] = K[s] . (Q or K)[r], so a lane
-      // holds four consecutive s of one row r and writes them as one 8-byte
-      // store per plane.  Operands of the next job are loaded first.
-      const int q0 = 5 * (pw - 1);
-      const int nj = pw == 3 ? 6 : 5;
+    }
+    {
+      // producer waves 1, 2, 3 take Gram jobs [0,5), [5,10), [10,15) and
+      // wave 0 job 15 after its solve.  Each tile is computed transposed,
+      // C[s][r] = K[s] . (Q or K)[r], so a lane holds four consecutive s of
+      // one row r and writes them as one 8-byte store per plane.  Operands
+      // of the next job are loaded first.
+      const int q0 = pw == 0 ? 15 : 5 * (pw - 1);
+      const int nj = pw == 0 ? 1 : 5;
       bf16x8 opa[2][D / 32], opb[2][D / 32];
-      auto ldjob = [&](int u) {
+      float grb[2];
+      f32x4 gsb[2];
+      auto ldjob = [&](int u) {  // operands and gates of job u
         const Job jb = job_of(q0 + u);
         const bf16 *B = jb.qk ? sl.Qr : sl.Kr;
+        grb[u & 1] = sm.g2[16 * jb.bi + c16];
+        gsb[u & 1] = *reinterpret_cast<const f32x4 *>(&sm.g2[16 * jb.bj + 4 * j]);
 #pragma unroll
         for (int t = 0; t < D / 32; ++t) {
           opa[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&sl.Kr[(16 * jb.bj + c16) * CF::LDK + 32 * t + 8 * j]);
@@ -957,9 +963,8 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
           for (int t = 0; t < D / 32; ++t) acc = mma(opa[u & 1][t], opb[u & 1][t], acc);
           sched_fence();
           const int r = 16 * jb.bi + c16;  // this lane's row
-          const float gr = sm.g2[r];
-          const float4 gs = *reinterpret_cast<const float4 *>(&sm.g2[16 * jb.bj + 4 * j]);
-          const float gsv[4] = {gs.x, gs.y, gs.z, gs.w};
+          const float gr = grb[u & 1];
+          const f32x4 gsv = gsb[u & 1];
           f32x4 vals;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
