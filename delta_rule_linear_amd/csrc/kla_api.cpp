@@ -47,14 +47,15 @@ size_t kla_fwd_chunked_workspace_size(int32_t, int64_t, int32_t, int32_t, int32_
   return 0;
 }
 
-kla_status kla_fwd_chunked(const void *q, const void *k, const void *v, const float *alpha,
-                           const float *eta, const int32_t *cu_seqlens, int32_t n_seqs,
-                           int64_t total_tok, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
-                           float eps, kla_dtype dtype, const float *initial_state, float *o,
-                           float *final_state, void *workspace, size_t workspace_bytes,
-                           void *stream) {
+kla_status kla_fwd_chunked_ex(const void *q, const void *k, const void *v, const float *alpha,
+                              const float *eta, const int32_t *cu_seqlens, int32_t n_seqs,
+                              int64_t total_tok, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                              float eps, kla_dtype dtype, kla_beta_mode beta_mode,
+                              const float *initial_state, float *o, float *final_state,
+                              void *workspace, size_t workspace_bytes, void *stream) {
   if (n_seqs <= 0 || H <= 0 || total_tok < 0 || !std::isfinite(eps) || eps < 0.f)
     return KLA_ERR_INVALID_ARG;
+  if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT) return KLA_ERR_INVALID_ARG;
   if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
   if (!supported_dim(dk, dv) || chunk != 64) return KLA_ERR_UNSUPPORTED;
   if (!cu_seqlens && total_tok % n_seqs != 0) return KLA_ERR_INVALID_ARG;
@@ -62,7 +63,7 @@ kla_status kla_fwd_chunked(const void *q, const void *k, const void *v, const fl
     return KLA_ERR_WORKSPACE;
   (void)workspace;
   const bool have_tokens = total_tok > 0;
-  if (have_tokens && (!q || !k || !v || !alpha || !eta || !o)) return KLA_ERR_INVALID_ARG;
+  if (have_tokens && (!q || !k || !v || !eta || !o)) return KLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       !aligned16(initial_state) || !aligned16(final_state))
     return KLA_ERR_INVALID_ARG;
@@ -70,7 +71,7 @@ kla_status kla_fwd_chunked(const void *q, const void *k, const void *v, const fl
   const int64_t esz = dtype == KLA_BF16 ? 2 : 4;
   const int64_t th = total_tok * H;
   const Range rq = range(q, th * dk * esz), rk = range(k, th * dk * esz),
-              rv = range(v, th * dv * esz), ra = range(alpha, th * 4), re = range(eta, th * 4),
+              rv = range(v, th * dv * esz), ra = range(alpha, alpha ? th * 4 : 0), re = range(eta, th * 4),
               ro = range(o, th * dv * 4),
               rcu = range(cu_seqlens, cu_seqlens ? (int64_t)(n_seqs + 1) * 4 : 0),
               rs0 = range(initial_state, initial_state ? (int64_t)n_seqs * H * dk * dv * 4 : 0),
@@ -96,6 +97,7 @@ kla_status kla_fwd_chunked(const void *q, const void *k, const void *v, const fl
   a.H = H;
   a.D = dk;
   a.eps = eps;
+  a.beta_direct = beta_mode == KLA_BETA_DIRECT;
   a.initial_state = initial_state;
   a.o = o;
   a.final_state = final_state;
@@ -105,19 +107,32 @@ kla_status kla_fwd_chunked(const void *q, const void *k, const void *v, const fl
   return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
 }
 
-kla_status kla_decode_step(const void *q, const void *k, const void *v, const float *alpha,
-                           const float *eta, float *state, float *o, int32_t n_seqs, int32_t H,
-                           int32_t dk, int32_t dv, float eps, kla_dtype dtype, void *stream) {
+kla_status kla_fwd_chunked(const void *q, const void *k, const void *v, const float *alpha,
+                           const float *eta, const int32_t *cu_seqlens, int32_t n_seqs,
+                           int64_t total_tok, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                           float eps, kla_dtype dtype, const float *initial_state, float *o,
+                           float *final_state, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+  return kla_fwd_chunked_ex(q, k, v, alpha, eta, cu_seqlens, n_seqs, total_tok, H, dk, dv, chunk,
+                            eps, dtype, KLA_BETA_KACZMARZ, initial_state, o, final_state,
+                            workspace, workspace_bytes, stream);
+}
+
+kla_status kla_decode_step_ex(const void *q, const void *k, const void *v, const float *alpha,
+                              const float *eta, float *state, float *o, int32_t n_seqs, int32_t H,
+                              int32_t dk, int32_t dv, float eps, kla_dtype dtype,
+                              kla_beta_mode beta_mode, void *stream) {
   if (n_seqs <= 0 || H <= 0 || !std::isfinite(eps) || eps < 0.f) return KLA_ERR_INVALID_ARG;
+  if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT) return KLA_ERR_INVALID_ARG;
   if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
   if (!supported_dim(dk, dv)) return KLA_ERR_UNSUPPORTED;
-  if (!q || !k || !v || !alpha || !eta || !state || !o) return KLA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !eta || !state || !o) return KLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o))
     return KLA_ERR_INVALID_ARG;
   const int64_t esz = dtype == KLA_BF16 ? 2 : 4;
   const int64_t nh = (int64_t)n_seqs * H;
   const Range rq = range(q, nh * dk * esz), rk = range(k, nh * dk * esz),
-              rv = range(v, nh * dv * esz), ra = range(alpha, nh * 4), re = range(eta, nh * 4),
+              rv = range(v, nh * dv * esz), ra = range(alpha, alpha ? nh * 4 : 0), re = range(eta, nh * 4),
               rs = range(state, nh * dk * dv * 4), ro = range(o, nh * dv * 4);
   for (const Range &in : {rq, rk, rv, ra, re, rs})
     if (overlap(ro, in)) return KLA_ERR_INVALID_ARG;
@@ -136,10 +151,18 @@ kla_status kla_decode_step(const void *q, const void *k, const void *v, const fl
   a.H = H;
   a.D = dk;
   a.eps = eps;
+  a.beta_direct = beta_mode == KLA_BETA_DIRECT;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e =
       dtype == KLA_BF16 ? kla::launch_decode_bf16(a, st) : kla::launch_decode_f32(a, st);
   return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
+}
+
+kla_status kla_decode_step(const void *q, const void *k, const void *v, const float *alpha,
+                           const float *eta, float *state, float *o, int32_t n_seqs, int32_t H,
+                           int32_t dk, int32_t dv, float eps, kla_dtype dtype, void *stream) {
+  return kla_decode_step_ex(q, k, v, alpha, eta, state, o, n_seqs, H, dk, dv, eps, dtype,
+                            KLA_BETA_KACZMARZ, stream);
 }
 
 }  // extern "C"

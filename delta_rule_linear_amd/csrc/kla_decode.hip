@@ -8,6 +8,10 @@
 //   beta = eta / (k.k + eps),  e = v - alpha x
 //   o = alpha y + beta (k.q) e            (= S_new^T q)
 //   S_new = alpha S + beta k e^T
+// With beta_direct the step is beta = eta, the learned scalar of Gated
+// DeltaNet that KLA replaces (same summary, introduction); without alpha the
+// decay is 1 (DeltaNet, "Linear Attention Architectures: Mechanisms,
+// Trade-offs, and Cross-Layer Routing", section "Notacao Unificada").
 // The kernel is bound by HBM bandwidth (0.75 flop/byte): one workgroup per
 // (sequence, head), each thread holds RPT rows x 4 columns of the state in
 // registers between the read and the write.
@@ -28,7 +32,7 @@ template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ eta, float *__restrict__ state,
-    float *__restrict__ o, float eps) {
+    float *__restrict__ o, float eps, int beta_direct) {
   constexpr int NQ = D / 4;              // float4 column groups per row
   constexpr int NRG = kThreads / NQ;     // row groups
   constexpr int RPT = D / NRG;           // rows per thread
@@ -53,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     sk[t] = to_f32(k[sh * D + t]);
     sv[t] = to_f32(v[sh * D + t]);
   }
-  const float a = alpha[sh];
+  const float a = alpha ? alpha[sh] : 1.f;
   const float et = eta[sh];
   __syncthreads();
 
@@ -72,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
       kq += __shfl_xor(kq, off, 64);
     }
   }
-  const float beta = et / (kk + eps);
+  const float beta = beta_direct ? et : et / (kk + eps);
 
   float4 xs = {0.f, 0.f, 0.f, 0.f}, ys = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -118,10 +122,10 @@ hipError_t launch(const DecodeArgs &a, hipStream_t st) {
           *v = static_cast<const E *>(a.v);
   if (a.D == 128)
     hipLaunchKernelGGL((decode_kernel<E, 128>), grid, block, 0, st, q, k, v, a.alpha, a.eta,
-                       a.state, a.o, a.eps);
+                       a.state, a.o, a.eps, a.beta_direct);
   else
     hipLaunchKernelGGL((decode_kernel<E, 64>), grid, block, 0, st, q, k, v, a.alpha, a.eta,
-                       a.state, a.o, a.eps);
+                       a.state, a.o, a.eps, a.beta_direct);
   return hipGetLastError();
 }
 

@@ -8,12 +8,13 @@ namespace kla {
 
 struct PrefillArgs {
   const void *q, *k, *v;
-  const float *alpha, *eta;
+  const float *alpha, *eta;   // alpha nullable (alpha = 1)
   const int32_t *cu_seqlens;  // device, or nullptr for dense
   int32_t n_seqs;
   int64_t seq_len_dense;      // tokens per sequence when cu_seqlens == nullptr
   int32_t H, D;               // D = dk = dv
   float eps;
+  int beta_direct;            // 1: beta = eta; 0: beta = eta / (|k|^2 + eps)
   const float *initial_state; // nullable
   float *o;
   float *final_state;         // nullable
@@ -21,10 +22,11 @@ struct PrefillArgs {
 
 struct DecodeArgs {
   const void *q, *k, *v;
-  const float *alpha, *eta;
+  const float *alpha, *eta;   // alpha nullable (alpha = 1)
   float *state, *o;
   int32_t n_seqs, H, D;
   float eps;
+  int beta_direct;            // 1: beta = eta; 0: beta = eta / (|k|^2 + eps)
 };
 
 // Each returns the HIP status of the launch.

@@ -5,7 +5,11 @@
 // DeltaNet's chunk-parallel algorithm and changes only the diagonal
 // coefficient matrix B = Diag(beta) of the chunk solver (section
 // "Implementacao"), with beta_t = eta_t / (|k_t|^2 + eps) (section
-// "A Regra de Atualizacao KLA").  For a chunk of n <= 64 tokens with
+// "A Regra de Atualizacao KLA").  With beta_direct the step is beta_t =
+// eta_t, the learned scalar of Gated DeltaNet that KLA replaces (same
+// summary, introduction); without alpha the decay is 1 (DeltaNet, "Linear
+// Attention Architectures: Mechanisms, Trade-offs, and Cross-Layer Routing",
+// section "Notacao Unificada").  For a chunk of n <= 64 tokens with
 // chunk-start state S (dk x dv), g_r = sum_{i<=r} log alpha_i:
 //
 //   L     = strictly-lower( Diag(beta) (K K^T o Gam) ),  Gam_rs = e^{g_r-g_s}
@@ -338,7 +342,7 @@ template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ eta,
-    const int32_t *__restrict__ cu_seqlens, int64_t seq_len_dense, int H, float eps,
+    const int32_t *__restrict__ cu_seqlens, int64_t seq_len_dense, int H, float eps, int beta_direct,
     const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ Sfin) {
   using CF = Cfg<E, D>;
   using P = typename CF::P;
@@ -417,7 +421,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + nb * DVB + cs * SEG_EL) * sizeof(E));
     }
     if (w == 0) {
-      const rsrc_t ra = make_rsrc(alpha + t0 * H, nn * H * 4);
+      // no alpha: an empty range (the scan then takes log alpha = 0)
+      const rsrc_t ra = make_rsrc(alpha ? alpha + t0 * H : eta, alpha ? nn * H * 4 : 0);
       const rsrc_t re = make_rsrc(eta + t0 * H, nn * H * 4);
       areg = buf_ld4(ra, (uint32_t)(l * H + h) * 4);  // zero past the end
       ereg = buf_ld4(re, (uint32_t)(l * H + h) * 4);
@@ -450,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     if (w == 0) {
       // cumulative log2-decay over the chunk (rows past the end: alpha = 1, eta = 0)
       sm.et[l] = ereg;
-      const float g = wave_scan(l < eos - t0 ? log2f(areg) : 0.f);  // alpha = 1 past the end
+      const float g = wave_scan(alpha && l < eos - t0 ? log2f(areg) : 0.f);  // alpha = 1 past the end
       const float glast = __shfl(g, 63, 64);
       sm.g2[l] = g;
       sm.gam[l] = exp2f(g);
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 
     // ---- 2. Gram tiles, diagonal block inverses, Q S, K S, R --------------
     if (w == 0) {
-      const float b_l = sm.et[l] / (sm.kk[l] + eps);
+      const float b_l = beta_direct ? sm.et[l] : sm.et[l] / (sm.kk[l] + eps);
       sm.beta[l] = b_l;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -760,7 +765,7 @@ template <int D>
 __global__ __launch_bounds__(512) void prefill_pc_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ eta,
-    const int32_t *__restrict__ cu_seqlens, int64_t seq_len_dense, int H, float eps,
+    const int32_t *__restrict__ cu_seqlens, int64_t seq_len_dense, int H, float eps, int beta_direct,
     const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ Sfin) {
   using CF = Cfg<bf16, D>;
   using SL = PSlot<D>;
@@ -831,7 +836,8 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + nb * DVB + cs * SEG_EL) * 2);
     }
     if (pw == 0) {
-      const rsrc_t ra = make_rsrc(alpha + t0 * H, nn * H * 4);
+      // no alpha: an empty range (the scan then takes log alpha = 0)
+      const rsrc_t ra = make_rsrc(alpha ? alpha + t0 * H : eta, alpha ? nn * H * 4 : 0);
       const rsrc_t re = make_rsrc(eta + t0 * H, nn * H * 4);
       areg = buf_ld4(ra, (uint32_t)(l * H + h) * 4);  // zero past the end
       ereg = buf_ld4(re, (uint32_t)(l * H + h) * 4);
@@ -851,7 +857,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
     }
     if (pw == 0) {
       sm.et[l] = ereg;
-      const float g = wave_scan(l < eos - t0 ? flog2(areg) : 0.f);  // alpha = 1 past the end
+      const float g = wave_scan(alpha && l < eos - t0 ? flog2(areg) : 0.f);  // alpha = 1 past the end
       const float glast = __shfl(g, 63, 64);
       sm.g2[l] = g;
       sl.gam[l] = fexp2(g);
@@ -876,7 +882,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
           sm.kk[16 * b + c16] = e == 0 ? dg[b][0] : e == 1 ? dg[b][1] : e == 2 ? dg[b][2] : dg[b][3];
       }
       wave_sync();
-      sm.beta[l] = sm.et[l] / (sm.kk[l] + eps);
+      sm.beta[l] = beta_direct ? sm.et[l] : sm.et[l] / (sm.kk[l] + eps);
       wave_sync();
       // every gate and beta this lane needs first, then the 16 values, then
       // one 16-byte write per block (rows 4j..4j+3 of column c16)
@@ -1195,7 +1201,7 @@ hipError_t launch_pc(const PrefillArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((prefill_pc_kernel<D>), dim3((unsigned)grid), dim3(512), 0, st,
                      static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
                      static_cast<const bf16 *>(a.v), a.alpha, a.eta, a.cu_seqlens, a.seq_len_dense,
-                     a.H, a.eps, a.initial_state, a.o, a.final_state);
+                     a.H, a.eps, a.beta_direct, a.initial_state, a.o, a.final_state);
   return hipGetLastError();
 }
 
@@ -1205,7 +1211,7 @@ hipError_t launch_d(const PrefillArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((prefill_kernel<E, D>), dim3((unsigned)grid), dim3(kThreads), 0, st,
                      static_cast<const E *>(a.q), static_cast<const E *>(a.k),
                      static_cast<const E *>(a.v), a.alpha, a.eta, a.cu_seqlens, a.seq_len_dense,
-                     a.H, a.eps, a.initial_state, a.o, a.final_state);
+                     a.H, a.eps, a.beta_direct, a.initial_state, a.o, a.final_state);
   return hipGetLastError();
 }
 

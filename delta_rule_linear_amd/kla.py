@@ -18,6 +18,8 @@ _lib = ctypes.CDLL(lib_path)
 
 KLA_OK, KLA_ERR_INVALID_ARG, KLA_ERR_UNSUPPORTED, KLA_ERR_WORKSPACE, KLA_ERR_HIP = 0, -1, -2, -3, -4
 KLA_F32, KLA_BF16 = 0, 1
+KLA_BETA_KACZMARZ, KLA_BETA_DIRECT = 0, 1
+_BETA_MODES = {"kaczmarz": KLA_BETA_KACZMARZ, "direct": KLA_BETA_DIRECT}
 
 _vp, _fp, _i32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
 _lib.kla_fwd_chunked_workspace_size.restype = ctypes.c_size_t
@@ -28,9 +30,14 @@ _lib.kla_fwd_chunked.argtypes = [_vp, _vp, _vp, _fp, _fp, _i32p, ctypes.c_int32,
                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_float, ctypes.c_int, _fp, _fp, _fp, _vp, ctypes.c_size_t,
                                  _vp]
+_lib.kla_fwd_chunked_ex.restype = ctypes.c_int
+_lib.kla_fwd_chunked_ex.argtypes = (_lib.kla_fwd_chunked.argtypes[:14] + [ctypes.c_int]
+                                    + _lib.kla_fwd_chunked.argtypes[14:])
 _lib.kla_decode_step.restype = ctypes.c_int
 _lib.kla_decode_step.argtypes = [_vp, _vp, _vp, _fp, _fp, _fp, _fp, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int, _vp]
+_lib.kla_decode_step_ex.restype = ctypes.c_int
+_lib.kla_decode_step_ex.argtypes = _lib.kla_decode_step.argtypes[:13] + [ctypes.c_int, _vp]
 _lib.kla_status_string.restype = ctypes.c_char_p
 _lib.kla_status_string.argtypes = [ctypes.c_int]
 _lib.kla_version.restype = ctypes.c_char_p
@@ -82,18 +89,43 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _beta_code(beta_mode):
+    try:
+        return _BETA_MODES[beta_mode]
+    except KeyError:
+        raise ValueError(f"beta_mode must be one of {sorted(_BETA_MODES)}, got {beta_mode!r}")
+
+
 def kla_fwd_chunked(q, k, v, alpha, eta, cu_seqlens=None, initial_state=None, eps=1e-6, chunk=64,
                     output_final_state=False, o=None, final_state=None, workspace=None,
                     stream=None):
     """Chunked KLA prefill (C ABI `kla_fwd_chunked`).
 
     q, k: [tok, H, dk] (packed, with cu_seqlens int32 [n+1]) or [B, T, H, dk]
-    (dense); v likewise with dv.  alpha, eta: [tok, H] or [B, T, H] fp32.
+    (dense); v likewise with dv.  alpha, eta: [tok, H] or [B, T, H] fp32;
+    alpha may be None (no decay).
     Returns (o fp32 shaped like v, final_state [n, H, dk, dv] fp32 or None).
     """
+    return _fwd(None, q, k, v, alpha, eta, cu_seqlens, initial_state, eps, chunk,
+                output_final_state, o, final_state, workspace, stream)
+
+
+def kla_fwd_chunked_ex(q, k, v, alpha, eta, cu_seqlens=None, initial_state=None, eps=1e-6,
+                       chunk=64, beta_mode="kaczmarz", output_final_state=False, o=None,
+                       final_state=None, workspace=None, stream=None):
+    """kla_fwd_chunked with the step-size rule chosen by beta_mode (C ABI
+    `kla_fwd_chunked_ex`): "kaczmarz" (beta = eta / (|k|^2 + eps)) or
+    "direct" (beta = eta, Gated DeltaNet; DeltaNet with alpha None)."""
+    return _fwd(_beta_code(beta_mode), q, k, v, alpha, eta, cu_seqlens, initial_state, eps, chunk,
+                output_final_state, o, final_state, workspace, stream)
+
+
+def _fwd(beta, q, k, v, alpha, eta, cu_seqlens, initial_state, eps, chunk, output_final_state, o,
+         final_state, workspace, stream):
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
-    _need(alpha, "alpha", torch.float32)
+    if alpha is not None:
+        _need(alpha, "alpha", torch.float32)
     _need(eta, "eta", torch.float32)
     dk, dv, H = q.shape[-1], v.shape[-1], q.shape[-2]
     if cu_seqlens is not None:
@@ -124,10 +156,13 @@ def kla_fwd_chunked(q, k, v, alpha, eta, cu_seqlens=None, initial_state=None, ep
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = _ptr(workspace)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _lib.kla_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(cu_seqlens),
-                              n_seqs, total, H, dk, dv, chunk, float(eps), _dtype_code(q),
-                              _ptr(initial_state), _ptr(o), _ptr(final_state), ws_ptr, ws_len,
-                              _stream(stream))
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(cu_seqlens), n_seqs, total, H,
+            dk, dv, chunk, float(eps), _dtype_code(q))
+    tail = (_ptr(initial_state), _ptr(o), _ptr(final_state), ws_ptr, ws_len, _stream(stream))
+    if beta is None:
+        st = _lib.kla_fwd_chunked(*head, *tail)
+    else:
+        st = _lib.kla_fwd_chunked_ex(*head, beta, *tail)
     if st != KLA_OK:
         raise KLAError(st)
     return o, final_state
@@ -136,12 +171,24 @@ def kla_fwd_chunked(q, k, v, alpha, eta, cu_seqlens=None, initial_state=None, ep
 def kla_decode_step(q, k, v, alpha, eta, state, eps=1e-6, o=None, stream=None):
     """One KLA decode step (C ABI `kla_decode_step`); `state` is updated in place.
 
-    q, k: [N, H, dk]; v: [N, H, dv]; alpha, eta: [N, H] fp32;
-    state: [N, H, dk, dv] fp32.  Returns o [N, H, dv] fp32.
+    q, k: [N, H, dk]; v: [N, H, dv]; alpha (or None: no decay), eta: [N, H]
+    fp32; state: [N, H, dk, dv] fp32.  Returns o [N, H, dv] fp32.
     """
+    return _decode(None, q, k, v, alpha, eta, state, eps, o, stream)
+
+
+def kla_decode_step_ex(q, k, v, alpha, eta, state, eps=1e-6, beta_mode="kaczmarz", o=None,
+                       stream=None):
+    """kla_decode_step with the step-size rule chosen by beta_mode (C ABI
+    `kla_decode_step_ex`), as in kla_fwd_chunked_ex."""
+    return _decode(_beta_code(beta_mode), q, k, v, alpha, eta, state, eps, o, stream)
+
+
+def _decode(beta, q, k, v, alpha, eta, state, eps, o, stream):
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
-    _need(alpha, "alpha", torch.float32)
+    if alpha is not None:
+        _need(alpha, "alpha", torch.float32)
     _need(eta, "eta", torch.float32)
     _need(state, "state", torch.float32)
     N, H, dk = q.shape
@@ -150,8 +197,12 @@ def kla_decode_step(q, k, v, alpha, eta, state, eps=1e-6, o=None, stream=None):
         o = torch.empty((N, H, dv), dtype=torch.float32, device=q.device)
     else:
         _need(o, "o", torch.float32)
-    st = _lib.kla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(state),
-                              _ptr(o), N, H, dk, dv, float(eps), _dtype_code(q), _stream(stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(state), _ptr(o), N, H, dk, dv,
+            float(eps), _dtype_code(q))
+    if beta is None:
+        st = _lib.kla_decode_step(*args, _stream(stream))
+    else:
+        st = _lib.kla_decode_step_ex(*args, beta, _stream(stream))
     if st != KLA_OK:
         raise KLAError(st)
     return o

@@ -17,6 +17,14 @@
  * alpha_t is the scalar decay gate and eta_t the relaxation gate; both are
  * per (token, head).  No scaling is applied to q (callers pre-scale).
  *
+ * The *_ex entry points also run the two gate variants the same kernels
+ * cover: beta_t = eta_t directly (KLA_BETA_DIRECT), the learned scalar step
+ * of Gated DeltaNet that KLA replaces (KLA summary, introduction), and, with
+ * alpha = NULL, no decay (alpha_t = 1): with the direct step this is
+ * DeltaNet ("Linear Attention Architectures: Mechanisms, Trade-offs, and
+ * Cross-Layer Routing", gist.science/pt/paper/2607.07953, section "Notacao
+ * Unificada", DeltaNet and Gated DeltaNet).
+ *
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers (HIP device memory) except where
  *     noted; the caller owns every buffer.  The library never allocates or
@@ -57,6 +65,11 @@ typedef enum {
     KLA_BF16 = 1  /* bfloat16 (8-bit exponent, 7-bit mantissa) */
 } kla_dtype;
 
+typedef enum {
+    KLA_BETA_KACZMARZ = 0, /* beta_t = eta_t / (k_t^T k_t + eps)   (KLA) */
+    KLA_BETA_DIRECT = 1    /* beta_t = eta_t; eps is unused       (Gated DeltaNet) */
+} kla_beta_mode;
+
 /*
  * Bytes of device workspace kla_fwd_chunked needs for these sizes.  The
  * current kernels need none and this returns 0; callers should still query
@@ -75,7 +88,8 @@ size_t kla_fwd_chunked_workspace_size(int32_t n_seqs, int64_t total_tok, int32_t
  *
  *   q, k        [total_tok, H, dk]   element type `dtype`
  *   v           [total_tok, H, dv]   element type `dtype`
- *   alpha, eta  [total_tok, H]       fp32; alpha in (0, 1], eta in [0, 1]
+ *   alpha, eta  [total_tok, H]       fp32; alpha in (0, 1], eta in [0, 1].
+ *               alpha may be NULL: alpha_t = 1 for every token (no decay).
  *   cu_seqlens  device int32 [n_seqs + 1] with 0 = cu[0] <= cu[1] <= ... <=
  *               cu[n_seqs] = total_tok: sequence s is tokens [cu[s], cu[s+1]).
  *               NULL means n_seqs equal sequences of total_tok / n_seqs tokens
@@ -109,6 +123,23 @@ kla_status kla_fwd_chunked(const void *q, const void *k, const void *v,
                            void *stream);
 
 /*
+ * kla_fwd_chunked with the step-size rule chosen by beta_mode (arguments in
+ * the same order, beta_mode after dtype).  KLA_BETA_KACZMARZ is exactly
+ * kla_fwd_chunked; KLA_BETA_DIRECT uses beta_t = eta_t (eta in [0, 1] as
+ * Gated DeltaNet's writing strength; eps is still range-checked but unused).
+ * The chunk algorithm is unchanged: only B = Diag(beta) differs (KLA summary,
+ * section "Implementacao").  Errors: as kla_fwd_chunked, plus
+ * KLA_ERR_INVALID_ARG for an unknown beta_mode.
+ */
+kla_status kla_fwd_chunked_ex(const void *q, const void *k, const void *v,
+                              const float *alpha, const float *eta,
+                              const int32_t *cu_seqlens, int32_t n_seqs, int64_t total_tok,
+                              int32_t H, int32_t dk, int32_t dv, int32_t chunk, float eps,
+                              kla_dtype dtype, kla_beta_mode beta_mode,
+                              const float *initial_state, float *o, float *final_state,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One recurrent decode step for n_seqs independent sequences: every
  * (sequence, head) state advances by one token IN PLACE, and o receives the
  * read of the new state.  It is the token recurrence above applied once,
@@ -118,7 +149,7 @@ kla_status kla_fwd_chunked(const void *q, const void *k, const void *v,
  *
  *   q, k        [n_seqs, H, dk]      element type `dtype`
  *   v           [n_seqs, H, dv]      element type `dtype`
- *   alpha, eta  [n_seqs, H]          fp32
+ *   alpha, eta  [n_seqs, H]          fp32 (alpha may be NULL: alpha = 1)
  *   state       [n_seqs, H, dk, dv]  fp32, read and updated in place
  *   o           [n_seqs, H, dv]      fp32, written
  *
@@ -128,6 +159,16 @@ kla_status kla_decode_step(const void *q, const void *k, const void *v,
                            const float *alpha, const float *eta, float *state, float *o,
                            int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, float eps,
                            kla_dtype dtype, void *stream);
+
+/*
+ * kla_decode_step with the step-size rule chosen by beta_mode (as in
+ * kla_fwd_chunked_ex).  Errors: as kla_decode_step, plus KLA_ERR_INVALID_ARG
+ * for an unknown beta_mode.
+ */
+kla_status kla_decode_step_ex(const void *q, const void *k, const void *v,
+                              const float *alpha, const float *eta, float *state, float *o,
+                              int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, float eps,
+                              kla_dtype dtype, kla_beta_mode beta_mode, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *kla_status_string(kla_status s);

@@ -43,14 +43,27 @@ def _load(path=None):
     lib.kla_oracle_decode_step.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_double, _dp]
+    lib.kla_oracle_fwd_ex.restype = ctypes.c_int
+    lib.kla_oracle_fwd_ex.argtypes = [_dp, _dp, _dp, _dp, _dp, _i64p,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_double, ctypes.c_int, _dp, _dp, _dp]
+    lib.kla_oracle_decode_step_ex.restype = ctypes.c_int
+    lib.kla_oracle_decode_step_ex.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_double, ctypes.c_int, _dp]
     lib.kla_oracle_num_threads.restype = ctypes.c_int
     lib.kla_oracle_num_threads.argtypes = []
     _libs[path] = lib
     return lib
 
 
+_BETA = {"kaczmarz": 0, "direct": 1}
+
+
 def _f64(x):
     """Contiguous float64 copy/view of an array-like (torch CPU tensors too)."""
+    if x is None:
+        return None
     if hasattr(x, "detach"):
         x = x.detach().to("cpu")
         import torch
@@ -67,14 +80,16 @@ def num_threads() -> int:
     return int(_load().kla_oracle_num_threads())
 
 
-def fwd(q, k, v, alpha, eta, cu_seqlens=None, eps=1e-6, initial_state=None, lib_path=None):
+def fwd(q, k, v, alpha, eta, cu_seqlens=None, eps=1e-6, initial_state=None, lib_path=None,
+        beta_mode="kaczmarz"):
     """Sequential fp64 KLA prefill.
 
     q, k: [tok, H, dk]; v: [tok, H, dv]; alpha, eta: [tok, H].  Packed
     sequences are given by cu_seqlens [n_seqs+1]; without it, q/k/v may
     also be [B, T, H, d] (dense batch, flattened here).  Returns
     (o [tok, H, dv] float64, final_state [n_seqs, H, dk, dv] float64), with
-    o shaped like v.
+    o shaped like v.  beta_mode "direct" takes beta = eta (Gated DeltaNet);
+    alpha None means no decay (alpha = 1).
     """
     lib = _load(lib_path)
     q, k, v, alpha, eta = (_f64(t) for t in (q, k, v, alpha, eta))
@@ -92,7 +107,7 @@ def fwd(q, k, v, alpha, eta, cu_seqlens=None, eps=1e-6, initial_state=None, lib_
     q = q.reshape(-1, H, dk)
     k = k.reshape(-1, H, dk)
     v = v.reshape(-1, H, dv)
-    alpha = alpha.reshape(-1, H)
+    alpha = None if alpha is None else alpha.reshape(-1, H)
     eta = eta.reshape(-1, H)
     n_seqs = cu.shape[0] - 1
     tok = q.shape[0]
@@ -101,20 +116,20 @@ def fwd(q, k, v, alpha, eta, cu_seqlens=None, eps=1e-6, initial_state=None, lib_
     init = None if initial_state is None else _f64(initial_state).reshape(n_seqs, H, dk, dv)
     o = np.zeros((tok, H, dv), dtype=np.float64)
     fin = np.zeros((n_seqs, H, dk, dv), dtype=np.float64)
-    rc = lib.kla_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
-                            cu.ctypes.data_as(_i64p), n_seqs, H, dk, dv, float(eps),
-                            _ptr(init), _ptr(o), _ptr(fin))
+    rc = lib.kla_oracle_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
+                               cu.ctypes.data_as(_i64p), n_seqs, H, dk, dv, float(eps),
+                               _BETA[beta_mode], _ptr(init), _ptr(o), _ptr(fin))
     if rc != 0:
         raise RuntimeError("kla_oracle_fwd failed")
     return o.reshape(out_shape), fin
 
 
-def decode_step(q, k, v, alpha, eta, state, eps=1e-6, lib_path=None):
+def decode_step(q, k, v, alpha, eta, state, eps=1e-6, lib_path=None, beta_mode="kaczmarz"):
     """One fp64 KLA decode step.
 
-    q, k: [N, H, dk]; v: [N, H, dv]; alpha, eta: [N, H]; state [N, H, dk, dv].
-    Returns (o [N, H, dv], new_state), both float64; the input state is not
-    modified.
+    q, k: [N, H, dk]; v: [N, H, dv]; alpha (or None: no decay), eta: [N, H];
+    state [N, H, dk, dv].  Returns (o [N, H, dv], new_state), both float64;
+    the input state is not modified.  beta_mode as in fwd.
     """
     lib = _load(lib_path)
     q, k, v, alpha, eta = (_f64(t) for t in (q, k, v, alpha, eta))
@@ -122,8 +137,9 @@ def decode_step(q, k, v, alpha, eta, state, eps=1e-6, lib_path=None):
     N, H, dk = q.shape
     dv = v.shape[-1]
     o = np.zeros((N, H, dv), dtype=np.float64)
-    rc = lib.kla_oracle_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
-                                    _ptr(S), N, H, dk, dv, float(eps), _ptr(o))
+    rc = lib.kla_oracle_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
+                                       _ptr(S), N, H, dk, dv, float(eps), _BETA[beta_mode],
+                                       _ptr(o))
     if rc != 0:
         raise RuntimeError("kla_oracle_decode_step failed")
     return o, S

@@ -22,6 +22,12 @@
  * state after the write; the pages never print the read, so this is a
  * stated reading.
  *
+ * Gate variants (the *_ex entry points): with beta_direct the step is
+ * beta_t = eta_t itself, the learned scalar of Gated DeltaNet that KLA
+ * replaces (KLA summary, introduction); alpha == NULL means alpha_t = 1,
+ * no decay, which with the direct step is DeltaNet (survey page, section
+ * "Notacao Unificada").  Everything else is the same recurrence.
+ *
  * This is the plain definition, token by token, in double precision,
  * with no blocking or chunking: the chunkwise algorithm of the GPU path
  * reaches the same result up to rounding.  Inputs arrive as doubles that
@@ -45,11 +51,11 @@
 /* One KLA write followed by the read, on one (sequence, head) state. */
 static void kla_token(double *S, double *e, const double *q, const double *k,
                       const double *v, double alpha, double eta, double eps,
-                      int dk, int dv, double *o)
+                      int beta_direct, int dk, int dv, double *o)
 {
     double kk = 0.0;
     for (int i = 0; i < dk; ++i) kk += k[i] * k[i];
-    const double beta = eta / (kk + eps);
+    const double beta = beta_direct ? eta : eta / (kk + eps);
 
     /* S~ = alpha S */
     for (int i = 0; i < dk; ++i)
@@ -87,15 +93,16 @@ int kla_oracle_num_threads(void)
  * Prefill over packed sequences.  The state starts at initial_state[s] (or
  * zero when initial_state is NULL) at the first token of each sequence and
  * the final state of each sequence goes to final_state (when not NULL).
+ * alpha may be NULL (alpha_t = 1).  beta_direct selects beta_t = eta_t.
  * Returns 0, or -1 on a malformed argument.
  */
-int kla_oracle_fwd(const double *q, const double *k, const double *v,
-                   const double *alpha, const double *eta,
-                   const int64_t *cu_seqlens, int n_seqs, int H, int dk, int dv,
-                   double eps, const double *initial_state, double *o,
-                   double *final_state)
+int kla_oracle_fwd_ex(const double *q, const double *k, const double *v,
+                      const double *alpha, const double *eta,
+                      const int64_t *cu_seqlens, int n_seqs, int H, int dk, int dv,
+                      double eps, int beta_direct, const double *initial_state, double *o,
+                      double *final_state)
 {
-    if (!q || !k || !v || !alpha || !eta || !cu_seqlens || !o) return -1;
+    if (!q || !k || !v || !eta || !cu_seqlens || !o) return -1;
     if (n_seqs <= 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
     for (int s = 0; s < n_seqs; ++s)
         if (cu_seqlens[s + 1] < cu_seqlens[s]) return -1;
@@ -121,7 +128,8 @@ int kla_oracle_fwd(const double *q, const double *k, const double *v,
             for (int64_t t = cu_seqlens[s]; t < cu_seqlens[s + 1]; ++t) {
                 const size_t th = (size_t)t * H + h;
                 kla_token(S, e, q + th * dk, k + th * dk, v + th * dv,
-                          alpha[th], eta[th], eps, dk, dv, o + th * dv);
+                          alpha ? alpha[th] : 1.0, eta[th], eps, beta_direct, dk, dv,
+                          o + th * dv);
             }
             if (final_state) memcpy(final_state + sh * sdim, S, sizeof(double) * sdim);
             free(S);
@@ -130,16 +138,29 @@ int kla_oracle_fwd(const double *q, const double *k, const double *v,
     return failed ? -1 : 0;
 }
 
+/* The KLA step (beta_t = eta_t / (|k_t|^2 + eps)). */
+int kla_oracle_fwd(const double *q, const double *k, const double *v,
+                   const double *alpha, const double *eta,
+                   const int64_t *cu_seqlens, int n_seqs, int H, int dk, int dv,
+                   double eps, const double *initial_state, double *o,
+                   double *final_state)
+{
+    return kla_oracle_fwd_ex(q, k, v, alpha, eta, cu_seqlens, n_seqs, H, dk, dv, eps, 0,
+                             initial_state, o, final_state);
+}
+
 /*
  * One decode step: every (sequence, head) state advances by one token in
  * place and o receives the read of the new state.
  *   q, k [n_seqs][H][dk], v, o [n_seqs][H][dv], alpha, eta [n_seqs][H]
+ * alpha may be NULL (alpha = 1); beta_direct selects beta = eta.
  */
-int kla_oracle_decode_step(const double *q, const double *k, const double *v,
-                           const double *alpha, const double *eta, double *state,
-                           int n_seqs, int H, int dk, int dv, double eps, double *o)
+int kla_oracle_decode_step_ex(const double *q, const double *k, const double *v,
+                              const double *alpha, const double *eta, double *state,
+                              int n_seqs, int H, int dk, int dv, double eps, int beta_direct,
+                              double *o)
 {
-    if (!q || !k || !v || !alpha || !eta || !state || !o) return -1;
+    if (!q || !k || !v || !eta || !state || !o) return -1;
     if (n_seqs <= 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
     const size_t sdim = (size_t)dk * dv;
     int failed = 0;
@@ -152,8 +173,16 @@ int kla_oracle_decode_step(const double *q, const double *k, const double *v,
             continue;
         }
         kla_token(state + sh * sdim, e, q + sh * dk, k + sh * dk, v + sh * dv,
-                  alpha[sh], eta[sh], eps, dk, dv, o + sh * dv);
+                  alpha ? alpha[sh] : 1.0, eta[sh], eps, beta_direct, dk, dv, o + sh * dv);
         free(e);
     }
     return failed ? -1 : 0;
+}
+
+/* The KLA step (beta = eta / (|k|^2 + eps)). */
+int kla_oracle_decode_step(const double *q, const double *k, const double *v,
+                           const double *alpha, const double *eta, double *state,
+                           int n_seqs, int H, int dk, int dv, double eps, double *o)
+{
+    return kla_oracle_decode_step_ex(q, k, v, alpha, eta, state, n_seqs, H, dk, dv, eps, 0, o);
 }

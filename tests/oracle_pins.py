@@ -1,9 +1,11 @@
 """Pins of the fp64 oracle against facts the KLA pages and the mathematics fix.
 
 Each pin takes the reference under test as two callables,
-  fwd(q, k, v, alpha, eta, cu_seqlens=None, eps=..., initial_state=None)
-      -> (o, final_state)
-  decode(q, k, v, alpha, eta, state, eps=...) -> (o, new_state)
+  fwd(q, k, v, alpha, eta, cu_seqlens=None, eps=..., initial_state=None,
+      beta_mode="kaczmarz") -> (o, final_state)
+  decode(q, k, v, alpha, eta, state, eps=..., beta_mode="kaczmarz")
+      -> (o, new_state)
+(alpha may be None: no decay; beta_mode "direct": beta = eta)
 so the same checks can run against deliberately broken builds of the
 reference (tests/test_oracle_mutants.py) and must fail there.
 
@@ -14,7 +16,9 @@ coefficient and the update (section "A Regra de Atualizacao KLA"), the
 three properties of the unrelaxed step (section "Propriedades Chave") and
 the drop-in relation to Gated DeltaNet (section "Implementacao").  The
 linear-attention survey page (gist.science/pt/paper/2607.07953, section
-"Metodologia e Estrutura") gives DeltaNet and Gated DeltaNet.
+"Metodologia e Estrutura" and "Notacao Unificada") gives DeltaNet and Gated
+DeltaNet; the KLA summary's introduction gives Gated DeltaNet's learned
+scalar step that KLA replaces (the "direct" step-size mode).
 """
 import json
 import os
@@ -280,7 +284,95 @@ def pin_zero_key(fwd, decode):
     assert rel(o[0, 0], 0.7 * S0[0, 0].T @ q[0, 0]) < TIGHT
 
 
+def _gdn_product_form(q, k, v, alpha, b, S0):
+    """Gated DeltaNet written as a product of maps, per head:
+    S_t = alpha_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T, o_t = S_t^T q_t."""
+    L, H, dk = k.shape
+    S = S0.copy()
+    o = np.zeros(v.shape)
+    for t in range(L):
+        for h in range(H):
+            kt = k[t, h]
+            a = 1.0 if alpha is None else alpha[t, h]
+            S[h] = a * (np.eye(dk) - b[t, h] * np.outer(kt, kt)) @ S[h] + b[t, h] * np.outer(kt, v[t, h])
+            o[t, h] = S[h].T @ q[t, h]
+    return o, S
+
+
+def pin_direct_step_product_form(fwd, decode):
+    """Step size given directly (beta = eta, Gated DeltaNet's learned scalar):
+    the recurrence equals Gated DeltaNet's product form with b_t = eta_t for
+    keys of any norm, and with no decay gate it is DeltaNet.  The decode step
+    in the same mode equals one more token."""
+    rng = np.random.default_rng(13)
+    L, H, dk, dv = 17, 2, 6, 4
+    q, k, v, alpha, _ = _rand_seq(rng, L + 1, H, dk, dv)
+    k = k * 0.3  # keep |b| |k|^2 moderate so the product form stays well conditioned
+    eta = rng.uniform(0.05, 1.0, (L + 1, H))
+    S0 = rng.standard_normal((1, H, dk, dv))
+    for a in (alpha, None):
+        aa = None if a is None else a[:L]
+        o, S = fwd(q[:L], k[:L], v[:L], aa, eta[:L], eps=0.5, initial_state=S0,
+                   beta_mode="direct")
+        eo, eS = _gdn_product_form(q[:L], k[:L], v[:L], aa, eta[:L], S0[0])
+        assert rel(o, eo) < 1e-11 and rel(S[0], eS) < 1e-11
+        ad = None if a is None else a[L:]
+        od, Sd = decode(q[L:], k[L:], v[L:], ad, eta[L:], S, eps=0.5, beta_mode="direct")
+        eo1, eS1 = _gdn_product_form(q[L:], k[L:], v[L:], ad, eta[L:], eS)
+        assert rel(od[0], eo1[0]) < 1e-11 and rel(Sd[0], eS1) < 1e-11
+
+
+def pin_no_alpha_is_unit_decay(fwd, decode):
+    """Leaving out the decay gate is alpha_t = 1 exactly, in both step-size
+    modes, for prefill and decode."""
+    rng = np.random.default_rng(14)
+    L, H, dk, dv = 21, 2, 5, 3
+    q, k, v, _, eta = _rand_seq(rng, L, H, dk, dv)
+    S0 = rng.standard_normal((1, H, dk, dv))
+    ones = np.ones((L, H))
+    for mode in ("kaczmarz", "direct"):
+        o1, S1 = fwd(q, k, v, None, eta, eps=1e-3, initial_state=S0, beta_mode=mode)
+        o2, S2 = fwd(q, k, v, ones, eta, eps=1e-3, initial_state=S0, beta_mode=mode)
+        assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+        d1 = decode(q[:1], k[:1], v[:1], None, eta[:1], S0, eps=1e-3, beta_mode=mode)
+        d2 = decode(q[:1], k[:1], v[:1], ones[:1], eta[:1], S0, eps=1e-3, beta_mode=mode)
+        assert np.array_equal(d1[0], d2[0]) and np.array_equal(d1[1], d2[1])
+    # and it is not the same as a decaying run
+    o3, _ = fwd(q, k, v, 0.5 * ones, eta, eps=1e-3, initial_state=S0)
+    assert rel(o3, o1) > 1e-3
+
+
+def pin_direct_equals_kaczmarz_on_unit_keys(fwd, decode):
+    """With unit-norm keys and eps = 0 the Kaczmarz step eta / |k|^2 is eta,
+    so the two step-size modes agree; with other norms they differ."""
+    rng = np.random.default_rng(15)
+    L, H, dk, dv = 19, 2, 7, 5
+    q, k, v, alpha, eta = _rand_seq(rng, L, H, dk, dv)
+    ku = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    a = fwd(q, ku, v, alpha, eta, eps=0.0, beta_mode="kaczmarz")
+    b = fwd(q, ku, v, alpha, eta, eps=0.0, beta_mode="direct")
+    assert rel(a[0], b[0]) < 1e-12 and rel(a[1], b[1]) < 1e-12
+    c = fwd(q, 2.0 * ku, v, alpha, eta, eps=0.0, beta_mode="direct")
+    d = fwd(q, 2.0 * ku, v, alpha, eta, eps=0.0, beta_mode="kaczmarz")
+    assert rel(c[0], d[0]) > 1e-3
+
+
+def pin_deltanet_exact_recall(fwd, decode):
+    """DeltaNet (no decay) with beta = 1 and orthonormal keys stores every
+    pair exactly: S^T k_j = v_j for all j after n <= dk writes."""
+    rng = np.random.default_rng(16)
+    dk, dv, n = 8, 5, 6
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    K = Qm[:, :n].T.reshape(n, 1, dk)
+    V = rng.standard_normal((n, 1, dv))
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    _, S = fwd(K, K, V, None, np.ones((n, 1)), eps=0.3, initial_state=S0, beta_mode="direct")
+    assert rel(K[:, 0] @ S[0, 0], V[:, 0]) < 1e-12
+
+
 ALL_PINS = [pin_worked_example, pin_orthogonal_projection, pin_min_norm_bruteforce,
             pin_exact_line_search, pin_normalised_gradient, pin_exact_recall, pin_eta_zero,
             pin_scalar_case, pin_gated_deltanet_form, pin_chunk_form, pin_packed_and_resume,
-            pin_decode_is_one_token, pin_zero_key]
+            pin_decode_is_one_token, pin_zero_key, pin_direct_step_product_form,
+            pin_no_alpha_is_unit_decay, pin_direct_equals_kaczmarz_on_unit_keys,
+            pin_deltanet_exact_recall]

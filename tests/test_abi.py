@@ -35,6 +35,11 @@ def lib():
     L.kla_decode_step.argtypes = [ctypes.c_void_p] * 7 + [
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
         ctypes.c_int, ctypes.c_void_p]
+    L.kla_fwd_chunked_ex.restype = ctypes.c_int
+    L.kla_fwd_chunked_ex.argtypes = (L.kla_fwd_chunked.argtypes[:14] + [ctypes.c_int]
+                                     + L.kla_fwd_chunked.argtypes[14:])
+    L.kla_decode_step_ex.restype = ctypes.c_int
+    L.kla_decode_step_ex.argtypes = L.kla_decode_step.argtypes[:13] + [ctypes.c_int, ctypes.c_void_p]
     L.kla_status_string.restype = ctypes.c_char_p
     L.kla_status_string.argtypes = [ctypes.c_int]
     L.kla_version.restype = ctypes.c_char_p
@@ -44,8 +49,10 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["kla_fwd_chunked", "kla_fwd_chunked_workspace_size",
-                                           "kla_decode_step", "kla_status_string", "kla_version"])
+    assert declared_functions() == sorted(["kla_fwd_chunked", "kla_fwd_chunked_ex",
+                                           "kla_fwd_chunked_workspace_size", "kla_decode_step",
+                                           "kla_decode_step_ex", "kla_status_string",
+                                           "kla_version"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -83,7 +90,7 @@ def fwd_args(**over):
     (dict(eps=float("nan")), INVALID),
     (dict(q=None), INVALID),
     (dict(o=None), INVALID),
-    (dict(alpha=None), INVALID),
+    (dict(eta=None), INVALID),         # alpha may be NULL (no decay), eta may not
     (dict(q=BASE + 2), INVALID),       # misaligned
     (dict(o=BASE + 256 * MB + 4), INVALID),
     (dict(o=BASE + 8), INVALID),       # o overlaps q
@@ -96,6 +103,19 @@ def fwd_args(**over):
 ])
 def test_fwd_rejects(lib, over, code):
     assert lib.kla_fwd_chunked(*fwd_args(**over)) == code
+
+
+@pytest.mark.parametrize("mode", [2, -1, 7])
+def test_fwd_ex_rejects_unknown_beta_mode(lib, mode):
+    a = fwd_args()
+    assert lib.kla_fwd_chunked_ex(*a[:14], mode, *a[14:]) == INVALID
+
+
+def test_fwd_ex_checks_like_fwd(lib):
+    for over, code in ((dict(n_seqs=0), INVALID), (dict(eta=None), INVALID),
+                       (dict(dk=96, dv=96), UNSUPPORTED), (dict(o=BASE + 8), INVALID)):
+        a = fwd_args(**over)
+        assert lib.kla_fwd_chunked_ex(*a[:14], 1, *a[14:]) == code
 
 
 def test_workspace_query(lib):
@@ -123,10 +143,18 @@ def dec_args(**over):
 ])
 def test_decode_rejects(lib, over, code):
     assert lib.kla_decode_step(*dec_args(**over)) == code
+    a = dec_args(**over)
+    assert lib.kla_decode_step_ex(*a[:13], 1, a[13]) == code
+
+
+@pytest.mark.parametrize("mode", [2, -3])
+def test_decode_ex_rejects_unknown_beta_mode(lib, mode):
+    a = dec_args()
+    assert lib.kla_decode_step_ex(*a[:13], mode, a[13]) == INVALID
 
 
 def test_binding_names_match_the_abi():
     import delta_rule_linear_amd as pkg
-    for name in ("kla_fwd_chunked", "kla_decode_step", "kla_fwd_chunked_workspace_size",
-                 "kla_status_string", "kla_version"):
+    for name in ("kla_fwd_chunked", "kla_decode_step", "kla_fwd_chunked_ex", "kla_decode_step_ex",
+                 "kla_fwd_chunked_workspace_size", "kla_status_string", "kla_version"):
         assert callable(getattr(pkg, name))

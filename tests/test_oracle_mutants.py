@@ -48,6 +48,13 @@ MUTANTS = {
         "kla_token(state + sh * sdim, e, q + sh * dk, k + sh * dk,",
         "kla_token(state + sh * sdim, e, k + sh * dk, q + sh * dk,"),
     "drops_last_token": lambda s: s.replace("t < cu_seqlens[s + 1]; ++t", "t + 1 < cu_seqlens[s + 1]; ++t"),
+    "direct_mode_ignored": lambda s: s.replace("beta_direct ? eta : eta / (kk + eps)",
+                                               "eta / (kk + eps)"),
+    "missing_alpha_is_zero": lambda s: s.replace("alpha ? alpha[th] : 1.0", "alpha ? alpha[th] : 0.0"),
+    "decode_missing_alpha_is_zero": lambda s: s.replace("alpha ? alpha[sh] : 1.0",
+                                                        "alpha ? alpha[sh] : 0.0"),
+    "decode_drops_direct_mode": lambda s: s.replace("eps, beta_direct, dk, dv, o + sh * dv",
+                                                    "eps, 0, dk, dv, o + sh * dv"),
     "decay_after_write": lambda s: s.replace(
         "    for (int i = 0; i < dk; ++i)\n        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= alpha;\n",
         "").replace("    /* o = S^T q */\n",
