@@ -26,6 +26,8 @@ bool overlap(Range a, Range b) {
 
 bool supported_dim(int32_t dk, int32_t dv) { return dk == dv && (dk == 64 || dk == 128); }
 
+constexpr int32_t kla_max_splits = 1024;
+
 }  // namespace
 
 extern "C" {
@@ -47,21 +49,33 @@ size_t kla_fwd_chunked_workspace_size(int32_t, int64_t, int32_t, int32_t, int32_
   return 0;
 }
 
-kla_status kla_fwd_chunked_ex(const void *q, const void *k, const void *v, const float *alpha,
-                              const float *eta, const int32_t *cu_seqlens, int32_t n_seqs,
-                              int64_t total_tok, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
-                              float eps, kla_dtype dtype, kla_beta_mode beta_mode,
-                              const float *initial_state, float *o, float *final_state,
-                              void *workspace, size_t workspace_bytes, void *stream) {
+size_t kla_fwd_chunked_split_workspace_size(int32_t n_seqs, int32_t H, int32_t dk, int32_t dv,
+                                            int32_t n_splits) {
+  if (n_seqs <= 0 || H <= 0 || n_splits <= 1 || !supported_dim(dk, dv)) return 0;
+  // A and B maps for segments 0..P-2, start states for segments 0..P-1
+  const size_t per = (size_t)dk * dv * sizeof(float);
+  return (size_t)n_seqs * H * per * (size_t)(3 * n_splits - 2);
+}
+
+namespace {
+kla_status fwd_impl(const void *q, const void *k, const void *v, const float *alpha,
+                    const float *eta, const int32_t *cu_seqlens, int32_t n_seqs,
+                    int64_t total_tok, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                    float eps, kla_dtype dtype, kla_beta_mode beta_mode, int32_t n_splits,
+                    const float *initial_state, float *o, float *final_state,
+                    void *workspace, size_t workspace_bytes, void *stream) {
   if (n_seqs <= 0 || H <= 0 || total_tok < 0 || !std::isfinite(eps) || eps < 0.f)
     return KLA_ERR_INVALID_ARG;
   if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT) return KLA_ERR_INVALID_ARG;
   if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
   if (!supported_dim(dk, dv) || chunk != 64) return KLA_ERR_UNSUPPORTED;
   if (!cu_seqlens && total_tok % n_seqs != 0) return KLA_ERR_INVALID_ARG;
-  if (workspace_bytes < kla_fwd_chunked_workspace_size(n_seqs, total_tok, H, dk, dv, chunk))
-    return KLA_ERR_WORKSPACE;
-  (void)workspace;
+  if (n_splits < 1 || n_splits > kla_max_splits) return KLA_ERR_INVALID_ARG;
+  const size_t ws_need = n_splits > 1
+      ? kla_fwd_chunked_split_workspace_size(n_seqs, H, dk, dv, n_splits)
+      : kla_fwd_chunked_workspace_size(n_seqs, total_tok, H, dk, dv, chunk);
+  if (workspace_bytes < ws_need) return KLA_ERR_WORKSPACE;
+  if (ws_need > 0 && (!workspace || !aligned16(workspace))) return KLA_ERR_INVALID_ARG;
   const bool have_tokens = total_tok > 0;
   if (have_tokens && (!q || !k || !v || !eta || !o)) return KLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
@@ -76,8 +90,11 @@ kla_status kla_fwd_chunked_ex(const void *q, const void *k, const void *v, const
               rcu = range(cu_seqlens, cu_seqlens ? (int64_t)(n_seqs + 1) * 4 : 0),
               rs0 = range(initial_state, initial_state ? (int64_t)n_seqs * H * dk * dv * 4 : 0),
               rs1 = range(final_state, final_state ? (int64_t)n_seqs * H * dk * dv * 4 : 0);
-  for (const Range &in : {rq, rk, rv, ra, re, rcu, rs0, rs1})
+  const Range rws = range(workspace, (int64_t)ws_need);
+  for (const Range &in : {rq, rk, rv, ra, re, rcu, rs0, rs1, rws})
     if (overlap(ro, in)) return KLA_ERR_INVALID_ARG;
+  for (const Range &in : {rq, rk, rv, ra, re, rcu, rs0, rs1})
+    if (overlap(rws, in)) return KLA_ERR_INVALID_ARG;
   if (final_state) {
     for (const Range &in : {rq, rk, rv, ra, re, rcu})
       if (overlap(rs1, in)) return KLA_ERR_INVALID_ARG;
@@ -102,9 +119,51 @@ kla_status kla_fwd_chunked_ex(const void *q, const void *k, const void *v, const
   a.o = o;
   a.final_state = final_state;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t e =
-      dtype == KLA_BF16 ? kla::launch_prefill_bf16(a, st) : kla::launch_prefill_f32(a, st);
+  auto run = [&]() {
+    return dtype == KLA_BF16 ? kla::launch_prefill_bf16(a, st) : kla::launch_prefill_f32(a, st);
+  };
+  if (n_splits == 1 || total_tok == 0) return run() == hipSuccess ? KLA_OK : KLA_ERR_HIP;
+  // split sequences: segment maps, scan of the maps, then every segment
+  const size_t mat = (size_t)n_seqs * H * dk * dv;
+  float *ws = static_cast<float *>(workspace);
+  a.n_splits = n_splits;
+  a.ws_a = ws;
+  a.ws_b = ws + mat * (n_splits - 1);
+  a.ws_s = ws + 2 * mat * (n_splits - 1);
+  hipError_t e = kla::launch_split_identity(a, st);
+  if (e == hipSuccess) {
+    a.seg_mode = 1;
+    e = run();
+  }
+  if (e == hipSuccess) e = kla::launch_split_scan(a, st);
+  if (e == hipSuccess) {
+    a.seg_mode = 2;
+    e = run();
+  }
   return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
+}
+}  // namespace
+
+kla_status kla_fwd_chunked_ex(const void *q, const void *k, const void *v, const float *alpha,
+                              const float *eta, const int32_t *cu_seqlens, int32_t n_seqs,
+                              int64_t total_tok, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                              float eps, kla_dtype dtype, kla_beta_mode beta_mode,
+                              const float *initial_state, float *o, float *final_state,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  return fwd_impl(q, k, v, alpha, eta, cu_seqlens, n_seqs, total_tok, H, dk, dv, chunk, eps, dtype,
+                  beta_mode, 1, initial_state, o, final_state, workspace, workspace_bytes, stream);
+}
+
+kla_status kla_fwd_chunked_split(const void *q, const void *k, const void *v, const float *alpha,
+                                 const float *eta, const int32_t *cu_seqlens, int32_t n_seqs,
+                                 int64_t total_tok, int32_t H, int32_t dk, int32_t dv,
+                                 int32_t chunk, float eps, kla_dtype dtype,
+                                 kla_beta_mode beta_mode, int32_t n_splits,
+                                 const float *initial_state, float *o, float *final_state,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+  return fwd_impl(q, k, v, alpha, eta, cu_seqlens, n_seqs, total_tok, H, dk, dv, chunk, eps, dtype,
+                  beta_mode, n_splits, initial_state, o, final_state, workspace, workspace_bytes,
+                  stream);
 }
 
 kla_status kla_fwd_chunked(const void *q, const void *k, const void *v, const float *alpha,

@@ -18,6 +18,11 @@ struct PrefillArgs {
   const float *initial_state; // nullable
   float *o;
   float *final_state;         // nullable
+  // split-sequence passes (0: whole sequences; 1: segment maps; 2: outputs)
+  int seg_mode = 0;
+  int n_splits = 1;
+  float *ws_a = nullptr, *ws_b = nullptr;  // [n_seqs, H, P-1, D, D]
+  const float *ws_s = nullptr;             // [n_seqs, H, P, D, D]
 };
 
 struct DecodeArgs {
@@ -33,6 +38,11 @@ struct DecodeArgs {
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s);
+// Split-sequence helpers: ws_a <- identity per (sequence, head, segment <
+// P-1); then the scan S_0 = initial state (or 0), S_{p+1} = A_p S_p + B_p,
+// written to ws_s for p = 0..P-1.
+hipError_t launch_split_identity(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_split_scan(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
 
 }  // namespace kla

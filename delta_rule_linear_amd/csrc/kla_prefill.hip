@@ -275,6 +275,83 @@ __device__ inline int64_t logical_block() {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + kx;
 }
 
+// What one workgroup computes.  Mode 0: one (sequence, head, 64-column block
+// of dv) over the whole sequence.  The split-sequence path cuts every
+// sequence into n_splits segments on chunk boundaries; the state map of a
+// segment is affine, S_end = A S_start + B, and the same kernels run it in
+// two passes around a scan of those maps:
+//   mode 1, segments 0..P-2: the state pass from the start [I | 0] with V
+//     read as [0 | V].  Column blocks 0..NB-1 give A (start and end in ws_a,
+//     set to I beforehand), blocks NB..2NB-1 give B (zero start, end in
+//     ws_b).  No output.
+//   mode 2, all segments: each from its start state in ws_s (written by the
+//     scan), writing o; the last segment writes the final state.
+struct SegParams {
+  int mode, n_splits;
+  float *ws_a, *ws_b;   // [n_seqs, H, P-1, D, D]
+  const float *ws_s;    // [n_seqs, H, P, D, D]
+};
+struct Work {
+  int h, nb, vb;        // head, state column block, V column block (-1: V read as zero)
+  int64_t bos, eos;     // token range of this workgroup
+  const float *s0;      // start state (D x D row-major) or null for zero
+  float *sfin;          // end state destination or null
+  bool out;             // write o
+};
+template <int NB, int D>
+__device__ inline Work resolve_work(const SegParams &sp, const int32_t *cu_seqlens,
+                                    int64_t seq_len_dense, int H, const float *S0, float *Sfin) {
+  const int64_t lb = logical_block();
+  const int P = sp.n_splits;
+  Work wk;
+  int64_t shi, p = 0;
+  if (sp.mode == 1) {
+    const int cb = (int)(lb % (2 * NB));
+    const int64_t r = lb / (2 * NB);
+    p = r % (P - 1);
+    shi = r / (P - 1);
+    wk.nb = cb < NB ? cb : cb - NB;
+    wk.vb = cb < NB ? -1 : cb - NB;
+  } else {
+    wk.nb = wk.vb = (int)(lb % NB);
+    const int64_t r = lb / NB;
+    p = sp.mode == 2 ? r % P : 0;
+    shi = sp.mode == 2 ? r / P : r;
+  }
+  wk.h = (int)(shi % H);
+  const int64_t s = shi / H, sh = shi;
+  int64_t bos, eos;
+  if (cu_seqlens) {
+    bos = cu_seqlens[s];
+    eos = cu_seqlens[s + 1];
+  } else {
+    bos = s * seq_len_dense;
+    eos = bos + seq_len_dense;
+  }
+  constexpr int64_t DD = (int64_t)D * D;
+  wk.out = sp.mode != 1;
+  if (sp.mode == 0) {
+    wk.bos = bos;
+    wk.eos = eos;
+    wk.s0 = S0 ? S0 + sh * DD : nullptr;
+    wk.sfin = Sfin ? Sfin + sh * DD : nullptr;
+    return wk;
+  }
+  const int64_t nch = (eos - bos + C - 1) / C, per = (nch + P - 1) / P;
+  const int64_t c0 = p * per < nch ? p * per : nch, c1 = (p + 1) * per < nch ? (p + 1) * per : nch;
+  wk.bos = bos + c0 * C;
+  wk.eos = bos + c1 * C < eos ? bos + c1 * C : eos;
+  if (sp.mode == 1) {
+    const int64_t m = (sh * (P - 1) + p) * DD;
+    wk.s0 = wk.vb < 0 ? sp.ws_a + m : nullptr;
+    wk.sfin = wk.vb < 0 ? sp.ws_a + m : sp.ws_b + m;
+  } else {
+    wk.s0 = sp.ws_s + (sh * P + p) * DD;
+    wk.sfin = (p == P - 1 && Sfin) ? Sfin + sh * DD : nullptr;
+  }
+  return wk;
+}
+
 // Gram jobs of waves 1-3, numbered 0..15: jobs 0-5 are the K K^T blocks
 // below the diagonal (-> -Ahat), in row order (1,0) (2,0) (2,1) (3,0) (3,1)
 // (3,2); jobs 6-15 are the Q K^T blocks on or below the diagonal (-> M), in
@@ -343,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ eta,
     const int32_t *__restrict__ cu_seqlens, int64_t seq_len_dense, int H, float eps, int beta_direct,
-    const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ Sfin) {
+    const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ Sfin, SegParams sp) {
   using CF = Cfg<E, D>;
   using P = typename CF::P;
   constexpr bool BF = CF::BF;
@@ -361,19 +438,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   const int l = tid & 63;
   const int j = l >> 4, c16 = l & 15;
 
-  const int64_t lb = logical_block();
-  const int nb = (int)(lb % NB);
-  const int64_t shi = lb / NB;
-  const int h = (int)(shi % H);
-  const int64_t s = shi / H;
-  int64_t bos, eos;
-  if (cu_seqlens) {
-    bos = cu_seqlens[s];
-    eos = cu_seqlens[s + 1];
-  } else {
-    bos = s * seq_len_dense;
-    eos = bos + seq_len_dense;
-  }
+  const Work wk = resolve_work<NB, D>(sp, cu_seqlens, seq_len_dense, H, S0, Sfin);
+  const int nb = wk.nb, h = wk.h;
+  const int64_t bos = wk.bos, eos = wk.eos;
   const int col = nb * DVB + 16 * w + c16;  // this lane's state/output column
 
   // M above the block diagonal is read as zero.
@@ -384,10 +451,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 
   // State tiles: tile t holds rows 16t+4j+i (i<4), column `col`.  A null
   // start state is an empty buffer range: every load returns zero.
-  const int64_t sbase = (s * H + h) * (int64_t)D * D;
   f32x4 S[NST];
   {
-    const rsrc_t rs = make_rsrc(S0 ? S0 + sbase : o, S0 ? (int64_t)D * D * 4 : 0);
+    const rsrc_t rs = make_rsrc(wk.s0 ? wk.s0 : o, wk.s0 ? (int64_t)D * D * 4 : 0);
 #pragma unroll
     for (int t = 0; t < NST; ++t)
 #pragma unroll
@@ -407,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const int64_t rowb = (int64_t)H * D * sizeof(E);
     const rsrc_t rk = make_rsrc(k + t0 * H * (int64_t)D, nn * rowb);
     const rsrc_t rq = make_rsrc(q + t0 * H * (int64_t)D, nn * rowb);
-    const rsrc_t rv = make_rsrc(v + t0 * H * (int64_t)D, nn * rowb);
+    const rsrc_t rv = make_rsrc(v + t0 * H * (int64_t)D, wk.vb >= 0 ? nn * rowb : 0);  // V = 0 for A blocks
 #pragma unroll
     for (int u = 0; u < NSEG; ++u) {
       const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
@@ -418,7 +484,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
     for (int u = 0; u < NVSEG; ++u) {
       const int sg = u * kThreads + tid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
-      vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + nb * DVB + cs * SEG_EL) * sizeof(E));
+      vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + wk.vb * DVB + cs * SEG_EL) * sizeof(E));
     }
     if (w == 0) {
       // no alpha: an empty range (the scan then takes log alpha = 0)
@@ -659,7 +725,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 
     // output rows < n (rows past the end fall outside the descriptor)
     {
-      const rsrc_t ro = make_rsrc(o + tok0 * H * (int64_t)D, (int64_t)n * H * D * 4);
+      const rsrc_t ro = make_rsrc(wk.out ? o + tok0 * H * (int64_t)D : o, wk.out ? (int64_t)n * H * D * 4 : 0);
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
@@ -705,7 +771,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   }
 
   {
-    const rsrc_t rs = make_rsrc(Sfin ? Sfin + sbase : o, Sfin ? (int64_t)D * D * 4 : 0);
+    const rsrc_t rs = make_rsrc(wk.sfin ? wk.sfin : o, wk.sfin ? (int64_t)D * D * 4 : 0);
 #pragma unroll
     for (int t = 0; t < NST; ++t)
 #pragma unroll
@@ -761,12 +827,14 @@ struct PSmem {
   alignas(16) float g2[C];
 };
 
-template <int D>
+// OUT = false: the segment-map pass, which writes no output and so needs
+// neither Q nor M (only K, V, the gates and the -Ahat, Y planes).
+template <int D, bool OUT>
 __global__ __launch_bounds__(512) void prefill_pc_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ eta,
     const int32_t *__restrict__ cu_seqlens, int64_t seq_len_dense, int H, float eps, int beta_direct,
-    const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ Sfin) {
+    const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ Sfin, SegParams sp) {
   using CF = Cfg<bf16, D>;
   using SL = PSlot<D>;
   constexpr int LDA = SL::LDA;
@@ -790,21 +858,10 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
   const int l = tid & 63;
   const int j = l >> 4, c16 = l & 15;
 
-  const int64_t lb = logical_block();
-  const int nb = (int)(lb % NB);
-  const int64_t shi = lb / NB;
-  const int h = (int)(shi % H);
-  const int64_t s = shi / H;
-  int64_t bos, eos;
-  if (cu_seqlens) {
-    bos = cu_seqlens[s];
-    eos = cu_seqlens[s + 1];
-  } else {
-    bos = s * seq_len_dense;
-    eos = bos + seq_len_dense;
-  }
+  const Work wk = resolve_work<NB, D>(sp, cu_seqlens, seq_len_dense, H, S0, Sfin);
+  const int nb = wk.nb, h = wk.h;
+  const int64_t bos = wk.bos, eos = wk.eos;
   const int col = nb * DVB + 16 * w + c16;  // consumer lane's state/output column
-  const int64_t sbase = (s * H + h) * (int64_t)D * D;
 
   // M above the block diagonal is read as zero (both slots).
   for (int i = tid; i < C * CF::LDP; i += 512) {
@@ -822,18 +879,18 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
     const int64_t rowb = (int64_t)H * D * 2;
     const rsrc_t rk = make_rsrc(k + t0 * H * (int64_t)D, nn * rowb);
     const rsrc_t rq = make_rsrc(q + t0 * H * (int64_t)D, nn * rowb);
-    const rsrc_t rv = make_rsrc(v + t0 * H * (int64_t)D, nn * rowb);
+    const rsrc_t rv = make_rsrc(v + t0 * H * (int64_t)D, wk.vb >= 0 ? nn * rowb : 0);  // V = 0 for A blocks
 #pragma unroll
     for (int u = 0; u < NSEG; ++u) {
       const int sg = u * PT + ptid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
       const uint32_t off = (uint32_t)((r * H + h) * D + cs * SEG_EL) * 2;
       kreg[u] = buf_ld16(rk, off);
-      qreg[u] = buf_ld16(rq, off);
+      if constexpr (OUT) qreg[u] = buf_ld16(rq, off);
     }
 #pragma unroll
     for (int u = 0; u < NVSEG; ++u) {
       const int sg = u * PT + ptid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
-      vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + nb * DVB + cs * SEG_EL) * 2);
+      vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + wk.vb * DVB + cs * SEG_EL) * 2);
     }
     if (pw == 0) {
       // no alpha: an empty range (the scan then takes log alpha = 0)
@@ -848,7 +905,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
     for (int u = 0; u < NSEG; ++u) {
       const int sg = u * PT + ptid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
       *reinterpret_cast<uint4 *>(&sl.Kr[r * CF::LDK + cs * SEG_EL]) = kreg[u];
-      *reinterpret_cast<uint4 *>(&sl.Qr[r * CF::LDK + cs * SEG_EL]) = qreg[u];
+      if constexpr (OUT) *reinterpret_cast<uint4 *>(&sl.Qr[r * CF::LDK + cs * SEG_EL]) = qreg[u];
     }
 #pragma unroll
     for (int u = 0; u < NVSEG; ++u) {
@@ -941,8 +998,9 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       // C[s][r] = K[s] . (Q or K)[r], so a lane holds four consecutive s of
       // one row r and writes them as one 8-byte store per plane.  Operands
       // of the next job are loaded first.
-      const int q0 = pw == 0 ? 15 : 5 * (pw - 1);
-      const int nj = pw == 0 ? 1 : 5;
+      // (without output only the six -Ahat jobs: two each for waves 1-3)
+      const int q0 = OUT ? (pw == 0 ? 15 : 5 * (pw - 1)) : 2 * (pw - 1);
+      const int nj = OUT ? (pw == 0 ? 1 : 5) : (pw == 0 ? 0 : 2);
       bf16x8 opa[2][D / 32], opb[2][D / 32];
       float grb[2];
       f32x4 gsb[2];
@@ -957,7 +1015,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
           opb[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&B[(16 * jb.bi + c16) * CF::LDK + 32 * t + 8 * j]);
         }
       };
-      ldjob(0);
+      if (nj > 0) ldjob(0);
 #pragma unroll
       for (int u = 0; u < 6; ++u) {
         if (u < nj) {
@@ -1018,7 +1076,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
   // ---- consumers ---------------------------------------------------------
   f32x4 S[NST];
   {
-    const rsrc_t rs = make_rsrc(S0 ? S0 + sbase : o, S0 ? (int64_t)D * D * 4 : 0);
+    const rsrc_t rs = make_rsrc(wk.s0 ? wk.s0 : o, wk.s0 ? (int64_t)D * D * 4 : 0);
 #pragma unroll
     for (int t = 0; t < NST; ++t)
 #pragma unroll
@@ -1048,7 +1106,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       bf16x8 qa[3], ka[3];
       auto ld = [&](int st) {
         const int kk = st / 4, bi = st % 4;
-        qa[st % 3] = lda_perm(&sl.Qr[(16 * bi + c16) * CF::LDK + 32 * kk], j);
+        if constexpr (OUT) qa[st % 3] = lda_perm(&sl.Qr[(16 * bi + c16) * CF::LDK + 32 * kk], j);
         ka[st % 3] = lda_perm(&sl.Kr[(16 * bi + c16) * CF::LDK + 32 * kk], j);
       };
       ld(0);
@@ -1061,9 +1119,9 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
         // Q S is formed transposed, (Q S)^T = S^T Q^T: the state fragments
         // serve as the A operand, so the output tile holds four consecutive
         // dv values of one token per lane (16-byte stores below)
-        QS[bi] = mma(Sf[kk].hi, qa[st % 3], QS[bi]);
+        if constexpr (OUT) QS[bi] = mma(Sf[kk].hi, qa[st % 3], QS[bi]);
         R[bi] = mma(ka[st % 3], Sf[kk].hi, R[bi]);
-        QS[bi] = mma(Sf[kk].lo, qa[st % 3], QS[bi]);
+        if constexpr (OUT) QS[bi] = mma(Sf[kk].lo, qa[st % 3], QS[bi]);
         R[bi] = mma(ka[st % 3], Sf[kk].lo, R[bi]);
         sched_fence();
       }
@@ -1117,36 +1175,38 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
         Ds[b] = split4(d);
       }
       const Split8 Df[2] = {join(Ds[0], Ds[1]), join(Ds[2], Ds[3])};
-      // O = Diag(gamma) Q S + M Delta: steps (kk, bi), bi >= 2 kk, kk-major
+      if constexpr (OUT) {
+        // O = Diag(gamma) Q S + M Delta: steps (kk, bi), bi >= 2 kk, kk-major
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi) QS[bi] *= sl.gam[16 * bi + c16];  // token column c16
-      {
-        constexpr int NSTEP = 6;
-        bf16x8 mh[3], ml[3];
-        auto ld = [&](int st) {
-          const int kk = st < 4 ? 0 : 1, bi = st < 4 ? st : st - 2;
-          const int off = (16 * bi + c16) * CF::LDP + 32 * kk;
-          mh[st % 3] = lda_perm(&sl.Mh[off], j);
-          ml[st % 3] = lda_perm(&sl.Ml[off], j);
-        };
-        ld(0);
-        ld(1);
+        for (int bi = 0; bi < 4; ++bi) QS[bi] *= sl.gam[16 * bi + c16];  // token column c16
+        {
+          constexpr int NSTEP = 6;
+          bf16x8 mh[3], ml[3];
+          auto ld = [&](int st) {
+            const int kk = st < 4 ? 0 : 1, bi = st < 4 ? st : st - 2;
+            const int off = (16 * bi + c16) * CF::LDP + 32 * kk;
+            mh[st % 3] = lda_perm(&sl.Mh[off], j);
+            ml[st % 3] = lda_perm(&sl.Ml[off], j);
+          };
+          ld(0);
+          ld(1);
 #pragma unroll
-        for (int st = 0; st < NSTEP; ++st) {
-          if (st + 2 < NSTEP) ld(st + 2);
-          sched_fence();
-          const int kk = st < 4 ? 0 : 1, bi = st < 4 ? st : st - 2;
-          // (M Delta)^T = Delta^T M^T, accumulated into the transposed output
-          QS[bi] = mma(Df[kk].hi, mh[st % 3], QS[bi]);
-          QS[bi] = mma(Df[kk].lo, mh[st % 3], QS[bi]);
-          QS[bi] = mma(Df[kk].hi, ml[st % 3], QS[bi]);
-          sched_fence();
+          for (int st = 0; st < NSTEP; ++st) {
+            if (st + 2 < NSTEP) ld(st + 2);
+            sched_fence();
+            const int kk = st < 4 ? 0 : 1, bi = st < 4 ? st : st - 2;
+            // (M Delta)^T = Delta^T M^T, accumulated into the transposed output
+            QS[bi] = mma(Df[kk].hi, mh[st % 3], QS[bi]);
+            QS[bi] = mma(Df[kk].lo, mh[st % 3], QS[bi]);
+            QS[bi] = mma(Df[kk].hi, ml[st % 3], QS[bi]);
+            sched_fence();
+          }
         }
-      }
-      const rsrc_t ro = make_rsrc(o + tok0 * H * (int64_t)D, (int64_t)n * H * D * 4);
+        const rsrc_t ro = make_rsrc(wk.out ? o + tok0 * H * (int64_t)D : o, wk.out ? (int64_t)n * H * D * 4 : 0);
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi)  // token 16bi + c16, dv 16w + 4j..+3; rows past the end are dropped
-        buf_st16(ro, (uint32_t)(((16 * bi + c16) * H + h) * D + nb * DVB + 16 * w + 4 * j) * 4, QS[bi]);
+        for (int bi = 0; bi < 4; ++bi)  // token 16bi + c16, dv 16w + 4j..+3; rows past the end are dropped
+          buf_st16(ro, (uint32_t)(((16 * bi + c16) * H + h) * D + nb * DVB + 16 * w + 4 * j) * 4, QS[bi]);
+      }
       // S' = 2^{g2_last} S + K^T Diag(2^{g2_last - g2}) Delta
       const float glast = sl.gam[C - 1];
 #pragma unroll
@@ -1184,7 +1244,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
   }
 
   {
-    const rsrc_t rs = make_rsrc(Sfin ? Sfin + sbase : o, Sfin ? (int64_t)D * D * 4 : 0);
+    const rsrc_t rs = make_rsrc(wk.sfin ? wk.sfin : o, wk.sfin ? (int64_t)D * D * 4 : 0);
 #pragma unroll
     for (int t = 0; t < NST; ++t)
 #pragma unroll
@@ -1195,23 +1255,41 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
   }
 }
 
+// Workgroups of one launch: (sequence, head) x [segment] x column block.
+inline int64_t grid_of(const PrefillArgs &a, int NB) {
+  const int64_t sh = (int64_t)a.n_seqs * a.H;
+  if (a.seg_mode == 1) return sh * (a.n_splits - 1) * 2 * NB;
+  if (a.seg_mode == 2) return sh * a.n_splits * NB;
+  return sh * NB;
+}
+inline SegParams seg_of(const PrefillArgs &a) {
+  SegParams sp;
+  sp.mode = a.seg_mode;
+  sp.n_splits = a.n_splits;
+  sp.ws_a = a.ws_a;
+  sp.ws_b = a.ws_b;
+  sp.ws_s = a.ws_s;
+  return sp;
+}
+
 template <int D>
 hipError_t launch_pc(const PrefillArgs &a, hipStream_t st) {
-  const int64_t grid = (int64_t)a.n_seqs * a.H * (D / DVB);
-  hipLaunchKernelGGL((prefill_pc_kernel<D>), dim3((unsigned)grid), dim3(512), 0, st,
+  const int64_t grid = grid_of(a, D / DVB);
+  auto kern = a.seg_mode == 1 ? prefill_pc_kernel<D, false> : prefill_pc_kernel<D, true>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, st,
                      static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
                      static_cast<const bf16 *>(a.v), a.alpha, a.eta, a.cu_seqlens, a.seq_len_dense,
-                     a.H, a.eps, a.beta_direct, a.initial_state, a.o, a.final_state);
+                     a.H, a.eps, a.beta_direct, a.initial_state, a.o, a.final_state, seg_of(a));
   return hipGetLastError();
 }
 
 template <typename E, int D>
 hipError_t launch_d(const PrefillArgs &a, hipStream_t st) {
-  const int64_t grid = (int64_t)a.n_seqs * a.H * (D / DVB);
+  const int64_t grid = grid_of(a, D / DVB);
   hipLaunchKernelGGL((prefill_kernel<E, D>), dim3((unsigned)grid), dim3(kThreads), 0, st,
                      static_cast<const E *>(a.q), static_cast<const E *>(a.k),
                      static_cast<const E *>(a.v), a.alpha, a.eta, a.cu_seqlens, a.seq_len_dense,
-                     a.H, a.eps, a.beta_direct, a.initial_state, a.o, a.final_state);
+                     a.H, a.eps, a.beta_direct, a.initial_state, a.o, a.final_state, seg_of(a));
   return hipGetLastError();
 }
 

@@ -1,0 +1,124 @@
+// Split-sequence prefill: the scan between the two passes of the prefill
+// kernel (modes 1 and 2 of resolve_work in kla_prefill.hip).
+//
+// Each chunk of the recurrence, and so each segment of chunks, maps the
+// state affinely: S_end = A S_start + B, with A depending on the keys and
+// gates only and B the end state from a zero start.  This is the chunk form
+// the KLA technical summary keeps from Gated DeltaNet ("Resumo Tecnico:
+// Atencao Linear Kaczmarz (KLA)", section "Implementacao"): the state update
+// of a chunk is linear in the chunk-start state.  Maps compose, so after
+// pass 1 has produced (A_p, B_p) for segments p = 0..P-2, the start state
+// of every segment follows by a sequential scan over P-1 small products:
+//   S_0 = initial state (or 0),  S_{p+1} = A_p S_p + B_p.
+// Pass 2 then runs all segments at once from those starts.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kla_internal.h"
+
+namespace kla {
+namespace {
+
+constexpr int kScanThreads = 256;
+constexpr int kCols = 64;  // state columns per scan workgroup
+
+// ws_a[m] <- I (D x D) for every m < count.
+template <int D>
+__global__ __launch_bounds__(256) void identity_kernel(float *__restrict__ ws_a, int64_t count) {
+  const int64_t total4 = count * D * D / 4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = 4 * i;
+    const int r = (int)((e / D) % D), c = (int)(e % D);  // four consecutive columns of row r
+    float4 x;
+    x.x = (c == r) ? 1.f : 0.f;
+    x.y = (c + 1 == r) ? 1.f : 0.f;
+    x.z = (c + 2 == r) ? 1.f : 0.f;
+    x.w = (c + 3 == r) ? 1.f : 0.f;
+    reinterpret_cast<float4 *>(ws_a)[i] = x;
+  }
+}
+
+// One workgroup per (sequence, head, block of 64 state columns).  The
+// running start state (D x 64) and the current A_p (D x D) live in LDS;
+// each thread owns CPT consecutive columns of one row of the next state.
+template <int D>
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const float *__restrict__ S0,
+                                                             const float *__restrict__ ws_a,
+                                                             const float *__restrict__ ws_b,
+                                                             float *__restrict__ ws_s, int H,
+                                                             int P) {
+  constexpr int NCB = D / kCols;
+  constexpr int TPR = kScanThreads / D;  // threads per state row
+  constexpr int CPT = kCols / TPR;       // columns per thread
+  static_assert(TPR * D == kScanThreads && CPT * TPR == kCols, "scan tiling");
+  __shared__ float As[D * (D + 1)];
+  __shared__ float Ss[D * kCols];
+  const int tid = threadIdx.x;
+  const int cb = (int)(blockIdx.x % NCB);
+  const int64_t sh = blockIdx.x / NCB;
+  const int r = tid / TPR, c0 = (tid % TPR) * CPT;
+  constexpr int64_t DD = (int64_t)D * D;
+  const int col0 = cb * kCols;
+
+  // S_0: the caller's start state or zero, also copied to ws_s[.., 0] so
+  // pass 2 never reads the caller's buffer (which may be the final state).
+  for (int i = tid; i < D * kCols; i += kScanThreads) {
+    const int rr = i / kCols, cc = i % kCols;
+    const float x = S0 ? S0[sh * DD + (int64_t)rr * D + col0 + cc] : 0.f;
+    Ss[i] = x;
+    ws_s[(sh * P) * DD + (int64_t)rr * D + col0 + cc] = x;
+  }
+  for (int p = 0; p + 1 < P; ++p) {
+    const float *A = ws_a + (sh * (P - 1) + p) * DD;
+    const float *B = ws_b + (sh * (P - 1) + p) * DD;
+    for (int i = tid; i < D * D; i += kScanThreads) As[(i / D) * (D + 1) + i % D] = A[i];
+    __syncthreads();
+    float acc[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[c] = B[(int64_t)r * D + col0 + c0 + c];
+    for (int k = 0; k < D; ++k) {
+      const float a = As[r * (D + 1) + k];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[c] = fmaf(a, Ss[k * kCols + c0 + c], acc[c]);
+    }
+    __syncthreads();  // every thread has read Ss and As
+    float *dst = ws_s + (sh * P + p + 1) * DD + (int64_t)r * D + col0 + c0;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      Ss[r * kCols + c0 + c] = acc[c];
+      dst[c] = acc[c];
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_split_identity(const PrefillArgs &a, hipStream_t st) {
+  const int64_t count = (int64_t)a.n_seqs * a.H * (a.n_splits - 1);
+  const int64_t total4 = count * a.D * a.D / 4;
+  const int64_t blocks = (total4 + 255) / 256 < 4096 ? (total4 + 255) / 256 : 4096;
+  if (a.D == 128)
+    hipLaunchKernelGGL((identity_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, st, a.ws_a,
+                       count);
+  else
+    hipLaunchKernelGGL((identity_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, st, a.ws_a,
+                       count);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_scan(const PrefillArgs &a, hipStream_t st) {
+  const int64_t grid = (int64_t)a.n_seqs * a.H * (a.D / kCols);
+  if (a.D == 128)
+    hipLaunchKernelGGL((scan_kernel<128>), dim3((unsigned)grid), dim3(kScanThreads), 0, st,
+                       a.initial_state, a.ws_a, a.ws_b, const_cast<float *>(a.ws_s), a.H,
+                       a.n_splits);
+  else
+    hipLaunchKernelGGL((scan_kernel<64>), dim3((unsigned)grid), dim3(kScanThreads), 0, st,
+                       a.initial_state, a.ws_a, a.ws_b, const_cast<float *>(a.ws_s), a.H,
+                       a.n_splits);
+  return hipGetLastError();
+}
+
+}  // namespace kla

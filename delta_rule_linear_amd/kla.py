@@ -33,6 +33,11 @@ _lib.kla_fwd_chunked.argtypes = [_vp, _vp, _vp, _fp, _fp, _i32p, ctypes.c_int32,
 _lib.kla_fwd_chunked_ex.restype = ctypes.c_int
 _lib.kla_fwd_chunked_ex.argtypes = (_lib.kla_fwd_chunked.argtypes[:14] + [ctypes.c_int]
                                     + _lib.kla_fwd_chunked.argtypes[14:])
+_lib.kla_fwd_chunked_split_workspace_size.restype = ctypes.c_size_t
+_lib.kla_fwd_chunked_split_workspace_size.argtypes = [ctypes.c_int32] * 5
+_lib.kla_fwd_chunked_split.restype = ctypes.c_int
+_lib.kla_fwd_chunked_split.argtypes = (_lib.kla_fwd_chunked.argtypes[:14] + [ctypes.c_int, ctypes.c_int32]
+                                       + _lib.kla_fwd_chunked.argtypes[14:])
 _lib.kla_decode_step.restype = ctypes.c_int
 _lib.kla_decode_step.argtypes = [_vp, _vp, _vp, _fp, _fp, _fp, _fp, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int, _vp]
@@ -120,8 +125,23 @@ def kla_fwd_chunked_ex(q, k, v, alpha, eta, cu_seqlens=None, initial_state=None,
                 output_final_state, o, final_state, workspace, stream)
 
 
+def kla_fwd_chunked_split_workspace_size(n_seqs, H, dk, dv, n_splits) -> int:
+    return int(_lib.kla_fwd_chunked_split_workspace_size(n_seqs, H, dk, dv, n_splits))
+
+
+def kla_fwd_chunked_split(q, k, v, alpha, eta, cu_seqlens=None, initial_state=None, eps=1e-6,
+                          chunk=64, beta_mode="kaczmarz", n_splits=2, output_final_state=False,
+                          o=None, final_state=None, workspace=None, stream=None):
+    """kla_fwd_chunked_ex with every sequence cut into n_splits segments
+    (C ABI `kla_fwd_chunked_split`): segment maps, a scan of the maps, then
+    all segments at once.  The workspace is allocated with torch when not
+    given."""
+    return _fwd(_beta_code(beta_mode), q, k, v, alpha, eta, cu_seqlens, initial_state, eps, chunk,
+                output_final_state, o, final_state, workspace, stream, n_splits=int(n_splits))
+
+
 def _fwd(beta, q, k, v, alpha, eta, cu_seqlens, initial_state, eps, chunk, output_final_state, o,
-         final_state, workspace, stream):
+         final_state, workspace, stream, n_splits=None):
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
     if alpha is not None:
@@ -151,7 +171,10 @@ def _fwd(beta, q, k, v, alpha, eta, cu_seqlens, initial_state, eps, chunk, outpu
         final_state = torch.empty((n_seqs, H, dk, dv), dtype=torch.float32, device=q.device)
     elif final_state is not None:
         _need(final_state, "final_state", torch.float32)
-    ws_bytes = kla_fwd_chunked_workspace_size(n_seqs, total, H, dk, dv, chunk)
+    if n_splits is not None and n_splits > 1:
+        ws_bytes = kla_fwd_chunked_split_workspace_size(n_seqs, H, dk, dv, n_splits)
+    else:
+        ws_bytes = kla_fwd_chunked_workspace_size(n_seqs, total, H, dk, dv, chunk)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = _ptr(workspace)
@@ -159,7 +182,9 @@ def _fwd(beta, q, k, v, alpha, eta, cu_seqlens, initial_state, eps, chunk, outpu
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(cu_seqlens), n_seqs, total, H,
             dk, dv, chunk, float(eps), _dtype_code(q))
     tail = (_ptr(initial_state), _ptr(o), _ptr(final_state), ws_ptr, ws_len, _stream(stream))
-    if beta is None:
+    if n_splits is not None:
+        st = _lib.kla_fwd_chunked_split(*head, beta, n_splits, *tail)
+    elif beta is None:
         st = _lib.kla_fwd_chunked(*head, *tail)
     else:
         st = _lib.kla_fwd_chunked_ex(*head, beta, *tail)

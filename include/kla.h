@@ -140,6 +140,51 @@ kla_status kla_fwd_chunked_ex(const void *q, const void *k, const void *v,
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device workspace kla_fwd_chunked_split needs: for every
+ * (sequence, head), the maps (A, B) of segments 0..n_splits-2 and the start
+ * states of all n_splits segments, each dk x dv fp32 (dk = dv):
+ * n_seqs * H * dk * dv * 4 * (3 n_splits - 2) bytes.  0 for n_splits <= 1.
+ */
+size_t kla_fwd_chunked_split_workspace_size(int32_t n_seqs, int32_t H, int32_t dk, int32_t dv,
+                                            int32_t n_splits);
+
+/*
+ * kla_fwd_chunked_ex with every sequence cut into n_splits segments on chunk
+ * boundaries (segment p = chunks [p*c, (p+1)*c) of the sequence, c =
+ * ceil(chunks / n_splits); trailing segments of short sequences may be
+ * empty), for batches with too few (sequence, head) pairs to fill the GPU.
+ *
+ * The state map of a segment is affine, S_end = A S_start + B (the chunk
+ * form of the KLA summary, section "Implementacao", is linear in the
+ * chunk-start state).  Four launches on the stream:
+ *   0. the A slots of the workspace are set to the identity;
+ *   1. for segments 0..n_splits-2: A from the start I with V read as 0, and
+ *      B from a zero start, by the prefill kernel (no output);
+ *   2. a scan: S_0 = initial state (or 0), S_{p+1} = A_p S_p + B_p;
+ *   3. every segment from its start state, writing o; the last segment
+ *      writes final_state.
+ * The result equals kla_fwd_chunked_ex up to rounding; the work is about
+ * (3 - 2/n_splits) times that of one pass, spread over n_splits times as
+ * many workgroups.
+ *
+ *   n_splits    1 .. 1024; 1 is exactly kla_fwd_chunked_ex.
+ *   workspace   device buffer of at least
+ *               kla_fwd_chunked_split_workspace_size(...) bytes, 16-byte
+ *               aligned, not overlapping any argument.  Its contents on
+ *               entry are ignored and on return are unspecified.
+ * Other arguments as kla_fwd_chunked_ex.  Errors: as kla_fwd_chunked_ex,
+ * plus KLA_ERR_INVALID_ARG for n_splits out of range or a workspace that
+ * overlaps an argument, KLA_ERR_WORKSPACE for a short workspace.
+ */
+kla_status kla_fwd_chunked_split(const void *q, const void *k, const void *v,
+                                 const float *alpha, const float *eta,
+                                 const int32_t *cu_seqlens, int32_t n_seqs, int64_t total_tok,
+                                 int32_t H, int32_t dk, int32_t dv, int32_t chunk, float eps,
+                                 kla_dtype dtype, kla_beta_mode beta_mode, int32_t n_splits,
+                                 const float *initial_state, float *o, float *final_state,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One recurrent decode step for n_seqs independent sequences: every
  * (sequence, head) state advances by one token IN PLACE, and o receives the
  * read of the new state.  It is the token recurrence above applied once,

@@ -370,9 +370,39 @@ def pin_deltanet_exact_recall(fwd, decode):
     assert rel(K[:, 0] @ S[0, 0], V[:, 0]) < 1e-12
 
 
+def pin_segment_map_is_affine(fwd, decode):
+    """The end state of a stretch of tokens is affine in its start state,
+    S_end = A S_start + B: B is the end state from a zero start and A the end
+    state from the start I with v = 0 (the columns of the state evolve
+    independently, each driven by its own column of v).  Composing two
+    stretches composes the maps.  This is what the split-sequence prefill
+    runs on (chunk form of the KLA summary, section "Implementacao")."""
+    rng = np.random.default_rng(17)
+    L, H, dk, dv = 23, 2, 5, 4
+    q, k, v, alpha, eta = _rand_seq(rng, L, H, dk, dv)
+    eye = np.broadcast_to(np.eye(dk), (1, H, dk, dk)).copy()
+    X = rng.standard_normal((1, H, dk, dv))
+    for mode, kk in (("kaczmarz", k), ("direct", k / np.linalg.norm(k, axis=-1, keepdims=True))):
+        _, B = fwd(q, kk, v, alpha, eta, eps=1e-3, beta_mode=mode)
+        _, A = fwd(q, kk, np.zeros((L, H, dk)), alpha, eta, eps=1e-3, initial_state=eye,
+                   beta_mode=mode)
+        _, SX = fwd(q, kk, v, alpha, eta, eps=1e-3, initial_state=X, beta_mode=mode)
+        assert rel(SX[0], A[0] @ X[0] + B[0]) < 1e-12
+        # two stretches: the maps compose
+        m = 9
+        _, B1 = fwd(q[:m], kk[:m], v[:m], alpha[:m], eta[:m], eps=1e-3, beta_mode=mode)
+        _, A1 = fwd(q[:m], kk[:m], np.zeros((m, H, dk)), alpha[:m], eta[:m], eps=1e-3,
+                    initial_state=eye, beta_mode=mode)
+        _, B2 = fwd(q[m:], kk[m:], v[m:], alpha[m:], eta[m:], eps=1e-3, beta_mode=mode)
+        _, A2 = fwd(q[m:], kk[m:], np.zeros((L - m, H, dk)), alpha[m:], eta[m:], eps=1e-3,
+                    initial_state=eye, beta_mode=mode)
+        assert rel(A2[0] @ (A1[0] @ X[0] + B1[0]) + B2[0], SX[0]) < 1e-12
+        assert rel(A2[0] @ A1[0], A[0]) < 1e-12
+
+
 ALL_PINS = [pin_worked_example, pin_orthogonal_projection, pin_min_norm_bruteforce,
             pin_exact_line_search, pin_normalised_gradient, pin_exact_recall, pin_eta_zero,
             pin_scalar_case, pin_gated_deltanet_form, pin_chunk_form, pin_packed_and_resume,
             pin_decode_is_one_token, pin_zero_key, pin_direct_step_product_form,
             pin_no_alpha_is_unit_decay, pin_direct_equals_kaczmarz_on_unit_keys,
-            pin_deltanet_exact_recall]
+            pin_deltanet_exact_recall, pin_segment_map_is_affine]

@@ -38,6 +38,11 @@ def lib():
     L.kla_fwd_chunked_ex.restype = ctypes.c_int
     L.kla_fwd_chunked_ex.argtypes = (L.kla_fwd_chunked.argtypes[:14] + [ctypes.c_int]
                                      + L.kla_fwd_chunked.argtypes[14:])
+    L.kla_fwd_chunked_split.restype = ctypes.c_int
+    L.kla_fwd_chunked_split.argtypes = (L.kla_fwd_chunked.argtypes[:14] + [ctypes.c_int, ctypes.c_int32]
+                                        + L.kla_fwd_chunked.argtypes[14:])
+    L.kla_fwd_chunked_split_workspace_size.restype = ctypes.c_size_t
+    L.kla_fwd_chunked_split_workspace_size.argtypes = [ctypes.c_int32] * 5
     L.kla_decode_step_ex.restype = ctypes.c_int
     L.kla_decode_step_ex.argtypes = L.kla_decode_step.argtypes[:13] + [ctypes.c_int, ctypes.c_void_p]
     L.kla_status_string.restype = ctypes.c_char_p
@@ -50,6 +55,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["kla_fwd_chunked", "kla_fwd_chunked_ex",
+                                           "kla_fwd_chunked_split",
+                                           "kla_fwd_chunked_split_workspace_size",
                                            "kla_fwd_chunked_workspace_size", "kla_decode_step",
                                            "kla_decode_step_ex", "kla_status_string",
                                            "kla_version"])
@@ -118,6 +125,33 @@ def test_fwd_ex_checks_like_fwd(lib):
         assert lib.kla_fwd_chunked_ex(*a[:14], 1, *a[14:]) == code
 
 
+def test_split_workspace_query(lib):
+    # maps (A, B) for P-1 segments and start states for P: (3P - 2) fp32 d x d per (seq, head)
+    assert lib.kla_fwd_chunked_split_workspace_size(2, 16, 128, 128, 3) == 2 * 16 * 128 * 128 * 4 * 7
+    assert lib.kla_fwd_chunked_split_workspace_size(2, 16, 64, 64, 2) == 2 * 16 * 64 * 64 * 4 * 4
+    assert lib.kla_fwd_chunked_split_workspace_size(2, 16, 128, 128, 1) == 0
+    assert lib.kla_fwd_chunked_split_workspace_size(2, 16, 96, 96, 3) == 0
+
+
+def split_call(lib, n_splits, **over):
+    a = fwd_args(**over)
+    return lib.kla_fwd_chunked_split(*a[:14], 0, n_splits, *a[14:])
+
+
+def test_split_rejects(lib):
+    ws = BASE + 512 * MB
+    need = 2 * 2 * 64 * 64 * 4 * 4   # fwd_args: n_seqs=2, H=2, d=64; P=2
+    assert split_call(lib, 0) == INVALID                         # n_splits < 1
+    assert split_call(lib, 1025) == INVALID                      # n_splits too large
+    assert split_call(lib, 2) == WORKSPACE                       # no workspace
+    assert split_call(lib, 2, ws=ws, wsb=need - 1) == WORKSPACE  # short workspace
+    assert split_call(lib, 2, ws=ws + 8, wsb=need) == INVALID    # misaligned
+    assert split_call(lib, 2, ws=BASE + 256 * MB, wsb=need) == INVALID  # overlaps o
+    assert split_call(lib, 2, ws=BASE, wsb=need) == INVALID      # overlaps q
+    assert split_call(lib, 2, ws=ws, wsb=need, n_seqs=0) == INVALID
+    assert split_call(lib, 2, ws=ws, wsb=need, dk=96, dv=96) == UNSUPPORTED
+
+
 def test_workspace_query(lib):
     assert lib.kla_fwd_chunked_workspace_size(8, 16384, 16, 128, 128, 64) == 0
 
@@ -156,5 +190,6 @@ def test_decode_ex_rejects_unknown_beta_mode(lib, mode):
 def test_binding_names_match_the_abi():
     import delta_rule_linear_amd as pkg
     for name in ("kla_fwd_chunked", "kla_decode_step", "kla_fwd_chunked_ex", "kla_decode_step_ex",
-                 "kla_fwd_chunked_workspace_size", "kla_status_string", "kla_version"):
+                 "kla_fwd_chunked_split", "kla_fwd_chunked_workspace_size",
+                 "kla_fwd_chunked_split_workspace_size", "kla_status_string", "kla_version"):
         assert callable(getattr(pkg, name))
