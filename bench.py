@@ -176,6 +176,48 @@ def bench_decode(args, torch, kla, workloads):
     return dict(N=N, H=H, d=d, steps=len(steps), wall=wall, ev_ms=ev_ms, state_bytes=state_bytes)
 
 
+def bench_long(args, torch, kla, workloads, n_splits=3, launches=20):
+    """Long-context prefill (2 sequences x 32768 tokens, 16 heads, d=128):
+    one pass against the split-sequence path.  With 32 (sequence, head)
+    pairs the one-pass kernel fills 64 of the 256 compute units; three
+    segments fill all of them in the segment-map pass (32 x 2 x 4
+    workgroups).  Each variant: 3 warm-up launches, then `launches` back to
+    back between one event pair."""
+    inp = workloads.prefill("long")
+    B, H, d = inp["n_seqs"], inp["H"], inp["d"]
+    T = inp["lengths"][0]
+    dev = "cuda:0"
+    q, k, v = (inp[n].to(dev).view(B, T, H, d) for n in ("q", "k", "v"))
+    a, e = (inp[n].to(dev).view(B, T, H) for n in ("alpha", "eta"))
+    o = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(kla.kla_fwd_chunked_split_workspace_size(B, H, d, d, n_splits),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def one():
+        kla.kla_fwd_chunked(q, k, v, a, e, eps=inp["eps"], o=o, final_state=S)
+
+    def split():
+        kla.kla_fwd_chunked_split(q, k, v, a, e, eps=inp["eps"], n_splits=n_splits, o=o,
+                                  final_state=S, workspace=ws)
+
+    res = {}
+    for name, fn in (("one_pass", one), ("split", split)):
+        for _ in range(3):
+            fn()
+        _, ev_ms = time_launches(fn, launches, stream)
+        res[name] = ev_ms * 1e3
+    tok = B * T
+    return {"workload": f"long-context KLA prefill: {B} sequences x {T} tokens, H={H}, "
+                        f"dk=dv={d}, bf16 q/k/v (dense batch)",
+            "n_splits": n_splits,
+            "us_one_pass": round(res["one_pass"], 1), "us_split": round(res["split"], 1),
+            "tokens_per_s_one_pass": round(tok / (res["one_pass"] * 1e-6), 1),
+            "tokens_per_s_split": round(tok / (res["split"] * 1e-6), 1),
+            "speedup": round(res["one_pass"] / res["split"], 3)}
+
+
 def cpu_baseline(pre, oracle):
     """fp64 reference on the host over the whole layer-shaped prefill."""
     import numpy as np
@@ -213,6 +255,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--skip-long", action="store_true",
+                    help="skip the long-context one-pass vs split-sequence comparison")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -281,6 +325,8 @@ def main():
                          "traffic": measured_traffic(DECODE_KERNEL), "kernel": DECODE_KERNEL, "avg_launch_us": round(dec["ev_ms"] * 1e3, 2),
                          "algorithmic_bytes_per_launch": dec["state_bytes"]},
         }
+    if not args.skip_long:
+        out["long_context"] = bench_long(args, torch, kla, workloads)
     if not args.skip_cpu_baseline:
         import oracle
         out["cpu_baseline"] = cpu_baseline(pre, oracle)
