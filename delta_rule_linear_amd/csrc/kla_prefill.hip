@@ -1085,17 +1085,26 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
   lds_barrier();
   lds_barrier();
 
-  int cur = 0;
-  for (int64_t tok0 = bos; tok0 < eos; tok0 += C, cur ^= 1) {
-    SL &sl = sm.slot[cur];
+  // One chunk: Sin is the state entering it, Sout receives the state after
+  // it.  The loop runs two chunks per trip, alternating the two state
+  // arrays and the two LDS slots, so slot addresses are constants and the
+  // update needs no copy back into the entering array.
+  f32x4 S2[NST];
+  auto cstep = [&](SL &sl, int64_t tok0, f32x4 (&Sin)[NST], f32x4 (&Sout)[NST])
+                   __attribute__((always_inline)) {
 
     // ---- segment A: Q S, K S, R = V - Diag(gamma) K S -----------------------
     f32x4 QS[4], R[4];
     {
       constexpr int NK = NST / 2, NSTEP = 4 * NK;
       Split8 Sf[NK];
+      // the decayed state for this chunk's update first, so the split below
+      // may consume Sin in place
+      const float glast = sl.gam[C - 1];
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) Sf[kk] = join(split4(S[2 * kk]), split4(S[2 * kk + 1]));
+      for (int t = 0; t < NST; ++t) Sout[t] = Sin[t] * glast;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) Sf[kk] = join(split4(Sin[2 * kk]), split4(Sin[2 * kk + 1]));
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
         QS[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1208,13 +1217,10 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
           buf_st16(ro, (uint32_t)(((16 * bi + c16) * H + h) * D + nb * DVB + 16 * w + 4 * j) * 4, QS[bi]);
       }
       // S' = 2^{g2_last} S + K^T Diag(2^{g2_last - g2}) Delta
-      const float glast = sl.gam[C - 1];
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
         for (int i = 0; i < 4; ++i) Dl[bi][i] *= sl.rgam[16 * bi + 4 * j + i];
-#pragma unroll
-      for (int t = 0; t < NST; ++t) S[t] *= glast;
       const Split8 Hf[2] = {join(split4(Dl[0]), split4(Dl[1])), join(split4(Dl[2]), split4(Dl[3]))};
       {
         // steps (kk, t), kk-major; K^T operands by transposing reads, two ahead
@@ -1234,13 +1240,29 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
           if (st + 2 < NSTEP) ld(st + 2);
           sched_fence();
           const int kk = st / NST, t = st % NST;
-          S[t] = mma(kt[st % 3], Hf[kk].hi, S[t]);
-          S[t] = mma(kt[st % 3], Hf[kk].lo, S[t]);
+          Sout[t] = mma(kt[st % 3], Hf[kk].hi, Sout[t]);
+          Sout[t] = mma(kt[st % 3], Hf[kk].lo, Sout[t]);
           sched_fence();
         }
       }
     }
     lds_barrier();
+  };
+  int64_t tok0 = bos;
+  bool in_s2 = false;  // the current state is in S2
+  while (tok0 < eos) {
+    cstep(sm.slot[0], tok0, S, S2);
+    tok0 += C;
+    if (tok0 >= eos) {
+      in_s2 = true;
+      break;
+    }
+    cstep(sm.slot[1], tok0, S2, S);
+    tok0 += C;
+  }
+  if (in_s2) {
+#pragma unroll
+    for (int t = 0; t < NST; ++t) S[t] = S2[t];
   }
 
   {
