@@ -51,6 +51,10 @@ def _load(path=None):
     lib.kla_oracle_decode_step_ex.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp,
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, ctypes.c_double, ctypes.c_int, _dp]
+    lib.kla_oracle_fwd_ch.restype = ctypes.c_int
+    lib.kla_oracle_fwd_ch.argtypes = lib.kla_oracle_fwd_ex.argtypes
+    lib.kla_oracle_decode_step_ch.restype = ctypes.c_int
+    lib.kla_oracle_decode_step_ch.argtypes = lib.kla_oracle_decode_step_ex.argtypes
     lib.kla_oracle_num_threads.restype = ctypes.c_int
     lib.kla_oracle_num_threads.argtypes = []
     _libs[path] = lib
@@ -81,7 +85,7 @@ def num_threads() -> int:
 
 
 def fwd(q, k, v, alpha, eta, cu_seqlens=None, eps=1e-6, initial_state=None, lib_path=None,
-        beta_mode="kaczmarz"):
+        beta_mode="kaczmarz", channel_decay=False):
     """Sequential fp64 KLA prefill.
 
     q, k: [tok, H, dk]; v: [tok, H, dv]; alpha, eta: [tok, H].  Packed
@@ -89,7 +93,8 @@ def fwd(q, k, v, alpha, eta, cu_seqlens=None, eps=1e-6, initial_state=None, lib_
     also be [B, T, H, d] (dense batch, flattened here).  Returns
     (o [tok, H, dv] float64, final_state [n_seqs, H, dk, dv] float64), with
     o shaped like v.  beta_mode "direct" takes beta = eta (Gated DeltaNet);
-    alpha None means no decay (alpha = 1).
+    alpha None means no decay (alpha = 1).  channel_decay: alpha holds one
+    decay per key channel, [tok, H, dk] (Kimi Delta Attention's gate).
     """
     lib = _load(lib_path)
     q, k, v, alpha, eta = (_f64(t) for t in (q, k, v, alpha, eta))
@@ -107,7 +112,12 @@ def fwd(q, k, v, alpha, eta, cu_seqlens=None, eps=1e-6, initial_state=None, lib_
     q = q.reshape(-1, H, dk)
     k = k.reshape(-1, H, dk)
     v = v.reshape(-1, H, dv)
-    alpha = None if alpha is None else alpha.reshape(-1, H)
+    if channel_decay:
+        if alpha is None:
+            raise ValueError("channel_decay needs alpha")
+        alpha = alpha.reshape(-1, H, dk)
+    else:
+        alpha = None if alpha is None else alpha.reshape(-1, H)
     eta = eta.reshape(-1, H)
     n_seqs = cu.shape[0] - 1
     tok = q.shape[0]
@@ -116,20 +126,22 @@ def fwd(q, k, v, alpha, eta, cu_seqlens=None, eps=1e-6, initial_state=None, lib_
     init = None if initial_state is None else _f64(initial_state).reshape(n_seqs, H, dk, dv)
     o = np.zeros((tok, H, dv), dtype=np.float64)
     fin = np.zeros((n_seqs, H, dk, dv), dtype=np.float64)
-    rc = lib.kla_oracle_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
-                               cu.ctypes.data_as(_i64p), n_seqs, H, dk, dv, float(eps),
-                               _BETA[beta_mode], _ptr(init), _ptr(o), _ptr(fin))
+    f = lib.kla_oracle_fwd_ch if channel_decay else lib.kla_oracle_fwd_ex
+    rc = f(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), cu.ctypes.data_as(_i64p), n_seqs, H,
+           dk, dv, float(eps), _BETA[beta_mode], _ptr(init), _ptr(o), _ptr(fin))
     if rc != 0:
         raise RuntimeError("kla_oracle_fwd failed")
     return o.reshape(out_shape), fin
 
 
-def decode_step(q, k, v, alpha, eta, state, eps=1e-6, lib_path=None, beta_mode="kaczmarz"):
+def decode_step(q, k, v, alpha, eta, state, eps=1e-6, lib_path=None, beta_mode="kaczmarz",
+                channel_decay=False):
     """One fp64 KLA decode step.
 
     q, k: [N, H, dk]; v: [N, H, dv]; alpha (or None: no decay), eta: [N, H];
     state [N, H, dk, dv].  Returns (o [N, H, dv], new_state), both float64;
-    the input state is not modified.  beta_mode as in fwd.
+    the input state is not modified.  beta_mode and channel_decay (alpha
+    [N, H, dk]) as in fwd.
     """
     lib = _load(lib_path)
     q, k, v, alpha, eta = (_f64(t) for t in (q, k, v, alpha, eta))
@@ -137,9 +149,11 @@ def decode_step(q, k, v, alpha, eta, state, eps=1e-6, lib_path=None, beta_mode="
     N, H, dk = q.shape
     dv = v.shape[-1]
     o = np.zeros((N, H, dv), dtype=np.float64)
-    rc = lib.kla_oracle_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
-                                       _ptr(S), N, H, dk, dv, float(eps), _BETA[beta_mode],
-                                       _ptr(o))
+    if channel_decay and (alpha is None or alpha.shape != (N, H, dk)):
+        raise ValueError("channel_decay needs alpha of shape [N, H, dk]")
+    f = lib.kla_oracle_decode_step_ch if channel_decay else lib.kla_oracle_decode_step_ex
+    rc = f(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(S), N, H, dk, dv, float(eps),
+           _BETA[beta_mode], _ptr(o))
     if rc != 0:
         raise RuntimeError("kla_oracle_decode_step failed")
     return o, S

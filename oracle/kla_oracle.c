@@ -28,6 +28,12 @@
  * no decay, which with the direct step is DeltaNet (survey page, section
  * "Notacao Unificada").  Everything else is the same recurrence.
  *
+ * Per-channel decay (the *_ch entry points): the survey page's Kimi Delta
+ * Attention (section "Metodologia e Estrutura") replaces the scalar decay by
+ * a vector with one rate per feature channel.  The state's rows are the key
+ * channels, so the decay becomes S~ = Diag(a_t) S_{t-1}: row i of the state
+ * is scaled by a_t[i].  The residual, the step and the write are KLA's.
+ *
  * This is the plain definition, token by token, in double precision,
  * with no blocking or chunking: the chunkwise algorithm of the GPU path
  * reaches the same result up to rounding.  Inputs arrive as doubles that
@@ -37,7 +43,7 @@
  * Layouts (all row-major, contiguous):
  *   q, k      [total_tok][H][dk]
  *   v, o      [total_tok][H][dv]
- *   alpha,eta [total_tok][H]
+ *   alpha,eta [total_tok][H]        (per-channel alpha: [total_tok][H][dk])
  *   state     [n_seqs][H][dk][dv]
  *   cu_seqlens[n_seqs+1], cu_seqlens[0] = 0, non-decreasing.
  */
@@ -78,6 +84,36 @@ static void kla_token(double *S, double *e, const double *q, const double *k,
         for (int i = 0; i < dk; ++i)
             for (int j = 0; j < dv; ++j) o[j] += S[(size_t)i * dv + j] * q[i];
     }
+}
+
+/* The same token with the decay per key channel: S~ = Diag(a) S. */
+static void kla_token_ch(double *S, double *e, const double *q, const double *k,
+                         const double *v, const double *a, double eta, double eps,
+                         int beta_direct, int dk, int dv, double *o)
+{
+    double kk = 0.0;
+    for (int i = 0; i < dk; ++i) kk += k[i] * k[i];
+    const double beta = beta_direct ? eta : eta / (kk + eps);
+
+    /* S~ = Diag(a) S: row i (key channel i) decays by a[i] */
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a[i];
+
+    /* e = v - S~^T k */
+    for (int j = 0; j < dv; ++j) e[j] = v[j];
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) e[j] -= S[(size_t)i * dv + j] * k[i];
+
+    /* S = S~ + beta k e^T */
+    for (int i = 0; i < dk; ++i) {
+        const double bk = beta * k[i];
+        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += bk * e[j];
+    }
+
+    /* o = S^T q */
+    for (int j = 0; j < dv; ++j) o[j] = 0.0;
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) o[j] += S[(size_t)i * dv + j] * q[i];
 }
 
 int kla_oracle_num_threads(void)
@@ -185,4 +221,74 @@ int kla_oracle_decode_step(const double *q, const double *k, const double *v,
                            int n_seqs, int H, int dk, int dv, double eps, double *o)
 {
     return kla_oracle_decode_step_ex(q, k, v, alpha, eta, state, n_seqs, H, dk, dv, eps, 0, o);
+}
+
+/*
+ * Prefill with the per-channel decay: alpha [total_tok][H][dk], required.
+ * Everything else as kla_oracle_fwd_ex.
+ */
+int kla_oracle_fwd_ch(const double *q, const double *k, const double *v,
+                      const double *alpha, const double *eta,
+                      const int64_t *cu_seqlens, int n_seqs, int H, int dk, int dv,
+                      double eps, int beta_direct, const double *initial_state, double *o,
+                      double *final_state)
+{
+    if (!q || !k || !v || !alpha || !eta || !cu_seqlens || !o) return -1;
+    if (n_seqs <= 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    for (int s = 0; s < n_seqs; ++s)
+        if (cu_seqlens[s + 1] < cu_seqlens[s]) return -1;
+    if (cu_seqlens[0] != 0) return -1;
+
+    const size_t sdim = (size_t)dk * dv;
+    int failed = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int s = 0; s < n_seqs; ++s) {
+        for (int h = 0; h < H; ++h) {
+            double *S = (double *)malloc(sizeof(double) * (sdim + dv));
+            if (!S) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            double *e = S + sdim;
+            const size_t sh = (size_t)s * H + h;
+            if (initial_state)
+                memcpy(S, initial_state + sh * sdim, sizeof(double) * sdim);
+            else
+                memset(S, 0, sizeof(double) * sdim);
+            for (int64_t t = cu_seqlens[s]; t < cu_seqlens[s + 1]; ++t) {
+                const size_t th = (size_t)t * H + h;
+                kla_token_ch(S, e, q + th * dk, k + th * dk, v + th * dv, alpha + th * dk,
+                             eta[th], eps, beta_direct, dk, dv, o + th * dv);
+            }
+            if (final_state) memcpy(final_state + sh * sdim, S, sizeof(double) * sdim);
+            free(S);
+        }
+    }
+    return failed ? -1 : 0;
+}
+
+/* One decode step with the per-channel decay: alpha [n_seqs][H][dk]. */
+int kla_oracle_decode_step_ch(const double *q, const double *k, const double *v,
+                              const double *alpha, const double *eta, double *state,
+                              int n_seqs, int H, int dk, int dv, double eps, int beta_direct,
+                              double *o)
+{
+    if (!q || !k || !v || !alpha || !eta || !state || !o) return -1;
+    if (n_seqs <= 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    const size_t sdim = (size_t)dk * dv;
+    int failed = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t sh = 0; sh < (int64_t)n_seqs * H; ++sh) {
+        double *e = (double *)malloc(sizeof(double) * dv);
+        if (!e) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        kla_token_ch(state + sh * sdim, e, q + sh * dk, k + sh * dk, v + sh * dv,
+                     alpha + sh * dk, eta[sh], eps, beta_direct, dk, dv, o + sh * dv);
+        free(e);
+    }
+    return failed ? -1 : 0;
 }

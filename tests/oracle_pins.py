@@ -18,14 +18,17 @@ the drop-in relation to Gated DeltaNet (section "Implementacao").  The
 linear-attention survey page (gist.science/pt/paper/2607.07953, section
 "Metodologia e Estrutura" and "Notacao Unificada") gives DeltaNet and Gated
 DeltaNet; the KLA summary's introduction gives Gated DeltaNet's learned
-scalar step that KLA replaces (the "direct" step-size mode).
+scalar step that KLA replaces (the "direct" step-size mode).  The survey
+page's Kimi Delta Attention (section "Metodologia e Estrutura") decays each
+feature channel at its own rate: with channel_decay=True alpha holds one
+decay per key channel and S~ = Diag(a_t) S (the pin_channel_* checks).
 """
 import json
 import os
 
 import numpy as np
 
-from chunk_model import chunked
+from chunk_model import chunked, chunked_ch
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 TIGHT = 1e-12
@@ -400,9 +403,142 @@ def pin_segment_map_is_affine(fwd, decode):
         assert rel(A2[0] @ A1[0], A[0]) < 1e-12
 
 
+
+# ---- per-channel decay (Kimi Delta Attention's gate) ------------------------
+
+def _rand_ch(rng, L, H, dk, amin=0.3):
+    return rng.uniform(amin, 1.0, (L, H, dk))
+
+
+def pin_channel_uniform_is_scalar(fwd, decode):
+    """A per-channel decay with the same rate in every channel is the
+    scalar decay (prefill and decode, both step modes)."""
+    rng = np.random.default_rng(31)
+    L, H, dk, dv = 21, 2, 5, 4
+    q, k, v, alpha, eta = _rand_seq(rng, L, H, dk, dv)
+    ach = np.repeat(alpha[..., None], dk, axis=-1)
+    S0 = rng.standard_normal((1, H, dk, dv))
+    for mode in ("kaczmarz", "direct"):
+        o1, S1 = fwd(q, k, v, ach, eta, eps=1e-3, initial_state=S0, beta_mode=mode,
+                     channel_decay=True)
+        o2, S2 = fwd(q, k, v, alpha, eta, eps=1e-3, initial_state=S0, beta_mode=mode)
+        assert rel(o1, o2) < TIGHT and rel(S1, S2) < TIGHT
+        Sd0 = np.repeat(S0, 3, axis=0)                         # 3 sequences x H heads
+        od1, Sd1 = decode(q[:3], k[:3], v[:3], ach[:3], eta[:3], Sd0, eps=1e-3, beta_mode=mode,
+                          channel_decay=True)
+        od2, Sd2 = decode(q[:3], k[:3], v[:3], alpha[:3], eta[:3], Sd0, eps=1e-3, beta_mode=mode)
+        assert rel(od1, od2) < TIGHT and rel(Sd1, Sd2) < TIGHT
+
+
+def pin_channel_eta_zero(fwd, decode):
+    """eta = 0: no write; row i of the state (key channel i) decays by the
+    product of that channel's rates, so o_t = (Diag(prod_{s<=t} a_s) S0)^T q_t."""
+    rng = np.random.default_rng(32)
+    L, H, dk, dv = 17, 2, 6, 4
+    q, k, v, _, _ = _rand_seq(rng, L, H, dk, dv)
+    a = _rand_ch(rng, L, H, dk, amin=0.7)
+    S0 = rng.standard_normal((1, H, dk, dv))
+    o, S = fwd(q, k, v, a, np.zeros((L, H)), eps=1e-6, initial_state=S0, channel_decay=True)
+    decay = np.cumprod(a, axis=0)                              # [L, H, dk]
+    exp_o = np.einsum("thi,hij,thi->thj", decay, S0[0], q)
+    assert rel(o, exp_o) < TIGHT
+    assert rel(S[0], decay[-1][:, :, None] * S0[0]) < TIGHT
+
+
+def pin_channel_orthogonal_projection(fwd, decode):
+    """eta = 1, eps = 0: whatever the decay, each write meets S_t^T k_t = v_t,
+    so reading with q_t = k_t returns v_t."""
+    rng = np.random.default_rng(33)
+    L, H, dk, dv = 30, 2, 7, 5
+    _, k, v, _, _ = _rand_seq(rng, L, H, dk, dv)
+    a = _rand_ch(rng, L, H, dk)
+    S0 = rng.standard_normal((1, H, dk, dv))
+    o, _ = fwd(k, k, v, a, np.ones((L, H)), eps=0.0, initial_state=S0, channel_decay=True)
+    assert rel(o, v) < TIGHT, rel(o, v)
+
+
+def pin_channel_min_norm_bruteforce(fwd, decode):
+    """Each write is the least-norm change of the channel-decayed state
+    Diag(a_t) S_{t-1} that meets S^T k = v (relaxed by eta |k|^2/(|k|^2+eps)),
+    solved with lstsq on the Kronecker constraint."""
+    rng = np.random.default_rng(34)
+    L, dk, dv, eps = 6, 4, 3, 0.2
+    q, k, v, _, eta = _rand_seq(rng, L, 1, dk, dv)
+    a = _rand_ch(rng, L, 1, dk)
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, S_fin = fwd(q, k, v, a, eta, eps=eps, initial_state=S0, channel_decay=True)
+    S = S0[0, 0].copy()
+    for t in range(L):
+        kt, vt = k[t, 0], v[t, 0]
+        St = a[t, 0][:, None] * S
+        Cmat = np.kron(np.eye(dv), kt[None, :])
+        r = vt - Cmat @ St.reshape(-1, order="F")
+        x = np.linalg.lstsq(Cmat, r, rcond=None)[0]
+        kk = float(kt @ kt)
+        S = St + (eta[t, 0] * kk / (kk + eps)) * x.reshape(dk, dv, order="F")
+        assert rel(o[t, 0], S.T @ q[t, 0]) < 1e-11
+    assert rel(S_fin[0, 0], S) < 1e-11
+
+
+def pin_channel_untouched_channel(fwd, decode):
+    """A key channel that no key and no query ever uses only decays: its row
+    of the final state is (prod_t a_t[c]) S0[c], and the outputs do not
+    depend on that channel's rates."""
+    rng = np.random.default_rng(35)
+    L, H, dk, dv, c = 19, 2, 5, 5, 2
+    q, k, v, _, eta = _rand_seq(rng, L, H, dk, dv)
+    q[:, :, c] = 0.0
+    k[:, :, c] = 0.0
+    a = _rand_ch(rng, L, H, dk)
+    S0 = rng.standard_normal((1, H, dk, dv))
+    o, S = fwd(q, k, v, a, eta, eps=1e-3, initial_state=S0, channel_decay=True)
+    assert rel(S[0, :, c], np.prod(a[:, :, c], axis=0)[:, None] * S0[0, :, c]) < TIGHT
+    a2 = a.copy()
+    a2[:, :, c] = rng.uniform(0.3, 1.0, (L, H))
+    o2, S2 = fwd(q, k, v, a2, eta, eps=1e-3, initial_state=S0, channel_decay=True)
+    assert rel(o2, o) < TIGHT
+    others = [i for i in range(dk) if i != c]
+    assert rel(S2[0][:, others], S[0][:, others]) < TIGHT
+
+
+def pin_channel_chunk_form(fwd, decode):
+    """The chunk form with per-channel decay factors (direct, and factored
+    per block of 16 rows as the GPU kernel forms it) gives the sequential
+    result for every chunk size, ragged last chunks included."""
+    rng = np.random.default_rng(36)
+    H, dk, dv = 2, 6, 5
+    cu = np.array([0, 1, 17, 80, 143])
+    L = int(cu[-1])
+    q, k, v, _, eta = _rand_seq(rng, L, H, dk, dv)
+    a = _rand_ch(rng, L, H, dk, amin=0.5)
+    S0 = rng.standard_normal((len(cu) - 1, H, dk, dv))
+    o, S = fwd(q, k, v, a, eta, cu_seqlens=cu, eps=1e-3, initial_state=S0, channel_decay=True)
+    for C in (1, 7, 16, 64):
+        for fac in (False, True):
+            oc, Sc = chunked_ch(q, k, v, a, eta, cu, 1e-3, C, S0, factored=fac)
+            assert rel(o, oc) < 1e-10 and rel(S, Sc) < 1e-10, (C, fac, rel(o, oc), rel(S, Sc))
+
+
+def pin_channel_decode_is_one_token(fwd, decode):
+    """A per-channel decode step after a prefill equals the prefill that is
+    one token longer."""
+    rng = np.random.default_rng(37)
+    L, H, dk, dv = 11, 3, 6, 4
+    q, k, v, _, eta = _rand_seq(rng, L + 1, H, dk, dv)
+    a = _rand_ch(rng, L + 1, H, dk)
+    _, S = fwd(q[:L], k[:L], v[:L], a[:L], eta[:L], eps=1e-4, channel_decay=True)
+    od, Sd = decode(q[L:], k[L:], v[L:], a[L:], eta[L:], S, eps=1e-4, channel_decay=True)
+    o_all, S_all = fwd(q, k, v, a, eta, eps=1e-4, channel_decay=True)
+    assert rel(od[0], o_all[L]) < TIGHT
+    assert rel(Sd, S_all) < TIGHT
+
 ALL_PINS = [pin_worked_example, pin_orthogonal_projection, pin_min_norm_bruteforce,
             pin_exact_line_search, pin_normalised_gradient, pin_exact_recall, pin_eta_zero,
             pin_scalar_case, pin_gated_deltanet_form, pin_chunk_form, pin_packed_and_resume,
             pin_decode_is_one_token, pin_zero_key, pin_direct_step_product_form,
             pin_no_alpha_is_unit_decay, pin_direct_equals_kaczmarz_on_unit_keys,
-            pin_deltanet_exact_recall, pin_segment_map_is_affine]
+            pin_deltanet_exact_recall, pin_segment_map_is_affine,
+            pin_channel_uniform_is_scalar, pin_channel_eta_zero,
+            pin_channel_orthogonal_projection, pin_channel_min_norm_bruteforce,
+            pin_channel_untouched_channel, pin_channel_chunk_form,
+            pin_channel_decode_is_one_token]

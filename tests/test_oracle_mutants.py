@@ -61,6 +61,36 @@ MUTANTS = {
                     "    for (int i = 0; i < dk; ++i)\n        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= alpha;\n    /* o = S^T q */\n"),
 }
 
+CH_DECAY = ("    /* S~ = Diag(a) S: row i (key channel i) decays by a[i] */\n"
+            "    for (int i = 0; i < dk; ++i)\n"
+            "        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a[i];\n")
+CH_WRITE = "    /* S = S~ + beta k e^T */\n    for (int i = 0; i < dk; ++i) {\n        const double bk = beta * k[i];"
+
+
+def _ch_residual_before_decay(src):
+    """Per-channel path: the residual reads the undecayed state."""
+    a = src.index(CH_DECAY)
+    src = src[:a] + src[a + len(CH_DECAY):]
+    b = src.index(CH_WRITE, a)
+    return src[:b] + CH_DECAY + src[b:]
+
+
+MUTANTS.update({
+    "ch_decays_columns": lambda s: s.replace("S[(size_t)i * dv + j] *= a[i];",
+                                             "S[(size_t)i * dv + j] *= a[j];"),
+    "ch_first_channel_only": lambda s: s.replace("S[(size_t)i * dv + j] *= a[i];",
+                                                 "S[(size_t)i * dv + j] *= a[0];"),
+    "ch_no_decay": lambda s: s.replace("S[(size_t)i * dv + j] *= a[i];", "(void)a;"),
+    "ch_residual_before_decay": _ch_residual_before_decay,
+    "ch_fwd_scalar_stride": lambda s: s.replace("alpha + th * dk,", "alpha + th,"),
+    "ch_decode_scalar_stride": lambda s: s.replace("alpha + sh * dk, eta[sh]", "alpha + sh, eta[sh]"),
+    "ch_fwd_ignores_direct": lambda s: s.replace(
+        "eta[th], eps, beta_direct, dk, dv, o + th * dv);\n            }\n            if (final_state) memcpy(final_state + sh * sdim, S, sizeof(double) * sdim);\n            free(S);\n        }\n    }\n    return failed ? -1 : 0;\n}\n\n/* One decode step with the per-channel",
+        "eta[th], eps, 0, dk, dv, o + th * dv);\n            }\n            if (final_state) memcpy(final_state + sh * sdim, S, sizeof(double) * sdim);\n            free(S);\n        }\n    }\n    return failed ? -1 : 0;\n}\n\n/* One decode step with the per-channel"),
+    "ch_decode_drops_direct": lambda s: s.replace("alpha + sh * dk, eta[sh], eps, beta_direct",
+                                                  "alpha + sh * dk, eta[sh], eps, 0"),
+})
+
 RUNNER = textwrap.dedent("""
     import sys, functools
     sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})

@@ -22,6 +22,12 @@ alpha and eta stay fp32.  eps = 1e-6 and the start state is zero.  Blocks
 are independent streams, so they are drawn in parallel and the values do
 not depend on the thread count.
 
+Per-channel decay (channel_decay=True, the Kimi Delta Attention gate): a
+separate seed sequence SeedSequence([seed, 0x4B4441]) gives, per block of
+BLOCK tokens, alpha_ch = sigmoid(alpha_mu + N(0, 1)) fp32 [tb, H, dk], one
+decay per key channel (decode step i: SeedSequence([seed, 0x4B4441, i]),
+one block of N tokens).  The other tensors are drawn exactly as above.
+
 Decode: ss.spawn(2) gives a state stream and a step stream.  The state is
 0.02 * N(0, 1) fp32 [N, H, dk, dv], drawn per sequence from
 PCG64(state_ss.spawn(N)[s]); step i draws one block of N tokens (as above)
@@ -105,15 +111,36 @@ def _tokens(seed_seqs, tok, H, dk, dv, dtype, alpha_mu, big_frac=0.0, big_scale=
     return q, k, v, alpha, eta
 
 
+_CH_TAG = 0x4B4441  # second entropy word of the per-channel gate stream
+
+
+def _channel_gates(seed, tok, H, dk, alpha_mu, step=None):
+    """alpha_ch = sigmoid(alpha_mu + N(0, 1)) fp32 [tok, H, dk], per block."""
+    words = [seed, _CH_TAG] if step is None else [seed, _CH_TAG, step]
+    nb = max(1, -(-tok // BLOCK))
+    seqs = np.random.SeedSequence(words).spawn(nb)
+    out = torch.empty((tok, H, dk), dtype=torch.float32)
+
+    def one(b):
+        a0 = b * BLOCK
+        tb = min(BLOCK, tok - a0)
+        rng = np.random.Generator(np.random.PCG64(seqs[b]))
+        x = rng.standard_normal((tb, H, dk), dtype=np.float32)
+        out[a0:a0 + tb] = torch.from_numpy(_sigmoid(np.float32(alpha_mu) + x))
+
+    list(_pool().map(one, range(nb)))
+    return out
+
+
 def prefill(name=None, *, seed=0, n_seqs=None, T=None, lengths=None, H=None, d=None, dtype=None,
-            alpha_mu=None, big_frac=None, big_scale=None):
+            alpha_mu=None, big_frac=None, big_scale=None, channel_decay=False):
     """Inputs of a named prefill workload, or of a custom one.
 
     `lengths` is either a (lo, hi) pair (drawn per sequence) or an explicit
     list of per-sequence lengths.  Returns a dict of CPU tensors:
     q, k, v [tok, H, d] (bf16 or fp32), alpha, eta [tok, H] fp32,
     cu_seqlens int32 [n+1] (None for equal-length batches), n_seqs,
-    lengths (list), eps.
+    lengths (list), eps; with channel_decay also alpha_ch [tok, H, d] fp32.
     """
     p = dict(PREFILL[name]) if name else {}
     for key, val in (("n_seqs", n_seqs), ("T", T), ("lengths", lengths), ("H", H), ("d", d),
@@ -137,13 +164,17 @@ def prefill(name=None, *, seed=0, n_seqs=None, T=None, lengths=None, H=None, d=N
                                   p.get("alpha_mu", 3.0), p.get("big_frac", 0.0),
                                   p.get("big_scale", 10.0))
     cu = None if dense else torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
-    return dict(q=q, k=k, v=v, alpha=alpha, eta=eta, cu_seqlens=cu, n_seqs=len(lens),
-                lengths=lens, eps=EPS, H=p["H"], d=p["d"], dtype=p["dtype"])
+    out = dict(q=q, k=k, v=v, alpha=alpha, eta=eta, cu_seqlens=cu, n_seqs=len(lens),
+               lengths=lens, eps=EPS, H=p["H"], d=p["d"], dtype=p["dtype"])
+    if channel_decay:
+        out["alpha_ch"] = _channel_gates(seed, tok, p["H"], p["d"], p.get("alpha_mu", 3.0))
+    return out
 
 
 def decode(*, seed=0, n_seqs=None, H=None, d=None, steps=None, dtype=None, alpha_mu=None,
-           state_std=None):
-    """Decode workload: dict(state fp32 [N,H,d,d], steps=[dict(q,k,v,alpha,eta)], eps)."""
+           state_std=None, channel_decay=False):
+    """Decode workload: dict(state fp32 [N,H,d,d], steps=[dict(q,k,v,alpha,eta)], eps);
+    with channel_decay every step also holds alpha_ch [N, H, d] fp32."""
     p = dict(DECODE)
     for key, val in (("n_seqs", n_seqs), ("H", H), ("d", d), ("steps", steps), ("dtype", dtype),
                      ("alpha_mu", alpha_mu), ("state_std", state_std)):
@@ -162,8 +193,11 @@ def decode(*, seed=0, n_seqs=None, H=None, d=None, steps=None, dtype=None, alpha
 
     list(_pool().map(one_seq, enumerate(state_ss.spawn(N))))
     out = []
-    for sq in step_ss.spawn(p["steps"]):
+    for i, sq in enumerate(step_ss.spawn(p["steps"])):
         q, k, v, alpha, eta = _tokens([sq], N, Hh, dd, dd, p["dtype"], p["alpha_mu"])
-        out.append(dict(q=q, k=k, v=v, alpha=alpha, eta=eta))
+        st = dict(q=q, k=k, v=v, alpha=alpha, eta=eta)
+        if channel_decay:
+            st["alpha_ch"] = _channel_gates(seed, N, Hh, dd, p["alpha_mu"], step=i)
+        out.append(st)
     return dict(state=state, steps=out, eps=EPS, n_seqs=N, H=Hh, d=dd,
                 dtype=p["dtype"])
