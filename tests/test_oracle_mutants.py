@@ -28,37 +28,44 @@ def _swap_write_and_read(src):
     return src[:a] + read_blk + write_blk + src[end:]
 
 
+def _first(s, old, new):
+    """Replace the first occurrence: the scalar step precedes the per-channel one."""
+    return s.replace(old, new, 1)
+
+
 MUTANTS = {
-    "no_decay": lambda s: s.replace("S[(size_t)i * dv + j] *= alpha;", "(void)alpha;"),
-    "beta_unnormalised": lambda s: s.replace("eta / (kk + eps)", "eta"),
-    "beta_norm_not_squared": lambda s: s.replace("eta / (kk + eps)", "eta / (__builtin_sqrt(kk) + eps)"),
-    "beta_drops_eps": lambda s: s.replace("eta / (kk + eps)", "eta / kk"),
-    "beta_times_alpha": lambda s: s.replace("eta / (kk + eps)", "alpha * eta / (kk + eps)"),
-    "residual_sign": lambda s: s.replace("e[j] -= S[(size_t)i * dv + j] * k[i];",
+    "no_decay": lambda s: _first(s, "S[(size_t)i * dv + j] *= alpha;", "(void)alpha;"),
+    "beta_unnormalised": lambda s: _first(s, "eta / (kk + eps)", "eta"),
+    "beta_norm_not_squared": lambda s: _first(s, "eta / (kk + eps)", "eta / (__builtin_sqrt(kk) + eps)"),
+    "beta_drops_eps": lambda s: _first(s, "eta / (kk + eps)", "eta / kk"),
+    "beta_times_alpha": lambda s: _first(s, "eta / (kk + eps)", "alpha * eta / (kk + eps)"),
+    "residual_sign": lambda s: _first(s, "e[j] -= S[(size_t)i * dv + j] * k[i];",
                                          "e[j] += S[(size_t)i * dv + j] * k[i];"),
-    "residual_undecayed": lambda s: s.replace("e[j] -= S[(size_t)i * dv + j] * k[i];",
+    "residual_undecayed": lambda s: _first(s, "e[j] -= S[(size_t)i * dv + j] * k[i];",
                                               "e[j] -= S[(size_t)i * dv + j] * k[i] / alpha;"),
-    "write_uses_v": lambda s: s.replace("S[(size_t)i * dv + j] += bk * e[j];",
+    "write_uses_v": lambda s: _first(s, "S[(size_t)i * dv + j] += bk * e[j];",
                                         "S[(size_t)i * dv + j] += bk * v[j];"),
-    "read_with_key": lambda s: s.replace("o[j] += S[(size_t)i * dv + j] * q[i];",
+    "read_with_key": lambda s: _first(s, "o[j] += S[(size_t)i * dv + j] * q[i];",
                                          "o[j] += S[(size_t)i * dv + j] * k[i];"),
     "read_before_write": _swap_write_and_read,
-    "ignores_initial_state": lambda s: s.replace("if (initial_state)\n", "if (0)\n"),
-    "decode_swaps_q_and_k": lambda s: s.replace(
+    "ignores_initial_state": lambda s: _first(s, "if (initial_state)\n", "if (0)\n"),
+    "decode_swaps_q_and_k": lambda s: _first(s, 
         "kla_token(state + sh * sdim, e, q + sh * dk, k + sh * dk,",
         "kla_token(state + sh * sdim, e, k + sh * dk, q + sh * dk,"),
-    "drops_last_token": lambda s: s.replace("t < cu_seqlens[s + 1]; ++t", "t + 1 < cu_seqlens[s + 1]; ++t"),
-    "direct_mode_ignored": lambda s: s.replace("beta_direct ? eta : eta / (kk + eps)",
+    "drops_last_token": lambda s: _first(s, "t < cu_seqlens[s + 1]; ++t", "t + 1 < cu_seqlens[s + 1]; ++t"),
+    "direct_mode_ignored": lambda s: _first(s, "beta_direct ? eta : eta / (kk + eps)",
                                                "eta / (kk + eps)"),
-    "missing_alpha_is_zero": lambda s: s.replace("alpha ? alpha[th] : 1.0", "alpha ? alpha[th] : 0.0"),
-    "decode_missing_alpha_is_zero": lambda s: s.replace("alpha ? alpha[sh] : 1.0",
+    "missing_alpha_is_zero": lambda s: _first(s, "alpha ? alpha[th] : 1.0", "alpha ? alpha[th] : 0.0"),
+    "decode_missing_alpha_is_zero": lambda s: _first(s, "alpha ? alpha[sh] : 1.0",
                                                         "alpha ? alpha[sh] : 0.0"),
-    "decode_drops_direct_mode": lambda s: s.replace("eps, beta_direct, dk, dv, o + sh * dv",
+    "decode_drops_direct_mode": lambda s: _first(s, "eps, beta_direct, dk, dv, o + sh * dv",
                                                     "eps, 0, dk, dv, o + sh * dv"),
-    "decay_after_write": lambda s: s.replace(
+    "decay_after_write": lambda s: _first(_first(
+        s,
         "    for (int i = 0; i < dk; ++i)\n        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= alpha;\n",
-        "").replace("    /* o = S^T q */\n",
-                    "    for (int i = 0; i < dk; ++i)\n        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= alpha;\n    /* o = S^T q */\n"),
+        ""),
+        "    /* o = S^T q */\n",
+        "    for (int i = 0; i < dk; ++i)\n        for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= alpha;\n    /* o = S^T q */\n"),
 }
 
 CH_DECAY = ("    /* S~ = Diag(a) S: row i (key channel i) decays by a[i] */\n"
