@@ -63,7 +63,8 @@ kla_status fwd_impl(const void *q, const void *k, const void *v, const float *al
                     int64_t total_tok, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
                     float eps, kla_dtype dtype, kla_beta_mode beta_mode, int32_t n_splits,
                     const float *initial_state, float *o, float *final_state,
-                    void *workspace, size_t workspace_bytes, void *stream) {
+                    void *workspace, size_t workspace_bytes, void *stream,
+                    bool channel_decay = false) {
   if (n_seqs <= 0 || H <= 0 || total_tok < 0 || !std::isfinite(eps) || eps < 0.f)
     return KLA_ERR_INVALID_ARG;
   if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT) return KLA_ERR_INVALID_ARG;
@@ -71,6 +72,7 @@ kla_status fwd_impl(const void *q, const void *k, const void *v, const float *al
   if (!supported_dim(dk, dv) || chunk != 64) return KLA_ERR_UNSUPPORTED;
   if (!cu_seqlens && total_tok % n_seqs != 0) return KLA_ERR_INVALID_ARG;
   if (n_splits < 1 || n_splits > kla_max_splits) return KLA_ERR_INVALID_ARG;
+  if (channel_decay && n_splits != 1) return KLA_ERR_UNSUPPORTED;
   const size_t ws_need = n_splits > 1
       ? kla_fwd_chunked_split_workspace_size(n_seqs, H, dk, dv, n_splits)
       : kla_fwd_chunked_workspace_size(n_seqs, total_tok, H, dk, dv, chunk);
@@ -78,14 +80,16 @@ kla_status fwd_impl(const void *q, const void *k, const void *v, const float *al
   if (ws_need > 0 && (!workspace || !aligned16(workspace))) return KLA_ERR_INVALID_ARG;
   const bool have_tokens = total_tok > 0;
   if (have_tokens && (!q || !k || !v || !eta || !o)) return KLA_ERR_INVALID_ARG;
+  if (have_tokens && channel_decay && !alpha) return KLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-      !aligned16(initial_state) || !aligned16(final_state))
+      !aligned16(initial_state) || !aligned16(final_state) || (channel_decay && !aligned16(alpha)))
     return KLA_ERR_INVALID_ARG;
 
   const int64_t esz = dtype == KLA_BF16 ? 2 : 4;
   const int64_t th = total_tok * H;
   const Range rq = range(q, th * dk * esz), rk = range(k, th * dk * esz),
-              rv = range(v, th * dv * esz), ra = range(alpha, alpha ? th * 4 : 0), re = range(eta, th * 4),
+              rv = range(v, th * dv * esz),
+              ra = range(alpha, alpha ? th * 4 * (channel_decay ? dk : 1) : 0), re = range(eta, th * 4),
               ro = range(o, th * dv * 4),
               rcu = range(cu_seqlens, cu_seqlens ? (int64_t)(n_seqs + 1) * 4 : 0),
               rs0 = range(initial_state, initial_state ? (int64_t)n_seqs * H * dk * dv * 4 : 0),
@@ -119,6 +123,8 @@ kla_status fwd_impl(const void *q, const void *k, const void *v, const float *al
   a.o = o;
   a.final_state = final_state;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (channel_decay)
+    return kla::launch_prefill_kda(a, dtype == KLA_BF16, st) == hipSuccess ? KLA_OK : KLA_ERR_HIP;
   auto run = [&]() {
     return dtype == KLA_BF16 ? kla::launch_prefill_bf16(a, st) : kla::launch_prefill_f32(a, st);
   };
@@ -177,21 +183,37 @@ kla_status kla_fwd_chunked(const void *q, const void *k, const void *v, const fl
                             workspace, workspace_bytes, stream);
 }
 
-kla_status kla_decode_step_ex(const void *q, const void *k, const void *v, const float *alpha,
-                              const float *eta, float *state, float *o, int32_t n_seqs, int32_t H,
-                              int32_t dk, int32_t dv, float eps, kla_dtype dtype,
-                              kla_beta_mode beta_mode, void *stream) {
+kla_status kla_fwd_chunked_kda(const void *q, const void *k, const void *v, const float *alpha,
+                               const float *eta, const int32_t *cu_seqlens, int32_t n_seqs,
+                               int64_t total_tok, int32_t H, int32_t dk, int32_t dv,
+                               int32_t chunk, float eps, kla_dtype dtype,
+                               kla_beta_mode beta_mode, const float *initial_state, float *o,
+                               float *final_state, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  return fwd_impl(q, k, v, alpha, eta, cu_seqlens, n_seqs, total_tok, H, dk, dv, chunk, eps, dtype,
+                  beta_mode, 1, initial_state, o, final_state, workspace, workspace_bytes, stream,
+                  true);
+}
+
+namespace {
+kla_status decode_impl(const void *q, const void *k, const void *v, const float *alpha,
+                       const float *eta, float *state, float *o, int32_t n_seqs, int32_t H,
+                       int32_t dk, int32_t dv, float eps, kla_dtype dtype,
+                       kla_beta_mode beta_mode, void *stream, bool channel_decay) {
   if (n_seqs <= 0 || H <= 0 || !std::isfinite(eps) || eps < 0.f) return KLA_ERR_INVALID_ARG;
   if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT) return KLA_ERR_INVALID_ARG;
   if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
   if (!supported_dim(dk, dv)) return KLA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !eta || !state || !o) return KLA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o))
+  if (channel_decay && !alpha) return KLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o) ||
+      (channel_decay && !aligned16(alpha)))
     return KLA_ERR_INVALID_ARG;
   const int64_t esz = dtype == KLA_BF16 ? 2 : 4;
   const int64_t nh = (int64_t)n_seqs * H;
   const Range rq = range(q, nh * dk * esz), rk = range(k, nh * dk * esz),
-              rv = range(v, nh * dv * esz), ra = range(alpha, alpha ? nh * 4 : 0), re = range(eta, nh * 4),
+              rv = range(v, nh * dv * esz),
+              ra = range(alpha, alpha ? nh * 4 * (channel_decay ? dk : 1) : 0), re = range(eta, nh * 4),
               rs = range(state, nh * dk * dv * 4), ro = range(o, nh * dv * 4);
   for (const Range &in : {rq, rk, rv, ra, re, rs})
     if (overlap(ro, in)) return KLA_ERR_INVALID_ARG;
@@ -211,10 +233,28 @@ kla_status kla_decode_step_ex(const void *q, const void *k, const void *v, const
   a.D = dk;
   a.eps = eps;
   a.beta_direct = beta_mode == KLA_BETA_DIRECT;
+  a.channel_decay = channel_decay;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e =
       dtype == KLA_BF16 ? kla::launch_decode_bf16(a, st) : kla::launch_decode_f32(a, st);
   return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
+}
+}  // namespace
+
+kla_status kla_decode_step_ex(const void *q, const void *k, const void *v, const float *alpha,
+                              const float *eta, float *state, float *o, int32_t n_seqs, int32_t H,
+                              int32_t dk, int32_t dv, float eps, kla_dtype dtype,
+                              kla_beta_mode beta_mode, void *stream) {
+  return decode_impl(q, k, v, alpha, eta, state, o, n_seqs, H, dk, dv, eps, dtype, beta_mode,
+                     stream, false);
+}
+
+kla_status kla_decode_step_kda(const void *q, const void *k, const void *v, const float *alpha,
+                               const float *eta, float *state, float *o, int32_t n_seqs,
+                               int32_t H, int32_t dk, int32_t dv, float eps, kla_dtype dtype,
+                               kla_beta_mode beta_mode, void *stream) {
+  return decode_impl(q, k, v, alpha, eta, state, o, n_seqs, H, dk, dv, eps, dtype, beta_mode,
+                     stream, true);
 }
 
 kla_status kla_decode_step(const void *q, const void *k, const void *v, const float *alpha,

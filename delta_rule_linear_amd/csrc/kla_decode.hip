@@ -11,7 +11,11 @@
 // With beta_direct the step is beta = eta, the learned scalar of Gated
 // DeltaNet that KLA replaces (same summary, introduction); without alpha the
 // decay is 1 (DeltaNet, "Linear Attention Architectures: Mechanisms,
-// Trade-offs, and Cross-Layer Routing", section "Notacao Unificada").
+// Trade-offs, and Cross-Layer Routing", section "Notacao Unificada").  With
+// the per-channel decay of Kimi Delta Attention (same page, section
+// "Metodologia e Estrutura") row r of the state decays by a[r]:
+//   x = S^T (a o k),  y = S^T (a o q),  e = v - x,  o = y + beta (k.q) e,
+//   S_new = Diag(a) S + beta k e^T.
 // The kernel is bound by HBM bandwidth (0.75 flop/byte): one workgroup per
 // (sequence, head), each thread holds RPT rows x 4 columns of the state in
 // registers between the read and the write.
@@ -28,7 +32,7 @@ constexpr int kThreads = 256;
 __device__ inline float to_f32(float x) { return x; }
 __device__ inline float to_f32(__bf16 x) { return static_cast<float>(x); }
 
-template <typename E, int D>
+template <typename E, int D, bool CH>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ eta, float *__restrict__ state,
@@ -38,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   constexpr int RPT = D / NRG;           // rows per thread
   static_assert(NQ * NRG == kThreads && RPT * NRG == D, "decode tiling");
 
-  __shared__ float sq[D], sk[D], sv[D], se[D];
+  __shared__ float sq[D], sk[D], sv[D], se[D], sa[CH ? D : 1];
   __shared__ float px[NRG][D], py[NRG][D];
 
   const int64_t sh = blockIdx.x;  // (sequence, head) pair
@@ -56,8 +60,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     sq[t] = to_f32(q[sh * D + t]);
     sk[t] = to_f32(k[sh * D + t]);
     sv[t] = to_f32(v[sh * D + t]);
+    if constexpr (CH) sa[t] = alpha[sh * D + t];
   }
-  const float a = alpha ? alpha[sh] : 1.f;
+  const float a = CH ? 1.f : (alpha ? alpha[sh] : 1.f);  // scalar decay (CH: per row below)
   const float et = eta[sh];
   __syncthreads();
 
@@ -81,7 +86,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   float4 xs = {0.f, 0.f, 0.f, 0.f}, ys = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const float kr = sk[rg + NRG * i], qr = sq[rg + NRG * i];
+    const float ar = CH ? sa[rg + NRG * i] : 1.f;
+    const float kr = ar * sk[rg + NRG * i], qr = ar * sq[rg + NRG * i];
     xs.x += s[i].x * kr; xs.y += s[i].y * kr; xs.z += s[i].z * kr; xs.w += s[i].w * kr;
     ys.x += s[i].x * qr; ys.y += s[i].y * qr; ys.z += s[i].z * qr; ys.w += s[i].w * qr;
   }
@@ -106,11 +112,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const float bk = beta * sk[rg + NRG * i];
+    const float ar = CH ? sa[rg + NRG * i] : a;
     float4 r;
-    r.x = a * s[i].x + bk * e4.x;
-    r.y = a * s[i].y + bk * e4.y;
-    r.z = a * s[i].z + bk * e4.z;
-    r.w = a * s[i].w + bk * e4.w;
+    r.x = ar * s[i].x + bk * e4.x;
+    r.y = ar * s[i].y + bk * e4.y;
+    r.z = ar * s[i].z + bk * e4.z;
+    r.w = ar * s[i].w + bk * e4.w;
     *reinterpret_cast<float4 *>(Sg + (rg + NRG * i) * D + 4 * cq) = r;
   }
 }
@@ -120,12 +127,10 @@ hipError_t launch(const DecodeArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)((int64_t)a.n_seqs * a.H)), block(kThreads);
   const E *q = static_cast<const E *>(a.q), *k = static_cast<const E *>(a.k),
           *v = static_cast<const E *>(a.v);
-  if (a.D == 128)
-    hipLaunchKernelGGL((decode_kernel<E, 128>), grid, block, 0, st, q, k, v, a.alpha, a.eta,
-                       a.state, a.o, a.eps, a.beta_direct);
-  else
-    hipLaunchKernelGGL((decode_kernel<E, 64>), grid, block, 0, st, q, k, v, a.alpha, a.eta,
-                       a.state, a.o, a.eps, a.beta_direct);
+  auto kern = a.D == 128 ? (a.channel_decay ? decode_kernel<E, 128, true> : decode_kernel<E, 128, false>)
+                        : (a.channel_decay ? decode_kernel<E, 64, true> : decode_kernel<E, 64, false>);
+  hipLaunchKernelGGL(kern, grid, block, 0, st, q, k, v, a.alpha, a.eta, a.state, a.o, a.eps,
+                     a.beta_direct);
   return hipGetLastError();
 }
 

@@ -1,0 +1,169 @@
+// Device helpers shared by the prefill kernels (kla_prefill.hip and
+// kla_kda.hip): vector types, MFMA wrappers, LDS-only barriers, DPP lane
+// movement and wave scans, range-checked buffer access, the XCD-aware
+// workgroup order, the DPP forward-substitution step and the numbering of
+// the off-diagonal Gram jobs.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+namespace kla {
+namespace {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int C = 64;             // chunk length
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int DVB = 16 * kWaves;  // dv columns per workgroup
+
+__device__ inline f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x4 mma(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x4 mma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Workgroup barrier that orders LDS traffic only.  __syncthreads() also
+// waits for every outstanding global load, which would expose the latency of
+// the next chunk's prefetch at each barrier.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Hardware base-2 exponential and logarithm (v_exp_f32, v_log_f32, about
+// 1 ulp).  Decay factors are 2^x with x <= 0; results below the normal range
+// flush to zero, which is exact to the precision of the outputs.
+__device__ inline float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float flog2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Keep the instruction scheduler from moving code across this point; used to
+// hold software-pipelined LDS loads ahead of the MFMAs that consume them.
+__device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// DPP lane movement within 16-lane rows (gfx9 controls plus row_share).
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Same, but lanes whose source is outside the row (or rows masked off by
+// ROWS) read zero.
+template <int CTRL, int ROWS = 0xF>
+__device__ inline float dpp0(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;       // quad_perm [1,0,3,2], [2,3,0,1]
+constexpr int kHalfMirror = 0x141, kRowRor4 = 0x124, kRowRor8 = 0x128;
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// Sum over aligned groups of N lanes (N = 8, 16 or 32); every lane gets it.
+template <int N>
+__device__ inline float group_sum(float x) {
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  if constexpr (N == 8) {
+    x += dpp<kHalfMirror>(x);
+  } else {
+    x += dpp<kRowRor4>(x);
+    x += dpp<kRowRor8>(x);
+  }
+  if constexpr (N == 32) x += __shfl_xor(x, 16, 64);
+  return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ inline float wave_scan(float x) {
+  x += dpp0<kRowShr1>(x);
+  x += dpp0<kRowShr2>(x);
+  x += dpp0<kRowShr4>(x);
+  x += dpp0<kRowShr8>(x);
+  x += dpp0<kRowBcast15, 0xA>(x);  // rows 1, 3 add the last lane of rows 0, 2
+  x += dpp0<kRowBcast31, 0xC>(x);  // rows 2, 3 add lane 31
+  return x;
+}
+
+// Range-checked buffer access: a load past the descriptor's byte range
+// returns zero and a store past it is dropped, so ragged chunk tails and
+// absent states need no branches (and no conservative waits on the memory
+// counter around them).  Word 3 selects the 32-bit raw data format.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline rsrc_t make_rsrc(const void *base, int64_t bytes) {
+  const int64_t b = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)(uint32_t)b, 0x00020000);
+}
+__device__ inline uint4 buf_ld16(rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return uint4{v.x, v.y, v.z, v.w};
+}
+__device__ inline float buf_ld4(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ inline void buf_st16(rsrc_t r, uint32_t off, f32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)off, 0, 0);
+}
+__device__ inline void buf_st4(rsrc_t r, uint32_t off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)off, 0, 0);
+}
+
+// XCD-aware workgroup order: consecutive logical ids land on one XCD so the
+// dv-blocks of one (sequence, head) share that XCD's L2.  Bijective for any
+// grid size, whatever the hardware dispatch order.
+__device__ inline int64_t logical_block() {
+  const int64_t G = gridDim.x, i = blockIdx.x;
+  const int64_t q = G / 8, r = G % 8, x = i % 8, kx = i / 8;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + kx;
+}
+
+// One column step of the 16x16 unit-lower-triangular substitution:
+// x[r] += (-L[r][t]) x[t] for r > t, one v_fmac_f32_dpp per row whose first
+// factor is broadcast from lane t of the 16-lane row.  lc holds -L and comes
+// straight from LDS, so no VALU write precedes its DPP read.
+template <int T>
+__device__ inline void solve_step(float (&x)[16], const float (&lc)[16]) {
+#pragma unroll
+  for (int r = T + 1; r < 16; ++r)
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(x[r]) : "v"(lc[r]), "v"(x[T]), "n"(T));
+}
+template <int... T>
+__device__ inline void solve_steps(float (&x)[16], const float (&lc)[16],
+                                   std::integer_sequence<int, T...>) {
+  (solve_step<T>(x, lc), ...);
+}
+
+// Gram jobs of waves 1-3, numbered 0..15: jobs 0-5 are the K K^T blocks
+// below the diagonal (-> -Ahat), in row order (1,0) (2,0) (2,1) (3,0) (3,1)
+// (3,2); jobs 6-15 are the Q K^T blocks on or below the diagonal (-> M), in
+// row order (0,0) (1,0) (1,1) (2,0) ... (3,3).  Decoded with scalar
+// arithmetic from a wave-uniform job number.
+struct Job {
+  bool qk;
+  int bi, bj;
+};
+__device__ inline Job job_of(int qj) {
+  Job jb;
+  jb.qk = qj >= 6;
+  if (!jb.qk) {
+    jb.bi = 1 + (qj >= 1) + (qj >= 3);
+    jb.bj = qj - (jb.bi - 1) * jb.bi / 2;
+  } else {
+    const int p = qj - 6;
+    jb.bi = (p >= 1) + (p >= 3) + (p >= 6);
+    jb.bj = p - jb.bi * (jb.bi + 1) / 2;
+  }
+  return jb;
+}
+
+}  // namespace
+}  // namespace kla

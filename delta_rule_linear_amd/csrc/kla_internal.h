@@ -32,6 +32,7 @@ struct DecodeArgs {
   int32_t n_seqs, H, D;
   float eps;
   int beta_direct;            // 1: beta = eta; 0: beta = eta / (|k|^2 + eps)
+  int channel_decay = 0;      // 1: alpha [n_seqs, H, D], one decay per key channel
 };
 
 // Each returns the HIP status of the launch.
@@ -44,5 +45,7 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_split_identity(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_split_scan(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
+// Per-channel decay prefill (alpha [total_tok, H, D]); whole sequences only.
+hipError_t launch_prefill_kda(const PrefillArgs &a, bool bf16_inputs, hipStream_t s);
 
 }  // namespace kla

@@ -1,0 +1,474 @@
+// KLA prefill with a per-channel decay (Kimi Delta Attention's gate) for
+// gfx950.
+//
+// The linear-attention survey page ("Linear Attention Architectures:
+// Mechanisms, Trade-offs, and Cross-Layer Routing", section "Metodologia e
+// Estrutura") describes Kimi Delta Attention's decay as a vector with one
+// rate per feature channel.  The state's rows are the key channels, so the
+// decayed state is S~ = Diag(a_t) S_{t-1}; the residual, the KLA step
+// beta_t = eta_t / (|k_t|^2 + eps) (or beta_t = eta_t) and the write are
+// those of the scalar kernels (KLA technical summary, "Resumo Tecnico:
+// Atencao Linear Kaczmarz (KLA)", sections "A Regra de Atualizacao KLA" and
+// "Implementacao").
+//
+// Chunk form.  Inside a chunk of n <= 64 tokens let G_t be the cumulative
+// log2-decay vector (one entry per key channel).  Every scalar decay factor
+// of the chunk solver becomes a per-channel one:
+//   Ahat_ts = sum_i k_t[i] k_s[i] 2^{G_t[i] - G_s[i]}        (t > s)
+//   M_ts    = sum_i q_t[i] k_s[i] 2^{G_t[i] - G_s[i]}        (t >= s)
+//   R       = V - (K o 2^G) S,  Delta = (I + StrictLower(Diag(beta) Ahat))^{-1} Diag(beta) R
+//   O       = (Q o 2^G) S + M Delta
+//   S'      = Diag(2^{G_n}) S + (K o 2^{G_n - G})^T Delta
+// The channel factor cannot be pulled out of the contraction, so the
+// operands carry it.  To keep every operand bounded, decays are measured
+// from ref_b = G just before 16-row block b:
+//   E_t = 2^{G_t - ref_b(t)} <= 1,   F_s = 2^{ref_b(s) - G_s} >= 1 (at most
+//   16 tokens of growth),  P_bc = 2^{ref_b - ref_c} <= 1 (b > c),
+//   Ahat_ts = sum_i (k_t E_t)[i] P_b(t)b(s)[i] (k_s F_s)[i],
+//   (K o 2^G)_t = (k_t E_t) o 2^{ref_b(t)},  (K o 2^{G_n-G})_s = (k_s F_s) o 2^{G_n - ref_b(s)}.
+// Domain: within any 16-token block the product of a channel's rates stays
+// above 2^-126 (every rate above ~0.005 suffices), so F is finite.
+//
+// Mapping.  One workgroup of 4 waves per (sequence, head, 64 columns of dv),
+// every operand in fp32 LDS and every contraction on the fp32 MFMA
+// (v_mfma_f32_16x16x4_f32).  Per chunk:
+//   stage  -> K, Q, V, log2(a) in LDS (from registers prefetched a chunk ahead)
+//   scan   -> G per channel (threads < dk), block references, factor vectors
+//   form   -> k o E, k o F, q o E in place
+//   gram   -> wave 0: diagonal Ahat tiles, 16x16 inverses, Y planes;
+//             waves 1-3: the 16 other Ahat / M tiles (kept in registers);
+//             every wave: Q S and K S for its columns, R
+//   write  -> -Ahat and M over the k o E and q o E space; k o F *= 2^{G_n - ref}
+//   state  -> substitution, output, state update (as the scalar fp32 kernel)
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kla_device.h"
+#include "kla_internal.h"
+
+namespace kla {
+namespace {
+
+template <int D>
+struct KdaCfg {
+  static constexpr int LDK = D + 4;    // fp32 rows of the K, Q operands
+  static constexpr int LDV = DVB + 4;  // V rows (this workgroup's columns)
+  static constexpr int LDP = C + 4;    // -Ahat and M planes (64 x 64)
+  static constexpr int LDY = 20;       // Y diagonal blocks (16 x 16)
+  static constexpr int NST = D / 16;   // state tiles per wave (dk direction)
+  static_assert(C * LDP <= C * LDK, "planes must fit in the operand space");
+};
+
+template <int D>
+struct KdaSmem {
+  using CF = KdaCfg<D>;
+  alignas(16) float KE[C * CF::LDK];  // k o E; after the Gram phase -Ahat [C][LDP]
+  alignas(16) float KF[C * CF::LDK];  // log2 a -> G while scanning; then k o F; then k o 2^{G_n - G}
+  alignas(16) float QE[C * CF::LDK];  // q o E; after the Gram phase M [C][LDP]
+  alignas(16) float Vs[C * CF::LDV];
+  alignas(16) float Yh[4 * 16 * CF::LDY];  // Y_bb = (I + L_bb)^{-1} Diag(beta_b)
+  alignas(16) float Ld[4 * 16 * 20];       // -Diag(beta) Ahat in the diagonal blocks, [block][col][row]
+  alignas(16) float kk[C];
+  alignas(16) float et[C];
+  alignas(16) float beta[C];
+  alignas(16) float ref[4][D];  // G just before block b (0 for b = 0)
+  alignas(16) float Z[4][D];    // 2^{ref_b}
+  alignas(16) float W[4][D];    // 2^{G_n - ref_b}
+  alignas(16) float P[6][D];    // 2^{ref_b - ref_c}, b > c, index b(b-1)/2 + c
+  alignas(16) float Zn[D];      // 2^{G_n}
+};
+
+__device__ inline f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ inline void st4(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
+
+// 16-byte segment (8 bf16 or 4 fp32) -> fp32 values
+__device__ inline void to_f32(const uint4 &u, __bf16, float (&x)[8]) {
+  const bf16x8 b = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(b[e]);
+}
+__device__ inline void to_f32(const uint4 &u, float, float (&x)[4]) {
+  x[0] = __uint_as_float(u.x);
+  x[1] = __uint_as_float(u.y);
+  x[2] = __uint_as_float(u.z);
+  x[3] = __uint_as_float(u.w);
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
+    const float *__restrict__ alpha, const float *__restrict__ eta,
+    const int32_t *__restrict__ cu_seqlens, int64_t seq_len_dense, int H, float eps,
+    int beta_direct, const float *__restrict__ S0, float *__restrict__ o,
+    float *__restrict__ Sfin) {
+  using CF = KdaCfg<D>;
+  constexpr int NB = D / DVB;
+  constexpr int NST = CF::NST;
+  constexpr int LDK = CF::LDK, LDV = CF::LDV, LDP = CF::LDP, LDY = CF::LDY;
+  constexpr int SEG_EL = 16 / sizeof(E);  // elements per 16-byte segment
+  constexpr int SEG_ROW = D / SEG_EL;     // segments per K/Q row
+  constexpr int SEG_VROW = DVB / SEG_EL;  // segments per V row (this block)
+  constexpr int SEG_AROW = D / 4;         // fp32 segments per decay row
+  constexpr int NSEG = C * SEG_ROW / kThreads;
+  constexpr int NVSEG = C * SEG_VROW / kThreads;
+  constexpr int NASEG = C * SEG_AROW / kThreads;
+  static_assert(NSEG * kThreads == C * SEG_ROW && NVSEG * kThreads == C * SEG_VROW &&
+                    NASEG * kThreads == C * SEG_AROW, "staging tiling");
+  static_assert(kThreads % SEG_ROW == 0, "row segments must not straddle waves");
+
+  __shared__ KdaSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int j = l >> 4, c16 = l & 15;
+
+  const int64_t lb = logical_block();
+  const int nb = (int)(lb % NB);
+  const int64_t sh = lb / NB;
+  const int h = (int)(sh % H);
+  const int64_t s = sh / H;
+  const int64_t bos = cu_seqlens ? (int64_t)cu_seqlens[s] : s * seq_len_dense;
+  const int64_t eos = cu_seqlens ? (int64_t)cu_seqlens[s + 1] : bos + seq_len_dense;
+  const int col = nb * DVB + 16 * w + c16;  // this lane's state/output column
+  constexpr int64_t DD = (int64_t)D * D;
+
+  f32x4 S[NST];
+  {
+    const rsrc_t rs = make_rsrc(S0 ? S0 + sh * DD : o, S0 ? DD * 4 : 0);
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[t][i] = buf_ld4(rs, ((16 * t + 4 * j + i) * D + col) * 4);
+  }
+
+  // ---- chunk inputs, one chunk ahead in registers ---------------------------
+  uint4 kreg[NSEG], qreg[NSEG], vreg[NVSEG], areg[NASEG];
+  float ereg = 0.f;
+  auto fetch = [&](int64_t t0) {
+    // rows past the end of the sequence fall outside the descriptors: zeros
+    const int64_t nn = (eos - t0) < C ? (eos - t0) : C;
+    const int64_t rowb = (int64_t)H * D * sizeof(E);
+    const rsrc_t rk = make_rsrc(k + t0 * H * (int64_t)D, nn * rowb);
+    const rsrc_t rq = make_rsrc(q + t0 * H * (int64_t)D, nn * rowb);
+    const rsrc_t rv = make_rsrc(v + t0 * H * (int64_t)D, nn * rowb);
+    const rsrc_t ra = make_rsrc(alpha + t0 * H * (int64_t)D, nn * (int64_t)H * D * 4);
+#pragma unroll
+    for (int u = 0; u < NSEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+      const uint32_t off = (uint32_t)((r * H + h) * D + cs * SEG_EL) * sizeof(E);
+      kreg[u] = buf_ld16(rk, off);
+      qreg[u] = buf_ld16(rq, off);
+    }
+#pragma unroll
+    for (int u = 0; u < NVSEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
+      vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + nb * DVB + cs * SEG_EL) * sizeof(E));
+    }
+#pragma unroll
+    for (int u = 0; u < NASEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_AROW, cs = sg % SEG_AROW;
+      areg[u] = buf_ld16(ra, (uint32_t)((r * H + h) * D + 4 * cs) * 4);
+    }
+    if (w == 0) {
+      const rsrc_t re = make_rsrc(eta + t0 * H, nn * H * 4);
+      ereg = buf_ld4(re, (uint32_t)(l * H + h) * 4);  // zero past the end
+    }
+  };
+  // registers -> LDS: K, Q, V as fp32, log2 of the rates (0 past the end:
+  // rate 1), row norms |k|^2 from the raw keys, eta
+  auto stage = [&](int64_t t0) {
+    const int64_t n = (eos - t0) < C ? (eos - t0) : C;
+#pragma unroll
+    for (int u = 0; u < NSEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+      float kx[SEG_EL], qx[SEG_EL];
+      to_f32(kreg[u], E(), kx);
+      to_f32(qreg[u], E(), qx);
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < SEG_EL; e += 4) {
+        st4(&sm.KE[r * LDK + cs * SEG_EL + e], f32x4{kx[e], kx[e + 1], kx[e + 2], kx[e + 3]});
+        st4(&sm.QE[r * LDK + cs * SEG_EL + e], f32x4{qx[e], qx[e + 1], qx[e + 2], qx[e + 3]});
+      }
+#pragma unroll
+      for (int e = 0; e < SEG_EL; ++e) part += kx[e] * kx[e];
+      part = group_sum<SEG_ROW>(part);
+      if (cs == 0) sm.kk[r] = part;
+    }
+#pragma unroll
+    for (int u = 0; u < NVSEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
+      float vx[SEG_EL];
+      to_f32(vreg[u], E(), vx);
+#pragma unroll
+      for (int e = 0; e < SEG_EL; e += 4)
+        st4(&sm.Vs[r * LDV + cs * SEG_EL + e], f32x4{vx[e], vx[e + 1], vx[e + 2], vx[e + 3]});
+    }
+#pragma unroll
+    for (int u = 0; u < NASEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_AROW, cs = sg % SEG_AROW;
+      const bool in = r < n;
+      f32x4 g;
+      g[0] = in ? flog2(__uint_as_float(areg[u].x)) : 0.f;
+      g[1] = in ? flog2(__uint_as_float(areg[u].y)) : 0.f;
+      g[2] = in ? flog2(__uint_as_float(areg[u].z)) : 0.f;
+      g[3] = in ? flog2(__uint_as_float(areg[u].w)) : 0.f;
+      st4(&sm.KF[r * LDK + 4 * cs], g);
+    }
+    if (w == 0) sm.et[l] = ereg;
+  };
+
+  fetch(bos);
+  stage(bos);
+  for (int64_t tok0 = bos; tok0 < eos; tok0 += C) {
+    const int n = (int)((eos - tok0) < C ? (eos - tok0) : C);
+    lds_barrier();  // chunk tok0 is staged
+    fetch(tok0 + C);
+
+    // ---- scan: G per channel, block references and factor vectors ----------
+    if (tid < D) {
+      const int ch = tid;
+      float g = 0.f, rf[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        rf[b] = g;  // G just before block b
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) {
+          const int t = 16 * b + tt;
+          g += sm.KF[t * LDK + ch];
+          sm.KF[t * LDK + ch] = g;
+        }
+      }
+      // g = G_n (the rates past the end are 1)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        sm.ref[b][ch] = rf[b];
+        sm.Z[b][ch] = fexp2(rf[b]);
+        sm.W[b][ch] = fexp2(g - rf[b]);
+      }
+#pragma unroll
+      for (int b = 1; b < 4; ++b)
+#pragma unroll
+        for (int c = 0; c < b; ++c) sm.P[b * (b - 1) / 2 + c][ch] = fexp2(rf[b] - rf[c]);
+      sm.Zn[ch] = fexp2(g);
+    }
+    lds_barrier();
+
+    // ---- form k o E, k o F, q o E in place -----------------------------------
+    {
+      constexpr int Q4 = D / 4;            // float4 per row
+      constexpr int RPP = kThreads / Q4;   // rows per pass
+      const int c4 = 4 * (tid % Q4);
+#pragma unroll
+      for (int r = tid / Q4; r < C; r += RPP) {
+        const f32x4 G = ld4(&sm.KF[r * LDK + c4]);
+        const f32x4 rf = ld4(&sm.ref[r >> 4][c4]);
+        const f32x4 kx = ld4(&sm.KE[r * LDK + c4]);
+        const f32x4 qx = ld4(&sm.QE[r * LDK + c4]);
+        f32x4 ke, kf, qe;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float Ev = fexp2(G[e] - rf[e]), Fv = fexp2(rf[e] - G[e]);
+          ke[e] = kx[e] * Ev;
+          kf[e] = kx[e] * Fv;
+          qe[e] = qx[e] * Ev;
+        }
+        st4(&sm.KE[r * LDK + c4], ke);
+        st4(&sm.KF[r * LDK + c4], kf);
+        st4(&sm.QE[r * LDK + c4], qe);
+      }
+    }
+    lds_barrier();
+
+    // ---- Gram tiles, diagonal inverses; Q S, K S, R --------------------------
+    f32x4 jt[6];  // waves 1-3: their Gram tiles until the operand space is free
+    if (w == 0) {
+      sm.beta[l] = beta_direct ? sm.et[l] : sm.et[l] / (sm.kk[l] + eps);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += 4)
+          acc = mma(sm.KE[(16 * b + c16) * LDK + k0 + j], sm.KF[(16 * b + c16) * LDK + k0 + j], acc);
+        // acc[i] = Ahat[16b + 4j + i][16b + c16]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * j + i;
+          sm.Ld[(b * 16 + c16) * 20 + r] = r > c16 ? -sm.beta[16 * b + r] * acc[i] : 0.f;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // lane (block j, column c16): column c16 of (I + L_jj)^{-1}
+      float lc[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v4 = ld4(&sm.Ld[(j * 16 + c16) * 20 + 4 * q4]);
+        lc[4 * q4] = v4[0];
+        lc[4 * q4 + 1] = v4[1];
+        lc[4 * q4 + 2] = v4[2];
+        lc[4 * q4 + 3] = v4[3];
+      }
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = (r == c16) ? 1.f : 0.f;
+      solve_steps(x, lc, std::make_integer_sequence<int, 15>{});
+      const float bc = sm.beta[16 * j + c16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.Yh[(j * 16 + r) * LDY + c16] = x[r] * bc;
+    } else {
+      // waves 1, 2, 3: jobs [0,5), [5,10), [10,16)
+      const int q0 = 5 * (w - 1);
+      const int nj = w == 3 ? 6 : 5;
+#pragma unroll
+      for (int u = 0; u < 6; ++u) {
+        if (u < nj) {
+          const Job jb = job_of(q0 + u);
+          const float *A = jb.qk ? sm.QE : sm.KE;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          if (jb.bi == jb.bj) {
+#pragma unroll
+            for (int k0 = 0; k0 < D; k0 += 4)
+              acc = mma(A[(16 * jb.bi + c16) * LDK + k0 + j], sm.KF[(16 * jb.bj + c16) * LDK + k0 + j], acc);
+          } else {
+            const float *Pv = sm.P[jb.bi * (jb.bi - 1) / 2 + jb.bj];
+#pragma unroll
+            for (int k0 = 0; k0 < D; k0 += 4)
+              acc = mma(A[(16 * jb.bi + c16) * LDK + k0 + j] * Pv[k0 + j],
+                        sm.KF[(16 * jb.bj + c16) * LDK + k0 + j], acc);
+          }
+          jt[u] = acc;
+        }
+      }
+    }
+
+    // Q S and K S with the state rows scaled by 2^{ref_bi}: (q o 2^G) S = (q o E) (Diag(2^{ref}) S)
+    f32x4 QS[4], R[4];
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      f32x4 Sz[NST];
+#pragma unroll
+      for (int t = 0; t < NST; ++t) Sz[t] = S[t] * ld4(&sm.Z[bi][16 * t + 4 * j]);
+      f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < NST; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int a_off = (16 * bi + c16) * LDK + 16 * t + 4 * j + i;
+          aq = mma(sm.QE[a_off], Sz[t][i], aq);
+          ak = mma(sm.KE[a_off], Sz[t][i], ak);
+        }
+      QS[bi] = aq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R[bi][i] = sm.Vs[(16 * bi + 4 * j + i) * LDV + 16 * w + c16] - ak[i];
+    }
+    lds_barrier();  // every read of k o E and q o E is done
+
+    // ---- planes over the operand space; k o F -> k o 2^{G_n - G} ------------
+    if (w != 0) {
+      const int q0 = 5 * (w - 1);
+      const int nj = w == 3 ? 6 : 5;
+#pragma unroll
+      for (int u = 0; u < 6; ++u) {
+        if (u < nj) {
+          const Job jb = job_of(q0 + u);
+          const int Sc = 16 * jb.bj + c16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int Rr = 16 * jb.bi + 4 * j + i;
+            if (jb.qk)
+              sm.QE[Rr * LDP + Sc] = Rr >= Sc ? jt[u][i] : 0.f;  // M, lower incl. diagonal
+            else
+              sm.KE[Rr * LDP + Sc] = -jt[u][i];                  // -Ahat, below the diagonal blocks
+          }
+        }
+      }
+    }
+    {
+      constexpr int Q4 = D / 4, RPP = kThreads / Q4;
+      const int c4 = 4 * (tid % Q4);
+#pragma unroll
+      for (int r = tid / Q4; r < C; r += RPP)
+        st4(&sm.KF[r * LDK + c4], ld4(&sm.KF[r * LDK + c4]) * ld4(&sm.W[r >> 4][c4]));
+    }
+    lds_barrier();
+
+    // ---- Delta by block substitution, output, state update ------------------
+    const float *Ah = sm.KE;
+    const float *Mh = sm.QE;
+    f32x4 Dl[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      f32x4 acc = R[b];
+#pragma unroll
+      for (int m = 0; m < b; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mma(Ah[(16 * b + c16) * LDP + 16 * m + 4 * j + i], Dl[m][i], acc);
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d = mma(sm.Yh[(b * 16 + c16) * LDY + 4 * j + i], acc[i], d);
+      Dl[b] = d;
+    }
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      f32x4 acc = QS[bi];
+#pragma unroll
+      for (int mt = 0; mt <= bi; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mma(Mh[(16 * bi + c16) * LDP + 16 * mt + 4 * j + i], Dl[mt][i], acc);
+      QS[bi] = acc;  // now the output tile
+    }
+    {
+      const rsrc_t ro = make_rsrc(o + tok0 * H * (int64_t)D, (int64_t)n * H * D * 4);
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          buf_st4(ro, (uint32_t)(((16 * bi + 4 * j + i) * H + h) * D + col) * 4, QS[bi][i]);
+    }
+    // S' = Diag(2^{G_n}) S + (k o 2^{G_n - G})^T Delta
+#pragma unroll
+    for (int t = 0; t < NST; ++t) S[t] *= ld4(&sm.Zn[16 * t + 4 * j]);
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          S[t] = mma(sm.KF[(16 * mt + 4 * j + i) * LDK + 16 * t + c16], Dl[mt][i], S[t]);
+    lds_barrier();  // everyone is done with this chunk's LDS
+    stage(tok0 + C);
+  }
+
+  {
+    const rsrc_t rs = make_rsrc(Sfin ? Sfin + sh * DD : o, Sfin ? DD * 4 : 0);
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) buf_st4(rs, ((16 * t + 4 * j + i) * D + col) * 4, S[t][i]);
+  }
+}
+
+template <typename E, int D>
+hipError_t launch_kda(const PrefillArgs &a, hipStream_t st) {
+  const int64_t grid = (int64_t)a.n_seqs * a.H * (D / DVB);
+  hipLaunchKernelGGL((prefill_kda_kernel<E, D>), dim3((unsigned)grid), dim3(kThreads), 0, st,
+                     static_cast<const E *>(a.q), static_cast<const E *>(a.k),
+                     static_cast<const E *>(a.v), a.alpha, a.eta, a.cu_seqlens, a.seq_len_dense,
+                     a.H, a.eps, a.beta_direct, a.initial_state, a.o, a.final_state);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_kda(const PrefillArgs &a, bool bf16_inputs, hipStream_t s) {
+  if (bf16_inputs) return a.D == 128 ? launch_kda<__bf16, 128>(a, s) : launch_kda<__bf16, 64>(a, s);
+  return a.D == 128 ? launch_kda<float, 128>(a, s) : launch_kda<float, 64>(a, s);
+}
+
+}  // namespace kla

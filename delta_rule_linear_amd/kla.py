@@ -43,6 +43,10 @@ _lib.kla_decode_step.argtypes = [_vp, _vp, _vp, _fp, _fp, _fp, _fp, ctypes.c_int
                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int, _vp]
 _lib.kla_decode_step_ex.restype = ctypes.c_int
 _lib.kla_decode_step_ex.argtypes = _lib.kla_decode_step.argtypes[:13] + [ctypes.c_int, _vp]
+_lib.kla_fwd_chunked_kda.restype = ctypes.c_int
+_lib.kla_fwd_chunked_kda.argtypes = _lib.kla_fwd_chunked_ex.argtypes
+_lib.kla_decode_step_kda.restype = ctypes.c_int
+_lib.kla_decode_step_kda.argtypes = _lib.kla_decode_step_ex.argtypes
 _lib.kla_status_string.restype = ctypes.c_char_p
 _lib.kla_status_string.argtypes = [ctypes.c_int]
 _lib.kla_version.restype = ctypes.c_char_p
@@ -140,8 +144,20 @@ def kla_fwd_chunked_split(q, k, v, alpha, eta, cu_seqlens=None, initial_state=No
                 output_final_state, o, final_state, workspace, stream, n_splits=int(n_splits))
 
 
+def kla_fwd_chunked_kda(q, k, v, alpha, eta, cu_seqlens=None, initial_state=None, eps=1e-6,
+                        chunk=64, beta_mode="kaczmarz", output_final_state=False, o=None,
+                        final_state=None, stream=None):
+    """Prefill with one decay rate per key channel (C ABI `kla_fwd_chunked_kda`,
+    Kimi Delta Attention's gate): alpha is [tok, H, dk] (or [B, T, H, dk])
+    fp32 and required.  Other arguments as kla_fwd_chunked_ex."""
+    if alpha is None or alpha.shape[:-1] != eta.shape or alpha.shape[-1] != q.shape[-1]:
+        raise ValueError("alpha must hold one rate per key channel: shape eta.shape + (dk,)")
+    return _fwd(_beta_code(beta_mode), q, k, v, alpha, eta, cu_seqlens, initial_state, eps, chunk,
+                output_final_state, o, final_state, None, stream, channel_decay=True)
+
+
 def _fwd(beta, q, k, v, alpha, eta, cu_seqlens, initial_state, eps, chunk, output_final_state, o,
-         final_state, workspace, stream, n_splits=None):
+         final_state, workspace, stream, n_splits=None, channel_decay=False):
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
     if alpha is not None:
@@ -182,7 +198,9 @@ def _fwd(beta, q, k, v, alpha, eta, cu_seqlens, initial_state, eps, chunk, outpu
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(cu_seqlens), n_seqs, total, H,
             dk, dv, chunk, float(eps), _dtype_code(q))
     tail = (_ptr(initial_state), _ptr(o), _ptr(final_state), ws_ptr, ws_len, _stream(stream))
-    if n_splits is not None:
+    if channel_decay:
+        st = _lib.kla_fwd_chunked_kda(*head, beta, *tail)
+    elif n_splits is not None:
         st = _lib.kla_fwd_chunked_split(*head, beta, n_splits, *tail)
     elif beta is None:
         st = _lib.kla_fwd_chunked(*head, *tail)
@@ -209,7 +227,17 @@ def kla_decode_step_ex(q, k, v, alpha, eta, state, eps=1e-6, beta_mode="kaczmarz
     return _decode(_beta_code(beta_mode), q, k, v, alpha, eta, state, eps, o, stream)
 
 
-def _decode(beta, q, k, v, alpha, eta, state, eps, o, stream):
+def kla_decode_step_kda(q, k, v, alpha, eta, state, eps=1e-6, beta_mode="kaczmarz", o=None,
+                        stream=None):
+    """One decode step with one decay rate per key channel (C ABI
+    `kla_decode_step_kda`): alpha [N, H, dk] fp32, required."""
+    if alpha is None or tuple(alpha.shape) != tuple(q.shape):
+        raise ValueError("alpha must hold one rate per key channel: shape [N, H, dk]")
+    return _decode(_beta_code(beta_mode), q, k, v, alpha, eta, state, eps, o, stream,
+                   channel_decay=True)
+
+
+def _decode(beta, q, k, v, alpha, eta, state, eps, o, stream, channel_decay=False):
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
     if alpha is not None:
@@ -224,7 +252,9 @@ def _decode(beta, q, k, v, alpha, eta, state, eps, o, stream):
         _need(o, "o", torch.float32)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(state), _ptr(o), N, H, dk, dv,
             float(eps), _dtype_code(q))
-    if beta is None:
+    if channel_decay:
+        st = _lib.kla_decode_step_kda(*args, beta, _stream(stream))
+    elif beta is None:
         st = _lib.kla_decode_step(*args, _stream(stream))
     else:
         st = _lib.kla_decode_step_ex(*args, beta, _stream(stream))

@@ -215,6 +215,45 @@ kla_status kla_decode_step_ex(const void *q, const void *k, const void *v,
                               int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, float eps,
                               kla_dtype dtype, kla_beta_mode beta_mode, void *stream);
 
+/*
+ * Per-channel decay (Kimi Delta Attention's gate; linear-attention survey
+ * page, "Linear Attention Architectures: Mechanisms, Trade-offs, and
+ * Cross-Layer Routing", section "Metodologia e Estrutura": one decay rate per
+ * feature channel).  The state's rows are the key channels, so the token
+ * step becomes
+ *   S~ = Diag(a_t) S_{t-1},  e_t = v_t - S~^T k_t,  S_t = S~ + beta_t k_t e_t^T,
+ *   o_t = S_t^T q_t,
+ * with beta_t from beta_mode as in kla_fwd_chunked_ex.
+ *
+ *   alpha       [total_tok, H, dk] fp32, required, 16-byte aligned; every
+ *               rate in (0, 1].  Domain: inside each aligned block of 16
+ *               tokens of a chunk, the product of one channel's rates stays
+ *               above 2^-126 (every rate above about 0.005 is enough);
+ *               outside it the results may be non-finite.
+ * Other arguments and errors as kla_fwd_chunked_ex (whole sequences only; no
+ * workspace is needed).  The arithmetic is fp32 throughout (fp32 MFMA), for
+ * bf16 and fp32 inputs alike.
+ */
+kla_status kla_fwd_chunked_kda(const void *q, const void *k, const void *v,
+                               const float *alpha, const float *eta,
+                               const int32_t *cu_seqlens, int32_t n_seqs, int64_t total_tok,
+                               int32_t H, int32_t dk, int32_t dv, int32_t chunk, float eps,
+                               kla_dtype dtype, kla_beta_mode beta_mode,
+                               const float *initial_state, float *o, float *final_state,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step with the per-channel decay (the step above, once):
+ *   x = S^T (a o k), y = S^T (a o q), e = v - x, o = y + beta (k^T q) e,
+ *   S <- Diag(a) S + beta k e^T.
+ *   alpha       [n_seqs, H, dk] fp32, required, 16-byte aligned.
+ * Other arguments and errors as kla_decode_step_ex.
+ */
+kla_status kla_decode_step_kda(const void *q, const void *k, const void *v,
+                               const float *alpha, const float *eta, float *state, float *o,
+                               int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, float eps,
+                               kla_dtype dtype, kla_beta_mode beta_mode, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *kla_status_string(kla_status s);
 

@@ -45,6 +45,10 @@ def lib():
     L.kla_fwd_chunked_split_workspace_size.argtypes = [ctypes.c_int32] * 5
     L.kla_decode_step_ex.restype = ctypes.c_int
     L.kla_decode_step_ex.argtypes = L.kla_decode_step.argtypes[:13] + [ctypes.c_int, ctypes.c_void_p]
+    L.kla_fwd_chunked_kda.restype = ctypes.c_int
+    L.kla_fwd_chunked_kda.argtypes = L.kla_fwd_chunked_ex.argtypes
+    L.kla_decode_step_kda.restype = ctypes.c_int
+    L.kla_decode_step_kda.argtypes = L.kla_decode_step_ex.argtypes
     L.kla_status_string.restype = ctypes.c_char_p
     L.kla_status_string.argtypes = [ctypes.c_int]
     L.kla_version.restype = ctypes.c_char_p
@@ -55,7 +59,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["kla_fwd_chunked", "kla_fwd_chunked_ex",
-                                           "kla_fwd_chunked_split",
+                                           "kla_fwd_chunked_split", "kla_fwd_chunked_kda",
+                                           "kla_decode_step_kda",
                                            "kla_fwd_chunked_split_workspace_size",
                                            "kla_fwd_chunked_workspace_size", "kla_decode_step",
                                            "kla_decode_step_ex", "kla_status_string",
@@ -152,6 +157,25 @@ def test_split_rejects(lib):
     assert split_call(lib, 2, ws=ws, wsb=need, dk=96, dv=96) == UNSUPPORTED
 
 
+@pytest.mark.parametrize("over,code", [
+    (dict(alpha=None), INVALID),                 # the per-channel rates are required
+    (dict(alpha=BASE + 192 * MB + 4), INVALID),  # misaligned rates
+    (dict(o=BASE + 192 * MB + 1024), INVALID),   # o inside the [tok, H, dk] rates
+    (dict(n_seqs=0), INVALID),
+    (dict(eta=None), INVALID),
+    (dict(dk=96, dv=96), UNSUPPORTED),
+    (dict(chunk=32), UNSUPPORTED),
+])
+def test_fwd_kda_rejects(lib, over, code):
+    a = fwd_args(**over)
+    assert lib.kla_fwd_chunked_kda(*a[:14], 0, *a[14:]) == code
+
+
+def test_fwd_kda_rejects_unknown_beta_mode(lib):
+    a = fwd_args()
+    assert lib.kla_fwd_chunked_kda(*a[:14], 5, *a[14:]) == INVALID
+
+
 def test_workspace_query(lib):
     assert lib.kla_fwd_chunked_workspace_size(8, 16384, 16, 128, 128, 64) == 0
 
@@ -181,6 +205,18 @@ def test_decode_rejects(lib, over, code):
     assert lib.kla_decode_step_ex(*a[:13], 1, a[13]) == code
 
 
+@pytest.mark.parametrize("over,code", [
+    (dict(alpha=None), INVALID),
+    (dict(alpha=BASE + 3 * MB + 8), INVALID),
+    (dict(o=BASE + 3 * MB + 2048), INVALID),  # o inside the [N, H, dk] rates
+    (dict(N=0), INVALID),
+    (dict(dk=32, dv=32), UNSUPPORTED),
+])
+def test_decode_kda_rejects(lib, over, code):
+    a = dec_args(**over)
+    assert lib.kla_decode_step_kda(*a[:13], 0, a[13]) == code
+
+
 @pytest.mark.parametrize("mode", [2, -3])
 def test_decode_ex_rejects_unknown_beta_mode(lib, mode):
     a = dec_args()
@@ -190,6 +226,7 @@ def test_decode_ex_rejects_unknown_beta_mode(lib, mode):
 def test_binding_names_match_the_abi():
     import delta_rule_linear_amd as pkg
     for name in ("kla_fwd_chunked", "kla_decode_step", "kla_fwd_chunked_ex", "kla_decode_step_ex",
-                 "kla_fwd_chunked_split", "kla_fwd_chunked_workspace_size",
+                 "kla_fwd_chunked_split", "kla_fwd_chunked_kda", "kla_decode_step_kda",
+                 "kla_fwd_chunked_workspace_size",
                  "kla_fwd_chunked_split_workspace_size", "kla_status_string", "kla_version"):
         assert callable(getattr(pkg, name))
