@@ -18,6 +18,9 @@ Algorithmic work counted per token-head (d = 128, C = 64):
                  K K^T, Q K^T, T R, M Delta: 2*C*d each; Q S, K S, K^T Delta:
                  2*d*d each  ->  8*C*d + 6*d*d = 163,840
   decode bytes   the fp32 state read and written once: 2*d*d*4 per (seq, head)
+  per-channel decay (Kimi Delta Attention gate, `kda` object): the same
+                 work with alpha fp32 [.., dk]: 1288 - 4 + 4*d = 1796 B per
+                 token-head; its prefill kernel computes in fp32 (fp32 MFMA)
 """
 import argparse
 import json
@@ -30,18 +33,35 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_MFMA_PEAK_TF = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+FP32_MFMA_PEAK_TF = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
 
 PREFILL_KERNEL = "prefill_pc_kernel"  # the bf16 prefill kernel (producer/consumer waves)
 DECODE_KERNEL = "decode_kernel"
+KDA_KERNEL = "prefill_kda_kernel"      # per-channel decay prefill
 KERNEL_SOURCES = {PREFILL_KERNEL: "delta_rule_linear_amd/csrc/kla_prefill.hip",
-                  DECODE_KERNEL: "delta_rule_linear_amd/csrc/kla_decode.hip"}
+                  DECODE_KERNEL: "delta_rule_linear_amd/csrc/kla_decode.hip",
+                  KDA_KERNEL: "delta_rule_linear_amd/csrc/kla_kda.hip"}
+# mangled-name fragments of the instantiations the benchmark times (bf16
+# inputs, d = 128; the decode one with the scalar decay)
+KERNEL_MATCH = {PREFILL_KERNEL: "prefill_pc_kernelILi128ELb1E",
+                DECODE_KERNEL: "decode_kernelIDF16bLi128ELb0E",
+                KDA_KERNEL: "prefill_kda_kernelIDF16bLi128E"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
+SHARED_HEADER = "delta_rule_linear_amd/csrc/kla_device.h"  # device helpers of the prefill kernels
+
+
 def source_hash(kernel):
+    """sha256 of the kernel's source file (followed by the shared device
+    header for the prefill kernels, which include it)."""
     import hashlib
-    with open(os.path.join(ROOT, KERNEL_SOURCES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    paths = [KERNEL_SOURCES[kernel]] + ([SHARED_HEADER] if kernel != DECODE_KERNEL else [])
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel):
@@ -83,8 +103,8 @@ def ingest_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
     write = per_kernel(write_csv, "WRITE_SIZE")
     out = {}
     for kernel in KERNEL_SOURCES:
-        fk = [v for k, v in fetch.items() if kernel in k]
-        wk = [v for k, v in write.items() if kernel in k]
+        fk = [v for k, v in fetch.items() if KERNEL_MATCH[kernel] in k]
+        wk = [v for k, v in write.items() if KERNEL_MATCH[kernel] in k]
         if not fk or not wk:
             continue
         rb, wb = fk[0] * f_scale * 1024, wk[0] * w_scale * 1024
@@ -218,6 +238,69 @@ def bench_long(args, torch, kla, workloads, n_splits=3, launches=20):
             "speedup": round(res["one_pass"] / res["split"], 3)}
 
 
+def bench_kda(args, torch, kla, workloads, launches=50):
+    """Per-channel decay (one rate per key channel): the layer-shaped prefill
+    with alpha [B, T, H, dk] and the decode workload with alpha [N, H, dk]."""
+    inp = workloads.prefill("layer", channel_decay=True)
+    B, H, d = inp["n_seqs"], inp["H"], inp["d"]
+    T = inp["lengths"][0]
+    dev = "cuda:0"
+    q, k, v = (inp[n].to(dev).view(B, T, H, d) for n in ("q", "k", "v"))
+    a = inp["alpha_ch"].to(dev).view(B, T, H, d)
+    e = inp["eta"].to(dev).view(B, T, H)
+    o = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kla.kla_fwd_chunked_kda(q, k, v, a, e, eps=inp["eps"], o=o, final_state=S)
+
+    for _ in range(10):
+        step()
+    _, ev_ms = time_launches(step, launches, stream)
+    th = B * T * H
+    nbytes = th * (3 * d * 2 + 4 * d + 4 + d * 4) + B * H * d * d * 4
+    flops = th * (8 * 64 * d + 6 * d * d)
+    gbs = nbytes / (ev_ms * 1e-3) / 1e9
+    tf = flops / (ev_ms * 1e-3) / 1e12
+    del q, k, v, a, e, o, S, inp
+    out = {"workload": f"per-channel decay prefill: {B} sequences x {T} tokens, H={H}, dk=dv={d}, "
+                       f"bf16 q/k/v, fp32 alpha [.., dk], eta, o, final state",
+           "prefill_us": round(ev_ms * 1e3, 2),
+           "prefill_tokens_per_s": round(B * T / (ev_ms * 1e-3), 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic(KDA_KERNEL), "kernel": KDA_KERNEL, "avg_launch_us": round(ev_ms * 1e3, 2),
+                        "algorithmic_bytes_per_launch": nbytes,
+                        "fp32_mfma_tflops": round(tf, 2),
+                        "fp32_mfma_frac": round(tf / FP32_MFMA_PEAK_TF, 4),
+                        "algorithmic_flops_per_launch": flops}}
+    if not args.skip_decode:
+        wl = workloads.decode(steps=args.decode_steps, channel_decay=True)
+        N = wl["n_seqs"]
+        state = wl["state"].to(dev)
+        steps = [{n: st[n].to(dev) for n in ("q", "k", "v", "alpha_ch", "eta")} for st in wl["steps"]]
+        od = torch.empty((N, H, d), dtype=torch.float32, device=dev)
+        scratch = state.clone()
+        for st in steps[:4]:
+            kla.kla_decode_step_kda(st["q"], st["k"], st["v"], st["alpha_ch"], st["eta"], scratch,
+                                    eps=wl["eps"], o=od)
+        del scratch
+        it = iter(range(len(steps)))
+
+        def one():
+            st = steps[next(it)]
+            kla.kla_decode_step_kda(st["q"], st["k"], st["v"], st["alpha_ch"], st["eta"], state,
+                                    eps=wl["eps"], o=od)
+
+        _, dms = time_launches(one, len(steps), stream)
+        dgbs = 2 * N * H * d * d * 4 / (dms * 1e-3) / 1e9
+        out["decode_us_per_step"] = round(dms * 1e3, 2)
+        out["decode_state_gbs"] = round(dgbs, 1)
+        out["decode_frac"] = round(dgbs / HBM_PEAK_GBS, 4)
+    return out
+
+
 def cpu_baseline(pre, oracle):
     """fp64 reference on the host over the whole layer-shaped prefill."""
     import numpy as np
@@ -257,6 +340,8 @@ def main():
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-long", action="store_true",
                     help="skip the long-context one-pass vs split-sequence comparison")
+    ap.add_argument("--skip-kda", action="store_true",
+                    help="skip the per-channel decay prefill and decode")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -327,6 +412,8 @@ def main():
         }
     if not args.skip_long:
         out["long_context"] = bench_long(args, torch, kla, workloads)
+    if not args.skip_kda:
+        out["kda"] = bench_kda(args, torch, kla, workloads)
     if not args.skip_cpu_baseline:
         import oracle
         out["cpu_baseline"] = cpu_baseline(pre, oracle)
