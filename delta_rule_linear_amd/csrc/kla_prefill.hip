@@ -982,12 +982,13 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
         sched_fence();
       }
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
+      for (int bi = 0; bi < 4; ++bi) {
+        // V rows 16bi+4j..+3 of this lane's column, one transposing read
+        const bf16x4 vv = ld_tr(&sl.Vs[(16 * bi + 4 * j + (c16 >> 2)) * CF::LDV + 16 * w + 4 * (c16 & 3)]);
+        const f32x4 gv = *reinterpret_cast<const f32x4 *>(&sl.gam[16 * bi + 4 * j]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * bi + 4 * j + i;
-          R[bi][i] = static_cast<float>(sl.Vs[r * CF::LDV + 16 * w + c16]) - sl.gam[r] * R[bi][i];
-        }
+        for (int i = 0; i < 4; ++i) R[bi][i] = static_cast<float>(vv[i]) - gv[i] * R[bi][i];
+      }
     }
     lds_barrier();
 
