@@ -157,3 +157,84 @@ def decode_step(q, k, v, alpha, eta, state, eps=1e-6, lib_path=None, beta_mode="
     if rc != 0:
         raise RuntimeError("kla_oracle_decode_step failed")
     return o, S
+
+
+def ccq_stride(dk):
+    """Doubles (or floats) per (sequence, head) in a curvature-conditioned
+    read's state record: P = sum k k^T (dk*dk), m = sum k (dk), n, 3 pad."""
+    return dk * dk + dk + 4
+
+
+def _ccq_lib(lib):
+    if not getattr(lib, "_ccq_ready", False):
+        lib.kla_oracle_fwd_ccq.restype = ctypes.c_int
+        lib.kla_oracle_fwd_ccq.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _i64p, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_double, ctypes.c_int, _dp, _dp, _dp, _dp, _dp]
+        lib.kla_oracle_decode_step_ccq.restype = ctypes.c_int
+        lib.kla_oracle_decode_step_ccq.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                                   ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                   ctypes.c_int, ctypes.c_double, ctypes.c_int, _dp]
+        lib._ccq_ready = True
+    return lib
+
+
+def fwd_ccq(q, k, v, alpha, eta, lam, cu_seqlens=None, eps=1e-6, initial_state=None,
+            ccq_state=None, lib_path=None, beta_mode="kaczmarz"):
+    """Sequential fp64 KLA prefill with the curvature-conditioned read
+    ("Don't Read Everything: A Curvature-Conditioned Query for Linear
+    Attention", section "O Mecanismo"): o_t = S_t^T (q_t - lambda_t Sigma_t q_t),
+    Sigma_t the uniformly weighted covariance of the keys so far.
+
+    lam: [tok, H] (like eta).  ccq_state: [n_seqs, H, ccq_stride(dk)] start
+    sums or None (zeros).  Returns (o, final_state, final ccq sums).
+    """
+    lib = _ccq_lib(_load(lib_path))
+    q, k, v, alpha, eta, lam = (_f64(t) for t in (q, k, v, alpha, eta, lam))
+    out_shape = v.shape
+    if cu_seqlens is None:
+        if q.ndim == 4:
+            B, T = q.shape[0], q.shape[1]
+            cu = np.arange(B + 1, dtype=np.int64) * T
+        else:
+            cu = np.array([0, q.shape[0]], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    dk, dv, H = q.shape[-1], v.shape[-1], q.shape[-2]
+    q, k, v = q.reshape(-1, H, dk), k.reshape(-1, H, dk), v.reshape(-1, H, dv)
+    alpha = None if alpha is None else alpha.reshape(-1, H)
+    eta, lam = eta.reshape(-1, H), lam.reshape(-1, H)
+    n_seqs, tok = cu.shape[0] - 1, q.shape[0]
+    if int(cu[-1]) != tok:
+        raise ValueError("cu_seqlens[-1] must equal the token count")
+    init = None if initial_state is None else _f64(initial_state).reshape(n_seqs, H, dk, dv)
+    cin = None if ccq_state is None else _f64(ccq_state).reshape(n_seqs, H, ccq_stride(dk))
+    o = np.zeros((tok, H, dv))
+    fin = np.zeros((n_seqs, H, dk, dv))
+    cout = np.zeros((n_seqs, H, ccq_stride(dk)))
+    rc = lib.kla_oracle_fwd_ccq(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(lam),
+                                cu.ctypes.data_as(_i64p), n_seqs, H, dk, dv, float(eps),
+                                _BETA[beta_mode], _ptr(init), _ptr(cin), _ptr(o), _ptr(fin),
+                                _ptr(cout))
+    if rc != 0:
+        raise RuntimeError("kla_oracle_fwd_ccq failed")
+    return o.reshape(out_shape), fin, cout
+
+
+def decode_step_ccq(q, k, v, alpha, eta, lam, state, ccq_state, eps=1e-6, lib_path=None,
+                    beta_mode="kaczmarz"):
+    """One fp64 decode step with the curvature-conditioned read.  Returns
+    (o, new_state, new ccq sums); the inputs are not modified."""
+    lib = _ccq_lib(_load(lib_path))
+    q, k, v, alpha, eta, lam = (_f64(t) for t in (q, k, v, alpha, eta, lam))
+    S = _f64(state).copy()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    cs = _f64(ccq_state).reshape(N, H, ccq_stride(dk)).copy()
+    o = np.zeros((N, H, dv))
+    rc = lib.kla_oracle_decode_step_ccq(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
+                                        _ptr(lam), _ptr(S), _ptr(cs), N, H, dk, dv, float(eps),
+                                        _BETA[beta_mode], _ptr(o))
+    if rc != 0:
+        raise RuntimeError("kla_oracle_decode_step_ccq failed")
+    return o, S, cs

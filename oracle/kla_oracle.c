@@ -34,6 +34,16 @@
  * channels, so the decay becomes S~ = Diag(a_t) S_{t-1}: row i of the state
  * is scaled by a_t[i].  The residual, the step and the write are KLA's.
  *
+ * Curvature-conditioned query (the *_ccq entry points; "Don't Read
+ * Everything: A Curvature-Conditioned Query for Linear Attention", sections
+ * "Derivacao Teorica" and "O Mecanismo"): only the read changes.  With
+ * Sigma_t the covariance of the keys seen so far, weighted uniformly (the
+ * Hessian of log sum_{j<=t} exp(k_j^T q) at q = 0),
+ *   Sigma_t = (1/n) sum_{j<=t} k_j k_j^T - mu_t mu_t^T,  mu_t = (1/n) sum_{j<=t} k_j,
+ *   q_clean = q_t - lambda_t Sigma_t q_t,   o_t = S_t^T q_clean,
+ * where n counts the keys j <= t.  The running sums (sum k k^T, sum k, n)
+ * are the extra state per head; a sequence may start from given sums.
+ *
  * This is the plain definition, token by token, in double precision,
  * with no blocking or chunking: the chunkwise algorithm of the GPU path
  * reaches the same result up to rounding.  Inputs arrive as doubles that
@@ -288,6 +298,117 @@ int kla_oracle_decode_step_ch(const double *q, const double *k, const double *v,
         }
         kla_token_ch(state + sh * sdim, e, q + sh * dk, k + sh * dk, v + sh * dv,
                      alpha + sh * dk, eta[sh], eps, beta_direct, dk, dv, o + sh * dv);
+        free(e);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
+ * Curvature-conditioned read.  The extra state per (sequence, head) is the
+ * running sums in one record of CCQ_STRIDE(dk) doubles:
+ *   [0, dk*dk)        P = sum k k^T (row-major)
+ *   [dk*dk, dk*dk+dk) m = sum k
+ *   [dk*dk+dk]        n, the number of keys
+ */
+#define CCQ_STRIDE(dk) ((size_t)(dk) * (dk) + (dk) + 4)
+
+/* Sums += k; qc = q - lambda Sigma q with Sigma from the updated sums. */
+static void ccq_clean(double *P, double *m, double *n, const double *q, const double *k,
+                      double lambda, int dk, double *qc)
+{
+    *n += 1.0;
+    for (int i = 0; i < dk; ++i) {
+        m[i] += k[i];
+        for (int c = 0; c < dk; ++c) P[(size_t)i * dk + c] += k[i] * k[c];
+    }
+    const double inv = 1.0 / *n;
+    double mq = 0.0;
+    for (int c = 0; c < dk; ++c) mq += m[c] * q[c];
+    for (int i = 0; i < dk; ++i) {
+        double pq = 0.0;
+        for (int c = 0; c < dk; ++c) pq += P[(size_t)i * dk + c] * q[c];
+        const double sq = pq * inv - (m[i] * inv) * (mq * inv);  /* (Sigma q)_i */
+        qc[i] = q[i] - lambda * sq;
+    }
+}
+
+/*
+ * Prefill with the curvature-conditioned read: lambda [total_tok][H];
+ * ccq_in / ccq_out [n_seqs][H][CCQ_STRIDE(dk)] (NULL: start from zero sums /
+ * do not write).  Everything else as kla_oracle_fwd_ex.
+ */
+int kla_oracle_fwd_ccq(const double *q, const double *k, const double *v,
+                       const double *alpha, const double *eta, const double *lambda,
+                       const int64_t *cu_seqlens, int n_seqs, int H, int dk, int dv,
+                       double eps, int beta_direct, const double *initial_state,
+                       const double *ccq_in, double *o, double *final_state, double *ccq_out)
+{
+    if (!q || !k || !v || !eta || !lambda || !cu_seqlens || !o) return -1;
+    if (n_seqs <= 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    for (int s = 0; s < n_seqs; ++s)
+        if (cu_seqlens[s + 1] < cu_seqlens[s]) return -1;
+    if (cu_seqlens[0] != 0) return -1;
+
+    const size_t sdim = (size_t)dk * dv, cst = CCQ_STRIDE(dk);
+    int failed = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int s = 0; s < n_seqs; ++s) {
+        for (int h = 0; h < H; ++h) {
+            double *S = (double *)malloc(sizeof(double) * (sdim + dv + cst + dk));
+            if (!S) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            double *e = S + sdim, *cs = e + dv, *qc = cs + cst;
+            const size_t sh = (size_t)s * H + h;
+            if (initial_state)
+                memcpy(S, initial_state + sh * sdim, sizeof(double) * sdim);
+            else
+                memset(S, 0, sizeof(double) * sdim);
+            if (ccq_in)
+                memcpy(cs, ccq_in + sh * cst, sizeof(double) * cst);
+            else
+                memset(cs, 0, sizeof(double) * cst);
+            double *P = cs, *m = cs + (size_t)dk * dk, *n = m + dk;
+            for (int64_t t = cu_seqlens[s]; t < cu_seqlens[s + 1]; ++t) {
+                const size_t th = (size_t)t * H + h;
+                ccq_clean(P, m, n, q + th * dk, k + th * dk, lambda[th], dk, qc);
+                kla_token(S, e, qc, k + th * dk, v + th * dv, alpha ? alpha[th] : 1.0, eta[th],
+                          eps, beta_direct, dk, dv, o + th * dv);
+            }
+            if (final_state) memcpy(final_state + sh * sdim, S, sizeof(double) * sdim);
+            if (ccq_out) memcpy(ccq_out + sh * cst, cs, sizeof(double) * cst);
+            free(S);
+        }
+    }
+    return failed ? -1 : 0;
+}
+
+/* One decode step with the curvature-conditioned read; ccq_state
+ * [n_seqs][H][CCQ_STRIDE(dk)] is updated in place with the new key. */
+int kla_oracle_decode_step_ccq(const double *q, const double *k, const double *v,
+                               const double *alpha, const double *eta, const double *lambda,
+                               double *state, double *ccq_state, int n_seqs, int H, int dk,
+                               int dv, double eps, int beta_direct, double *o)
+{
+    if (!q || !k || !v || !eta || !lambda || !state || !ccq_state || !o) return -1;
+    if (n_seqs <= 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    const size_t sdim = (size_t)dk * dv, cst = CCQ_STRIDE(dk);
+    int failed = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t sh = 0; sh < (int64_t)n_seqs * H; ++sh) {
+        double *e = (double *)malloc(sizeof(double) * (dv + dk));
+        if (!e) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        double *qc = e + dv, *cs = ccq_state + sh * cst;
+        ccq_clean(cs, cs + (size_t)dk * dk, cs + (size_t)dk * dk + dk, q + sh * dk, k + sh * dk,
+                  lambda[sh], dk, qc);
+        kla_token(state + sh * sdim, e, qc, k + sh * dk, v + sh * dv, alpha ? alpha[sh] : 1.0,
+                  eta[sh], eps, beta_direct, dk, dv, o + sh * dv);
         free(e);
     }
     return failed ? -1 : 0;

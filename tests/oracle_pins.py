@@ -22,6 +22,9 @@ scalar step that KLA replaces (the "direct" step-size mode).  The survey
 page's Kimi Delta Attention (section "Metodologia e Estrutura") decays each
 feature channel at its own rate: with channel_decay=True alpha holds one
 decay per key channel and S~ = Diag(a_t) S (the pin_channel_* checks).
+The curvature-conditioned read ("Don't Read Everything: A Curvature-
+Conditioned Query for Linear Attention", sections "Derivacao Teorica" and
+"O Mecanismo") cleans the query with the keys' covariance (pin_ccq_*).
 """
 import json
 import os
@@ -532,6 +535,123 @@ def pin_channel_decode_is_one_token(fwd, decode):
     assert rel(od[0], o_all[L]) < TIGHT
     assert rel(Sd, S_all) < TIGHT
 
+
+# ---- curvature-conditioned read ---------------------------------------------
+
+def _ccq(fwd):
+    """The oracle's fwd_ccq / decode_step_ccq bound to the build under test."""
+    import functools
+    import oracle
+    lp = getattr(fwd, "keywords", {}).get("lib_path")
+    return (functools.partial(oracle.fwd_ccq, lib_path=lp),
+            functools.partial(oracle.decode_step_ccq, lib_path=lp))
+
+
+def _clean_queries_numpy(q, k, lam, covariance):
+    """q_clean_t = q_t - lambda_t Sigma_t q_t per head, Sigma_t from `covariance`
+    applied to the keys k[0..t] of that head."""
+    L, H, dk = q.shape
+    out = np.empty_like(q)
+    for h in range(H):
+        for t in range(L):
+            Sig = covariance(k[:t + 1, h])
+            out[t, h] = q[t, h] - lam[t, h] * Sig @ q[t, h]
+    return out
+
+
+def pin_ccq_numpy_covariance(fwd, decode):
+    """The read uses q - lambda Sigma_t q with Sigma_t the uniformly weighted
+    covariance of the keys k_1..k_t (numpy.cov with bias=True); the state
+    recurrence is the plain one, so the CCQ output equals the plain oracle
+    fed those cleaned queries."""
+    fwd_ccq, _ = _ccq(fwd)
+    rng = np.random.default_rng(41)
+    L, H, dk, dv = 23, 2, 5, 4
+    q, k, v, alpha, eta = _rand_seq(rng, L, H, dk, dv)
+    lam = rng.uniform(0.0, 1.0, (L, H))
+    cov = lambda K: np.cov(K.T, bias=True).reshape(dk, dk) if K.shape[0] > 1 else np.zeros((dk, dk))
+    qc = _clean_queries_numpy(q, k, lam, cov)
+    S0 = rng.standard_normal((1, H, dk, dv))
+    for mode in ("kaczmarz", "direct"):
+        o, S, _ = fwd_ccq(q, k, v, alpha, eta, lam, eps=1e-3, initial_state=S0, beta_mode=mode)
+        o2, S2 = fwd(qc, k, v, alpha, eta, eps=1e-3, initial_state=S0, beta_mode=mode)
+        assert rel(o, o2) < 1e-12 and rel(S, S2) < TIGHT
+
+
+def pin_ccq_logsumexp_hessian(fwd, decode):
+    """Sigma_t is the Hessian at q = 0 of log sum_{j<=t} exp(k_j^T q), the
+    softmax normaliser the read stands in for; here by central differences
+    of scipy's logsumexp."""
+    from scipy.special import logsumexp
+    fwd_ccq, _ = _ccq(fwd)
+    rng = np.random.default_rng(42)
+    L, H, dk, dv = 9, 1, 3, 2
+    q, k, v, alpha, eta = _rand_seq(rng, L, H, dk, dv)
+    lam = rng.uniform(0.2, 1.0, (L, H))
+    hstep = 1e-3
+
+    def hessian(K):
+        f = lambda x: logsumexp(K @ x)
+        Hm = np.zeros((dk, dk))
+        E = np.eye(dk) * hstep
+        for a in range(dk):
+            for b in range(dk):
+                Hm[a, b] = (f(E[a] + E[b]) - f(E[a] - E[b]) - f(-E[a] + E[b]) + f(-E[a] - E[b])) / (4 * hstep * hstep)
+        return Hm
+
+    qc = _clean_queries_numpy(q, k, lam, hessian)
+    o, _, _ = fwd_ccq(q, k, v, alpha, eta, lam, eps=1e-3)
+    o2, _ = fwd(qc, k, v, alpha, eta, eps=1e-3)
+    assert rel(o, o2) < 1e-5, rel(o, o2)
+
+
+def pin_ccq_lambda_zero_and_state(fwd, decode):
+    """lambda = 0 reads with the raw query (the plain recurrence); for any
+    lambda the state is the plain one (only the read changes)."""
+    fwd_ccq, _ = _ccq(fwd)
+    rng = np.random.default_rng(43)
+    L, H, dk, dv = 17, 2, 4, 3
+    q, k, v, alpha, eta = _rand_seq(rng, L, H, dk, dv)
+    o0, S0 = fwd(q, k, v, alpha, eta, eps=1e-4)
+    o, S, _ = fwd_ccq(q, k, v, alpha, eta, np.zeros((L, H)), eps=1e-4)
+    assert rel(o, o0) < TIGHT and rel(S, S0) < TIGHT
+    o1, S1, _ = fwd_ccq(q, k, v, alpha, eta, rng.uniform(0, 1, (L, H)), eps=1e-4)
+    assert rel(S1, S0) < TIGHT and rel(o1, o0) > 1e-3
+
+
+def pin_ccq_constant_keys(fwd, decode):
+    """Every key the same: the covariance is zero and the read is the raw
+    query's, whatever lambda."""
+    fwd_ccq, _ = _ccq(fwd)
+    rng = np.random.default_rng(44)
+    L, H, dk, dv = 12, 1, 4, 3
+    q, _, v, alpha, eta = _rand_seq(rng, L, H, dk, dv)
+    k = np.broadcast_to(rng.standard_normal((1, H, dk)), (L, H, dk)).copy()
+    o, _, c = fwd_ccq(q, k, v, alpha, eta, rng.uniform(0.5, 1, (L, H)), eps=1e-4)
+    o0, _ = fwd(q, k, v, alpha, eta, eps=1e-4)
+    assert rel(o, o0) < 1e-12
+    assert c[0, 0, dk * dk + dk] == L
+
+
+def pin_ccq_resume_and_decode(fwd, decode):
+    """Carrying the running sums (and the state): two prefills equal one,
+    and a decode step after a prefill equals the prefill one token longer."""
+    fwd_ccq, dec_ccq = _ccq(fwd)
+    rng = np.random.default_rng(45)
+    L, H, dk, dv, m = 26, 2, 4, 3, 11
+    q, k, v, alpha, eta = _rand_seq(rng, L + 1, H, dk, dv)
+    lam = rng.uniform(0, 1, (L + 1, H))
+    o_all, S_all, c_all = fwd_ccq(q[:L], k[:L], v[:L], alpha[:L], eta[:L], lam[:L], eps=1e-4)
+    o1, S1, c1 = fwd_ccq(q[:m], k[:m], v[:m], alpha[:m], eta[:m], lam[:m], eps=1e-4)
+    o2, S2, c2 = fwd_ccq(q[m:L], k[m:L], v[m:L], alpha[m:L], eta[m:L], lam[m:L], eps=1e-4,
+                         initial_state=S1, ccq_state=c1)
+    assert rel(np.concatenate([o1, o2]), o_all) < TIGHT
+    assert rel(S2, S_all) < TIGHT and rel(c2, c_all) < TIGHT
+    od, Sd, cd = dec_ccq(q[L:][0][None], k[L:][0][None], v[L:][0][None], alpha[L:][0][None],
+                         eta[L:][0][None], lam[L:][0][None], S_all, c_all, eps=1e-4)
+    o_l, S_l, c_l = fwd_ccq(q, k, v, alpha, eta, lam, eps=1e-4)
+    assert rel(od[0], o_l[L]) < TIGHT and rel(Sd, S_l) < TIGHT and rel(cd, c_l) < TIGHT
+
 ALL_PINS = [pin_worked_example, pin_orthogonal_projection, pin_min_norm_bruteforce,
             pin_exact_line_search, pin_normalised_gradient, pin_exact_recall, pin_eta_zero,
             pin_scalar_case, pin_gated_deltanet_form, pin_chunk_form, pin_packed_and_resume,
@@ -541,4 +661,6 @@ ALL_PINS = [pin_worked_example, pin_orthogonal_projection, pin_min_norm_brutefor
             pin_channel_uniform_is_scalar, pin_channel_eta_zero,
             pin_channel_orthogonal_projection, pin_channel_min_norm_bruteforce,
             pin_channel_untouched_channel, pin_channel_chunk_form,
-            pin_channel_decode_is_one_token]
+            pin_channel_decode_is_one_token,
+            pin_ccq_numpy_covariance, pin_ccq_logsumexp_hessian, pin_ccq_lambda_zero_and_state,
+            pin_ccq_constant_keys, pin_ccq_resume_and_decode]

@@ -98,6 +98,36 @@ MUTANTS.update({
                                                   "alpha + sh * dk, eta[sh], eps, 0"),
 })
 
+CCQ_UPDATE = ("    *n += 1.0;\n"
+              "    for (int i = 0; i < dk; ++i) {\n"
+              "        m[i] += k[i];\n"
+              "        for (int c = 0; c < dk; ++c) P[(size_t)i * dk + c] += k[i] * k[c];\n"
+              "    }\n")
+
+
+def _ccq_excludes_current_key(src):
+    """The covariance of the keys before t (the sums updated after the read)."""
+    a = src.index(CCQ_UPDATE)
+    src = src[:a] + "    const double inv0 = 1.0 / (*n + 1.0); (void)inv0;\n" + src[a + len(CCQ_UPDATE):]
+    b = src.index("        qc[i] = q[i] - lambda * sq;\n    }\n", a) + len("        qc[i] = q[i] - lambda * sq;\n    }\n")
+    return src[:b] + CCQ_UPDATE + src[b:]
+
+
+MUTANTS.update({
+    "ccq_no_mean": lambda s: s.replace("const double sq = pq * inv - (m[i] * inv) * (mq * inv);",
+                                       "const double sq = pq * inv;"),
+    "ccq_unbiased": lambda s: s.replace("const double inv = 1.0 / *n;",
+                                        "const double inv = *n > 1.0 ? 1.0 / (*n - 1.0) : 0.0;"),
+    "ccq_lambda_sign": lambda s: s.replace("qc[i] = q[i] - lambda * sq;", "qc[i] = q[i] + lambda * sq;"),
+    "ccq_mean_once": lambda s: s.replace("(m[i] * inv) * (mq * inv)", "(m[i] * inv) * mq"),
+    "ccq_excludes_current_key": _ccq_excludes_current_key,
+    "ccq_reads_raw_query": lambda s: s.replace(
+        "kla_token(S, e, qc, k + th * dk,", "kla_token(S, e, q + th * dk, k + th * dk,"),
+    "ccq_decode_reads_raw_query": lambda s: s.replace(
+        "kla_token(state + sh * sdim, e, qc,", "kla_token(state + sh * sdim, e, q + sh * dk,"),
+    "ccq_ignores_start_sums": lambda s: s.replace("if (ccq_in)\n", "if (0)\n"),
+})
+
 RUNNER = textwrap.dedent("""
     import sys, functools
     sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
