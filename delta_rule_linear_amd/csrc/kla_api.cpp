@@ -265,3 +265,197 @@ kla_status kla_decode_step(const void *q, const void *k, const void *v, const fl
 }
 
 }  // extern "C"
+
+// ---- curvature-conditioned read ---------------------------------------------
+namespace {
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ccq_record(int32_t dk) { return (int64_t)dk * dk + dk + 4; }
+}  // namespace
+
+extern "C" {
+
+size_t kla_ccq_state_floats(int32_t dk) { return dk > 0 ? (size_t)ccq_record(dk) : 0; }
+
+size_t kla_fwd_chunked_ccq_workspace_size(int64_t total_tok, int32_t H, int32_t dk, int32_t dv,
+                                          kla_dtype dtype) {
+  if (total_tok <= 0 || H <= 0 || !supported_dim(dk, dv)) return 0;
+  const size_t th = (size_t)total_tok * H;
+  if (dtype == KLA_BF16)  // q_clean hi and lo (bf16), the lo read's output (fp32)
+    return 2 * round_up(th * dk * 2) + round_up(th * dv * 4);
+  return round_up(th * dk * 4);  // q_clean (fp32)
+}
+
+size_t kla_decode_step_ccq_workspace_size(int32_t n_seqs, int32_t H, int32_t dk) {
+  if (n_seqs <= 0 || H <= 0 || dk <= 0) return 0;
+  return round_up((size_t)n_seqs * H * dk * 4);
+}
+
+kla_status kla_fwd_chunked_ccq(const void *q, const void *k, const void *v, const float *alpha,
+                               const float *eta, const float *lambda, const int32_t *cu_seqlens,
+                               int32_t n_seqs, int64_t total_tok, int32_t H, int32_t dk,
+                               int32_t dv, int32_t chunk, float eps, kla_dtype dtype,
+                               kla_beta_mode beta_mode, const float *initial_state,
+                               const float *ccq_in, float *o, float *final_state, float *ccq_out,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  if (n_seqs <= 0 || H <= 0 || total_tok < 0 || !std::isfinite(eps) || eps < 0.f)
+    return KLA_ERR_INVALID_ARG;
+  if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT) return KLA_ERR_INVALID_ARG;
+  if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
+  if (!supported_dim(dk, dv) || chunk != 64) return KLA_ERR_UNSUPPORTED;
+  if (!cu_seqlens && total_tok % n_seqs != 0) return KLA_ERR_INVALID_ARG;
+  const size_t ws_need = kla_fwd_chunked_ccq_workspace_size(total_tok, H, dk, dv, dtype);
+  if (workspace_bytes < ws_need) return KLA_ERR_WORKSPACE;
+  if (ws_need > 0 && (!workspace || !aligned16(workspace))) return KLA_ERR_INVALID_ARG;
+  if (total_tok > 0 && (!q || !k || !v || !eta || !lambda || !o)) return KLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      !aligned16(initial_state) || !aligned16(final_state) || !aligned16(ccq_in) ||
+      !aligned16(ccq_out))
+    return KLA_ERR_INVALID_ARG;
+  const int64_t esz = dtype == KLA_BF16 ? 2 : 4;
+  const int64_t th = total_tok * H, rec = (int64_t)n_seqs * H * ccq_record(dk) * 4;
+  const Range rq = range(q, th * dk * esz), rk = range(k, th * dk * esz),
+              rv = range(v, th * dv * esz), ra = range(alpha, alpha ? th * 4 : 0),
+              re = range(eta, th * 4), rl = range(lambda, th * 4), ro = range(o, th * dv * 4),
+              rcu = range(cu_seqlens, cu_seqlens ? (int64_t)(n_seqs + 1) * 4 : 0),
+              rs0 = range(initial_state, initial_state ? (int64_t)n_seqs * H * dk * dv * 4 : 0),
+              rs1 = range(final_state, final_state ? (int64_t)n_seqs * H * dk * dv * 4 : 0),
+              rc0 = range(ccq_in, ccq_in ? rec : 0), rc1 = range(ccq_out, ccq_out ? rec : 0),
+              rws = range(workspace, (int64_t)ws_need);
+  for (const Range &in : {rq, rk, rv, ra, re, rl, rcu, rs0, rs1, rc0, rc1, rws})
+    if (overlap(ro, in)) return KLA_ERR_INVALID_ARG;
+  for (const Range &in : {rq, rk, rv, ra, re, rl, rcu, rs0, rs1, rc0, rc1})
+    if (overlap(rws, in)) return KLA_ERR_INVALID_ARG;
+  for (const Range &in : {rq, rk, rv, ra, re, rl, rcu, rs0, rs1, rc0})
+    if (overlap(rc1, in)) return KLA_ERR_INVALID_ARG;  // the end sums: a buffer of their own
+  if (final_state) {
+    for (const Range &in : {rq, rk, rv, ra, re, rl, rcu, rc0})
+      if (overlap(rs1, in)) return KLA_ERR_INVALID_ARG;
+    if (initial_state && initial_state != final_state && overlap(rs0, rs1))
+      return KLA_ERR_INVALID_ARG;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  kla::CcqArgs c;
+  c.q = q;
+  c.k = k;
+  c.lambda = lambda;
+  c.cu_seqlens = cu_seqlens;
+  c.n_seqs = n_seqs;
+  c.seq_len_dense = cu_seqlens ? 0 : total_tok / n_seqs;
+  c.H = H;
+  c.D = dk;
+  c.bf16_inputs = dtype == KLA_BF16;
+  c.ccq_in = ccq_in;
+  c.ccq_out = ccq_out;
+  c.qh = ws;
+  c.ql = dtype == KLA_BF16 ? ws + round_up((size_t)th * dk * 2) : nullptr;
+  hipError_t e = kla::launch_ccq_query(c, st);
+
+  kla::PrefillArgs a;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.eta = eta;
+  a.cu_seqlens = cu_seqlens;
+  a.n_seqs = n_seqs;
+  a.seq_len_dense = c.seq_len_dense;
+  a.H = H;
+  a.D = dk;
+  a.eps = eps;
+  a.beta_direct = beta_mode == KLA_BETA_DIRECT;
+  a.initial_state = initial_state;
+  // With no tokens the kernels only copy the start state and sums to the end
+  // ones (workspace and query pointers are then never dereferenced).
+  if (dtype == KLA_BF16) {
+    // o is linear in the query and the state does not depend on it: read
+    // with the lo part first (no end state, so an in-place start state is
+    // still intact), then with the hi part, and add.
+    float *o_lo = reinterpret_cast<float *>(ws + 2 * round_up((size_t)th * dk * 2));
+    a.q = c.ql;
+    a.o = o_lo;
+    a.final_state = nullptr;
+    if (e == hipSuccess) e = kla::launch_prefill_bf16(a, st);
+    a.q = c.qh;
+    a.o = o;
+    a.final_state = final_state;
+    if (e == hipSuccess) e = kla::launch_prefill_bf16(a, st);
+    if (e == hipSuccess) e = kla::launch_add(o, o_lo, th * dv, st);
+  } else {
+    a.q = c.qh;
+    a.o = o;
+    a.final_state = final_state;
+    if (e == hipSuccess) e = kla::launch_prefill_f32(a, st);
+  }
+  return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
+}
+
+kla_status kla_decode_step_ccq(const void *q, const void *k, const void *v, const float *alpha,
+                               const float *eta, const float *lambda, float *state,
+                               float *ccq_state, float *o, int32_t n_seqs, int32_t H, int32_t dk,
+                               int32_t dv, float eps, kla_dtype dtype, kla_beta_mode beta_mode,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  if (n_seqs <= 0 || H <= 0 || !std::isfinite(eps) || eps < 0.f) return KLA_ERR_INVALID_ARG;
+  if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT) return KLA_ERR_INVALID_ARG;
+  if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
+  if (!supported_dim(dk, dv)) return KLA_ERR_UNSUPPORTED;
+  const size_t ws_need = kla_decode_step_ccq_workspace_size(n_seqs, H, dk);
+  if (workspace_bytes < ws_need) return KLA_ERR_WORKSPACE;
+  if (!q || !k || !v || !eta || !lambda || !state || !ccq_state || !o || !workspace)
+    return KLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(o) ||
+      !aligned16(ccq_state) || !aligned16(workspace))
+    return KLA_ERR_INVALID_ARG;
+  const int64_t esz = dtype == KLA_BF16 ? 2 : 4;
+  const int64_t nh = (int64_t)n_seqs * H;
+  const Range rq = range(q, nh * dk * esz), rk = range(k, nh * dk * esz),
+              rv = range(v, nh * dv * esz), ra = range(alpha, alpha ? nh * 4 : 0),
+              re = range(eta, nh * 4), rl = range(lambda, nh * 4), rs = range(state, nh * dk * dv * 4),
+              rc = range(ccq_state, nh * ccq_record(dk) * 4), ro = range(o, nh * dv * 4),
+              rws = range(workspace, (int64_t)ws_need);
+  for (const Range &in : {rq, rk, rv, ra, re, rl, rs, rc, rws})
+    if (overlap(ro, in)) return KLA_ERR_INVALID_ARG;
+  for (const Range &in : {rq, rk, rv, ra, re, rl, rc, rws})
+    if (overlap(rs, in)) return KLA_ERR_INVALID_ARG;
+  for (const Range &in : {rq, rk, rv, ra, re, rl, rws})
+    if (overlap(rc, in)) return KLA_ERR_INVALID_ARG;
+  for (const Range &in : {rq, rk, rv, ra, re, rl})
+    if (overlap(rws, in)) return KLA_ERR_INVALID_ARG;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  kla::CcqArgs c;
+  c.q = q;
+  c.k = k;
+  c.lambda = lambda;
+  c.cu_seqlens = nullptr;
+  c.n_seqs = n_seqs;
+  c.seq_len_dense = 1;
+  c.H = H;
+  c.D = dk;
+  c.bf16_inputs = dtype == KLA_BF16;
+  c.ccq_in = nullptr;
+  c.ccq_out = ccq_state;
+  c.qh = workspace;
+  c.ql = nullptr;
+  hipError_t e = kla::launch_ccq_decode(c, st);
+
+  kla::DecodeArgs a;
+  a.q = workspace;  // q_clean, fp32
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.eta = eta;
+  a.state = state;
+  a.o = o;
+  a.n_seqs = n_seqs;
+  a.H = H;
+  a.D = dk;
+  a.eps = eps;
+  a.beta_direct = beta_mode == KLA_BETA_DIRECT;
+  a.q_is_f32 = 1;
+  if (e == hipSuccess)
+    e = dtype == KLA_BF16 ? kla::launch_decode_bf16(a, st) : kla::launch_decode_f32(a, st);
+  return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,406 @@
+// Curvature-conditioned read (CCQ) for the KLA path on gfx950: the query
+// cleaning that runs before the prefill / decode read.
+//
+// "Don't Read Everything: A Curvature-Conditioned Query for Linear
+// Attention" (sections "Derivacao Teorica" and "O Mecanismo"): the read uses
+//   q_clean_t = q_t - lambda_t Sigma_t q_t,
+// Sigma_t the covariance of the keys j <= t with uniform weights (the
+// Hessian at q = 0 of log sum_j exp(k_j^T q)):
+//   Sigma_t q = P_t q / n_t - m_t (m_t . q) / n_t^2,
+//   P_t = sum_{j<=t} k_j k_j^T,  m_t = sum_{j<=t} k_j,  n_t = number of keys.
+// The write is untouched, so the KLA kernels then read with q_clean.
+//
+// The running sums (P, m, n) are the extra state per head, one record of
+// CcqStride(D) floats: [P row-major | m | n | 3 pad].
+//
+// Prefill pre-pass, chunk form.  For a chunk of n <= 64 tokens with sums
+// (P, m, n0) at its start:
+//   P_t q_t   = (Q P)_t + (lower(Q K^T) K)_t        (t >= s inside the chunk)
+//   m_t       = m + prefix sums of the chunk's keys
+//   m_t . q_t = m . q_t + row sums of lower(Q K^T)
+//   P += K^T K (summed over the chunk first, then added: two-level sums)
+// Mapping as the fp32 prefill kernel: one workgroup of 4 waves per
+// (sequence, head, 64 columns), each wave owning 16 columns of P in MFMA
+// accumulator tiles, every contraction on the fp32 MFMA.  The columns of
+// q_clean follow the columns of P; both workgroups of a (sequence, head)
+// keep the whole m.  Output: q_clean as fp32, or as a bf16 hi / lo pair
+// (q_clean = hi + lo to 2^-17), for the bf16 read.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kla_device.h"
+#include "kla_internal.h"
+
+namespace kla {
+namespace {
+
+template <int D>
+struct CcqSmem {
+  static constexpr int LDK = D + 4;
+  static constexpr int LDP = C + 4;
+  static constexpr int LDC = DVB + 4;
+  alignas(16) float Kr[C * LDK];   // keys of the chunk (fp32)
+  alignas(16) float Qr[C * LDK];   // queries of the chunk (fp32)
+  alignas(16) float G[C * LDP];    // lower(Q K^T), zero above the diagonal
+  alignas(16) float cm[C * LDC];   // m_t for this workgroup's columns
+  alignas(16) float msum[D];       // m at the chunk start (all columns)
+  alignas(16) float md[C];         // m . q_t
+  alignas(16) float mq[C];         // m_t . q_t
+  alignas(16) float lam[C];
+};
+
+template <typename E>
+__device__ inline void seg_to_f32(const uint4 &u, float *dst);
+template <>
+__device__ inline void seg_to_f32<__bf16>(const uint4 &u, float *dst) {
+  const bf16x8 b = __builtin_bit_cast(bf16x8, u);
+  *reinterpret_cast<f32x4 *>(dst) = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+  *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{(float)b[4], (float)b[5], (float)b[6], (float)b[7]};
+}
+template <>
+__device__ inline void seg_to_f32<float>(const uint4 &u, float *dst) {
+  *reinterpret_cast<f32x4 *>(dst) =
+      f32x4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
+}
+
+// OUT_BF16: write q_clean as bf16 hi (qh) and lo (ql) planes; else fp32 to qh.
+template <typename E, int D, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void ccq_query_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const float *__restrict__ lambda,
+    const int32_t *__restrict__ cu_seqlens, int64_t seq_len_dense, int H,
+    const float *__restrict__ ccq_in, float *__restrict__ ccq_out, void *__restrict__ qh,
+    void *__restrict__ ql) {
+  using SM = CcqSmem<D>;
+  constexpr int NB = D / DVB;
+  constexpr int NST = D / 16;
+  constexpr int LDK = SM::LDK, LDP = SM::LDP, LDC = SM::LDC;
+  constexpr int SEG_EL = 16 / sizeof(E);
+  constexpr int SEG_ROW = D / SEG_EL;
+  constexpr int NSEG = C * SEG_ROW / kThreads;
+  static_assert(NSEG * kThreads == C * SEG_ROW, "staging tiling");
+  constexpr int64_t REC = (int64_t)D * D + D + 4;  // record stride (floats)
+
+  __shared__ SM sm;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int j = l >> 4, c16 = l & 15;
+
+  const int64_t lb = logical_block();
+  const int nb = (int)(lb % NB);
+  const int64_t sh = lb / NB;
+  const int h = (int)(sh % H);
+  const int64_t s = sh / H;
+  const int64_t bos = cu_seqlens ? (int64_t)cu_seqlens[s] : s * seq_len_dense;
+  const int64_t eos = cu_seqlens ? (int64_t)cu_seqlens[s + 1] : bos + seq_len_dense;
+  const int cl = 16 * w + c16;       // column within this workgroup's block
+  const int col = nb * DVB + cl;     // column of P and of q_clean
+
+  // G above the diagonal blocks stays zero
+  for (int i = tid; i < C * LDP; i += kThreads) sm.G[i] = 0.f;
+
+  // start sums: P tiles (rows 16t+4j+i, column col), m, n
+  f32x4 P[NST];
+  float n0;
+  {
+    const rsrc_t rr = make_rsrc(ccq_in ? ccq_in + sh * REC : lambda, ccq_in ? REC * 4 : 0);
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) P[t][i] = buf_ld4(rr, (uint32_t)(((16 * t + 4 * j + i) * D + col) * 4));
+    if (tid < D) sm.msum[tid] = buf_ld4(rr, (uint32_t)((D * D + tid) * 4));
+    n0 = buf_ld4(rr, (uint32_t)((D * D + D) * 4));
+  }
+
+  uint4 kreg[NSEG], qreg[NSEG];
+  float lreg = 0.f;
+  auto fetch = [&](int64_t t0) {
+    const int64_t nn = (eos - t0) < C ? (eos - t0) : C;
+    const int64_t rowb = (int64_t)H * D * sizeof(E);
+    const rsrc_t rk = make_rsrc(k + t0 * H * (int64_t)D, nn * rowb);
+    const rsrc_t rq = make_rsrc(q + t0 * H * (int64_t)D, nn * rowb);
+#pragma unroll
+    for (int u = 0; u < NSEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+      const uint32_t off = (uint32_t)((r * H + h) * D + cs * SEG_EL) * sizeof(E);
+      kreg[u] = buf_ld16(rk, off);
+      qreg[u] = buf_ld16(rq, off);
+    }
+    if (w == 0) {
+      const rsrc_t rl = make_rsrc(lambda + t0 * H, nn * H * 4);
+      lreg = buf_ld4(rl, (uint32_t)(l * H + h) * 4);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int u = 0; u < NSEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+      seg_to_f32<E>(kreg[u], &sm.Kr[r * LDK + cs * SEG_EL]);
+      seg_to_f32<E>(qreg[u], &sm.Qr[r * LDK + cs * SEG_EL]);
+    }
+    if (w == 0) sm.lam[l] = lreg;
+  };
+
+  fetch(bos);
+  stage();
+  for (int64_t tok0 = bos; tok0 < eos; tok0 += C) {
+    const int n = (int)((eos - tok0) < C ? (eos - tok0) : C);
+    lds_barrier();  // chunk staged (and m of the chunk start final)
+    fetch(tok0 + C);
+
+    // ---- lower(Q K^T) tiles, Q P for this wave's columns, m . q_t ----------
+    {
+      // tiles (bi, bj), bj <= bi, numbered 0..9 in row order; wave w takes
+      // tiles w, w + 4, w + 8
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int tn = w + 4 * u;
+        if (tn < 10) {
+          const int bi = (tn >= 1) + (tn >= 3) + (tn >= 6);
+          const int bj = tn - bi * (bi + 1) / 2;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k0 = 0; k0 < D; k0 += 4)
+            acc = mma(sm.Qr[(16 * bi + c16) * LDK + k0 + j], sm.Kr[(16 * bj + c16) * LDK + k0 + j], acc);
+          // acc[i] = (Q K^T)[16bi + 4j + i][16bj + c16]
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int R = 16 * bi + 4 * j + i, Sc = 16 * bj + c16;
+            sm.G[R * LDP + Sc] = R >= Sc ? acc[i] : 0.f;
+          }
+        }
+      }
+    }
+    f32x4 PQ[4];
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < NST; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mma(sm.Qr[(16 * bi + c16) * LDK + 16 * t + 4 * j + i], P[t][i], acc);
+      PQ[bi] = acc;  // (Q P)[16bi + 4j + i][col]
+    }
+    if (w == 0) {
+      float d = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < D; ++c) d += sm.msum[c] * sm.Qr[l * LDK + c];
+      sm.md[l] = d;
+    }
+    lds_barrier();
+
+    // ---- m_t . q_t (row sums of lower(Q K^T)); m_t for this block's columns --
+    if (w == 0) {
+      float rs = sm.md[l];
+#pragma unroll 8
+      for (int c = 0; c < C; ++c) rs += sm.G[l * LDP + c];
+      sm.mq[l] = rs;
+    } else if (w == 1) {
+      // one column per lane: running key sums over the chunk's tokens
+      float run = sm.msum[nb * DVB + l];
+      for (int t = 0; t < C; ++t) {
+        run += sm.Kr[t * LDK + nb * DVB + l];
+        sm.cm[t * LDC + l] = run;
+      }
+    }
+    lds_barrier();
+
+    // ---- P_t q_t = (Q P)_t + (lower(Q K^T) K)_t; q_clean -----------------------
+    f32x4 Kc[4];  // K[16mt + 4j + i][col], the B operand of the two products below
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Kc[mt][i] = sm.Kr[(16 * mt + 4 * j + i) * LDK + col];
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      f32x4 acc = PQ[bi];
+#pragma unroll
+      for (int mt = 0; mt <= bi; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mma(sm.G[(16 * bi + c16) * LDP + 16 * mt + 4 * j + i], Kc[mt][i], acc);
+      PQ[bi] = acc;
+    }
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * bi + 4 * j + i;
+        if (r < n) {
+          const float nt = n0 + (float)(r + 1);
+          const float inv = 1.f / nt;
+          const float sq = PQ[bi][i] * inv - (sm.cm[r * LDC + cl] * inv) * (sm.mq[r] * inv);
+          const float qc = sm.Qr[r * LDK + col] - sm.lam[r] * sq;
+          const int64_t idx = ((tok0 + r) * H + h) * (int64_t)D + col;
+          if constexpr (OUT_BF16) {
+            const __bf16 hi = static_cast<__bf16>(qc);
+            static_cast<__bf16 *>(qh)[idx] = hi;
+            static_cast<__bf16 *>(ql)[idx] = static_cast<__bf16>(qc - static_cast<float>(hi));
+          } else {
+            static_cast<float *>(qh)[idx] = qc;
+          }
+        }
+      }
+
+    // ---- P += K^T K (the chunk's sum first), m, n -----------------------------
+    {
+      f32x4 Pc[NST];
+#pragma unroll
+      for (int t = 0; t < NST; ++t) {
+        Pc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            Pc[t] = mma(sm.Kr[(16 * mt + 4 * j + i) * LDK + 16 * t + c16], Kc[mt][i], Pc[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < NST; ++t) P[t] += Pc[t];
+    }
+    lds_barrier();  // every read of this chunk's K, Q, m is done
+    if (tid < D) {
+      float a = 0.f;
+      for (int t = 0; t < C; ++t) a += sm.Kr[t * LDK + tid];
+      sm.msum[tid] += a;
+    }
+    n0 += (float)n;
+    lds_barrier();
+    stage();
+  }
+
+  if (ccq_out) {
+    float *rec = ccq_out + sh * REC;
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rec[(16 * t + 4 * j + i) * D + col] = P[t][i];
+    if (nb == 0) {
+      if (tid < D) rec[D * D + tid] = sm.msum[tid];
+      if (tid < 4) rec[D * D + D + tid] = tid == 0 ? n0 : 0.f;  // n, then the zero pad
+    }
+  }
+}
+
+// One decode token: the sums take the new key, then q_clean (fp32) for the
+// read.  One workgroup of 256 threads per (sequence, head); thread (row
+// group, column group) holds rows rg + NRG i, columns 4 cq .. 4 cq + 3 of P.
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void ccq_decode_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const float *__restrict__ lambda,
+    float *__restrict__ ccq_state, float *__restrict__ qc_out) {
+  constexpr int NQ = D / 4, NRG = kThreads / NQ, RPT = D / NRG;
+  static_assert(NQ * NRG == kThreads && RPT * NRG == D, "tiling");
+  constexpr int64_t REC = (int64_t)D * D + D + 4;
+  __shared__ float sq[D], sk[D], sm_m[D], pr[NRG][D], red[2];
+  const int64_t sh = blockIdx.x;
+  const int t = threadIdx.x, cq = t % NQ, rg = t / NQ;
+  float *rec = ccq_state + sh * REC;
+  float4 p[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) p[i] = *reinterpret_cast<const float4 *>(rec + (rg + NRG * i) * D + 4 * cq);
+  if (t < D) {
+    sq[t] = static_cast<float>(q[sh * D + t]);
+    sk[t] = static_cast<float>(k[sh * D + t]);
+  }
+  __syncthreads();
+  // P += k k^T; partial (P q) over this thread's rows for its 4 columns
+  // (P is symmetric: (P q)_c = sum_r P[r][c] q[r])
+  const float4 kc = *reinterpret_cast<const float4 *>(&sk[4 * cq]);
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg + NRG * i;
+    const float kr = sk[r], qr = sq[r];
+    p[i].x += kr * kc.x; p[i].y += kr * kc.y; p[i].z += kr * kc.z; p[i].w += kr * kc.w;
+    acc.x += p[i].x * qr; acc.y += p[i].y * qr; acc.z += p[i].z * qr; acc.w += p[i].w * qr;
+    *reinterpret_cast<float4 *>(rec + r * D + 4 * cq) = p[i];
+  }
+  *reinterpret_cast<float4 *>(&pr[rg][4 * cq]) = acc;
+  if (t < 64) {
+    // m += k, n += 1 and m . q (wave 0)
+    float mq = 0.f;
+    for (int c = t; c < D; c += 64) {
+      const float m = rec[D * D + c] + sk[c];
+      rec[D * D + c] = m;
+      sm_m[c] = m;
+      mq += m * sq[c];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mq += __shfl_xor(mq, off, 64);
+    if (t == 0) {
+      const float n = rec[D * D + D] + 1.f;
+      rec[D * D + D] = n;
+      red[0] = mq;
+      red[1] = n;
+    }
+  }
+  __syncthreads();
+  if (t < D) {
+    float pq = 0.f;
+#pragma unroll
+    for (int r = 0; r < NRG; ++r) pq += pr[r][t];
+    const float inv = 1.f / red[1];
+    const float m = sm_m[t];
+    const float sg = pq * inv - (m * inv) * (red[0] * inv);
+    qc_out[sh * D + t] = sq[t] - lambda[sh] * sg;
+  }
+}
+
+// o += o2 (fp32, n elements; n a multiple of 4, 16-byte aligned)
+__global__ __launch_bounds__(256) void add_kernel(float *__restrict__ o, const float *__restrict__ o2,
+                                                  int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float4 a = reinterpret_cast<float4 *>(o)[i];
+    const float4 b = reinterpret_cast<const float4 *>(o2)[i];
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    reinterpret_cast<float4 *>(o)[i] = a;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ccq_query(const CcqArgs &a, hipStream_t st) {
+  const int64_t grid = (int64_t)a.n_seqs * a.H * (a.D / DVB);
+  const dim3 g((unsigned)grid), b(kThreads);
+#define KLA_CCQ_LAUNCH(E, DD, BF)                                                                   \
+  hipLaunchKernelGGL((ccq_query_kernel<E, DD, BF>), g, b, 0, st, static_cast<const E *>(a.q),       \
+                     static_cast<const E *>(a.k), a.lambda, a.cu_seqlens, a.seq_len_dense, a.H,     \
+                     a.ccq_in, a.ccq_out, a.qh, a.ql)
+  if (a.bf16_inputs) {
+    if (a.D == 128) KLA_CCQ_LAUNCH(__bf16, 128, true); else KLA_CCQ_LAUNCH(__bf16, 64, true);
+  } else {
+    if (a.D == 128) KLA_CCQ_LAUNCH(float, 128, false); else KLA_CCQ_LAUNCH(float, 64, false);
+  }
+#undef KLA_CCQ_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_ccq_decode(const CcqArgs &a, hipStream_t st) {
+  const dim3 g((unsigned)((int64_t)a.n_seqs * a.H)), b(kThreads);
+  float *qc = static_cast<float *>(a.qh);
+  if (a.bf16_inputs) {
+    if (a.D == 128)
+      hipLaunchKernelGGL((ccq_decode_kernel<__bf16, 128>), g, b, 0, st, static_cast<const __bf16 *>(a.q),
+                         static_cast<const __bf16 *>(a.k), a.lambda, a.ccq_out, qc);
+    else
+      hipLaunchKernelGGL((ccq_decode_kernel<__bf16, 64>), g, b, 0, st, static_cast<const __bf16 *>(a.q),
+                         static_cast<const __bf16 *>(a.k), a.lambda, a.ccq_out, qc);
+  } else {
+    if (a.D == 128)
+      hipLaunchKernelGGL((ccq_decode_kernel<float, 128>), g, b, 0, st, static_cast<const float *>(a.q),
+                         static_cast<const float *>(a.k), a.lambda, a.ccq_out, qc);
+    else
+      hipLaunchKernelGGL((ccq_decode_kernel<float, 64>), g, b, 0, st, static_cast<const float *>(a.q),
+                         static_cast<const float *>(a.k), a.lambda, a.ccq_out, qc);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_add(float *o, const float *o2, int64_t n, hipStream_t st) {
+  const int64_t n4 = n / 4;
+  const int64_t blocks = (n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096;
+  if (blocks > 0) hipLaunchKernelGGL(add_kernel, dim3((unsigned)blocks), dim3(256), 0, st, o, o2, n4);
+  return hipGetLastError();
+}
+
+}  // namespace kla

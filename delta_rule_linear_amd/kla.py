@@ -261,3 +261,105 @@ def _decode(beta, q, k, v, alpha, eta, state, eps, o, stream, channel_decay=Fals
     if st != KLA_OK:
         raise KLAError(st)
     return o
+
+
+# ---- curvature-conditioned read (C ABI kla_*_ccq) ---------------------------
+_lib.kla_ccq_state_floats.restype = ctypes.c_size_t
+_lib.kla_ccq_state_floats.argtypes = [ctypes.c_int32]
+_lib.kla_fwd_chunked_ccq_workspace_size.restype = ctypes.c_size_t
+_lib.kla_fwd_chunked_ccq_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.c_int]
+_lib.kla_decode_step_ccq_workspace_size.restype = ctypes.c_size_t
+_lib.kla_decode_step_ccq_workspace_size.argtypes = [ctypes.c_int32] * 3
+_lib.kla_fwd_chunked_ccq.restype = ctypes.c_int
+_lib.kla_fwd_chunked_ccq.argtypes = [_vp, _vp, _vp, _fp, _fp, _fp, _i32p, ctypes.c_int32,
+                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int,
+                                     ctypes.c_int, _fp, _fp, _fp, _fp, _fp, _vp, ctypes.c_size_t,
+                                     _vp]
+_lib.kla_decode_step_ccq.restype = ctypes.c_int
+_lib.kla_decode_step_ccq.argtypes = [_vp, _vp, _vp, _fp, _fp, _fp, _fp, _fp, _fp, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp,
+                                     ctypes.c_size_t, _vp]
+
+
+def kla_ccq_state_floats(dk) -> int:
+    """fp32 values per (sequence, head) in the curvature-conditioned read's
+    running sums: [sum k k^T | sum k | n | pad]."""
+    return int(_lib.kla_ccq_state_floats(dk))
+
+
+def kla_fwd_chunked_ccq(q, k, v, alpha, eta, lam, cu_seqlens=None, initial_state=None,
+                        ccq_state=None, eps=1e-6, chunk=64, beta_mode="kaczmarz",
+                        output_final_state=False, output_ccq_state=False, o=None,
+                        final_state=None, ccq_out=None, workspace=None, stream=None):
+    """Prefill with the curvature-conditioned read (C ABI `kla_fwd_chunked_ccq`):
+    o_t = S_t^T (q_t - lam_t Sigma_t q_t), Sigma_t the covariance of the keys
+    so far.  lam: [tok, H] (or [B, T, H]) fp32.  ccq_state / ccq_out:
+    [n_seqs, H, kla_ccq_state_floats(dk)] fp32 running sums.  Returns
+    (o, final_state or None, ccq_out or None)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    if alpha is not None:
+        _need(alpha, "alpha", torch.float32)
+    _need(eta, "eta", torch.float32)
+    _need(lam, "lambda", torch.float32)
+    dk, dv, H = q.shape[-1], v.shape[-1], q.shape[-2]
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        n_seqs, total = cu_seqlens.numel() - 1, q.shape[0]
+    elif q.dim() == 4:
+        n_seqs, total = q.shape[0], q.shape[0] * q.shape[1]
+    else:
+        n_seqs, total = 1, q.shape[0]
+    rec = kla_ccq_state_floats(dk)
+    for name, t in (("initial_state", initial_state), ("ccq_state", ccq_state)):
+        if t is not None:
+            _need(t, name, torch.float32)
+    if o is None:
+        o = torch.empty(v.shape, dtype=torch.float32, device=v.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n_seqs, H, dk, dv), dtype=torch.float32, device=q.device)
+    if ccq_out is None and output_ccq_state:
+        ccq_out = torch.empty((n_seqs, H, rec), dtype=torch.float32, device=q.device)
+    ws_bytes = int(_lib.kla_fwd_chunked_ccq_workspace_size(total, H, dk, dv, _dtype_code(q)))
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.kla_fwd_chunked_ccq(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(lam),
+                                  _ptr(cu_seqlens), n_seqs, total, H, dk, dv, chunk, float(eps),
+                                  _dtype_code(q), _beta_code(beta_mode), _ptr(initial_state),
+                                  _ptr(ccq_state), _ptr(o), _ptr(final_state), _ptr(ccq_out),
+                                  _ptr(workspace), ws_len, _stream(stream))
+    if st != KLA_OK:
+        raise KLAError(st)
+    return o, final_state, ccq_out
+
+
+def kla_decode_step_ccq(q, k, v, alpha, eta, lam, state, ccq_state, eps=1e-6,
+                        beta_mode="kaczmarz", o=None, workspace=None, stream=None):
+    """One decode step with the curvature-conditioned read (C ABI
+    `kla_decode_step_ccq`); `state` and `ccq_state` are updated in place.
+    Returns o [N, H, dv] fp32."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    if alpha is not None:
+        _need(alpha, "alpha", torch.float32)
+    for name, t in (("eta", eta), ("lambda", lam), ("state", state), ("ccq_state", ccq_state)):
+        _need(t, name, torch.float32)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=torch.float32, device=q.device)
+    ws_bytes = int(_lib.kla_decode_step_ccq_workspace_size(N, H, dk))
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_len = workspace.numel() * workspace.element_size()
+    st = _lib.kla_decode_step_ccq(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(lam),
+                                  _ptr(state), _ptr(ccq_state), _ptr(o), N, H, dk, dv, float(eps),
+                                  _dtype_code(q), _beta_code(beta_mode), _ptr(workspace), ws_len,
+                                  _stream(stream))
+    if st != KLA_OK:
+        raise KLAError(st)
+    return o

@@ -254,6 +254,74 @@ kla_status kla_decode_step_kda(const void *q, const void *k, const void *v,
                                int32_t n_seqs, int32_t H, int32_t dk, int32_t dv, float eps,
                                kla_dtype dtype, kla_beta_mode beta_mode, void *stream);
 
+/*
+ * Curvature-conditioned read ("Don't Read Everything: A Curvature-Conditioned
+ * Query for Linear Attention", sections "Derivacao Teorica", "O Mecanismo"
+ * and "Integracao").  Only the read changes: with Sigma_t the covariance of
+ * the keys j <= t of the sequence, weighted uniformly (the Hessian at q = 0
+ * of log sum_j exp(k_j^T q)),
+ *   q_clean_t = q_t - lambda_t Sigma_t q_t,   o_t = S_t^T q_clean_t,
+ *   Sigma_t q = P_t q / n_t - m_t (m_t . q) / n_t^2,
+ *   P_t = sum_{j<=t} k_j k_j^T,  m_t = sum_{j<=t} k_j,  n_t = number of keys.
+ * The running sums are the extra state per (sequence, head): one record of
+ * kla_ccq_state_floats(dk) = dk*dk + dk + 4 fp32, [P row-major | m | n | pad].
+ * n is held in fp32 (exact up to 2^24 keys).
+ */
+size_t kla_ccq_state_floats(int32_t dk);
+
+/* Workspace bytes of kla_fwd_chunked_ccq: the cleaned queries (bf16 inputs:
+ * a bf16 hi and lo pair, plus the lo read's fp32 output; fp32 inputs: fp32),
+ * 256-byte rounded parts.  0 when total_tok <= 0. */
+size_t kla_fwd_chunked_ccq_workspace_size(int64_t total_tok, int32_t H, int32_t dk, int32_t dv,
+                                          kla_dtype dtype);
+
+/*
+ * Prefill with the curvature-conditioned read.  Launches on the stream:
+ *   1. the query cleaning for every token (chunked: Q P + lower(Q K^T) K,
+ *      the running sums carried over chunks) into the workspace;
+ *   2. bf16 inputs: the bf16 prefill reading with the lo part (no end
+ *      state), then with the hi part (end state), then o += the lo output
+ *      (o is linear in the query and the state does not depend on it);
+ *      fp32 inputs: the fp32 prefill reading with the fp32 cleaned query.
+ *   lambda      [total_tok, H] fp32, the contraction gate (any real value).
+ *   ccq_in      [n_seqs, H, kla_ccq_state_floats(dk)] fp32 start sums, or NULL
+ *               for zero (a sequence that starts here).
+ *   ccq_out     same shape, written with the end sums, or NULL.  It must not
+ *               overlap any other argument (ccq_in included).
+ *   workspace   >= kla_fwd_chunked_ccq_workspace_size(...) bytes, 16-byte
+ *               aligned, overlapping nothing; contents unspecified on return.
+ * Other arguments as kla_fwd_chunked_ex.  Errors: as kla_fwd_chunked_ex,
+ * plus KLA_ERR_INVALID_ARG for a null lambda or an overlapping ccq_out,
+ * KLA_ERR_WORKSPACE for a short workspace.
+ */
+kla_status kla_fwd_chunked_ccq(const void *q, const void *k, const void *v,
+                               const float *alpha, const float *eta, const float *lambda,
+                               const int32_t *cu_seqlens, int32_t n_seqs, int64_t total_tok,
+                               int32_t H, int32_t dk, int32_t dv, int32_t chunk, float eps,
+                               kla_dtype dtype, kla_beta_mode beta_mode,
+                               const float *initial_state, const float *ccq_in, float *o,
+                               float *final_state, float *ccq_out, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of kla_decode_step_ccq: the fp32 cleaned query per
+ * (sequence, head), rounded to 256. */
+size_t kla_decode_step_ccq_workspace_size(int32_t n_seqs, int32_t H, int32_t dk);
+
+/*
+ * One decode step with the curvature-conditioned read: ccq_state [n_seqs, H,
+ * kla_ccq_state_floats(dk)] takes the new key (in place), the cleaned query
+ * goes to the workspace, and the decode step reads with it (state updated
+ * in place as kla_decode_step_ex).  lambda [n_seqs, H] fp32.  Errors: as
+ * kla_decode_step_ex, plus KLA_ERR_INVALID_ARG for a null lambda, ccq_state
+ * or workspace or any overlap, KLA_ERR_WORKSPACE for a short workspace.
+ */
+kla_status kla_decode_step_ccq(const void *q, const void *k, const void *v,
+                               const float *alpha, const float *eta, const float *lambda,
+                               float *state, float *ccq_state, float *o, int32_t n_seqs,
+                               int32_t H, int32_t dk, int32_t dv, float eps, kla_dtype dtype,
+                               kla_beta_mode beta_mode, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *kla_status_string(kla_status s);
 

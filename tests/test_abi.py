@@ -49,6 +49,19 @@ def lib():
     L.kla_fwd_chunked_kda.argtypes = L.kla_fwd_chunked_ex.argtypes
     L.kla_decode_step_kda.restype = ctypes.c_int
     L.kla_decode_step_kda.argtypes = L.kla_decode_step_ex.argtypes
+    L.kla_ccq_state_floats.restype = ctypes.c_size_t
+    L.kla_ccq_state_floats.argtypes = [ctypes.c_int32]
+    L.kla_fwd_chunked_ccq_workspace_size.restype = ctypes.c_size_t
+    L.kla_fwd_chunked_ccq_workspace_size.argtypes = [ctypes.c_int64] + [ctypes.c_int32] * 3 + [ctypes.c_int]
+    L.kla_decode_step_ccq_workspace_size.restype = ctypes.c_size_t
+    L.kla_decode_step_ccq_workspace_size.argtypes = [ctypes.c_int32] * 3
+    V, F = ctypes.c_void_p, ctypes.c_float
+    L.kla_fwd_chunked_ccq.restype = ctypes.c_int
+    L.kla_fwd_chunked_ccq.argtypes = [V] * 7 + [ctypes.c_int32, ctypes.c_int64] + [ctypes.c_int32] * 4 + [
+        F, ctypes.c_int, ctypes.c_int] + [V] * 6 + [ctypes.c_size_t, V]
+    L.kla_decode_step_ccq.restype = ctypes.c_int
+    L.kla_decode_step_ccq.argtypes = [V] * 9 + [ctypes.c_int32] * 4 + [F, ctypes.c_int, ctypes.c_int, V,
+                                                                        ctypes.c_size_t, V]
     L.kla_status_string.restype = ctypes.c_char_p
     L.kla_status_string.argtypes = [ctypes.c_int]
     L.kla_version.restype = ctypes.c_char_p
@@ -60,7 +73,9 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["kla_fwd_chunked", "kla_fwd_chunked_ex",
                                            "kla_fwd_chunked_split", "kla_fwd_chunked_kda",
-                                           "kla_decode_step_kda",
+                                           "kla_decode_step_kda", "kla_ccq_state_floats",
+                                           "kla_fwd_chunked_ccq", "kla_fwd_chunked_ccq_workspace_size",
+                                           "kla_decode_step_ccq", "kla_decode_step_ccq_workspace_size",
                                            "kla_fwd_chunked_split_workspace_size",
                                            "kla_fwd_chunked_workspace_size", "kla_decode_step",
                                            "kla_decode_step_ex", "kla_status_string",
@@ -176,6 +191,67 @@ def test_fwd_kda_rejects_unknown_beta_mode(lib):
     assert lib.kla_fwd_chunked_kda(*a[:14], 5, *a[14:]) == INVALID
 
 
+def test_ccq_sizes(lib):
+    assert lib.kla_ccq_state_floats(128) == 128 * 128 + 128 + 4
+    th = 100 * 2
+    r = lambda x: (x + 255) // 256 * 256
+    assert lib.kla_fwd_chunked_ccq_workspace_size(100, 2, 64, 64, 1) == 2 * r(th * 64 * 2) + r(th * 64 * 4)
+    assert lib.kla_fwd_chunked_ccq_workspace_size(100, 2, 64, 64, 0) == r(th * 64 * 4)
+    assert lib.kla_fwd_chunked_ccq_workspace_size(0, 2, 64, 64, 1) == 0
+    assert lib.kla_decode_step_ccq_workspace_size(4, 2, 128) == r(4 * 2 * 128 * 4)
+
+
+def ccq_args(**over):
+    # fwd_args layout plus lambda, ccq_in/ccq_out and a workspace large enough
+    a = dict(q=BASE, k=BASE + 64 * MB, v=BASE + 128 * MB, alpha=BASE + 192 * MB,
+             eta=BASE + 200 * MB, lam=BASE + 208 * MB, cu=None, n_seqs=2, tok=128, H=2, dk=64,
+             dv=64, chunk=64, eps=1e-6, dtype=1, beta=0, s0=None, c0=None, o=BASE + 256 * MB,
+             s1=None, c1=None, ws=BASE + 512 * MB, wsb=1 << 24, stream=None)
+    a.update(over)
+    return [a[x] for x in ("q", "k", "v", "alpha", "eta", "lam", "cu", "n_seqs", "tok", "H", "dk",
+                           "dv", "chunk", "eps", "dtype", "beta", "s0", "c0", "o", "s1", "c1", "ws",
+                           "wsb", "stream")]
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(lam=None), INVALID),                  # the gate is required
+    (dict(wsb=0), WORKSPACE),
+    (dict(ws=BASE + 512 * MB + 8), INVALID),     # misaligned workspace
+    (dict(ws=BASE), INVALID),                   # workspace overlaps q
+    (dict(c1=BASE + 256 * MB + 64), INVALID),   # end sums overlap o
+    (dict(c0=BASE + 300 * MB, c1=BASE + 300 * MB), INVALID),  # end sums alias the start sums
+    (dict(c1=BASE + 300 * MB + 4), INVALID),    # misaligned end sums
+    (dict(beta=3), INVALID),
+    (dict(dk=96, dv=96), UNSUPPORTED),
+    (dict(n_seqs=0), INVALID),
+])
+def test_fwd_ccq_rejects(lib, over, code):
+    assert lib.kla_fwd_chunked_ccq(*ccq_args(**over)) == code
+
+
+def dccq_args(**over):
+    a = dict(q=BASE, k=BASE + MB, v=BASE + 2 * MB, alpha=BASE + 3 * MB, eta=BASE + 4 * MB,
+             lam=BASE + 5 * MB, state=BASE + 8 * MB, cs=BASE + 16 * MB, o=BASE + 64 * MB, N=4, H=2,
+             dk=128, dv=128, eps=1e-6, dtype=1, beta=0, ws=BASE + 128 * MB, wsb=1 << 20,
+             stream=None)
+    a.update(over)
+    return [a[x] for x in ("q", "k", "v", "alpha", "eta", "lam", "state", "cs", "o", "N", "H",
+                           "dk", "dv", "eps", "dtype", "beta", "ws", "wsb", "stream")]
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(lam=None), INVALID),
+    (dict(cs=None), INVALID),
+    (dict(ws=None), INVALID),
+    (dict(wsb=16), WORKSPACE),
+    (dict(cs=BASE + 8 * MB + 1024), INVALID),   # sums overlap the state
+    (dict(o=BASE + 16 * MB + 64), INVALID),     # o inside the sums
+    (dict(dk=32, dv=32), UNSUPPORTED),
+])
+def test_decode_ccq_rejects(lib, over, code):
+    assert lib.kla_decode_step_ccq(*dccq_args(**over)) == code
+
+
 def test_workspace_query(lib):
     assert lib.kla_fwd_chunked_workspace_size(8, 16384, 16, 128, 128, 64) == 0
 
@@ -227,6 +303,7 @@ def test_binding_names_match_the_abi():
     import delta_rule_linear_amd as pkg
     for name in ("kla_fwd_chunked", "kla_decode_step", "kla_fwd_chunked_ex", "kla_decode_step_ex",
                  "kla_fwd_chunked_split", "kla_fwd_chunked_kda", "kla_decode_step_kda",
+                 "kla_fwd_chunked_ccq", "kla_decode_step_ccq", "kla_ccq_state_floats",
                  "kla_fwd_chunked_workspace_size",
                  "kla_fwd_chunked_split_workspace_size", "kla_status_string", "kla_version"):
         assert callable(getattr(pkg, name))

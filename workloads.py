@@ -28,6 +28,9 @@ BLOCK tokens, alpha_ch = sigmoid(alpha_mu + N(0, 1)) fp32 [tb, H, dk], one
 decay per key channel (decode step i: SeedSequence([seed, 0x4B4441, i]),
 one block of N tokens).  The other tensors are drawn exactly as above.
 
+Curvature-conditioned read gate (ccq_gate): lambda = sigmoid(N(0, 1)) fp32
+[tok, H] from SeedSequence([seed, 0x434351]) (one stream, drawn in token order).
+
 Decode: ss.spawn(2) gives a state stream and a step stream.  The state is
 0.02 * N(0, 1) fp32 [N, H, dk, dv], drawn per sequence from
 PCG64(state_ss.spawn(N)[s]); step i draws one block of N tokens (as above)
@@ -130,6 +133,13 @@ def _channel_gates(seed, tok, H, dk, alpha_mu, step=None):
 
     list(_pool().map(one, range(nb)))
     return out
+
+
+def ccq_gate(seed, tok, H):
+    """lambda = sigmoid(N(0, 1)) fp32 [tok, H], the contraction gate of the
+    curvature-conditioned read."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0x434351])))
+    return torch.from_numpy(_sigmoid(rng.standard_normal((tok, H), dtype=np.float32)))
 
 
 def prefill(name=None, *, seed=0, n_seqs=None, T=None, lengths=None, H=None, d=None, dtype=None,
