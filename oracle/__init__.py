@@ -238,3 +238,69 @@ def decode_step_ccq(q, k, v, alpha, eta, lam, state, ccq_state, eps=1e-6, lib_pa
     if rc != 0:
         raise RuntimeError("kla_oracle_decode_step_ccq failed")
     return o, S, cs
+
+
+def _bwd_lib(lib):
+    if not getattr(lib, "_bwd_bound", False):
+        lib.kla_oracle_bwd_ex.restype = ctypes.c_int
+        lib.kla_oracle_bwd_ex.argtypes = [_dp, _dp, _dp, _dp, _dp, _i64p, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_double, ctypes.c_int, _dp, _dp, _dp, _dp,
+                                          _dp, _dp, _dp, _dp, _dp]
+        lib._bwd_bound = True
+    return lib
+
+
+def bwd(q, k, v, alpha, eta, d_o, cu_seqlens=None, eps=1e-6, initial_state=None,
+        d_final=None, lib_path=None, beta_mode="kaczmarz"):
+    """fp64 gradient of the KLA prefill (reverse sweep of the plain
+    recurrence, kla_oracle_bwd_ex).
+
+    Inputs as fwd, plus d_o (the loss's gradient with respect to o, shaped
+    like v) and d_final ([n_seqs, H, dk, dv] or None: the final state does
+    not reach the loss).  Returns a dict with dq, dk, dv, dalpha (None
+    when alpha is None), deta and dS0 ([n_seqs, H, dk, dv]), float64,
+    shaped like the corresponding inputs.
+    """
+    lib = _bwd_lib(_load(lib_path))
+    q, k, v, alpha, eta, d_o = (_f64(t) for t in (q, k, v, alpha, eta, d_o))
+    shapes = {"q": q.shape, "k": k.shape, "v": v.shape, "eta": eta.shape,
+              "alpha": None if alpha is None else alpha.shape}
+    if cu_seqlens is None:
+        if q.ndim == 4:
+            B, T = q.shape[0], q.shape[1]
+            cu = np.arange(B + 1, dtype=np.int64) * T
+        else:
+            cu = np.array([0, q.shape[0]], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    dk, dv = q.shape[-1], v.shape[-1]
+    H = q.shape[-2]
+    q = q.reshape(-1, H, dk)
+    k = k.reshape(-1, H, dk)
+    v = v.reshape(-1, H, dv)
+    d_o = d_o.reshape(-1, H, dv)
+    alpha = None if alpha is None else alpha.reshape(-1, H)
+    eta = eta.reshape(-1, H)
+    n_seqs = cu.shape[0] - 1
+    tok = q.shape[0]
+    if int(cu[-1]) != tok:
+        raise ValueError("cu_seqlens[-1] must equal the token count")
+    init = None if initial_state is None else _f64(initial_state).reshape(n_seqs, H, dk, dv)
+    dfin = None if d_final is None else _f64(d_final).reshape(n_seqs, H, dk, dv)
+    gq = np.zeros((tok, H, dk))
+    gk = np.zeros((tok, H, dk))
+    gv = np.zeros((tok, H, dv))
+    ga = None if alpha is None else np.zeros((tok, H))
+    ge = np.zeros((tok, H))
+    g0 = np.zeros((n_seqs, H, dk, dv))
+    rc = lib.kla_oracle_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta),
+                               cu.ctypes.data_as(_i64p), n_seqs, H, dk, dv, float(eps),
+                               _BETA[beta_mode], _ptr(init), _ptr(d_o), _ptr(dfin), _ptr(gq),
+                               _ptr(gk), _ptr(gv), _ptr(ga), _ptr(ge), _ptr(g0))
+    if rc != 0:
+        raise RuntimeError("kla_oracle_bwd_ex failed")
+    return {"dq": gq.reshape(shapes["q"]), "dk": gk.reshape(shapes["k"]),
+            "dv": gv.reshape(shapes["v"]),
+            "dalpha": None if ga is None else ga.reshape(shapes["alpha"]),
+            "deta": ge.reshape(shapes["eta"]), "dS0": g0}

@@ -44,6 +44,11 @@
  * where n counts the keys j <= t.  The running sums (sum k k^T, sum k, n)
  * are the extra state per head; a sequence may start from given sums.
  *
+ * Backward (kla_oracle_bwd_ex): the gradient of the prefill's outputs (o and
+ * the final state) with respect to q, k, v, alpha, eta and the initial
+ * state, by the reverse sweep of the same token loop (each forward line's
+ * adjoint, in reverse order; see the function).
+ *
  * This is the plain definition, token by token, in double precision,
  * with no blocking or chunking: the chunkwise algorithm of the GPU path
  * reaches the same result up to rounding.  Inputs arrive as doubles that
@@ -410,6 +415,158 @@ int kla_oracle_decode_step_ccq(const double *q, const double *k, const double *v
         kla_token(state + sh * sdim, e, qc, k + sh * dk, v + sh * dv, alpha ? alpha[sh] : 1.0,
                   eta[sh], eps, beta_direct, dk, dv, o + sh * dv);
         free(e);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
+ * Backward (reverse-mode gradient) of the prefill.
+ *
+ * The pages keep Gated DeltaNet's training algorithm and change only the
+ * step size (KLA summary, section "Implementacao"), so the gradient is
+ * the derivative of the same recurrence.  Given the loss's gradients with
+ * respect to every output o_t (d_o) and to each sequence's final state
+ * (d_final, or none), this returns the gradients of the loss with respect
+ * to q, k, v, alpha, eta and the initial state.
+ *
+ * It is the plain reverse sweep: the forward pass runs token by token and
+ * keeps every state; then, from the last token back, the adjoint of each of
+ * the five forward lines is applied in reverse order, with dS the gradient
+ * of the state just after the token's write:
+ *   (5) o = S^T q          dS += q d_o^T            dq  = S d_o
+ *   (4) S = S~ + b k e^T   dS~ = dS                 db  = k^T dS e
+ *                          dk  = b dS e             de  = b dS^T k
+ *   (3) e = v - S~^T k     dv  = de                 dS~ -= k de^T
+ *                          dk -= S~ de
+ *   (2) S~ = alpha S_prev  dalpha = <dS~, S_prev>   dS_prev = alpha dS~
+ *   (1) b = eta / (k.k + eps)
+ *                          deta = db / (k.k + eps)
+ *                          dk  -= 2 eta db / (k.k + eps)^2 k
+ * (with beta_direct: b = eta, deta = db and no k term).  After the first
+ * token of a sequence dS is the gradient of its initial state.
+ *
+ * Layouts as the forward; d_alpha may be NULL when alpha is NULL (no decay
+ * gate), d_final and d_initial may be NULL.
+ */
+int kla_oracle_bwd_ex(const double *q, const double *k, const double *v, const double *alpha,
+                      const double *eta, const int64_t *cu_seqlens, int n_seqs, int H, int dk,
+                      int dv, double eps, int beta_direct, const double *initial_state,
+                      const double *d_o, const double *d_final, double *dq, double *dk_out,
+                      double *dv_out, double *d_alpha, double *d_eta, double *d_initial)
+{
+    if (!q || !k || !v || !eta || !cu_seqlens || !d_o || !dq || !dk_out || !dv_out || !d_eta)
+        return -1;
+    if (alpha && !d_alpha) return -1;
+    if (n_seqs <= 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    for (int s = 0; s < n_seqs; ++s)
+        if (cu_seqlens[s + 1] < cu_seqlens[s]) return -1;
+    if (cu_seqlens[0] != 0) return -1;
+
+    const size_t sdim = (size_t)dk * dv;
+    int failed = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int s = 0; s < n_seqs; ++s) {
+        for (int h = 0; h < H; ++h) {
+            const int64_t t0 = cu_seqlens[s], L = cu_seqlens[s + 1] - t0;
+            const size_t sh = (size_t)s * H + h;
+            /* states S_0 .. S_L (the state after each token), the gradient
+             * dS, the decayed state S~ and the vectors e, de */
+            double *St = (double *)malloc(sizeof(double) * ((size_t)(L + 1) * sdim + 2 * sdim +
+                                                            2 * (size_t)dv));
+            if (!St) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            double *dS = St + (size_t)(L + 1) * sdim, *Sd = dS + sdim;
+            double *e = Sd + sdim, *de = e + dv;
+
+            /* forward, keeping every state */
+            if (initial_state)
+                memcpy(St, initial_state + sh * sdim, sizeof(double) * sdim);
+            else
+                memset(St, 0, sizeof(double) * sdim);
+            for (int64_t t = 0; t < L; ++t) {
+                const size_t th = (size_t)(t0 + t) * H + h;
+                double *S = St + (size_t)(t + 1) * sdim;
+                memcpy(S, St + (size_t)t * sdim, sizeof(double) * sdim);
+                kla_token(S, e, q + th * dk, k + th * dk, v + th * dv, alpha ? alpha[th] : 1.0,
+                          eta[th], eps, beta_direct, dk, dv, NULL);
+            }
+
+            /* reverse sweep */
+            if (d_final)
+                memcpy(dS, d_final + sh * sdim, sizeof(double) * sdim);
+            else
+                memset(dS, 0, sizeof(double) * sdim);
+            for (int64_t t = L - 1; t >= 0; --t) {
+                const size_t th = (size_t)(t0 + t) * H + h;
+                const double *qt = q + th * dk, *kt = k + th * dk, *vt = v + th * dv;
+                const double *gt = d_o + th * dv;
+                const double *S = St + (size_t)(t + 1) * sdim, *Sp = St + (size_t)t * sdim;
+                const double a = alpha ? alpha[th] : 1.0;
+                double *gq = dq + th * dk, *gk = dk_out + th * dk, *gv = dv_out + th * dv;
+
+                double kk = 0.0;
+                for (int i = 0; i < dk; ++i) kk += kt[i] * kt[i];
+                const double b = beta_direct ? eta[th] : eta[th] / (kk + eps);
+                /* recompute S~ and e of this token */
+                for (size_t x = 0; x < sdim; ++x) Sd[x] = a * Sp[x];
+                for (int j = 0; j < dv; ++j) e[j] = vt[j];
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j) e[j] -= Sd[(size_t)i * dv + j] * kt[i];
+
+                /* (5) */
+                for (int i = 0; i < dk; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        dS[(size_t)i * dv + j] += qt[i] * gt[j];
+                        acc += S[(size_t)i * dv + j] * gt[j];
+                    }
+                    gq[i] = acc;
+                }
+                /* (4) */
+                double db = 0.0;
+                for (int j = 0; j < dv; ++j) de[j] = 0.0;
+                for (int i = 0; i < dk; ++i) {
+                    double dse = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        dse += dS[(size_t)i * dv + j] * e[j];
+                        de[j] += dS[(size_t)i * dv + j] * kt[i];
+                    }
+                    db += kt[i] * dse;
+                    gk[i] = b * dse;
+                }
+                for (int j = 0; j < dv; ++j) de[j] *= b;
+                /* (3) */
+                for (int j = 0; j < dv; ++j) gv[j] = de[j];
+                for (int i = 0; i < dk; ++i) {
+                    double sde = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        sde += Sd[(size_t)i * dv + j] * de[j];
+                        dS[(size_t)i * dv + j] -= kt[i] * de[j];
+                    }
+                    gk[i] -= sde;
+                }
+                /* (2) */
+                double da = 0.0;
+                for (size_t x = 0; x < sdim; ++x) {
+                    da += dS[x] * Sp[x];
+                    dS[x] *= a;
+                }
+                if (d_alpha) d_alpha[th] = alpha ? da : 0.0;
+                /* (1) */
+                if (beta_direct) {
+                    d_eta[th] = db;
+                } else {
+                    d_eta[th] = db / (kk + eps);
+                    const double c = 2.0 * eta[th] * db / ((kk + eps) * (kk + eps));
+                    for (int i = 0; i < dk; ++i) gk[i] -= c * kt[i];
+                }
+            }
+            if (d_initial) memcpy(d_initial + sh * sdim, dS, sizeof(double) * sdim);
+            free(St);
+        }
     }
     return failed ? -1 : 0;
 }

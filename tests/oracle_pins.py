@@ -652,6 +652,131 @@ def pin_ccq_resume_and_decode(fwd, decode):
     o_l, S_l, c_l = fwd_ccq(q, k, v, alpha, eta, lam, eps=1e-4)
     assert rel(od[0], o_l[L]) < TIGHT and rel(Sd, S_l) < TIGHT and rel(cd, c_l) < TIGHT
 
+
+# ---- backward (gradient of the prefill) -------------------------------------
+
+def _bwd(fwd):
+    """The oracle's bwd bound to the build under test."""
+    import functools
+    import oracle
+    lp = getattr(fwd, "keywords", {}).get("lib_path")
+    return functools.partial(oracle.bwd, lib_path=lp)
+
+
+def _fd_check(fwd, bwd, q, k, v, alpha, eta, S0, d_o, d_fin, cu, eps, beta_mode, tol):
+    """Every gradient the reverse sweep returns equals the central finite
+    difference of L = sum(d_o * o) + sum(d_fin * S_final), with o and
+    S_final from the forward reference (pinned on its own above)."""
+    def loss(q, k, v, alpha, eta, S0):
+        o, S = fwd(q, k, v, alpha, eta, cu_seqlens=cu, eps=eps, initial_state=S0,
+                   beta_mode=beta_mode)
+        return float(np.sum(o * d_o) + np.sum(S * d_fin))
+
+    g = bwd(q, k, v, alpha, eta, d_o, cu_seqlens=cu, eps=eps, initial_state=S0, d_final=d_fin,
+            beta_mode=beta_mode)
+    args = {"q": q, "k": k, "v": v, "alpha": alpha, "eta": eta, "S0": S0}
+    names = {"q": "dq", "k": "dk", "v": "dv", "alpha": "dalpha", "eta": "deta", "S0": "dS0"}
+    for name, x in list(args.items()):
+        if x is None:
+            assert g[names[name]] is None
+            continue
+        fd = np.zeros_like(x)
+        h = 1e-6
+        for idx in np.ndindex(x.shape):
+            xp = x.copy()
+            xp[idx] += h
+            xm = x.copy()
+            xm[idx] -= h
+            fd[idx] = (loss(**dict(args, **{name: xp})) - loss(**dict(args, **{name: xm}))) / (2 * h)
+        assert rel(g[names[name]], fd) < tol, (name, rel(g[names[name]], fd))
+
+
+def pin_bwd_finite_differences(fwd, decode):
+    """The gradient of the prefill with respect to q, k, v, alpha, eta and the
+    initial state equals central finite differences of the forward
+    reference, over two packed sequences and an empty one, with a gradient
+    arriving both through o and through the final state."""
+    rng = np.random.default_rng(50)
+    lens = [5, 0, 4]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    L, H, dk, dv = int(cu[-1]), 2, 3, 2
+    q, k, v, alpha, eta = _rand_seq(rng, L, H, dk, dv)
+    S0 = rng.standard_normal((3, H, dk, dv))
+    d_o = rng.standard_normal((L, H, dv))
+    d_fin = rng.standard_normal((3, H, dk, dv))
+    _fd_check(fwd, _bwd(fwd), q, k, v, alpha, eta, S0, d_o, d_fin, cu, 1e-3, "kaczmarz", 1e-7)
+
+
+def pin_bwd_finite_differences_direct(fwd, decode):
+    """The same check for the direct step (beta = eta) without a decay gate
+    (DeltaNet), and for the direct step with decay (Gated DeltaNet)."""
+    rng = np.random.default_rng(51)
+    L, H, dk, dv = 6, 1, 3, 3
+    q, k, v, alpha, eta = _rand_seq(rng, L, H, dk, dv)
+    k = k / np.linalg.norm(k, axis=-1, keepdims=True) * 0.8  # a contraction for beta <= 1
+    S0 = rng.standard_normal((1, H, dk, dv))
+    d_o = rng.standard_normal((L, H, dv))
+    d_fin = rng.standard_normal((1, H, dk, dv))
+    cu = np.array([0, L])
+    _fd_check(fwd, _bwd(fwd), q, k, v, None, eta, S0, d_o, d_fin, cu, 1e-3, "direct", 1e-7)
+    _fd_check(fwd, _bwd(fwd), q, k, v, alpha, eta, S0, d_o, d_fin, cu, 1e-3, "direct", 1e-7)
+
+
+def pin_bwd_eta_zero_closed_form(fwd, decode):
+    """eta = 0: no write, o_t = g_t S0^T q_t and S_L = g_L S0 with
+    g_t = alpha_1 ... alpha_t.  The gradients then have closed forms:
+    dq_t = g_t S0 d_o_t;  dv = dk = 0;
+    dS0 = sum_t g_t q_t d_o_t^T + g_L d_fin;
+    dalpha_t = (1/alpha_t) (sum_{r>=t} g_r q_r^T S0 d_o_r + g_L <d_fin, S0>);
+    deta_t = k_t^T G_t e_t / (|k_t|^2 + eps) with e_t = v_t - g_t S0^T k_t and
+    G_t = sum_{r>=t} (g_r/g_t) q_r d_o_r^T + (g_L/g_t) d_fin."""
+    bwd = _bwd(fwd)
+    rng = np.random.default_rng(52)
+    L, H, dk, dv, eps = 7, 2, 4, 3, 1e-3
+    q, k, v, alpha, _ = _rand_seq(rng, L, H, dk, dv)
+    eta = np.zeros((L, H))
+    S0 = rng.standard_normal((1, H, dk, dv))
+    d_o = rng.standard_normal((L, H, dv))
+    d_fin = rng.standard_normal((1, H, dk, dv))
+    g = bwd(q, k, v, alpha, eta, d_o, eps=eps, initial_state=S0, d_final=d_fin)
+    assert np.max(np.abs(g["dv"])) == 0.0 and np.max(np.abs(g["dk"])) == 0.0
+    for h in range(H):
+        S, F = S0[0, h], d_fin[0, h]
+        gam = np.cumprod(alpha[:, h])
+        dq = np.stack([gam[t] * S @ d_o[t, h] for t in range(L)])
+        assert rel(g["dq"][:, h], dq) < TIGHT
+        dS0 = sum(gam[t] * np.outer(q[t, h], d_o[t, h]) for t in range(L)) + gam[-1] * F
+        assert rel(g["dS0"][0, h], dS0) < TIGHT
+        read = np.array([gam[r] * q[r, h] @ S @ d_o[r, h] for r in range(L)])
+        fin = gam[-1] * np.sum(F * S)
+        da = np.array([(read[t:].sum() + fin) / alpha[t, h] for t in range(L)])
+        assert rel(g["dalpha"][:, h], da) < TIGHT
+        de = np.zeros(L)
+        for t in range(L):
+            G = sum((gam[r] / gam[t]) * np.outer(q[r, h], d_o[r, h]) for r in range(t, L))
+            G = G + (gam[-1] / gam[t]) * F
+            e = v[t, h] - gam[t] * S.T @ k[t, h]
+            de[t] = k[t, h] @ G @ e / (k[t, h] @ k[t, h] + eps)
+        assert rel(g["deta"][:, h], de) < TIGHT
+
+
+def pin_bwd_linear_in_upstream(fwd, decode):
+    """The gradient is linear in (d_o, d_fin): the gradients for d_o alone and
+    for d_fin alone add up to the gradients for both."""
+    bwd = _bwd(fwd)
+    rng = np.random.default_rng(53)
+    L, H, dk, dv = 9, 2, 3, 4
+    q, k, v, alpha, eta = _rand_seq(rng, L, H, dk, dv)
+    S0 = rng.standard_normal((1, H, dk, dv))
+    d_o = rng.standard_normal((L, H, dv))
+    d_fin = rng.standard_normal((1, H, dk, dv))
+    both = bwd(q, k, v, alpha, eta, d_o, initial_state=S0, d_final=d_fin)
+    a = bwd(q, k, v, alpha, eta, d_o, initial_state=S0)
+    b = bwd(q, k, v, alpha, eta, np.zeros_like(d_o), initial_state=S0, d_final=d_fin)
+    for key in ("dq", "dk", "dv", "dalpha", "deta", "dS0"):
+        assert rel(a[key] + b[key], both[key]) < TIGHT, key
+
+
 ALL_PINS = [pin_worked_example, pin_orthogonal_projection, pin_min_norm_bruteforce,
             pin_exact_line_search, pin_normalised_gradient, pin_exact_recall, pin_eta_zero,
             pin_scalar_case, pin_gated_deltanet_form, pin_chunk_form, pin_packed_and_resume,
@@ -663,4 +788,6 @@ ALL_PINS = [pin_worked_example, pin_orthogonal_projection, pin_min_norm_brutefor
             pin_channel_untouched_channel, pin_channel_chunk_form,
             pin_channel_decode_is_one_token,
             pin_ccq_numpy_covariance, pin_ccq_logsumexp_hessian, pin_ccq_lambda_zero_and_state,
-            pin_ccq_constant_keys, pin_ccq_resume_and_decode]
+            pin_ccq_constant_keys, pin_ccq_resume_and_decode,
+            pin_bwd_finite_differences, pin_bwd_finite_differences_direct,
+            pin_bwd_eta_zero_closed_form, pin_bwd_linear_in_upstream]

@@ -128,6 +128,21 @@ MUTANTS.update({
     "ccq_ignores_start_sums": lambda s: s.replace("if (ccq_in)\n", "if (0)\n"),
 })
 
+MUTANTS.update({
+    "bwd_drops_residual_path": lambda s: s.replace("gk[i] -= sde;", "(void)sde;"),
+    "bwd_drops_step_norm_term": lambda s: s.replace("for (int i = 0; i < dk; ++i) gk[i] -= c * kt[i];",
+                                                    "(void)c;"),
+    "bwd_dalpha_from_new_state": lambda s: s.replace("da += dS[x] * Sp[x];", "da += dS[x] * S[x];"),
+    "bwd_state_grad_undecayed": lambda s: s.replace("dS[x] *= a;", "(void)a;"),
+    "bwd_residual_grad_unscaled": lambda s: s.replace("for (int j = 0; j < dv; ++j) de[j] *= b;", ""),
+    "bwd_dq_from_old_state": lambda s: s.replace("acc += S[(size_t)i * dv + j] * gt[j];",
+                                                 "acc += Sp[(size_t)i * dv + j] * gt[j];"),
+    "bwd_deta_unnormalised": lambda s: s.replace("d_eta[th] = db / (kk + eps);", "d_eta[th] = db;"),
+    "bwd_ignores_final_grad": lambda s: s.replace("if (d_final)\n", "if (0)\n"),
+    "bwd_write_grad_sign": lambda s: s.replace("dS[(size_t)i * dv + j] -= kt[i] * de[j];",
+                                               "dS[(size_t)i * dv + j] += kt[i] * de[j];"),
+})
+
 RUNNER = textwrap.dedent("""
     import sys, functools
     sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
