@@ -458,4 +458,109 @@ kla_status kla_decode_step_ccq(const void *q, const void *k, const void *v, cons
   return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
 }
 
+namespace {
+// Workspace sections of the backward, in floats, each rounded up to 64.
+struct BwdWs {
+  size_t ckpt, dq, dk, db, c, kk, total;
+};
+size_t up64(size_t x) { return (x + 63) / 64 * 64; }
+BwdWs bwd_ws(int32_t n_seqs, int64_t total_tok, int32_t H, int32_t d) {
+  BwdWs w;
+  const size_t th = (size_t)total_tok * H, ns = (size_t)d / 16;
+  w.ckpt = up64(((size_t)total_tok / 64 + n_seqs) * H * d * d);
+  w.dq = up64(ns * th * d);
+  w.dk = w.dq;
+  w.db = up64(ns * th);
+  w.c = w.db;
+  w.kk = up64(th);
+  w.total = w.ckpt + w.dq + w.dk + w.db + w.c + w.kk;
+  return w;
+}
+}  // namespace
+
+size_t kla_bwd_chunked_workspace_size(int32_t n_seqs, int64_t total_tok, int32_t H, int32_t dk,
+                                      int32_t dv, int32_t chunk) {
+  if (n_seqs <= 0 || H <= 0 || total_tok < 0 || !supported_dim(dk, dv) || chunk != 64) return 0;
+  return bwd_ws(n_seqs, total_tok, H, dk).total * sizeof(float);
+}
+
+kla_status kla_bwd_chunked(const void *q, const void *k, const void *v, const float *alpha,
+                           const float *eta, const int32_t *cu_seqlens, int32_t n_seqs,
+                           int64_t total_tok, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                           float eps, kla_dtype dtype, kla_beta_mode beta_mode,
+                           const float *initial_state, const float *d_o, const float *d_final,
+                           float *dq, float *dk_out, float *dv_out, float *d_alpha, float *d_eta,
+                           float *d_initial, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+  if (n_seqs <= 0 || H <= 0 || total_tok < 0 || !std::isfinite(eps) || eps < 0.f)
+    return KLA_ERR_INVALID_ARG;
+  if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT) return KLA_ERR_INVALID_ARG;
+  if (dtype != KLA_F32 && dtype != KLA_BF16) return KLA_ERR_UNSUPPORTED;
+  if (!supported_dim(dk, dv) || chunk != 64) return KLA_ERR_UNSUPPORTED;
+  if (!cu_seqlens && total_tok % n_seqs != 0) return KLA_ERR_INVALID_ARG;
+  const size_t ws_need = kla_bwd_chunked_workspace_size(n_seqs, total_tok, H, dk, dv, chunk);
+  if (workspace_bytes < ws_need) return KLA_ERR_WORKSPACE;
+  if (!workspace || !aligned16(workspace)) return KLA_ERR_INVALID_ARG;
+  const bool have_tokens = total_tok > 0;
+  if (have_tokens && (!q || !k || !v || !eta || !d_o || !dq || !dk_out || !dv_out || !d_eta ||
+                      (alpha && !d_alpha)))
+    return KLA_ERR_INVALID_ARG;
+  for (const void *ptr : {q, k, v, (const void *)d_o, (const void *)dq, (const void *)dk_out,
+                          (const void *)dv_out, (const void *)initial_state,
+                          (const void *)d_final, (const void *)d_initial})
+    if (!aligned16(ptr)) return KLA_ERR_INVALID_ARG;
+
+  const int64_t esz = dtype == KLA_BF16 ? 2 : 4;
+  const int64_t th = total_tok * H, st = (int64_t)n_seqs * H * dk * dv * 4;
+  const Range in[] = {range(q, th * dk * esz), range(k, th * dk * esz), range(v, th * dv * esz),
+                      range(alpha, alpha ? th * 4 : 0), range(eta, th * 4),
+                      range(cu_seqlens, cu_seqlens ? (int64_t)(n_seqs + 1) * 4 : 0),
+                      range(initial_state, initial_state ? st : 0), range(d_o, th * dv * 4),
+                      range(d_final, d_final ? st : 0)};
+  const Range out[] = {range(dq, th * dk * 4), range(dk_out, th * dk * 4), range(dv_out, th * dv * 4),
+                       range(alpha ? d_alpha : nullptr, alpha ? th * 4 : 0), range(d_eta, th * 4),
+                       range(d_initial, d_initial ? st : 0), range(workspace, (int64_t)ws_need)};
+  for (size_t a = 0; a < sizeof(out) / sizeof(out[0]); ++a) {
+    for (const Range &r : in)
+      if (overlap(out[a], r)) return KLA_ERR_INVALID_ARG;
+    for (size_t b = a + 1; b < sizeof(out) / sizeof(out[0]); ++b)
+      if (overlap(out[a], out[b])) return KLA_ERR_INVALID_ARG;
+  }
+
+  const BwdWs w = bwd_ws(n_seqs, total_tok, H, dk);
+  float *ws = static_cast<float *>(workspace);
+  kla::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.alpha = alpha;
+  p.eta = eta;
+  p.cu_seqlens = cu_seqlens;
+  p.n_seqs = n_seqs;
+  p.seq_len_dense = cu_seqlens ? 0 : total_tok / n_seqs;
+  p.total_tok = total_tok;
+  p.H = H;
+  p.D = dk;
+  p.eps = eps;
+  p.beta_direct = beta_mode == KLA_BETA_DIRECT;
+  p.initial_state = initial_state;
+  p.d_o = d_o;
+  p.d_final = d_final;
+  p.dq = dq;
+  p.dk = dk_out;
+  p.dv = dv_out;
+  p.d_alpha = alpha ? d_alpha : nullptr;
+  p.d_eta = d_eta;
+  p.d_initial = d_initial;
+  p.ws_ckpt = ws;
+  p.ws_dq = p.ws_ckpt + w.ckpt;
+  p.ws_dk = p.ws_dq + w.dq;
+  p.ws_db = p.ws_dk + w.dk;
+  p.ws_c = p.ws_db + w.db;
+  p.ws_kk = p.ws_c + w.c;
+  return kla::launch_bwd(p, dtype == KLA_BF16, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? KLA_OK
+             : KLA_ERR_HIP;
+}
+
 }  // extern "C"

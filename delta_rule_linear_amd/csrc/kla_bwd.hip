@@ -1,0 +1,583 @@
+// Chunkwise backward of the KLA prefill for gfx950.
+//
+// The KLA summary ("Resumo Tecnico: Atencao Linear Kaczmarz (KLA)", section
+// "Implementacao") keeps Gated DeltaNet's chunk algorithm for training and
+// changes only the step beta_t = eta_t / (|k_t|^2 + eps) (or beta_t = eta_t,
+// the direct step).  This file computes the gradients of the prefill's
+// outputs (o and the final state) with respect to q, k, v, alpha, eta and the
+// initial state.
+//
+// Reverse recurrence.  With G_t the gradient of the state after token t plus
+// the read's q_t dO_t^T, u_t = G_t^T k_t and dS_{t-1} = alpha_t (G_t - beta_t
+// k_t u_t^T).  Inside a chunk of n tokens (gamma_t = alpha_1..alpha_t,
+// Gam_ts = gamma_t / gamma_s for t >= s, B = Diag(beta), S the chunk-start
+// state, Gend the gradient of the state after the chunk):
+//   (I + StrictLower(Gam o K K^T) B) E = V - Diag(gamma) K S        residuals
+//   (I + StrictUpper(Gam^T o K K^T) B) U = Diag(gamma_n/gamma) K Gend
+//                                         + Mq^T dO,  Mq = Lower(Gam o Q K^T)
+//   O        = Diag(gamma) Q S + Mq B E
+//   dv       = B U,   dbeta_t = u_t . e_t
+//   dk       = B (Diag(gamma_n/gamma) E Gend^T - Diag(gamma) U S^T + Z^T Q - W B K)
+//              + Diag(dbeta o (beta^2 - 2 beta / (|k|^2 + eps))) K
+//   dq       = Diag(gamma) dO S^T + Z B K
+//   dS_start = gamma_n Gend + Q^T Diag(gamma) dO - K^T Diag(gamma beta) U
+// with Z = Lower(Gam o dO E^T) and W the symmetric matrix W_ts = Gam_hl
+// (u_h . e_l), h = max(t, s), l = min(t, s).  The direct step drops the
+// -2 beta / (|k|^2 + eps) term.  The decay's gradient comes from a reverse
+// running sum: c_t = alpha_t dalpha_t = c_{t+1} + dO_t . o_t - beta_t u_t . v_t,
+// started at <Gend, S_end> at each chunk's end.
+//
+// Every quantity is linear in the state's columns (dv), so one workgroup of
+// 4 waves takes one (sequence, head, 16 columns of dv): the fp32 slices of
+// S and Gend, K and Q of a chunk and the 64 x 64 planes fit in LDS.  A first
+// sweep runs the chunks forward and stores each chunk-start state slice in
+// the workspace; the reverse sweep then takes the chunks from last to first.
+// Products are fp32 MFMA (v_mfma_f32_16x16x4_f32); the two triangular solves
+// are 16 x 16 block substitutions.  The column slices' contributions to dq,
+// dk, dbeta and c land in the workspace and a second kernel adds them in a
+// fixed order (deterministic, no atomics) and finishes dk, deta, dalpha.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kla_device.h"
+#include "kla_internal.h"
+
+namespace kla {
+namespace {
+
+constexpr int DVS = 16;         // state columns per workgroup
+constexpr int LDSL = DVS + 4;   // row pitch of the column-slice tiles
+constexpr int LDN = C + 4;      // row pitch of the 64 x 64 planes
+
+template <int D>
+struct BwdSmem {
+  static constexpr int LDK = D + 4;
+  alignas(16) float K[C * LDK];
+  alignas(16) float Q[C * LDK];
+  alignas(16) float Sc[D * LDSL];  // chunk-start state, this workgroup's columns
+  alignas(16) float Gd[D * LDSL];  // gradient of the state after the chunk
+  alignas(16) float Vs[C * LDSL];
+  alignas(16) float Ds[C * LDSL];  // dO
+  alignas(16) float Es[C * LDSL];  // residuals e_t
+  alignas(16) float Us[C * LDSL];  // u_t
+  alignas(16) float Os[C * LDSL];  // outputs o_t
+  alignas(16) float Am[C * LDN];   // lower: Gam o KK^T B; upper: its reverse twin; later W
+  alignas(16) float Xm[C * LDN];   // Mq, later Z (lower, diagonal included)
+  float gl[C];    // cumulative log2 decay inside the chunk
+  float gm[C];    // 2^gl
+  float beta[C];
+  float kk[C];
+  float fc[C];    // per-row factor of the state update
+  float scan[C];
+  float red[kWaves];
+};
+
+struct Tok {
+  int64_t bos;
+  int L;
+};
+
+__device__ inline Tok seq_of(const BwdParams &p, int64_t s) {
+  Tok t;
+  t.bos = p.cu_seqlens ? (int64_t)p.cu_seqlens[s] : s * p.seq_len_dense;
+  const int64_t eos = p.cu_seqlens ? (int64_t)p.cu_seqlens[s + 1] : t.bos + p.seq_len_dense;
+  t.L = (int)(eos - t.bos);
+  return t;
+}
+
+template <typename E>
+__device__ inline float ld(const E *p, int64_t i) {
+  return static_cast<float>(p[i]);
+}
+
+// 16x16 output tile, acc[i] = sum_k A(16 rows)[4j+i][k] B[k][c16] over
+// K = 4 * steps, with the operands fetched by a(k) = A[c16][k] and
+// b(k) = B[k][c16] (k the lane's own index 4 * step + j).
+template <int STEPS, typename FA, typename FB>
+__device__ __attribute__((always_inline)) inline f32x4 tile_mm(f32x4 acc, int k0, int j, FA a, FB b) {
+#pragma unroll 4
+  for (int st = 0; st < STEPS; ++st) {
+    const int kx = k0 + 4 * st + j;
+    acc = mma(a(kx), b(kx), acc);
+  }
+  return acc;
+}
+__device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Lower tile p (0..9) of a 4x4 block grid, in row order.
+__device__ inline void lower_tile(int p, int &bt, int &bs) {
+  bt = (p >= 1) + (p >= 3) + (p >= 6);
+  bs = p - bt * (bt + 1) / 2;
+}
+
+template <typename E, int D>
+__device__ inline void load_chunk(BwdSmem<D> &sm, const BwdParams &p, const E *__restrict__ q,
+                                  const E *__restrict__ k, const E *__restrict__ v, int64_t t0,
+                                  int n, int h, int col0, bool with_q, int tid) {
+  constexpr int LDK = BwdSmem<D>::LDK;
+  for (int idx = tid; idx < C * D; idx += kThreads) {
+    const int r = idx / D, i = idx % D;
+    const int64_t g = ((t0 + r) * p.H + h) * D + i;
+    sm.K[r * LDK + i] = r < n ? ld(k, g) : 0.f;
+    if (with_q) sm.Q[r * LDK + i] = r < n ? ld(q, g) : 0.f;
+  }
+  for (int idx = tid; idx < C * DVS; idx += kThreads) {
+    const int r = idx / DVS, c = idx % DVS;
+    const int64_t g = ((t0 + r) * p.H + h) * D + col0 + c;
+    sm.Vs[r * LDSL + c] = r < n ? ld(v, g) : 0.f;
+    if (with_q) sm.Ds[r * LDSL + c] = r < n ? p.d_o[g] : 0.f;
+  }
+}
+
+// Row scalars: |k|^2, beta, the cumulative log2 decay and 2^gl (wave 0).
+template <int D>
+__device__ inline void row_scalars(BwdSmem<D> &sm, const BwdParams &p, int64_t t0, int n, int h,
+                                   int tid) {
+  constexpr int LDK = BwdSmem<D>::LDK;
+  if (tid < C) {
+    const int r = tid;
+    float kk = 0.f;
+    for (int i = 0; i < D; ++i) kk = fmaf(sm.K[r * LDK + i], sm.K[r * LDK + i], kk);
+    float beta = 0.f, la = 0.f;
+    if (r < n) {
+      const int64_t th = (t0 + r) * p.H + h;
+      const float eta = p.eta[th];
+      beta = p.beta_direct ? eta : eta / (kk + p.eps);
+      if (p.alpha) la = flog2(p.alpha[th]);
+    }
+    const float g = wave_scan(la);
+    sm.kk[r] = kk;
+    sm.beta[r] = beta;
+    sm.gl[r] = g;
+    sm.gm[r] = fexp2(g);
+  }
+}
+
+// Am <- Gam o K K^T B below the diagonal and its reverse twin
+// (Gam^T o K K^T B) above it; with_q: Xm <- Lower(Gam o Q K^T).
+template <int D>
+__device__ inline void gram(BwdSmem<D> &sm, bool with_q, int w, int j, int c16) {
+  constexpr int LDK = BwdSmem<D>::LDK;
+  const int jobs = with_q ? 20 : 10;
+  for (int jb = w; jb < jobs; jb += kWaves) {
+    const bool qk = jb >= 10;
+    int bt, bs;
+    lower_tile(qk ? jb - 10 : jb, bt, bs);
+    const float *X = qk ? sm.Q : sm.K;
+    f32x4 acc = tile_mm<D / 4>(zero4(), 0, j,
+                               [&](int kx) { return X[(16 * bt + c16) * LDK + kx]; },
+                               [&](int kx) { return sm.K[(16 * bs + c16) * LDK + kx]; });
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * bt + 4 * j + i, s = 16 * bs + c16;
+      if (t < s) continue;
+      const float G = fexp2(sm.gl[t] - sm.gl[s]);
+      if (qk) {
+        sm.Xm[t * LDN + s] = G * acc[i];
+        if (t != s) sm.Xm[s * LDN + t] = 0.f;
+      } else if (t == s) {
+        sm.Am[t * LDN + t] = 0.f;
+      } else {
+        sm.Am[t * LDN + s] = G * acc[i] * sm.beta[s];
+        sm.Am[s * LDN + t] = G * acc[i] * sm.beta[t];
+      }
+    }
+  }
+}
+
+// Es <- V - Diag(gamma) K S for output tile bt (16 rows, the 16 columns).
+template <int D>
+__device__ inline void residual_tile(BwdSmem<D> &sm, int bt, int j, int c16) {
+  constexpr int LDK = BwdSmem<D>::LDK;
+  f32x4 acc = tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return sm.K[(16 * bt + c16) * LDK + kx]; },
+                             [&](int kx) { return sm.Sc[kx * LDSL + c16]; });
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 16 * bt + 4 * j + i;
+    sm.Es[t * LDSL + c16] = sm.Vs[t * LDSL + c16] - sm.gm[t] * acc[i];
+  }
+}
+
+// Block substitution on X (64 x 16, in place) with the unit triangle of Am:
+// lower (forward, E) or upper (backward, U).  One wave.
+template <bool UPPER>
+__device__ inline void tri_solve(float *X, const float *Am, int l, int j, int c16) {
+#pragma unroll 1
+  for (int bb = 0; bb < 4; ++bb) {
+    const int b = UPPER ? 3 - bb : bb;
+    const int k0 = UPPER ? 16 * (b + 1) : 0;
+    const int steps = UPPER ? 4 * (3 - b) : 4 * b;
+    if (steps > 0) {
+      f32x4 acc = zero4();
+      for (int st = 0; st < steps; ++st) {
+        const int kx = k0 + 4 * st + j;
+        acc = mma(Am[(16 * b + c16) * LDN + kx], X[kx * LDSL + c16], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[(16 * b + 4 * j + i) * LDSL + c16] -= acc[i];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block's rows are in LDS
+    if (l < 16) {
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = X[(16 * b + r) * LDSL + l];
+      if (UPPER) {
+#pragma unroll
+        for (int r = 14; r >= 0; --r)
+#pragma unroll
+          for (int s = r + 1; s < 16; ++s) x[r] = fmaf(-Am[(16 * b + r) * LDN + 16 * b + s], x[s], x[r]);
+      } else {
+#pragma unroll
+        for (int r = 1; r < 16; ++r)
+#pragma unroll
+          for (int s = 0; s < r; ++s) x[r] = fmaf(-Am[(16 * b + r) * LDN + 16 * b + s], x[s], x[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) X[(16 * b + r) * LDSL + l] = x[r];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+  }
+}
+
+template <int D>
+__device__ inline float block_sum(BwdSmem<D> &sm, float x, int w, int l) {
+  x = group_sum<32>(x);
+  x += __shfl_xor(x, 32, 64);
+  __syncthreads();
+  if (l == 0) sm.red[w] = x;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) t += sm.red[i];
+  return t;
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
+  constexpr int LDK = BwdSmem<D>::LDK;
+  constexpr int NS = D / DVS;
+  constexpr int DD = D * D;
+  __shared__ BwdSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int j = l >> 4, c16 = l & 15;
+
+  const int64_t lb = logical_block();
+  const int sl = (int)(lb % NS);
+  const int64_t sh = lb / NS;
+  const int h = (int)(sh % p.H);
+  const int64_t s = sh / p.H;
+  const int col0 = sl * DVS;
+  const Tok sq = seq_of(p, s);
+  const int nch = (sq.L + C - 1) / C;
+  const E *q = static_cast<const E *>(p.q);
+  const E *k = static_cast<const E *>(p.k);
+  const E *v = static_cast<const E *>(p.v);
+  // checkpoint slots of this sequence: floor(bos / C) + s onwards (disjoint)
+  float *ck = p.ws_ckpt + ((sq.bos / C + s) * p.H + h) * (int64_t)DD;
+  const int64_t TH = p.total_tok * p.H;
+
+  // ---- forward sweep: chunk-start states -------------------------------
+  for (int idx = tid; idx < D * DVS; idx += kThreads) {
+    const int i = idx / DVS, c = idx % DVS;
+    sm.Sc[i * LDSL + c] = p.initial_state ? p.initial_state[sh * DD + i * D + col0 + c] : 0.f;
+  }
+  for (int ci = 0; ci < nch; ++ci) {
+    const int64_t t0 = sq.bos + (int64_t)ci * C;
+    const int n = min(C, sq.L - ci * C);
+    __syncthreads();
+    load_chunk<E, D>(sm, p, q, k, v, t0, n, h, col0, false, tid);
+    for (int idx = tid; idx < D * DVS; idx += kThreads) {
+      const int i = idx / DVS, c = idx % DVS;
+      ck[(int64_t)ci * p.H * DD + i * D + col0 + c] = sm.Sc[i * LDSL + c];
+    }
+    __syncthreads();
+    row_scalars<D>(sm, p, t0, n, h, tid);
+    __syncthreads();
+    gram<D>(sm, false, w, j, c16);
+    residual_tile<D>(sm, w, j, c16);
+    if (tid < C) sm.fc[tid] = sm.beta[tid] * fexp2(sm.gl[C - 1] - sm.gl[tid]);
+    __syncthreads();
+    if (w == 0) tri_solve<false>(sm.Es, sm.Am, l, j, c16);
+    __syncthreads();
+    // S <- gamma_n S + K^T Diag(beta gamma_n / gamma) E
+    const float gn = sm.gm[C - 1];
+    for (int ti = w; ti < D / 16; ti += kWaves) {
+      f32x4 acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = gn * sm.Sc[(16 * ti + 4 * j + i) * LDSL + c16];
+      acc = tile_mm<C / 4>(acc, 0, j, [&](int kx) { return sm.K[kx * LDK + 16 * ti + c16]; },
+                           [&](int kx) { return sm.fc[kx] * sm.Es[kx * LDSL + c16]; });
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.Sc[(16 * ti + 4 * j + i) * LDSL + c16] = acc[i];
+    }
+  }
+  __syncthreads();
+
+  // ---- reverse sweep ----------------------------------------------------
+  for (int idx = tid; idx < D * DVS; idx += kThreads) {
+    const int i = idx / DVS, c = idx % DVS;
+    sm.Gd[i * LDSL + c] = p.d_final ? p.d_final[sh * DD + i * D + col0 + c] : 0.f;
+  }
+  __syncthreads();
+  float cend;
+  {
+    float x = 0.f;
+    for (int idx = tid; idx < D * DVS; idx += kThreads) {
+      const int i = idx / DVS, c = idx % DVS;
+      x = fmaf(sm.Gd[i * LDSL + c], sm.Sc[i * LDSL + c], x);
+    }
+    cend = block_sum<D>(sm, x, w, l);
+  }
+  float *dqp = p.ws_dq + (int64_t)sl * TH * D;
+  float *dkp = p.ws_dk + (int64_t)sl * TH * D;
+  float *dbp = p.ws_db + (int64_t)sl * TH;
+  float *cp = p.ws_c + (int64_t)sl * TH;
+
+  for (int ci = nch - 1; ci >= 0; --ci) {
+    const int64_t t0 = sq.bos + (int64_t)ci * C;
+    const int n = min(C, sq.L - ci * C);
+    __syncthreads();
+    load_chunk<E, D>(sm, p, q, k, v, t0, n, h, col0, true, tid);
+    for (int idx = tid; idx < D * DVS; idx += kThreads) {
+      const int i = idx / DVS, c = idx % DVS;
+      sm.Sc[i * LDSL + c] = ck[(int64_t)ci * p.H * DD + i * D + col0 + c];
+    }
+    __syncthreads();
+    row_scalars<D>(sm, p, t0, n, h, tid);
+    if (sl == 0 && tid < n) p.ws_kk[(t0 + tid) * p.H + h] = sm.kk[tid];
+    __syncthreads();
+    gram<D>(sm, true, w, j, c16);
+    residual_tile<D>(sm, w, j, c16);
+    __syncthreads();
+    const float glast = sm.gl[C - 1];
+    if (w == 0) {
+      tri_solve<false>(sm.Es, sm.Am, l, j, c16);
+    } else {
+      // U right-hand side: Diag(gamma_n/gamma) K Gend + Mq^T dO
+      for (int bt = w - 1; bt < 4; bt += kWaves - 1) {
+        f32x4 a1 = tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return sm.K[(16 * bt + c16) * LDK + kx]; },
+                                  [&](int kx) { return sm.Gd[kx * LDSL + c16]; });
+        f32x4 a2 = zero4();
+        for (int st = 4 * bt; st < 16; ++st) {
+          const int kx = 4 * st + j;
+          a2 = mma(sm.Xm[kx * LDN + 16 * bt + c16], sm.Ds[kx * LDSL + c16], a2);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * bt + 4 * j + i;
+          sm.Us[t * LDSL + c16] = fexp2(glast - sm.gl[t]) * a1[i] + a2[i];
+        }
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      tri_solve<true>(sm.Us, sm.Am, l, j, c16);
+    } else {
+      // O = Diag(gamma) Q S + Mq B E
+      for (int bt = w - 1; bt < 4; bt += kWaves - 1) {
+        f32x4 a1 = tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return sm.Q[(16 * bt + c16) * LDK + kx]; },
+                                  [&](int kx) { return sm.Sc[kx * LDSL + c16]; });
+        f32x4 a2 = zero4();
+        for (int st = 0; st < 4 * (bt + 1); ++st) {
+          const int kx = 4 * st + j;
+          a2 = mma(sm.Xm[(16 * bt + c16) * LDN + kx], sm.beta[kx] * sm.Es[kx * LDSL + c16], a2);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * bt + 4 * j + i;
+          sm.Os[t * LDSL + c16] = sm.gm[t] * a1[i] + a2[i];
+        }
+      }
+    }
+    __syncthreads();
+    // per-row outputs: dv, the dbeta part and the decay running sum
+    if (tid < C) {
+      const int r = tid;
+      const float b = sm.beta[r];
+      float db = 0.f, term = 0.f;
+#pragma unroll
+      for (int c = 0; c < DVS; ++c) {
+        const float u = sm.Us[r * LDSL + c];
+        db = fmaf(u, sm.Es[r * LDSL + c], db);
+        term = fmaf(sm.Ds[r * LDSL + c], sm.Os[r * LDSL + c], term);
+        term = fmaf(-b * u, sm.Vs[r * LDSL + c], term);
+      }
+      // suffix sum over rows r..63 (padded rows add zero)
+      const float suf = wave_scan(__shfl(term, 63 - r, 64));
+      sm.scan[63 - r] = suf;
+      if (r < n) {
+        const int64_t th = (t0 + r) * p.H + h;
+        dbp[th] = db;
+      }
+    }
+    for (int idx = tid; idx < C * DVS; idx += kThreads) {
+      const int r = idx / DVS, c = idx % DVS;
+      if (r < n) p.dv[((t0 + r) * p.H + h) * D + col0 + c] = sm.beta[r] * sm.Us[r * LDSL + c];
+    }
+    __syncthreads();
+    if (tid < n) cp[(t0 + tid) * p.H + h] = cend + sm.scan[tid];
+    // W (symmetric, from U E^T) into Am; Z = Lower(Gam o dO E^T) into Xm
+    for (int jb = w; jb < 20; jb += kWaves) {
+      const bool zq = jb >= 10;
+      int bt, bs;
+      lower_tile(zq ? jb - 10 : jb, bt, bs);
+      const float *X = zq ? sm.Ds : sm.Us;
+      f32x4 acc = tile_mm<DVS / 4>(zero4(), 0, j, [&](int kx) { return X[(16 * bt + c16) * LDSL + kx]; },
+                                   [&](int kx) { return sm.Es[(16 * bs + c16) * LDSL + kx]; });
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * bt + 4 * j + i, s2 = 16 * bs + c16;
+        if (t < s2) continue;
+        const float val = fexp2(sm.gl[t] - sm.gl[s2]) * acc[i];
+        if (zq) {
+          sm.Xm[t * LDN + s2] = val;
+          if (t != s2) sm.Xm[s2 * LDN + t] = 0.f;
+        } else {
+          sm.Am[t * LDN + s2] = val;
+          sm.Am[s2 * LDN + t] = val;
+        }
+      }
+    }
+    __syncthreads();
+    // dq and dk contributions of these columns: 2 x (4 x D/16) tiles
+    for (int jb = w; jb < 8 * (D / 16); jb += kWaves) {
+      const bool isq = jb >= 4 * (D / 16);
+      const int tt = isq ? jb - 4 * (D / 16) : jb;
+      const int bt = tt & 3, bi = tt >> 2;
+      f32x4 out;
+      if (isq) {
+        f32x4 a1 = tile_mm<DVS / 4>(zero4(), 0, j, [&](int kx) { return sm.Ds[(16 * bt + c16) * LDSL + kx]; },
+                                    [&](int kx) { return sm.Sc[(16 * bi + c16) * LDSL + kx]; });
+        f32x4 a2 = zero4();
+        for (int st = 0; st < 4 * (bt + 1); ++st) {
+          const int kx = 4 * st + j;
+          a2 = mma(sm.Xm[(16 * bt + c16) * LDN + kx], sm.beta[kx] * sm.K[kx * LDK + 16 * bi + c16], a2);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = sm.gm[16 * bt + 4 * j + i] * a1[i] + a2[i];
+      } else {
+        f32x4 a1 = tile_mm<DVS / 4>(zero4(), 0, j, [&](int kx) { return sm.Es[(16 * bt + c16) * LDSL + kx]; },
+                                    [&](int kx) { return sm.Gd[(16 * bi + c16) * LDSL + kx]; });
+        f32x4 a2 = tile_mm<DVS / 4>(zero4(), 0, j, [&](int kx) { return sm.Us[(16 * bt + c16) * LDSL + kx]; },
+                                    [&](int kx) { return sm.Sc[(16 * bi + c16) * LDSL + kx]; });
+        f32x4 a3 = zero4();
+        for (int st = 4 * bt; st < 16; ++st) {
+          const int kx = 4 * st + j;
+          a3 = mma(sm.Xm[kx * LDN + 16 * bt + c16], sm.Q[kx * LDK + 16 * bi + c16], a3);
+        }
+        a3 = tile_mm<C / 4>(a3, 0, j, [&](int kx) { return -sm.Am[(16 * bt + c16) * LDN + kx]; },
+                            [&](int kx) { return sm.beta[kx] * sm.K[kx * LDK + 16 * bi + c16]; });
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * bt + 4 * j + i;
+          out[i] = sm.beta[t] * (fexp2(glast - sm.gl[t]) * a1[i] - sm.gm[t] * a2[i] + a3[i]);
+        }
+      }
+      float *dst = isq ? dqp : dkp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * bt + 4 * j + i;
+        if (t < n) dst[((t0 + t) * p.H + h) * D + 16 * bi + c16] = out[i];
+      }
+    }
+    // Gend <- gamma_n Gend + Q^T Diag(gamma) dO - K^T Diag(gamma beta) U
+    constexpr int NT = D / 16 / kWaves;  // state tiles per wave (2 or 1)
+    f32x4 gnew[NT];
+    {
+      const float gn = sm.gm[C - 1];
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        const int ti = w + kWaves * m;
+        f32x4 acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = gn * sm.Gd[(16 * ti + 4 * j + i) * LDSL + c16];
+        acc = tile_mm<C / 4>(acc, 0, j, [&](int kx) { return sm.Q[kx * LDK + 16 * ti + c16]; },
+                             [&](int kx) { return sm.gm[kx] * sm.Ds[kx * LDSL + c16]; });
+        acc = tile_mm<C / 4>(acc, 0, j, [&](int kx) { return sm.K[kx * LDK + 16 * ti + c16]; },
+                             [&](int kx) { return -sm.gm[kx] * sm.beta[kx] * sm.Us[kx * LDSL + c16]; });
+        gnew[m] = acc;
+      }
+    }
+    __syncthreads();
+    {
+      float x = 0.f;
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        const int ti = w + kWaves * m;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * ti + 4 * j + i;
+          sm.Gd[r * LDSL + c16] = gnew[m][i];
+          x = fmaf(gnew[m][i], sm.Sc[r * LDSL + c16], x);
+        }
+      }
+      cend = block_sum<D>(sm, x, w, l);
+    }
+  }
+  __syncthreads();
+  if (p.d_initial) {
+    for (int idx = tid; idx < D * DVS; idx += kThreads) {
+      const int i = idx / DVS, c = idx % DVS;
+      p.d_initial[sh * DD + i * D + col0 + c] = sm.Gd[i * LDSL + c];
+    }
+  }
+}
+
+// Adds the column slices' contributions in slice order and finishes dk,
+// deta and dalpha.  One thread per (token, head, key channel).
+template <typename E, int D>
+__global__ __launch_bounds__(256) void bwd_finish_kernel(BwdParams p) {
+  constexpr int NS = D / DVS;
+  const int64_t TH = p.total_tok * p.H;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= TH * D) return;
+  const int64_t th = g / D;
+  const int i = (int)(g % D);
+  float dq = 0.f, dk = 0.f, db = 0.f, c = 0.f;
+  for (int s = 0; s < NS; ++s) {
+    dq += p.ws_dq[(int64_t)s * TH * D + g];
+    dk += p.ws_dk[(int64_t)s * TH * D + g];
+    db += p.ws_db[(int64_t)s * TH + th];
+    c += p.ws_c[(int64_t)s * TH + th];
+  }
+  const float kk = p.ws_kk[th];
+  const float eta = p.eta[th];
+  const float kv = static_cast<float>(static_cast<const E *>(p.k)[g]);
+  float coef;
+  if (p.beta_direct) {
+    coef = eta * eta;
+  } else {
+    const float den = kk + p.eps;
+    const float beta = eta / den;
+    coef = beta * beta - 2.f * beta / den;
+  }
+  p.dq[g] = dq;
+  p.dk[g] = fmaf(db * coef, kv, dk);
+  if (i == 0) {
+    p.d_eta[th] = p.beta_direct ? db : db / (kk + p.eps);
+    if (p.alpha) p.d_alpha[th] = c / p.alpha[th];
+  }
+}
+
+template <typename E, int D>
+hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
+  const int64_t groups = (int64_t)p.n_seqs * p.H * (D / DVS);
+  hipLaunchKernelGGL((bwd_kernel<E, D>), dim3((unsigned)groups), dim3(kThreads), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.total_tok == 0) return e;
+  const int64_t n = p.total_tok * p.H * D;
+  hipLaunchKernelGGL((bwd_finish_kernel<E, D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams &p, bool bf16_inputs, hipStream_t st) {
+  if (bf16_inputs) return p.D == 64 ? launch_bwd_t<__bf16, 64>(p, st) : launch_bwd_t<__bf16, 128>(p, st);
+  return p.D == 64 ? launch_bwd_t<float, 64>(p, st) : launch_bwd_t<float, 128>(p, st);
+}
+
+}  // namespace kla

@@ -50,6 +50,29 @@ struct CcqArgs {
   void *qh, *ql;              // cleaned query: fp32 in qh, or bf16 hi / lo planes (prefill, bf16)
 };
 
+// Backward of the prefill (gradients of o and of the final state).
+struct BwdParams {
+  const void *q, *k, *v;      // [total_tok, H, D], bf16 or fp32
+  const float *alpha, *eta;   // alpha nullable (alpha = 1)
+  const int32_t *cu_seqlens;  // device, or nullptr for dense
+  int32_t n_seqs;
+  int64_t seq_len_dense;
+  int64_t total_tok;
+  int32_t H, D;
+  float eps;
+  int beta_direct;
+  const float *initial_state;  // nullable
+  const float *d_o;            // [total_tok, H, D] fp32
+  const float *d_final;        // nullable
+  float *dq, *dk, *dv;         // [total_tok, H, D] fp32
+  float *d_alpha;              // [total_tok, H], written when alpha is set
+  float *d_eta;                // [total_tok, H]
+  float *d_initial;            // nullable
+  // workspace: chunk-start states [floor(tok/64) + n_seqs, H, D, D], the
+  // column slices' dq, dk [D/16, tok, H, D], dbeta, c [D/16, tok, H], |k|^2 [tok, H]
+  float *ws_ckpt, *ws_dq, *ws_dk, *ws_db, *ws_c, *ws_kk;
+};
+
 // Each returns the HIP status of the launch.
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t s);
@@ -67,5 +90,7 @@ hipError_t launch_ccq_decode(const CcqArgs &a, hipStream_t s);
 hipError_t launch_add(float *o, const float *o2, int64_t n, hipStream_t s);
 // Per-channel decay prefill (alpha [total_tok, H, D]); whole sequences only.
 hipError_t launch_prefill_kda(const PrefillArgs &a, bool bf16_inputs, hipStream_t s);
+// Backward: the two-sweep kernel, then the reduction over column slices.
+hipError_t launch_bwd(const BwdParams &p, bool bf16_inputs, hipStream_t s);
 
 }  // namespace kla

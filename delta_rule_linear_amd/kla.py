@@ -363,3 +363,72 @@ def kla_decode_step_ccq(q, k, v, alpha, eta, lam, state, ccq_state, eps=1e-6,
     if st != KLA_OK:
         raise KLAError(st)
     return o
+
+
+_lib.kla_bwd_chunked_workspace_size.restype = ctypes.c_size_t
+_lib.kla_bwd_chunked_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+_lib.kla_bwd_chunked.restype = ctypes.c_int
+_lib.kla_bwd_chunked.argtypes = ([_vp, _vp, _vp, _fp, _fp, _i32p, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_float, ctypes.c_int, ctypes.c_int]
+                                 + [_fp] * 9 + [_vp, ctypes.c_size_t, _vp])
+
+
+def kla_bwd_chunked_workspace_size(n_seqs, total_tok, H, dk, dv, chunk=64) -> int:
+    return int(_lib.kla_bwd_chunked_workspace_size(n_seqs, total_tok, H, dk, dv, chunk))
+
+
+def kla_bwd_chunked(q, k, v, alpha, eta, d_o, cu_seqlens=None, initial_state=None, d_final=None,
+                    eps=1e-6, chunk=64, beta_mode="kaczmarz", workspace=None, stream=None):
+    """Gradients of the prefill (C ABI `kla_bwd_chunked`).
+
+    The forward arguments exactly as given to kla_fwd_chunked_ex, plus d_o
+    (fp32, shaped like v) and d_final ([n, H, dk, dv] fp32 or None).
+    Returns a dict of fp32 tensors: dq, dk (shaped like q), dv (like v),
+    dalpha (like eta, or None without alpha), deta (like eta) and dS0
+    ([n, H, dk, dv]).  The workspace is allocated with torch when not given.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype)
+    if alpha is not None:
+        _need(alpha, "alpha", torch.float32)
+    _need(eta, "eta", torch.float32)
+    _need(d_o, "d_o", torch.float32)
+    dk, dv, H = q.shape[-1], v.shape[-1], q.shape[-2]
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        if q.dim() != 3:
+            raise ValueError("packed input (cu_seqlens given) must be [tok, H, d]")
+        n_seqs, total = cu_seqlens.numel() - 1, q.shape[0]
+    elif q.dim() == 4:
+        n_seqs, total = q.shape[0], q.shape[0] * q.shape[1]
+    elif q.dim() == 3:
+        n_seqs, total = 1, q.shape[0]
+    else:
+        raise ValueError("q must be [tok, H, d] or [B, T, H, d]")
+    if d_o.shape != v.shape:
+        raise ValueError("d_o must be shaped like v")
+    for name, t in (("initial_state", initial_state), ("d_final", d_final)):
+        if t is not None:
+            _need(t, name, torch.float32)
+    dev = q.device
+    out = {"dq": torch.empty(q.shape, dtype=torch.float32, device=dev),
+           "dk": torch.empty(k.shape, dtype=torch.float32, device=dev),
+           "dv": torch.empty(v.shape, dtype=torch.float32, device=dev),
+           "dalpha": None if alpha is None else torch.empty(eta.shape, dtype=torch.float32, device=dev),
+           "deta": torch.empty(eta.shape, dtype=torch.float32, device=dev),
+           "dS0": torch.empty((n_seqs, H, dk, dv), dtype=torch.float32, device=dev)}
+    ws_bytes = kla_bwd_chunked_workspace_size(n_seqs, total, H, dk, dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    st = _lib.kla_bwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(cu_seqlens),
+                              n_seqs, total, H, dk, dv, chunk, float(eps), _dtype_code(q),
+                              _beta_code(beta_mode), _ptr(initial_state), _ptr(d_o), _ptr(d_final),
+                              _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]),
+                              _ptr(out["deta"]), _ptr(out["dS0"]), _ptr(workspace), ws_len,
+                              _stream(stream))
+    if st != KLA_OK:
+        raise KLAError(st)
+    return out

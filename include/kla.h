@@ -322,6 +322,50 @@ kla_status kla_decode_step_ccq(const void *q, const void *k, const void *v,
                                kla_beta_mode beta_mode, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/*
+ * Backward of the prefill: the gradients of a loss with respect to q, k, v,
+ * alpha, eta and the initial state, given the loss's gradients with respect
+ * to o (d_o) and to the final state (d_final).  The KLA summary ("Resumo
+ * Tecnico: Atencao Linear Kaczmarz (KLA)", section "Implementacao") keeps
+ * Gated DeltaNet's chunk algorithm, training included, and changes only
+ * the step size; this is the derivative of the recurrence above, computed
+ * chunkwise: a forward sweep stores each chunk-start state in the
+ * workspace, a reverse sweep carries the state's gradient from the last
+ * chunk to the first, and a second launch adds the column slices'
+ * contributions in a fixed order (bitwise deterministic).
+ *
+ *   q, k, v, alpha, eta, cu_seqlens, n_seqs, total_tok, H, dk, dv, chunk,
+ *   eps, dtype, beta_mode, initial_state
+ *               exactly as the kla_fwd_chunked_ex call being differentiated.
+ *   d_o         [total_tok, H, dv] fp32, required when total_tok > 0.
+ *   d_final     [n_seqs, H, dk, dv] fp32, or NULL (the final state does not
+ *               reach the loss).
+ *   dq, dk_out  [total_tok, H, dk] fp32, written.
+ *   dv_out      [total_tok, H, dv] fp32, written.
+ *   d_alpha     [total_tok, H] fp32, written; required when alpha is set,
+ *               ignored when alpha is NULL.
+ *   d_eta       [total_tok, H] fp32, written.
+ *   d_initial   [n_seqs, H, dk, dv] fp32, or NULL; written with the
+ *               gradient of the initial state (of a zero start when
+ *               initial_state is NULL).
+ *   workspace   device buffer of at least kla_bwd_chunked_workspace_size
+ *               bytes, 16-byte aligned, not overlapping any argument;
+ *               contents on entry ignored, on return unspecified.
+ * Outputs must not overlap each other or any input.  Errors: as
+ * kla_fwd_chunked_ex, plus KLA_ERR_INVALID_ARG for a missing required
+ * pointer or an overlap, KLA_ERR_WORKSPACE for a short workspace.
+ */
+size_t kla_bwd_chunked_workspace_size(int32_t n_seqs, int64_t total_tok, int32_t H, int32_t dk,
+                                      int32_t dv, int32_t chunk);
+kla_status kla_bwd_chunked(const void *q, const void *k, const void *v, const float *alpha,
+                           const float *eta, const int32_t *cu_seqlens, int32_t n_seqs,
+                           int64_t total_tok, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                           float eps, kla_dtype dtype, kla_beta_mode beta_mode,
+                           const float *initial_state, const float *d_o, const float *d_final,
+                           float *dq, float *dk_out, float *dv_out, float *d_alpha, float *d_eta,
+                           float *d_initial, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *kla_status_string(kla_status s);
 

@@ -134,3 +134,123 @@ def chunked_ch(q, k, v, alpha, eta, cu_seqlens, eps, C, initial_state=None, fact
             o[a:b, h], fin[s, h] = chunked_ch_seq(q[a:b, h], k[a:b, h], v[a:b, h], alpha[a:b, h],
                                                   eta[a:b, h], eps, C, S0, factored)
     return o, fin
+
+
+# ---------------------------------------------------------------------------
+# Chunk form of the backward (gradient of o and of the final state).
+#
+# The gradient of the state after token t, G_t (with the read's q_t d_o_t^T
+# added), obeys the reverse of the forward recurrence:
+#   G_t = dS_t + q_t d_o_t^T,   u_t = G_t^T k_t,
+#   dS_{t-1} = alpha_t (G_t - beta_t k_t u_t^T).
+# Inside a chunk of n tokens, with Gamma_ts = gamma_t / gamma_s (t >= s) and
+# Gend the gradient of the state after the chunk:
+#   (I + StrictLower(Gam o K K^T) B) E = V - Diag(gamma) K S          (residuals)
+#   (I + StrictUpper(Gam^T o K K^T) B) U = Diag(gamma_n/gamma) K Gend
+#                                          + Upper(Gam^T o K Q^T) dO
+#   O   = Diag(gamma) Q S + Lower(Gam o Q K^T) B E
+#   dv  = B U,   dbeta_t = u_t . e_t
+#   G e = Diag(gamma_n/gamma) E Gend^T + Upper(Gam^T o E dO^T) Q
+#         - StrictUpper(Gam^T o E U^T) B K                  (rows G_t e_t)
+#   S u = Diag(gamma) U S^T + Lower(Gam o U E^T) B K          (rows S_t u_t)
+#   dq  = Diag(gamma) dO S^T + Lower(Gam o dO E^T) B K
+#   dk  = B (G e - S u) + Diag(dbeta o (beta^2 - 2 beta/(|k|^2+eps))) K
+#         (the direct step drops the second beta term)
+#   dS_start = gamma_n Gend + Q^T Diag(gamma) dO - K^T Diag(gamma beta) U
+# with B = Diag(beta).  The decay gradient uses
+#   alpha_t dalpha_t = <G_t, S_t> - beta_t u_t . v_t   and
+#   <G_t, S_t> = alpha_{t+1} dalpha_{t+1} + d_o_t . o_t,
+# so c_t = alpha_t dalpha_t is a reverse running sum inside the chunk that
+# starts from <Gend, S_end> at the chunk's end.
+# Every quantity is linear in the columns of the state (dv), so the model
+# can run on column slices and add the slices' contributions.
+# ---------------------------------------------------------------------------
+
+def chunked_bwd_seq(q, k, v, alpha, eta, eps, C, S0, d_o, d_fin, beta_direct=False,
+                    dv_slices=1):
+    """One (sequence, head) in fp64: returns dq, dk, dv, dalpha, deta, dS0."""
+    L, dk = q.shape
+    dv = v.shape[1]
+    alpha = np.ones(L) if alpha is None else alpha
+    kk = np.sum(k * k, axis=1)
+    beta_all = eta if beta_direct else eta / (kk + eps)
+    # forward pass: chunk-start states and the final state
+    starts = []
+    S = np.array(S0, dtype=np.float64, copy=True)
+    chunks = [(c0, min(c0 + C, L)) for c0 in range(0, L, C)]
+    ops = []
+    for a, b in chunks:
+        K, Q, V = k[a:b], q[a:b], v[a:b]
+        n = b - a
+        g = np.cumsum(np.log(alpha[a:b]))
+        gam = np.exp(g)
+        Gam = np.tril(np.exp(np.minimum(g[:, None] - g[None, :], 0.0)))
+        beta = beta_all[a:b]
+        E = solve_triangular(np.eye(n) + np.tril(Gam * (K @ K.T), -1) * beta[None, :],
+                             V - gam[:, None] * (K @ S), lower=True)
+        starts.append(S.copy())
+        ops.append((gam, Gam, beta, E))
+        S = gam[-1] * S + K.T @ ((beta * gam[-1] / gam)[:, None] * E)
+    S_L = S
+    dq = np.zeros((L, dk))
+    dkp = np.zeros((L, dk))
+    dvv = np.zeros((L, dv))
+    dbeta = np.zeros(L)
+    c = np.zeros(L)
+    dS0 = np.zeros((dk, dv))
+    for cols in np.array_split(np.arange(dv), dv_slices):
+        Gend = np.array(d_fin[:, cols], dtype=np.float64, copy=True)
+        cend = float(np.sum(Gend * S_L[:, cols]))
+        for (a, b), Sc, (gam, Gam, beta, E) in reversed(list(zip(chunks, starts, ops))):
+            K, Q, V, dO = k[a:b], q[a:b], v[a:b][:, cols], d_o[a:b][:, cols]
+            Sc, E = Sc[:, cols], E[:, cols]
+            n = b - a
+            B = beta
+            O = gam[:, None] * (Q @ Sc) + (Gam * (Q @ K.T) * B[None, :]) @ E
+            U = solve_triangular(np.eye(n) + np.triu(Gam.T * (K @ K.T), 1) * B[None, :],
+                                 (gam[-1] / gam)[:, None] * (K @ Gend) + (Gam.T * (K @ Q.T)) @ dO,
+                                 lower=False)
+            dvv[a:b, cols] = B[:, None] * U
+            dbeta[a:b] += np.sum(U * E, axis=1)
+            terms = np.sum(dO * O, axis=1) - B * np.sum(U * V, axis=1)
+            c[a:b] += cend + np.cumsum(terms[::-1])[::-1]
+            Ge = ((gam[-1] / gam)[:, None] * (E @ Gend.T) + (Gam.T * (E @ dO.T)) @ Q
+                  - (np.triu(Gam.T * (E @ U.T), 1) * B[None, :]) @ K)
+            Su = gam[:, None] * (U @ Sc.T) + (Gam * (U @ E.T) * B[None, :]) @ K
+            dq[a:b] += gam[:, None] * (dO @ Sc.T) + (Gam * (dO @ E.T) * B[None, :]) @ K
+            dkp[a:b] += B[:, None] * (Ge - Su)
+            Gend = gam[-1] * Gend + Q.T @ (gam[:, None] * dO) - K.T @ ((gam * B)[:, None] * U)
+            cend = float(np.sum(Gend * Sc))
+        dS0[:, cols] = Gend
+    if beta_direct:
+        dkk = dkp + (dbeta * beta_all ** 2)[:, None] * k
+        deta = dbeta
+    else:
+        dkk = dkp + (dbeta * (beta_all ** 2 - 2 * beta_all / (kk + eps)))[:, None] * k
+        deta = dbeta / (kk + eps)
+    return dq, dkk, dvv, c / alpha, deta, dS0
+
+
+def chunked_bwd(q, k, v, alpha, eta, d_o, cu_seqlens, eps, C, initial_state=None, d_final=None,
+                beta_direct=False, dv_slices=1):
+    """Packed layout as `chunked`; returns a dict like the oracle's bwd."""
+    tok, H, dk = q.shape
+    dv = v.shape[2]
+    n = len(cu_seqlens) - 1
+    out = {"dq": np.zeros((tok, H, dk)), "dk": np.zeros((tok, H, dk)),
+           "dv": np.zeros((tok, H, dv)), "dalpha": np.zeros((tok, H)),
+           "deta": np.zeros((tok, H)), "dS0": np.zeros((n, H, dk, dv))}
+    for s in range(n):
+        a, b = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        for h in range(H):
+            S0 = np.zeros((dk, dv)) if initial_state is None else initial_state[s, h]
+            dF = np.zeros((dk, dv)) if d_final is None else d_final[s, h]
+            r = chunked_bwd_seq(q[a:b, h], k[a:b, h], v[a:b, h],
+                                None if alpha is None else alpha[a:b, h], eta[a:b, h], eps, C,
+                                S0, d_o[a:b, h], dF, beta_direct, dv_slices)
+            for key, val in zip(("dq", "dk", "dv", "dalpha", "deta"), r[:5]):
+                out[key][a:b, h] = val
+            out["dS0"][s, h] = r[5]
+    if alpha is None:
+        out["dalpha"] = None
+    return out

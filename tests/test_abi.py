@@ -65,6 +65,11 @@ def lib():
     L.kla_status_string.restype = ctypes.c_char_p
     L.kla_status_string.argtypes = [ctypes.c_int]
     L.kla_version.restype = ctypes.c_char_p
+    L.kla_bwd_chunked_workspace_size.restype = ctypes.c_size_t
+    L.kla_bwd_chunked_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64] + [ctypes.c_int32] * 4
+    L.kla_bwd_chunked.restype = ctypes.c_int
+    L.kla_bwd_chunked.argtypes = [V] * 6 + [ctypes.c_int32, ctypes.c_int64] + [ctypes.c_int32] * 4 + [
+        F, ctypes.c_int, ctypes.c_int] + [V] * 9 + [V, ctypes.c_size_t, V]
     L.kla_fwd_chunked_workspace_size.restype = ctypes.c_size_t
     L.kla_fwd_chunked_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64] + [ctypes.c_int32] * 4
     return L
@@ -79,7 +84,8 @@ def test_header_declares_the_entry_points():
                                            "kla_fwd_chunked_split_workspace_size",
                                            "kla_fwd_chunked_workspace_size", "kla_decode_step",
                                            "kla_decode_step_ex", "kla_status_string",
-                                           "kla_version"])
+                                           "kla_version", "kla_bwd_chunked",
+                                           "kla_bwd_chunked_workspace_size"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -307,3 +313,60 @@ def test_binding_names_match_the_abi():
                  "kla_fwd_chunked_workspace_size",
                  "kla_fwd_chunked_split_workspace_size", "kla_status_string", "kla_version"):
         assert callable(getattr(pkg, name))
+
+
+def test_bwd_workspace_query(lib):
+    # chunk-start states (tok/64 + n_seqs slots), 8 column slices of dq and dk,
+    # their dbeta and decay sums, and |k|^2 (each section rounded up to 64 floats)
+    n, tok, H, d = 8, 16384, 16, 128
+    up = lambda x: (x + 63) // 64 * 64
+    want = (up((tok // 64 + n) * H * d * d) + 2 * up(8 * tok * H * d) + 2 * up(8 * tok * H)
+            + up(tok * H)) * 4
+    assert lib.kla_bwd_chunked_workspace_size(n, tok, H, d, d, 64) == want
+    assert lib.kla_bwd_chunked_workspace_size(n, tok, H, 96, 96, 64) == 0
+    assert lib.kla_bwd_chunked_workspace_size(n, tok, H, d, d, 32) == 0
+    assert lib.kla_bwd_chunked_workspace_size(0, tok, H, d, d, 64) == 0
+
+
+def bwd_args(lib, **over):
+    a = dict(q=BASE, k=BASE + 64 * MB, v=BASE + 128 * MB, alpha=BASE + 192 * MB,
+             eta=BASE + 200 * MB, cu=None, n_seqs=2, tok=128, H=2, dk=64, dv=64, chunk=64,
+             eps=1e-6, dtype=1, beta=0, s0=None, do=BASE + 256 * MB, dfin=None,
+             dq=BASE + 320 * MB, dkk=BASE + 384 * MB, dvv=BASE + 448 * MB, da=BASE + 512 * MB,
+             de=BASE + 520 * MB, ds0=None, ws=BASE + 1024 * MB, wsb=None, stream=None)
+    a.update(over)
+    if a["wsb"] is None:
+        a["wsb"] = lib.kla_bwd_chunked_workspace_size(2, 128, 2, 64, 64, 64)
+    return [a[x] for x in ("q", "k", "v", "alpha", "eta", "cu", "n_seqs", "tok", "H", "dk", "dv",
+                           "chunk", "eps", "dtype", "beta", "s0", "do", "dfin", "dq", "dkk", "dvv",
+                           "da", "de", "ds0", "ws", "wsb", "stream")]
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(n_seqs=0), INVALID),
+    (dict(tok=129), INVALID),
+    (dict(eps=-1.0), INVALID),
+    (dict(beta=2), INVALID),
+    (dict(do=None), INVALID),
+    (dict(dq=None), INVALID),
+    (dict(de=None), INVALID),
+    (dict(da=None), INVALID),           # alpha given: its gradient is required
+    (dict(ws=None), INVALID),
+    (dict(wsb=1024), WORKSPACE),
+    (dict(dq=BASE + 8), INVALID),       # output overlaps q
+    (dict(dkk=BASE + 320 * MB + 64), INVALID),  # dk overlaps dq
+    (dict(ds0=BASE + 256 * MB), INVALID),       # initial-state gradient overlaps d_o
+    (dict(ws=BASE + 448 * MB), INVALID),        # workspace overlaps dv
+    (dict(dvv=BASE + 448 * MB + 4), INVALID),   # misaligned
+    (dict(dk=96, dv=96), UNSUPPORTED),
+    (dict(chunk=32), UNSUPPORTED),
+    (dict(dtype=5), UNSUPPORTED),
+])
+def test_bwd_rejects(lib, over, code):
+    assert lib.kla_bwd_chunked(*bwd_args(lib, **over)) == code
+
+
+def test_bwd_no_alpha_needs_no_alpha_gradient(lib):
+    # without a decay gate the alpha gradient pointer is ignored; a wrong dk
+    # size still fails, so validation ran to the end without launching
+    assert lib.kla_bwd_chunked(*bwd_args(lib, alpha=None, da=None, dk=96, dv=96)) == UNSUPPORTED

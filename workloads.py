@@ -211,3 +211,15 @@ def decode(*, seed=0, n_seqs=None, H=None, d=None, steps=None, dtype=None, alpha
         out.append(st)
     return dict(state=state, steps=out, eps=EPS, n_seqs=N, H=Hh, d=dd,
                 dtype=p["dtype"])
+
+
+def grad_inputs(seed, tok, H, d, n_seqs, state_std=0.02):
+    """Seeded upstream gradients and start state for the backward:
+    d_o ~ N(0, 1) fp32 [tok, H, d], d_final ~ N(0, 1) fp32 [n_seqs, H, d, d]
+    and an initial state ~ N(0, state_std^2) fp32 [n_seqs, H, d, d]."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0x425744])))
+    d_o = rng.standard_normal((tok, H, d), dtype=np.float32)
+    d_final = rng.standard_normal((n_seqs, H, d, d), dtype=np.float32)
+    s0 = rng.standard_normal((n_seqs, H, d, d), dtype=np.float32) * np.float32(state_std)
+    return dict(d_o=torch.from_numpy(d_o), d_final=torch.from_numpy(d_final),
+                initial_state=torch.from_numpy(s0))
