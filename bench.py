@@ -18,6 +18,11 @@ Algorithmic work counted per token-head (d = 128, C = 64):
                  K K^T, Q K^T, T R, M Delta: 2*C*d each; Q S, K S, K^T Delta:
                  2*d*d each  ->  8*C*d + 6*d*d = 163,840
   decode bytes   the fp32 state read and written once: 2*d*d*4 per (seq, head)
+  backward       (`backward` object) the gradients of the layer-shaped
+                 prefill: reads q, k, v bf16, alpha, eta, d_o fp32, writes
+                 dq, dk, dv, dalpha, deta fp32: 2832 B per token-head; full-
+                 tile flops of the chunk form 20*C*d + 20*d*d = 491,520 per
+                 token-head, on the fp32 MFMA
   per-channel decay (Kimi Delta Attention gate, `kda` object): the same
                  work with alpha fp32 [.., dk]: 1288 - 4 + 4*d = 1796 B per
                  token-head; its prefill kernel computes in fp32 (fp32 MFMA)
@@ -301,6 +306,51 @@ def bench_kda(args, torch, kla, workloads, launches=50):
     return out
 
 
+def bench_bwd(args, torch, kla, workloads, launches=10):
+    """Backward of the layer-shaped prefill (kla_bwd_chunked): gradients of
+    q, k, v, alpha, eta and the start state from seeded d_o and d_final.
+    One call is two launches (the two-sweep kernel and the reduction over
+    column slices); the events bracket whole calls."""
+    inp = workloads.prefill("layer")
+    B, H, d = inp["n_seqs"], inp["H"], inp["d"]
+    T = inp["lengths"][0]
+    dev = "cuda:0"
+    g = workloads.grad_inputs(5, B * T, H, d, B)
+    q, k, v = (inp[n].to(dev).view(B, T, H, d) for n in ("q", "k", "v"))
+    a, e = (inp[n].to(dev).view(B, T, H) for n in ("alpha", "eta"))
+    do = g["d_o"].to(dev).view(B, T, H, d)
+    dfin = g["d_final"].to(dev)
+    ws = torch.empty(kla.kla_bwd_chunked_workspace_size(B, B * T, H, d, d), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kla.kla_bwd_chunked(q, k, v, a, e, do, d_final=dfin, eps=inp["eps"], workspace=ws)
+
+    for _ in range(3):
+        step()
+    _, ev_ms = time_launches(step, launches, stream)
+    th = B * T * H
+    nbytes = th * (3 * d * 2 + 2 * 4 + d * 4 + 3 * d * 4 + 2 * 4) + 2 * B * H * d * d * 4
+    flops = th * (20 * 64 * d + 20 * d * d)
+    tf = flops / (ev_ms * 1e-3) / 1e12
+    ws_bytes = ws.numel()
+    del q, k, v, a, e, do, dfin, ws, inp, g
+    return {"workload": f"backward of the layer-shaped prefill: {B} sequences x {T} tokens, H={H}, "
+                        f"dk=dv={d}, bf16 q/k/v, fp32 gates, d_o and d_final; gradients of q, k, "
+                        f"v, alpha, eta and the start state (fp32)",
+            "us_per_call": round(ev_ms * 1e3, 2),
+            "tokens_per_s": round(B * T / (ev_ms * 1e-3), 1),
+            "workspace_bytes": ws_bytes,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_MFMA_PEAK_TF,
+                         "unit": "TFLOP/s", "frac": round(tf / FP32_MFMA_PEAK_TF, 4),
+                         "traffic": None, "kernel": "bwd_kernel + bwd_finish_kernel (one call)",
+                         "avg_launch_us": round(ev_ms * 1e3, 2),
+                         "algorithmic_flops_per_launch": flops,
+                         "algorithmic_bytes_per_launch": nbytes,
+                         "hbm_gbs": round(nbytes / (ev_ms * 1e-3) / 1e9, 1)}}
+
+
 def cpu_baseline(pre, oracle):
     """fp64 reference on the host over the whole layer-shaped prefill."""
     import numpy as np
@@ -342,6 +392,8 @@ def main():
                     help="skip the long-context one-pass vs split-sequence comparison")
     ap.add_argument("--skip-kda", action="store_true",
                     help="skip the per-channel decay prefill and decode")
+    ap.add_argument("--skip-bwd", action="store_true",
+                    help="skip the backward of the layer-shaped prefill")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -414,6 +466,8 @@ def main():
         out["long_context"] = bench_long(args, torch, kla, workloads)
     if not args.skip_kda:
         out["kda"] = bench_kda(args, torch, kla, workloads)
+    if not args.skip_bwd:
+        out["backward"] = bench_bwd(args, torch, kla, workloads)
     if not args.skip_cpu_baseline:
         import oracle
         out["cpu_baseline"] = cpu_baseline(pre, oracle)

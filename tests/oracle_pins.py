@@ -31,7 +31,7 @@ import os
 
 import numpy as np
 
-from chunk_model import chunked, chunked_ch
+from chunk_model import chunked, chunked_bwd, chunked_ch
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 TIGHT = 1e-12
@@ -777,6 +777,35 @@ def pin_bwd_linear_in_upstream(fwd, decode):
         assert rel(a[key] + b[key], both[key]) < TIGHT, key
 
 
+
+def pin_bwd_chunk_form(fwd, decode):
+    """The chunk form of the backward (tests/chunk_model.py: adjoint
+    triangular solve, W and Z planes, reverse running sum for the decay,
+    also split into column slices of the state) gives the reverse sweep's
+    gradients for C in {1, 7, 16, 64}, ragged and empty sequences, both step
+    modes, with and without decay."""
+    bwd = _bwd(fwd)
+    rng = np.random.default_rng(54)
+    lens = [37, 0, 70, 5]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    L, H, dk, dv = int(cu[-1]), 2, 5, 6
+    q, k, v, alpha, eta = _rand_seq(rng, L, H, dk, dv)
+    S0 = rng.standard_normal((4, H, dk, dv))
+    d_o = rng.standard_normal((L, H, dv))
+    d_fin = rng.standard_normal((4, H, dk, dv))
+    for mode in ("kaczmarz", "direct"):
+        for a in (alpha, None):
+            ref = bwd(q, k, v, a, eta, d_o, cu_seqlens=cu, eps=1e-3, initial_state=S0,
+                      d_final=d_fin, beta_mode=mode)
+            for C, sl in ((1, 1), (7, 3), (16, 1), (64, 3)):
+                m = chunked_bwd(q, k, v, a, eta, d_o, cu, 1e-3, C, S0, d_fin,
+                                beta_direct=mode == "direct", dv_slices=sl)
+                for key in ref:
+                    if ref[key] is None:
+                        assert m[key] is None
+                    else:
+                        assert rel(m[key], ref[key]) < 1e-11, (mode, a is None, C, key)
+
 ALL_PINS = [pin_worked_example, pin_orthogonal_projection, pin_min_norm_bruteforce,
             pin_exact_line_search, pin_normalised_gradient, pin_exact_recall, pin_eta_zero,
             pin_scalar_case, pin_gated_deltanet_form, pin_chunk_form, pin_packed_and_resume,
@@ -790,4 +819,4 @@ ALL_PINS = [pin_worked_example, pin_orthogonal_projection, pin_min_norm_brutefor
             pin_ccq_numpy_covariance, pin_ccq_logsumexp_hessian, pin_ccq_lambda_zero_and_state,
             pin_ccq_constant_keys, pin_ccq_resume_and_decode,
             pin_bwd_finite_differences, pin_bwd_finite_differences_direct,
-            pin_bwd_eta_zero_closed_form, pin_bwd_linear_in_upstream]
+            pin_bwd_eta_zero_closed_form, pin_bwd_linear_in_upstream, pin_bwd_chunk_form]
