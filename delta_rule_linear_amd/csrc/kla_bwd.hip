@@ -69,6 +69,8 @@ struct BwdSmem {
   float kk[C];
   float fc[C];    // per-row factor of the state update
   float scan[C];
+  float la[C];    // log2 alpha of the chunk's rows (0 for padding or no decay)
+  float eta[C];
   float red[kWaves];
 };
 
@@ -110,43 +112,137 @@ __device__ inline void lower_tile(int p, int &bt, int &bs) {
   bs = p - bt * (bt + 1) / 2;
 }
 
+// One chunk's operands in registers (16-byte segments), fetched a chunk
+// ahead of their use with range-checked buffer loads: rows past the chunk's
+// end read zero, so a ragged tail needs no branch.
 template <typename E, int D>
-__device__ inline void load_chunk(BwdSmem<D> &sm, const BwdParams &p, const E *__restrict__ q,
-                                  const E *__restrict__ k, const E *__restrict__ v, int64_t t0,
-                                  int n, int h, int col0, bool with_q, int tid) {
-  constexpr int LDK = BwdSmem<D>::LDK;
-  for (int idx = tid; idx < C * D; idx += kThreads) {
-    const int r = idx / D, i = idx % D;
-    const int64_t g = ((t0 + r) * p.H + h) * D + i;
-    sm.K[r * LDK + i] = r < n ? ld(k, g) : 0.f;
-    if (with_q) sm.Q[r * LDK + i] = r < n ? ld(q, g) : 0.f;
+struct Fetch {
+  static constexpr int SEG_EL = 16 / sizeof(E);     // elements per segment
+  static constexpr int SEG_ROW = D / SEG_EL;        // segments per K / Q row
+  static constexpr int NKQ = C * SEG_ROW / kThreads;
+  static constexpr int VSEG = DVS / SEG_EL;         // segments per V row slice
+  static constexpr int NSS = D * (DVS / 4) / kThreads;  // state-slice segments
+  static_assert(NKQ * kThreads == C * SEG_ROW && NSS * kThreads == D * (DVS / 4), "tiling");
+  static_assert(C * VSEG <= kThreads && C * (DVS / 4) == kThreads, "slice tiling");
+  uint4 k[NKQ], q[NKQ];
+  uint4 v, d;
+  uint4 s[NSS];
+  float a, e;
+};
+
+template <typename E, int D>
+__device__ inline void fetch(Fetch<E, D> &f, const BwdParams &p, int64_t t0, int n, int h,
+                             int col0, const float *ckslot, bool rev, int tid) {
+  using F = Fetch<E, D>;
+  constexpr int esz = sizeof(E);
+  const int64_t HD = (int64_t)p.H * D;
+  const int64_t base = t0 * HD + (int64_t)h * D;
+  const int64_t rows_kq = n > 0 ? ((int64_t)(n - 1) * HD + D) * esz : 0;
+  const rsrc_t rk = make_rsrc(static_cast<const E *>(p.k) + base, rows_kq);
+#pragma unroll
+  for (int m = 0; m < F::NKQ; ++m) {
+    const int sg = tid + kThreads * m, r = sg / F::SEG_ROW, cs = sg % F::SEG_ROW;
+    f.k[m] = buf_ld16(rk, (uint32_t)(r * HD * esz + cs * 16));
   }
-  for (int idx = tid; idx < C * DVS; idx += kThreads) {
-    const int r = idx / DVS, c = idx % DVS;
-    const int64_t g = ((t0 + r) * p.H + h) * D + col0 + c;
-    sm.Vs[r * LDSL + c] = r < n ? ld(v, g) : 0.f;
-    if (with_q) sm.Ds[r * LDSL + c] = r < n ? p.d_o[g] : 0.f;
+  if (rev) {
+    const rsrc_t rq = make_rsrc(static_cast<const E *>(p.q) + base, rows_kq);
+#pragma unroll
+    for (int m = 0; m < F::NKQ; ++m) {
+      const int sg = tid + kThreads * m, r = sg / F::SEG_ROW, cs = sg % F::SEG_ROW;
+      f.q[m] = buf_ld16(rq, (uint32_t)(r * HD * esz + cs * 16));
+    }
+    const rsrc_t rd = make_rsrc(p.d_o + base + col0, n > 0 ? ((int64_t)(n - 1) * HD + DVS) * 4 : 0);
+    f.d = buf_ld16(rd, (uint32_t)((tid / 4) * HD * 4 + (tid % 4) * 16));
+#pragma unroll
+    for (int m = 0; m < F::NSS; ++m) {
+      const int sg = tid + kThreads * m, r = sg / 4, cs = sg % 4;
+      f.s[m] = *reinterpret_cast<const uint4 *>(ckslot + (int64_t)r * D + col0 + 4 * cs);
+    }
+  }
+  const rsrc_t rv = make_rsrc(static_cast<const E *>(p.v) + base + col0,
+                              n > 0 ? ((int64_t)(n - 1) * HD + DVS) * esz : 0);
+  if (tid < C * F::VSEG)
+    f.v = buf_ld16(rv, (uint32_t)((tid / F::VSEG) * HD * esz + (tid % F::VSEG) * 16));
+  if (tid < C) {
+    const int64_t gb = t0 * p.H + h;
+    const int64_t rows_s = n > 0 ? ((int64_t)(n - 1) * p.H + 1) * 4 : 0;
+    f.e = buf_ld4(make_rsrc(p.eta + gb, rows_s), (uint32_t)(tid * p.H * 4));
+    f.a = p.alpha ? buf_ld4(make_rsrc(p.alpha + gb, rows_s), (uint32_t)(tid * p.H * 4)) : 1.f;
   }
 }
 
-// Row scalars: |k|^2, beta, the cumulative log2 decay and 2^gl (wave 0).
-template <int D>
-__device__ inline void row_scalars(BwdSmem<D> &sm, const BwdParams &p, int64_t t0, int n, int h,
-                                   int tid) {
+__device__ inline void cvt(const uint4 &u, __bf16, float (&x)[8]) {
+  const bf16x8 b = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(b[e]);
+}
+__device__ inline void cvt(const uint4 &u, float, float (&x)[4]) {
+  x[0] = __uint_as_float(u.x);
+  x[1] = __uint_as_float(u.y);
+  x[2] = __uint_as_float(u.z);
+  x[3] = __uint_as_float(u.w);
+}
+__device__ inline void st4(float *dst, const float *x) {
+  *reinterpret_cast<f32x4 *>(dst) = f32x4{x[0], x[1], x[2], x[3]};
+}
+
+// Registers -> LDS (fp32), with the row norms |k|^2 and the raw gates.
+template <typename E, int D>
+__device__ inline void commit(BwdSmem<D> &sm, const Fetch<E, D> &f, int n, bool rev, int tid) {
+  using F = Fetch<E, D>;
   constexpr int LDK = BwdSmem<D>::LDK;
+#pragma unroll
+  for (int m = 0; m < F::NKQ; ++m) {
+    const int sg = tid + kThreads * m, r = sg / F::SEG_ROW, cs = sg % F::SEG_ROW;
+    float x[F::SEG_EL];
+    cvt(f.k[m], E{}, x);
+    float kk = 0.f;
+#pragma unroll
+    for (int e = 0; e < F::SEG_EL; ++e) kk = fmaf(x[e], x[e], kk);
+#pragma unroll
+    for (int e = 0; e < F::SEG_EL; e += 4) st4(&sm.K[r * LDK + cs * F::SEG_EL + e], x + e);
+    kk = group_sum<F::SEG_ROW>(kk);  // the SEG_ROW lanes of row r hold its segments
+    if (cs == 0) sm.kk[r] = kk;
+    if (rev) {
+      cvt(f.q[m], E{}, x);
+#pragma unroll
+      for (int e = 0; e < F::SEG_EL; e += 4) st4(&sm.Q[r * LDK + cs * F::SEG_EL + e], x + e);
+    }
+  }
+  if (tid < C * F::VSEG) {
+    float x[F::SEG_EL];
+    cvt(f.v, E{}, x);
+    const int r = tid / F::VSEG, cs = tid % F::VSEG;
+#pragma unroll
+    for (int e = 0; e < F::SEG_EL; e += 4) st4(&sm.Vs[r * LDSL + cs * F::SEG_EL + e], x + e);
+  }
+  if (rev) {
+    float x[4];
+    cvt(f.d, float{}, x);
+    st4(&sm.Ds[(tid / 4) * LDSL + (tid % 4) * 4], x);
+#pragma unroll
+    for (int m = 0; m < F::NSS; ++m) {
+      const int sg = tid + kThreads * m;
+      cvt(f.s[m], float{}, x);
+      st4(&sm.Sc[(sg / 4) * LDSL + (sg % 4) * 4], x);
+    }
+  }
+  if (tid < C) {
+    sm.la[tid] = (tid < n && f.a != 1.f) ? flog2(f.a) : 0.f;
+    sm.eta[tid] = tid < n ? f.e : 0.f;
+  }
+}
+
+// Row scalars from LDS: |k|^2, beta, the cumulative log2 decay and 2^gl
+// (wave 0).
+template <int D>
+__device__ inline void row_scalars(BwdSmem<D> &sm, const BwdParams &p, int n, int tid) {
   if (tid < C) {
     const int r = tid;
-    float kk = 0.f;
-    for (int i = 0; i < D; ++i) kk = fmaf(sm.K[r * LDK + i], sm.K[r * LDK + i], kk);
-    float beta = 0.f, la = 0.f;
-    if (r < n) {
-      const int64_t th = (t0 + r) * p.H + h;
-      const float eta = p.eta[th];
-      beta = p.beta_direct ? eta : eta / (kk + p.eps);
-      if (p.alpha) la = flog2(p.alpha[th]);
-    }
-    const float g = wave_scan(la);
-    sm.kk[r] = kk;
+    const float kk = sm.kk[r];
+    const float eta = sm.eta[r];
+    const float beta = r < n ? (p.beta_direct ? eta : eta / (kk + p.eps)) : 0.f;
+    const float g = wave_scan(sm.la[r]);
     sm.beta[r] = beta;
     sm.gl[r] = g;
     sm.gm[r] = fexp2(g);
@@ -243,9 +339,9 @@ template <int D>
 __device__ inline float block_sum(BwdSmem<D> &sm, float x, int w, int l) {
   x = group_sum<32>(x);
   x += __shfl_xor(x, 32, 64);
-  __syncthreads();
+  lds_barrier();
   if (l == 0) sm.red[w] = x;
-  __syncthreads();
+  lds_barrier();
   float t = 0.f;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) t += sm.red[i];
@@ -272,36 +368,41 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
   const int col0 = sl * DVS;
   const Tok sq = seq_of(p, s);
   const int nch = (sq.L + C - 1) / C;
-  const E *q = static_cast<const E *>(p.q);
-  const E *k = static_cast<const E *>(p.k);
-  const E *v = static_cast<const E *>(p.v);
   // checkpoint slots of this sequence: floor(bos / C) + s onwards (disjoint)
   float *ck = p.ws_ckpt + ((sq.bos / C + s) * p.H + h) * (int64_t)DD;
+  const int64_t slot = (int64_t)p.H * DD;
   const int64_t TH = p.total_tok * p.H;
+  using F = Fetch<E, D>;
+  F f;
 
   // ---- forward sweep: chunk-start states -------------------------------
   for (int idx = tid; idx < D * DVS; idx += kThreads) {
     const int i = idx / DVS, c = idx % DVS;
     sm.Sc[i * LDSL + c] = p.initial_state ? p.initial_state[sh * DD + i * D + col0 + c] : 0.f;
   }
+  if (nch > 0) fetch<E, D>(f, p, sq.bos, min(C, sq.L), h, col0, ck, false, tid);
   for (int ci = 0; ci < nch; ++ci) {
-    const int64_t t0 = sq.bos + (int64_t)ci * C;
     const int n = min(C, sq.L - ci * C);
-    __syncthreads();
-    load_chunk<E, D>(sm, p, q, k, v, t0, n, h, col0, false, tid);
-    for (int idx = tid; idx < D * DVS; idx += kThreads) {
-      const int i = idx / DVS, c = idx % DVS;
-      ck[(int64_t)ci * p.H * DD + i * D + col0 + c] = sm.Sc[i * LDSL + c];
+    lds_barrier();
+    commit<E, D>(sm, f, n, false, tid);
+#pragma unroll
+    for (int m = 0; m < F::NSS; ++m) {
+      const int sg = tid + kThreads * m, r = sg / 4, cs = sg % 4;
+      *reinterpret_cast<f32x4 *>(ck + ci * slot + (int64_t)r * D + col0 + 4 * cs) =
+          *reinterpret_cast<const f32x4 *>(&sm.Sc[r * LDSL + 4 * cs]);
     }
-    __syncthreads();
-    row_scalars<D>(sm, p, t0, n, h, tid);
-    __syncthreads();
+    if (ci + 1 < nch)
+      fetch<E, D>(f, p, sq.bos + (int64_t)(ci + 1) * C, min(C, sq.L - (ci + 1) * C), h, col0, ck,
+                  false, tid);
+    lds_barrier();
+    row_scalars<D>(sm, p, n, tid);
+    lds_barrier();
     gram<D>(sm, false, w, j, c16);
     residual_tile<D>(sm, w, j, c16);
     if (tid < C) sm.fc[tid] = sm.beta[tid] * fexp2(sm.gl[C - 1] - sm.gl[tid]);
-    __syncthreads();
+    lds_barrier();
     if (w == 0) tri_solve<false>(sm.Es, sm.Am, l, j, c16);
-    __syncthreads();
+    lds_barrier();
     // S <- gamma_n S + K^T Diag(beta gamma_n / gamma) E
     const float gn = sm.gm[C - 1];
     for (int ti = w; ti < D / 16; ti += kWaves) {
@@ -314,6 +415,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
       for (int i = 0; i < 4; ++i) sm.Sc[(16 * ti + 4 * j + i) * LDSL + c16] = acc[i];
     }
   }
+  // the checkpoints are read back below by the threads that wrote them
   __syncthreads();
 
   // ---- reverse sweep ----------------------------------------------------
@@ -321,7 +423,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
     const int i = idx / DVS, c = idx % DVS;
     sm.Gd[i * LDSL + c] = p.d_final ? p.d_final[sh * DD + i * D + col0 + c] : 0.f;
   }
-  __syncthreads();
+  if (nch > 0)
+    fetch<E, D>(f, p, sq.bos + (int64_t)(nch - 1) * C, sq.L - (nch - 1) * C, h, col0,
+                ck + (nch - 1) * slot, true, tid);
+  lds_barrier();
   float cend;
   {
     float x = 0.f;
@@ -336,22 +441,28 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
   float *dbp = p.ws_db + (int64_t)sl * TH;
   float *cp = p.ws_c + (int64_t)sl * TH;
 
+  const int64_t HD = (int64_t)p.H * D;
   for (int ci = nch - 1; ci >= 0; --ci) {
     const int64_t t0 = sq.bos + (int64_t)ci * C;
     const int n = min(C, sq.L - ci * C);
-    __syncthreads();
-    load_chunk<E, D>(sm, p, q, k, v, t0, n, h, col0, true, tid);
-    for (int idx = tid; idx < D * DVS; idx += kThreads) {
-      const int i = idx / DVS, c = idx % DVS;
-      sm.Sc[i * LDSL + c] = ck[(int64_t)ci * p.H * DD + i * D + col0 + c];
-    }
-    __syncthreads();
-    row_scalars<D>(sm, p, t0, n, h, tid);
-    if (sl == 0 && tid < n) p.ws_kk[(t0 + tid) * p.H + h] = sm.kk[tid];
-    __syncthreads();
+    lds_barrier();
+    commit<E, D>(sm, f, n, true, tid);
+    if (ci > 0) fetch<E, D>(f, p, t0 - C, C, h, col0, ck + (ci - 1) * slot, true, tid);
+    // range-checked stores: rows past the chunk's end are dropped
+    const int64_t nrow = n - 1;
+    const rsrc_t r_kk = make_rsrc(p.ws_kk + t0 * p.H + h, (nrow * p.H + 1) * 4);
+    const rsrc_t r_db = make_rsrc(dbp + t0 * p.H + h, (nrow * p.H + 1) * 4);
+    const rsrc_t r_c = make_rsrc(cp + t0 * p.H + h, (nrow * p.H + 1) * 4);
+    const rsrc_t r_dv = make_rsrc(p.dv + t0 * HD + (int64_t)h * D + col0, (nrow * HD + DVS) * 4);
+    const rsrc_t r_dq = make_rsrc(dqp + t0 * HD + (int64_t)h * D, (nrow * HD + D) * 4);
+    const rsrc_t r_dk = make_rsrc(dkp + t0 * HD + (int64_t)h * D, (nrow * HD + D) * 4);
+    lds_barrier();
+    row_scalars<D>(sm, p, n, tid);
+    lds_barrier();
+    if (sl == 0 && tid < C) buf_st4(r_kk, (uint32_t)(tid * p.H * 4), sm.kk[tid]);
     gram<D>(sm, true, w, j, c16);
     residual_tile<D>(sm, w, j, c16);
-    __syncthreads();
+    lds_barrier();
     const float glast = sm.gl[C - 1];
     if (w == 0) {
       tri_solve<false>(sm.Es, sm.Am, l, j, c16);
@@ -372,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (w == 0) {
       tri_solve<true>(sm.Us, sm.Am, l, j, c16);
     } else {
@@ -392,7 +503,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     // per-row outputs: dv, the dbeta part and the decay running sum
     if (tid < C) {
       const int r = tid;
@@ -408,17 +519,16 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
       // suffix sum over rows r..63 (padded rows add zero)
       const float suf = wave_scan(__shfl(term, 63 - r, 64));
       sm.scan[63 - r] = suf;
-      if (r < n) {
-        const int64_t th = (t0 + r) * p.H + h;
-        dbp[th] = db;
-      }
+      buf_st4(r_db, (uint32_t)(r * p.H * 4), db);
     }
-    for (int idx = tid; idx < C * DVS; idx += kThreads) {
-      const int r = idx / DVS, c = idx % DVS;
-      if (r < n) p.dv[((t0 + r) * p.H + h) * D + col0 + c] = sm.beta[r] * sm.Us[r * LDSL + c];
+    {
+      const int r = tid / 4, cs = tid % 4;
+      const float b = sm.beta[r];
+      const f32x4 u = *reinterpret_cast<const f32x4 *>(&sm.Us[r * LDSL + 4 * cs]);
+      buf_st16(r_dv, (uint32_t)(r * HD * 4 + cs * 16), f32x4{b * u[0], b * u[1], b * u[2], b * u[3]});
     }
-    __syncthreads();
-    if (tid < n) cp[(t0 + tid) * p.H + h] = cend + sm.scan[tid];
+    lds_barrier();
+    if (tid < C) buf_st4(r_c, (uint32_t)(tid * p.H * 4), cend + sm.scan[tid]);
     // W (symmetric, from U E^T) into Am; Z = Lower(Gam o dO E^T) into Xm
     for (int jb = w; jb < 20; jb += kWaves) {
       const bool zq = jb >= 10;
@@ -441,7 +551,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     // dq and dk contributions of these columns: 2 x (4 x D/16) tiles
     for (int jb = w; jb < 8 * (D / 16); jb += kWaves) {
       const bool isq = jb >= 4 * (D / 16);
@@ -476,11 +586,11 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
           out[i] = sm.beta[t] * (fexp2(glast - sm.gl[t]) * a1[i] - sm.gm[t] * a2[i] + a3[i]);
         }
       }
-      float *dst = isq ? dqp : dkp;
+      const rsrc_t rd = isq ? r_dq : r_dk;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * bt + 4 * j + i;
-        if (t < n) dst[((t0 + t) * p.H + h) * D + 16 * bi + c16] = out[i];
+        buf_st4(rd, (uint32_t)((t * HD + 16 * bi + c16) * 4), out[i]);
       }
     }
     // Gend <- gamma_n Gend + Q^T Diag(gamma) dO - K^T Diag(gamma beta) U
@@ -501,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
         gnew[m] = acc;
       }
     }
-    __syncthreads();
+    lds_barrier();
     {
       float x = 0.f;
 #pragma unroll
@@ -527,25 +637,36 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
 }
 
 // Adds the column slices' contributions in slice order and finishes dk,
-// deta and dalpha.  One thread per (token, head, key channel).
+// deta and dalpha.  One thread per 4 consecutive key channels of a
+// (token, head).
+__device__ inline f32x4 ld_k4(const __bf16 *k, int64_t g) {
+  const bf16x4 b = *reinterpret_cast<const bf16x4 *>(k + g);
+  return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+}
+__device__ inline f32x4 ld_k4(const float *k, int64_t g) {
+  return *reinterpret_cast<const f32x4 *>(k + g);
+}
+
 template <typename E, int D>
 __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdParams p) {
   constexpr int NS = D / DVS;
   const int64_t TH = p.total_tok * p.H;
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= TH * D) return;
-  const int64_t th = g / D;
+  const int64_t g4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g4 >= TH * (D / 4)) return;
+  const int64_t g = 4 * g4, th = g / D;
   const int i = (int)(g % D);
-  float dq = 0.f, dk = 0.f, db = 0.f, c = 0.f;
+  f32x4 dq = zero4(), dk = zero4();
+  float db = 0.f, c = 0.f;
+#pragma unroll
   for (int s = 0; s < NS; ++s) {
-    dq += p.ws_dq[(int64_t)s * TH * D + g];
-    dk += p.ws_dk[(int64_t)s * TH * D + g];
+    dq += *reinterpret_cast<const f32x4 *>(p.ws_dq + (int64_t)s * TH * D + g);
+    dk += *reinterpret_cast<const f32x4 *>(p.ws_dk + (int64_t)s * TH * D + g);
     db += p.ws_db[(int64_t)s * TH + th];
     c += p.ws_c[(int64_t)s * TH + th];
   }
   const float kk = p.ws_kk[th];
   const float eta = p.eta[th];
-  const float kv = static_cast<float>(static_cast<const E *>(p.k)[g]);
+  const f32x4 kv = ld_k4(static_cast<const E *>(p.k), g);
   float coef;
   if (p.beta_direct) {
     coef = eta * eta;
@@ -554,8 +675,10 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdParams p) {
     const float beta = eta / den;
     coef = beta * beta - 2.f * beta / den;
   }
-  p.dq[g] = dq;
-  p.dk[g] = fmaf(db * coef, kv, dk);
+  const float f = db * coef;
+  *reinterpret_cast<f32x4 *>(p.dq + g) = dq;
+  *reinterpret_cast<f32x4 *>(p.dk + g) =
+      f32x4{fmaf(f, kv[0], dk[0]), fmaf(f, kv[1], dk[1]), fmaf(f, kv[2], dk[2]), fmaf(f, kv[3], dk[3])};
   if (i == 0) {
     p.d_eta[th] = p.beta_direct ? db : db / (kk + p.eps);
     if (p.alpha) p.d_alpha[th] = c / p.alpha[th];
@@ -568,8 +691,8 @@ hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
   hipLaunchKernelGGL((bwd_kernel<E, D>), dim3((unsigned)groups), dim3(kThreads), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.total_tok == 0) return e;
-  const int64_t n = p.total_tok * p.H * D;
-  hipLaunchKernelGGL((bwd_finish_kernel<E, D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
+  const int64_t n4 = p.total_tok * p.H * (D / 4);
+  hipLaunchKernelGGL((bwd_finish_kernel<E, D>), dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
