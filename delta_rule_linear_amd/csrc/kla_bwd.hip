@@ -28,7 +28,7 @@
 // started at <Gend, S_end> at each chunk's end.
 //
 // Every quantity is linear in the state's columns (dv), so one workgroup of
-// 4 waves takes one (sequence, head, 16 columns of dv): the fp32 slices of
+// 8 waves (two per SIMD) takes one (sequence, head, 16 columns of dv): the fp32 slices of
 // S and Gend, K and Q of a chunk and the 64 x 64 planes fit in LDS.  A first
 // sweep runs the chunks forward and stores each chunk-start state slice in
 // the workspace; the reverse sweep then takes the chunks from last to first.
@@ -46,6 +46,8 @@ namespace kla {
 namespace {
 
 constexpr int DVS = 16;         // state columns per workgroup
+constexpr int BW = 8;           // waves per workgroup (two per SIMD)
+constexpr int BT = 64 * BW;     // threads per workgroup
 constexpr int LDSL = DVS + 4;   // row pitch of the column-slice tiles
 constexpr int LDN = C + 4;      // row pitch of the 64 x 64 planes
 
@@ -71,7 +73,7 @@ struct BwdSmem {
   float scan[C];
   float la[C];    // log2 alpha of the chunk's rows (0 for padding or no decay)
   float eta[C];
-  float red[kWaves];
+  float red[BW];
 };
 
 struct Tok {
@@ -119,11 +121,12 @@ template <typename E, int D>
 struct Fetch {
   static constexpr int SEG_EL = 16 / sizeof(E);     // elements per segment
   static constexpr int SEG_ROW = D / SEG_EL;        // segments per K / Q row
-  static constexpr int NKQ = C * SEG_ROW / kThreads;
+  static constexpr int NKQ = C * SEG_ROW / BT;
   static constexpr int VSEG = DVS / SEG_EL;         // segments per V row slice
-  static constexpr int NSS = D * (DVS / 4) / kThreads;  // state-slice segments
-  static_assert(NKQ * kThreads == C * SEG_ROW && NSS * kThreads == D * (DVS / 4), "tiling");
-  static_assert(C * VSEG <= kThreads && C * (DVS / 4) == kThreads, "slice tiling");
+  static constexpr int NSSEG = D * (DVS / 4);       // state-slice segments
+  static constexpr int NSS = (NSSEG + BT - 1) / BT;
+  static_assert(NKQ * BT == C * SEG_ROW, "tiling");
+  static_assert(C * VSEG <= BT && C * (DVS / 4) <= BT, "slice tiling");
   uint4 k[NKQ], q[NKQ];
   uint4 v, d;
   uint4 s[NSS];
@@ -141,22 +144,22 @@ __device__ inline void fetch(Fetch<E, D> &f, const BwdParams &p, int64_t t0, int
   const rsrc_t rk = make_rsrc(static_cast<const E *>(p.k) + base, rows_kq);
 #pragma unroll
   for (int m = 0; m < F::NKQ; ++m) {
-    const int sg = tid + kThreads * m, r = sg / F::SEG_ROW, cs = sg % F::SEG_ROW;
+    const int sg = tid + BT * m, r = sg / F::SEG_ROW, cs = sg % F::SEG_ROW;
     f.k[m] = buf_ld16(rk, (uint32_t)(r * HD * esz + cs * 16));
   }
   if (rev) {
     const rsrc_t rq = make_rsrc(static_cast<const E *>(p.q) + base, rows_kq);
 #pragma unroll
     for (int m = 0; m < F::NKQ; ++m) {
-      const int sg = tid + kThreads * m, r = sg / F::SEG_ROW, cs = sg % F::SEG_ROW;
+      const int sg = tid + BT * m, r = sg / F::SEG_ROW, cs = sg % F::SEG_ROW;
       f.q[m] = buf_ld16(rq, (uint32_t)(r * HD * esz + cs * 16));
     }
     const rsrc_t rd = make_rsrc(p.d_o + base + col0, n > 0 ? ((int64_t)(n - 1) * HD + DVS) * 4 : 0);
-    f.d = buf_ld16(rd, (uint32_t)((tid / 4) * HD * 4 + (tid % 4) * 16));
+    if (tid < C * (DVS / 4)) f.d = buf_ld16(rd, (uint32_t)((tid / 4) * HD * 4 + (tid % 4) * 16));
 #pragma unroll
     for (int m = 0; m < F::NSS; ++m) {
-      const int sg = tid + kThreads * m, r = sg / 4, cs = sg % 4;
-      f.s[m] = *reinterpret_cast<const uint4 *>(ckslot + (int64_t)r * D + col0 + 4 * cs);
+      const int sg = tid + BT * m, r = sg / 4, cs = sg % 4;
+      if (sg < F::NSSEG) f.s[m] = *reinterpret_cast<const uint4 *>(ckslot + (int64_t)r * D + col0 + 4 * cs);
     }
   }
   const rsrc_t rv = make_rsrc(static_cast<const E *>(p.v) + base + col0,
@@ -193,7 +196,7 @@ __device__ inline void commit(BwdSmem<D> &sm, const Fetch<E, D> &f, int n, bool 
   constexpr int LDK = BwdSmem<D>::LDK;
 #pragma unroll
   for (int m = 0; m < F::NKQ; ++m) {
-    const int sg = tid + kThreads * m, r = sg / F::SEG_ROW, cs = sg % F::SEG_ROW;
+    const int sg = tid + BT * m, r = sg / F::SEG_ROW, cs = sg % F::SEG_ROW;
     float x[F::SEG_EL];
     cvt(f.k[m], E{}, x);
     float kk = 0.f;
@@ -218,13 +221,17 @@ __device__ inline void commit(BwdSmem<D> &sm, const Fetch<E, D> &f, int n, bool 
   }
   if (rev) {
     float x[4];
-    cvt(f.d, float{}, x);
-    st4(&sm.Ds[(tid / 4) * LDSL + (tid % 4) * 4], x);
+    if (tid < C * (DVS / 4)) {
+      cvt(f.d, float{}, x);
+      st4(&sm.Ds[(tid / 4) * LDSL + (tid % 4) * 4], x);
+    }
 #pragma unroll
     for (int m = 0; m < F::NSS; ++m) {
-      const int sg = tid + kThreads * m;
-      cvt(f.s[m], float{}, x);
-      st4(&sm.Sc[(sg / 4) * LDSL + (sg % 4) * 4], x);
+      const int sg = tid + BT * m;
+      if (sg < F::NSSEG) {
+        cvt(f.s[m], float{}, x);
+        st4(&sm.Sc[(sg / 4) * LDSL + (sg % 4) * 4], x);
+      }
     }
   }
   if (tid < C) {
@@ -255,7 +262,7 @@ template <int D>
 __device__ inline void gram(BwdSmem<D> &sm, bool with_q, int w, int j, int c16) {
   constexpr int LDK = BwdSmem<D>::LDK;
   const int jobs = with_q ? 20 : 10;
-  for (int jb = w; jb < jobs; jb += kWaves) {
+  for (int jb = w; jb < jobs; jb += BW) {
     const bool qk = jb >= 10;
     int bt, bs;
     lower_tile(qk ? jb - 10 : jb, bt, bs);
@@ -344,12 +351,12 @@ __device__ inline float block_sum(BwdSmem<D> &sm, float x, int w, int l) {
   lds_barrier();
   float t = 0.f;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) t += sm.red[i];
+  for (int i = 0; i < BW; ++i) t += sm.red[i];
   return t;
 }
 
 template <typename E, int D>
-__global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
   constexpr int LDK = BwdSmem<D>::LDK;
   constexpr int NS = D / DVS;
   constexpr int DD = D * D;
@@ -376,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
   F f;
 
   // ---- forward sweep: chunk-start states -------------------------------
-  for (int idx = tid; idx < D * DVS; idx += kThreads) {
+  for (int idx = tid; idx < D * DVS; idx += BT) {
     const int i = idx / DVS, c = idx % DVS;
     sm.Sc[i * LDSL + c] = p.initial_state ? p.initial_state[sh * DD + i * D + col0 + c] : 0.f;
   }
@@ -387,9 +394,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
     commit<E, D>(sm, f, n, false, tid);
 #pragma unroll
     for (int m = 0; m < F::NSS; ++m) {
-      const int sg = tid + kThreads * m, r = sg / 4, cs = sg % 4;
-      *reinterpret_cast<f32x4 *>(ck + ci * slot + (int64_t)r * D + col0 + 4 * cs) =
-          *reinterpret_cast<const f32x4 *>(&sm.Sc[r * LDSL + 4 * cs]);
+      const int sg = tid + BT * m, r = sg / 4, cs = sg % 4;
+      if (sg < F::NSSEG)
+        *reinterpret_cast<f32x4 *>(ck + ci * slot + (int64_t)r * D + col0 + 4 * cs) =
+            *reinterpret_cast<const f32x4 *>(&sm.Sc[r * LDSL + 4 * cs]);
     }
     if (ci + 1 < nch)
       fetch<E, D>(f, p, sq.bos + (int64_t)(ci + 1) * C, min(C, sq.L - (ci + 1) * C), h, col0, ck,
@@ -398,14 +406,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
     row_scalars<D>(sm, p, n, tid);
     lds_barrier();
     gram<D>(sm, false, w, j, c16);
-    residual_tile<D>(sm, w, j, c16);
+    if (w < 4) residual_tile<D>(sm, w, j, c16);
     if (tid < C) sm.fc[tid] = sm.beta[tid] * fexp2(sm.gl[C - 1] - sm.gl[tid]);
     lds_barrier();
     if (w == 0) tri_solve<false>(sm.Es, sm.Am, l, j, c16);
     lds_barrier();
     // S <- gamma_n S + K^T Diag(beta gamma_n / gamma) E
     const float gn = sm.gm[C - 1];
-    for (int ti = w; ti < D / 16; ti += kWaves) {
+    for (int ti = w; ti < D / 16; ti += BW) {
       f32x4 acc;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = gn * sm.Sc[(16 * ti + 4 * j + i) * LDSL + c16];
@@ -419,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
   __syncthreads();
 
   // ---- reverse sweep ----------------------------------------------------
-  for (int idx = tid; idx < D * DVS; idx += kThreads) {
+  for (int idx = tid; idx < D * DVS; idx += BT) {
     const int i = idx / DVS, c = idx % DVS;
     sm.Gd[i * LDSL + c] = p.d_final ? p.d_final[sh * DD + i * D + col0 + c] : 0.f;
   }
@@ -430,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
   float cend;
   {
     float x = 0.f;
-    for (int idx = tid; idx < D * DVS; idx += kThreads) {
+    for (int idx = tid; idx < D * DVS; idx += BT) {
       const int i = idx / DVS, c = idx % DVS;
       x = fmaf(sm.Gd[i * LDSL + c], sm.Sc[i * LDSL + c], x);
     }
@@ -461,14 +469,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
     lds_barrier();
     if (sl == 0 && tid < C) buf_st4(r_kk, (uint32_t)(tid * p.H * 4), sm.kk[tid]);
     gram<D>(sm, true, w, j, c16);
-    residual_tile<D>(sm, w, j, c16);
+    if (w < 4) residual_tile<D>(sm, w, j, c16);
     lds_barrier();
     const float glast = sm.gl[C - 1];
     if (w == 0) {
       tri_solve<false>(sm.Es, sm.Am, l, j, c16);
     } else {
       // U right-hand side: Diag(gamma_n/gamma) K Gend + Mq^T dO
-      for (int bt = w - 1; bt < 4; bt += kWaves - 1) {
+      for (int bt = w - 1; bt < 4; bt += BW - 1) {
         f32x4 a1 = tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return sm.K[(16 * bt + c16) * LDK + kx]; },
                                   [&](int kx) { return sm.Gd[kx * LDSL + c16]; });
         f32x4 a2 = zero4();
@@ -488,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
       tri_solve<true>(sm.Us, sm.Am, l, j, c16);
     } else {
       // O = Diag(gamma) Q S + Mq B E
-      for (int bt = w - 1; bt < 4; bt += kWaves - 1) {
+      for (int bt = w - 1; bt < 4; bt += BW - 1) {
         f32x4 a1 = tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return sm.Q[(16 * bt + c16) * LDK + kx]; },
                                   [&](int kx) { return sm.Sc[kx * LDSL + c16]; });
         f32x4 a2 = zero4();
@@ -521,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
       sm.scan[63 - r] = suf;
       buf_st4(r_db, (uint32_t)(r * p.H * 4), db);
     }
-    {
+    if (tid < C * (DVS / 4)) {
       const int r = tid / 4, cs = tid % 4;
       const float b = sm.beta[r];
       const f32x4 u = *reinterpret_cast<const f32x4 *>(&sm.Us[r * LDSL + 4 * cs]);
@@ -530,7 +538,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
     lds_barrier();
     if (tid < C) buf_st4(r_c, (uint32_t)(tid * p.H * 4), cend + sm.scan[tid]);
     // W (symmetric, from U E^T) into Am; Z = Lower(Gam o dO E^T) into Xm
-    for (int jb = w; jb < 20; jb += kWaves) {
+    for (int jb = w; jb < 20; jb += BW) {
       const bool zq = jb >= 10;
       int bt, bs;
       lower_tile(zq ? jb - 10 : jb, bt, bs);
@@ -553,7 +561,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
     }
     lds_barrier();
     // dq and dk contributions of these columns: 2 x (4 x D/16) tiles
-    for (int jb = w; jb < 8 * (D / 16); jb += kWaves) {
+    for (int jb = w; jb < 8 * (D / 16); jb += BW) {
       const bool isq = jb >= 4 * (D / 16);
       const int tt = isq ? jb - 4 * (D / 16) : jb;
       const int bt = tt & 3, bi = tt >> 2;
@@ -594,13 +602,14 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
       }
     }
     // Gend <- gamma_n Gend + Q^T Diag(gamma) dO - K^T Diag(gamma beta) U
-    constexpr int NT = D / 16 / kWaves;  // state tiles per wave (2 or 1)
+    constexpr int NT = (D / 16 + BW - 1) / BW;  // state tiles per wave
     f32x4 gnew[NT];
     {
       const float gn = sm.gm[C - 1];
 #pragma unroll
       for (int m = 0; m < NT; ++m) {
-        const int ti = w + kWaves * m;
+        const int ti = w + BW * m;
+        if (ti >= D / 16) break;
         f32x4 acc;
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = gn * sm.Gd[(16 * ti + 4 * j + i) * LDSL + c16];
@@ -616,7 +625,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
       float x = 0.f;
 #pragma unroll
       for (int m = 0; m < NT; ++m) {
-        const int ti = w + kWaves * m;
+        const int ti = w + BW * m;
+        if (ti >= D / 16) break;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * ti + 4 * j + i;
@@ -629,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdParams p) {
   }
   __syncthreads();
   if (p.d_initial) {
-    for (int idx = tid; idx < D * DVS; idx += kThreads) {
+    for (int idx = tid; idx < D * DVS; idx += BT) {
       const int i = idx / DVS, c = idx % DVS;
       p.d_initial[sh * DD + i * D + col0 + c] = sm.Gd[i * LDSL + c];
     }
@@ -688,7 +698,7 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdParams p) {
 template <typename E, int D>
 hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
   const int64_t groups = (int64_t)p.n_seqs * p.H * (D / DVS);
-  hipLaunchKernelGGL((bwd_kernel<E, D>), dim3((unsigned)groups), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((bwd_kernel<E, D>), dim3((unsigned)groups), dim3(BT), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.total_tok == 0) return e;
   const int64_t n4 = p.total_tok * p.H * (D / 4);
