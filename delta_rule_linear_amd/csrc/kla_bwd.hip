@@ -33,7 +33,8 @@
 // sweep runs the chunks forward and stores each chunk-start state slice in
 // the workspace; the reverse sweep then takes the chunks from last to first.
 // Products are fp32 MFMA (v_mfma_f32_16x16x4_f32); the two triangular solves
-// are 16 x 16 block substitutions.  The column slices' contributions to dq,
+// are 16 x 16 block substitutions whose diagonal blocks are inverted first,
+// one wave per block, so the substitution itself is MFMA only.  The column slices' contributions to dq,
 // dk, dbeta and c land in the workspace and a second kernel adds them in a
 // fixed order (deterministic, no atomics) and finishes dk, deta, dalpha.
 #include <hip/hip_runtime.h>
@@ -50,6 +51,7 @@ constexpr int BW = 8;           // waves per workgroup (two per SIMD)
 constexpr int BT = 64 * BW;     // threads per workgroup
 constexpr int LDSL = DVS + 4;   // row pitch of the column-slice tiles
 constexpr int LDN = C + 4;      // row pitch of the 64 x 64 planes
+constexpr int LDY = 20;         // row pitch of the 16 x 16 diagonal-block inverses
 
 template <int D>
 struct BwdSmem {
@@ -65,6 +67,8 @@ struct BwdSmem {
   alignas(16) float Os[C * LDSL];  // outputs o_t
   alignas(16) float Am[C * LDN];   // lower: Gam o KK^T B; upper: its reverse twin; later W
   alignas(16) float Xm[C * LDN];   // Mq, later Z (lower, diagonal included)
+  alignas(16) float Yl[4 * 16 * LDY];  // (I + L_bb)^-1, unit lower, per diagonal block
+  alignas(16) float Yu[4 * 16 * LDY];  // (I + Lu_bb)^-1, unit upper
   float gl[C];    // cumulative log2 decay inside the chunk
   float gm[C];    // 2^gl
   float beta[C];
@@ -301,43 +305,65 @@ __device__ inline void residual_tile(BwdSmem<D> &sm, int bt, int j, int c16) {
   }
 }
 
-// Block substitution on X (64 x 16, in place) with the unit triangle of Am:
-// lower (forward, E) or upper (backward, U).  One wave.
+// Inverse of the unit triangular diagonal block b of Am (lower: the strict
+// lower part, upper: the strict upper part), one column per lane (lanes
+// 0..15 of the calling wave), by column substitution, into Y.
 template <bool UPPER>
-__device__ inline void tri_solve(float *X, const float *Am, int l, int j, int c16) {
-#pragma unroll 1
+__device__ inline void invert_block(const float *Am, float *Y, int b, int l) {
+  if (l < 16) {
+    float y[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) y[r] = r == l ? 1.f : 0.f;
+    const float *L = Am + 16 * b * LDN + 16 * b;
+    if (UPPER) {
+#pragma unroll
+      for (int r = 14; r >= 0; --r)
+#pragma unroll
+        for (int s = r + 1; s < 16; ++s) y[r] = fmaf(-L[r * LDN + s], y[s], y[r]);
+    } else {
+#pragma unroll
+      for (int r = 1; r < 16; ++r)
+#pragma unroll
+        for (int s = 0; s < r; ++s) y[r] = fmaf(-L[r * LDN + s], y[s], y[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Y[b * 16 * LDY + r * LDY + l] = y[r];
+  }
+}
+
+// Block substitution on X (64 x 16, in place) with the unit triangle of Am,
+// the diagonal blocks applied through their inverses Y: for each block b
+// (forward for the lower triangle, backward for the upper one)
+//   X_b <- Y_b (X_b - sum_c Am_bc X_c).  One wave; MFMA only.
+template <bool UPPER>
+__device__ inline void tri_solve_y(float *X, const float *Am, const float *Y, int j, int c16) {
+#pragma unroll
   for (int bb = 0; bb < 4; ++bb) {
     const int b = UPPER ? 3 - bb : bb;
     const int k0 = UPPER ? 16 * (b + 1) : 0;
     const int steps = UPPER ? 4 * (3 - b) : 4 * b;
+    f32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = X[(16 * b + 4 * j + i) * LDSL + c16];
     if (steps > 0) {
       f32x4 acc = zero4();
+#pragma unroll 4
       for (int st = 0; st < steps; ++st) {
         const int kx = k0 + 4 * st + j;
         acc = mma(Am[(16 * b + c16) * LDN + kx], X[kx * LDSL + c16], acc);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) X[(16 * b + 4 * j + i) * LDSL + c16] -= acc[i];
+      for (int i = 0; i < 4; ++i) X[(16 * b + 4 * j + i) * LDSL + c16] = r[i] - acc[i];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block's rows are in LDS
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block's rows are in LDS
-    if (l < 16) {
-      float x[16];
+    f32x4 x = zero4();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = X[(16 * b + r) * LDSL + l];
-      if (UPPER) {
-#pragma unroll
-        for (int r = 14; r >= 0; --r)
-#pragma unroll
-          for (int s = r + 1; s < 16; ++s) x[r] = fmaf(-Am[(16 * b + r) * LDN + 16 * b + s], x[s], x[r]);
-      } else {
-#pragma unroll
-        for (int r = 1; r < 16; ++r)
-#pragma unroll
-          for (int s = 0; s < r; ++s) x[r] = fmaf(-Am[(16 * b + r) * LDN + 16 * b + s], x[s], x[r]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) X[(16 * b + r) * LDSL + l] = x[r];
+    for (int st = 0; st < 4; ++st) {
+      const int kx = 4 * st + j;
+      x = mma(Y[b * 16 * LDY + c16 * LDY + kx], X[(16 * b + kx) * LDSL + c16], x);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) X[(16 * b + 4 * j + i) * LDSL + c16] = x[i];
     __builtin_amdgcn_s_waitcnt(0xc07f);
   }
 }
@@ -406,10 +432,12 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
     row_scalars<D>(sm, p, n, tid);
     lds_barrier();
     gram<D>(sm, false, w, j, c16);
-    if (w < 4) residual_tile<D>(sm, w, j, c16);
     if (tid < C) sm.fc[tid] = sm.beta[tid] * fexp2(sm.gl[C - 1] - sm.gl[tid]);
     lds_barrier();
-    if (w == 0) tri_solve<false>(sm.Es, sm.Am, l, j, c16);
+    if (w < 4) invert_block<false>(sm.Am, sm.Yl, w, l);
+    else residual_tile<D>(sm, w - 4, j, c16);
+    lds_barrier();
+    if (w == 0) tri_solve_y<false>(sm.Es, sm.Am, sm.Yl, j, c16);
     lds_barrier();
     // S <- gamma_n S + K^T Diag(beta gamma_n / gamma) E
     const float gn = sm.gm[C - 1];
@@ -471,9 +499,12 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
     gram<D>(sm, true, w, j, c16);
     if (w < 4) residual_tile<D>(sm, w, j, c16);
     lds_barrier();
+    if (w < 4) invert_block<false>(sm.Am, sm.Yl, w, l);
+    else invert_block<true>(sm.Am, sm.Yu, w - 4, l);
+    lds_barrier();
     const float glast = sm.gl[C - 1];
     if (w == 0) {
-      tri_solve<false>(sm.Es, sm.Am, l, j, c16);
+      tri_solve_y<false>(sm.Es, sm.Am, sm.Yl, j, c16);
     } else {
       // U right-hand side: Diag(gamma_n/gamma) K Gend + Mq^T dO
       for (int bt = w - 1; bt < 4; bt += BW - 1) {
@@ -493,7 +524,7 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
     }
     lds_barrier();
     if (w == 0) {
-      tri_solve<true>(sm.Us, sm.Am, l, j, c16);
+      tri_solve_y<true>(sm.Us, sm.Am, sm.Yu, j, c16);
     } else {
       // O = Diag(gamma) Q S + Mq B E
       for (int bt = w - 1; bt < 4; bt += BW - 1) {
