@@ -262,7 +262,24 @@ __device__ inline void row_scalars(BwdSmem<D> &sm, const BwdParams &p, int n, in
 
 // Am <- Gam o K K^T B below the diagonal and its reverse twin
 // (Gam^T o K K^T B) above it; with_q: Xm <- Lower(Gam o Q K^T).
-template <int D>
+// 8 fp32 values that hold bf16 numbers -> bf16x8 (exact).
+__device__ inline bf16x8 to_bf8(const float *p) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = static_cast<bf16>(a[e]);
+    r[4 + e] = static_cast<bf16>(b[e]);
+  }
+  return r;
+}
+
+// Am <- Gam o K K^T B below the diagonal and its reverse twin
+// (Gam^T o K K^T B) above it; with_q: Xm <- Lower(Gam o Q K^T).  With bf16
+// inputs K and Q hold bf16 values, so the Gram tiles use the bf16 MFMA
+// (exact products, fp32 accumulation); fp32 inputs use the fp32 MFMA.
+template <typename E, int D>
 __device__ inline void gram(BwdSmem<D> &sm, bool with_q, int w, int j, int c16) {
   constexpr int LDK = BwdSmem<D>::LDK;
   const int jobs = with_q ? 20 : 10;
@@ -271,9 +288,16 @@ __device__ inline void gram(BwdSmem<D> &sm, bool with_q, int w, int j, int c16) 
     int bt, bs;
     lower_tile(qk ? jb - 10 : jb, bt, bs);
     const float *X = qk ? sm.Q : sm.K;
-    f32x4 acc = tile_mm<D / 4>(zero4(), 0, j,
-                               [&](int kx) { return X[(16 * bt + c16) * LDK + kx]; },
-                               [&](int kx) { return sm.K[(16 * bs + c16) * LDK + kx]; });
+    f32x4 acc = zero4();
+    if constexpr (sizeof(E) == 2) {
+#pragma unroll
+      for (int kb = 0; kb < D / 32; ++kb)
+        acc = mma(to_bf8(&X[(16 * bt + c16) * LDK + 32 * kb + 8 * j]),
+                  to_bf8(&sm.K[(16 * bs + c16) * LDK + 32 * kb + 8 * j]), acc);
+    } else {
+      acc = tile_mm<D / 4>(acc, 0, j, [&](int kx) { return X[(16 * bt + c16) * LDK + kx]; },
+                           [&](int kx) { return sm.K[(16 * bs + c16) * LDK + kx]; });
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * bt + 4 * j + i, s = 16 * bs + c16;
@@ -431,7 +455,7 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
     lds_barrier();
     row_scalars<D>(sm, p, n, tid);
     lds_barrier();
-    gram<D>(sm, false, w, j, c16);
+    gram<E, D>(sm, false, w, j, c16);
     if (tid < C) sm.fc[tid] = sm.beta[tid] * fexp2(sm.gl[C - 1] - sm.gl[tid]);
     lds_barrier();
     if (w < 4) invert_block<false>(sm.Am, sm.Yl, w, l);
@@ -496,7 +520,7 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
     row_scalars<D>(sm, p, n, tid);
     lds_barrier();
     if (sl == 0 && tid < C) buf_st4(r_kk, (uint32_t)(tid * p.H * 4), sm.kk[tid]);
-    gram<D>(sm, true, w, j, c16);
+    gram<E, D>(sm, true, w, j, c16);
     if (w < 4) residual_tile<D>(sm, w, j, c16);
     lds_barrier();
     if (w < 4) invert_block<false>(sm.Am, sm.Yl, w, l);
