@@ -392,6 +392,62 @@ __device__ inline void tri_solve_y(float *X, const float *Am, const float *Y, in
   }
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ inline f32x16 mma32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// The column slice's contributions to dk and dq for rows 32 T .. 32 T + 31 and
+// columns 32 I .. 32 I + 31 (v_mfma_f32_32x32x2_f32: lane l supplies row or
+// column l % 32 at k = l / 32; result r of lane l is row 8 (r/4) + 4 (l/32)
+// + r % 4, column l % 32):
+//   dk = B (Diag(gamma_n/gamma) E Gend^T - Diag(gamma) U S^T + Z^T Q - W B K)
+//   dq = Diag(gamma) dO S^T + Z B K
+// The row scalings ride on the A operands, so each output has one
+// accumulator, and the B K column reads serve both.
+template <int D>
+__device__ __attribute__((always_inline)) inline void dq_dk_tile(
+    BwdSmem<D> &sm, int T, int I, int l, float glast, rsrc_t r_dq, rsrc_t r_dk, int64_t HD) {
+  constexpr int LDK = BwdSmem<D>::LDK;
+  const int r32 = l & 31, kh = l >> 5;
+  const int ta = 32 * T + r32;  // this lane's A row
+  const int ib = 32 * I + r32;  // this lane's B column
+  const float fe = fexp2(glast - sm.gl[ta]), fg = sm.gm[ta];
+  f32x16 ak = {}, aq = {};
+#pragma unroll 2
+  for (int st = 0; st < DVS / 2; ++st) {
+    const int c = 2 * st + kh;
+    const float sc = sm.Sc[ib * LDSL + c];
+    ak = mma32(fe * sm.Es[ta * LDSL + c], sm.Gd[ib * LDSL + c], ak);
+    ak = mma32(-fg * sm.Us[ta * LDSL + c], sc, ak);
+    aq = mma32(fg * sm.Ds[ta * LDSL + c], sc, aq);
+  }
+  // Z^T Q over r >= 32 T (Z[r][t] = 0 for r < t)
+  for (int g = T; g < 2; ++g) {
+#pragma unroll 2
+    for (int st = 16 * g; st < 16 * g + 16; ++st) {
+      const int r = 2 * st + kh;
+      ak = mma32(sm.Xm[r * LDN + ta], sm.Q[r * LDK + ib], ak);
+    }
+  }
+  // - W B K over all s; Z B K over s < 32 (T + 1)
+  for (int g = 0; g < 2; ++g) {
+#pragma unroll 2
+    for (int st = 16 * g; st < 16 * g + 16; ++st) {
+      const int s2 = 2 * st + kh;
+      const float kb = sm.beta[s2] * sm.K[s2 * LDK + ib];
+      ak = mma32(-sm.Am[ta * LDN + s2], kb, ak);
+      if (g <= T) aq = mma32(sm.Xm[ta * LDN + s2], kb, aq);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int t = 32 * T + 8 * (r >> 2) + 4 * kh + (r & 3);
+    buf_st4(r_dk, (uint32_t)((t * HD + ib) * 4), sm.beta[t] * ak[r]);
+    buf_st4(r_dq, (uint32_t)((t * HD + ib) * 4), aq[r]);
+  }
+}
+
 template <int D>
 __device__ inline float block_sum(BwdSmem<D> &sm, float x, int w, int l) {
   x = group_sum<32>(x);
@@ -615,47 +671,9 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
       }
     }
     lds_barrier();
-    // dq and dk contributions of these columns: 2 x (4 x D/16) tiles
-    for (int jb = w; jb < 8 * (D / 16); jb += BW) {
-      const bool isq = jb >= 4 * (D / 16);
-      const int tt = isq ? jb - 4 * (D / 16) : jb;
-      const int bt = tt & 3, bi = tt >> 2;
-      f32x4 out;
-      if (isq) {
-        f32x4 a1 = tile_mm<DVS / 4>(zero4(), 0, j, [&](int kx) { return sm.Ds[(16 * bt + c16) * LDSL + kx]; },
-                                    [&](int kx) { return sm.Sc[(16 * bi + c16) * LDSL + kx]; });
-        f32x4 a2 = zero4();
-        for (int st = 0; st < 4 * (bt + 1); ++st) {
-          const int kx = 4 * st + j;
-          a2 = mma(sm.Xm[(16 * bt + c16) * LDN + kx], sm.beta[kx] * sm.K[kx * LDK + 16 * bi + c16], a2);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = sm.gm[16 * bt + 4 * j + i] * a1[i] + a2[i];
-      } else {
-        f32x4 a1 = tile_mm<DVS / 4>(zero4(), 0, j, [&](int kx) { return sm.Es[(16 * bt + c16) * LDSL + kx]; },
-                                    [&](int kx) { return sm.Gd[(16 * bi + c16) * LDSL + kx]; });
-        f32x4 a2 = tile_mm<DVS / 4>(zero4(), 0, j, [&](int kx) { return sm.Us[(16 * bt + c16) * LDSL + kx]; },
-                                    [&](int kx) { return sm.Sc[(16 * bi + c16) * LDSL + kx]; });
-        f32x4 a3 = zero4();
-        for (int st = 4 * bt; st < 16; ++st) {
-          const int kx = 4 * st + j;
-          a3 = mma(sm.Xm[kx * LDN + 16 * bt + c16], sm.Q[kx * LDK + 16 * bi + c16], a3);
-        }
-        a3 = tile_mm<C / 4>(a3, 0, j, [&](int kx) { return -sm.Am[(16 * bt + c16) * LDN + kx]; },
-                            [&](int kx) { return sm.beta[kx] * sm.K[kx * LDK + 16 * bi + c16]; });
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * bt + 4 * j + i;
-          out[i] = sm.beta[t] * (fexp2(glast - sm.gl[t]) * a1[i] - sm.gm[t] * a2[i] + a3[i]);
-        }
-      }
-      const rsrc_t rd = isq ? r_dq : r_dk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * bt + 4 * j + i;
-        buf_st4(rd, (uint32_t)((t * HD + 16 * bi + c16) * 4), out[i]);
-      }
-    }
+    // dq and dk contributions of these columns, as 32 x 32 tiles: wave w takes
+    // row block w & 1 and column block w >> 1 of both (D = 64: waves 0-3)
+    if (w < D / 16) dq_dk_tile<D>(sm, w & 1, w >> 1, l, glast, r_dq, r_dk, HD);
     // Gend <- gamma_n Gend + Q^T Diag(gamma) dO - K^T Diag(gamma beta) U
     constexpr int NT = (D / 16 + BW - 1) / BW;  // state tiles per wave
     f32x4 gnew[NT];
