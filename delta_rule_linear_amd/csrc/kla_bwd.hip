@@ -576,8 +576,8 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
     row_scalars<D>(sm, p, n, tid);
     lds_barrier();
     if (sl == 0 && tid < C) buf_st4(r_kk, (uint32_t)(tid * p.H * 4), sm.kk[tid]);
-    gram<E, D>(sm, true, w, j, c16);
-    if (w < 4) residual_tile<D>(sm, w, j, c16);
+    gram<E, D>(sm, true, w, j, c16);  // waves 0-3 take three Gram jobs, 4-7 two
+    if (w >= 4) residual_tile<D>(sm, w - 4, j, c16);
     lds_barrier();
     if (w < 4) invert_block<false>(sm.Am, sm.Yl, w, l);
     else invert_block<true>(sm.Am, sm.Yu, w - 4, l);
