@@ -128,3 +128,37 @@ def test_bwd_deterministic(kla):
     torch.cuda.synchronize()
     for key in KEYS:
         assert torch.equal(a[key], b[key]), key
+
+
+def test_bwd_long_workload_sampled_heads(kla):
+    say("bwd long workload B=2 H=16 T=32768 d=128 bf16 (oracle on sequence 1, heads 3 and 12)")
+    inp = workloads.prefill("long")
+    g = workloads.grad_inputs(7, inp["q"].shape[0], inp["H"], inp["d"], inp["n_seqs"])
+    dev = "cuda"
+    cu = cu_of(inp)
+    out = kla.kla_bwd_chunked(inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev),
+                              inp["alpha"].to(dev), inp["eta"].to(dev), g["d_o"].to(dev),
+                              cu_seqlens=torch.from_numpy(cu.astype(np.int32)).to(dev),
+                              d_final=g["d_final"].to(dev), eps=inp["eps"])
+    torch.cuda.synchronize()
+    heads = [3, 12]
+    ti = torch.arange(int(cu[1]), int(cu[2]))
+    sub = {n: inp[n][ti][:, heads].contiguous() for n in ("q", "k", "v", "alpha", "eta")}
+    ref = oracle.bwd(sub["q"], sub["k"], sub["v"], sub["alpha"], sub["eta"],
+                     g["d_o"][ti][:, heads].contiguous(), cu_seqlens=np.array([0, len(ti)]),
+                     eps=float(np.float32(inp["eps"])), d_final=g["d_final"][1:2, heads])
+    for key in KEYS:
+        got = out[key].cpu()
+        got = got[1:2, heads] if key == "dS0" else got[ti][:, heads]
+        check(f"bwd long {key}", got, ref[key], TOL["bf16"])
+
+
+def test_bwd_packed_workload_sampled(kla):
+    say("bwd packed workload 64 seqs lengths U[128,8192] H=16 d=128 bf16 (oracle on 4 sequences)")
+    inp = workloads.prefill("packed")
+    g = workloads.grad_inputs(8, inp["q"].shape[0], inp["H"], inp["d"], inp["n_seqs"])
+    lens = np.array(inp["lengths"])
+    rng = np.random.default_rng(321)
+    seqs = sorted(set([int(lens.argmax()), int(lens.argmin())]
+                      + [int(x) for x in rng.choice(len(lens), 2, replace=False)]))
+    run_case(kla, "bwd packed", inp, g, with_s0=False, seqs=seqs)
