@@ -28,8 +28,10 @@
 // started at <Gend, S_end> at each chunk's end.
 //
 // Every quantity is linear in the state's columns (dv), so one workgroup of
-// 8 waves (two per SIMD) takes one (sequence, head, 16 columns of dv): the fp32 slices of
-// S and Gend, K and Q of a chunk and the 64 x 64 planes fit in LDS.  A first
+// 8 waves (two per SIMD) takes one (sequence, head, DV columns of dv): the
+// fp32 slices of S and Gend, K and Q of a chunk and the 64 x 64 planes fit
+// in LDS.  With bf16 inputs K and Q stay bf16 in LDS and DV = 32; with fp32
+// inputs DV = 16.  A first
 // sweep runs the chunks forward and stores each chunk-start state slice in
 // the workspace; the reverse sweep then takes the chunks from last to first.
 // Products are fp32 MFMA (v_mfma_f32_16x16x4_f32); the two triangular solves
@@ -46,25 +48,32 @@
 namespace kla {
 namespace {
 
-constexpr int DVS = 16;         // state columns per workgroup
 constexpr int BW = 8;           // waves per workgroup (two per SIMD)
 constexpr int BT = 64 * BW;     // threads per workgroup
-constexpr int LDSL = DVS + 4;   // row pitch of the column-slice tiles
 constexpr int LDN = C + 4;      // row pitch of the 64 x 64 planes
 constexpr int LDY = 20;         // row pitch of the 16 x 16 diagonal-block inverses
 
-template <int D>
+// State columns per workgroup and the LDS layout, per input type: bf16 K and
+// Q are kept as bf16 (exact), which leaves room for 32 columns.
+template <typename E, int D>
+struct BwdCfg {
+  static constexpr int DV = sizeof(E) == 2 ? 32 : 16;  // state columns per workgroup
+  static constexpr int NCB = DV / 16;                  // 16-column blocks
+  static constexpr int LDSL = DV + 4;                  // row pitch of the column-slice planes
+  static constexpr int LDK = D + 16 / (int)sizeof(E);  // row pitch of K, Q (16-byte rows)
+};
+
+template <typename E, int D>
 struct BwdSmem {
-  static constexpr int LDK = D + 4;
-  alignas(16) float K[C * LDK];
-  alignas(16) float Q[C * LDK];
-  alignas(16) float Sc[D * LDSL];  // chunk-start state, this workgroup's columns
-  alignas(16) float Gd[D * LDSL];  // gradient of the state after the chunk
-  alignas(16) float Vs[C * LDSL];
-  alignas(16) float Ds[C * LDSL];  // dO
-  alignas(16) float Es[C * LDSL];  // residuals e_t
-  alignas(16) float Us[C * LDSL];  // u_t
-  alignas(16) float Os[C * LDSL];  // outputs o_t
+  using CF = BwdCfg<E, D>;
+  alignas(16) E K[C * CF::LDK];
+  alignas(16) E Q[C * CF::LDK];
+  alignas(16) float Sc[D * CF::LDSL];  // chunk-start state, this workgroup's columns
+  alignas(16) float Gd[D * CF::LDSL];  // gradient of the state after the chunk
+  alignas(16) float Vs[C * CF::LDSL];
+  alignas(16) float Ds[C * CF::LDSL];  // dO
+  alignas(16) float Es[C * CF::LDSL];  // residuals e_t
+  alignas(16) float Us[C * CF::LDSL];  // u_t
   alignas(16) float Am[C * LDN];   // lower: Gam o KK^T B; upper: its reverse twin; later W
   alignas(16) float Xm[C * LDN];   // Mq, later Z (lower, diagonal included)
   alignas(16) float Yl[4 * 16 * LDY];  // (I + L_bb)^-1, unit lower, per diagonal block
@@ -77,8 +86,12 @@ struct BwdSmem {
   float scan[C];
   float la[C];    // log2 alpha of the chunk's rows (0 for padding or no decay)
   float eta[C];
+  float tpart[CF::NCB][C];  // per 16-column block: sum_c dO[t][c] o[t][c]
   float red[BW];
 };
+
+__device__ inline float kf(float x) { return x; }
+__device__ inline float kf(__bf16 x) { return static_cast<float>(x); }
 
 struct Tok {
   int64_t bos;
@@ -91,11 +104,6 @@ __device__ inline Tok seq_of(const BwdParams &p, int64_t s) {
   const int64_t eos = p.cu_seqlens ? (int64_t)p.cu_seqlens[s + 1] : t.bos + p.seq_len_dense;
   t.L = (int)(eos - t.bos);
   return t;
-}
-
-template <typename E>
-__device__ inline float ld(const E *p, int64_t i) {
-  return static_cast<float>(p[i]);
 }
 
 // 16x16 output tile, acc[i] = sum_k A(16 rows)[4j+i][k] B[k][c16] over
@@ -123,14 +131,16 @@ __device__ inline void lower_tile(int p, int &bt, int &bs) {
 // end read zero, so a ragged tail needs no branch.
 template <typename E, int D>
 struct Fetch {
+  static constexpr int DV = BwdCfg<E, D>::DV;
   static constexpr int SEG_EL = 16 / sizeof(E);     // elements per segment
   static constexpr int SEG_ROW = D / SEG_EL;        // segments per K / Q row
   static constexpr int NKQ = C * SEG_ROW / BT;
-  static constexpr int VSEG = DVS / SEG_EL;         // segments per V row slice
-  static constexpr int NSSEG = D * (DVS / 4);       // state-slice segments
+  static constexpr int VSEG = DV / SEG_EL;          // segments per V row slice
+  static constexpr int DSEG = DV / 4;               // segments per fp32 row slice
+  static constexpr int NSSEG = D * DSEG;            // state-slice segments
   static constexpr int NSS = (NSSEG + BT - 1) / BT;
   static_assert(NKQ * BT == C * SEG_ROW, "tiling");
-  static_assert(C * VSEG <= BT && C * (DVS / 4) <= BT, "slice tiling");
+  static_assert(C * VSEG <= BT && C * DSEG <= BT, "slice tiling");
   uint4 k[NKQ], q[NKQ];
   uint4 v, d;
   uint4 s[NSS];
@@ -158,16 +168,17 @@ __device__ inline void fetch(Fetch<E, D> &f, const BwdParams &p, int64_t t0, int
       const int sg = tid + BT * m, r = sg / F::SEG_ROW, cs = sg % F::SEG_ROW;
       f.q[m] = buf_ld16(rq, (uint32_t)(r * HD * esz + cs * 16));
     }
-    const rsrc_t rd = make_rsrc(p.d_o + base + col0, n > 0 ? ((int64_t)(n - 1) * HD + DVS) * 4 : 0);
-    if (tid < C * (DVS / 4)) f.d = buf_ld16(rd, (uint32_t)((tid / 4) * HD * 4 + (tid % 4) * 16));
+    const rsrc_t rd = make_rsrc(p.d_o + base + col0, n > 0 ? ((int64_t)(n - 1) * HD + F::DV) * 4 : 0);
+    if (tid < C * F::DSEG)
+      f.d = buf_ld16(rd, (uint32_t)((tid / F::DSEG) * HD * 4 + (tid % F::DSEG) * 16));
 #pragma unroll
     for (int m = 0; m < F::NSS; ++m) {
-      const int sg = tid + BT * m, r = sg / 4, cs = sg % 4;
+      const int sg = tid + BT * m, r = sg / F::DSEG, cs = sg % F::DSEG;
       if (sg < F::NSSEG) f.s[m] = *reinterpret_cast<const uint4 *>(ckslot + (int64_t)r * D + col0 + 4 * cs);
     }
   }
   const rsrc_t rv = make_rsrc(static_cast<const E *>(p.v) + base + col0,
-                              n > 0 ? ((int64_t)(n - 1) * HD + DVS) * esz : 0);
+                              n > 0 ? ((int64_t)(n - 1) * HD + F::DV) * esz : 0);
   if (tid < C * F::VSEG)
     f.v = buf_ld16(rv, (uint32_t)((tid / F::VSEG) * HD * esz + (tid % F::VSEG) * 16));
   if (tid < C) {
@@ -193,11 +204,13 @@ __device__ inline void st4(float *dst, const float *x) {
   *reinterpret_cast<f32x4 *>(dst) = f32x4{x[0], x[1], x[2], x[3]};
 }
 
-// Registers -> LDS (fp32), with the row norms |k|^2 and the raw gates.
+// Registers -> LDS (K, Q in the input type, the rest fp32), with the row
+// norms |k|^2 and the raw gates.
 template <typename E, int D>
-__device__ inline void commit(BwdSmem<D> &sm, const Fetch<E, D> &f, int n, bool rev, int tid) {
+__device__ inline void commit(BwdSmem<E, D> &sm, const Fetch<E, D> &f, int n, bool rev, int tid) {
   using F = Fetch<E, D>;
-  constexpr int LDK = BwdSmem<D>::LDK;
+  using CF = BwdCfg<E, D>;
+  constexpr int LDK = CF::LDK, LDSL = CF::LDSL;
 #pragma unroll
   for (int m = 0; m < F::NKQ; ++m) {
     const int sg = tid + BT * m, r = sg / F::SEG_ROW, cs = sg % F::SEG_ROW;
@@ -206,15 +219,10 @@ __device__ inline void commit(BwdSmem<D> &sm, const Fetch<E, D> &f, int n, bool 
     float kk = 0.f;
 #pragma unroll
     for (int e = 0; e < F::SEG_EL; ++e) kk = fmaf(x[e], x[e], kk);
-#pragma unroll
-    for (int e = 0; e < F::SEG_EL; e += 4) st4(&sm.K[r * LDK + cs * F::SEG_EL + e], x + e);
+    *reinterpret_cast<uint4 *>(&sm.K[r * LDK + cs * F::SEG_EL]) = f.k[m];
     kk = group_sum<F::SEG_ROW>(kk);  // the SEG_ROW lanes of row r hold its segments
     if (cs == 0) sm.kk[r] = kk;
-    if (rev) {
-      cvt(f.q[m], E{}, x);
-#pragma unroll
-      for (int e = 0; e < F::SEG_EL; e += 4) st4(&sm.Q[r * LDK + cs * F::SEG_EL + e], x + e);
-    }
+    if (rev) *reinterpret_cast<uint4 *>(&sm.Q[r * LDK + cs * F::SEG_EL]) = f.q[m];
   }
   if (tid < C * F::VSEG) {
     float x[F::SEG_EL];
@@ -225,16 +233,16 @@ __device__ inline void commit(BwdSmem<D> &sm, const Fetch<E, D> &f, int n, bool 
   }
   if (rev) {
     float x[4];
-    if (tid < C * (DVS / 4)) {
+    if (tid < C * F::DSEG) {
       cvt(f.d, float{}, x);
-      st4(&sm.Ds[(tid / 4) * LDSL + (tid % 4) * 4], x);
+      st4(&sm.Ds[(tid / F::DSEG) * LDSL + (tid % F::DSEG) * 4], x);
     }
 #pragma unroll
     for (int m = 0; m < F::NSS; ++m) {
       const int sg = tid + BT * m;
       if (sg < F::NSSEG) {
         cvt(f.s[m], float{}, x);
-        st4(&sm.Sc[(sg / 4) * LDSL + (sg % 4) * 4], x);
+        st4(&sm.Sc[(sg / F::DSEG) * LDSL + (sg % F::DSEG) * 4], x);
       }
     }
   }
@@ -244,10 +252,9 @@ __device__ inline void commit(BwdSmem<D> &sm, const Fetch<E, D> &f, int n, bool 
   }
 }
 
-// Row scalars from LDS: |k|^2, beta, the cumulative log2 decay and 2^gl
-// (wave 0).
-template <int D>
-__device__ inline void row_scalars(BwdSmem<D> &sm, const BwdParams &p, int n, int tid) {
+// Row scalars from LDS: beta, the cumulative log2 decay and 2^gl (wave 0).
+template <typename E, int D>
+__device__ inline void row_scalars(BwdSmem<E, D> &sm, const BwdParams &p, int n, int tid) {
   if (tid < C) {
     const int r = tid;
     const float kk = sm.kk[r];
@@ -261,39 +268,25 @@ __device__ inline void row_scalars(BwdSmem<D> &sm, const BwdParams &p, int n, in
 }
 
 // Am <- Gam o K K^T B below the diagonal and its reverse twin
-// (Gam^T o K K^T B) above it; with_q: Xm <- Lower(Gam o Q K^T).
-// 8 fp32 values that hold bf16 numbers -> bf16x8 (exact).
-__device__ inline bf16x8 to_bf8(const float *p) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[e] = static_cast<bf16>(a[e]);
-    r[4 + e] = static_cast<bf16>(b[e]);
-  }
-  return r;
-}
-
-// Am <- Gam o K K^T B below the diagonal and its reverse twin
-// (Gam^T o K K^T B) above it; with_q: Xm <- Lower(Gam o Q K^T).  With bf16
-// inputs K and Q hold bf16 values, so the Gram tiles use the bf16 MFMA
-// (exact products, fp32 accumulation); fp32 inputs use the fp32 MFMA.
+// (Gam^T o K K^T B) above it; with_q: Xm <- Lower(Gam o Q K^T).  bf16 K and
+// Q go to the bf16 MFMA (exact products, fp32 accumulation); fp32 inputs use
+// the fp32 MFMA.
 template <typename E, int D>
-__device__ inline void gram(BwdSmem<D> &sm, bool with_q, int w, int j, int c16) {
-  constexpr int LDK = BwdSmem<D>::LDK;
+__device__ inline void gram(BwdSmem<E, D> &sm, bool with_q, int w, int j, int c16) {
+  constexpr int LDK = BwdCfg<E, D>::LDK;
   const int jobs = with_q ? 20 : 10;
   for (int jb = w; jb < jobs; jb += BW) {
     const bool qk = jb >= 10;
     int bt, bs;
     lower_tile(qk ? jb - 10 : jb, bt, bs);
-    const float *X = qk ? sm.Q : sm.K;
+    const E *X = qk ? sm.Q : sm.K;
     f32x4 acc = zero4();
     if constexpr (sizeof(E) == 2) {
 #pragma unroll
       for (int kb = 0; kb < D / 32; ++kb)
-        acc = mma(to_bf8(&X[(16 * bt + c16) * LDK + 32 * kb + 8 * j]),
-                  to_bf8(&sm.K[(16 * bs + c16) * LDK + 32 * kb + 8 * j]), acc);
+        acc = mma(*reinterpret_cast<const bf16x8 *>(&X[(16 * bt + c16) * LDK + 32 * kb + 8 * j]),
+                  *reinterpret_cast<const bf16x8 *>(&sm.K[(16 * bs + c16) * LDK + 32 * kb + 8 * j]),
+                  acc);
     } else {
       acc = tile_mm<D / 4>(acc, 0, j, [&](int kx) { return X[(16 * bt + c16) * LDK + kx]; },
                            [&](int kx) { return sm.K[(16 * bs + c16) * LDK + kx]; });
@@ -316,16 +309,19 @@ __device__ inline void gram(BwdSmem<D> &sm, bool with_q, int w, int j, int c16) 
   }
 }
 
-// Es <- V - Diag(gamma) K S for output tile bt (16 rows, the 16 columns).
-template <int D>
-__device__ inline void residual_tile(BwdSmem<D> &sm, int bt, int j, int c16) {
-  constexpr int LDK = BwdSmem<D>::LDK;
-  f32x4 acc = tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return sm.K[(16 * bt + c16) * LDK + kx]; },
-                             [&](int kx) { return sm.Sc[kx * LDSL + c16]; });
+// Es <- V - Diag(gamma) K S for tile `tile` (rows 16 (tile % 4), columns
+// 16 (tile / 4) of the slice).
+template <typename E, int D>
+__device__ inline void residual_tile(BwdSmem<E, D> &sm, int tile, int j, int c16) {
+  using CF = BwdCfg<E, D>;
+  constexpr int LDK = CF::LDK, LDSL = CF::LDSL;
+  const int bt = tile & 3, cc = 16 * (tile >> 2) + c16;
+  f32x4 acc = tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return kf(sm.K[(16 * bt + c16) * LDK + kx]); },
+                             [&](int kx) { return sm.Sc[kx * LDSL + cc]; });
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = 16 * bt + 4 * j + i;
-    sm.Es[t * LDSL + c16] = sm.Vs[t * LDSL + c16] - sm.gm[t] * acc[i];
+    sm.Es[t * LDSL + cc] = sm.Vs[t * LDSL + cc] - sm.gm[t] * acc[i];
   }
 }
 
@@ -355,12 +351,14 @@ __device__ inline void invert_block(const float *Am, float *Y, int b, int l) {
   }
 }
 
-// Block substitution on X (64 x 16, in place) with the unit triangle of Am,
-// the diagonal blocks applied through their inverses Y: for each block b
-// (forward for the lower triangle, backward for the upper one)
-//   X_b <- Y_b (X_b - sum_c Am_bc X_c).  One wave; MFMA only.
-template <bool UPPER>
-__device__ inline void tri_solve_y(float *X, const float *Am, const float *Y, int j, int c16) {
+// Block substitution on 16 columns (from c0) of X (64 rows, pitch LDSL, in
+// place) with the unit triangle of Am, the diagonal blocks applied through
+// their inverses Y: for each block b (forward for the lower triangle,
+// backward for the upper one)  X_b <- Y_b (X_b - sum_c Am_bc X_c).  One
+// wave; MFMA only.
+template <bool UPPER, int LDSL>
+__device__ inline void tri_solve_y(float *X, const float *Am, const float *Y, int c0, int j, int c16) {
+  const int cc = c0 + c16;
 #pragma unroll
   for (int bb = 0; bb < 4; ++bb) {
     const int b = UPPER ? 3 - bb : bb;
@@ -368,26 +366,26 @@ __device__ inline void tri_solve_y(float *X, const float *Am, const float *Y, in
     const int steps = UPPER ? 4 * (3 - b) : 4 * b;
     f32x4 r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = X[(16 * b + 4 * j + i) * LDSL + c16];
+    for (int i = 0; i < 4; ++i) r[i] = X[(16 * b + 4 * j + i) * LDSL + cc];
     if (steps > 0) {
       f32x4 acc = zero4();
 #pragma unroll 4
       for (int st = 0; st < steps; ++st) {
         const int kx = k0 + 4 * st + j;
-        acc = mma(Am[(16 * b + c16) * LDN + kx], X[kx * LDSL + c16], acc);
+        acc = mma(Am[(16 * b + c16) * LDN + kx], X[kx * LDSL + cc], acc);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) X[(16 * b + 4 * j + i) * LDSL + c16] = r[i] - acc[i];
+      for (int i = 0; i < 4; ++i) X[(16 * b + 4 * j + i) * LDSL + cc] = r[i] - acc[i];
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block's rows are in LDS
     }
     f32x4 x = zero4();
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int kx = 4 * st + j;
-      x = mma(Y[b * 16 * LDY + c16 * LDY + kx], X[(16 * b + kx) * LDSL + c16], x);
+      x = mma(Y[b * 16 * LDY + c16 * LDY + kx], X[(16 * b + kx) * LDSL + cc], x);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) X[(16 * b + 4 * j + i) * LDSL + c16] = x[i];
+    for (int i = 0; i < 4; ++i) X[(16 * b + 4 * j + i) * LDSL + cc] = x[i];
     __builtin_amdgcn_s_waitcnt(0xc07f);
   }
 }
@@ -405,17 +403,18 @@ __device__ inline f32x16 mma32(float a, float b, f32x16 c) {
 //   dq = Diag(gamma) dO S^T + Z B K
 // The row scalings ride on the A operands, so each output has one
 // accumulator, and the B K column reads serve both.
-template <int D>
+template <typename E, int D>
 __device__ __attribute__((always_inline)) inline void dq_dk_tile(
-    BwdSmem<D> &sm, int T, int I, int l, float glast, rsrc_t r_dq, rsrc_t r_dk, int64_t HD) {
-  constexpr int LDK = BwdSmem<D>::LDK;
+    BwdSmem<E, D> &sm, int T, int I, int l, float glast, rsrc_t r_dq, rsrc_t r_dk, int64_t HD) {
+  using CF = BwdCfg<E, D>;
+  constexpr int LDK = CF::LDK, LDSL = CF::LDSL;
   const int r32 = l & 31, kh = l >> 5;
   const int ta = 32 * T + r32;  // this lane's A row
   const int ib = 32 * I + r32;  // this lane's B column
   const float fe = fexp2(glast - sm.gl[ta]), fg = sm.gm[ta];
   f32x16 ak = {}, aq = {};
 #pragma unroll 2
-  for (int st = 0; st < DVS / 2; ++st) {
+  for (int st = 0; st < CF::DV / 2; ++st) {
     const int c = 2 * st + kh;
     const float sc = sm.Sc[ib * LDSL + c];
     ak = mma32(fe * sm.Es[ta * LDSL + c], sm.Gd[ib * LDSL + c], ak);
@@ -427,7 +426,7 @@ __device__ __attribute__((always_inline)) inline void dq_dk_tile(
 #pragma unroll 2
     for (int st = 16 * g; st < 16 * g + 16; ++st) {
       const int r = 2 * st + kh;
-      ak = mma32(sm.Xm[r * LDN + ta], sm.Q[r * LDK + ib], ak);
+      ak = mma32(sm.Xm[r * LDN + ta], kf(sm.Q[r * LDK + ib]), ak);
     }
   }
   // - W B K over all s; Z B K over s < 32 (T + 1)
@@ -435,7 +434,7 @@ __device__ __attribute__((always_inline)) inline void dq_dk_tile(
 #pragma unroll 2
     for (int st = 16 * g; st < 16 * g + 16; ++st) {
       const int s2 = 2 * st + kh;
-      const float kb = sm.beta[s2] * sm.K[s2 * LDK + ib];
+      const float kb = sm.beta[s2] * kf(sm.K[s2 * LDK + ib]);
       ak = mma32(-sm.Am[ta * LDN + s2], kb, ak);
       if (g <= T) aq = mma32(sm.Xm[ta * LDN + s2], kb, aq);
     }
@@ -448,8 +447,8 @@ __device__ __attribute__((always_inline)) inline void dq_dk_tile(
   }
 }
 
-template <int D>
-__device__ inline float block_sum(BwdSmem<D> &sm, float x, int w, int l) {
+template <typename E, int D>
+__device__ inline float block_sum(BwdSmem<E, D> &sm, float x, int w, int l) {
   x = group_sum<32>(x);
   x += __shfl_xor(x, 32, 64);
   lds_barrier();
@@ -463,10 +462,12 @@ __device__ inline float block_sum(BwdSmem<D> &sm, float x, int w, int l) {
 
 template <typename E, int D>
 __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
-  constexpr int LDK = BwdSmem<D>::LDK;
-  constexpr int NS = D / DVS;
+  using CF = BwdCfg<E, D>;
+  constexpr int LDK = CF::LDK, LDSL = CF::LDSL, DV = CF::DV, NCB = CF::NCB;
+  constexpr int NS = D / DV;
   constexpr int DD = D * D;
-  __shared__ BwdSmem<D> sm;
+  constexpr int NST = (D / 16) * NCB;  // 16x16 tiles of the state slice
+  __shared__ BwdSmem<E, D> sm;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -478,7 +479,7 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
   const int64_t sh = lb / NS;
   const int h = (int)(sh % p.H);
   const int64_t s = sh / p.H;
-  const int col0 = sl * DVS;
+  const int col0 = sl * DV;
   const Tok sq = seq_of(p, s);
   const int nch = (sq.L + C - 1) / C;
   // checkpoint slots of this sequence: floor(bos / C) + s onwards (disjoint)
@@ -489,8 +490,8 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
   F f;
 
   // ---- forward sweep: chunk-start states -------------------------------
-  for (int idx = tid; idx < D * DVS; idx += BT) {
-    const int i = idx / DVS, c = idx % DVS;
+  for (int idx = tid; idx < D * DV; idx += BT) {
+    const int i = idx / DV, c = idx % DV;
     sm.Sc[i * LDSL + c] = p.initial_state ? p.initial_state[sh * DD + i * D + col0 + c] : 0.f;
   }
   if (nch > 0) fetch<E, D>(f, p, sq.bos, min(C, sq.L), h, col0, ck, false, tid);
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
     commit<E, D>(sm, f, n, false, tid);
 #pragma unroll
     for (int m = 0; m < F::NSS; ++m) {
-      const int sg = tid + BT * m, r = sg / 4, cs = sg % 4;
+      const int sg = tid + BT * m, r = sg / F::DSEG, cs = sg % F::DSEG;
       if (sg < F::NSSEG)
         *reinterpret_cast<f32x4 *>(ck + ci * slot + (int64_t)r * D + col0 + 4 * cs) =
             *reinterpret_cast<const f32x4 *>(&sm.Sc[r * LDSL + 4 * cs]);
@@ -509,34 +510,36 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
       fetch<E, D>(f, p, sq.bos + (int64_t)(ci + 1) * C, min(C, sq.L - (ci + 1) * C), h, col0, ck,
                   false, tid);
     lds_barrier();
-    row_scalars<D>(sm, p, n, tid);
+    row_scalars<E, D>(sm, p, n, tid);
     lds_barrier();
     gram<E, D>(sm, false, w, j, c16);
     if (tid < C) sm.fc[tid] = sm.beta[tid] * fexp2(sm.gl[C - 1] - sm.gl[tid]);
     lds_barrier();
     if (w < 4) invert_block<false>(sm.Am, sm.Yl, w, l);
-    else residual_tile<D>(sm, w - 4, j, c16);
+    else
+      for (int tile = w - 4; tile < 4 * NCB; tile += 4) residual_tile<E, D>(sm, tile, j, c16);
     lds_barrier();
-    if (w == 0) tri_solve_y<false>(sm.Es, sm.Am, sm.Yl, j, c16);
+    if (w < NCB) tri_solve_y<false, LDSL>(sm.Es, sm.Am, sm.Yl, 16 * w, j, c16);
     lds_barrier();
     // S <- gamma_n S + K^T Diag(beta gamma_n / gamma) E
     const float gn = sm.gm[C - 1];
-    for (int ti = w; ti < D / 16; ti += BW) {
+    for (int tt = w; tt < NST; tt += BW) {
+      const int ti = tt % (D / 16), cc = 16 * (tt / (D / 16)) + c16;
       f32x4 acc;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = gn * sm.Sc[(16 * ti + 4 * j + i) * LDSL + c16];
-      acc = tile_mm<C / 4>(acc, 0, j, [&](int kx) { return sm.K[kx * LDK + 16 * ti + c16]; },
-                           [&](int kx) { return sm.fc[kx] * sm.Es[kx * LDSL + c16]; });
+      for (int i = 0; i < 4; ++i) acc[i] = gn * sm.Sc[(16 * ti + 4 * j + i) * LDSL + cc];
+      acc = tile_mm<C / 4>(acc, 0, j, [&](int kx) { return kf(sm.K[kx * LDK + 16 * ti + c16]); },
+                           [&](int kx) { return sm.fc[kx] * sm.Es[kx * LDSL + cc]; });
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.Sc[(16 * ti + 4 * j + i) * LDSL + c16] = acc[i];
+      for (int i = 0; i < 4; ++i) sm.Sc[(16 * ti + 4 * j + i) * LDSL + cc] = acc[i];
     }
   }
   // the checkpoints are read back below by the threads that wrote them
   __syncthreads();
 
   // ---- reverse sweep ----------------------------------------------------
-  for (int idx = tid; idx < D * DVS; idx += BT) {
-    const int i = idx / DVS, c = idx % DVS;
+  for (int idx = tid; idx < D * DV; idx += BT) {
+    const int i = idx / DV, c = idx % DV;
     sm.Gd[i * LDSL + c] = p.d_final ? p.d_final[sh * DD + i * D + col0 + c] : 0.f;
   }
   if (nch > 0)
@@ -546,11 +549,11 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
   float cend;
   {
     float x = 0.f;
-    for (int idx = tid; idx < D * DVS; idx += BT) {
-      const int i = idx / DVS, c = idx % DVS;
+    for (int idx = tid; idx < D * DV; idx += BT) {
+      const int i = idx / DV, c = idx % DV;
       x = fmaf(sm.Gd[i * LDSL + c], sm.Sc[i * LDSL + c], x);
     }
-    cend = block_sum<D>(sm, x, w, l);
+    cend = block_sum<E, D>(sm, x, w, l);
   }
   float *dqp = p.ws_dq + (int64_t)sl * TH * D;
   float *dkp = p.ws_dk + (int64_t)sl * TH * D;
@@ -569,56 +572,60 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
     const rsrc_t r_kk = make_rsrc(p.ws_kk + t0 * p.H + h, (nrow * p.H + 1) * 4);
     const rsrc_t r_db = make_rsrc(dbp + t0 * p.H + h, (nrow * p.H + 1) * 4);
     const rsrc_t r_c = make_rsrc(cp + t0 * p.H + h, (nrow * p.H + 1) * 4);
-    const rsrc_t r_dv = make_rsrc(p.dv + t0 * HD + (int64_t)h * D + col0, (nrow * HD + DVS) * 4);
+    const rsrc_t r_dv = make_rsrc(p.dv + t0 * HD + (int64_t)h * D + col0, (nrow * HD + DV) * 4);
     const rsrc_t r_dq = make_rsrc(dqp + t0 * HD + (int64_t)h * D, (nrow * HD + D) * 4);
     const rsrc_t r_dk = make_rsrc(dkp + t0 * HD + (int64_t)h * D, (nrow * HD + D) * 4);
     lds_barrier();
-    row_scalars<D>(sm, p, n, tid);
+    row_scalars<E, D>(sm, p, n, tid);
     lds_barrier();
     if (sl == 0 && tid < C) buf_st4(r_kk, (uint32_t)(tid * p.H * 4), sm.kk[tid]);
     gram<E, D>(sm, true, w, j, c16);  // waves 0-3 take three Gram jobs, 4-7 two
-    if (w >= 4) residual_tile<D>(sm, w - 4, j, c16);
+    if (w >= 4)
+      for (int tile = w - 4; tile < 4 * NCB; tile += 4) residual_tile<E, D>(sm, tile, j, c16);
     lds_barrier();
     if (w < 4) invert_block<false>(sm.Am, sm.Yl, w, l);
     else invert_block<true>(sm.Am, sm.Yu, w - 4, l);
     lds_barrier();
     const float glast = sm.gl[C - 1];
-    if (w == 0) {
-      tri_solve_y<false>(sm.Es, sm.Am, sm.Yl, j, c16);
+    if (w < NCB) {
+      tri_solve_y<false, LDSL>(sm.Es, sm.Am, sm.Yl, 16 * w, j, c16);
     } else {
       // U right-hand side: Diag(gamma_n/gamma) K Gend + Mq^T dO
-      for (int bt = w - 1; bt < 4; bt += BW - 1) {
-        f32x4 a1 = tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return sm.K[(16 * bt + c16) * LDK + kx]; },
-                                  [&](int kx) { return sm.Gd[kx * LDSL + c16]; });
+      for (int tile = w - NCB; tile < 4 * NCB; tile += BW - NCB) {
+        const int bt = tile & 3, cc = 16 * (tile >> 2) + c16;
+        f32x4 a1 = tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return kf(sm.K[(16 * bt + c16) * LDK + kx]); },
+                                  [&](int kx) { return sm.Gd[kx * LDSL + cc]; });
         f32x4 a2 = zero4();
         for (int st = 4 * bt; st < 16; ++st) {
           const int kx = 4 * st + j;
-          a2 = mma(sm.Xm[kx * LDN + 16 * bt + c16], sm.Ds[kx * LDSL + c16], a2);
+          a2 = mma(sm.Xm[kx * LDN + 16 * bt + c16], sm.Ds[kx * LDSL + cc], a2);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = 16 * bt + 4 * j + i;
-          sm.Us[t * LDSL + c16] = fexp2(glast - sm.gl[t]) * a1[i] + a2[i];
+          sm.Us[t * LDSL + cc] = fexp2(glast - sm.gl[t]) * a1[i] + a2[i];
         }
       }
     }
     lds_barrier();
-    if (w == 0) {
-      tri_solve_y<true>(sm.Us, sm.Am, sm.Yu, j, c16);
+    if (w < NCB) {
+      tri_solve_y<true, LDSL>(sm.Us, sm.Am, sm.Yu, 16 * w, j, c16);
     } else {
-      // O = Diag(gamma) Q S + Mq B E
-      for (int bt = w - 1; bt < 4; bt += BW - 1) {
-        f32x4 a1 = tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return sm.Q[(16 * bt + c16) * LDK + kx]; },
-                                  [&](int kx) { return sm.Sc[kx * LDSL + c16]; });
+      // O = Diag(gamma) Q S + Mq B E, reduced at once to the rows' dO . o
+      for (int tile = w - NCB; tile < 4 * NCB; tile += BW - NCB) {
+        const int bt = tile & 3, cb = tile >> 2, cc = 16 * cb + c16;
+        f32x4 a1 = tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return kf(sm.Q[(16 * bt + c16) * LDK + kx]); },
+                                  [&](int kx) { return sm.Sc[kx * LDSL + cc]; });
         f32x4 a2 = zero4();
         for (int st = 0; st < 4 * (bt + 1); ++st) {
           const int kx = 4 * st + j;
-          a2 = mma(sm.Xm[(16 * bt + c16) * LDN + kx], sm.beta[kx] * sm.Es[kx * LDSL + c16], a2);
+          a2 = mma(sm.Xm[(16 * bt + c16) * LDN + kx], sm.beta[kx] * sm.Es[kx * LDSL + cc], a2);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = 16 * bt + 4 * j + i;
-          sm.Os[t * LDSL + c16] = sm.gm[t] * a1[i] + a2[i];
+          const float part = group_sum<16>(sm.Ds[t * LDSL + cc] * (sm.gm[t] * a1[i] + a2[i]));
+          if (c16 == 0) sm.tpart[cb][t] = part;
         }
       }
     }
@@ -629,10 +636,11 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
       const float b = sm.beta[r];
       float db = 0.f, term = 0.f;
 #pragma unroll
-      for (int c = 0; c < DVS; ++c) {
+      for (int cb = 0; cb < NCB; ++cb) term += sm.tpart[cb][r];
+#pragma unroll
+      for (int c = 0; c < DV; ++c) {
         const float u = sm.Us[r * LDSL + c];
         db = fmaf(u, sm.Es[r * LDSL + c], db);
-        term = fmaf(sm.Ds[r * LDSL + c], sm.Os[r * LDSL + c], term);
         term = fmaf(-b * u, sm.Vs[r * LDSL + c], term);
       }
       // suffix sum over rows r..63 (padded rows add zero)
@@ -640,8 +648,8 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
       sm.scan[63 - r] = suf;
       buf_st4(r_db, (uint32_t)(r * p.H * 4), db);
     }
-    if (tid < C * (DVS / 4)) {
-      const int r = tid / 4, cs = tid % 4;
+    if (tid < C * F::DSEG) {
+      const int r = tid / F::DSEG, cs = tid % F::DSEG;
       const float b = sm.beta[r];
       const f32x4 u = *reinterpret_cast<const f32x4 *>(&sm.Us[r * LDSL + 4 * cs]);
       buf_st16(r_dv, (uint32_t)(r * HD * 4 + cs * 16), f32x4{b * u[0], b * u[1], b * u[2], b * u[3]});
@@ -654,8 +662,8 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
       int bt, bs;
       lower_tile(zq ? jb - 10 : jb, bt, bs);
       const float *X = zq ? sm.Ds : sm.Us;
-      f32x4 acc = tile_mm<DVS / 4>(zero4(), 0, j, [&](int kx) { return X[(16 * bt + c16) * LDSL + kx]; },
-                                   [&](int kx) { return sm.Es[(16 * bs + c16) * LDSL + kx]; });
+      f32x4 acc = tile_mm<DV / 4>(zero4(), 0, j, [&](int kx) { return X[(16 * bt + c16) * LDSL + kx]; },
+                                  [&](int kx) { return sm.Es[(16 * bs + c16) * LDSL + kx]; });
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * bt + 4 * j + i, s2 = 16 * bs + c16;
@@ -673,23 +681,24 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
     lds_barrier();
     // dq and dk contributions of these columns, as 32 x 32 tiles: wave w takes
     // row block w & 1 and column block w >> 1 of both (D = 64: waves 0-3)
-    if (w < D / 16) dq_dk_tile<D>(sm, w & 1, w >> 1, l, glast, r_dq, r_dk, HD);
+    if (w < D / 16) dq_dk_tile<E, D>(sm, w & 1, w >> 1, l, glast, r_dq, r_dk, HD);
     // Gend <- gamma_n Gend + Q^T Diag(gamma) dO - K^T Diag(gamma beta) U
-    constexpr int NT = (D / 16 + BW - 1) / BW;  // state tiles per wave
+    constexpr int NT = (NST + BW - 1) / BW;  // state tiles per wave
     f32x4 gnew[NT];
     {
       const float gn = sm.gm[C - 1];
 #pragma unroll
       for (int m = 0; m < NT; ++m) {
-        const int ti = w + BW * m;
-        if (ti >= D / 16) break;
+        const int tt = w + BW * m;
+        if (tt >= NST) break;
+        const int ti = tt % (D / 16), cc = 16 * (tt / (D / 16)) + c16;
         f32x4 acc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = gn * sm.Gd[(16 * ti + 4 * j + i) * LDSL + c16];
-        acc = tile_mm<C / 4>(acc, 0, j, [&](int kx) { return sm.Q[kx * LDK + 16 * ti + c16]; },
-                             [&](int kx) { return sm.gm[kx] * sm.Ds[kx * LDSL + c16]; });
-        acc = tile_mm<C / 4>(acc, 0, j, [&](int kx) { return sm.K[kx * LDK + 16 * ti + c16]; },
-                             [&](int kx) { return -sm.gm[kx] * sm.beta[kx] * sm.Us[kx * LDSL + c16]; });
+        for (int i = 0; i < 4; ++i) acc[i] = gn * sm.Gd[(16 * ti + 4 * j + i) * LDSL + cc];
+        acc = tile_mm<C / 4>(acc, 0, j, [&](int kx) { return kf(sm.Q[kx * LDK + 16 * ti + c16]); },
+                             [&](int kx) { return sm.gm[kx] * sm.Ds[kx * LDSL + cc]; });
+        acc = tile_mm<C / 4>(acc, 0, j, [&](int kx) { return kf(sm.K[kx * LDK + 16 * ti + c16]); },
+                             [&](int kx) { return -sm.gm[kx] * sm.beta[kx] * sm.Us[kx * LDSL + cc]; });
         gnew[m] = acc;
       }
     }
@@ -698,22 +707,23 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
       float x = 0.f;
 #pragma unroll
       for (int m = 0; m < NT; ++m) {
-        const int ti = w + BW * m;
-        if (ti >= D / 16) break;
+        const int tt = w + BW * m;
+        if (tt >= NST) break;
+        const int ti = tt % (D / 16), cc = 16 * (tt / (D / 16)) + c16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * ti + 4 * j + i;
-          sm.Gd[r * LDSL + c16] = gnew[m][i];
-          x = fmaf(gnew[m][i], sm.Sc[r * LDSL + c16], x);
+          sm.Gd[r * LDSL + cc] = gnew[m][i];
+          x = fmaf(gnew[m][i], sm.Sc[r * LDSL + cc], x);
         }
       }
-      cend = block_sum<D>(sm, x, w, l);
+      cend = block_sum<E, D>(sm, x, w, l);
     }
   }
   __syncthreads();
   if (p.d_initial) {
-    for (int idx = tid; idx < D * DVS; idx += BT) {
-      const int i = idx / DVS, c = idx % DVS;
+    for (int idx = tid; idx < D * DV; idx += BT) {
+      const int i = idx / DV, c = idx % DV;
       p.d_initial[sh * DD + i * D + col0 + c] = sm.Gd[i * LDSL + c];
     }
   }
@@ -732,7 +742,7 @@ __device__ inline f32x4 ld_k4(const float *k, int64_t g) {
 
 template <typename E, int D>
 __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdParams p) {
-  constexpr int NS = D / DVS;
+  constexpr int NS = D / BwdCfg<E, D>::DV;
   const int64_t TH = p.total_tok * p.H;
   const int64_t g4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (g4 >= TH * (D / 4)) return;
@@ -770,7 +780,7 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdParams p) {
 
 template <typename E, int D>
 hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
-  const int64_t groups = (int64_t)p.n_seqs * p.H * (D / DVS);
+  const int64_t groups = (int64_t)p.n_seqs * p.H * (D / BwdCfg<E, D>::DV);
   hipLaunchKernelGGL((bwd_kernel<E, D>), dim3((unsigned)groups), dim3(BT), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.total_tok == 0) return e;
