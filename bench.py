@@ -43,14 +43,20 @@ FP32_MFMA_PEAK_TF = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
 PREFILL_KERNEL = "prefill_pc_kernel"  # the bf16 prefill kernel (producer/consumer waves)
 DECODE_KERNEL = "decode_kernel"
 KDA_KERNEL = "prefill_kda_kernel"      # per-channel decay prefill
+BWD_KERNEL = "bwd_kernel"              # backward: the two-sweep kernel
+BWD_FINISH = "bwd_finish_kernel"       # backward: the sum over column slices
 KERNEL_SOURCES = {PREFILL_KERNEL: "delta_rule_linear_amd/csrc/kla_prefill.hip",
                   DECODE_KERNEL: "delta_rule_linear_amd/csrc/kla_decode.hip",
-                  KDA_KERNEL: "delta_rule_linear_amd/csrc/kla_kda.hip"}
+                  KDA_KERNEL: "delta_rule_linear_amd/csrc/kla_kda.hip",
+                  BWD_KERNEL: "delta_rule_linear_amd/csrc/kla_bwd.hip",
+                  BWD_FINISH: "delta_rule_linear_amd/csrc/kla_bwd.hip"}
 # mangled-name fragments of the instantiations the benchmark times (bf16
 # inputs, d = 128; the decode one with the scalar decay)
 KERNEL_MATCH = {PREFILL_KERNEL: "prefill_pc_kernelILi128ELb1E",
                 DECODE_KERNEL: "decode_kernelIDF16bLi128ELb0E",
-                KDA_KERNEL: "prefill_kda_kernelIDF16bLi128E"}
+                KDA_KERNEL: "prefill_kda_kernelIDF16bLi128E",
+                BWD_KERNEL: "bwd_kernelIDF16bLi128E",
+                BWD_FINISH: "bwd_finish_kernelIDF16bLi128E"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -86,7 +92,8 @@ def ingest_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
     """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) into
     bytes per launch, scaled by what the same counters read for a plain
     1 GiB device copy (bench.py --calibrate-copy), and record them with the
-    kernel source hash in profiles/hbm_traffic.json."""
+    kernel source hash in profiles/hbm_traffic.json (kernels absent from the
+    runs keep their earlier records)."""
     import csv
     from collections import defaultdict
 
@@ -106,10 +113,16 @@ def ingest_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
     w_scale = gib_kib / copy_kib(cal_write_csv, "WRITE_SIZE")
     fetch = per_kernel(fetch_csv, "FETCH_SIZE")
     write = per_kernel(write_csv, "WRITE_SIZE")
-    out = {}
+    try:
+        with open(TRAFFIC_JSON) as f:
+            out = json.load(f)
+    except (OSError, ValueError):
+        out = {}
     for kernel in KERNEL_SOURCES:
-        fk = [v for k, v in fetch.items() if KERNEL_MATCH[kernel] in k]
-        wk = [v for k, v in write.items() if KERNEL_MATCH[kernel] in k]
+        fk = [v for k, v in fetch.items() if KERNEL_MATCH[kernel] in k and
+              (kernel != BWD_KERNEL or "finish" not in k)]
+        wk = [v for k, v in write.items() if KERNEL_MATCH[kernel] in k and
+              (kernel != BWD_KERNEL or "finish" not in k)]
         if not fk or not wk:
             continue
         rb, wb = fk[0] * f_scale * 1024, wk[0] * w_scale * 1024
@@ -335,6 +348,7 @@ def bench_bwd(args, torch, kla, workloads, launches=10):
     flops = th * (20 * 64 * d + 20 * d * d)
     tf = flops / (ev_ms * 1e-3) / 1e12
     ws_bytes = ws.numel()
+    tb, tf_ = measured_traffic(BWD_KERNEL), measured_traffic(BWD_FINISH)
     del q, k, v, a, e, do, dfin, ws, inp, g
     return {"workload": f"backward of the layer-shaped prefill: {B} sequences x {T} tokens, H={H}, "
                         f"dk=dv={d}, bf16 q/k/v, fp32 gates, d_o and d_final; gradients of q, k, "
@@ -344,7 +358,8 @@ def bench_bwd(args, torch, kla, workloads, launches=10):
             "workspace_bytes": ws_bytes,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_MFMA_PEAK_TF,
                          "unit": "TFLOP/s", "frac": round(tf / FP32_MFMA_PEAK_TF, 4),
-                         "traffic": None, "kernel": "bwd_kernel + bwd_finish_kernel (one call)",
+                         "traffic": None if tb is None or tf_ is None else tb + tf_,
+                         "kernel": "bwd_kernel + bwd_finish_kernel (one call)",
                          "avg_launch_us": round(ev_ms * 1e3, 2),
                          "algorithmic_flops_per_launch": flops,
                          "algorithmic_bytes_per_launch": nbytes,
