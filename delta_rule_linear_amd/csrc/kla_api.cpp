@@ -461,7 +461,7 @@ kla_status kla_decode_step_ccq(const void *q, const void *k, const void *v, cons
 namespace {
 // Workspace sections of the backward, in floats, each rounded up to 64.
 struct BwdWs {
-  size_t ckpt, dq, dk, db, c, kk, total;
+  size_t ckpt, dq, dk, db, c, kk, fin, total;
 };
 size_t up64(size_t x) { return (x + 63) / 64 * 64; }
 BwdWs bwd_ws(int32_t n_seqs, int64_t total_tok, int32_t H, int32_t d) {
@@ -473,7 +473,8 @@ BwdWs bwd_ws(int32_t n_seqs, int64_t total_tok, int32_t H, int32_t d) {
   w.db = up64(ns * th);
   w.c = w.db;
   w.kk = up64(th);
-  w.total = w.ckpt + w.dq + w.dk + w.db + w.c + w.kk;
+  w.fin = up64((size_t)n_seqs * H * d * d);
+  w.total = w.ckpt + w.dq + w.dk + w.db + w.c + w.kk + w.fin;
   return w;
 }
 }  // namespace
@@ -558,6 +559,7 @@ kla_status kla_bwd_chunked(const void *q, const void *k, const void *v, const fl
   p.ws_db = p.ws_dk + w.dk;
   p.ws_c = p.ws_db + w.db;
   p.ws_kk = p.ws_c + w.c;
+  p.ws_fin = p.ws_kk + w.kk;
   return kla::launch_bwd(p, dtype == KLA_BF16, static_cast<hipStream_t>(stream)) == hipSuccess
              ? KLA_OK
              : KLA_ERR_HIP;

@@ -490,12 +490,16 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
   F f;
 
   // ---- forward sweep: chunk-start states -------------------------------
+  // (skipped when the states-only prefill has written them, with the final
+  // state in ws_fin)
   for (int idx = tid; idx < D * DV; idx += BT) {
     const int i = idx / DV, c = idx % DV;
-    sm.Sc[i * LDSL + c] = p.initial_state ? p.initial_state[sh * DD + i * D + col0 + c] : 0.f;
+    const float *src = p.ws_fin ? p.ws_fin : p.initial_state;
+    sm.Sc[i * LDSL + c] = src ? src[sh * DD + i * D + col0 + c] : 0.f;
   }
-  if (nch > 0) fetch<E, D>(f, p, sq.bos, min(C, sq.L), h, col0, ck, false, tid);
-  for (int ci = 0; ci < nch; ++ci) {
+  const int nfwd = p.ws_fin ? 0 : nch;
+  if (nfwd > 0) fetch<E, D>(f, p, sq.bos, min(C, sq.L), h, col0, ck, false, tid);
+  for (int ci = 0; ci < nfwd; ++ci) {
     const int n = min(C, sq.L - ci * C);
     lds_barrier();
     commit<E, D>(sm, f, n, false, tid);
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
         *reinterpret_cast<f32x4 *>(ck + ci * slot + (int64_t)r * D + col0 + 4 * cs) =
             *reinterpret_cast<const f32x4 *>(&sm.Sc[r * LDSL + 4 * cs]);
     }
-    if (ci + 1 < nch)
+    if (ci + 1 < nfwd)
       fetch<E, D>(f, p, sq.bos + (int64_t)(ci + 1) * C, min(C, sq.L - (ci + 1) * C), h, col0, ck,
                   false, tid);
     lds_barrier();
@@ -780,6 +784,28 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdParams p) {
 
 template <typename E, int D>
 hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
+  if (p.ws_fin && p.total_tok > 0) {
+    // bf16: the chunk-start states from the states-only prefill
+    PrefillArgs a;
+    a.q = p.q;
+    a.k = p.k;
+    a.v = p.v;
+    a.alpha = p.alpha;
+    a.eta = p.eta;
+    a.cu_seqlens = p.cu_seqlens;
+    a.n_seqs = p.n_seqs;
+    a.seq_len_dense = p.seq_len_dense;
+    a.H = p.H;
+    a.D = D;
+    a.eps = p.eps;
+    a.beta_direct = p.beta_direct;
+    a.initial_state = p.initial_state;
+    a.o = p.dv;  // not written by the states-only pass
+    a.final_state = p.ws_fin;
+    a.ws_ckpt = p.ws_ckpt;
+    hipError_t e = launch_prefill_states(a, st);
+    if (e != hipSuccess) return e;
+  }
   const int64_t groups = (int64_t)p.n_seqs * p.H * (D / BwdCfg<E, D>::DV);
   hipLaunchKernelGGL((bwd_kernel<E, D>), dim3((unsigned)groups), dim3(BT), 0, st, p);
   hipError_t e = hipGetLastError();
@@ -791,7 +817,9 @@ hipError_t launch_bwd_t(const BwdParams &p, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdParams &p, bool bf16_inputs, hipStream_t st) {
+hipError_t launch_bwd(const BwdParams &p_in, bool bf16_inputs, hipStream_t st) {
+  BwdParams p = p_in;
+  if (!bf16_inputs || p.total_tok == 0) p.ws_fin = nullptr;  // fp32: the kernel's own forward sweep
   if (bf16_inputs) return p.D == 64 ? launch_bwd_t<__bf16, 64>(p, st) : launch_bwd_t<__bf16, 128>(p, st);
   return p.D == 64 ? launch_bwd_t<float, 64>(p, st) : launch_bwd_t<float, 128>(p, st);
 }

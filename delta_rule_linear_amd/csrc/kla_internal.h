@@ -23,6 +23,7 @@ struct PrefillArgs {
   int n_splits = 1;
   float *ws_a = nullptr, *ws_b = nullptr;  // [n_seqs, H, P-1, D, D]
   const float *ws_s = nullptr;             // [n_seqs, H, P, D, D]
+  float *ws_ckpt = nullptr;                // states-only pass: chunk-start state slots
 };
 
 struct DecodeArgs {
@@ -71,6 +72,10 @@ struct BwdParams {
   // workspace: chunk-start states [floor(tok/64) + n_seqs, H, D, D], the
   // column slices' dq, dk [D/16, tok, H, D], dbeta, c [D/16, tok, H], |k|^2 [tok, H]
   float *ws_ckpt, *ws_dq, *ws_dk, *ws_db, *ws_c, *ws_kk;
+  // final states [n_seqs, H, D, D]; when set, ws_ckpt already holds the
+  // chunk-start states (written by the states-only prefill) and the
+  // backward kernel skips its own forward sweep
+  float *ws_fin = nullptr;
 };
 
 // Each returns the HIP status of the launch.
@@ -90,6 +95,10 @@ hipError_t launch_ccq_decode(const CcqArgs &a, hipStream_t s);
 hipError_t launch_add(float *o, const float *o2, int64_t n, hipStream_t s);
 // Per-channel decay prefill (alpha [total_tok, H, D]); whole sequences only.
 hipError_t launch_prefill_kda(const PrefillArgs &a, bool bf16_inputs, hipStream_t s);
+// bf16 prefill without output (whole sequences): every chunk-start state to
+// its slot of ws_ckpt (sequence s, chunk c: slot floor(bos_s / 64) + s + c,
+// each [H, D, D]) and the final state to final_state.  o is not written.
+hipError_t launch_prefill_states(const PrefillArgs &a, hipStream_t s);
 // Backward: the two-sweep kernel, then the reduction over column slices.
 hipError_t launch_bwd(const BwdParams &p, bool bf16_inputs, hipStream_t s);
 

@@ -173,16 +173,21 @@ __device__ inline void store_split(float *h, float *, int idx, float x) { h[idx]
 //     ws_b).  No output.
 //   mode 2, all segments: each from its start state in ws_s (written by the
 //     scan), writing o; the last segment writes the final state.
+//   mode 3, whole sequences, states only (the OUT = false instance): each
+//     chunk-start state goes to its slot of ckpt (sequence s, chunk c: slot
+//     floor(bos_s / 64) + s + c, each [H, D, D]) and the final state to Sfin.
 struct SegParams {
   int mode, n_splits;
   float *ws_a, *ws_b;   // [n_seqs, H, P-1, D, D]
   const float *ws_s;    // [n_seqs, H, P, D, D]
+  float *ckpt;          // mode 3: chunk-start state slots
 };
 struct Work {
   int h, nb, vb;        // head, state column block, V column block (-1: V read as zero)
   int64_t bos, eos;     // token range of this workgroup
   const float *s0;      // start state (D x D row-major) or null for zero
   float *sfin;          // end state destination or null
+  float *ck;            // mode 3: this (sequence, head)'s first chunk-start slot
   bool out;             // write o
 };
 template <int NB, int D>
@@ -217,11 +222,13 @@ __device__ inline Work resolve_work(const SegParams &sp, const int32_t *cu_seqle
   }
   constexpr int64_t DD = (int64_t)D * D;
   wk.out = sp.mode != 1;
-  if (sp.mode == 0) {
+  wk.ck = nullptr;
+  if (sp.mode == 0 || sp.mode == 3) {
     wk.bos = bos;
     wk.eos = eos;
     wk.s0 = S0 ? S0 + sh * DD : nullptr;
     wk.sfin = Sfin ? Sfin + sh * DD : nullptr;
+    if (sp.mode == 3) wk.ck = sp.ckpt + ((bos / C + s) * H + wk.h) * DD;
     return wk;
   }
   const int64_t nch = (eos - bos + C - 1) / C, per = (nch + P - 1) / P;
@@ -1096,15 +1103,30 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
     }
     lds_barrier();
   };
+  // states-only pass: the state entering each chunk to its slot
+  auto store_ck = [&](const f32x4 (&Sx)[NST], int64_t t0) __attribute__((always_inline)) {
+    if constexpr (!OUT) {
+      if (wk.ck) {
+        const int64_t DD = (int64_t)D * D;
+        const rsrc_t rc = make_rsrc(wk.ck + ((t0 - bos) / C) * H * DD, DD * 4);
+#pragma unroll
+        for (int t = 0; t < NST; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) buf_st4(rc, ((16 * t + 4 * j + i) * D + col) * 4, Sx[t][i]);
+      }
+    }
+  };
   int64_t tok0 = bos;
   bool in_s2 = false;  // the current state is in S2
   while (tok0 < eos) {
+    store_ck(S, tok0);
     cstep(sm.slot[0], tok0, S, S2);
     tok0 += C;
     if (tok0 >= eos) {
       in_s2 = true;
       break;
     }
+    store_ck(S2, tok0);
     cstep(sm.slot[1], tok0, S2, S);
     tok0 += C;
   }
@@ -1139,6 +1161,7 @@ inline SegParams seg_of(const PrefillArgs &a) {
   sp.ws_a = a.ws_a;
   sp.ws_b = a.ws_b;
   sp.ws_s = a.ws_s;
+  sp.ckpt = a.ws_ckpt;
   return sp;
 }
 
@@ -1167,6 +1190,19 @@ hipError_t launch_d(const PrefillArgs &a, hipStream_t st) {
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s) {
   return a.D == 128 ? launch_pc<128>(a, s) : launch_pc<64>(a, s);
+}
+hipError_t launch_prefill_states(const PrefillArgs &a, hipStream_t st) {
+  // whole sequences (mode 3), no output: the chunk-start states and the final state
+  PrefillArgs b = a;
+  b.seg_mode = 3;
+  b.n_splits = 1;
+  const int64_t grid = (int64_t)a.n_seqs * a.H * (a.D / DVB);
+  auto kern = a.D == 128 ? prefill_pc_kernel<128, false> : prefill_pc_kernel<64, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, st,
+                     static_cast<const bf16 *>(b.q), static_cast<const bf16 *>(b.k),
+                     static_cast<const bf16 *>(b.v), b.alpha, b.eta, b.cu_seqlens, b.seq_len_dense,
+                     b.H, b.eps, b.beta_direct, b.initial_state, b.o, b.final_state, seg_of(b));
+  return hipGetLastError();
 }
 hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t s) {
   return a.D == 128 ? launch_d<float, 128>(a, s) : launch_d<float, 64>(a, s);

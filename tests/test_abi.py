@@ -317,11 +317,12 @@ def test_binding_names_match_the_abi():
 
 def test_bwd_workspace_query(lib):
     # chunk-start states (tok/64 + n_seqs slots), 8 column slices of dq and dk,
-    # their dbeta and decay sums, and |k|^2 (each section rounded up to 64 floats)
+    # their dbeta and decay sums, |k|^2 and the final states (each section
+    # rounded up to 64 floats)
     n, tok, H, d = 8, 16384, 16, 128
     up = lambda x: (x + 63) // 64 * 64
     want = (up((tok // 64 + n) * H * d * d) + 2 * up(8 * tok * H * d) + 2 * up(8 * tok * H)
-            + up(tok * H)) * 4
+            + up(tok * H) + up(n * H * d * d)) * 4
     assert lib.kla_bwd_chunked_workspace_size(n, tok, H, d, d, 64) == want
     assert lib.kla_bwd_chunked_workspace_size(n, tok, H, 96, 96, 64) == 0
     assert lib.kla_bwd_chunked_workspace_size(n, tok, H, d, d, 32) == 0
