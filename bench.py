@@ -45,18 +45,21 @@ DECODE_KERNEL = "decode_kernel"
 KDA_KERNEL = "prefill_kda_kernel"      # per-channel decay prefill
 BWD_KERNEL = "bwd_kernel"              # backward: the two-sweep kernel
 BWD_FINISH = "bwd_finish_kernel"       # backward: the sum over column slices
+BWD_STATES = "prefill_pc_kernel_states"  # backward (bf16): chunk-start states, no output
 KERNEL_SOURCES = {PREFILL_KERNEL: "delta_rule_linear_amd/csrc/kla_prefill.hip",
                   DECODE_KERNEL: "delta_rule_linear_amd/csrc/kla_decode.hip",
                   KDA_KERNEL: "delta_rule_linear_amd/csrc/kla_kda.hip",
                   BWD_KERNEL: "delta_rule_linear_amd/csrc/kla_bwd.hip",
-                  BWD_FINISH: "delta_rule_linear_amd/csrc/kla_bwd.hip"}
+                  BWD_FINISH: "delta_rule_linear_amd/csrc/kla_bwd.hip",
+                  BWD_STATES: "delta_rule_linear_amd/csrc/kla_prefill.hip"}
 # mangled-name fragments of the instantiations the benchmark times (bf16
 # inputs, d = 128; the decode one with the scalar decay)
 KERNEL_MATCH = {PREFILL_KERNEL: "prefill_pc_kernelILi128ELb1E",
                 DECODE_KERNEL: "decode_kernelIDF16bLi128ELb0E",
                 KDA_KERNEL: "prefill_kda_kernelIDF16bLi128E",
                 BWD_KERNEL: "bwd_kernelIDF16bLi128E",
-                BWD_FINISH: "bwd_finish_kernelIDF16bLi128E"}
+                BWD_FINISH: "bwd_finish_kernelIDF16bLi128E",
+                BWD_STATES: "prefill_pc_kernelILi128ELb0E"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -322,7 +325,8 @@ def bench_kda(args, torch, kla, workloads, launches=50):
 def bench_bwd(args, torch, kla, workloads, launches=10):
     """Backward of the layer-shaped prefill (kla_bwd_chunked): gradients of
     q, k, v, alpha, eta and the start state from seeded d_o and d_final.
-    One call is two launches (the two-sweep kernel and the reduction over
+    One call is three launches (the states-only prefill that writes the
+    chunk-start states, the reverse-sweep kernel and the reduction over
     column slices); the events bracket whole calls."""
     inp = workloads.prefill("layer")
     B, H, d = inp["n_seqs"], inp["H"], inp["d"]
@@ -348,7 +352,7 @@ def bench_bwd(args, torch, kla, workloads, launches=10):
     flops = th * (20 * 64 * d + 20 * d * d)
     tf = flops / (ev_ms * 1e-3) / 1e12
     ws_bytes = ws.numel()
-    tb, tf_ = measured_traffic(BWD_KERNEL), measured_traffic(BWD_FINISH)
+    parts = [measured_traffic(x) for x in (BWD_STATES, BWD_KERNEL, BWD_FINISH)]
     del q, k, v, a, e, do, dfin, ws, inp, g
     return {"workload": f"backward of the layer-shaped prefill: {B} sequences x {T} tokens, H={H}, "
                         f"dk=dv={d}, bf16 q/k/v, fp32 gates, d_o and d_final; gradients of q, k, "
@@ -358,8 +362,9 @@ def bench_bwd(args, torch, kla, workloads, launches=10):
             "workspace_bytes": ws_bytes,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_MFMA_PEAK_TF,
                          "unit": "TFLOP/s", "frac": round(tf / FP32_MFMA_PEAK_TF, 4),
-                         "traffic": None if tb is None or tf_ is None else tb + tf_,
-                         "kernel": "bwd_kernel + bwd_finish_kernel (one call)",
+                         "traffic": None if None in parts else sum(parts),
+                         "kernel": "prefill_pc_kernel<states> + bwd_kernel + bwd_finish_kernel "
+                                   "(one call)",
                          "avg_launch_us": round(ev_ms * 1e3, 2),
                          "algorithmic_flops_per_launch": flops,
                          "algorithmic_bytes_per_launch": nbytes,
