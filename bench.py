@@ -23,6 +23,13 @@ Algorithmic work counted per token-head (d = 128, C = 64):
                  dq, dk, dv, dalpha, deta fp32: 2832 B per token-head; full-
                  tile flops of the chunk form 20*C*d + 20*d*d = 491,520 per
                  token-head, on the fp32 MFMA
+  gate_variants  the layer prefill with the direct step (Gated DeltaNet) and
+                 without decay (DeltaNet), same kernel
+  ccq            the curvature-conditioned read: layer prefill (query-
+                 cleaning pass + bf16 prefill on the cleaned query's hi and
+                 lo parts + sum; algorithmic bytes as the prefill plus lambda
+                 and the per-(sequence, head) sums) and the decode step
+                 (state and running sums read and written once)
   per-channel decay (Kimi Delta Attention gate, `kda` object): the same
                  work with alpha fp32 [.., dk]: 1288 - 4 + 4*d = 1796 B per
                  token-head; its prefill kernel computes in fp32 (fp32 MFMA)
@@ -371,6 +378,98 @@ def bench_bwd(args, torch, kla, workloads, launches=10):
                          "hbm_gbs": round(nbytes / (ev_ms * 1e-3) / 1e9, 1)}}
 
 
+def bench_variants(args, torch, kla, workloads, launches=50):
+    """The layer-shaped prefill with the other step-size rules on the same
+    kernel: the direct step beta = eta (Gated DeltaNet) and the direct step
+    without decay (DeltaNet)."""
+    inp = workloads.prefill("layer")
+    B, H, d = inp["n_seqs"], inp["H"], inp["d"]
+    T = inp["lengths"][0]
+    dev = "cuda:0"
+    q, k, v = (inp[n].to(dev).view(B, T, H, d) for n in ("q", "k", "v"))
+    # these step rules assume unit-norm keys (with |k| up to e^3 the direct
+    # step beta = eta would make the recurrence diverge)
+    kf = k.float()
+    k = (kf / kf.norm(dim=-1, keepdim=True)).to(k.dtype).contiguous()
+    a, e = (inp[n].to(dev).view(B, T, H) for n in ("alpha", "eta"))
+    o = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    out = {"workload": f"layer-shaped prefill ({B} x {T} tokens, H={H}, d={d}, bf16, unit-norm "
+                       f"keys) with the direct step (Gated DeltaNet) and without decay (DeltaNet)"}
+    for name, alpha in (("gated_deltanet", a), ("deltanet", None)):
+        def step():
+            kla.kla_fwd_chunked_ex(q, k, v, alpha, e, eps=inp["eps"], beta_mode="direct", o=o,
+                                   final_state=S)
+        for _ in range(200):  # as the headline prefill: the clock settles first
+            step()
+        _, ms = time_launches(step, launches, stream)
+        out[name + "_us"] = round(ms * 1e3, 2)
+        out[name + "_tokens_per_s"] = round(B * T / (ms * 1e-3), 1)
+    del q, k, kf, v, a, e, o, S, inp
+    return out
+
+
+def bench_ccq(args, torch, kla, workloads, launches=50):
+    """The curvature-conditioned read: the layer-shaped prefill and the
+    decode workload with o_t = S_t^T (q_t - lambda_t Sigma_t q_t).  One
+    prefill call = the query-cleaning pass, the bf16 prefill on the cleaned
+    query's hi and lo parts, and their sum; one decode step = the sums update
+    with the cleaned query, then the decode kernel."""
+    inp = workloads.prefill("layer")
+    B, H, d = inp["n_seqs"], inp["H"], inp["d"]
+    T = inp["lengths"][0]
+    dev = "cuda:0"
+    q, k, v = (inp[n].to(dev).view(B, T, H, d) for n in ("q", "k", "v"))
+    a, e = (inp[n].to(dev).view(B, T, H) for n in ("alpha", "eta"))
+    lam = workloads.ccq_gate(0, B * T, H).to(dev).view(B, T, H)
+    o = torch.empty((B, T, H, d), dtype=torch.float32, device=dev)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    rec = kla.kla_ccq_state_floats(d)
+    cout = torch.empty((B, H, rec), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kla.kla_fwd_chunked_ccq(q, k, v, a, e, lam, eps=inp["eps"], o=o, final_state=S,
+                                ccq_out=cout)
+
+    for _ in range(10):
+        step()
+    _, ms = time_launches(step, launches, stream)
+    th = B * T * H
+    nbytes = th * (3 * d * 2 + 3 * 4 + d * 4) + B * H * (d * d + rec) * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del q, k, v, a, e, lam, o, S, cout, inp
+    out = {"workload": f"curvature-conditioned read, layer-shaped prefill: {B} x {T} tokens, H={H}, "
+                       f"d={d}, bf16 q/k/v, fp32 gates and lambda",
+           "prefill_us": round(ms * 1e3, 2),
+           "prefill_tokens_per_s": round(B * T / (ms * 1e-3), 1),
+           "prefill_hbm_gbs": round(gbs, 1),
+           "prefill_algorithmic_bytes": nbytes}
+    if not args.skip_decode:
+        wl = workloads.decode(steps=args.decode_steps)
+        N = wl["n_seqs"]
+        state = wl["state"].to(dev)
+        sums = torch.zeros((N, H, rec), dtype=torch.float32, device=dev)
+        steps = [{n: st[n].to(dev) for n in ("q", "k", "v", "alpha", "eta")} for st in wl["steps"]]
+        lams = [workloads.ccq_gate(100 + i, N, H).to(dev) for i in range(len(steps))]
+        od = torch.empty((N, H, d), dtype=torch.float32, device=dev)
+        it = iter(range(len(steps)))
+
+        def one():
+            i = next(it)
+            st = steps[i]
+            kla.kla_decode_step_ccq(st["q"], st["k"], st["v"], st["alpha"], st["eta"], lams[i],
+                                    state, sums, eps=wl["eps"], o=od)
+
+        _, dms = time_launches(one, len(steps), stream)
+        dbytes = 2 * N * H * (d * d + rec) * 4
+        out["decode_us_per_step"] = round(dms * 1e3, 2)
+        out["decode_gbs"] = round(dbytes / (dms * 1e-3) / 1e9, 1)
+        out["decode_bytes_per_step"] = dbytes
+    return out
+
+
 def cpu_baseline(pre, oracle):
     """fp64 reference on the host over the whole layer-shaped prefill."""
     import numpy as np
@@ -412,6 +511,10 @@ def main():
                     help="skip the long-context one-pass vs split-sequence comparison")
     ap.add_argument("--skip-kda", action="store_true",
                     help="skip the per-channel decay prefill and decode")
+    ap.add_argument("--skip-variants", action="store_true",
+                    help="skip the direct-step (Gated DeltaNet, DeltaNet) prefills")
+    ap.add_argument("--skip-ccq", action="store_true",
+                    help="skip the curvature-conditioned read (prefill and decode)")
     ap.add_argument("--skip-bwd", action="store_true",
                     help="skip the backward of the layer-shaped prefill")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
@@ -486,6 +589,10 @@ def main():
         out["long_context"] = bench_long(args, torch, kla, workloads)
     if not args.skip_kda:
         out["kda"] = bench_kda(args, torch, kla, workloads)
+    if not args.skip_variants:
+        out["gate_variants"] = bench_variants(args, torch, kla, workloads)
+    if not args.skip_ccq:
+        out["ccq"] = bench_ccq(args, torch, kla, workloads)
     if not args.skip_bwd:
         out["backward"] = bench_bwd(args, torch, kla, workloads)
     if not args.skip_cpu_baseline:
