@@ -162,3 +162,20 @@ def test_bwd_packed_workload_sampled(kla):
     seqs = sorted(set([int(lens.argmax()), int(lens.argmin())]
                       + [int(x) for x in rng.choice(len(lens), 2, replace=False)]))
     run_case(kla, "bwd packed", inp, g, with_s0=False, seqs=seqs)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_dense_batch(kla, dtype):
+    B, T = 3, 200
+    say(f"bwd dense batch B={B} T={T} H=2 d=128 {dtype}: dense equals packed, and the oracle")
+    inp = workloads.prefill(n_seqs=B, T=T, H=2, d=128, dtype=dtype, seed=15)
+    g = workloads.grad_inputs(9, B * T, 2, 128, B)
+    dev = "cuda"
+    view = lambda x: x.to(dev).view(B, T, *x.shape[1:])
+    dense = kla.kla_bwd_chunked(view(inp["q"]), view(inp["k"]), view(inp["v"]), view(inp["alpha"]),
+                                view(inp["eta"]), view(g["d_o"]), initial_state=g["initial_state"].to(dev),
+                                d_final=g["d_final"].to(dev), eps=inp["eps"])
+    torch.cuda.synchronize()
+    got = run_case(kla, f"bwd dense-as-packed {dtype}", inp, g)
+    for key in KEYS:
+        assert torch.equal(dense[key].reshape(got[key].shape).cpu(), got[key]), key
