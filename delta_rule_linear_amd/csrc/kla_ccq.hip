@@ -34,13 +34,17 @@
 namespace kla {
 namespace {
 
-template <int D>
+template <typename E, int D>
 struct CcqSmem {
   static constexpr int LDK = D + 4;
   static constexpr int LDP = C + 4;
   static constexpr int LDC = DVB + 4;
+  static constexpr int LDT = C + 8;  // row pitch of the transposed bf16 keys
   alignas(16) float Kr[C * LDK];   // keys of the chunk (fp32)
   alignas(16) float Qr[C * LDK];   // queries of the chunk (fp32)
+  // bf16 inputs: the chunk's keys transposed, [feature][token] (exact), the
+  // operands of K^T K on the bf16 MFMA
+  alignas(16) __bf16 Kt[sizeof(E) == 2 ? D * LDT : 8];
   alignas(16) float G[C * LDP];    // lower(Q K^T), zero above the diagonal
   alignas(16) float cm[C * LDC];   // m_t for this workgroup's columns
   alignas(16) float msum[D];       // m at the chunk start (all columns)
@@ -70,10 +74,11 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
     const int32_t *__restrict__ cu_seqlens, int64_t seq_len_dense, int H,
     const float *__restrict__ ccq_in, float *__restrict__ ccq_out, void *__restrict__ qh,
     void *__restrict__ ql) {
-  using SM = CcqSmem<D>;
+  using SM = CcqSmem<E, D>;
   constexpr int NB = D / DVB;
   constexpr int NST = D / 16;
-  constexpr int LDK = SM::LDK, LDP = SM::LDP, LDC = SM::LDC;
+  constexpr int LDK = SM::LDK, LDP = SM::LDP, LDC = SM::LDC, LDT = SM::LDT;
+  constexpr bool BF = sizeof(E) == 2;
   constexpr int SEG_EL = 16 / sizeof(E);
   constexpr int SEG_ROW = D / SEG_EL;
   constexpr int NSEG = C * SEG_ROW / kThreads;
@@ -137,8 +142,24 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
       const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
       seg_to_f32<E>(kreg[u], &sm.Kr[r * LDK + cs * SEG_EL]);
       seg_to_f32<E>(qreg[u], &sm.Qr[r * LDK + cs * SEG_EL]);
+      if constexpr (BF) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, kreg[u]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.Kt[(cs * SEG_EL + e) * LDT + r] = b[e];
+      }
     }
     if (w == 0) sm.lam[l] = lreg;
+  };
+  // 8 fp32 values that hold bf16 numbers -> bf16x8 (exact)
+  auto bf8 = [](const float *p) __attribute__((always_inline)) {
+    const f32x4 x = *reinterpret_cast<const f32x4 *>(p), y = *reinterpret_cast<const f32x4 *>(p + 4);
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r[e] = static_cast<__bf16>(x[e]);
+      r[4 + e] = static_cast<__bf16>(y[e]);
+    }
+    return r;
   };
 
   fetch(bos);
@@ -159,9 +180,16 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
           const int bi = (tn >= 1) + (tn >= 3) + (tn >= 6);
           const int bj = tn - bi * (bi + 1) / 2;
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (BF) {
 #pragma unroll
-          for (int k0 = 0; k0 < D; k0 += 4)
-            acc = mma(sm.Qr[(16 * bi + c16) * LDK + k0 + j], sm.Kr[(16 * bj + c16) * LDK + k0 + j], acc);
+            for (int kb = 0; kb < D / 32; ++kb)
+              acc = mma(bf8(&sm.Qr[(16 * bi + c16) * LDK + 32 * kb + 8 * j]),
+                        bf8(&sm.Kr[(16 * bj + c16) * LDK + 32 * kb + 8 * j]), acc);
+          } else {
+#pragma unroll
+            for (int k0 = 0; k0 < D; k0 += 4)
+              acc = mma(sm.Qr[(16 * bi + c16) * LDK + k0 + j], sm.Kr[(16 * bj + c16) * LDK + k0 + j], acc);
+          }
           // acc[i] = (Q K^T)[16bi + 4j + i][16bj + c16]
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -247,11 +275,20 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
 #pragma unroll
       for (int t = 0; t < NST; ++t) {
         Pc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (BF) {
+          // (K^T K)[16t + 4j + i][col]: A = K^T rows 16t + c16, B = K^T row col,
+          // eight consecutive tokens per lane from the transposed keys
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+          for (int kb = 0; kb < C / 32; ++kb)
+            Pc[t] = mma(*reinterpret_cast<const bf16x8 *>(&sm.Kt[(16 * t + c16) * LDT + 32 * kb + 8 * j]),
+                        *reinterpret_cast<const bf16x8 *>(&sm.Kt[col * LDT + 32 * kb + 8 * j]), Pc[t]);
+        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            Pc[t] = mma(sm.Kr[(16 * mt + 4 * j + i) * LDK + 16 * t + c16], Kc[mt][i], Pc[t]);
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              Pc[t] = mma(sm.Kr[(16 * mt + 4 * j + i) * LDK + 16 * t + c16], Kc[mt][i], Pc[t]);
+        }
       }
 #pragma unroll
       for (int t = 0; t < NST; ++t) P[t] += Pc[t];
