@@ -200,14 +200,42 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
       }
     }
     f32x4 PQ[4];
+    if constexpr (BF) {
+      // P split into bf16 hi + lo (to 2^-17) and used in place as the B
+      // operand of the 32-deep bf16 MFMA (tiles 2kk, 2kk+1 joined: lane group
+      // j holds rows 32kk + 4j + i and 32kk + 16 + 4j + i); the A operand
+      // reads the query columns in the same order.  Hi and lo products go to
+      // separate MFMAs.
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int bi = 0; bi < 4; ++bi) PQ[bi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < NST; ++t)
+      for (int kk = 0; kk < NST / 2; ++kk) {
+        const Split8 pf = join(split4(P[2 * kk]), split4(P[2 * kk + 1]));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc = mma(sm.Qr[(16 * bi + c16) * LDK + 16 * t + 4 * j + i], P[t][i], acc);
-      PQ[bi] = acc;  // (Q P)[16bi + 4j + i][col]
+        for (int bi = 0; bi < 4; ++bi) {
+          const float *row = &sm.Qr[(16 * bi + c16) * LDK + 32 * kk];
+          const f32x4 x = *reinterpret_cast<const f32x4 *>(row + 4 * j);
+          const f32x4 y = *reinterpret_cast<const f32x4 *>(row + 16 + 4 * j);
+          bf16x8 a;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] = static_cast<__bf16>(x[e]);
+            a[4 + e] = static_cast<__bf16>(y[e]);
+          }
+          PQ[bi] = mma(a, pf.hi, PQ[bi]);
+          PQ[bi] = mma(a, pf.lo, PQ[bi]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NST; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc = mma(sm.Qr[(16 * bi + c16) * LDK + 16 * t + 4 * j + i], P[t][i], acc);
+        PQ[bi] = acc;  // (Q P)[16bi + 4j + i][col]
+      }
     }
     if (w == 0) {
       float d = 0.f;

@@ -1,8 +1,9 @@
-// Device helpers shared by the prefill kernels (kla_prefill.hip and
-// kla_kda.hip): vector types, MFMA wrappers, LDS-only barriers, DPP lane
-// movement and wave scans, range-checked buffer access, the XCD-aware
-// workgroup order, the DPP forward-substitution step and the numbering of
-// the off-diagonal Gram jobs.
+// Device helpers shared by the chunked kernels (kla_prefill.hip, kla_kda.hip,
+// kla_ccq.hip, kla_bwd.hip): vector types, MFMA wrappers, the bf16 hi/lo
+// split of an accumulator tile, LDS-only barriers, DPP lane movement and
+// wave scans, range-checked buffer access, the XCD-aware workgroup order,
+// the DPP forward-substitution step and the numbering of the off-diagonal
+// Gram jobs.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,6 +34,50 @@ __device__ inline f32x4 mma(bf16x4 a, bf16x4 b, f32x4 c) {
 }
 __device__ inline f32x4 mma(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+struct Split4 {
+  bf16x4 hi, lo;
+};
+struct Split8 {
+  bf16x8 hi, lo;
+};
+
+// One accumulator tile as the B operand of a 16-deep MFMA (lane-group j
+// holds contraction rows 4j..4j+3, exactly the tile's own rows), split into
+// hi = bf16(x) (round to nearest even) + lo = bf16(x - hi).  The residual
+// x - hi is exact in fp32; one v_dot2 of the packed hi pair with (-1, 0) or
+// (0, -1) forms it without unpacking hi.
+// The bf16 pairs (-1, 0) and (0, -1) as opaque scalar values: written by an
+// s_mov the compiler cannot see through, so it never folds them into an
+// inline constant (the inline constant -1.0 reads as the f32 bit pattern,
+// i.e. the pair (0, -1), for packed bf16 operands).
+__device__ inline bf16x2 sgpr_pair(uint32_t bits) {
+  uint32_t r;
+  asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(bits));
+  return __builtin_bit_cast(bf16x2, r);
+}
+__device__ inline Split4 split4(f32x4 c) {
+  const bf16x2 m0 = sgpr_pair(0x0000BF80u), m1 = sgpr_pair(0xBF800000u);
+  const bf16x2 h01 = __builtin_convertvector(__builtin_shufflevector(c, c, 0, 1), bf16x2);
+  const bf16x2 h23 = __builtin_convertvector(__builtin_shufflevector(c, c, 2, 3), bf16x2);
+  const f32x4 res = {__builtin_amdgcn_fdot2_f32_bf16(h01, m0, c[0], false),
+                     __builtin_amdgcn_fdot2_f32_bf16(h01, m1, c[1], false),
+                     __builtin_amdgcn_fdot2_f32_bf16(h23, m0, c[2], false),
+                     __builtin_amdgcn_fdot2_f32_bf16(h23, m1, c[3], false)};
+  Split4 r;
+  r.hi = __builtin_shufflevector(h01, h23, 0, 1, 2, 3);
+  r.lo = __builtin_convertvector(res, bf16x4);
+  return r;
+}
+// Two tiles covering contraction rows [0,16) and [16,32) as the B operand of
+// a 32-deep MFMA: element i of lane-group j holds row 4j+i (i<4) or
+// 16+4j+(i-4) (i>=4).
+__device__ inline Split8 join(const Split4 &a, const Split4 &b) {
+  Split8 r;
+  r.hi = __builtin_shufflevector(a.hi, b.hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  r.lo = __builtin_shufflevector(a.lo, b.lo, 0, 1, 2, 3, 4, 5, 6, 7);
+  return r;
 }
 
 // Workgroup barrier that orders LDS traffic only.  __syncthreads() also
