@@ -39,7 +39,9 @@ struct CcqSmem {
   static constexpr int LDK = D + 4;
   static constexpr int LDP = C + 4;
   static constexpr int LDC = DVB + 4;
-  static constexpr int LDT = C + 8;  // row pitch of the transposed bf16 keys
+  // row pitch of the transposed bf16 keys: 8-byte rows, and rows 8 apart
+  // (the rows one token's 16-byte segments scatter to) on different banks
+  static constexpr int LDT = C + 4;
   alignas(16) float Kr[C * LDK];   // keys of the chunk (fp32)
   alignas(16) float Qr[C * LDK];   // queries of the chunk (fp32)
   // bf16 inputs: the chunk's keys transposed, [feature][token] (exact), the
@@ -307,9 +309,17 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
           // (K^T K)[16t + 4j + i][col]: A = K^T rows 16t + c16, B = K^T row col,
           // eight consecutive tokens per lane from the transposed keys
 #pragma unroll
-          for (int kb = 0; kb < C / 32; ++kb)
-            Pc[t] = mma(*reinterpret_cast<const bf16x8 *>(&sm.Kt[(16 * t + c16) * LDT + 32 * kb + 8 * j]),
-                        *reinterpret_cast<const bf16x8 *>(&sm.Kt[col * LDT + 32 * kb + 8 * j]), Pc[t]);
+          for (int kb = 0; kb < C / 32; ++kb) {
+            const __bf16 *pa = &sm.Kt[(16 * t + c16) * LDT + 32 * kb + 8 * j];
+            const __bf16 *pb = &sm.Kt[col * LDT + 32 * kb + 8 * j];
+            const bf16x8 a = __builtin_shufflevector(*reinterpret_cast<const bf16x4 *>(pa),
+                                                     *reinterpret_cast<const bf16x4 *>(pa + 4),
+                                                     0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 b = __builtin_shufflevector(*reinterpret_cast<const bf16x4 *>(pb),
+                                                     *reinterpret_cast<const bf16x4 *>(pb + 4),
+                                                     0, 1, 2, 3, 4, 5, 6, 7);
+            Pc[t] = mma(a, b, Pc[t]);
+          }
         } else {
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
