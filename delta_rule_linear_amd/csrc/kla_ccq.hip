@@ -38,7 +38,6 @@ template <typename E, int D>
 struct CcqSmem {
   static constexpr int LDK = D + 4;
   static constexpr int LDP = C + 4;
-  static constexpr int LDC = DVB + 4;
   // row pitch of the transposed bf16 keys: 8-byte rows, and rows 8 apart
   // (the rows one token's 16-byte segments scatter to) on different banks
   static constexpr int LDT = C + 4;
@@ -48,9 +47,10 @@ struct CcqSmem {
   // operands of K^T K on the bf16 MFMA
   alignas(16) __bf16 Kt[sizeof(E) == 2 ? D * LDT : 8];
   alignas(16) float G[C * LDP];    // lower(Q K^T), zero above the diagonal
-  alignas(16) float cm[C * LDC];   // m_t for this workgroup's columns
   alignas(16) float msum[D];       // m at the chunk start (all columns)
-  alignas(16) float md[C];         // m . q_t
+  alignas(16) float mdp[4 * C];    // m . q_t, one partial per wave (a quarter of the columns each)
+  alignas(16) float rsum[4 * C];   // row sums of lower(Q K^T), one partial per 16-column block
+  alignas(16) float kp[kThreads];  // the chunk's key sums, kThreads / D partials per column
   alignas(16) float mq[C];         // m_t . q_t
   alignas(16) float lam[C];
 };
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
   using SM = CcqSmem<E, D>;
   constexpr int NB = D / DVB;
   constexpr int NST = D / 16;
-  constexpr int LDK = SM::LDK, LDP = SM::LDP, LDC = SM::LDC, LDT = SM::LDT;
+  constexpr int LDK = SM::LDK, LDP = SM::LDP, LDT = SM::LDT;
   constexpr bool BF = sizeof(E) == 2;
   constexpr int SEG_EL = 16 / sizeof(E);
   constexpr int SEG_ROW = D / SEG_EL;
@@ -103,8 +103,10 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
   const int cl = 16 * w + c16;       // column within this workgroup's block
   const int col = nb * DVB + cl;     // column of P and of q_clean
 
-  // G above the diagonal blocks stays zero
+  // G above the diagonal blocks stays zero, and so do the row-sum partials
+  // of the blocks above the diagonal (never written)
   for (int i = tid; i < C * LDP; i += kThreads) sm.G[i] = 0.f;
+  for (int i = tid; i < 4 * C; i += kThreads) sm.rsum[i] = 0.f;
 
   // start sums: P tiles (rows 16t+4j+i, column col), m, n
   f32x4 P[NST];
@@ -192,12 +194,22 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
             for (int k0 = 0; k0 < D; k0 += 4)
               acc = mma(sm.Qr[(16 * bi + c16) * LDK + k0 + j], sm.Kr[(16 * bj + c16) * LDK + k0 + j], acc);
           }
-          // acc[i] = (Q K^T)[16bi + 4j + i][16bj + c16]
+          // acc[i] = (Q K^T)[16bi + 4j + i][16bj + c16]; its row sums over
+          // the tile's 16 columns (the lanes of group j) go to rsum[bj]
+          float rs[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int R = 16 * bi + 4 * j + i, Sc = 16 * bj + c16;
-            sm.G[R * LDP + Sc] = R >= Sc ? acc[i] : 0.f;
+            const float g = R >= Sc ? acc[i] : 0.f;
+            sm.G[R * LDP + Sc] = g;
+            rs[i] = g;
           }
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rs[i] += __shfl_xor(rs[i], off, 64);
+          if (c16 < 4)
+            sm.rsum[bj * C + 16 * bi + 4 * j + c16] = c16 == 0 ? rs[0] : c16 == 1 ? rs[1] : c16 == 2 ? rs[2] : rs[3];
         }
       }
     }
@@ -239,27 +251,28 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
         PQ[bi] = acc;  // (Q P)[16bi + 4j + i][col]
       }
     }
-    if (w == 0) {
+    {
+      // m . q_t over this wave's quarter of the columns (token l)
+      constexpr int QW = D / 4;
+      const float *qrow = &sm.Qr[l * LDK + QW * w];
+      const float *mrow = &sm.msum[QW * w];
       float d = 0.f;
-#pragma unroll 8
-      for (int c = 0; c < D; ++c) d += sm.msum[c] * sm.Qr[l * LDK + c];
-      sm.md[l] = d;
+#pragma unroll
+      for (int c = 0; c < QW; c += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(qrow + c);
+        const f32x4 m = *reinterpret_cast<const f32x4 *>(mrow + c);
+        d += x[0] * m[0] + x[1] * m[1] + x[2] * m[2] + x[3] * m[3];
+      }
+      sm.mdp[w * C + l] = d;
     }
     lds_barrier();
 
-    // ---- m_t . q_t (row sums of lower(Q K^T)); m_t for this block's columns --
+    // ---- m_t . q_t = m . q_t + row sums of lower(Q K^T) -----------------------
     if (w == 0) {
-      float rs = sm.md[l];
-#pragma unroll 8
-      for (int c = 0; c < C; ++c) rs += sm.G[l * LDP + c];
+      float rs = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rs += sm.mdp[u * C + l] + sm.rsum[u * C + l];
       sm.mq[l] = rs;
-    } else if (w == 1) {
-      // one column per lane: running key sums over the chunk's tokens
-      float run = sm.msum[nb * DVB + l];
-      for (int t = 0; t < C; ++t) {
-        run += sm.Kr[t * LDK + nb * DVB + l];
-        sm.cm[t * LDC + l] = run;
-      }
     }
     lds_barrier();
 
@@ -269,6 +282,22 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) Kc[mt][i] = sm.Kr[(16 * mt + 4 * j + i) * LDK + col];
+    // m_t for this lane's column: the chunk-start m plus running key sums, on
+    // the MFMA with a lower ones mask per diagonal block and the block
+    // totals (row 15 of each block, held by lane group 3) carried
+    f32x4 cmv[4];
+    {
+      float carry = sm.msum[col];
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a = mma(c16 >= 4 * j + i ? 1.f : 0.f, Kc[bi][i], a);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cmv[bi][i] = carry + a[i];
+        carry += __shfl(a[3], 48 + c16, 64);
+      }
+    }
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
       f32x4 acc = PQ[bi];
@@ -286,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
         if (r < n) {
           const float nt = n0 + (float)(r + 1);
           const float inv = 1.f / nt;
-          const float sq = PQ[bi][i] * inv - (sm.cm[r * LDC + cl] * inv) * (sm.mq[r] * inv);
+          const float sq = PQ[bi][i] * inv - (cmv[bi][i] * inv) * (sm.mq[r] * inv);
           const float qc = sm.Qr[r * LDK + col] - sm.lam[r] * sq;
           const int64_t idx = ((tok0 + r) * H + h) * (int64_t)D + col;
           if constexpr (OUT_BF16) {
@@ -331,15 +360,25 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
 #pragma unroll
       for (int t = 0; t < NST; ++t) P[t] += Pc[t];
     }
+    {
+      // the chunk's key sums: thread tid sums a 1 / (kThreads / D) share of
+      // the tokens for column tid % D
+      constexpr int TP = C * D / kThreads;
+      const int c = tid % D, part = tid / D;
+      float a = 0.f;
+#pragma unroll 8
+      for (int t = 0; t < TP; ++t) a += sm.Kr[(part * TP + t) * LDK + c];
+      sm.kp[tid] = a;
+    }
     lds_barrier();  // every read of this chunk's K, Q, m is done
     if (tid < D) {
       float a = 0.f;
-      for (int t = 0; t < C; ++t) a += sm.Kr[t * LDK + tid];
+#pragma unroll
+      for (int u = 0; u < kThreads / D; ++u) a += sm.kp[u * D + tid];
       sm.msum[tid] += a;
     }
     n0 += (float)n;
-    lds_barrier();
-    stage();
+    stage();  // writes K, Q, lambda only: no reader of them is left in this chunk
   }
 
   if (ccq_out) {
