@@ -21,7 +21,11 @@
 //   P += K^T K (summed over the chunk first, then added: two-level sums)
 // Mapping as the fp32 prefill kernel: one workgroup of 4 waves per
 // (sequence, head, 64 columns), each wave owning 16 columns of P in MFMA
-// accumulator tiles, every contraction on the fp32 MFMA.  The columns of
+// accumulator tiles.  Every contraction runs on the MFMA: for bf16 inputs
+// Q K^T and K^T K on the bf16 MFMA (exact products), Q P with P split into
+// bf16 hi + lo, and the fp32 products (lower(Q K^T) K) on the fp32 MFMA;
+// for fp32 inputs all on the fp32 MFMA.  The running key sums m_t come from
+// the MFMA too (a lower ones mask per diagonal block).  The columns of
 // q_clean follow the columns of P; both workgroups of a (sequence, head)
 // keep the whole m.  Output: q_clean as fp32, or as a bf16 hi / lo pair
 // (q_clean = hi + lo to 2^-17), for the bf16 read.
