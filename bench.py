@@ -215,13 +215,24 @@ def bench_decode(args, torch, kla, workloads):
     it = iter(range(len(steps)))
 
     def one():
-        st = steps[next(it)]
+        st = steps[next(it) % len(steps)]
         kla.kla_decode_step(st["q"], st["k"], st["v"], st["alpha"], st["eta"], state,
                             eps=wl["eps"], o=o)
 
     wall, ev_ms = time_launches(one, len(steps), stream)
     state_bytes = 2 * N * H * d * d * 4
-    return dict(N=N, H=H, d=d, steps=len(steps), wall=wall, ev_ms=ev_ms, state_bytes=state_bytes)
+    # Successive steps on one 268 MB state let the GPU's 256 MB last-level
+    # cache serve part of it.  The same step after a read sweep over 1 GiB
+    # (which leaves none of the state cached): (sweep + step) - sweep.
+    sweep = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    red = torch.empty((), dtype=torch.float32, device=dev)
+    n_sw = 16
+    it = iter(range(2 * n_sw))
+    both = time_launches(lambda: (torch.amax(sweep, dim=0, out=red), one()), n_sw, stream)[1]
+    only = time_launches(lambda: torch.amax(sweep, dim=0, out=red), n_sw, stream)[1]
+    del sweep
+    return dict(N=N, H=H, d=d, steps=len(steps), wall=wall, ev_ms=ev_ms, state_bytes=state_bytes,
+                swept_ms=both - only)
 
 
 def bench_long(args, torch, kla, workloads, n_splits=3, launches=20):
@@ -584,6 +595,9 @@ def main():
                          "unit": "GB/s", "frac": round(dgbs / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic(DECODE_KERNEL), "kernel": DECODE_KERNEL, "avg_launch_us": round(dec["ev_ms"] * 1e3, 2),
                          "algorithmic_bytes_per_launch": dec["state_bytes"]},
+            "us_per_step_after_cache_sweep": round(dec["swept_ms"] * 1e3, 2),
+            "frac_after_cache_sweep": round(dec["state_bytes"] / (dec["swept_ms"] * 1e-3) / 1e9
+                                            / HBM_PEAK_GBS, 4),
         }
     if not args.skip_long:
         out["long_context"] = bench_long(args, torch, kla, workloads)

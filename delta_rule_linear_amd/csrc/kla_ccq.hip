@@ -399,14 +399,17 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
 }
 
 // One decode token: the sums take the new key, then q_clean (fp32) for the
-// read.  One workgroup of 256 threads per (sequence, head); thread (row
+// read.  One workgroup of 512 threads per (sequence, head); thread (row
 // group, column group) holds rows rg + NRG i, columns 4 cq .. 4 cq + 3 of P.
+// The updated P goes out with non-temporal stores (read again only by the
+// next step).
+constexpr int kDecThreads = 512;
 template <typename E, int D>
-__global__ __launch_bounds__(kThreads) void ccq_decode_kernel(
+__global__ __launch_bounds__(kDecThreads) void ccq_decode_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const float *__restrict__ lambda,
     float *__restrict__ ccq_state, float *__restrict__ qc_out) {
-  constexpr int NQ = D / 4, NRG = kThreads / NQ, RPT = D / NRG;
-  static_assert(NQ * NRG == kThreads && RPT * NRG == D, "tiling");
+  constexpr int NQ = D / 4, NRG = kDecThreads / NQ, RPT = D / NRG;
+  static_assert(NQ * NRG == kDecThreads && RPT * NRG == D, "tiling");
   constexpr int64_t REC = (int64_t)D * D + D + 4;
   __shared__ float sq[D], sk[D], sm_m[D], pr[NRG][D], red[2];
   const int64_t sh = blockIdx.x;
@@ -430,7 +433,8 @@ __global__ __launch_bounds__(kThreads) void ccq_decode_kernel(
     const float kr = sk[r], qr = sq[r];
     p[i].x += kr * kc.x; p[i].y += kr * kc.y; p[i].z += kr * kc.z; p[i].w += kr * kc.w;
     acc.x += p[i].x * qr; acc.y += p[i].y * qr; acc.z += p[i].z * qr; acc.w += p[i].w * qr;
-    *reinterpret_cast<float4 *>(rec + r * D + 4 * cq) = p[i];
+    __builtin_nontemporal_store(f32x4{p[i].x, p[i].y, p[i].z, p[i].w},
+                                reinterpret_cast<f32x4 *>(rec + r * D + 4 * cq));
   }
   *reinterpret_cast<float4 *>(&pr[rg][4 * cq]) = acc;
   if (t < 64) {
@@ -494,7 +498,7 @@ hipError_t launch_ccq_query(const CcqArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_ccq_decode(const CcqArgs &a, hipStream_t st) {
-  const dim3 g((unsigned)((int64_t)a.n_seqs * a.H)), b(kThreads);
+  const dim3 g((unsigned)((int64_t)a.n_seqs * a.H)), b(kDecThreads);
   float *qc = static_cast<float *>(a.qh);
   if (a.bf16_inputs) {
     if (a.D == 128)

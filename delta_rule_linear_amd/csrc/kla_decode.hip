@@ -16,9 +16,11 @@
 // "Metodologia e Estrutura") row r of the state decays by a[r]:
 //   x = S^T (a o k),  y = S^T (a o q),  e = v - x,  o = y + beta (k.q) e,
 //   S_new = Diag(a) S + beta k e^T.
-// The kernel is bound by HBM bandwidth (0.75 flop/byte): one workgroup per
-// (sequence, head), each thread holds RPT rows x 4 columns of the state in
-// registers between the read and the write.
+// The kernel is bound by HBM bandwidth (0.75 flop/byte): one workgroup of
+// 512 threads per (sequence, head), each thread holds RPT rows x 4 columns of
+// the state in registers between the read and the write.  The new state goes
+// out with non-temporal stores (it is read again only by the next step, after
+// the whole state has streamed through the caches).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,7 +29,8 @@
 namespace kla {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 __device__ inline float to_f32(float x) { return x; }
 __device__ inline float to_f32(__bf16 x) { return static_cast<float>(x); }
@@ -113,12 +116,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   for (int i = 0; i < RPT; ++i) {
     const float bk = beta * sk[rg + NRG * i];
     const float ar = CH ? sa[rg + NRG * i] : a;
-    float4 r;
-    r.x = ar * s[i].x + bk * e4.x;
-    r.y = ar * s[i].y + bk * e4.y;
-    r.z = ar * s[i].z + bk * e4.z;
-    r.w = ar * s[i].w + bk * e4.w;
-    *reinterpret_cast<float4 *>(Sg + (rg + NRG * i) * D + 4 * cq) = r;
+    const f32x4v r = {ar * s[i].x + bk * e4.x, ar * s[i].y + bk * e4.y, ar * s[i].z + bk * e4.z,
+                      ar * s[i].w + bk * e4.w};
+    __builtin_nontemporal_store(r, reinterpret_cast<f32x4v *>(Sg + (rg + NRG * i) * D + 4 * cq));
   }
 }
 
