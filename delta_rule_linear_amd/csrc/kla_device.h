@@ -157,6 +157,11 @@ __device__ inline float buf_ld4(rsrc_t r, uint32_t off) {
 __device__ inline void buf_st16(rsrc_t r, uint32_t off, f32x4 x) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)off, 0, 0);
 }
+// Non-temporal (cache policy nt): for outputs written once and not read back
+// by the kernel, so they do not displace its inputs from the caches.
+__device__ inline void buf_st16_nt(rsrc_t r, uint32_t off, f32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)off, 0, 2);
+}
 __device__ inline void buf_st4(rsrc_t r, uint32_t off, float x) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)off, 0, 0);
 }

@@ -1025,7 +1025,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
         const rsrc_t ro = make_rsrc(wk.out ? o + tok0 * H * (int64_t)D : o, wk.out ? (int64_t)n * H * D * 4 : 0);
 #pragma unroll
         for (int bi = 0; bi < 4; ++bi)  // token 16bi + c16, dv 16w + 4j..+3; rows past the end are dropped
-          buf_st16(ro, (uint32_t)(((16 * bi + c16) * H + h) * D + nb * DVB + 16 * w + 4 * j) * 4, QS[bi]);
+          buf_st16_nt(ro, (uint32_t)(((16 * bi + c16) * H + h) * D + nb * DVB + 16 * w + 4 * j) * 4, QS[bi]);
       }
       // S' = 2^{g2_last} S + K^T Diag(2^{g2_last - g2}) Delta
 #pragma unroll
