@@ -422,39 +422,24 @@ kla_status kla_decode_step_ccq(const void *q, const void *k, const void *v, cons
   for (const Range &in : {rq, rk, rv, ra, re, rl})
     if (overlap(rws, in)) return KLA_ERR_INVALID_ARG;
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  kla::CcqArgs c;
-  c.q = q;
-  c.k = k;
-  c.lambda = lambda;
-  c.cu_seqlens = nullptr;
-  c.n_seqs = n_seqs;
-  c.seq_len_dense = 1;
-  c.H = H;
-  c.D = dk;
-  c.bf16_inputs = dtype == KLA_BF16;
-  c.ccq_in = nullptr;
-  c.ccq_out = ccq_state;
-  c.qh = workspace;
-  c.ql = nullptr;
-  hipError_t e = kla::launch_ccq_decode(c, st);
-
-  kla::DecodeArgs a;
-  a.q = workspace;  // q_clean, fp32
+  kla::CcqDecodeArgs a;
+  a.q = q;
   a.k = k;
   a.v = v;
+  a.lambda = lambda;
   a.alpha = alpha;
   a.eta = eta;
+  a.ccq_state = ccq_state;
   a.state = state;
   a.o = o;
+  a.q_clean = static_cast<float *>(workspace);
   a.n_seqs = n_seqs;
   a.H = H;
   a.D = dk;
   a.eps = eps;
   a.beta_direct = beta_mode == KLA_BETA_DIRECT;
-  a.q_is_f32 = 1;
-  if (e == hipSuccess)
-    e = dtype == KLA_BF16 ? kla::launch_decode_bf16(a, st) : kla::launch_decode_f32(a, st);
+  a.bf16_inputs = dtype == KLA_BF16;
+  const hipError_t e = kla::launch_ccq_decode_step(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KLA_OK : KLA_ERR_HIP;
 }
 

@@ -398,45 +398,61 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
   }
 }
 
-// One decode token: the sums take the new key, then q_clean (fp32) for the
-// read.  One workgroup of 512 threads per (sequence, head); thread (row
-// group, column group) holds rows rg + NRG i, columns 4 cq .. 4 cq + 3 of P.
-// The updated P goes out with non-temporal stores (read again only by the
-// next step).
+// One decode token, fused: the sums take the new key, q_clean is formed, and
+// the KLA decode step reads with it (x = S^T k, y = S^T q_clean from one read
+// of S; e = v - alpha x; o = alpha y + beta (k . q_clean) e; S <- alpha S +
+// beta k e^T).  One workgroup of 512 threads per (sequence, head); thread
+// (row group, column group) holds rows rg + NRG i, columns 4 cq .. 4 cq + 3 of
+// both P and S, loaded together at the start.  Both go back with
+// non-temporal stores (read again only by the next step).  q_clean is also
+// written to qc_out.
 constexpr int kDecThreads = 512;
 template <typename E, int D>
-__global__ __launch_bounds__(kDecThreads) void ccq_decode_kernel(
-    const E *__restrict__ q, const E *__restrict__ k, const float *__restrict__ lambda,
-    float *__restrict__ ccq_state, float *__restrict__ qc_out) {
+__global__ __launch_bounds__(kDecThreads) void ccq_decode_step_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
+    const float *__restrict__ lambda, const float *__restrict__ alpha, const float *__restrict__ eta,
+    float *__restrict__ ccq_state, float *__restrict__ state, float *__restrict__ o,
+    float *__restrict__ qc_out, float eps, int beta_direct) {
   constexpr int NQ = D / 4, NRG = kDecThreads / NQ, RPT = D / NRG;
   static_assert(NQ * NRG == kDecThreads && RPT * NRG == D, "tiling");
   constexpr int64_t REC = (int64_t)D * D + D + 4;
-  __shared__ float sq[D], sk[D], sm_m[D], pr[NRG][D], red[2];
+  __shared__ float sq[D], sk[D], sv[D], sqc[D], se[D], sm_m[D], red[2];
+  __shared__ float px[NRG][D], py[NRG][D];
   const int64_t sh = blockIdx.x;
   const int t = threadIdx.x, cq = t % NQ, rg = t / NQ;
   float *rec = ccq_state + sh * REC;
-  float4 p[RPT];
+  float *Sg = state + sh * (int64_t)(D * D);
+  float4 p[RPT], s[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) p[i] = *reinterpret_cast<const float4 *>(rec + (rg + NRG * i) * D + 4 * cq);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) s[i] = *reinterpret_cast<const float4 *>(Sg + (rg + NRG * i) * D + 4 * cq);
   if (t < D) {
     sq[t] = static_cast<float>(q[sh * D + t]);
     sk[t] = static_cast<float>(k[sh * D + t]);
+    sv[t] = static_cast<float>(v[sh * D + t]);
   }
+  const float a = alpha ? alpha[sh] : 1.f;
+  const float et = eta[sh];
   __syncthreads();
-  // P += k k^T; partial (P q) over this thread's rows for its 4 columns
-  // (P is symmetric: (P q)_c = sum_r P[r][c] q[r])
-  const float4 kc = *reinterpret_cast<const float4 *>(&sk[4 * cq]);
-  float4 acc = {0.f, 0.f, 0.f, 0.f};
+
+  // ---- sums: P += k k^T, m += k, n += 1; then q_clean -------------------------
+  // partial (P q) over this thread's rows for its 4 columns (P is symmetric:
+  // (P q)_c = sum_r P[r][c] q[r])
+  {
+    const float4 kc = *reinterpret_cast<const float4 *>(&sk[4 * cq]);
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = rg + NRG * i;
-    const float kr = sk[r], qr = sq[r];
-    p[i].x += kr * kc.x; p[i].y += kr * kc.y; p[i].z += kr * kc.z; p[i].w += kr * kc.w;
-    acc.x += p[i].x * qr; acc.y += p[i].y * qr; acc.z += p[i].z * qr; acc.w += p[i].w * qr;
-    __builtin_nontemporal_store(f32x4{p[i].x, p[i].y, p[i].z, p[i].w},
-                                reinterpret_cast<f32x4 *>(rec + r * D + 4 * cq));
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rg + NRG * i;
+      const float kr = sk[r], qr = sq[r];
+      p[i].x += kr * kc.x; p[i].y += kr * kc.y; p[i].z += kr * kc.z; p[i].w += kr * kc.w;
+      acc.x += p[i].x * qr; acc.y += p[i].y * qr; acc.z += p[i].z * qr; acc.w += p[i].w * qr;
+      __builtin_nontemporal_store(f32x4{p[i].x, p[i].y, p[i].z, p[i].w},
+                                  reinterpret_cast<f32x4 *>(rec + r * D + 4 * cq));
+    }
+    *reinterpret_cast<float4 *>(&px[rg][4 * cq]) = acc;
   }
-  *reinterpret_cast<float4 *>(&pr[rg][4 * cq]) = acc;
   if (t < 64) {
     // m += k, n += 1 and m . q (wave 0)
     float mq = 0.f;
@@ -459,11 +475,64 @@ __global__ __launch_bounds__(kDecThreads) void ccq_decode_kernel(
   if (t < D) {
     float pq = 0.f;
 #pragma unroll
-    for (int r = 0; r < NRG; ++r) pq += pr[r][t];
+    for (int r = 0; r < NRG; ++r) pq += px[r][t];
     const float inv = 1.f / red[1];
     const float m = sm_m[t];
     const float sg = pq * inv - (m * inv) * (red[0] * inv);
-    qc_out[sh * D + t] = sq[t] - lambda[sh] * sg;
+    const float qc = sq[t] - lambda[sh] * sg;
+    sqc[t] = qc;
+    qc_out[sh * D + t] = qc;
+  }
+  __syncthreads();  // q_clean complete; every read of px done
+
+  // ---- KLA decode step with q_clean ------------------------------------------
+  // k.k and k.q_clean: every wave reduces its own copy (fixed order)
+  float kk = 0.f, kq = 0.f;
+  {
+    const int l = t & 63;
+#pragma unroll
+    for (int i = l; i < D; i += 64) {
+      kk += sk[i] * sk[i];
+      kq += sk[i] * sqc[i];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      kk += __shfl_xor(kk, off, 64);
+      kq += __shfl_xor(kq, off, 64);
+    }
+  }
+  const float beta = beta_direct ? et : et / (kk + eps);
+  {
+    float4 xs = {0.f, 0.f, 0.f, 0.f}, ys = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const float kr = sk[rg + NRG * i], qr = sqc[rg + NRG * i];
+      xs.x += s[i].x * kr; xs.y += s[i].y * kr; xs.z += s[i].z * kr; xs.w += s[i].w * kr;
+      ys.x += s[i].x * qr; ys.y += s[i].y * qr; ys.z += s[i].z * qr; ys.w += s[i].w * qr;
+    }
+    *reinterpret_cast<float4 *>(&px[rg][4 * cq]) = xs;
+    *reinterpret_cast<float4 *>(&py[rg][4 * cq]) = ys;
+  }
+  __syncthreads();
+  if (t < D) {
+    float x = 0.f, y = 0.f;
+#pragma unroll
+    for (int r = 0; r < NRG; ++r) {
+      x += px[r][t];
+      y += py[r][t];
+    }
+    const float e = sv[t] - a * x;
+    se[t] = e;
+    o[sh * D + t] = a * y + beta * kq * e;
+  }
+  __syncthreads();
+  const float4 e4 = *reinterpret_cast<const float4 *>(&se[4 * cq]);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const float bk = beta * sk[rg + NRG * i];
+    const f32x4 r = {a * s[i].x + bk * e4.x, a * s[i].y + bk * e4.y, a * s[i].z + bk * e4.z,
+                     a * s[i].w + bk * e4.w};
+    __builtin_nontemporal_store(r, reinterpret_cast<f32x4 *>(Sg + (rg + NRG * i) * D + 4 * cq));
   }
 }
 
@@ -497,24 +566,18 @@ hipError_t launch_ccq_query(const CcqArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_ccq_decode(const CcqArgs &a, hipStream_t st) {
+hipError_t launch_ccq_decode_step(const CcqDecodeArgs &a, hipStream_t st) {
   const dim3 g((unsigned)((int64_t)a.n_seqs * a.H)), b(kDecThreads);
-  float *qc = static_cast<float *>(a.qh);
+#define KLA_CCQ_DEC_LAUNCH(E, DD)                                                                   \
+  hipLaunchKernelGGL((ccq_decode_step_kernel<E, DD>), g, b, 0, st, static_cast<const E *>(a.q),     \
+                     static_cast<const E *>(a.k), static_cast<const E *>(a.v), a.lambda, a.alpha,    \
+                     a.eta, a.ccq_state, a.state, a.o, a.q_clean, a.eps, a.beta_direct)
   if (a.bf16_inputs) {
-    if (a.D == 128)
-      hipLaunchKernelGGL((ccq_decode_kernel<__bf16, 128>), g, b, 0, st, static_cast<const __bf16 *>(a.q),
-                         static_cast<const __bf16 *>(a.k), a.lambda, a.ccq_out, qc);
-    else
-      hipLaunchKernelGGL((ccq_decode_kernel<__bf16, 64>), g, b, 0, st, static_cast<const __bf16 *>(a.q),
-                         static_cast<const __bf16 *>(a.k), a.lambda, a.ccq_out, qc);
+    if (a.D == 128) KLA_CCQ_DEC_LAUNCH(__bf16, 128); else KLA_CCQ_DEC_LAUNCH(__bf16, 64);
   } else {
-    if (a.D == 128)
-      hipLaunchKernelGGL((ccq_decode_kernel<float, 128>), g, b, 0, st, static_cast<const float *>(a.q),
-                         static_cast<const float *>(a.k), a.lambda, a.ccq_out, qc);
-    else
-      hipLaunchKernelGGL((ccq_decode_kernel<float, 64>), g, b, 0, st, static_cast<const float *>(a.q),
-                         static_cast<const float *>(a.k), a.lambda, a.ccq_out, qc);
+    if (a.D == 128) KLA_CCQ_DEC_LAUNCH(float, 128); else KLA_CCQ_DEC_LAUNCH(float, 64);
   }
+#undef KLA_CCQ_DEC_LAUNCH
   return hipGetLastError();
 }
 

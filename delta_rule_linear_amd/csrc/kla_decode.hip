@@ -35,9 +35,9 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 __device__ inline float to_f32(float x) { return x; }
 __device__ inline float to_f32(__bf16 x) { return static_cast<float>(x); }
 
-template <typename E, int D, bool CH, typename EQ = E>
+template <typename E, int D, bool CH>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
-    const EQ *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ eta, float *__restrict__ state,
     float *__restrict__ o, float eps, int beta_direct) {
   constexpr int NQ = D / 4;              // float4 column groups per row
@@ -127,13 +127,6 @@ hipError_t launch(const DecodeArgs &a, hipStream_t st) {
   const dim3 grid((unsigned)((int64_t)a.n_seqs * a.H)), block(kThreads);
   const E *q = static_cast<const E *>(a.q), *k = static_cast<const E *>(a.k),
           *v = static_cast<const E *>(a.v);
-  if (a.q_is_f32) {  // the cleaned query of the curvature-conditioned read
-    const float *qf = static_cast<const float *>(a.q);
-    auto kf = a.D == 128 ? decode_kernel<E, 128, false, float> : decode_kernel<E, 64, false, float>;
-    hipLaunchKernelGGL(kf, grid, block, 0, st, qf, k, v, a.alpha, a.eta, a.state, a.o, a.eps,
-                       a.beta_direct);
-    return hipGetLastError();
-  }
   auto kern = a.D == 128 ? (a.channel_decay ? decode_kernel<E, 128, true> : decode_kernel<E, 128, false>)
                         : (a.channel_decay ? decode_kernel<E, 64, true> : decode_kernel<E, 64, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, st, q, k, v, a.alpha, a.eta, a.state, a.o, a.eps,

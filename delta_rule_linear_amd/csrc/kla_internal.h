@@ -34,7 +34,6 @@ struct DecodeArgs {
   float eps;
   int beta_direct;            // 1: beta = eta; 0: beta = eta / (|k|^2 + eps)
   int channel_decay = 0;      // 1: alpha [n_seqs, H, D], one decay per key channel
-  int q_is_f32 = 0;           // 1: q is fp32 whatever the k, v type (the cleaned query)
 };
 
 // Curvature-conditioned read: query cleaning before the KLA read.
@@ -47,8 +46,23 @@ struct CcqArgs {
   int32_t H, D;
   bool bf16_inputs;
   const float *ccq_in;        // prefill: start sums or nullptr
-  float *ccq_out;             // prefill: end sums or nullptr; decode: the sums, in place
-  void *qh, *ql;              // cleaned query: fp32 in qh, or bf16 hi / lo planes (prefill, bf16)
+  float *ccq_out;             // end sums or nullptr
+  void *qh, *ql;              // cleaned query: fp32 in qh, or bf16 hi / lo planes (bf16)
+};
+
+// Curvature-conditioned decode step, one kernel: the sums take the new key,
+// q_clean is formed (and written to q_clean), and the KLA decode step reads
+// with it.
+struct CcqDecodeArgs {
+  const void *q, *k, *v;               // [n_seqs, H, D], bf16 or fp32
+  const float *lambda, *alpha, *eta;   // [n_seqs, H]; alpha nullable (alpha = 1)
+  float *ccq_state;                    // the sums, updated in place
+  float *state, *o;                    // fp32 state (in place), o [n_seqs, H, D]
+  float *q_clean;                      // [n_seqs, H, D] fp32
+  int32_t n_seqs, H, D;
+  float eps;
+  int beta_direct;
+  bool bf16_inputs;
 };
 
 // Backward of the prefill (gradients of o and of the final state).
@@ -88,10 +102,10 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_split_identity(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_split_scan(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
-// CCQ: the prefill pre-pass (q_clean for every token), the decode step's
-// cleaning (sums updated in place, q_clean fp32), and o += o2.
+// CCQ: the prefill pre-pass (q_clean for every token), the fused decode
+// step, and o += o2.
 hipError_t launch_ccq_query(const CcqArgs &a, hipStream_t s);
-hipError_t launch_ccq_decode(const CcqArgs &a, hipStream_t s);
+hipError_t launch_ccq_decode_step(const CcqDecodeArgs &a, hipStream_t s);
 hipError_t launch_add(float *o, const float *o2, int64_t n, hipStream_t s);
 // Per-channel decay prefill (alpha [total_tok, H, D]); whole sequences only.
 hipError_t launch_prefill_kda(const PrefillArgs &a, bool bf16_inputs, hipStream_t s);
