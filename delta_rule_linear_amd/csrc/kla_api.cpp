@@ -372,6 +372,7 @@ kla_status kla_fwd_chunked_ccq(const void *q, const void *k, const void *v, cons
     // with the lo part first (no end state, so an in-place start state is
     // still intact), then with the hi part, and add.
     float *o_lo = reinterpret_cast<float *>(ws + 2 * round_up((size_t)th * dk * 2));
+    a.o_write_back = 1;  // both outputs are read back by the sum
     a.q = c.ql;
     a.o = o_lo;
     a.final_state = nullptr;

@@ -24,6 +24,9 @@ struct PrefillArgs {
   float *ws_a = nullptr, *ws_b = nullptr;  // [n_seqs, H, P-1, D, D]
   const float *ws_s = nullptr;             // [n_seqs, H, P, D, D]
   float *ws_ckpt = nullptr;                // states-only pass: chunk-start state slots
+  // bf16 prefill: 1 stores o write-back (for a caller that reads it straight
+  // back); 0 stores it non-temporal (the output is not read by this work)
+  int o_write_back = 0;
 };
 
 struct DecodeArgs {

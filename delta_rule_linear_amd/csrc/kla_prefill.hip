@@ -137,6 +137,7 @@ struct SegParams {
   float *ws_a, *ws_b;   // [n_seqs, H, P-1, D, D]
   const float *ws_s;    // [n_seqs, H, P, D, D]
   float *ckpt;          // mode 3: chunk-start state slots
+  int o_wb;             // 1: o with write-back stores (read back right away), else non-temporal
 };
 struct Work {
   int h, nb, vb;        // head, state column block, V column block (-1: V read as zero)
@@ -1025,7 +1026,13 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
         const rsrc_t ro = make_rsrc(wk.out ? o + tok0 * H * (int64_t)D : o, wk.out ? (int64_t)n * H * D * 4 : 0);
 #pragma unroll
         for (int bi = 0; bi < 4; ++bi)  // token 16bi + c16, dv 16w + 4j..+3; rows past the end are dropped
-          buf_st16_nt(ro, (uint32_t)(((16 * bi + c16) * H + h) * D + nb * DVB + 16 * w + 4 * j) * 4, QS[bi]);
+        {
+          const uint32_t off = (uint32_t)(((16 * bi + c16) * H + h) * D + nb * DVB + 16 * w + 4 * j) * 4;
+          if (sp.o_wb)
+            buf_st16(ro, off, QS[bi]);
+          else
+            buf_st16_nt(ro, off, QS[bi]);
+        }
       }
       // S' = 2^{g2_last} S + K^T Diag(2^{g2_last - g2}) Delta
 #pragma unroll
@@ -1118,6 +1125,7 @@ inline SegParams seg_of(const PrefillArgs &a) {
   sp.ws_b = a.ws_b;
   sp.ws_s = a.ws_s;
   sp.ckpt = a.ws_ckpt;
+  sp.o_wb = a.o_write_back;
   return sp;
 }
 
