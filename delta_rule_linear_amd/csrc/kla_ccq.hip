@@ -311,26 +311,31 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
         for (int i = 0; i < 4; ++i) acc = mma(sm.G[(16 * bi + c16) * LDP + 16 * mt + 4 * j + i], Kc[mt][i], acc);
       PQ[bi] = acc;
     }
+    {
+      // range-checked stores: rows past the chunk's n tokens are dropped
+      constexpr int OSZ = OUT_BF16 ? 2 : 4;
+      const int64_t base = tok0 * H * (int64_t)D, bytes = (int64_t)n * H * D * OSZ;
+      const rsrc_t rh = make_rsrc(static_cast<char *>(qh) + base * OSZ, bytes);
+      const rsrc_t rl = make_rsrc(OUT_BF16 ? static_cast<char *>(ql) + base * OSZ : static_cast<char *>(qh), bytes);
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
+      for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * bi + 4 * j + i;
-        if (r < n) {
-          const float nt = n0 + (float)(r + 1);
-          const float inv = 1.f / nt;
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * bi + 4 * j + i;
+          const float inv = 1.f / (n0 + (float)(r + 1));
           const float sq = PQ[bi][i] * inv - (cmv[bi][i] * inv) * (sm.mq[r] * inv);
           const float qc = sm.Qr[r * LDK + col] - sm.lam[r] * sq;
-          const int64_t idx = ((tok0 + r) * H + h) * (int64_t)D + col;
+          const uint32_t off = (uint32_t)(((r * H + h) * D + col) * OSZ);
           if constexpr (OUT_BF16) {
             const __bf16 hi = static_cast<__bf16>(qc);
-            static_cast<__bf16 *>(qh)[idx] = hi;
-            static_cast<__bf16 *>(ql)[idx] = static_cast<__bf16>(qc - static_cast<float>(hi));
+            const __bf16 lo = static_cast<__bf16>(qc - static_cast<float>(hi));
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hi), rh, (int)off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, lo), rl, (int)off, 0, 0);
           } else {
-            static_cast<float *>(qh)[idx] = qc;
+            buf_st4(rh, off, qc);
           }
         }
-      }
+    }
 
     // ---- P += K^T K (the chunk's sum first), m, n -----------------------------
     {
