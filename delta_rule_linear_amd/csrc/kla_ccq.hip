@@ -1,5 +1,6 @@
 // Curvature-conditioned read (CCQ) for the KLA path on gfx950: the query
-// cleaning that runs before the prefill / decode read.
+// cleaning that runs before the prefill read, and the decode step with its
+// cleaning fused in.
 //
 // "Don't Read Everything: A Curvature-Conditioned Query for Linear
 // Attention" (sections "Derivacao Teorica" and "O Mecanismo"): the read uses
