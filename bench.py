@@ -486,19 +486,25 @@ def bench_ccq(args, torch, kla, workloads, launches=50):
     return out
 
 
-def cpu_baseline(pre, oracle):
-    """fp64 reference on the host over the whole layer-shaped prefill."""
+def cpu_baseline(pre, oracle, runs=5):
+    """fp64 reference on the host over the whole layer-shaped prefill, run
+    `runs` times (about 2 s of wall time, some 30 s of CPU time on 16 host
+    threads); the median run is reported."""
     import numpy as np
     inp = pre["inp"]
     B, T, H, d = pre["shape"]
     cu = np.arange(B + 1, dtype=np.int64) * T
-    t0 = time.perf_counter()
-    oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["eta"], cu_seqlens=cu,
-               eps=float(np.float32(inp["eps"])))
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["eta"], cu_seqlens=cu,
+                   eps=float(np.float32(inp["eps"])))
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[runs // 2]
     return dict(value=B * T / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
                 sample=f"whole layer-shaped prefill ({B} seqs x {T} tokens x {H} heads, d={d}), "
-                       f"one run, {dt:.2f} s wall including the fp64 conversion of the inputs",
+                       f"median of {runs} runs ({', '.join(f'{x:.2f}' for x in times)} s wall, each "
+                       f"including the fp64 conversion of the inputs)",
                 seconds=round(dt, 3))
 
 
