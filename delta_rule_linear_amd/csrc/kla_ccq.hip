@@ -200,7 +200,8 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
               acc = mma(sm.Qr[(16 * bi + c16) * LDK + k0 + j], sm.Kr[(16 * bj + c16) * LDK + k0 + j], acc);
           }
           // acc[i] = (Q K^T)[16bi + 4j + i][16bj + c16]; its row sums over
-          // the tile's 16 columns (the lanes of group j) go to rsum[bj]
+          // the tile's 16 columns (the 16 lanes of group j, one DPP row) go to
+          // rsum[bj]
           float rs[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -210,9 +211,7 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
             rs[i] = g;
           }
 #pragma unroll
-          for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rs[i] += __shfl_xor(rs[i], off, 64);
+          for (int i = 0; i < 4; ++i) rs[i] = group_sum<16>(rs[i]);  // DPP within the 16-lane row
           if (c16 < 4)
             sm.rsum[bj * C + 16 * bi + 4 * j + c16] = c16 == 0 ? rs[0] : c16 == 1 ? rs[1] : c16 == 2 ? rs[2] : rs[3];
         }
