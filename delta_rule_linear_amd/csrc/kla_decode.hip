@@ -19,8 +19,8 @@
 // The kernel is bound by HBM bandwidth (0.75 flop/byte): one workgroup of
 // 512 threads per (sequence, head), each thread holds RPT rows x 4 columns of
 // the state in registers between the read and the write.  The new state goes
-// out with non-temporal stores (it is read again only by the next step, after
-// the whole state has streamed through the caches).
+// out with non-temporal stores: nothing reads it before the next step, and
+// the stores then keep the caches for the loads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
