@@ -140,3 +140,37 @@ def test_ccq_decode_after_prefill(kla, d, dtype):
     check(f"ccq decode d={d} {dtype} o (last step)", od.cpu(), ro[last], TOL[dtype])
     check(f"ccq decode d={d} {dtype} S", S.cpu(), rS, TOL[dtype])
     check(f"ccq decode d={d} {dtype} sums", c.cpu(), rc, SUMS_TOL)
+
+
+@pytest.mark.parametrize("d,dtype,beta_mode,no_alpha", [
+    (128, "f32", "direct", True), (64, "bf16", "kaczmarz", True),
+    (128, "bf16", "direct", False), (64, "f32", "kaczmarz", False)])
+def test_ccq_decode_modes_from_empty_sums(kla, d, dtype, beta_mode, no_alpha):
+    """Decode steps of the fused kernel from zero sums (the first key gives
+    n = 1, a zero covariance), against the oracle step by step, for both step
+    rules, with and without decay."""
+    print(f"[case] CCQ decode from empty sums, d={d} {dtype} {beta_mode} "
+          f"{'no alpha' if no_alpha else 'alpha'}", flush=True)
+    N, H, steps = 5, 3, 3
+    inp = workloads.prefill(lengths=[steps] * N, H=H, d=d, dtype=dtype, seed=77)
+    lam = 4.0 * workloads.ccq_gate(78, N * steps, H)
+    dev = "cuda"
+    rng = np.random.default_rng(79)
+    S0 = (0.02 * rng.standard_normal((N, H, d, d))).astype(np.float32)
+    S = torch.from_numpy(S0).to(dev)
+    c = torch.zeros((N, H, kla.kla_ccq_state_floats(d)), dtype=torch.float32, device=dev)
+    rS, rc = S0.astype(np.float64), np.zeros((N, H, kla.kla_ccq_state_floats(d)))
+    eta = inp["eta"] * 0.5 if beta_mode == "direct" else inp["eta"]
+    for t in range(steps):
+        idx = torch.tensor([s * steps + t for s in range(N)])
+        a = None if no_alpha else inp["alpha"][idx]
+        od = kla.kla_decode_step_ccq(*(inp[n][idx].to(dev) for n in ("q", "k", "v")),
+                                     None if a is None else a.to(dev), eta[idx].to(dev),
+                                     lam[idx].to(dev), S, c, eps=inp["eps"], beta_mode=beta_mode)
+        ro, rS, rc = oracle.decode_step_ccq(inp["q"][idx], inp["k"][idx], inp["v"][idx], a, eta[idx],
+                                            lam[idx], rS, rc, eps=float(np.float32(inp["eps"])),
+                                            beta_mode=beta_mode)
+        torch.cuda.synchronize()
+        check(f"ccq decode {d} {dtype} {beta_mode} step {t} o", od.cpu(), ro, TOL[dtype])
+    check(f"ccq decode {d} {dtype} {beta_mode} S", S.cpu(), rS, TOL[dtype])
+    check(f"ccq decode {d} {dtype} {beta_mode} sums", c.cpu(), rc, SUMS_TOL)
