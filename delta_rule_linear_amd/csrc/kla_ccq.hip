@@ -43,14 +43,12 @@ template <typename E, int D>
 struct CcqSmem {
   static constexpr int LDK = D + 4;
   static constexpr int LDP = C + 4;
-  // row pitch of the transposed bf16 keys: 8-byte rows, and rows 8 apart
-  // (the rows one token's 16-byte segments scatter to) on different banks
-  static constexpr int LDT = C + 4;
+  static constexpr int LDB = D + 8;  // row pitch of the bf16 keys
   alignas(16) float Kr[C * LDK];   // keys of the chunk (fp32)
   alignas(16) float Qr[C * LDK];   // queries of the chunk (fp32)
-  // bf16 inputs: the chunk's keys transposed, [feature][token] (exact), the
-  // operands of K^T K on the bf16 MFMA
-  alignas(16) __bf16 Kt[sizeof(E) == 2 ? D * LDT : 8];
+  // bf16 inputs: the chunk's keys as read (exact), row-major; the operands of
+  // K^T K on the bf16 MFMA come from them by transposing reads
+  alignas(16) __bf16 Kb[sizeof(E) == 2 ? C * LDB : 8];
   alignas(16) float G[C * LDP];    // lower(Q K^T), zero above the diagonal
   alignas(16) float msum[D];       // m at the chunk start (all columns)
   alignas(16) float mdp[4 * C];    // m . q_t, one partial per wave (a quarter of the columns each)
@@ -84,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
   using SM = CcqSmem<E, D>;
   constexpr int NB = D / DVB;
   constexpr int NST = D / 16;
-  constexpr int LDK = SM::LDK, LDP = SM::LDP, LDT = SM::LDT;
+  constexpr int LDK = SM::LDK, LDP = SM::LDP, LDB = SM::LDB;
   constexpr bool BF = sizeof(E) == 2;
   constexpr int SEG_EL = 16 / sizeof(E);
   constexpr int SEG_ROW = D / SEG_EL;
@@ -151,11 +149,7 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
       const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
       seg_to_f32<E>(kreg[u], &sm.Kr[r * LDK + cs * SEG_EL]);
       seg_to_f32<E>(qreg[u], &sm.Qr[r * LDK + cs * SEG_EL]);
-      if constexpr (BF) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, kreg[u]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm.Kt[(cs * SEG_EL + e) * LDT + r] = b[e];
-      }
+      if constexpr (BF) *reinterpret_cast<uint4 *>(&sm.Kb[r * LDB + cs * SEG_EL]) = kreg[u];
     }
     if (w == 0) sm.lam[l] = lreg;
   };
@@ -340,23 +334,30 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
     // ---- P += K^T K (the chunk's sum first), m, n -----------------------------
     {
       f32x4 Pc[NST];
+      // bf16: (K^T K)[16t + 4j + i][col] with A = K^T rows 16t + c16 and B = K^T
+      // row col, both by transposing reads of the row-major keys; lane group j
+      // takes tokens 32kb + 4j .. +3 and 32kb + 16 + 4j .. +3 in both operands
+      // (the same order of the contraction index on both sides)
+      [[maybe_unused]] bf16x8 bk[C / 32];
+      if constexpr (BF) {
+        const __bf16 *pb = &sm.Kb[nb * DVB + 16 * w + 4 * (c16 & 3)];
+#pragma unroll
+        for (int kb = 0; kb < C / 32; ++kb)
+          bk[kb] = __builtin_shufflevector(ld_tr(pb + (32 * kb + 4 * j + (c16 >> 2)) * LDB),
+                                           ld_tr(pb + (32 * kb + 16 + 4 * j + (c16 >> 2)) * LDB),
+                                           0, 1, 2, 3, 4, 5, 6, 7);
+      }
 #pragma unroll
       for (int t = 0; t < NST; ++t) {
         Pc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (BF) {
-          // (K^T K)[16t + 4j + i][col]: A = K^T rows 16t + c16, B = K^T row col,
-          // eight consecutive tokens per lane from the transposed keys
+          const __bf16 *pa = &sm.Kb[16 * t + 4 * (c16 & 3)];
 #pragma unroll
           for (int kb = 0; kb < C / 32; ++kb) {
-            const __bf16 *pa = &sm.Kt[(16 * t + c16) * LDT + 32 * kb + 8 * j];
-            const __bf16 *pb = &sm.Kt[col * LDT + 32 * kb + 8 * j];
-            const bf16x8 a = __builtin_shufflevector(*reinterpret_cast<const bf16x4 *>(pa),
-                                                     *reinterpret_cast<const bf16x4 *>(pa + 4),
+            const bf16x8 a = __builtin_shufflevector(ld_tr(pa + (32 * kb + 4 * j + (c16 >> 2)) * LDB),
+                                                     ld_tr(pa + (32 * kb + 16 + 4 * j + (c16 >> 2)) * LDB),
                                                      0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8 b = __builtin_shufflevector(*reinterpret_cast<const bf16x4 *>(pb),
-                                                     *reinterpret_cast<const bf16x4 *>(pb + 4),
-                                                     0, 1, 2, 3, 4, 5, 6, 7);
-            Pc[t] = mma(a, b, Pc[t]);
+            Pc[t] = mma(a, bk[kb], Pc[t]);
           }
         } else {
 #pragma unroll

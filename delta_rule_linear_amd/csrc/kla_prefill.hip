@@ -101,16 +101,6 @@ __device__ inline bf16x8 lda_perm(const bf16 *row, int j) {
 }
 __device__ inline bf16x4 lda4(const bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
 
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group,
-// lane i receives element i%4 of the 8-byte chunks addressed by lanes
-// 4e + i/4, e = 0..3.  With lane c addressing row (r0 + c/4), columns
-// c0 + 4(c%4) .. +3 of a row-major tile, lane i gets column c0 + i of rows
-// r0 .. r0+3: a transposed 4-element operand.
-__device__ inline bf16x4 ld_tr(const bf16 *p) {
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
-
 __device__ inline void store_split(bf16 *h, bf16 *l, int idx, float x) {
   const bf16 hv = static_cast<bf16>(x);
   h[idx] = hv;
