@@ -44,11 +44,14 @@ struct CcqSmem {
   static constexpr int LDK = D + 4;
   static constexpr int LDP = C + 4;
   static constexpr int LDB = D + 8;  // row pitch of the bf16 keys
-  alignas(16) float Kr[C * LDK];   // keys of the chunk (fp32)
-  alignas(16) float Qr[C * LDK];   // queries of the chunk (fp32)
-  // bf16 inputs: the chunk's keys as read (exact), row-major; the operands of
-  // K^T K on the bf16 MFMA come from them by transposing reads
+  // fp32 inputs: the chunk's keys and queries
+  alignas(16) float Kr[sizeof(E) == 2 ? 4 : C * LDK];
+  alignas(16) float Qr[sizeof(E) == 2 ? 4 : C * LDK];
+  // bf16 inputs: the chunk's keys and queries as read (exact), row-major, the
+  // MFMA operands (K^T K by transposing reads) and converted where an fp32
+  // value is needed
   alignas(16) __bf16 Kb[sizeof(E) == 2 ? C * LDB : 8];
+  alignas(16) __bf16 Qb[sizeof(E) == 2 ? C * LDB : 8];
   alignas(16) float G[C * LDP];    // lower(Q K^T), zero above the diagonal
   alignas(16) float msum[D];       // m at the chunk start (all columns)
   alignas(16) float mdp[4 * C];    // m . q_t, one partial per wave (a quarter of the columns each)
@@ -58,16 +61,8 @@ struct CcqSmem {
   alignas(16) float lam[C];
 };
 
-template <typename E>
-__device__ inline void seg_to_f32(const uint4 &u, float *dst);
-template <>
-__device__ inline void seg_to_f32<__bf16>(const uint4 &u, float *dst) {
-  const bf16x8 b = __builtin_bit_cast(bf16x8, u);
-  *reinterpret_cast<f32x4 *>(dst) = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
-  *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{(float)b[4], (float)b[5], (float)b[6], (float)b[7]};
-}
-template <>
-__device__ inline void seg_to_f32<float>(const uint4 &u, float *dst) {
+// a 16-byte segment of fp32 inputs to LDS
+__device__ inline void seg_to_f32(const uint4 &u, float *dst) {
   *reinterpret_cast<f32x4 *>(dst) =
       f32x4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
 }
@@ -147,22 +142,24 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
 #pragma unroll
     for (int u = 0; u < NSEG; ++u) {
       const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
-      seg_to_f32<E>(kreg[u], &sm.Kr[r * LDK + cs * SEG_EL]);
-      seg_to_f32<E>(qreg[u], &sm.Qr[r * LDK + cs * SEG_EL]);
-      if constexpr (BF) *reinterpret_cast<uint4 *>(&sm.Kb[r * LDB + cs * SEG_EL]) = kreg[u];
+      if constexpr (BF) {
+        *reinterpret_cast<uint4 *>(&sm.Kb[r * LDB + cs * SEG_EL]) = kreg[u];
+        *reinterpret_cast<uint4 *>(&sm.Qb[r * LDB + cs * SEG_EL]) = qreg[u];
+      } else {
+        seg_to_f32(kreg[u], &sm.Kr[r * LDK + cs * SEG_EL]);
+        seg_to_f32(qreg[u], &sm.Qr[r * LDK + cs * SEG_EL]);
+      }
     }
     if (w == 0) sm.lam[l] = lreg;
   };
-  // 8 fp32 values that hold bf16 numbers -> bf16x8 (exact)
-  auto bf8 = [](const float *p) __attribute__((always_inline)) {
-    const f32x4 x = *reinterpret_cast<const f32x4 *>(p), y = *reinterpret_cast<const f32x4 *>(p + 4);
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      r[e] = static_cast<__bf16>(x[e]);
-      r[4 + e] = static_cast<__bf16>(y[e]);
-    }
-    return r;
+  // element (token r, feature c) of the chunk's keys / queries as fp32
+  auto kval = [&](int r, int c) __attribute__((always_inline)) -> float {
+    if constexpr (BF) return static_cast<float>(sm.Kb[r * LDB + c]);
+    else return sm.Kr[r * LDK + c];
+  };
+  auto qval = [&](int r, int c) __attribute__((always_inline)) -> float {
+    if constexpr (BF) return static_cast<float>(sm.Qb[r * LDB + c]);
+    else return sm.Qr[r * LDK + c];
   };
 
   fetch(bos);
@@ -186,8 +183,8 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
           if constexpr (BF) {
 #pragma unroll
             for (int kb = 0; kb < D / 32; ++kb)
-              acc = mma(bf8(&sm.Qr[(16 * bi + c16) * LDK + 32 * kb + 8 * j]),
-                        bf8(&sm.Kr[(16 * bj + c16) * LDK + 32 * kb + 8 * j]), acc);
+              acc = mma(*reinterpret_cast<const bf16x8 *>(&sm.Qb[(16 * bi + c16) * LDB + 32 * kb + 8 * j]),
+                        *reinterpret_cast<const bf16x8 *>(&sm.Kb[(16 * bj + c16) * LDB + 32 * kb + 8 * j]), acc);
           } else {
 #pragma unroll
             for (int k0 = 0; k0 < D; k0 += 4)
@@ -225,15 +222,10 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
         const Split8 pf = join(split4(P[2 * kk]), split4(P[2 * kk + 1]));
 #pragma unroll
         for (int bi = 0; bi < 4; ++bi) {
-          const float *row = &sm.Qr[(16 * bi + c16) * LDK + 32 * kk];
-          const f32x4 x = *reinterpret_cast<const f32x4 *>(row + 4 * j);
-          const f32x4 y = *reinterpret_cast<const f32x4 *>(row + 16 + 4 * j);
-          bf16x8 a;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a[e] = static_cast<__bf16>(x[e]);
-            a[4 + e] = static_cast<__bf16>(y[e]);
-          }
+          const __bf16 *row = &sm.Qb[(16 * bi + c16) * LDB + 32 * kk];
+          const bf16x8 a = __builtin_shufflevector(*reinterpret_cast<const bf16x4 *>(row + 4 * j),
+                                                   *reinterpret_cast<const bf16x4 *>(row + 16 + 4 * j),
+                                                   0, 1, 2, 3, 4, 5, 6, 7);
           PQ[bi] = mma(a, pf.hi, PQ[bi]);
           PQ[bi] = mma(a, pf.lo, PQ[bi]);
         }
@@ -252,12 +244,17 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
     {
       // m . q_t over this wave's quarter of the columns (token l)
       constexpr int QW = D / 4;
-      const float *qrow = &sm.Qr[l * LDK + QW * w];
       const float *mrow = &sm.msum[QW * w];
       float d = 0.f;
 #pragma unroll
       for (int c = 0; c < QW; c += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(qrow + c);
+        f32x4 x;
+        if constexpr (BF) {
+          const bf16x4 b = *reinterpret_cast<const bf16x4 *>(&sm.Qb[l * LDB + QW * w + c]);
+          x = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+        } else {
+          x = *reinterpret_cast<const f32x4 *>(&sm.Qr[l * LDK + QW * w + c]);
+        }
         const f32x4 m = *reinterpret_cast<const f32x4 *>(mrow + c);
         d += x[0] * m[0] + x[1] * m[1] + x[2] * m[2] + x[3] * m[3];
       }
@@ -279,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Kc[mt][i] = sm.Kr[(16 * mt + 4 * j + i) * LDK + col];
+      for (int i = 0; i < 4; ++i) Kc[mt][i] = kval(16 * mt + 4 * j + i, col);
     // m_t for this lane's column: the chunk-start m plus running key sums, on
     // the MFMA with a lower ones mask per diagonal block and the block
     // totals (row 15 of each block, held by lane group 3) carried
@@ -318,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
           const int r = 16 * bi + 4 * j + i;
           const float inv = 1.f / (n0 + (float)(r + 1));
           const float sq = PQ[bi][i] * inv - (cmv[bi][i] * inv) * (sm.mq[r] * inv);
-          const float qc = sm.Qr[r * LDK + col] - sm.lam[r] * sq;
+          const float qc = qval(r, col) - sm.lam[r] * sq;
           const uint32_t off = (uint32_t)(((r * H + h) * D + col) * OSZ);
           if constexpr (OUT_BF16) {
             const __bf16 hi = static_cast<__bf16>(qc);
@@ -377,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
       const int c = tid % D, part = tid / D;
       float a = 0.f;
 #pragma unroll 8
-      for (int t = 0; t < TP; ++t) a += sm.Kr[(part * TP + t) * LDK + c];
+      for (int t = 0; t < TP; ++t) a += kval(part * TP + t, c);
       sm.kp[tid] = a;
     }
     lds_barrier();  // every read of this chunk's K, Q, m is done
