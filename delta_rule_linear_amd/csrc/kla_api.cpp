@@ -350,6 +350,10 @@ kla_status kla_fwd_chunked_ccq(const void *q, const void *k, const void *v, cons
   c.ccq_out = ccq_out;
   c.qh = ws;
   c.ql = dtype == KLA_BF16 ? ws + round_up((size_t)th * dk * 2) : nullptr;
+  // the lo read's output area is free until that read: it holds the sums of
+  // the first halves of long sequences
+  c.half_sums = dtype == KLA_BF16 ? reinterpret_cast<float *>(ws + 2 * round_up((size_t)th * dk * 2))
+                                  : nullptr;
   hipError_t e = kla::launch_ccq_query(c, st);
 
   kla::PrefillArgs a;

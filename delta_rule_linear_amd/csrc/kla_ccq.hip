@@ -68,12 +68,22 @@ __device__ inline void seg_to_f32(const uint4 &u, float *dst) {
 }
 
 // OUT_BF16: write q_clean as bf16 hi (qh) and lo (ql) planes; else fp32 to qh.
-template <typename E, int D, bool OUT_BF16>
+// SUMS_ONLY: only the running sums (the first halves of split sequences).
+//
+// split_mode 0: one workgroup per (sequence, head, column block) over the
+// whole sequence.  Sequences of at least LMIN tokens can instead be cut at a
+// chunk boundary into two halves: split_mode 1 (SUMS_ONLY) runs over the
+// first halves and leaves their end sums in half_sums, at the sequence's own
+// token rows (the output area of a later pass, unused until then; its
+// LMIN x H x D floats hold the H records); split_mode 2 then runs both
+// halves, one workgroup each, the second starting from those sums, and every
+// shorter sequence whole.
+template <typename E, int D, bool OUT_BF16, bool SUMS_ONLY>
 __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const float *__restrict__ lambda,
     const int32_t *__restrict__ cu_seqlens, int64_t seq_len_dense, int H,
     const float *__restrict__ ccq_in, float *__restrict__ ccq_out, void *__restrict__ qh,
-    void *__restrict__ ql) {
+    void *__restrict__ ql, int split_mode, float *__restrict__ half_sums) {
   using SM = CcqSmem<E, D>;
   constexpr int NB = D / DVB;
   constexpr int NST = D / 16;
@@ -84,6 +94,8 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
   constexpr int NSEG = C * SEG_ROW / kThreads;
   static_assert(NSEG * kThreads == C * SEG_ROW, "staging tiling");
   constexpr int64_t REC = (int64_t)D * D + D + 4;  // record stride (floats)
+  constexpr int64_t LMIN = (REC + D - 1) / D > C + 1 ? (REC + D - 1) / D : C + 1;
+  static_assert(!SUMS_ONLY || BF, "the sums-only pass serves bf16 inputs");
 
   __shared__ SM sm;
   const int tid = threadIdx.x;
@@ -93,11 +105,34 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
 
   const int64_t lb = logical_block();
   const int nb = (int)(lb % NB);
-  const int64_t sh = lb / NB;
+  const int seg = split_mode == 2 ? (int)((lb / NB) % 2) : 0;
+  const int64_t sh = split_mode == 2 ? lb / (2 * NB) : lb / NB;
   const int h = (int)(sh % H);
   const int64_t s = sh / H;
   const int64_t bos = cu_seqlens ? (int64_t)cu_seqlens[s] : s * seq_len_dense;
   const int64_t eos = cu_seqlens ? (int64_t)cu_seqlens[s + 1] : bos + seq_len_dense;
+  // this workgroup's tokens [lo, hi), start sums (null: zero), end sums (null: none)
+  const int64_t len = eos - bos;
+  const bool split = split_mode != 0 && len >= LMIN;
+  const int64_t mid = bos + (int64_t)C * (((len + C - 1) / C + 1) / 2);
+  float *const hrec = split ? half_sums + bos * H * (int64_t)D + (int64_t)h * REC : nullptr;
+  int64_t lo = bos, hi = eos;
+  const float *rin = ccq_in ? ccq_in + sh * REC : nullptr;
+  float *rout = ccq_out ? ccq_out + sh * REC : nullptr;
+  if (split_mode == 1) {
+    if (!split) return;
+    hi = mid;
+    rout = hrec;
+  } else if (split_mode == 2) {
+    if (seg == 1) {
+      if (!split) return;
+      lo = mid;
+      rin = hrec;
+    } else if (split) {
+      hi = mid;
+      rout = nullptr;
+    }
+  }
   const int cl = 16 * w + c16;       // column within this workgroup's block
   const int col = nb * DVB + cl;     // column of P and of q_clean
 
@@ -110,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
   f32x4 P[NST];
   float n0;
   {
-    const rsrc_t rr = make_rsrc(ccq_in ? ccq_in + sh * REC : lambda, ccq_in ? REC * 4 : 0);
+    const rsrc_t rr = make_rsrc(rin ? rin : lambda, rin ? REC * 4 : 0);
 #pragma unroll
     for (int t = 0; t < NST; ++t)
 #pragma unroll
@@ -122,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
   uint4 kreg[NSEG], qreg[NSEG];
   float lreg = 0.f;
   auto fetch = [&](int64_t t0) {
-    const int64_t nn = (eos - t0) < C ? (eos - t0) : C;
+    const int64_t nn = (hi - t0) < C ? (hi - t0) : C;
     const int64_t rowb = (int64_t)H * D * sizeof(E);
     const rsrc_t rk = make_rsrc(k + t0 * H * (int64_t)D, nn * rowb);
     const rsrc_t rq = make_rsrc(q + t0 * H * (int64_t)D, nn * rowb);
@@ -131,9 +166,9 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
       const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
       const uint32_t off = (uint32_t)((r * H + h) * D + cs * SEG_EL) * sizeof(E);
       kreg[u] = buf_ld16(rk, off);
-      qreg[u] = buf_ld16(rq, off);
+      if constexpr (!SUMS_ONLY) qreg[u] = buf_ld16(rq, off);
     }
-    if (w == 0) {
+    if (!SUMS_ONLY && w == 0) {
       const rsrc_t rl = make_rsrc(lambda + t0 * H, nn * H * 4);
       lreg = buf_ld4(rl, (uint32_t)(l * H + h) * 4);
     }
@@ -144,13 +179,13 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
       const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
       if constexpr (BF) {
         *reinterpret_cast<uint4 *>(&sm.Kb[r * LDB + cs * SEG_EL]) = kreg[u];
-        *reinterpret_cast<uint4 *>(&sm.Qb[r * LDB + cs * SEG_EL]) = qreg[u];
+        if constexpr (!SUMS_ONLY) *reinterpret_cast<uint4 *>(&sm.Qb[r * LDB + cs * SEG_EL]) = qreg[u];
       } else {
         seg_to_f32(kreg[u], &sm.Kr[r * LDK + cs * SEG_EL]);
         seg_to_f32(qreg[u], &sm.Qr[r * LDK + cs * SEG_EL]);
       }
     }
-    if (w == 0) sm.lam[l] = lreg;
+    if (!SUMS_ONLY && w == 0) sm.lam[l] = lreg;
   };
   // element (token r, feature c) of the chunk's keys / queries as fp32
   auto kval = [&](int r, int c) __attribute__((always_inline)) -> float {
@@ -162,13 +197,15 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
     else return sm.Qr[r * LDK + c];
   };
 
-  fetch(bos);
+  fetch(lo);
   stage();
-  for (int64_t tok0 = bos; tok0 < eos; tok0 += C) {
-    const int n = (int)((eos - tok0) < C ? (eos - tok0) : C);
+  for (int64_t tok0 = lo; tok0 < hi; tok0 += C) {
+    const int n = (int)((hi - tok0) < C ? (hi - tok0) : C);
     lds_barrier();  // chunk staged (and m of the chunk start final)
     fetch(tok0 + C);
 
+    f32x4 PQ[4];  // (Q P + lower(Q K^T) K)[16bi + 4j + i][col]
+    if constexpr (!SUMS_ONLY) {
     // ---- lower(Q K^T) tiles, Q P for this wave's columns, m . q_t ----------
     {
       // tiles (bi, bj), bj <= bi, numbered 0..9 in row order; wave w takes
@@ -208,7 +245,6 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
         }
       }
     }
-    f32x4 PQ[4];
     if constexpr (BF) {
       // P split into bf16 hi + lo (to 2^-17) and used in place as the B
       // operand of the 32-deep bf16 MFMA (tiles 2kk, 2kk+1 joined: lane group
@@ -260,10 +296,11 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
       }
       sm.mdp[w * C + l] = d;
     }
+    }  // !SUMS_ONLY
     lds_barrier();
 
     // ---- m_t . q_t = m . q_t + row sums of lower(Q K^T) -----------------------
-    if (w == 0) {
+    if (!SUMS_ONLY && w == 0) {
       float rs = 0.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) rs += sm.mdp[u * C + l] + sm.rsum[u * C + l];
@@ -273,6 +310,7 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
 
     // ---- P_t q_t = (Q P)_t + (lower(Q K^T) K)_t; q_clean -----------------------
     f32x4 Kc[4];  // K[16mt + 4j + i][col], the B operand of the two products below
+    if constexpr (!SUMS_ONLY) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -328,6 +366,7 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
         }
     }
 
+    }  // !SUMS_ONLY
     // ---- P += K^T K (the chunk's sum first), m, n -----------------------------
     {
       f32x4 Pc[NST];
@@ -388,8 +427,8 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
     stage();  // writes K, Q, lambda only: no reader of them is left in this chunk
   }
 
-  if (ccq_out) {
-    float *rec = ccq_out + sh * REC;
+  if (rout) {
+    float *rec = rout;
 #pragma unroll
     for (int t = 0; t < NST; ++t)
 #pragma unroll
@@ -555,15 +594,25 @@ __global__ __launch_bounds__(256) void add_kernel(float *__restrict__ o, const f
 
 hipError_t launch_ccq_query(const CcqArgs &a, hipStream_t st) {
   const int64_t grid = (int64_t)a.n_seqs * a.H * (a.D / DVB);
-  const dim3 g((unsigned)grid), b(kThreads);
-#define KLA_CCQ_LAUNCH(E, DD, BF)                                                                   \
-  hipLaunchKernelGGL((ccq_query_kernel<E, DD, BF>), g, b, 0, st, static_cast<const E *>(a.q),       \
-                     static_cast<const E *>(a.k), a.lambda, a.cu_seqlens, a.seq_len_dense, a.H,     \
-                     a.ccq_in, a.ccq_out, a.qh, a.ql)
-  if (a.bf16_inputs) {
-    if (a.D == 128) KLA_CCQ_LAUNCH(__bf16, 128, true); else KLA_CCQ_LAUNCH(__bf16, 64, true);
+  const dim3 b(kThreads);
+#define KLA_CCQ_LAUNCH(E, DD, BF, SO, MODE, G)                                                     \
+  hipLaunchKernelGGL((ccq_query_kernel<E, DD, BF, SO>), dim3((unsigned)(G)), b, 0, st,             \
+                     static_cast<const E *>(a.q), static_cast<const E *>(a.k), a.lambda,          \
+                     a.cu_seqlens, a.seq_len_dense, a.H, a.ccq_in, a.ccq_out, a.qh, a.ql, MODE,   \
+                     a.half_sums)
+  if (a.bf16_inputs && a.half_sums) {
+    // long sequences in two halves: the first halves' sums, then both halves
+    if (a.D == 128) {
+      KLA_CCQ_LAUNCH(__bf16, 128, true, true, 1, grid);
+      KLA_CCQ_LAUNCH(__bf16, 128, true, false, 2, 2 * grid);
+    } else {
+      KLA_CCQ_LAUNCH(__bf16, 64, true, true, 1, grid);
+      KLA_CCQ_LAUNCH(__bf16, 64, true, false, 2, 2 * grid);
+    }
+  } else if (a.bf16_inputs) {
+    if (a.D == 128) KLA_CCQ_LAUNCH(__bf16, 128, true, false, 0, grid); else KLA_CCQ_LAUNCH(__bf16, 64, true, false, 0, grid);
   } else {
-    if (a.D == 128) KLA_CCQ_LAUNCH(float, 128, false); else KLA_CCQ_LAUNCH(float, 64, false);
+    if (a.D == 128) KLA_CCQ_LAUNCH(float, 128, false, false, 0, grid); else KLA_CCQ_LAUNCH(float, 64, false, false, 0, grid);
   }
 #undef KLA_CCQ_LAUNCH
   return hipGetLastError();

@@ -51,6 +51,10 @@ struct CcqArgs {
   const float *ccq_in;        // prefill: start sums or nullptr
   float *ccq_out;             // end sums or nullptr
   void *qh, *ql;              // cleaned query: fp32 in qh, or bf16 hi / lo planes (bf16)
+  // bf16 only, nullable: [total_tok, H, D] fp32 scratch (free during the
+  // pass) for the sums of the first halves of long sequences; when set, each
+  // long sequence is cleaned as two halves in parallel
+  float *half_sums = nullptr;
 };
 
 // Curvature-conditioned decode step, one kernel: the sums take the new key,
