@@ -28,7 +28,9 @@
 // for fp32 inputs all on the fp32 MFMA.  The running key sums m_t come from
 // the MFMA too (a lower ones mask per diagonal block).  The columns of
 // q_clean follow the columns of P; both workgroups of a (sequence, head)
-// keep the whole m.  Output: q_clean as fp32, or as a bf16 hi / lo pair
+// keep the whole m.  For bf16 inputs long sequences run as two halves (a
+// sums-only pass over the first halves, then both halves in parallel), so
+// that two workgroups share each CU.  Output: q_clean as fp32, or as a bf16 hi / lo pair
 // (q_clean = hi + lo to 2^-17), for the bf16 read.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
