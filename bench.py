@@ -14,9 +14,14 @@ launch stream, and the fp64 reference timed on the host cores.
 Algorithmic work counted per token-head (d = 128, C = 64):
   prefill bytes  q,k,v bf16 3*256 + alpha,eta 2*4 + o fp32 512 = 1288 B,
                  plus the final state (d*d*4 B) once per (sequence, head)
-  prefill flops  full 16x16-tile MFMA count of the method as implemented:
-                 K K^T, Q K^T, T R, M Delta: 2*C*d each; Q S, K S, K^T Delta:
-                 2*d*d each  ->  8*C*d + 6*d*d = 163,840
+  prefill flops  full 16x16-tile MFMA count of the chunk algorithm in its
+                 W/U form: K K^T, Q K^T, T V, T Diag(g) K, M Delta: 2*C*d
+                 each; Q S, W S, K^T Delta: 2*d*d each -> 10*C*d + 6*d*d =
+                 180,224 (`mfma_frac`); the kernel's regrouped form forms no
+                 W: 8*C*d + 6*d*d = 163,840 (`mfma_frac_regrouped`)
+  packed         (`packed` object) the packed variable-length workload (64
+                 sequences of 128..8192 tokens, cu_seqlens): bytes and flops
+                 as the prefill over its token-heads
   decode bytes   the fp32 state read and written once: 2*d*d*4 per (seq, head)
   backward       (`backward` object) the gradients of the layer-shaped
                  prefill: reads q, k, v bf16, alpha, eta, d_o fp32, writes
@@ -33,6 +38,15 @@ Algorithmic work counted per token-head (d = 128, C = 64):
   per-channel decay (Kimi Delta Attention gate, `kda` object): the same
                  work with alpha fp32 [.., dk]: 1288 - 4 + 4*d = 1796 B per
                  token-head; its prefill kernel computes in fp32 (fp32 MFMA)
+
+Clock.  The GPU needs some tens of milliseconds of sustained work to reach
+its steady clock.  Every leg first runs its own launch back to back for at
+least --settle-ms of wall time (reported as `clock_settle_ms`), then the
+--warmup counted warm-up launches, then its timed launches.
+
+Oracle timings.  The fp64 oracle is timed on the host threads beside the
+layer prefill (`cpu_baseline`) and beside the long-context, packed and
+decode workloads (`oracle` inside those objects, one run each).
 """
 import argparse
 import json
@@ -147,11 +161,40 @@ def ingest_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
     print(json.dumps(out, indent=1))
 
 
-def prefill_work(n_seqs, T, H, d, C=64):
-    th = n_seqs * T * H
-    bytes_ = th * (3 * d * 2 + 2 * 4 + d * 4) + n_seqs * H * d * d * 4
-    flops = th * (8 * C * d + 6 * d * d)
-    return bytes_, flops
+def prefill_work(token_heads, n_seqs, H, d, C=64):
+    """Algorithmic bytes and flops of one prefill launch over `token_heads`
+    token-heads in n_seqs sequences.  Flops are full-tile counts: the W/U
+    form of the chunk algorithm, 10Cd + 6d^2 per token-head (K K^T, Q K^T,
+    T V, T Diag(g) K, M Delta at 2Cd each; Q S, W S, K^T Delta at 2d^2
+    each), and this kernel's regrouped form, 8Cd + 6d^2 (no W)."""
+    bytes_ = token_heads * (3 * d * 2 + 2 * 4 + d * 4) + n_seqs * H * d * d * 4
+    flops = token_heads * (10 * C * d + 6 * d * d)
+    flops_impl = token_heads * (8 * C * d + 6 * d * d)
+    return bytes_, flops, flops_impl
+
+
+def settle(fn, min_ms):
+    """Run fn back to back for at least min_ms of wall time (synchronising
+    every 16 launches), so the GPU reaches its steady clock before the
+    counted warm-ups and the timed launches.  Returns the wall ms spent."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(16):
+            fn()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3
+        if ms >= min_ms:
+            return ms
+
+
+def warm(fn, args):
+    """The clock-settle phase, then args.warmup counted warm-up launches."""
+    ms = settle(fn, args.settle_ms)
+    for _ in range(args.warmup):
+        fn()
+    return ms
 
 
 def time_launches(fn, n, stream):
@@ -190,12 +233,11 @@ def bench_prefill(args, torch, kla, workloads):
     def step():
         kla.kla_fwd_chunked(q, k, v, a, e, eps=inp["eps"], o=o, final_state=S)
 
-    for _ in range(args.warmup):
-        step()
+    settle_ms = warm(step, args)
     wall, ev_ms = time_launches(step, args.steps, stream)
-    nbytes, flops = prefill_work(B, T, H, d)
+    nbytes, flops, flops_impl = prefill_work(B * T * H, B, H, d)
     return dict(inp=inp, tokens=B * T, wall=wall, ev_ms=ev_ms, bytes=nbytes, flops=flops,
-                shape=(B, T, H, d))
+                flops_impl=flops_impl, shape=(B, T, H, d), settle_ms=settle_ms)
 
 
 def bench_decode(args, torch, kla, workloads):
@@ -206,11 +248,16 @@ def bench_decode(args, torch, kla, workloads):
     steps = [{n: st[n].to(dev) for n in ("q", "k", "v", "alpha", "eta")} for st in wl["steps"]]
     o = torch.empty((N, H, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    # warm up on a scratch copy so the timed run starts from the drawn state
+    # settle and warm up on a scratch copy so the timed run starts from the drawn state
     scratch = state.clone()
-    for st in steps[:4]:
+    wi = iter(range(1 << 30))
+
+    def on_scratch():
+        st = steps[next(wi) % len(steps)]
         kla.kla_decode_step(st["q"], st["k"], st["v"], st["alpha"], st["eta"], scratch,
                             eps=wl["eps"], o=o)
+
+    settle_ms = warm(on_scratch, args)
     del scratch
     it = iter(range(len(steps)))
 
@@ -237,7 +284,7 @@ def bench_decode(args, torch, kla, workloads):
                    for _ in range(reps))
     del sweep
     return dict(N=N, H=H, d=d, steps=len(steps), wall=wall, ev_ms=ev_ms, state_bytes=state_bytes,
-                swept_ms=diffs[reps // 2])
+                swept_ms=diffs[reps // 2], settle_ms=settle_ms, wl=wl)
 
 
 def bench_long(args, torch, kla, workloads, n_splits=3, launches=20):
@@ -266,20 +313,31 @@ def bench_long(args, torch, kla, workloads, n_splits=3, launches=20):
         kla.kla_fwd_chunked_split(q, k, v, a, e, eps=inp["eps"], n_splits=n_splits, o=o,
                                   final_state=S, workspace=ws)
 
-    res = {}
+    res, settled = {}, {}
     for name, fn in (("one_pass", one), ("split", split)):
-        for _ in range(3):
-            fn()
+        settled[name] = warm(fn, args)
         _, ev_ms = time_launches(fn, launches, stream)
         res[name] = ev_ms * 1e3
     tok = B * T
-    return {"workload": f"long-context KLA prefill: {B} sequences x {T} tokens, H={H}, "
-                        f"dk=dv={d}, bf16 q/k/v (dense batch)",
-            "n_splits": n_splits,
-            "us_one_pass": round(res["one_pass"], 1), "us_split": round(res["split"], 1),
-            "tokens_per_s_one_pass": round(tok / (res["one_pass"] * 1e-6), 1),
-            "tokens_per_s_split": round(tok / (res["split"] * 1e-6), 1),
-            "speedup": round(res["one_pass"] / res["split"], 3)}
+    nbytes, flops, _ = prefill_work(tok * H, B, H, d)
+    best = min(res.values())
+    gbs = nbytes / (best * 1e-6) / 1e9
+    del q, k, v, a, e, o, S, ws
+    out = {"workload": f"long-context KLA prefill: {B} sequences x {T} tokens, H={H}, "
+                       f"dk=dv={d}, bf16 q/k/v (dense batch)",
+           "n_splits": n_splits,
+           "us_one_pass": round(res["one_pass"], 1), "us_split": round(res["split"], 1),
+           "tokens_per_s_one_pass": round(tok / (res["one_pass"] * 1e-6), 1),
+           "tokens_per_s_split": round(tok / (res["split"] * 1e-6), 1),
+           "speedup": round(res["one_pass"] / res["split"], 3),
+           "roofline_best": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                             "algorithmic_bytes_per_launch": nbytes,
+                             "mfma_frac": round(flops / (best * 1e-6) / 1e12 / BF16_MFMA_PEAK_TF, 4)},
+           "clock_settle_ms": {k2: round(v2, 1) for k2, v2 in settled.items()}}
+    if not args.skip_cpu_baseline:
+        out["oracle"] = time_oracle(inp, tok)
+    return out
 
 
 def bench_kda(args, torch, kla, workloads, launches=50):
@@ -299,12 +357,11 @@ def bench_kda(args, torch, kla, workloads, launches=50):
     def step():
         kla.kla_fwd_chunked_kda(q, k, v, a, e, eps=inp["eps"], o=o, final_state=S)
 
-    for _ in range(10):
-        step()
+    settle_ms = warm(step, args)
     _, ev_ms = time_launches(step, launches, stream)
     th = B * T * H
     nbytes = th * (3 * d * 2 + 4 * d + 4 + d * 4) + B * H * d * d * 4
-    flops = th * (8 * 64 * d + 6 * d * d)
+    flops = th * (10 * 64 * d + 6 * d * d)
     gbs = nbytes / (ev_ms * 1e-3) / 1e9
     tf = flops / (ev_ms * 1e-3) / 1e12
     del q, k, v, a, e, o, S, inp
@@ -318,7 +375,8 @@ def bench_kda(args, torch, kla, workloads, launches=50):
                         "algorithmic_bytes_per_launch": nbytes,
                         "fp32_mfma_tflops": round(tf, 2),
                         "fp32_mfma_frac": round(tf / FP32_MFMA_PEAK_TF, 4),
-                        "algorithmic_flops_per_launch": flops}}
+                        "algorithmic_flops_per_launch": flops},
+           "clock_settle_ms": round(settle_ms, 1)}
     if not args.skip_decode:
         wl = workloads.decode(steps=args.decode_steps, channel_decay=True)
         N = wl["n_seqs"]
@@ -326,9 +384,14 @@ def bench_kda(args, torch, kla, workloads, launches=50):
         steps = [{n: st[n].to(dev) for n in ("q", "k", "v", "alpha_ch", "eta")} for st in wl["steps"]]
         od = torch.empty((N, H, d), dtype=torch.float32, device=dev)
         scratch = state.clone()
-        for st in steps[:4]:
+        wi = iter(range(1 << 30))
+
+        def on_scratch():
+            st = steps[next(wi) % len(steps)]
             kla.kla_decode_step_kda(st["q"], st["k"], st["v"], st["alpha_ch"], st["eta"], scratch,
                                     eps=wl["eps"], o=od)
+
+        warm(on_scratch, args)
         del scratch
         it = iter(range(len(steps)))
 
@@ -367,8 +430,7 @@ def bench_bwd(args, torch, kla, workloads, launches=10):
     def step():
         kla.kla_bwd_chunked(q, k, v, a, e, do, d_final=dfin, eps=inp["eps"], workspace=ws)
 
-    for _ in range(3):
-        step()
+    settle_ms = warm(step, args)
     _, ev_ms = time_launches(step, launches, stream)
     th = B * T * H
     nbytes = th * (3 * d * 2 + 2 * 4 + d * 4 + 3 * d * 4 + 2 * 4) + 2 * B * H * d * d * 4
@@ -391,7 +453,8 @@ def bench_bwd(args, torch, kla, workloads, launches=10):
                          "avg_launch_us": round(ev_ms * 1e3, 2),
                          "algorithmic_flops_per_launch": flops,
                          "algorithmic_bytes_per_launch": nbytes,
-                         "hbm_gbs": round(nbytes / (ev_ms * 1e-3) / 1e9, 1)}}
+                         "hbm_gbs": round(nbytes / (ev_ms * 1e-3) / 1e9, 1)},
+            "clock_settle_ms": round(settle_ms, 1)}
 
 
 def bench_variants(args, torch, kla, workloads, launches=50):
@@ -417,8 +480,7 @@ def bench_variants(args, torch, kla, workloads, launches=50):
         def step():
             kla.kla_fwd_chunked_ex(q, k, v, alpha, e, eps=inp["eps"], beta_mode="direct", o=o,
                                    final_state=S)
-        for _ in range(200):  # as the headline prefill: the clock settles first
-            step()
+        warm(step, args)
         _, ms = time_launches(step, launches, stream)
         out[name + "_us"] = round(ms * 1e3, 2)
         out[name + "_tokens_per_s"] = round(B * T / (ms * 1e-3), 1)
@@ -449,8 +511,7 @@ def bench_ccq(args, torch, kla, workloads, launches=50):
         kla.kla_fwd_chunked_ccq(q, k, v, a, e, lam, eps=inp["eps"], o=o, final_state=S,
                                 ccq_out=cout)
 
-    for _ in range(10):
-        step()
+    settle_ms = warm(step, args)
     _, ms = time_launches(step, launches, stream)
     th = B * T * H
     nbytes = th * (3 * d * 2 + 3 * 4 + d * 4) + B * H * (d * d + rec) * 4
@@ -461,7 +522,8 @@ def bench_ccq(args, torch, kla, workloads, launches=50):
            "prefill_us": round(ms * 1e3, 2),
            "prefill_tokens_per_s": round(B * T / (ms * 1e-3), 1),
            "prefill_hbm_gbs": round(gbs, 1),
-           "prefill_algorithmic_bytes": nbytes}
+           "prefill_algorithmic_bytes": nbytes,
+           "clock_settle_ms": round(settle_ms, 1)}
     if not args.skip_decode:
         wl = workloads.decode(steps=args.decode_steps)
         N = wl["n_seqs"]
@@ -470,6 +532,17 @@ def bench_ccq(args, torch, kla, workloads, launches=50):
         steps = [{n: st[n].to(dev) for n in ("q", "k", "v", "alpha", "eta")} for st in wl["steps"]]
         lams = [workloads.ccq_gate(100 + i, N, H).to(dev) for i in range(len(steps))]
         od = torch.empty((N, H, d), dtype=torch.float32, device=dev)
+        s_scr, c_scr = state.clone(), sums.clone()
+        wi = iter(range(1 << 30))
+
+        def on_scratch():
+            i = next(wi) % len(steps)
+            st = steps[i]
+            kla.kla_decode_step_ccq(st["q"], st["k"], st["v"], st["alpha"], st["eta"], lams[i],
+                                    s_scr, c_scr, eps=wl["eps"], o=od)
+
+        warm(on_scratch, args)
+        del s_scr, c_scr
         it = iter(range(len(steps)))
 
         def one():
@@ -484,6 +557,85 @@ def bench_ccq(args, torch, kla, workloads, launches=50):
         out["decode_gbs"] = round(dbytes / (dms * 1e-3) / 1e9, 1)
         out["decode_bytes_per_step"] = dbytes
     return out
+
+
+def bench_packed(args, torch, kla, workloads, launches=20):
+    """The packed variable-length prefill (64 sequences of 128..8192 tokens,
+    16 heads, d = 128, 5% of keys x10) through cu_seqlens, one launch per
+    call; bytes and flops as the prefill over its token-heads."""
+    inp = workloads.prefill("packed")
+    H, d, n = inp["H"], inp["d"], inp["n_seqs"]
+    dev = "cuda:0"
+    q, k, v, a, e = (inp[x].to(dev) for x in ("q", "k", "v", "alpha", "eta"))
+    cu = inp["cu_seqlens"].to(dev)
+    tok = q.shape[0]
+    o = torch.empty((tok, H, d), dtype=torch.float32, device=dev)
+    S = torch.empty((n, H, d, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kla.kla_fwd_chunked(q, k, v, a, e, cu_seqlens=cu, eps=inp["eps"], o=o, final_state=S)
+
+    settle_ms = warm(step, args)
+    _, ev_ms = time_launches(step, launches, stream)
+    nbytes, flops, flops_impl = prefill_work(tok * H, n, H, d)
+    us = ev_ms * 1e3
+    gbs = nbytes / (us * 1e-6) / 1e9
+    tf = flops / (us * 1e-6) / 1e12
+    del q, k, v, a, e, cu, o, S
+    lens = inp["lengths"]
+    out = {"workload": f"packed variable-length KLA prefill: {n} sequences, lengths uniform in "
+                       f"[128, 8192] (seeded: {min(lens)}..{max(lens)}, {tok} tokens), H={H}, "
+                       f"dk=dv={d}, bf16 q/k/v, 5% of keys x10, cu_seqlens",
+           "tokens": tok,
+           "us_per_launch": round(us, 1),
+           "tokens_per_s": round(tok / (us * 1e-6), 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "kernel": PREFILL_KERNEL, "avg_launch_us": round(us, 1),
+                        "algorithmic_bytes_per_launch": nbytes,
+                        "mfma_tflops": round(tf, 2),
+                        "mfma_frac": round(tf / BF16_MFMA_PEAK_TF, 4),
+                        "mfma_frac_regrouped": round(flops_impl / (us * 1e-6) / 1e12
+                                                     / BF16_MFMA_PEAK_TF, 4),
+                        "algorithmic_flops_per_launch": flops},
+           "clock_settle_ms": round(settle_ms, 1)}
+    if not args.skip_cpu_baseline:
+        out["oracle"] = time_oracle(inp, tok)
+    return out
+
+
+def time_oracle(inp, tokens):
+    """One wall-clock run of the fp64 oracle over a whole prefill workload on
+    the host threads (fp64 conversion of the inputs included)."""
+    import numpy as np
+    import oracle
+    cu = (inp["cu_seqlens"].numpy().astype(np.int64) if inp["cu_seqlens"] is not None
+          else np.concatenate([[0], np.cumsum(inp["lengths"])]).astype(np.int64))
+    t0 = time.perf_counter()
+    oracle.fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["eta"], cu_seqlens=cu,
+               eps=float(np.float32(inp["eps"])))
+    dt = time.perf_counter() - t0
+    return {"seconds": round(dt, 3), "tokens_per_s": round(tokens / dt, 1),
+            "threads": oracle.num_threads(), "kind": "oracle", "sample": "whole workload, one run"}
+
+
+def time_oracle_decode(wl):
+    """The fp64 oracle over all steps of the decode workload (every sequence
+    and head), one run, from the drawn start state."""
+    import numpy as np
+    import oracle
+    t0 = time.perf_counter()
+    state = wl["state"].double().numpy()
+    for st in wl["steps"]:
+        _, state = oracle.decode_step(st["q"], st["k"], st["v"], st["alpha"], st["eta"], state,
+                                      eps=float(np.float32(wl["eps"])))
+    dt = time.perf_counter() - t0
+    n = wl["n_seqs"] * len(wl["steps"])
+    return {"seconds": round(dt, 3), "tokens_per_s": round(n / dt, 1),
+            "us_per_step": round(dt * 1e6 / len(wl["steps"]), 1),
+            "threads": oracle.num_threads(), "kind": "oracle",
+            "sample": f"all {len(wl['steps'])} steps of {wl['n_seqs']} sequences x {wl['H']} heads, one run"}
 
 
 def cpu_baseline(pre, oracle, runs=5):
@@ -523,10 +675,11 @@ def calibrate_copy(torch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
-    # The GPU takes some tens of milliseconds of sustained work to reach its
-    # steady clock; 200 warm-up launches (about 30 ms) cover that.
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    # The GPU takes some tens of milliseconds of sustained work to reach its
+    # steady clock: every leg first runs its launch for this long.
+    ap.add_argument("--settle-ms", type=float, default=200.0)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--skip-long", action="store_true",
@@ -539,6 +692,8 @@ def main():
                     help="skip the curvature-conditioned read (prefill and decode)")
     ap.add_argument("--skip-bwd", action="store_true",
                     help="skip the backward of the layer-shaped prefill")
+    ap.add_argument("--skip-packed", action="store_true",
+                    help="skip the packed variable-length prefill")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -569,6 +724,7 @@ def main():
     value = pre["tokens"] / (pre["wall"] / args.steps)
     ach_gbs = pre["bytes"] / (pre["ev_ms"] * 1e-3) / 1e9
     ach_tf = pre["flops"] / (pre["ev_ms"] * 1e-3) / 1e12
+    ach_tf_impl = pre["flops_impl"] / (pre["ev_ms"] * 1e-3) / 1e12
     B, T, H, d = pre["shape"]
     out = {
         "metric": "KLA prefill tokens/s (H=16,d=128) + decode state GB/s, % of MI355X roofline",
@@ -592,7 +748,11 @@ def main():
                      "algorithmic_bytes_per_launch": pre["bytes"],
                      "mfma_tflops": round(ach_tf, 2),
                      "mfma_frac": round(ach_tf / BF16_MFMA_PEAK_TF, 4),
-                     "algorithmic_flops_per_launch": pre["flops"]},
+                     "algorithmic_flops_per_launch": pre["flops"],
+                     "flops_convention": "full-tile 10Cd+6d^2 = 180,224 per token-head (W/U form)",
+                     "mfma_frac_regrouped": round(ach_tf_impl / BF16_MFMA_PEAK_TF, 4),
+                     "algorithmic_flops_regrouped": pre["flops_impl"]},
+        "clock_settle_ms": round(pre["settle_ms"], 1),
     }
     if not args.skip_decode:
         dec = bench_decode(args, torch, kla, workloads)
@@ -609,7 +769,13 @@ def main():
             "us_per_step_after_cache_sweep": round(dec["swept_ms"] * 1e3, 2),
             "frac_after_cache_sweep": round(dec["state_bytes"] / (dec["swept_ms"] * 1e-3) / 1e9
                                             / HBM_PEAK_GBS, 4),
+            "clock_settle_ms": round(dec["settle_ms"], 1),
         }
+        if not args.skip_cpu_baseline:
+            out["decode"]["oracle"] = time_oracle_decode(dec["wl"])
+        del dec
+    if not args.skip_packed:
+        out["packed"] = bench_packed(args, torch, kla, workloads)
     if not args.skip_long:
         out["long_context"] = bench_long(args, torch, kla, workloads)
     if not args.skip_kda:

@@ -39,6 +39,7 @@ const char *kla_status_string(kla_status s) {
     case KLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case KLA_ERR_WORKSPACE: return "workspace too small";
     case KLA_ERR_HIP: return "HIP runtime error";
+    default: break;
   }
   return "unknown status";
 }

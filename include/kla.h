@@ -52,22 +52,32 @@
 extern "C" {
 #endif
 
+/* Every enum below also names the int32 bounds (the *_RANGE_ members, never
+ * valid arguments), so any int32 a C caller passes is a value of the type:
+ * an unknown value reaches the library's argument checks and is rejected,
+ * instead of being undefined behaviour in the C++ implementation. */
 typedef enum {
     KLA_OK = 0,
     KLA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, aliasing */
     KLA_ERR_UNSUPPORTED = -2, /* valid but not implemented (dk, dv, chunk, dtype) */
     KLA_ERR_WORKSPACE = -3,   /* workspace smaller than the query returned */
-    KLA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+    KLA_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+    KLA_STATUS_RANGE_MIN = -2147483647 - 1,
+    KLA_STATUS_RANGE_MAX = 2147483647
 } kla_status;
 
 typedef enum {
     KLA_F32 = 0,  /* IEEE binary32 */
-    KLA_BF16 = 1  /* bfloat16 (8-bit exponent, 7-bit mantissa) */
+    KLA_BF16 = 1, /* bfloat16 (8-bit exponent, 7-bit mantissa) */
+    KLA_DTYPE_RANGE_MIN = -2147483647 - 1,
+    KLA_DTYPE_RANGE_MAX = 2147483647
 } kla_dtype;
 
 typedef enum {
     KLA_BETA_KACZMARZ = 0, /* beta_t = eta_t / (k_t^T k_t + eps)   (KLA) */
-    KLA_BETA_DIRECT = 1    /* beta_t = eta_t; eps is unused       (Gated DeltaNet) */
+    KLA_BETA_DIRECT = 1,   /* beta_t = eta_t; eps is unused       (Gated DeltaNet) */
+    KLA_BETA_RANGE_MIN = -2147483647 - 1,
+    KLA_BETA_RANGE_MAX = 2147483647
 } kla_beta_mode;
 
 /*

@@ -17,7 +17,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libkla_oracle.so")
+# KLA_ORACLE_LIB: another build of the same source (the sanitizer build of
+# the CPU tests); the default is the in-tree build.
+_LIB_PATH = os.environ.get("KLA_ORACLE_LIB") or os.path.join(_HERE, "libkla_oracle.so")
 _dp = ctypes.POINTER(ctypes.c_double)
 _i64p = ctypes.POINTER(ctypes.c_int64)
 

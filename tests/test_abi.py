@@ -9,7 +9,9 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kla.h")
-LIB = os.path.join(ROOT, "delta_rule_linear_amd", "libkla.so")
+# KLA_TEST_LIB: the host-only sanitizer build of the C-ABI layer
+# (tests/sanitize/build.py); the default is the in-tree library.
+LIB = os.environ.get("KLA_TEST_LIB") or os.path.join(ROOT, "delta_rule_linear_amd", "libkla.so")
 
 OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
 

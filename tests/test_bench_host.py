@@ -58,13 +58,26 @@ def test_recorded_traffic_needs_the_current_source(tmp_path, monkeypatch):
 
 
 def test_prefill_work_per_launch():
-    """1288 B and 163,840 flops per token-head, plus the final state per
-    (sequence, head): the layer workload's figures."""
+    """1288 B per token-head plus the final state per (sequence, head);
+    180,224 full-tile flops per token-head in the W/U form and 163,840 in
+    the kernel's regrouped form: the layer workload's figures."""
     n, T, H, d = 8, 2048, 16, 128
-    b, f = bench.prefill_work(n, T, H, d)
     th = n * T * H
+    b, f, fi = bench.prefill_work(th, n, H, d)
     assert b == th * (3 * 256 + 8 + 512) + n * H * d * d * 4 == 346_030_080
-    assert f == th * (8 * 64 * d + 6 * d * d) == 42_949_672_960
+    assert f == th * 180_224 == 47_244_640_256
+    assert fi == th * (8 * 64 * d + 6 * d * d) == 42_949_672_960
+
+
+def test_settle_runs_for_the_requested_time(monkeypatch):
+    """The clock-settle phase keeps launching until the wall time is spent."""
+    import types
+    calls = []
+    fake = types.SimpleNamespace(cuda=types.SimpleNamespace(synchronize=lambda: None))
+    monkeypatch.setitem(sys.modules, "torch", fake)
+    import time as _t
+    ms = bench.settle(lambda: (calls.append(1), _t.sleep(0.001)), 30.0)
+    assert ms >= 30.0 and len(calls) % 16 == 0 and len(calls) >= 16
 
 
 def test_more_than_one_gpu_is_refused():
