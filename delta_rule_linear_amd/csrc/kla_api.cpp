@@ -65,7 +65,7 @@ kla_status fwd_impl(const void *q, const void *k, const void *v, const float *al
                     float eps, kla_dtype dtype, kla_beta_mode beta_mode, int32_t n_splits,
                     const float *initial_state, float *o, float *final_state,
                     void *workspace, size_t workspace_bytes, void *stream,
-                    bool channel_decay = false) {
+                    bool channel_decay = false, bool noalloc = false) {
   if (n_seqs <= 0 || H <= 0 || total_tok < 0 || !std::isfinite(eps) || eps < 0.f)
     return KLA_ERR_INVALID_ARG;
   if (beta_mode != KLA_BETA_KACZMARZ && beta_mode != KLA_BETA_DIRECT) return KLA_ERR_INVALID_ARG;
@@ -77,8 +77,11 @@ kla_status fwd_impl(const void *q, const void *k, const void *v, const float *al
   const size_t ws_need = n_splits > 1
       ? kla_fwd_chunked_split_workspace_size(n_seqs, H, dk, dv, n_splits)
       : kla_fwd_chunked_workspace_size(n_seqs, total_tok, H, dk, dv, chunk);
+  // no-allocation variant: the library's static scratch array stands in for
+  // the workspace (its device address is taken after every other check)
+  if (noalloc) workspace_bytes = KLA_NOALLOC_SCRATCH_BYTES;
   if (workspace_bytes < ws_need) return KLA_ERR_WORKSPACE;
-  if (ws_need > 0 && (!workspace || !aligned16(workspace))) return KLA_ERR_INVALID_ARG;
+  if (!noalloc && ws_need > 0 && (!workspace || !aligned16(workspace))) return KLA_ERR_INVALID_ARG;
   const bool have_tokens = total_tok > 0;
   if (have_tokens && (!q || !k || !v || !eta || !o)) return KLA_ERR_INVALID_ARG;
   if (have_tokens && channel_decay && !alpha) return KLA_ERR_INVALID_ARG;
@@ -95,7 +98,7 @@ kla_status fwd_impl(const void *q, const void *k, const void *v, const float *al
               rcu = range(cu_seqlens, cu_seqlens ? (int64_t)(n_seqs + 1) * 4 : 0),
               rs0 = range(initial_state, initial_state ? (int64_t)n_seqs * H * dk * dv * 4 : 0),
               rs1 = range(final_state, final_state ? (int64_t)n_seqs * H * dk * dv * 4 : 0);
-  const Range rws = range(workspace, (int64_t)ws_need);
+  const Range rws = range(noalloc ? nullptr : workspace, noalloc ? 0 : (int64_t)ws_need);
   for (const Range &in : {rq, rk, rv, ra, re, rcu, rs0, rs1, rws})
     if (overlap(ro, in)) return KLA_ERR_INVALID_ARG;
   for (const Range &in : {rq, rk, rv, ra, re, rcu, rs0, rs1})
@@ -130,6 +133,7 @@ kla_status fwd_impl(const void *q, const void *k, const void *v, const float *al
     return dtype == KLA_BF16 ? kla::launch_prefill_bf16(a, st) : kla::launch_prefill_f32(a, st);
   };
   if (n_splits == 1 || total_tok == 0) return run() == hipSuccess ? KLA_OK : KLA_ERR_HIP;
+  if (noalloc && kla::noalloc_scratch(&workspace) != hipSuccess) return KLA_ERR_HIP;
   // split sequences: segment maps, scan of the maps, then every segment
   const size_t mat = (size_t)n_seqs * H * dk * dv;
   float *ws = static_cast<float *>(workspace);
@@ -171,6 +175,19 @@ kla_status kla_fwd_chunked_split(const void *q, const void *k, const void *v, co
   return fwd_impl(q, k, v, alpha, eta, cu_seqlens, n_seqs, total_tok, H, dk, dv, chunk, eps, dtype,
                   beta_mode, n_splits, initial_state, o, final_state, workspace, workspace_bytes,
                   stream);
+}
+
+kla_status kla_fwd_chunked_split_noalloc(const void *q, const void *k, const void *v,
+                                         const float *alpha, const float *eta,
+                                         const int32_t *cu_seqlens, int32_t n_seqs,
+                                         int64_t total_tok, int32_t H, int32_t dk, int32_t dv,
+                                         int32_t chunk, float eps, kla_dtype dtype,
+                                         kla_beta_mode beta_mode, int32_t n_splits,
+                                         const float *initial_state, float *o,
+                                         float *final_state, void *stream) {
+  return fwd_impl(q, k, v, alpha, eta, cu_seqlens, n_seqs, total_tok, H, dk, dv, chunk, eps, dtype,
+                  beta_mode, n_splits, initial_state, o, final_state, nullptr, 0, stream, false,
+                  true);
 }
 
 kla_status kla_fwd_chunked(const void *q, const void *k, const void *v, const float *alpha,

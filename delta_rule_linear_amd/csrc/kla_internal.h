@@ -108,6 +108,10 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s);
 // written to ws_s for p = 0..P-1.
 hipError_t launch_split_identity(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_split_scan(const PrefillArgs &a, hipStream_t s);
+// Device address, on the current device, of the library's static scratch
+// array (KLA_NOALLOC_SCRATCH_BYTES, kla_split.hip), taken once per device
+// with hipGetSymbolAddress and kept.
+hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
 // CCQ: the prefill pre-pass (q_clean for every token), the fused decode
 // step, and o += o2.

@@ -11,10 +11,24 @@
 // of every segment follows by a sequential scan over P-1 small products:
 //   S_0 = initial state (or 0),  S_{p+1} = A_p S_p + B_p.
 // Pass 2 then runs all segments at once from those starts.
+//
+// The no-allocation variant of the split-sequence prefill keeps the maps and
+// start states in `scratch`, a file-scope device array below, instead of a
+// caller workspace.  Host code never passes the array's name to a kernel
+// (in host code it is a stand-in, not a device address): the device address
+// is taken with hipGetSymbolAddress, once per device with that device
+// current, and kept.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
+#include "../../include/kla.h"
 #include "kla_internal.h"
+
+// Scratch of kla_fwd_chunked_split_noalloc; every GPU the library runs on
+// holds one copy until the process ends.  Calls on one GPU share it.
+static __device__ __align__(256) float scratch[KLA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace kla {
 namespace {
@@ -106,6 +120,26 @@ hipError_t launch_split_identity(const PrefillArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((identity_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, st, a.ws_a,
                        count);
   return hipGetLastError();
+}
+
+hipError_t noalloc_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_split_scan(const PrefillArgs &a, hipStream_t st) {

@@ -38,6 +38,9 @@ _lib.kla_fwd_chunked_split_workspace_size.argtypes = [ctypes.c_int32] * 5
 _lib.kla_fwd_chunked_split.restype = ctypes.c_int
 _lib.kla_fwd_chunked_split.argtypes = (_lib.kla_fwd_chunked.argtypes[:14] + [ctypes.c_int, ctypes.c_int32]
                                        + _lib.kla_fwd_chunked.argtypes[14:])
+_lib.kla_fwd_chunked_split_noalloc.restype = ctypes.c_int
+_lib.kla_fwd_chunked_split_noalloc.argtypes = (_lib.kla_fwd_chunked.argtypes[:14]
+                                               + [ctypes.c_int, ctypes.c_int32, _fp, _fp, _fp, _vp])
 _lib.kla_decode_step.restype = ctypes.c_int
 _lib.kla_decode_step.argtypes = [_vp, _vp, _vp, _fp, _fp, _fp, _fp, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int, _vp]
@@ -144,6 +147,21 @@ def kla_fwd_chunked_split(q, k, v, alpha, eta, cu_seqlens=None, initial_state=No
                 output_final_state, o, final_state, workspace, stream, n_splits=int(n_splits))
 
 
+def kla_fwd_chunked_split_noalloc(q, k, v, alpha, eta, cu_seqlens=None, initial_state=None,
+                                  eps=1e-6, chunk=64, beta_mode="kaczmarz", n_splits=2, o=None,
+                                  final_state=None, stream=None):
+    """kla_fwd_chunked_split without a workspace (C ABI
+    `kla_fwd_chunked_split_noalloc`): the library keeps the segment maps and
+    start states in its static device scratch array (at most
+    KLA_NOALLOC_SCRATCH_BYTES = 32 MiB per GPU; calls that overlap in time on
+    one GPU race on it).  o and final_state must be given (nothing is
+    allocated here either)."""
+    if o is None:
+        raise ValueError("o must be given: this entry point allocates nothing")
+    return _fwd(_beta_code(beta_mode), q, k, v, alpha, eta, cu_seqlens, initial_state, eps, chunk,
+                False, o, final_state, None, stream, n_splits=int(n_splits), noalloc=True)
+
+
 def kla_fwd_chunked_kda(q, k, v, alpha, eta, cu_seqlens=None, initial_state=None, eps=1e-6,
                         chunk=64, beta_mode="kaczmarz", output_final_state=False, o=None,
                         final_state=None, stream=None):
@@ -157,7 +175,7 @@ def kla_fwd_chunked_kda(q, k, v, alpha, eta, cu_seqlens=None, initial_state=None
 
 
 def _fwd(beta, q, k, v, alpha, eta, cu_seqlens, initial_state, eps, chunk, output_final_state, o,
-         final_state, workspace, stream, n_splits=None, channel_decay=False):
+         final_state, workspace, stream, n_splits=None, channel_decay=False, noalloc=False):
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, q.dtype)
     if alpha is not None:
@@ -187,7 +205,9 @@ def _fwd(beta, q, k, v, alpha, eta, cu_seqlens, initial_state, eps, chunk, outpu
         final_state = torch.empty((n_seqs, H, dk, dv), dtype=torch.float32, device=q.device)
     elif final_state is not None:
         _need(final_state, "final_state", torch.float32)
-    if n_splits is not None and n_splits > 1:
+    if noalloc:
+        ws_bytes = 0
+    elif n_splits is not None and n_splits > 1:
         ws_bytes = kla_fwd_chunked_split_workspace_size(n_seqs, H, dk, dv, n_splits)
     else:
         ws_bytes = kla_fwd_chunked_workspace_size(n_seqs, total, H, dk, dv, chunk)
@@ -198,7 +218,9 @@ def _fwd(beta, q, k, v, alpha, eta, cu_seqlens, initial_state, eps, chunk, outpu
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(eta), _ptr(cu_seqlens), n_seqs, total, H,
             dk, dv, chunk, float(eps), _dtype_code(q))
     tail = (_ptr(initial_state), _ptr(o), _ptr(final_state), ws_ptr, ws_len, _stream(stream))
-    if channel_decay:
+    if noalloc:
+        st = _lib.kla_fwd_chunked_split_noalloc(*head, beta, n_splits, *tail[:3], tail[5])
+    elif channel_decay:
         st = _lib.kla_fwd_chunked_kda(*head, beta, *tail)
     elif n_splits is not None:
         st = _lib.kla_fwd_chunked_split(*head, beta, n_splits, *tail)

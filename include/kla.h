@@ -28,7 +28,8 @@
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers (HIP device memory) except where
  *     noted; the caller owns every buffer.  The library never allocates or
- *     frees memory and keeps no state between calls.
+ *     frees memory and keeps no state between calls, apart from the static
+ *     scratch array of kla_fwd_chunked_split_noalloc.
  *   - Tensors are dense, row-major, with the innermost dimension contiguous.
  *     Pointers to q, k, v, o and states must be 16-byte aligned.
  *   - q, k, v share one element type (kla_dtype).  alpha, eta, o and all
@@ -193,6 +194,43 @@ kla_status kla_fwd_chunked_split(const void *q, const void *k, const void *v,
                                  kla_dtype dtype, kla_beta_mode beta_mode, int32_t n_splits,
                                  const float *initial_state, float *o, float *final_state,
                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Size in bytes of the device scratch array that kla_fwd_chunked_split_noalloc
+ * uses in place of a caller workspace (32 MiB per GPU).
+ */
+#define KLA_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+
+/*
+ * kla_fwd_chunked_split for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operation, arguments and result, without the
+ * workspace arguments.  The segment maps and start states live in a static
+ * device array of KLA_NOALLOC_SCRATCH_BYTES inside the library, one copy per
+ * GPU, held until the process ends.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); on its first call on a
+ * device it looks up that device's copy of the array once.
+ *
+ *   Limit: kla_fwd_chunked_split_workspace_size(n_seqs, H, dk, dv, n_splits)
+ *          must not exceed KLA_NOALLOC_SCRATCH_BYTES, else KLA_ERR_WORKSPACE
+ *          and nothing is launched (for example, at dk = dv = 128 the long
+ *          dense batch of 2 sequences x 16 heads allows n_splits <= 6).
+ *   Sharing: every call on one GPU uses the same array, whose contents are
+ *          the last call's (no call needs them cleared: each call writes
+ *          every part it reads).  Calls that overlap in time on one GPU
+ *          (concurrent streams, or threads) race on it and give wrong
+ *          results; order them on one stream.
+ * Other arguments and errors as kla_fwd_chunked_split (KLA_ERR_HIP also when
+ * the array's device address cannot be obtained).
+ */
+kla_status kla_fwd_chunked_split_noalloc(const void *q, const void *k, const void *v,
+                                         const float *alpha, const float *eta,
+                                         const int32_t *cu_seqlens, int32_t n_seqs,
+                                         int64_t total_tok, int32_t H, int32_t dk, int32_t dv,
+                                         int32_t chunk, float eps, kla_dtype dtype,
+                                         kla_beta_mode beta_mode, int32_t n_splits,
+                                         const float *initial_state, float *o,
+                                         float *final_state, void *stream);
 
 /*
  * One recurrent decode step for n_seqs independent sequences: every

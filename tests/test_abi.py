@@ -80,6 +80,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["kla_fwd_chunked", "kla_fwd_chunked_ex",
                                            "kla_fwd_chunked_split", "kla_fwd_chunked_kda",
+                                           "kla_fwd_chunked_split_noalloc",
                                            "kla_decode_step_kda", "kla_ccq_state_floats",
                                            "kla_fwd_chunked_ccq", "kla_fwd_chunked_ccq_workspace_size",
                                            "kla_decode_step_ccq", "kla_decode_step_ccq_workspace_size",
@@ -164,6 +165,43 @@ def test_split_workspace_query(lib):
 def split_call(lib, n_splits, **over):
     a = fwd_args(**over)
     return lib.kla_fwd_chunked_split(*a[:14], 0, n_splits, *a[14:])
+
+
+NOALLOC_MAX = 32 * MB
+
+
+def noalloc_call(lib, n_splits, **over):
+    a = fwd_args(**over)
+    # the workspace arguments (a[17], a[18]) are not part of this entry point
+    return lib.kla_fwd_chunked_split_noalloc(*a[:14], 0, n_splits, a[14], a[15], a[16], a[19])
+
+
+def test_noalloc_header_limit_matches():
+    text = open(HEADER).read()
+    m = re.search(r"#define KLA_NOALLOC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", text)
+    assert m and int(m.group(1)) * MB == NOALLOC_MAX
+
+
+def test_noalloc_split_rejects_on_the_host(lib):
+    """Validation and the scratch limit come before any HIP call."""
+    L = lib
+    L.kla_fwd_chunked_split_noalloc.restype = ctypes.c_int
+    L.kla_fwd_chunked_split_noalloc.argtypes = (L.kla_fwd_chunked.argtypes[:14]
+                                                + [ctypes.c_int, ctypes.c_int32]
+                                                + [ctypes.c_void_p] * 4)
+    assert noalloc_call(lib, 0) == INVALID                    # n_splits < 1
+    assert noalloc_call(lib, 1025) == INVALID                 # n_splits too large
+    assert noalloc_call(lib, 2, n_seqs=0) == INVALID
+    assert noalloc_call(lib, 2, q=BASE + 2) == INVALID        # misaligned
+    assert noalloc_call(lib, 2, o=BASE + 8) == INVALID        # o overlaps q
+    assert noalloc_call(lib, 2, dk=96, dv=96) == UNSUPPORTED
+    # (3P - 2) d x d fp32 per (sequence, head) must fit the 32 MiB array:
+    # 2 sequences x 16 heads at d = 128 allow P <= 6
+    big = dict(n_seqs=2, H=16, dk=128, dv=128, tok=2 * 64,
+               o=BASE + 4096 * MB, eta=BASE + 3072 * MB, alpha=BASE + 3200 * MB)
+    assert lib.kla_fwd_chunked_split_workspace_size(2, 16, 128, 128, 7) > NOALLOC_MAX
+    assert lib.kla_fwd_chunked_split_workspace_size(2, 16, 128, 128, 6) <= NOALLOC_MAX
+    assert noalloc_call(lib, 7, **big) == WORKSPACE
 
 
 def test_split_rejects(lib):
