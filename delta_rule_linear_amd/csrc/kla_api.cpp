@@ -46,8 +46,12 @@ const char *kla_status_string(kla_status s) {
 
 const char *kla_version(void) { return "0.1.0 gfx950"; }
 
-size_t kla_fwd_chunked_workspace_size(int32_t, int64_t, int32_t, int32_t, int32_t, int32_t) {
-  return 0;
+size_t kla_fwd_chunked_workspace_size(int32_t n_seqs, int64_t, int32_t, int32_t, int32_t,
+                                      int32_t) {
+  // the longest-first order of packed sequences (int32 per sequence), used
+  // when cu_seqlens is given for 2 .. kSeqOrderMax sequences
+  if (n_seqs < 2 || n_seqs > kla::kSeqOrderMax) return 0;
+  return ((size_t)n_seqs * 4 + 255) / 256 * 256;
 }
 
 size_t kla_fwd_chunked_split_workspace_size(int32_t n_seqs, int32_t H, int32_t dk, int32_t dv,
@@ -74,9 +78,11 @@ kla_status fwd_impl(const void *q, const void *k, const void *v, const float *al
   if (!cu_seqlens && total_tok % n_seqs != 0) return KLA_ERR_INVALID_ARG;
   if (n_splits < 1 || n_splits > kla_max_splits) return KLA_ERR_INVALID_ARG;
   if (channel_decay && n_splits != 1) return KLA_ERR_UNSUPPORTED;
+  // one pass over packed sequences: their longest-first order
+  const bool order = n_splits == 1 && !channel_decay && cu_seqlens && total_tok > 0;
   const size_t ws_need = n_splits > 1
       ? kla_fwd_chunked_split_workspace_size(n_seqs, H, dk, dv, n_splits)
-      : kla_fwd_chunked_workspace_size(n_seqs, total_tok, H, dk, dv, chunk);
+      : order ? kla_fwd_chunked_workspace_size(n_seqs, total_tok, H, dk, dv, chunk) : 0;
   // no-allocation variant: the library's static scratch array stands in for
   // the workspace (its device address is taken after every other check)
   if (noalloc) workspace_bytes = KLA_NOALLOC_SCRATCH_BYTES;
@@ -132,6 +138,11 @@ kla_status fwd_impl(const void *q, const void *k, const void *v, const float *al
   auto run = [&]() {
     return dtype == KLA_BF16 ? kla::launch_prefill_bf16(a, st) : kla::launch_prefill_f32(a, st);
   };
+  if (order && ws_need > 0) {
+    int32_t *ord = static_cast<int32_t *>(workspace);
+    if (kla::launch_seq_order(cu_seqlens, n_seqs, ord, st) != hipSuccess) return KLA_ERR_HIP;
+    a.seq_order = ord;
+  }
   if (n_splits == 1 || total_tok == 0) return run() == hipSuccess ? KLA_OK : KLA_ERR_HIP;
   if (noalloc && kla::noalloc_scratch(&workspace) != hipSuccess) return KLA_ERR_HIP;
   // split sequences: segment maps, scan of the maps, then every segment

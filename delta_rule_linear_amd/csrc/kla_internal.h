@@ -27,6 +27,9 @@ struct PrefillArgs {
   // bf16 prefill: 1 stores o write-back (for a caller that reads it straight
   // back); 0 stores it non-temporal (the output is not read by this work)
   int o_write_back = 0;
+  // whole-sequence passes: sequence indices by decreasing length (device,
+  // written by launch_seq_order), or null for the given order
+  const int32_t *seq_order = nullptr;
 };
 
 struct DecodeArgs {
@@ -100,6 +103,10 @@ struct BwdParams {
 };
 
 // Each returns the HIP status of the launch.
+// order[0..n_seqs) <- the sequences of cu_seqlens by decreasing length
+// (ties by index); n_seqs <= kla::kSeqOrderMax.
+constexpr int kSeqOrderMax = 1024;
+hipError_t launch_seq_order(const int32_t *cu_seqlens, int n_seqs, int32_t *order, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s);

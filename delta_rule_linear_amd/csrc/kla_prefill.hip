@@ -109,7 +109,14 @@ __device__ inline void store_split(bf16 *h, bf16 *l, int idx, float x) {
 __device__ inline void store_split(float *h, float *, int idx, float x) { h[idx] = x; }
 
 // What one workgroup computes.  Mode 0: one (sequence, head, 64-column block
-// of dv) over the whole sequence.  The split-sequence path cuts every
+// of dv) over the whole sequence.  Mode 0 deals the (sequence, head) pairs
+// out longest sequence first (sp.order: sequence indices by decreasing
+// length, or null for the given order), round-robin over the eight XCDs:
+// workgroup i runs on XCD i % 8, and the (i / 8)-th workgroup of an XCD
+// takes column block (i / 8) % NB of pair 8 ((i / 8) / NB) + i % 8, so both
+// column blocks of a pair share one XCD's L2 and each XCD gets an equal
+// share of the long sequences.  The grid is padded to a multiple of 8 NB;
+// the padding workgroups do nothing.  The split-sequence path cuts every
 // sequence into n_splits segments on chunk boundaries; the state map of a
 // segment is affine, S_end = A S_start + B, and the same kernels run it in
 // two passes around a scan of those maps:
@@ -124,6 +131,8 @@ __device__ inline void store_split(float *h, float *, int idx, float x) { h[idx]
 //     floor(bos_s / 64) + s + c, each [H, D, D]) and the final state to Sfin.
 struct SegParams {
   int mode, n_splits;
+  int64_t n_pairs;       // n_seqs * H
+  const int32_t *order;  // mode 0: sequences by decreasing length, or null
   float *ws_a, *ws_b;   // [n_seqs, H, P-1, D, D]
   const float *ws_s;    // [n_seqs, H, P, D, D]
   float *ckpt;          // mode 3: chunk-start state slots
@@ -144,6 +153,28 @@ __device__ inline Work resolve_work(const SegParams &sp, const int32_t *cu_seqle
   const int P = sp.n_splits;
   Work wk;
   int64_t shi, p = 0;
+  if (sp.mode == 0) {
+    const int64_t kx = (int64_t)blockIdx.x / 8, pair = (kx / NB) * 8 + blockIdx.x % 8;
+    wk.nb = wk.vb = (int)(kx % NB);
+    wk.out = true;
+    wk.ck = nullptr;
+    if (pair >= sp.n_pairs) {  // grid padding: no tokens, no state
+      wk.h = 0;
+      wk.bos = wk.eos = 0;
+      wk.s0 = nullptr;
+      wk.sfin = nullptr;
+      return wk;
+    }
+    const int64_t r = pair / H;
+    wk.h = (int)(pair % H);
+    const int64_t s = sp.order ? sp.order[r] : r, sh = s * H + wk.h;
+    wk.bos = cu_seqlens ? cu_seqlens[s] : s * seq_len_dense;
+    wk.eos = cu_seqlens ? cu_seqlens[s + 1] : wk.bos + seq_len_dense;
+    constexpr int64_t DD0 = (int64_t)D * D;
+    wk.s0 = S0 ? S0 + sh * DD0 : nullptr;
+    wk.sfin = Sfin ? Sfin + sh * DD0 : nullptr;
+    return wk;
+  }
   if (sp.mode == 1) {
     const int cb = (int)(lb % (2 * NB));
     const int64_t r = lb / (2 * NB);
@@ -170,7 +201,7 @@ __device__ inline Work resolve_work(const SegParams &sp, const int32_t *cu_seqle
   constexpr int64_t DD = (int64_t)D * D;
   wk.out = sp.mode != 1;
   wk.ck = nullptr;
-  if (sp.mode == 0 || sp.mode == 3) {
+  if (sp.mode == 3) {
     wk.bos = bos;
     wk.eos = eos;
     wk.s0 = S0 ? S0 + sh * DD : nullptr;
@@ -1105,12 +1136,15 @@ inline int64_t grid_of(const PrefillArgs &a, int NB) {
   const int64_t sh = (int64_t)a.n_seqs * a.H;
   if (a.seg_mode == 1) return sh * (a.n_splits - 1) * 2 * NB;
   if (a.seg_mode == 2) return sh * a.n_splits * NB;
+  if (a.seg_mode == 0) return (sh + 7) / 8 * 8 * NB;  // padded: 8 XCDs x whole pairs
   return sh * NB;
 }
 inline SegParams seg_of(const PrefillArgs &a) {
   SegParams sp;
   sp.mode = a.seg_mode;
   sp.n_splits = a.n_splits;
+  sp.n_pairs = (int64_t)a.n_seqs * a.H;
+  sp.order = a.seq_order;
   sp.ws_a = a.ws_a;
   sp.ws_b = a.ws_b;
   sp.ws_s = a.ws_s;
@@ -1140,7 +1174,31 @@ hipError_t launch_d(const PrefillArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Longest-first order of packed sequences: order[rank] = s, rank = the
+// number of sequences longer than s, or as long with a smaller index (a
+// stable sort by decreasing length; deterministic).  One workgroup; the
+// lengths are staged in LDS.
+constexpr int kOrderMax = 1024;
+__global__ __launch_bounds__(kOrderMax) void seq_order_kernel(const int32_t *__restrict__ cu,
+                                                              int n, int32_t *__restrict__ order) {
+  __shared__ int32_t len[kOrderMax];
+  const int s = threadIdx.x;
+  if (s < n) len[s] = cu[s + 1] - cu[s];
+  __syncthreads();
+  if (s >= n) return;
+  const int ls = len[s];
+  int rank = 0;
+  for (int t = 0; t < n; ++t) rank += (len[t] > ls) | ((len[t] == ls) & (t < s));
+  order[rank] = s;
+}
+
 }  // namespace
+
+hipError_t launch_seq_order(const int32_t *cu_seqlens, int n_seqs, int32_t *order, hipStream_t st) {
+  if (n_seqs > kOrderMax) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(seq_order_kernel, dim3(1), dim3(kOrderMax), 0, st, cu_seqlens, n_seqs, order);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s) {
   return a.D == 128 ? launch_pc<128>(a, s) : launch_pc<64>(a, s);

@@ -82,9 +82,11 @@ typedef enum {
 } kla_beta_mode;
 
 /*
- * Bytes of device workspace kla_fwd_chunked needs for these sizes.  The
- * current kernels need none and this returns 0; callers should still query
- * it and pass a buffer at least that large.
+ * Bytes of device workspace kla_fwd_chunked (and kla_fwd_chunked_ex) needs
+ * for these sizes: with cu_seqlens, the order in which the sequences are
+ * scheduled (longest first, one int32 per sequence, rounded up to 256 bytes)
+ * for 2 .. 1024 sequences; 0 otherwise.  A dense batch (cu_seqlens NULL)
+ * needs none, but callers may always pass the queried size.
  */
 size_t kla_fwd_chunked_workspace_size(int32_t n_seqs, int64_t total_tok, int32_t H,
                                       int32_t dk, int32_t dv, int32_t chunk);
@@ -117,7 +119,12 @@ size_t kla_fwd_chunked_workspace_size(int32_t n_seqs, int64_t total_tok, int32_t
  *               state, or NULL.  It may be the same buffer as initial_state
  *               (in-place update); any other overlap is an error.
  *   workspace   device buffer of workspace_bytes >= the size query (may be
- *               NULL when the query returns 0).
+ *               NULL when the query returns 0, or when cu_seqlens is NULL),
+ *               16-byte aligned, not overlapping any argument; contents on
+ *               entry ignored, on return unspecified.  With cu_seqlens, a
+ *               first launch writes the sequences' longest-first order
+ *               into it and the prefill takes (sequence, head) pairs in
+ *               that order, so long sequences do not start last.
  *
  * Errors: KLA_ERR_INVALID_ARG for null required pointers, misalignment,
  * n_seqs <= 0, H <= 0, total_tok < 0, total_tok not divisible by n_seqs when

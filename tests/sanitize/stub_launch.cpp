@@ -12,6 +12,7 @@ hipError_t launch_decode_f32(const DecodeArgs &, hipStream_t) { return hipErrorN
 hipError_t launch_split_identity(const PrefillArgs &, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_split_scan(const PrefillArgs &, hipStream_t) { return hipErrorNotSupported; }
 hipError_t noalloc_scratch(void **) { return hipErrorNotSupported; }
+hipError_t launch_seq_order(const int32_t *, int, int32_t *, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_ccq_query(const CcqArgs &, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_ccq_decode_step(const CcqDecodeArgs &, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_add(float *, const float *, int64_t, hipStream_t) { return hipErrorNotSupported; }

@@ -299,7 +299,28 @@ def test_decode_ccq_rejects(lib, over, code):
 
 
 def test_workspace_query(lib):
-    assert lib.kla_fwd_chunked_workspace_size(8, 16384, 16, 128, 128, 64) == 0
+    # the longest-first order of 2 .. 1024 packed sequences: one int32 each, 256-byte rounded
+    assert lib.kla_fwd_chunked_workspace_size(8, 16384, 16, 128, 128, 64) == 256
+    assert lib.kla_fwd_chunked_workspace_size(64, 282233, 16, 128, 128, 64) == 256
+    assert lib.kla_fwd_chunked_workspace_size(65, 1000, 16, 128, 128, 64) == 512
+    assert lib.kla_fwd_chunked_workspace_size(1024, 1000, 16, 128, 128, 64) == 4096
+    assert lib.kla_fwd_chunked_workspace_size(1, 1000, 16, 128, 128, 64) == 0
+    assert lib.kla_fwd_chunked_workspace_size(1025, 100000, 16, 128, 128, 64) == 0
+
+
+def test_packed_needs_the_order_workspace(lib):
+    cu = BASE + 500 * MB
+    ws = BASE + 600 * MB
+    a = fwd_args(cu=cu)
+    assert lib.kla_fwd_chunked(*a) == WORKSPACE                    # none given
+    a = fwd_args(cu=cu, ws=ws, wsb=255)
+    assert lib.kla_fwd_chunked(*a) == WORKSPACE                    # short
+    a = fwd_args(cu=cu, ws=ws + 4, wsb=256)
+    assert lib.kla_fwd_chunked(*a) == INVALID                      # misaligned
+    a = fwd_args(cu=cu, ws=BASE + 256 * MB, wsb=256)
+    assert lib.kla_fwd_chunked(*a) == INVALID                      # overlaps o
+    a = fwd_args(cu=cu, ws=cu, wsb=256)
+    assert lib.kla_fwd_chunked(*a) == INVALID                      # overlaps cu_seqlens
 
 
 def dec_args(**over):

@@ -195,6 +195,21 @@ def test_ragged_lengths_with_initial_state(kla, d, dtype):
     assert torch.equal(S[4], s0[4])
 
 
+def test_packed_longest_first_with_ties(kla):
+    """Packed sequences with equal lengths (the longest-first order breaks
+    ties by index), an empty one and a single token, in an order the
+    schedule permutes; every sequence against the oracle."""
+    lengths = [70, 300, 70, 0, 300, 1, 70, 129, 64]
+    say(f"packed longest-first with ties lengths={lengths} H=3 + initial state")
+    inp = workloads.prefill(lengths=lengths, H=3, d=128, dtype="bf16", seed=31)
+    s0 = 0.3 * torch.randn((len(lengths), 3, 128, 128), generator=torch.Generator().manual_seed(4))
+    o, S = gpu_fwd(kla, inp, initial_state=s0)
+    ro, rS = ref_fwd(inp, initial_state=s0)
+    check("ties o", o, ro, TOL["bf16"])
+    check("ties S_T", S, rS, TOL["bf16"])
+    assert torch.equal(S[3], s0[3])
+
+
 def test_edge_gates_and_keys(kla):
     say("edges: zero keys, alpha=1, eta=0, 100x keys, length-1 sequence")
     inp = workloads.prefill(lengths=[150, 1, 77], H=4, d=128, dtype="bf16", seed=11)
