@@ -310,7 +310,7 @@ size_t kla_fwd_chunked_ccq_workspace_size(int64_t total_tok, int32_t H, int32_t 
                                           kla_dtype dtype) {
   if (total_tok <= 0 || H <= 0 || !supported_dim(dk, dv)) return 0;
   const size_t th = (size_t)total_tok * H;
-  if (dtype == KLA_BF16)  // q_clean hi and lo (bf16), the lo read's output (fp32)
+  if (dtype == KLA_BF16)  // q_clean hi and lo (bf16), the half-sequence sums' rows (fp32)
     return 2 * round_up(th * dk * 2) + round_up(th * dv * 4);
   return round_up(th * dk * 4);  // q_clean (fp32)
 }
@@ -379,8 +379,8 @@ kla_status kla_fwd_chunked_ccq(const void *q, const void *k, const void *v, cons
   c.ccq_out = ccq_out;
   c.qh = ws;
   c.ql = dtype == KLA_BF16 ? ws + round_up((size_t)th * dk * 2) : nullptr;
-  // the lo read's output area is free until that read: it holds the sums of
-  // the first halves of long sequences
+  // the third part of the workspace holds the sums of the first halves of
+  // long sequences (each in its own token rows) for the cleaning pass
   c.half_sums = dtype == KLA_BF16 ? reinterpret_cast<float *>(ws + 2 * round_up((size_t)th * dk * 2))
                                   : nullptr;
   hipError_t e = kla::launch_ccq_query(c, st);
@@ -401,20 +401,13 @@ kla_status kla_fwd_chunked_ccq(const void *q, const void *k, const void *v, cons
   // With no tokens the kernels only copy the start state and sums to the end
   // ones (workspace and query pointers are then never dereferenced).
   if (dtype == KLA_BF16) {
-    // o is linear in the query and the state does not depend on it: read
-    // with the lo part first (no end state, so an in-place start state is
-    // still intact), then with the hi part, and add.
-    float *o_lo = reinterpret_cast<float *>(ws + 2 * round_up((size_t)th * dk * 2));
-    a.o_write_back = 1;  // both outputs are read back by the sum
-    a.q = c.ql;
-    a.o = o_lo;
-    a.final_state = nullptr;
-    if (e == hipSuccess) e = kla::launch_prefill_bf16(a, st);
+    // one state pass that reads with both bf16 parts of the cleaned query:
+    // o = S^T (q_hi + q_lo)
     a.q = c.qh;
+    a.q_lo = c.ql;
     a.o = o;
     a.final_state = final_state;
     if (e == hipSuccess) e = kla::launch_prefill_bf16(a, st);
-    if (e == hipSuccess) e = kla::launch_add(o, o_lo, th * dv, st);
   } else {
     a.q = c.qh;
     a.o = o;

@@ -31,7 +31,8 @@
 // keep the whole m.  For bf16 inputs long sequences run as two halves (a
 // sums-only pass over the first halves, then both halves in parallel), so
 // that two workgroups share each CU.  Output: q_clean as fp32, or as a bf16 hi / lo pair
-// (q_clean = hi + lo to 2^-17), for the bf16 read.
+// (q_clean = hi + lo to 2^-17) for the bf16 prefill, which reads with both
+// planes in one state pass.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -76,8 +77,8 @@ __device__ inline void seg_to_f32(const uint4 &u, float *dst) {
 // whole sequence.  Sequences of at least LMIN tokens can instead be cut at a
 // chunk boundary into two halves: split_mode 1 (SUMS_ONLY) runs over the
 // first halves and leaves their end sums in half_sums, at the sequence's own
-// token rows (the output area of a later pass, unused until then; its
-// LMIN x H x D floats hold the H records); split_mode 2 then runs both
+// token rows (a scratch area of total_tok x H x D floats: a sequence's
+// LMIN x H x D floats hold its H records); split_mode 2 then runs both
 // halves, one workgroup each, the second starting from those sums, and every
 // shorter sequence whole.
 template <typename E, int D, bool OUT_BF16, bool SUMS_ONLY>
@@ -97,6 +98,8 @@ __global__ __launch_bounds__(kThreads) void ccq_query_kernel(
   static_assert(NSEG * kThreads == C * SEG_ROW, "staging tiling");
   constexpr int64_t REC = (int64_t)D * D + D + 4;  // record stride (floats)
   constexpr int64_t LMIN = (REC + D - 1) / D > C + 1 ? (REC + D - 1) / D : C + 1;
+  // a split sequence's H records fit its own LMIN x H x D floats of half_sums
+  static_assert(REC <= LMIN * D, "the half-sums records must fit a sequence's own rows");
   static_assert(!SUMS_ONLY || BF, "the sums-only pass serves bf16 inputs");
 
   __shared__ SM sm;
@@ -580,18 +583,6 @@ __global__ __launch_bounds__(kDecThreads) void ccq_decode_step_kernel(
   }
 }
 
-// o += o2 (fp32, n elements; n a multiple of 4, 16-byte aligned)
-__global__ __launch_bounds__(256) void add_kernel(float *__restrict__ o, const float *__restrict__ o2,
-                                                  int64_t n4) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    float4 a = reinterpret_cast<float4 *>(o)[i];
-    const float4 b = reinterpret_cast<const float4 *>(o2)[i];
-    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-    reinterpret_cast<float4 *>(o)[i] = a;
-  }
-}
-
 }  // namespace
 
 hipError_t launch_ccq_query(const CcqArgs &a, hipStream_t st) {
@@ -632,13 +623,6 @@ hipError_t launch_ccq_decode_step(const CcqDecodeArgs &a, hipStream_t st) {
     if (a.D == 128) KLA_CCQ_DEC_LAUNCH(float, 128); else KLA_CCQ_DEC_LAUNCH(float, 64);
   }
 #undef KLA_CCQ_DEC_LAUNCH
-  return hipGetLastError();
-}
-
-hipError_t launch_add(float *o, const float *o2, int64_t n, hipStream_t st) {
-  const int64_t n4 = n / 4;
-  const int64_t blocks = (n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096;
-  if (blocks > 0) hipLaunchKernelGGL(add_kernel, dim3((unsigned)blocks), dim3(256), 0, st, o, o2, n4);
   return hipGetLastError();
 }
 

@@ -8,6 +8,8 @@ namespace kla {
 
 struct PrefillArgs {
   const void *q, *k, *v;
+  // bf16 prefill only, nullable: the lo plane of a split query (q + q_lo)
+  const void *q_lo = nullptr;
   const float *alpha, *eta;   // alpha nullable (alpha = 1)
   const int32_t *cu_seqlens;  // device, or nullptr for dense
   int32_t n_seqs;
@@ -120,11 +122,10 @@ hipError_t launch_split_scan(const PrefillArgs &a, hipStream_t s);
 // with hipGetSymbolAddress and kept.
 hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_decode_f32(const DecodeArgs &a, hipStream_t s);
-// CCQ: the prefill pre-pass (q_clean for every token), the fused decode
-// step, and o += o2.
+// CCQ: the prefill pre-pass (q_clean for every token) and the fused decode
+// step.
 hipError_t launch_ccq_query(const CcqArgs &a, hipStream_t s);
 hipError_t launch_ccq_decode_step(const CcqDecodeArgs &a, hipStream_t s);
-hipError_t launch_add(float *o, const float *o2, int64_t n, hipStream_t s);
 // Per-channel decay prefill (alpha [total_tok, H, D]); whole sequences only.
 hipError_t launch_prefill_kda(const PrefillArgs &a, bool bf16_inputs, hipStream_t s);
 // bf16 prefill without output (whole sequences): every chunk-start state to

@@ -619,56 +619,76 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 //
 // Eight waves per workgroup.  Waves 0-3 (consumers) own 16 state columns
 // each and run the state-dependent chain of chunk c; waves 4-7 (producers)
-// stage chunk c+1 in LDS and compute its Gram tiles and diagonal-block
-// inverses at the same time.  Each SIMD hosts one consumer and one producer,
-// so the two halves of the chunk work overlap instead of running in turn.
-// Chunk data lives in two LDS slots used alternately; per chunk:
-//   segment A: producers stage chunk c+1 (and prefetch c+2 from HBM);
-//              consumers form Q S, K S and R for chunk c;
+// stage the chunks and build their Gram tiles and diagonal-block inverses.
+// Each SIMD hosts one consumer and one producer.  Per chunk c:
+//   segment A: consumers form Q S, K S and R for chunk c;
+//              producers stage K of chunk c+1 and scan its decays, and
+//              build chunk c's M = lower(Q K^T o Gam) planes;
 //   barrier;
-//   segment B: producers build chunk c+1's operand planes;
-//              consumers run the substitution, output and state update of c;
+//   segment B: consumers run the substitution, output and state update of c;
+//              producers build chunk c+1's -Ahat planes and diagonal-block
+//              inverses, and stage Q and V of chunk c+1;
 //   barrier.
+// K, the -Ahat and Y planes and the gates live in two slots (chunk parity);
+// Q, V and the M planes have one buffer each: Q and V of chunk c are read
+// only in segment A of c and chunk c+1's are staged in segment B, and M of
+// chunk c is built in segment A of c and read in segment B of c.
+//
+// QLO: the query is a pair of bf16 planes, q + q_lo (a split fp32 query).
+// The lo plane enters Q S as q_lo S_hi and the M planes as q_lo K^T; its
+// share of the output is about 2^-8 of the whole, so the terms dropped
+// (q_lo S_lo) are below 2^-16 of the output.
 // ===========================================================================
 
-template <int D>
+// SQ (single query buffer, the two-plane read): Q, its lo plane, V and the
+// M planes have one buffer each; otherwise they live in the two slots with
+// K, the -Ahat and Y planes and the gates.
+template <int D, bool OUT, bool SQ>
 struct PSlot {
   using CF = Cfg<bf16, D>;
+  static constexpr bool PER_SLOT = OUT && !SQ;
   static constexpr int LDA = 20;  // compact 16x16 blocks of -Ahat and Y
   alignas(16) bf16 Kr[C * CF::LDK];
-  alignas(16) bf16 Qr[C * CF::LDK];
-  alignas(16) bf16 Vs[C * CF::LDV];
+  alignas(16) bf16 Qr[PER_SLOT ? C * CF::LDK : 8];
+  alignas(16) bf16 Vs[SQ ? 8 : C * CF::LDV];
   alignas(16) bf16 Ah[6 * 16 * LDA];  // -Ahat blocks (b, m), m < b, index b(b-1)/2 + m
   alignas(16) bf16 Al[6 * 16 * LDA];
-  alignas(16) bf16 Mh[C * CF::LDP];   // M = lower(Q K^T o Gam), zero above the block diagonal
-  alignas(16) bf16 Ml[C * CF::LDP];
+  alignas(16) bf16 Mh[PER_SLOT ? C * CF::LDP : 8];  // M = lower(Q K^T o Gam), zero above the block diagonal
+  alignas(16) bf16 Ml[PER_SLOT ? C * CF::LDP : 8];
   static constexpr int LDYT = 24;     // Y^T rows: 16 values + pad, 16-byte aligned
   alignas(16) bf16 Yh[4 * 16 * LDYT];  // Y_bb^T, Y_bb = (I + L_bb)^{-1} Diag(beta_b)
   alignas(16) bf16 Yl[4 * 16 * LDYT];
   alignas(16) float gam[C];
   alignas(16) float rgam[C];
+  alignas(16) float g2[C];            // cumulative log2-decay
 };
-template <int D>
+template <int D, bool OUT, bool SQ>
 struct PSmem {
-  PSlot<D> slot[2];
+  using CF = Cfg<bf16, D>;
+  PSlot<D, OUT, SQ> slot[2];
+  alignas(16) bf16 Qr[SQ ? C * CF::LDK : 8];
+  alignas(16) bf16 Qlr[SQ ? C * CF::LDK : 8];
+  alignas(16) bf16 Vs[SQ ? C * CF::LDV : 8];
+  alignas(16) bf16 Mh[SQ ? C * CF::LDP : 8];
+  alignas(16) bf16 Ml[SQ ? C * CF::LDP : 8];
   // producer scratch for the chunk being prepared
   alignas(16) float Ld[4 * 16 * 20];  // -Diag(beta) Ahat below the diagonal of the diagonal blocks, [block][col][row]
   alignas(16) float kk[C];
   alignas(16) float et[C];
   alignas(16) float beta[C];
-  alignas(16) float g2[C];
 };
 
 // OUT = false: the segment-map pass, which writes no output and so needs
 // neither Q nor M (only K, V, the gates and the -Ahat, Y planes).
-template <int D, bool OUT>
+template <int D, bool OUT, bool QLO>
 __global__ __launch_bounds__(512) void prefill_pc_kernel(
-    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ q, const bf16 *__restrict__ q_lo, const bf16 *__restrict__ k,
+    const bf16 *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ eta,
     const int32_t *__restrict__ cu_seqlens, int64_t seq_len_dense, int H, float eps, int beta_direct,
     const float *__restrict__ S0, float *__restrict__ o, float *__restrict__ Sfin, SegParams sp) {
   using CF = Cfg<bf16, D>;
-  using SL = PSlot<D>;
+  using SL = PSlot<D, OUT, QLO>;
   constexpr int LDA = SL::LDA;
   constexpr int NB = D / DVB;
   constexpr int NST = CF::NST;
@@ -680,7 +700,8 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
   constexpr int NVSEG = C * SEG_VROW / PT;
   static_assert(NSEG * PT == C * SEG_ROW && NVSEG * PT == C * SEG_VROW, "tiling");
 
-  __shared__ PSmem<D> sm;
+  static_assert(OUT || !QLO, "a second query plane needs the output");
+  __shared__ PSmem<D, OUT, QLO> sm;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -695,34 +716,42 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
   const int64_t bos = wk.bos, eos = wk.eos;
   const int col = nb * DVB + 16 * w + c16;  // consumer lane's state/output column
 
-  // M above the block diagonal is read as zero (both slots).
-  for (int i = tid; i < C * CF::LDP; i += 512) {
-    sm.slot[0].Mh[i] = bf16(0.f);
-    sm.slot[0].Ml[i] = bf16(0.f);
-    sm.slot[1].Mh[i] = bf16(0.f);
-    sm.slot[1].Ml[i] = bf16(0.f);
+  // Q, V and M of a chunk: in its slot, or in the single buffers (QLO)
+  auto QB = [&](SL &sl) __attribute__((always_inline)) -> bf16 * {
+    if constexpr (QLO) return sm.Qr; else return sl.Qr;
+  };
+  auto VB = [&](SL &sl) __attribute__((always_inline)) -> bf16 * {
+    if constexpr (QLO) return sm.Vs; else return sl.Vs;
+  };
+  auto MHB = [&](SL &sl) __attribute__((always_inline)) -> bf16 * {
+    if constexpr (QLO) return sm.Mh; else return sl.Mh;
+  };
+  auto MLB = [&](SL &sl) __attribute__((always_inline)) -> bf16 * {
+    if constexpr (QLO) return sm.Ml; else return sl.Ml;
+  };
+  // M above the block diagonal is read as zero.
+  if constexpr (OUT) {
+    for (int i = tid; i < C * CF::LDP; i += 512) {
+      MHB(sm.slot[0])[i] = bf16(0.f);
+      MLB(sm.slot[0])[i] = bf16(0.f);
+      MHB(sm.slot[1])[i] = bf16(0.f);
+      MLB(sm.slot[1])[i] = bf16(0.f);
+    }
   }
 
   // ---- producer pieces ------------------------------------------------------
-  uint4 kreg[NSEG], qreg[NSEG], vreg[NVSEG];
+  // K and the gates of a chunk are fetched into registers two chunks ahead
+  // of their consumption and staged in segment A; Q (and its lo plane) and
+  // V likewise, staged in segment B.
+  uint4 kreg[NSEG], qreg[NSEG], qlreg[QLO ? NSEG : 1], vreg[NVSEG];
   float areg = 1.f, ereg = 0.f;
-  auto fetch = [&](int64_t t0) {  // HBM -> registers (zeros past the end)
+  auto fetch_k = [&](int64_t t0) __attribute__((always_inline)) {  // HBM -> registers (zeros past the end)
     const int64_t nn = (eos - t0) < C ? (eos - t0) : C;
-    const int64_t rowb = (int64_t)H * D * 2;
-    const rsrc_t rk = make_rsrc(k + t0 * H * (int64_t)D, nn * rowb);
-    const rsrc_t rq = make_rsrc(q + t0 * H * (int64_t)D, nn * rowb);
-    const rsrc_t rv = make_rsrc(v + t0 * H * (int64_t)D, wk.vb >= 0 ? nn * rowb : 0);  // V = 0 for A blocks
+    const rsrc_t rk = make_rsrc(k + t0 * H * (int64_t)D, nn * (int64_t)H * D * 2);
 #pragma unroll
     for (int u = 0; u < NSEG; ++u) {
       const int sg = u * PT + ptid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
-      const uint32_t off = (uint32_t)((r * H + h) * D + cs * SEG_EL) * 2;
-      kreg[u] = buf_ld16(rk, off);
-      if constexpr (OUT) qreg[u] = buf_ld16(rq, off);
-    }
-#pragma unroll
-    for (int u = 0; u < NVSEG; ++u) {
-      const int sg = u * PT + ptid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
-      vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + wk.vb * DVB + cs * SEG_EL) * 2);
+      kreg[u] = buf_ld16(rk, (uint32_t)((r * H + h) * D + cs * SEG_EL) * 2);
     }
     if (pw == 0) {
       // no alpha: an empty range (the scan then takes log alpha = 0)
@@ -732,174 +761,251 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       ereg = buf_ld4(re, (uint32_t)(l * H + h) * 4);
     }
   };
-  auto stage = [&](SL &sl, int64_t t0) {  // registers -> LDS slot, row norms, decay scan
+  auto fetch_qv = [&](int64_t t0) __attribute__((always_inline)) {
+    const int64_t nn = (eos - t0) < C ? (eos - t0) : C;
+    const int64_t rowb = (int64_t)H * D * 2;
+    const rsrc_t rv = make_rsrc(v + t0 * H * (int64_t)D, wk.vb >= 0 ? nn * rowb : 0);  // V = 0 for A blocks
+    if constexpr (OUT) {
+      const rsrc_t rq = make_rsrc(q + t0 * H * (int64_t)D, nn * rowb);
+      const rsrc_t rql = make_rsrc(QLO ? q_lo + t0 * H * (int64_t)D : q, QLO ? nn * rowb : 0);
 #pragma unroll
-    for (int u = 0; u < NSEG; ++u) {
-      const int sg = u * PT + ptid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
-      *reinterpret_cast<uint4 *>(&sl.Kr[r * CF::LDK + cs * SEG_EL]) = kreg[u];
-      if constexpr (OUT) *reinterpret_cast<uint4 *>(&sl.Qr[r * CF::LDK + cs * SEG_EL]) = qreg[u];
+      for (int u = 0; u < NSEG; ++u) {
+        const int sg = u * PT + ptid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+        const uint32_t off = (uint32_t)((r * H + h) * D + cs * SEG_EL) * 2;
+        qreg[u] = buf_ld16(rq, off);
+        if constexpr (QLO) qlreg[u] = buf_ld16(rql, off);
+      }
     }
 #pragma unroll
     for (int u = 0; u < NVSEG; ++u) {
       const int sg = u * PT + ptid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
-      *reinterpret_cast<uint4 *>(&sl.Vs[r * CF::LDV + cs * SEG_EL]) = vreg[u];
+      vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + wk.vb * DVB + cs * SEG_EL) * 2);
+    }
+  };
+  auto stage_k = [&](SL &sl, int64_t t0) __attribute__((always_inline)) {  // K and the decays into a slot
+#pragma unroll
+    for (int u = 0; u < NSEG; ++u) {
+      const int sg = u * PT + ptid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+      *reinterpret_cast<uint4 *>(&sl.Kr[r * CF::LDK + cs * SEG_EL]) = kreg[u];
     }
     if (pw == 0) {
       sm.et[l] = ereg;
       const float g = wave_scan(alpha && l < eos - t0 ? flog2(areg) : 0.f);  // alpha = 1 past the end
       const float glast = __shfl(g, 63, 64);
-      sm.g2[l] = g;
+      sl.g2[l] = g;
       sl.gam[l] = fexp2(g);
       sl.rgam[l] = fexp2(glast - g);
     }
   };
-  auto wave_sync = [&]() {  // order this wave's LDS writes before its reads
+  auto stage_qv = [&](SL &sl) __attribute__((always_inline)) {  // Q (+ lo plane) and V
+    if constexpr (OUT) {
+      bf16 *qb = QB(sl);
+#pragma unroll
+      for (int u = 0; u < NSEG; ++u) {
+        const int sg = u * PT + ptid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+        *reinterpret_cast<uint4 *>(&qb[r * CF::LDK + cs * SEG_EL]) = qreg[u];
+        if constexpr (QLO) *reinterpret_cast<uint4 *>(&sm.Qlr[r * CF::LDK + cs * SEG_EL]) = qlreg[u];
+      }
+    }
+    bf16 *vb = VB(sl);
+#pragma unroll
+    for (int u = 0; u < NVSEG; ++u) {
+      const int sg = u * PT + ptid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
+      *reinterpret_cast<uint4 *>(&vb[r * CF::LDV + cs * SEG_EL]) = vreg[u];
+    }
+  };
+  auto wave_sync = [&]() __attribute__((always_inline)) {  // order this wave's LDS writes before its reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  auto prepare = [&](SL &sl) {  // Gram tiles, diagonal inverses, operand planes
-    if (pw == 0) {
-      f32x4 dg[4];
+  // Gram jobs q0 .. q0+nj-1 of a slot's chunk (numbering of job_of: 0-5 the
+  // -Ahat blocks, 6-15 the M blocks).  Each tile is computed transposed,
+  // C[s][r] = K[s] . (Q or K)[r], so a lane holds four consecutive s of one
+  // row r and writes them as one 8-byte store per plane.  Operands of the
+  // next job are loaded first.
+  auto jobs = [&](SL &sl, int q0, int nj) __attribute__((always_inline)) {
+    bf16 *const qb = QB(sl);
+    bf16x8 opa[2][D / 32], opb[2][D / 32], opl[2][QLO ? D / 32 : 1];
+    float grb[2];
+    f32x4 gsb[2];
+    auto ldjob = [&](int u) __attribute__((always_inline)) {  // operands and gates of job u
+      const Job jb = job_of(q0 + u);
+      const bf16 *B = jb.qk ? qb : sl.Kr;
+      grb[u & 1] = sl.g2[16 * jb.bi + c16];
+      gsb[u & 1] = *reinterpret_cast<const f32x4 *>(&sl.g2[16 * jb.bj + 4 * j]);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) dg[b] = gram_tile<bf16, D>(sl.Kr, sl.Kr, 16 * b, 16 * b, j, c16);
-      // |k_r|^2 is the diagonal: row 16b + c16 sits in lane (c16 / 4, c16), element c16 % 4
-      if ((c16 >> 2) == j) {
-        const int e = c16 & 3;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          sm.kk[16 * b + c16] = e == 0 ? dg[b][0] : e == 1 ? dg[b][1] : e == 2 ? dg[b][2] : dg[b][3];
+      for (int t = 0; t < D / 32; ++t) {
+        opa[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&sl.Kr[(16 * jb.bj + c16) * CF::LDK + 32 * t + 8 * j]);
+        opb[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&B[(16 * jb.bi + c16) * CF::LDK + 32 * t + 8 * j]);
+        if constexpr (QLO) {
+          if (jb.qk) opl[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&sm.Qlr[(16 * jb.bi + c16) * CF::LDK + 32 * t + 8 * j]);
+        }
       }
-      wave_sync();
-      sm.beta[l] = beta_direct ? sm.et[l] : sm.et[l] / (sm.kk[l] + eps);
-      wave_sync();
-      // every gate and beta this lane needs first, then the 16 values, then
-      // one 16-byte write per block (rows 4j..4j+3 of column c16)
-      f32x4 gr[4], br[4];
-      float gc[4];
+    };
+    if (nj > 0) ldjob(0);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        gr[b] = *reinterpret_cast<const f32x4 *>(&sm.g2[16 * b + 4 * j]);
-        br[b] = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * b + 4 * j]);
-        gc[b] = sm.g2[16 * b + c16];
-      }
+    for (int u = 0; u < 4; ++u) {
+      if (u < nj) {
+        if (u + 1 < nj) ldjob(u + 1);
+        sched_fence();
+        const Job jb = job_of(q0 + u);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        f32x4 val;
+        for (int t = 0; t < D / 32; ++t) acc = mma(opa[u & 1][t], opb[u & 1][t], acc);
+        if constexpr (QLO) {
+          if (jb.qk) {
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t) acc = mma(opa[u & 1][t], opl[u & 1][t], acc);
+          }
+        }
+        sched_fence();
+        const int r = 16 * jb.bi + c16;  // this lane's row
+        const float gr = grb[u & 1];
+        const f32x4 gsv = gsb[u & 1];
+        f32x4 vals;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float x = -br[b][i] * dg[b][i] * fexp2(fminf(gr[b][i] - gc[b], 0.f));
-          val[i] = 4 * j + i > c16 ? x : 0.f;  // -L below the diagonal
+          const int sc = 16 * jb.bj + 4 * j + i;
+          const float val = acc[i] * fexp2(fminf(gr - gsv[i], 0.f));
+          vals[i] = jb.qk ? (r >= sc ? val : 0.f) : -val;
         }
-        *reinterpret_cast<f32x4 *>(&sm.Ld[(b * 16 + c16) * 20 + 4 * j]) = val;
-      }
-      wave_sync();
-      // lane (block j, column c16): column c16 of (I + L_jj)^{-1}, DPP substitution
-      float lc[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 v4 = *reinterpret_cast<const float4 *>(&sm.Ld[(j * 16 + c16) * 20 + 4 * q4]);
-        lc[4 * q4] = v4.x;
-        lc[4 * q4 + 1] = v4.y;
-        lc[4 * q4 + 2] = v4.z;
-        lc[4 * q4 + 3] = v4.w;
-      }
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == c16) ? 1.f : 0.f;
-      solve_steps(x, lc, std::make_integer_sequence<int, 15>{});
-      const float bc = sm.beta[16 * j + c16];
-      // column c16 of Y_jj, contiguous in Y^T: two 16-byte writes per plane
-      Split4 yq[4];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        yq[q4] = split4(f32x4{x[4 * q4] * bc, x[4 * q4 + 1] * bc, x[4 * q4 + 2] * bc, x[4 * q4 + 3] * bc});
-      const bf16x8 yh0 = __builtin_shufflevector(yq[0].hi, yq[1].hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 yh1 = __builtin_shufflevector(yq[2].hi, yq[3].hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 yl0 = __builtin_shufflevector(yq[0].lo, yq[1].lo, 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 yl1 = __builtin_shufflevector(yq[2].lo, yq[3].lo, 0, 1, 2, 3, 4, 5, 6, 7);
-      const int yo = (j * 16 + c16) * SL::LDYT;
-      *reinterpret_cast<bf16x8 *>(&sl.Yh[yo]) = yh0;
-      *reinterpret_cast<bf16x8 *>(&sl.Yh[yo + 8]) = yh1;
-      *reinterpret_cast<bf16x8 *>(&sl.Yl[yo]) = yl0;
-      *reinterpret_cast<bf16x8 *>(&sl.Yl[yo + 8]) = yl1;
-    }
-    {
-      // producer waves 1, 2, 3 take Gram jobs [0,5), [5,10), [10,15) and
-      // wave 0 job 15 after its solve.  Each tile is computed transposed,
-      // C[s][r] = K[s] . (Q or K)[r], so a lane holds four consecutive s of
-      // one row r and writes them as one 8-byte store per plane.  Operands
-      // of the next job are loaded first.
-      // (without output only the six -Ahat jobs: two each for waves 1-3)
-      const int q0 = OUT ? (pw == 0 ? 15 : 5 * (pw - 1)) : 2 * (pw - 1);
-      const int nj = OUT ? (pw == 0 ? 1 : 5) : (pw == 0 ? 0 : 2);
-      bf16x8 opa[2][D / 32], opb[2][D / 32];
-      float grb[2];
-      f32x4 gsb[2];
-      auto ldjob = [&](int u) {  // operands and gates of job u
-        const Job jb = job_of(q0 + u);
-        const bf16 *B = jb.qk ? sl.Qr : sl.Kr;
-        grb[u & 1] = sm.g2[16 * jb.bi + c16];
-        gsb[u & 1] = *reinterpret_cast<const f32x4 *>(&sm.g2[16 * jb.bj + 4 * j]);
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          opa[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&sl.Kr[(16 * jb.bj + c16) * CF::LDK + 32 * t + 8 * j]);
-          opb[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&B[(16 * jb.bi + c16) * CF::LDK + 32 * t + 8 * j]);
-        }
-      };
-      if (nj > 0) ldjob(0);
-#pragma unroll
-      for (int u = 0; u < 6; ++u) {
-        if (u < nj) {
-          if (u + 1 < nj) ldjob(u + 1);
-          sched_fence();
-          const Job jb = job_of(q0 + u);
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int t = 0; t < D / 32; ++t) acc = mma(opa[u & 1][t], opb[u & 1][t], acc);
-          sched_fence();
-          const int r = 16 * jb.bi + c16;  // this lane's row
-          const float gr = grb[u & 1];
-          const f32x4 gsv = gsb[u & 1];
-          f32x4 vals;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int sc = 16 * jb.bj + 4 * j + i;
-            const float val = acc[i] * fexp2(fminf(gr - gsv[i], 0.f));
-            vals[i] = jb.qk ? (r >= sc ? val : 0.f) : -val;
-          }
-          const Split4 sp = split4(vals);
-          if (jb.qk) {
-            const int off = r * CF::LDP + 16 * jb.bj + 4 * j;
-            *reinterpret_cast<bf16x4 *>(&sl.Mh[off]) = sp.hi;
-            *reinterpret_cast<bf16x4 *>(&sl.Ml[off]) = sp.lo;
-          } else {
-            const int off = ((jb.bi * (jb.bi - 1) / 2 + jb.bj) * 16 + c16) * LDA + 4 * j;
-            *reinterpret_cast<bf16x4 *>(&sl.Ah[off]) = sp.hi;
-            *reinterpret_cast<bf16x4 *>(&sl.Al[off]) = sp.lo;
-          }
+        const Split4 sp = split4(vals);
+        if (jb.qk) {
+          const int off = r * CF::LDP + 16 * jb.bj + 4 * j;
+          *reinterpret_cast<bf16x4 *>(&MHB(sl)[off]) = sp.hi;
+          *reinterpret_cast<bf16x4 *>(&MLB(sl)[off]) = sp.lo;
+        } else {
+          const int off = ((jb.bi * (jb.bi - 1) / 2 + jb.bj) * 16 + c16) * LDA + 4 * j;
+          *reinterpret_cast<bf16x4 *>(&sl.Ah[off]) = sp.hi;
+          *reinterpret_cast<bf16x4 *>(&sl.Al[off]) = sp.lo;
         }
       }
     }
+  };
+  // The diagonal blocks of a slot's chunk (producer wave 0): the diagonal
+  // K K^T tiles, |k|^2 off their diagonal, beta, -L on the diagonal blocks
+  // and the four 16x16 inverses Y_bb (one DPP column substitution per lane:
+  // lane (j, c16) solves column c16 of block j).
+  auto diag = [&](SL &sl) __attribute__((always_inline)) {
+    f32x4 dg[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) dg[b] = gram_tile<bf16, D>(sl.Kr, sl.Kr, 16 * b, 16 * b, j, c16);
+    // |k_r|^2 is the diagonal: row 16b + c16 sits in lane (c16 / 4, c16), element c16 % 4
+    if ((c16 >> 2) == j) {
+      const int e = c16 & 3;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        sm.kk[16 * b + c16] = e == 0 ? dg[b][0] : e == 1 ? dg[b][1] : e == 2 ? dg[b][2] : dg[b][3];
+    }
+    wave_sync();
+    sm.beta[l] = beta_direct ? sm.et[l] : sm.et[l] / (sm.kk[l] + eps);
+    wave_sync();
+    // every gate and beta this lane needs first, then the 16 values, then
+    // one 16-byte write per block (rows 4j..4j+3 of column c16)
+    f32x4 gr[4], br[4];
+    float gc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      gr[b] = *reinterpret_cast<const f32x4 *>(&sl.g2[16 * b + 4 * j]);
+      br[b] = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * b + 4 * j]);
+      gc[b] = sl.g2[16 * b + c16];
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      f32x4 val;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = -br[b][i] * dg[b][i] * fexp2(fminf(gr[b][i] - gc[b], 0.f));
+        val[i] = 4 * j + i > c16 ? x : 0.f;  // -L below the diagonal
+      }
+      *reinterpret_cast<f32x4 *>(&sm.Ld[(b * 16 + c16) * 20 + 4 * j]) = val;
+    }
+    wave_sync();
+    float lc[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 v4 = *reinterpret_cast<const float4 *>(&sm.Ld[(j * 16 + c16) * 20 + 4 * q4]);
+      lc[4 * q4] = v4.x;
+      lc[4 * q4 + 1] = v4.y;
+      lc[4 * q4 + 2] = v4.z;
+      lc[4 * q4 + 3] = v4.w;
+    }
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = (r == c16) ? 1.f : 0.f;
+    solve_steps(x, lc, std::make_integer_sequence<int, 15>{});
+    const float bc = sm.beta[16 * j + c16];
+    // column c16 of Y_jj, contiguous in Y^T: two 16-byte writes per plane
+    Split4 yq[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      yq[q4] = split4(f32x4{x[4 * q4] * bc, x[4 * q4 + 1] * bc, x[4 * q4 + 2] * bc, x[4 * q4 + 3] * bc});
+    const int yo = (j * 16 + c16) * SL::LDYT;
+    *reinterpret_cast<bf16x8 *>(&sl.Yh[yo]) = __builtin_shufflevector(yq[0].hi, yq[1].hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    *reinterpret_cast<bf16x8 *>(&sl.Yh[yo + 8]) = __builtin_shufflevector(yq[2].hi, yq[3].hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    *reinterpret_cast<bf16x8 *>(&sl.Yl[yo]) = __builtin_shufflevector(yq[0].lo, yq[1].lo, 0, 1, 2, 3, 4, 5, 6, 7);
+    *reinterpret_cast<bf16x8 *>(&sl.Yl[yo + 8]) = __builtin_shufflevector(yq[2].lo, yq[3].lo, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // Where the Gram jobs of a chunk run (numbering of job_of).  Any job of
+  // chunk c may run in segment B of the trip before c or in segment A of
+  // c's trip; the split balances the two segments.
+  //   two slots:  segment B before c: wave 0 the diagonal blocks, waves 1-3
+  //               jobs 0-3, 4-7, 8-11 (only the -Ahat jobs 0-5 without
+  //               output: 0-1, 2-3, 4-5); segment A of c: jobs 12-15, one
+  //               per wave;
+  //   single Q (QLO): Q of c is staged in segment B before c, so its M
+  //               jobs wait for segment A of c: wave 0 job 6, waves 1-3
+  //               jobs 7-9, 10-12, 13-15; segment B before c: wave 0 the
+  //               diagonal blocks, waves 1-3 two -Ahat jobs each.
+  auto seg_a_jobs = [&](SL &cs) __attribute__((always_inline)) {
+    if constexpr (QLO)
+      jobs(cs, pw == 0 ? 6 : 4 + 3 * pw, pw == 0 ? 1 : 3);
+    else if constexpr (OUT)
+      jobs(cs, 12 + pw, 1);
+  };
+  auto seg_b_jobs = [&](SL &nx) __attribute__((always_inline)) {
+    if (pw == 0)
+      diag(nx);
+    else if constexpr (OUT && !QLO)
+      jobs(nx, 4 * (pw - 1), 4);
+    else
+      jobs(nx, 2 * (pw - 1), 2);
   };
 
   // The two roles run separate loops with the same number of barriers, so
   // neither role's loop-carried registers are live in the other's code.
   if (producer) {
-    // prologue: chunk 0 into slot 0
-    fetch(bos);
-    stage(sm.slot[0], bos);
-    fetch(bos + C);
+    // prologue: chunk 0 (K, gates, Q, V) staged and its segment-B jobs;
+    // chunk 1 fetched
+    fetch_k(bos);
+    fetch_qv(bos);
+    stage_k(sm.slot[0], bos);
+    stage_qv(sm.slot[0]);
+    fetch_k(bos + C);
+    fetch_qv(bos + C);
     lds_barrier();
-    if (bos < eos) prepare(sm.slot[0]);
+    if (bos < eos) seg_b_jobs(sm.slot[0]);
     lds_barrier();
     int cur = 0;
     for (int64_t tok0 = bos; tok0 < eos; tok0 += C, cur ^= 1) {
-      SL &nx = sm.slot[cur ^ 1];
-      stage(nx, tok0 + C);       // segment A
-      fetch(tok0 + 2 * C);
+      SL &cs = sm.slot[cur], &nx = sm.slot[cur ^ 1];
+      // segment A: chunk c+1's K (with Q and V in the two-slot layout), then
+      // chunk c's remaining jobs
+      stage_k(nx, tok0 + C);
+      fetch_k(tok0 + 2 * C);
+      if constexpr (!QLO) {
+        stage_qv(nx);
+        fetch_qv(tok0 + 2 * C);
+      }
+      seg_a_jobs(cs);
       lds_barrier();
-      if (tok0 + C < eos) prepare(nx);  // segment B
+      // segment B: (QLO: chunk c+1's Q and V, then) chunk c+1's first jobs
+      if constexpr (QLO) {
+        stage_qv(nx);
+        fetch_qv(tok0 + 2 * C);
+      }
+      if (tok0 + C < eos) seg_b_jobs(nx);
       lds_barrier();
     }
     return;
@@ -944,10 +1050,11 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       }
       // steps run kk-major so consecutive MFMAs update different tiles; the
       // A operands are loaded two steps ahead
-      bf16x8 qa[3], ka[3];
+      bf16x8 qa[3], ka[3], qla[QLO ? 3 : 1];
       auto ld = [&](int st) {
         const int kk = st / 4, bi = st % 4;
-        if constexpr (OUT) qa[st % 3] = lda_perm(&sl.Qr[(16 * bi + c16) * CF::LDK + 32 * kk], j);
+        if constexpr (OUT) qa[st % 3] = lda_perm(&QB(sl)[(16 * bi + c16) * CF::LDK + 32 * kk], j);
+        if constexpr (QLO) qla[st % 3] = lda_perm(&sm.Qlr[(16 * bi + c16) * CF::LDK + 32 * kk], j);
         ka[st % 3] = lda_perm(&sl.Kr[(16 * bi + c16) * CF::LDK + 32 * kk], j);
       };
       ld(0);
@@ -964,12 +1071,13 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
         R[bi] = mma(ka[st % 3], Sf[kk].hi, R[bi]);
         if constexpr (OUT) QS[bi] = mma(Sf[kk].lo, qa[st % 3], QS[bi]);
         R[bi] = mma(ka[st % 3], Sf[kk].lo, R[bi]);
+        if constexpr (QLO) QS[bi] = mma(Sf[kk].hi, qla[st % 3], QS[bi]);
         sched_fence();
       }
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) {
         // V rows 16bi+4j..+3 of this lane's column, one transposing read
-        const bf16x4 vv = ld_tr(&sl.Vs[(16 * bi + 4 * j + (c16 >> 2)) * CF::LDV + 16 * w + 4 * (c16 & 3)]);
+        const bf16x4 vv = ld_tr(&VB(sl)[(16 * bi + 4 * j + (c16 >> 2)) * CF::LDV + 16 * w + 4 * (c16 & 3)]);
         const f32x4 gv = *reinterpret_cast<const f32x4 *>(&sl.gam[16 * bi + 4 * j]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) R[bi][i] = static_cast<float>(vv[i]) - gv[i] * R[bi][i];
@@ -1027,8 +1135,8 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
           auto ld = [&](int st) {
             const int kk = st < 4 ? 0 : 1, bi = st < 4 ? st : st - 2;
             const int off = (16 * bi + c16) * CF::LDP + 32 * kk;
-            mh[st % 3] = lda_perm(&sl.Mh[off], j);
-            ml[st % 3] = lda_perm(&sl.Ml[off], j);
+            mh[st % 3] = lda_perm(&MHB(sl)[off], j);
+            ml[st % 3] = lda_perm(&MLB(sl)[off], j);
           };
           ld(0);
           ld(1);
@@ -1156,11 +1264,14 @@ inline SegParams seg_of(const PrefillArgs &a) {
 template <int D>
 hipError_t launch_pc(const PrefillArgs &a, hipStream_t st) {
   const int64_t grid = grid_of(a, D / DVB);
-  auto kern = a.seg_mode == 1 ? prefill_pc_kernel<D, false> : prefill_pc_kernel<D, true>;
+  auto kern = a.seg_mode == 1 ? prefill_pc_kernel<D, false, false>
+              : a.q_lo        ? prefill_pc_kernel<D, true, true>
+                              : prefill_pc_kernel<D, true, false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, st,
-                     static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
-                     static_cast<const bf16 *>(a.v), a.alpha, a.eta, a.cu_seqlens, a.seq_len_dense,
-                     a.H, a.eps, a.beta_direct, a.initial_state, a.o, a.final_state, seg_of(a));
+                     static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.q_lo),
+                     static_cast<const bf16 *>(a.k), static_cast<const bf16 *>(a.v), a.alpha,
+                     a.eta, a.cu_seqlens, a.seq_len_dense, a.H, a.eps, a.beta_direct,
+                     a.initial_state, a.o, a.final_state, seg_of(a));
   return hipGetLastError();
 }
 
@@ -1209,11 +1320,12 @@ hipError_t launch_prefill_states(const PrefillArgs &a, hipStream_t st) {
   b.seg_mode = 3;
   b.n_splits = 1;
   const int64_t grid = (int64_t)a.n_seqs * a.H * (a.D / DVB);
-  auto kern = a.D == 128 ? prefill_pc_kernel<128, false> : prefill_pc_kernel<64, false>;
+  auto kern = a.D == 128 ? prefill_pc_kernel<128, false, false> : prefill_pc_kernel<64, false, false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, st,
-                     static_cast<const bf16 *>(b.q), static_cast<const bf16 *>(b.k),
-                     static_cast<const bf16 *>(b.v), b.alpha, b.eta, b.cu_seqlens, b.seq_len_dense,
-                     b.H, b.eps, b.beta_direct, b.initial_state, b.o, b.final_state, seg_of(b));
+                     static_cast<const bf16 *>(b.q), static_cast<const bf16 *>(nullptr),
+                     static_cast<const bf16 *>(b.k), static_cast<const bf16 *>(b.v), b.alpha, b.eta,
+                     b.cu_seqlens, b.seq_len_dense, b.H, b.eps, b.beta_direct, b.initial_state, b.o,
+                     b.final_state, seg_of(b));
   return hipGetLastError();
 }
 hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t s) {

@@ -325,8 +325,9 @@ kla_status kla_decode_step_kda(const void *q, const void *k, const void *v,
 size_t kla_ccq_state_floats(int32_t dk);
 
 /* Workspace bytes of kla_fwd_chunked_ccq: the cleaned queries (bf16 inputs:
- * a bf16 hi and lo pair, plus the lo read's fp32 output; fp32 inputs: fp32),
- * 256-byte rounded parts.  0 when total_tok <= 0. */
+ * a bf16 hi and lo pair, plus total_tok x H x dv fp32 of scratch for the
+ * cleaning pass; fp32 inputs: fp32), 256-byte rounded parts.  0 when
+ * total_tok <= 0. */
 size_t kla_fwd_chunked_ccq_workspace_size(int64_t total_tok, int32_t H, int32_t dk, int32_t dv,
                                           kla_dtype dtype);
 
@@ -334,9 +335,14 @@ size_t kla_fwd_chunked_ccq_workspace_size(int64_t total_tok, int32_t H, int32_t 
  * Prefill with the curvature-conditioned read.  Launches on the stream:
  *   1. the query cleaning for every token (chunked: Q P + lower(Q K^T) K,
  *      the running sums carried over chunks) into the workspace;
- *   2. bf16 inputs: the bf16 prefill reading with the lo part (no end
- *      state), then with the hi part (end state), then o += the lo output
- *      (o is linear in the query and the state does not depend on it);
+ *      For bf16 inputs the cleaned query is written as a bf16 hi and lo
+ *      pair, and sequences of at least ceil((dk*dk + dk + 4) / dk) tokens
+ *      are cleaned as two halves in parallel: a first launch leaves the
+ *      running sums of the first halves in the scratch part of the
+ *      workspace (each sequence in its own token rows), a second cleans
+ *      both halves;
+ *   2. bf16 inputs: one bf16 prefill reading with both parts of the
+ *      cleaned query, o = S^T (q_hi + q_lo), which writes the end state;
  *      fp32 inputs: the fp32 prefill reading with the fp32 cleaned query.
  *   lambda      [total_tok, H] fp32, the contraction gate (any real value).
  *   ccq_in      [n_seqs, H, kla_ccq_state_floats(dk)] fp32 start sums, or NULL

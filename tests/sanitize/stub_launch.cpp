@@ -15,7 +15,6 @@ hipError_t noalloc_scratch(void **) { return hipErrorNotSupported; }
 hipError_t launch_seq_order(const int32_t *, int, int32_t *, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_ccq_query(const CcqArgs &, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_ccq_decode_step(const CcqDecodeArgs &, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_add(float *, const float *, int64_t, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_prefill_kda(const PrefillArgs &, bool, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_prefill_states(const PrefillArgs &, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_bwd(const BwdParams &, bool, hipStream_t) { return hipErrorNotSupported; }
