@@ -247,7 +247,7 @@ __device__ inline void commit(BwdSmem<E, D> &sm, const Fetch<E, D> &f, int n, bo
     }
   }
   if (tid < C) {
-    sm.la[tid] = (tid < n && f.a != 1.f) ? flog2(f.a) : 0.f;
+    sm.la[tid] = (tid < n && f.a != 1.f) ? flog2_rate(f.a) : 0.f;
     sm.eta[tid] = tid < n ? f.e : 0.f;
   }
 }

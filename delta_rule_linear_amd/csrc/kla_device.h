@@ -90,6 +90,11 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 // flush to zero, which is exact to the precision of the outputs.
 __device__ inline float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float flog2(float x) { return __builtin_amdgcn_logf(x); }
+// log2 of a decay rate in (0, 1]: rates below the smallest normal fp32
+// number count as 2^-126 (what they multiply is below 2^-126 of its size
+// either way), so the log stays finite even where the hardware log flushes
+// subnormal inputs to zero.
+__device__ inline float flog2_rate(float x) { return __builtin_amdgcn_logf(fmaxf(x, 0x1p-126f)); }
 
 // Keep the instruction scheduler from moving code across this point; used to
 // hold software-pipelined LDS loads ahead of the MFMAs that consume them.

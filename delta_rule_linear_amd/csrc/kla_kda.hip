@@ -26,8 +26,15 @@
 //   16 tokens of growth),  P_bc = 2^{ref_b - ref_c} <= 1 (b > c),
 //   Ahat_ts = sum_i (k_t E_t)[i] P_b(t)b(s)[i] (k_s F_s)[i],
 //   (K o 2^G)_t = (k_t E_t) o 2^{ref_b(t)},  (K o 2^{G_n-G})_s = (k_s F_s) o 2^{G_n - ref_b(s)}.
-// Domain: within any 16-token block the product of a channel's rates stays
-// above 2^-126 (every rate above ~0.005 suffices), so F is finite.
+// F stays below 2^100 as long as, inside every 16-token block, the product
+// of each channel's rates stays above 2^-100 (every rate above ~0.013
+// suffices); products that underflow lose terms below 2^-26 of their
+// factor's scale.  A chunk where some channel's rates multiply below 2^-100
+// inside a block (the scan flags it) takes an exact path instead: its Gram
+// tiles are summed directly, sum_i x_t[i] k_s[i] 2^{G_t[i] - G_s[i]} with
+// every factor <= 1, and its operands carry the absolute factors 2^{G_t}
+// and 2^{G_n - G_s} (also <= 1), so nothing overflows for any rates in
+// (0, 1].
 //
 // Mapping.  One workgroup of 4 waves per (sequence, head, 64 columns of dv),
 // every operand in fp32 LDS and every contraction on the fp32 MFMA
@@ -76,6 +83,8 @@ struct KdaSmem {
   alignas(16) float W[4][D];    // 2^{G_n - ref_b}
   alignas(16) float P[6][D];    // 2^{ref_b - ref_c}, b > c, index b(b-1)/2 + c
   alignas(16) float Zn[D];      // 2^{G_n}
+  alignas(16) float Gn[D];      // G_n
+  int deep;                     // this chunk takes the exact path
 };
 
 __device__ inline f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
@@ -210,13 +219,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
       const int sg = u * kThreads + tid, r = sg / SEG_AROW, cs = sg % SEG_AROW;
       const bool in = r < n;
       f32x4 g;
-      g[0] = in ? flog2(__uint_as_float(areg[u].x)) : 0.f;
-      g[1] = in ? flog2(__uint_as_float(areg[u].y)) : 0.f;
-      g[2] = in ? flog2(__uint_as_float(areg[u].z)) : 0.f;
-      g[3] = in ? flog2(__uint_as_float(areg[u].w)) : 0.f;
+      g[0] = in ? flog2_rate(__uint_as_float(areg[u].x)) : 0.f;
+      g[1] = in ? flog2_rate(__uint_as_float(areg[u].y)) : 0.f;
+      g[2] = in ? flog2_rate(__uint_as_float(areg[u].z)) : 0.f;
+      g[3] = in ? flog2_rate(__uint_as_float(areg[u].w)) : 0.f;
       st4(&sm.KF[r * LDK + 4 * cs], g);
     }
     if (w == 0) sm.et[l] = ereg;
+    if (tid == 0) sm.deep = 0;
   };
 
   fetch(bos);
@@ -240,7 +250,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
           sm.KF[t * LDK + ch] = g;
         }
       }
-      // g = G_n (the rates past the end are 1)
+      // g = G_n (the rates past the end are 1); a block whose rates multiply
+      // below 2^-100 in this channel sends the chunk down the exact path
+      bool deep = false;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) deep |= rf[b] - (b < 3 ? rf[b + 1] : g) > 100.f;
+      if (deep) sm.deep = 1;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         sm.ref[b][ch] = rf[b];
@@ -252,11 +267,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
 #pragma unroll
         for (int c = 0; c < b; ++c) sm.P[b * (b - 1) / 2 + c][ch] = fexp2(rf[b] - rf[c]);
       sm.Zn[ch] = fexp2(g);
+      sm.Gn[ch] = g;
     }
     lds_barrier();
 
+    // uniform (written before the last barrier): read as a scalar so the
+    // branches on it are scalar
+    const bool deep = __builtin_amdgcn_readfirstlane(sm.deep) != 0;
+
     // ---- form k o E, k o F, q o E in place -----------------------------------
-    {
+    // (exact path: k o 2^G, q o 2^G and k o 2^{G_n - G}, with Z = W = 1)
+    auto form = [&](bool exact) __attribute__((always_inline)) {
       constexpr int Q4 = D / 4;            // float4 per row
       constexpr int RPP = kThreads / Q4;   // rows per pass
       const int c4 = 4 * (tid % Q4);
@@ -264,12 +285,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
       for (int r = tid / Q4; r < C; r += RPP) {
         const f32x4 G = ld4(&sm.KF[r * LDK + c4]);
         const f32x4 rf = ld4(&sm.ref[r >> 4][c4]);
+        const f32x4 gn = ld4(&sm.Gn[c4]);
         const f32x4 kx = ld4(&sm.KE[r * LDK + c4]);
         const f32x4 qx = ld4(&sm.QE[r * LDK + c4]);
         f32x4 ke, kf, qe;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float Ev = fexp2(G[e] - rf[e]), Fv = fexp2(rf[e] - G[e]);
+          const float Ev = exact ? fexp2(G[e]) : fexp2(G[e] - rf[e]);
+          const float Fv = exact ? fexp2(fminf(gn[e] - G[e], 0.f)) : fexp2(rf[e] - G[e]);
           ke[e] = kx[e] * Ev;
           kf[e] = kx[e] * Fv;
           qe[e] = qx[e] * Ev;
@@ -278,27 +301,65 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
         st4(&sm.KF[r * LDK + c4], kf);
         st4(&sm.QE[r * LDK + c4], qe);
       }
-    }
-    lds_barrier();
-
+    };
+    // exact Gram element: sum_i X_t[i] K_s[i] 2^{G_t[i] - G_s[i]} for t >= s
+    // (raw X = Q or K and G still in LDS), else 0
+    auto exact_tile = [&](bool qk, int bi, int bj) __attribute__((always_inline)) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int sc = 16 * bj + c16;
+      const float *X = qk ? sm.QE : sm.KE;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * bi + 4 * j + i;
+        if (t >= sc) {
+          float a = 0.f;
+#pragma unroll 1
+          for (int ch = 0; ch < D; ch += 4) {
+            const f32x4 x = ld4(&X[t * LDK + ch]), kv = ld4(&sm.KE[sc * LDK + ch]);
+            const f32x4 gt = ld4(&sm.KF[t * LDK + ch]), gs = ld4(&sm.KF[sc * LDK + ch]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a += x[e] * kv[e] * fexp2(fminf(gt[e] - gs[e], 0.f));
+          }
+          acc[i] = a;
+        }
+      }
+      return acc;
+    };
     // ---- Gram tiles, diagonal inverses; Q S, K S, R --------------------------
     f32x4 jt[6];  // waves 1-3: their Gram tiles until the operand space is free
+    auto gram = [&](bool exact) __attribute__((always_inline)) {
     if (w == 0) {
       sm.beta[l] = beta_direct ? sm.et[l] : sm.et[l] / (sm.kk[l] + eps);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k0 = 0; k0 < D; k0 += 4)
-          acc = mma(sm.KE[(16 * b + c16) * LDK + k0 + j], sm.KF[(16 * b + c16) * LDK + k0 + j], acc);
-        // acc[i] = Ahat[16b + 4j + i][16b + c16]
+      // diagonal tiles -> -Diag(beta) Ahat below the diagonal of each block
+      // (acc[i] = Ahat[16b + 4j + i][16b + c16])
+      auto ld_write = [&](int b, const f32x4 &acc) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * j + i;
           sm.Ld[(b * 16 + c16) * 20 + r] = r > c16 ? -sm.beta[16 * b + r] * acc[i] : 0.f;
+        }
+      };
+      if (exact) {
+#pragma unroll 1
+        for (int b = 0; b < 4; ++b) {
+          const f32x4 acc = exact_tile(false, b, b);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * j + i;
+            sm.Ld[(b * 16 + c16) * 20 + r] = r > c16 ? -sm.beta[16 * b + r] * acc[i] : 0.f;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k0 = 0; k0 < D; k0 += 4)
+            acc = mma(sm.KE[(16 * b + c16) * LDK + k0 + j], sm.KF[(16 * b + c16) * LDK + k0 + j], acc);
+          ld_write(b, acc);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -325,6 +386,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
       // waves 1, 2, 3: jobs [0,5), [5,10), [10,16)
       const int q0 = 5 * (w - 1);
       const int nj = w == 3 ? 6 : 5;
+      if (exact) {
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+          if (u < nj) {
+            const Job jb = job_of(q0 + u);
+            jt[u] = exact_tile(jb.qk, jb.bi, jb.bj);
+          }
+        }
+        return;
+      }
 #pragma unroll
       for (int u = 0; u < 6; ++u) {
         if (u < nj) {
@@ -345,6 +416,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
           jt[u] = acc;
         }
       }
+    }
+    };
+    // fast path: operands, then the Gram tiles on the MFMA; exact path: the
+    // Gram tiles from the raw inputs, then the operands with absolute
+    // factors (Z = W = 1)
+    if (!deep) form(false);
+    lds_barrier();
+    gram(deep);
+    if (deep) {
+      lds_barrier();  // every read of the raw inputs is done
+      if (tid < D) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          sm.Z[b][tid] = 1.f;
+          sm.W[b][tid] = 1.f;
+        }
+      }
+      form(true);
+      lds_barrier();
     }
 
     // Q S and K S with the state rows scaled by 2^{ref_bi}: (q o 2^G) S = (q o E) (Diag(2^{ref}) S)

@@ -790,7 +790,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
     }
     if (pw == 0) {
       sm.et[l] = ereg;
-      const float g = wave_scan(alpha && l < eos - t0 ? flog2(areg) : 0.f);  // alpha = 1 past the end
+      const float g = wave_scan(alpha && l < eos - t0 ? flog2_rate(areg) : 0.f);  // alpha = 1 past the end
       const float glast = __shfl(g, 63, 64);
       sl.g2[l] = g;
       sl.gam[l] = fexp2(g);

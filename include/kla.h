@@ -281,10 +281,9 @@ kla_status kla_decode_step_ex(const void *q, const void *k, const void *v,
  * with beta_t from beta_mode as in kla_fwd_chunked_ex.
  *
  *   alpha       [total_tok, H, dk] fp32, required, 16-byte aligned; every
- *               rate in (0, 1].  Domain: inside each aligned block of 16
- *               tokens of a chunk, the product of one channel's rates stays
- *               above 2^-126 (every rate above about 0.005 is enough);
- *               outside it the results may be non-finite.
+ *               rate in (0, 1], however small.  (A chunk in which one
+ *               channel's rates multiply below 2^-100 inside an aligned
+ *               block of 16 tokens takes a slower exact path.)
  * Other arguments and errors as kla_fwd_chunked_ex (whole sequences only; no
  * workspace is needed).  The arithmetic is fp32 throughout (fp32 MFMA), for
  * bf16 and fp32 inputs alike.

@@ -75,6 +75,48 @@ def test_kda_prefill_ragged(kla, d, dtype, mode):
     assert torch.equal(S[4].cpu(), s0[4])  # the empty sequence keeps its start state
 
 
+def _tiny(a, case, d):
+    if case == "deep_channels":      # a quarter of the channels at 1e-3: 2^-159 per 16 tokens
+        a[:, :, : d // 4] = 1e-3
+    elif case == "near_zero_run":     # a short run of near-zero rates in some channels
+        a[10:14, 0, d // 4: d // 2] = 1e-30
+    elif case == "subnormal":         # a single token below the normal fp32 range
+        a[70, 1, d // 2:] = 1e-38
+    elif case == "past_bound":        # 0.004 per token: just past the fast path's bound
+        a[150:160, :, 3 * d // 4:] = 0.004
+    elif case == "all":
+        for c in ("deep_channels", "near_zero_run", "subnormal", "past_bound"):
+            _tiny(a, c, d)
+    return a
+
+
+@pytest.mark.parametrize("d,dtype,case", [
+    (128, "bf16", "deep_channels"), (128, "bf16", "near_zero_run"), (128, "bf16", "subnormal"),
+    (128, "bf16", "past_bound"), (128, "bf16", "all"), (64, "f32", "all")])
+def test_kda_prefill_tiny_rates(kla, d, dtype, case):
+    """Per-channel rates whose product inside a 16-token block falls far
+    below 2^-126, mixed with ordinary rates: every output finite and within
+    the bar against the oracle."""
+    lengths = [200, 64, 1, 130]
+    print(f"[case] per-channel prefill with tiny rates ({case}) d={d} {dtype} lengths={lengths} H=2",
+          flush=True)
+    inp = workloads.prefill(lengths=lengths, H=2, d=d, dtype=dtype, seed=63, channel_decay=True)
+    a = _tiny(inp["alpha_ch"].clone(), case, d)
+    g = torch.Generator().manual_seed(64)
+    s0 = 0.5 * torch.randn((len(lengths), 2, d, d), generator=g)
+    dev = "cuda"
+    o, S = kla.kla_fwd_chunked_kda(inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev),
+                                   a.to(dev), inp["eta"].to(dev),
+                                   cu_seqlens=inp["cu_seqlens"].to(dev), initial_state=s0.to(dev),
+                                   eps=inp["eps"], output_final_state=True)
+    torch.cuda.synchronize()
+    ro, rS = oracle.fwd(inp["q"], inp["k"], inp["v"], a, inp["eta"],
+                        cu_seqlens=inp["cu_seqlens"].numpy().astype(np.int64),
+                        eps=float(np.float32(inp["eps"])), initial_state=s0, channel_decay=True)
+    check(f"kda tiny rates {case} d={d} {dtype} o", o.cpu(), ro, TOL[dtype])
+    check(f"kda tiny rates {case} d={d} {dtype} S_T", S.cpu(), rS, TOL[dtype])
+
+
 def test_kda_layer_workload(kla):
     print("[case] per-channel prefill, layer shape 8 x 2048 tokens, H=16, d=128 bf16 (full oracle)",
           flush=True)
