@@ -75,12 +75,13 @@ KERNEL_SOURCES = {PREFILL_KERNEL: "delta_rule_linear_amd/csrc/kla_prefill.hip",
                   BWD_STATES: "delta_rule_linear_amd/csrc/kla_prefill.hip"}
 # mangled-name fragments of the instantiations the benchmark times (bf16
 # inputs, d = 128; the decode one with the scalar decay)
-KERNEL_MATCH = {PREFILL_KERNEL: "prefill_pc_kernelILi128ELb1E",
+# (prefill_pc_kernel<D, OUT, QLO>: the plain prefill is <128, true, false>)
+KERNEL_MATCH = {PREFILL_KERNEL: "prefill_pc_kernelILi128ELb1ELb0E",
                 DECODE_KERNEL: "decode_kernelIDF16bLi128ELb0E",
                 KDA_KERNEL: "prefill_kda_kernelIDF16bLi128E",
                 BWD_KERNEL: "bwd_kernelIDF16bLi128E",
                 BWD_FINISH: "bwd_finish_kernelIDF16bLi128E",
-                BWD_STATES: "prefill_pc_kernelILi128ELb0E"}
+                BWD_STATES: "prefill_pc_kernelILi128ELb0ELb0E"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
