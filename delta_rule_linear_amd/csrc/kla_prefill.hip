@@ -101,6 +101,17 @@ __device__ inline bf16x8 lda_perm(const bf16 *row, int j) {
 }
 __device__ inline bf16x4 lda4(const bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
 
+// Column order of the bf16 K and Q rows (and of the M planes' token columns)
+// in the producer/consumer kernel's LDS: within each 32-column block the
+// 4-column groups sit in the order 0, 4, 1, 5, 2, 6, 3, 7.  A state
+// fragment pair (rows 4j..4j+3 of two 16-row tiles) then meets its eight
+// operand values in one 16-byte read, and a Gram tile, which contracts over
+// this index on both sides, is unchanged.  pcol maps a logical column (a
+// multiple of 4) to its place.
+__device__ constexpr int pcol(int c) { return (c & ~31) + ((c & 15) >> 2) * 8 + ((c >> 4) & 1) * 4; }
+static_assert(pcol(0) == 0 && pcol(4) == 8 && pcol(16) == 4 && pcol(20) == 12 && pcol(28) == 28 &&
+                  pcol(44) == 56, "column order");
+
 __device__ inline void store_split(bf16 *h, bf16 *l, int idx, float x) {
   const bf16 hv = static_cast<bf16>(x);
   h[idx] = hv;
@@ -782,11 +793,17 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + wk.vb * DVB + cs * SEG_EL) * 2);
     }
   };
+  // a 16-byte segment of a K or Q row (logical columns 8cs..8cs+7) into its
+  // two places in the LDS column order
+  auto put_row_seg = [&](bf16 *rowp, int cs, const uint4 &x) __attribute__((always_inline)) {
+    *reinterpret_cast<uint2 *>(&rowp[pcol(cs * SEG_EL)]) = uint2{x.x, x.y};
+    *reinterpret_cast<uint2 *>(&rowp[pcol(cs * SEG_EL + 4)]) = uint2{x.z, x.w};
+  };
   auto stage_k = [&](SL &sl, int64_t t0) __attribute__((always_inline)) {  // K and the decays into a slot
 #pragma unroll
     for (int u = 0; u < NSEG; ++u) {
       const int sg = u * PT + ptid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
-      *reinterpret_cast<uint4 *>(&sl.Kr[r * CF::LDK + cs * SEG_EL]) = kreg[u];
+      put_row_seg(&sl.Kr[r * CF::LDK], cs, kreg[u]);
     }
     if (pw == 0) {
       sm.et[l] = ereg;
@@ -803,8 +820,8 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
 #pragma unroll
       for (int u = 0; u < NSEG; ++u) {
         const int sg = u * PT + ptid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
-        *reinterpret_cast<uint4 *>(&qb[r * CF::LDK + cs * SEG_EL]) = qreg[u];
-        if constexpr (QLO) *reinterpret_cast<uint4 *>(&sm.Qlr[r * CF::LDK + cs * SEG_EL]) = qlreg[u];
+        put_row_seg(&qb[r * CF::LDK], cs, qreg[u]);
+        if constexpr (QLO) put_row_seg(&sm.Qlr[r * CF::LDK], cs, qlreg[u]);
       }
     }
     bf16 *vb = VB(sl);
@@ -872,7 +889,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
         }
         const Split4 sp = split4(vals);
         if (jb.qk) {
-          const int off = r * CF::LDP + 16 * jb.bj + 4 * j;
+          const int off = r * CF::LDP + pcol(16 * jb.bj + 4 * j);
           *reinterpret_cast<bf16x4 *>(&MHB(sl)[off]) = sp.hi;
           *reinterpret_cast<bf16x4 *>(&MLB(sl)[off]) = sp.lo;
         } else {
@@ -1053,9 +1070,10 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       bf16x8 qa[3], ka[3], qla[QLO ? 3 : 1];
       auto ld = [&](int st) {
         const int kk = st / 4, bi = st % 4;
-        if constexpr (OUT) qa[st % 3] = lda_perm(&QB(sl)[(16 * bi + c16) * CF::LDK + 32 * kk], j);
-        if constexpr (QLO) qla[st % 3] = lda_perm(&sm.Qlr[(16 * bi + c16) * CF::LDK + 32 * kk], j);
-        ka[st % 3] = lda_perm(&sl.Kr[(16 * bi + c16) * CF::LDK + 32 * kk], j);
+        const int off = (16 * bi + c16) * CF::LDK + 32 * kk + 8 * j;
+        if constexpr (OUT) qa[st % 3] = *reinterpret_cast<const bf16x8 *>(&QB(sl)[off]);
+        if constexpr (QLO) qla[st % 3] = *reinterpret_cast<const bf16x8 *>(&sm.Qlr[off]);
+        ka[st % 3] = *reinterpret_cast<const bf16x8 *>(&sl.Kr[off]);
       };
       ld(0);
       ld(1);
@@ -1134,9 +1152,9 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
           bf16x8 mh[3], ml[3];
           auto ld = [&](int st) {
             const int kk = st < 4 ? 0 : 1, bi = st < 4 ? st : st - 2;
-            const int off = (16 * bi + c16) * CF::LDP + 32 * kk;
-            mh[st % 3] = lda_perm(&MHB(sl)[off], j);
-            ml[st % 3] = lda_perm(&MLB(sl)[off], j);
+            const int off = (16 * bi + c16) * CF::LDP + 32 * kk + 8 * j;
+            mh[st % 3] = *reinterpret_cast<const bf16x8 *>(&MHB(sl)[off]);
+            ml[st % 3] = *reinterpret_cast<const bf16x8 *>(&MLB(sl)[off]);
           };
           ld(0);
           ld(1);
@@ -1175,7 +1193,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
         bf16x8 kt[3];
         auto ld = [&](int st) {
           const int kk = st / NST, t = st % NST;
-          const bf16 *base = &sl.Kr[16 * t + 4 * (c16 & 3)];
+          const bf16 *base = &sl.Kr[pcol(16 * t + 4 * (c16 & 3))];
           const bf16x4 x0 = ld_tr(base + (32 * kk + 4 * j + (c16 >> 2)) * CF::LDK);
           const bf16x4 x1 = ld_tr(base + (32 * kk + 16 + 4 * j + (c16 >> 2)) * CF::LDK);
           kt[st % 3] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
