@@ -192,8 +192,11 @@ __device__ inline int64_t logical_block() {
 
 // One column step of the 16x16 unit-lower-triangular substitution:
 // x[r] += (-L[r][t]) x[t] for r > t, one v_fmac_f32_dpp per row whose first
-// factor is broadcast from lane t of the 16-lane row.  lc holds -L and comes
-// straight from LDS, so no VALU write precedes its DPP read.
+// factor is broadcast from lane t of the 16-lane row.  The compiler adds no
+// wait states in front of inline asm, so lc must not have been written by a
+// VALU instruction within the two preceding wait states: callers load it
+// from LDS or pass it through an s_nop (checked on the generated assembly by
+// the test suite).
 template <int T>
 __device__ inline void solve_step(float (&x)[16], const float (&lc)[16]) {
 #pragma unroll

@@ -236,7 +236,7 @@ __device__ inline Work resolve_work(const SegParams &sp, const int32_t *cu_seqle
 }
 
 // 16x16 Gram tile G[r][s] = sum_d A[r0+r][d] B[s0+s][d] (rows of A, B in LDS).
-template <typename E, int D>
+template <typename E, int D, int LDK = Cfg<E, D>::LDK>
 __device__ inline f32x4 gram_tile(const E *A, const E *B, int r0, int s0, int j, int c16) {
   using CF = Cfg<E, D>;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -245,15 +245,15 @@ __device__ inline f32x4 gram_tile(const E *A, const E *B, int r0, int s0, int j,
     bf16x8 a[D / 32], b[D / 32];
 #pragma unroll
     for (int u = 0; u < D / 32; ++u) {
-      a[u] = *reinterpret_cast<const bf16x8 *>(&A[(r0 + c16) * CF::LDK + 32 * u + 8 * j]);
-      b[u] = *reinterpret_cast<const bf16x8 *>(&B[(s0 + c16) * CF::LDK + 32 * u + 8 * j]);
+      a[u] = *reinterpret_cast<const bf16x8 *>(&A[(r0 + c16) * LDK + 32 * u + 8 * j]);
+      b[u] = *reinterpret_cast<const bf16x8 *>(&B[(s0 + c16) * LDK + 32 * u + 8 * j]);
     }
 #pragma unroll
     for (int u = 0; u < D / 32; ++u) acc = mma(a[u], b[u], acc);
   } else {
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += 4)
-      acc = mma(A[(r0 + c16) * CF::LDK + k0 + j], B[(s0 + c16) * CF::LDK + k0 + j], acc);
+      acc = mma(A[(r0 + c16) * LDK + k0 + j], B[(s0 + c16) * LDK + k0 + j], acc);
   }
   return acc;
 }
@@ -659,13 +659,19 @@ struct PSlot {
   using CF = Cfg<bf16, D>;
   static constexpr bool PER_SLOT = OUT && !SQ;
   static constexpr int LDA = 20;  // compact 16x16 blocks of -Ahat and Y
-  alignas(16) bf16 Kr[C * CF::LDK];
-  alignas(16) bf16 Qr[PER_SLOT ? C * CF::LDK : 8];
+  // Row pitches (elements) of K, Q and the M planes: 2 * LDK and 2 * LDP
+  // bytes are 32 more than a multiple of 128, which keeps the consumers'
+  // row-per-lane 16-byte reads and the transposing K^T reads free of LDS
+  // bank conflicts.
+  static constexpr int LDK = D + 16;
+  static constexpr int LDP = C + 16;
+  alignas(16) bf16 Kr[C * LDK];
+  alignas(16) bf16 Qr[PER_SLOT ? C * LDK : 8];
   alignas(16) bf16 Vs[SQ ? 8 : C * CF::LDV];
   alignas(16) bf16 Ah[6 * 16 * LDA];  // -Ahat blocks (b, m), m < b, index b(b-1)/2 + m
   alignas(16) bf16 Al[6 * 16 * LDA];
-  alignas(16) bf16 Mh[PER_SLOT ? C * CF::LDP : 8];  // M = lower(Q K^T o Gam), zero above the block diagonal
-  alignas(16) bf16 Ml[PER_SLOT ? C * CF::LDP : 8];
+  alignas(16) bf16 Mh[PER_SLOT ? C * LDP : 8];  // M = lower(Q K^T o Gam), zero above the block diagonal
+  alignas(16) bf16 Ml[PER_SLOT ? C * LDP : 8];
   static constexpr int LDYT = 24;     // Y^T rows: 16 values + pad, 16-byte aligned
   alignas(16) bf16 Yh[4 * 16 * LDYT];  // Y_bb^T, Y_bb = (I + L_bb)^{-1} Diag(beta_b)
   alignas(16) bf16 Yl[4 * 16 * LDYT];
@@ -676,14 +682,14 @@ struct PSlot {
 template <int D, bool OUT, bool SQ>
 struct PSmem {
   using CF = Cfg<bf16, D>;
-  PSlot<D, OUT, SQ> slot[2];
-  alignas(16) bf16 Qr[SQ ? C * CF::LDK : 8];
-  alignas(16) bf16 Qlr[SQ ? C * CF::LDK : 8];
+  using SL = PSlot<D, OUT, SQ>;
+  SL slot[2];
+  alignas(16) bf16 Qr[SQ ? C * SL::LDK : 8];
+  alignas(16) bf16 Qlr[SQ ? C * SL::LDK : 8];
   alignas(16) bf16 Vs[SQ ? C * CF::LDV : 8];
-  alignas(16) bf16 Mh[SQ ? C * CF::LDP : 8];
-  alignas(16) bf16 Ml[SQ ? C * CF::LDP : 8];
+  alignas(16) bf16 Mh[SQ ? C * SL::LDP : 8];
+  alignas(16) bf16 Ml[SQ ? C * SL::LDP : 8];
   // producer scratch for the chunk being prepared
-  alignas(16) float Ld[4 * 16 * 20];  // -Diag(beta) Ahat below the diagonal of the diagonal blocks, [block][col][row]
   alignas(16) float kk[C];
   alignas(16) float et[C];
   alignas(16) float beta[C];
@@ -742,7 +748,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
   };
   // M above the block diagonal is read as zero.
   if constexpr (OUT) {
-    for (int i = tid; i < C * CF::LDP; i += 512) {
+    for (int i = tid; i < C * SL::LDP; i += 512) {
       MHB(sm.slot[0])[i] = bf16(0.f);
       MLB(sm.slot[0])[i] = bf16(0.f);
       MHB(sm.slot[1])[i] = bf16(0.f);
@@ -803,7 +809,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
 #pragma unroll
     for (int u = 0; u < NSEG; ++u) {
       const int sg = u * PT + ptid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
-      put_row_seg(&sl.Kr[r * CF::LDK], cs, kreg[u]);
+      put_row_seg(&sl.Kr[r * SL::LDK], cs, kreg[u]);
     }
     if (pw == 0) {
       sm.et[l] = ereg;
@@ -820,8 +826,8 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
 #pragma unroll
       for (int u = 0; u < NSEG; ++u) {
         const int sg = u * PT + ptid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
-        put_row_seg(&qb[r * CF::LDK], cs, qreg[u]);
-        if constexpr (QLO) put_row_seg(&sm.Qlr[r * CF::LDK], cs, qlreg[u]);
+        put_row_seg(&qb[r * SL::LDK], cs, qreg[u]);
+        if constexpr (QLO) put_row_seg(&sm.Qlr[r * SL::LDK], cs, qlreg[u]);
       }
     }
     bf16 *vb = VB(sl);
@@ -853,10 +859,10 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       gsb[u & 1] = *reinterpret_cast<const f32x4 *>(&sl.g2[16 * jb.bj + 4 * j]);
 #pragma unroll
       for (int t = 0; t < D / 32; ++t) {
-        opa[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&sl.Kr[(16 * jb.bj + c16) * CF::LDK + 32 * t + 8 * j]);
-        opb[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&B[(16 * jb.bi + c16) * CF::LDK + 32 * t + 8 * j]);
+        opa[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&sl.Kr[(16 * jb.bj + c16) * SL::LDK + 32 * t + 8 * j]);
+        opb[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&B[(16 * jb.bi + c16) * SL::LDK + 32 * t + 8 * j]);
         if constexpr (QLO) {
-          if (jb.qk) opl[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&sm.Qlr[(16 * jb.bi + c16) * CF::LDK + 32 * t + 8 * j]);
+          if (jb.qk) opl[u & 1][t] = *reinterpret_cast<const bf16x8 *>(&sm.Qlr[(16 * jb.bi + c16) * SL::LDK + 32 * t + 8 * j]);
         }
       }
     };
@@ -889,7 +895,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
         }
         const Split4 sp = split4(vals);
         if (jb.qk) {
-          const int off = r * CF::LDP + pcol(16 * jb.bj + 4 * j);
+          const int off = r * SL::LDP + pcol(16 * jb.bj + 4 * j);
           *reinterpret_cast<bf16x4 *>(&MHB(sl)[off]) = sp.hi;
           *reinterpret_cast<bf16x4 *>(&MLB(sl)[off]) = sp.lo;
         } else {
@@ -907,7 +913,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
   auto diag = [&](SL &sl) __attribute__((always_inline)) {
     f32x4 dg[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) dg[b] = gram_tile<bf16, D>(sl.Kr, sl.Kr, 16 * b, 16 * b, j, c16);
+    for (int b = 0; b < 4; ++b) dg[b] = gram_tile<bf16, D, SL::LDK>(sl.Kr, sl.Kr, 16 * b, 16 * b, j, c16);
     // |k_r|^2 is the diagonal: row 16b + c16 sits in lane (c16 / 4, c16), element c16 % 4
     if ((c16 >> 2) == j) {
       const int e = c16 & 3;
@@ -918,8 +924,8 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
     wave_sync();
     sm.beta[l] = beta_direct ? sm.et[l] : sm.et[l] / (sm.kk[l] + eps);
     wave_sync();
-    // every gate and beta this lane needs first, then the 16 values, then
-    // one 16-byte write per block (rows 4j..4j+3 of column c16)
+    // every gate and beta this lane needs first, then -L: lane (j, c16)
+    // holds rows 4j..4j+3 of column c16 of each diagonal block b
     f32x4 gr[4], br[4];
     float gc[4];
 #pragma unroll
@@ -928,26 +934,38 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       br[b] = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * b + 4 * j]);
       gc[b] = sl.g2[16 * b + c16];
     }
+    f32x4 val[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      f32x4 val;
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float x = -br[b][i] * dg[b][i] * fexp2(fminf(gr[b][i] - gc[b], 0.f));
-        val[i] = 4 * j + i > c16 ? x : 0.f;  // -L below the diagonal
+        val[b][i] = 4 * j + i > c16 ? x : 0.f;  // -L below the diagonal
       }
-      *reinterpret_cast<f32x4 *>(&sm.Ld[(b * 16 + c16) * 20 + 4 * j]) = val;
-    }
-    wave_sync();
+    // The solve wants lane (b, c16) to hold all of column c16 of block b:
+    // for each i, a 4x4 transpose of (16-lane row, block register), by
+    // swapping the upper 32 lanes of blocks 0, 1 with the lower 32 of
+    // blocks 2, 3, then the odd rows of blocks 0, 2 with the even rows of
+    // blocks 1, 3.  Afterwards lc[4r + i] = -L_b[4r + i][c16].
     float lc[16];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 v4 = *reinterpret_cast<const float4 *>(&sm.Ld[(j * 16 + c16) * 20 + 4 * q4]);
-      lc[4 * q4] = v4.x;
-      lc[4 * q4 + 1] = v4.y;
-      lc[4 * q4 + 2] = v4.z;
-      lc[4 * q4 + 3] = v4.w;
+    for (int i = 0; i < 4; ++i) {
+      const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(val[0][i]), __float_as_uint(val[2][i]), false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(val[1][i]), __float_as_uint(val[3][i]), false, false);
+      const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+      const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+      lc[i] = __uint_as_float(s01[0]);
+      lc[4 + i] = __uint_as_float(s01[1]);
+      lc[8 + i] = __uint_as_float(s23[0]);
+      lc[12 + i] = __uint_as_float(s23[1]);
     }
+    // The solve reads lc through DPP, which needs two wait states after a
+    // VALU write of the register (the compiler adds none before inline asm):
+    // every lc passes through this one statement, whose s_nop provides them.
+    asm volatile("s_nop 2"
+                 : "+v"(lc[0]), "+v"(lc[1]), "+v"(lc[2]), "+v"(lc[3]), "+v"(lc[4]), "+v"(lc[5]),
+                   "+v"(lc[6]), "+v"(lc[7]), "+v"(lc[8]), "+v"(lc[9]), "+v"(lc[10]), "+v"(lc[11]),
+                   "+v"(lc[12]), "+v"(lc[13]), "+v"(lc[14]), "+v"(lc[15]));
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = (r == c16) ? 1.f : 0.f;
@@ -1070,7 +1088,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
       bf16x8 qa[3], ka[3], qla[QLO ? 3 : 1];
       auto ld = [&](int st) {
         const int kk = st / 4, bi = st % 4;
-        const int off = (16 * bi + c16) * CF::LDK + 32 * kk + 8 * j;
+        const int off = (16 * bi + c16) * SL::LDK + 32 * kk + 8 * j;
         if constexpr (OUT) qa[st % 3] = *reinterpret_cast<const bf16x8 *>(&QB(sl)[off]);
         if constexpr (QLO) qla[st % 3] = *reinterpret_cast<const bf16x8 *>(&sm.Qlr[off]);
         ka[st % 3] = *reinterpret_cast<const bf16x8 *>(&sl.Kr[off]);
@@ -1152,7 +1170,7 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
           bf16x8 mh[3], ml[3];
           auto ld = [&](int st) {
             const int kk = st < 4 ? 0 : 1, bi = st < 4 ? st : st - 2;
-            const int off = (16 * bi + c16) * CF::LDP + 32 * kk + 8 * j;
+            const int off = (16 * bi + c16) * SL::LDP + 32 * kk + 8 * j;
             mh[st % 3] = *reinterpret_cast<const bf16x8 *>(&MHB(sl)[off]);
             ml[st % 3] = *reinterpret_cast<const bf16x8 *>(&MLB(sl)[off]);
           };
@@ -1194,8 +1212,8 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
         auto ld = [&](int st) {
           const int kk = st / NST, t = st % NST;
           const bf16 *base = &sl.Kr[pcol(16 * t + 4 * (c16 & 3))];
-          const bf16x4 x0 = ld_tr(base + (32 * kk + 4 * j + (c16 >> 2)) * CF::LDK);
-          const bf16x4 x1 = ld_tr(base + (32 * kk + 16 + 4 * j + (c16 >> 2)) * CF::LDK);
+          const bf16x4 x0 = ld_tr(base + (32 * kk + 4 * j + (c16 >> 2)) * SL::LDK);
+          const bf16x4 x1 = ld_tr(base + (32 * kk + 16 + 4 * j + (c16 >> 2)) * SL::LDK);
           kt[st % 3] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
         };
         ld(0);
