@@ -1188,16 +1188,6 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
             sched_fence();
           }
         }
-        const rsrc_t ro = make_rsrc(wk.out ? o + tok0 * H * (int64_t)D : o, wk.out ? (int64_t)n * H * D * 4 : 0);
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi)  // token 16bi + c16, dv 16w + 4j..+3; rows past the end are dropped
-        {
-          const uint32_t off = (uint32_t)(((16 * bi + c16) * H + h) * D + nb * DVB + 16 * w + 4 * j) * 4;
-          if (sp.o_wb)
-            buf_st16(ro, off, QS[bi]);
-          else
-            buf_st16_nt(ro, off, QS[bi]);
-        }
       }
       // S' = 2^{g2_last} S + K^T Diag(2^{g2_last - g2}) Delta
 #pragma unroll
@@ -1226,6 +1216,20 @@ __global__ __launch_bounds__(512) void prefill_pc_kernel(
           Sout[t] = mma(kt[st % 3], Hf[kk].hi, Sout[t]);
           Sout[t] = mma(kt[st % 3], Hf[kk].lo, Sout[t]);
           sched_fence();
+        }
+      }
+      // the output last, so the M Delta products have drained during the
+      // state update
+      if constexpr (OUT) {
+        const rsrc_t ro = make_rsrc(wk.out ? o + tok0 * H * (int64_t)D : o, wk.out ? (int64_t)n * H * D * 4 : 0);
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi)  // token 16bi + c16, dv 16w + 4j..+3; rows past the end are dropped
+        {
+          const uint32_t off = (uint32_t)(((16 * bi + c16) * H + h) * D + nb * DVB + 16 * w + 4 * j) * 4;
+          if (sp.o_wb)
+            buf_st16(ro, off, QS[bi]);
+          else
+            buf_st16_nt(ro, off, QS[bi]);
         }
       }
     }
