@@ -80,6 +80,18 @@ __device__ inline Split8 join(const Split4 &a, const Split4 &b) {
   return r;
 }
 
+// Column order of bf16 operand rows kept in LDS for the 32-deep MFMA (K and
+// Q rows, the M planes' token columns, the per-channel-decay operands):
+// within each 32-column block the 4-column groups sit in the order 0, 4, 1,
+// 5, 2, 6, 3, 7.  A state
+// fragment pair (rows 4j..4j+3 of two 16-row tiles) then meets its eight
+// operand values in one 16-byte read, and a Gram tile, which contracts over
+// this index on both sides, is unchanged.  pcol maps a logical column (a
+// multiple of 4) to its place.
+__device__ constexpr int pcol(int c) { return (c & ~31) + ((c & 15) >> 2) * 8 + ((c >> 4) & 1) * 4; }
+static_assert(pcol(0) == 0 && pcol(4) == 8 && pcol(16) == 4 && pcol(20) == 12 && pcol(28) == 28 &&
+                  pcol(44) == 56, "column order");
+
 // Workgroup barrier that orders LDS traffic only.  __syncthreads() also
 // waits for every outstanding global load, which would expose the latency of
 // the next chunk's prefetch at each barrier.

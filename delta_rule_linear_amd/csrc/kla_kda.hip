@@ -544,6 +544,546 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
   }
 }
 
+// ---- bf16 inputs: the contractions on the bf16 MFMA ------------------------
+// The same chunk form, scan, exact path and substitution as above, with the
+// three large contraction groups moved to v_mfma_f32_16x16x32_bf16: the
+// Gram tiles (k o E or q o E against k o F), Q S and K S, and the state
+// update (k o 2^{G_n - G})^T Delta.  Every fp32 factor there enters as a
+// bf16 pair hi = bf16(x), lo = bf16(x - hi), and a product of two split
+// factors is the three MFMAs hi*hi + hi*lo + lo*hi (the lo*lo term is below
+// 2^-16 of the product).  The operand planes are kept as bf16 hi and lo
+// planes in the pcol column order, so a state fragment pair or a Gram
+// operand is one 16-byte read.  The substitution and M Delta stay on the
+// fp32 MFMA.
+//
+// LDS: the k o E and q o E planes (hi, lo); the k o F planes share their
+// rows with the log-decays: until the operands are formed, the same bytes
+// hold G as fp32 (D + 8 floats a row), and each row is formed by the one
+// wave that read it, G first.
+template <int D>
+struct KdaBfSmem {
+  static constexpr int LDB = D + 16;      // k o E, q o E rows (bf16; 2 LDB bytes = 32 mod 128)
+  static constexpr int LDR = 2 * D + 16;  // k o F rows (bf16): hi at 0, lo at LO; 2 LDR bytes = 32 mod 128
+  static constexpr int LO = D + 8;
+  static constexpr int LDG = D + 8;       // the same rows as fp32 G
+  static constexpr int LDV = DVB + 4;
+  static constexpr int LDP = C + 4;       // -Ahat and M planes (fp32), over the k o E and q o E space
+  static constexpr int LDY = 20;
+  static_assert(C * LDP * 4 <= 2 * C * LDB * 2, "planes must fit in the operand space");
+  alignas(16) bf16 KE[2 * C * LDB];  // hi plane then lo plane; raw k in the hi plane until formed
+  alignas(16) bf16 QE[2 * C * LDB];
+  alignas(16) bf16 KF[C * LDR];
+  alignas(16) float Vs[C * LDV];
+  alignas(16) float Yh[4 * 16 * LDY];
+  alignas(16) float Ld[4 * 16 * 20];
+  alignas(16) float kk[C];
+  alignas(16) float et[C];
+  alignas(16) float beta[C];
+  alignas(16) float ref[4][D];
+  alignas(16) float Z[4][D];
+  alignas(16) float W[4][D];
+  alignas(16) float P[6][D];
+  alignas(16) float Zn[D];
+  alignas(16) float Gn[D];
+  int deep;
+};
+
+__device__ inline f32x4 to_f32x4(bf16x4 x) {
+  return f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
+               static_cast<float>(x[3])};
+}
+__device__ inline Split8 split8(f32x4 a, f32x4 b) { return join(split4(a), split4(b)); }
+__device__ inline bf16x4 half_lo(bf16x8 x) { return __builtin_shufflevector(x, x, 0, 1, 2, 3); }
+__device__ inline bf16x4 half_hi(bf16x8 x) { return __builtin_shufflevector(x, x, 4, 5, 6, 7); }
+// hi*hi + hi*lo + lo*hi on the 32-deep bf16 MFMA
+__device__ inline f32x4 mma3(const Split8 &a, const Split8 &b, f32x4 c) {
+  c = mma(a.hi, b.hi, c);
+  c = mma(a.hi, b.lo, c);
+  return mma(a.lo, b.hi, c);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ alpha, const float *__restrict__ eta,
+    const int32_t *__restrict__ cu_seqlens, int64_t seq_len_dense, int H, float eps,
+    int beta_direct, const float *__restrict__ S0, float *__restrict__ o,
+    float *__restrict__ Sfin) {
+  using SM = KdaBfSmem<D>;
+  constexpr int NB = D / DVB;
+  constexpr int NST = D / 16;
+  constexpr int LDB = SM::LDB, LDR = SM::LDR, LO = SM::LO, LDG = SM::LDG, LDV = SM::LDV,
+                LDP = SM::LDP, LDY = SM::LDY;
+  constexpr int SEG_EL = 8;               // bf16 per 16-byte segment
+  constexpr int SEG_ROW = D / SEG_EL;     // segments per K/Q row
+  constexpr int SEG_VROW = DVB / SEG_EL;  // segments per V row (this block)
+  constexpr int SEG_AROW = D / 4;         // fp32 segments per decay row
+  constexpr int NSEG = C * SEG_ROW / kThreads;
+  constexpr int NVSEG = C * SEG_VROW / kThreads;
+  constexpr int NASEG = C * SEG_AROW / kThreads;
+  static_assert(NSEG * kThreads == C * SEG_ROW && NVSEG * kThreads == C * SEG_VROW &&
+                    NASEG * kThreads == C * SEG_AROW, "staging tiling");
+  static_assert(kThreads % SEG_ROW == 0, "row segments must not straddle waves");
+  constexpr int Q4 = D / 4;           // 4-column groups per row
+  constexpr int RPP = kThreads / Q4;  // rows per pass of the element-wise phases
+  static_assert(64 % Q4 == 0, "a row of the element-wise phases stays inside one wave");
+
+  __shared__ SM sm;
+  bf16 *const KEh = sm.KE, *const KEl = sm.KE + C * LDB;
+  bf16 *const QEh = sm.QE, *const QEl = sm.QE + C * LDB;
+  float *const Gp = reinterpret_cast<float *>(sm.KF);
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63;
+  const int j = l >> 4, c16 = l & 15;
+
+  const int64_t lb = logical_block();
+  const int nb = (int)(lb % NB);
+  const int64_t sh = lb / NB;
+  const int h = (int)(sh % H);
+  const int64_t s = sh / H;
+  const int64_t bos = cu_seqlens ? (int64_t)cu_seqlens[s] : s * seq_len_dense;
+  const int64_t eos = cu_seqlens ? (int64_t)cu_seqlens[s + 1] : bos + seq_len_dense;
+  const int col = nb * DVB + 16 * w + c16;  // this lane's state/output column
+  constexpr int64_t DD = (int64_t)D * D;
+
+  f32x4 S[NST];
+  {
+    const rsrc_t rs = make_rsrc(S0 ? S0 + sh * DD : o, S0 ? DD * 4 : 0);
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[t][i] = buf_ld4(rs, ((16 * t + 4 * j + i) * D + col) * 4);
+  }
+
+  // ---- chunk inputs, one chunk ahead in registers ---------------------------
+  uint4 kreg[NSEG], qreg[NSEG], vreg[NVSEG], areg[NASEG];
+  float ereg = 0.f;
+  auto fetch = [&](int64_t t0) {
+    const int64_t nn = (eos - t0) < C ? (eos - t0) : C;
+    const int64_t rowb = (int64_t)H * D * 2;
+    const rsrc_t rk = make_rsrc(k + t0 * H * (int64_t)D, nn * rowb);
+    const rsrc_t rq = make_rsrc(q + t0 * H * (int64_t)D, nn * rowb);
+    const rsrc_t rv = make_rsrc(v + t0 * H * (int64_t)D, nn * rowb);
+    const rsrc_t ra = make_rsrc(alpha + t0 * H * (int64_t)D, nn * (int64_t)H * D * 4);
+#pragma unroll
+    for (int u = 0; u < NSEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+      const uint32_t off = (uint32_t)((r * H + h) * D + cs * SEG_EL) * 2;
+      kreg[u] = buf_ld16(rk, off);
+      qreg[u] = buf_ld16(rq, off);
+    }
+#pragma unroll
+    for (int u = 0; u < NVSEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
+      vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + nb * DVB + cs * SEG_EL) * 2);
+    }
+#pragma unroll
+    for (int u = 0; u < NASEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_AROW, cs = sg % SEG_AROW;
+      areg[u] = buf_ld16(ra, (uint32_t)((r * H + h) * D + 4 * cs) * 4);
+    }
+    if (w == 0) {
+      const rsrc_t re = make_rsrc(eta + t0 * H, nn * H * 4);
+      ereg = buf_ld4(re, (uint32_t)(l * H + h) * 4);  // zero past the end
+    }
+  };
+  // registers -> LDS: raw K and Q (bf16, pcol order) in the hi planes, V as
+  // fp32, log2 of the rates as G's input (0 past the end: rate 1), |k|^2,
+  // eta
+  auto stage = [&](int64_t t0) {
+    const int64_t n = (eos - t0) < C ? (eos - t0) : C;
+#pragma unroll
+    for (int u = 0; u < NSEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+      const uint4 kx = kreg[u], qx = qreg[u];
+      *reinterpret_cast<uint2 *>(&KEh[r * LDB + pcol(cs * SEG_EL)]) = uint2{kx.x, kx.y};
+      *reinterpret_cast<uint2 *>(&KEh[r * LDB + pcol(cs * SEG_EL + 4)]) = uint2{kx.z, kx.w};
+      *reinterpret_cast<uint2 *>(&QEh[r * LDB + pcol(cs * SEG_EL)]) = uint2{qx.x, qx.y};
+      *reinterpret_cast<uint2 *>(&QEh[r * LDB + pcol(cs * SEG_EL + 4)]) = uint2{qx.z, qx.w};
+      const bf16x8 kb = __builtin_bit_cast(bf16x8, kx);
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < SEG_EL; ++e) {
+        const float x = static_cast<float>(kb[e]);
+        part += x * x;
+      }
+      part = group_sum<SEG_ROW>(part);
+      if (cs == 0) sm.kk[r] = part;
+    }
+#pragma unroll
+    for (int u = 0; u < NVSEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, vreg[u]);
+      st4(&sm.Vs[r * LDV + cs * SEG_EL], f32x4{static_cast<float>(vb[0]), static_cast<float>(vb[1]),
+                                               static_cast<float>(vb[2]), static_cast<float>(vb[3])});
+      st4(&sm.Vs[r * LDV + cs * SEG_EL + 4], f32x4{static_cast<float>(vb[4]), static_cast<float>(vb[5]),
+                                                   static_cast<float>(vb[6]), static_cast<float>(vb[7])});
+    }
+#pragma unroll
+    for (int u = 0; u < NASEG; ++u) {
+      const int sg = u * kThreads + tid, r = sg / SEG_AROW, cs = sg % SEG_AROW;
+      const bool in = r < n;
+      f32x4 g;
+      g[0] = in ? flog2_rate(__uint_as_float(areg[u].x)) : 0.f;
+      g[1] = in ? flog2_rate(__uint_as_float(areg[u].y)) : 0.f;
+      g[2] = in ? flog2_rate(__uint_as_float(areg[u].z)) : 0.f;
+      g[3] = in ? flog2_rate(__uint_as_float(areg[u].w)) : 0.f;
+      st4(&Gp[r * LDG + 4 * cs], g);
+    }
+    if (w == 0) sm.et[l] = ereg;
+    if (tid == 0) sm.deep = 0;
+  };
+
+  fetch(bos);
+  stage(bos);
+  for (int64_t tok0 = bos; tok0 < eos; tok0 += C) {
+    const int n = (int)((eos - tok0) < C ? (eos - tok0) : C);
+    lds_barrier();  // chunk tok0 is staged
+    fetch(tok0 + C);
+
+    // ---- scan: G per channel, block references and factor vectors ----------
+    if (tid < D) {
+      const int ch = tid;
+      float g = 0.f, rf[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        rf[b] = g;  // G just before block b
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) {
+          const int t = 16 * b + tt;
+          g += Gp[t * LDG + ch];
+          Gp[t * LDG + ch] = g;
+        }
+      }
+      bool deep = false;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) deep |= rf[b] - (b < 3 ? rf[b + 1] : g) > 100.f;
+      if (deep) sm.deep = 1;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        sm.ref[b][ch] = rf[b];
+        sm.Z[b][ch] = fexp2(rf[b]);
+        sm.W[b][ch] = fexp2(g - rf[b]);
+      }
+#pragma unroll
+      for (int b = 1; b < 4; ++b)
+#pragma unroll
+        for (int c = 0; c < b; ++c) sm.P[b * (b - 1) / 2 + c][ch] = fexp2(rf[b] - rf[c]);
+      sm.Zn[ch] = fexp2(g);
+      sm.Gn[ch] = g;
+    }
+    lds_barrier();
+    const bool deep = __builtin_amdgcn_readfirstlane(sm.deep) != 0;
+
+    // ---- form k o E, k o F, q o E as hi/lo planes --------------------------
+    // (exact path: k o 2^G, q o 2^G and k o 2^{G_n - G}, with Z = W = 1).
+    // The k o F row overwrites that row's G: every G of the row is read
+    // (by this wave) before any of the row is written.
+    auto form = [&](bool exact) __attribute__((always_inline)) {
+      const int c4 = 4 * (tid % Q4);
+#pragma unroll
+      for (int r = tid / Q4; r < C; r += RPP) {
+        const f32x4 G = ld4(&Gp[r * LDG + c4]);
+        const f32x4 rf = ld4(&sm.ref[r >> 4][c4]);
+        const f32x4 gn = ld4(&sm.Gn[c4]);
+        const f32x4 kx = to_f32x4(*reinterpret_cast<const bf16x4 *>(&KEh[r * LDB + pcol(c4)]));
+        const f32x4 qx = to_f32x4(*reinterpret_cast<const bf16x4 *>(&QEh[r * LDB + pcol(c4)]));
+        asm volatile("" ::: "memory");  // the row's reads above, its writes below
+        f32x4 ke, kf, qe;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float Ev = exact ? fexp2(G[e]) : fexp2(G[e] - rf[e]);
+          const float Fv = exact ? fexp2(fminf(gn[e] - G[e], 0.f)) : fexp2(rf[e] - G[e]);
+          ke[e] = kx[e] * Ev;
+          kf[e] = kx[e] * Fv;
+          qe[e] = qx[e] * Ev;
+        }
+        const Split4 sk = split4(ke), sf = split4(kf), sq = split4(qe);
+        *reinterpret_cast<bf16x4 *>(&KEh[r * LDB + pcol(c4)]) = sk.hi;
+        *reinterpret_cast<bf16x4 *>(&KEl[r * LDB + pcol(c4)]) = sk.lo;
+        *reinterpret_cast<bf16x4 *>(&QEh[r * LDB + pcol(c4)]) = sq.hi;
+        *reinterpret_cast<bf16x4 *>(&QEl[r * LDB + pcol(c4)]) = sq.lo;
+        *reinterpret_cast<bf16x4 *>(&sm.KF[r * LDR + pcol(c4)]) = sf.hi;
+        *reinterpret_cast<bf16x4 *>(&sm.KF[r * LDR + LO + pcol(c4)]) = sf.lo;
+        asm volatile("" ::: "memory");
+      }
+    };
+    // exact Gram element: sum_i X_t[i] K_s[i] 2^{G_t[i] - G_s[i]} for t >= s
+    // (raw X = Q or K in the hi planes, G still in LDS), else 0
+    auto exact_tile = [&](bool qk, int bi, int bj) __attribute__((always_inline)) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int sc = 16 * bj + c16;
+      const bf16 *X = qk ? QEh : KEh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * bi + 4 * j + i;
+        if (t >= sc) {
+          float a = 0.f;
+#pragma unroll 1
+          for (int ch = 0; ch < D; ch += 4) {
+            const f32x4 x = to_f32x4(*reinterpret_cast<const bf16x4 *>(&X[t * LDB + pcol(ch)]));
+            const f32x4 kv = to_f32x4(*reinterpret_cast<const bf16x4 *>(&KEh[sc * LDB + pcol(ch)]));
+            const f32x4 gt = ld4(&Gp[t * LDG + ch]), gs = ld4(&Gp[sc * LDG + ch]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a += x[e] * kv[e] * fexp2(fminf(gt[e] - gs[e], 0.f));
+          }
+          acc[i] = a;
+        }
+      }
+      return acc;
+    };
+    // Gram tile on the bf16 MFMA: rows 16bi.. of A (k o E or q o E), scaled
+    // per channel by P (off-diagonal pairs), against rows 16bj.. of k o F
+    auto bf_tile = [&](bool qk, int bi, int bj) __attribute__((always_inline)) {
+      const bf16 *Ah = qk ? QEh : KEh, *Al = qk ? QEl : KEl;
+      const bool diag_pair = bi == bj;
+      const float *Pv = sm.P[diag_pair ? 0 : bi * (bi - 1) / 2 + bj];
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u) {
+        const int ao = (16 * bi + c16) * LDB + 32 * u + 8 * j;
+        const int bo = (16 * bj + c16) * LDR + 32 * u + 8 * j;
+        Split8 a, b;
+        a.hi = *reinterpret_cast<const bf16x8 *>(&Ah[ao]);
+        a.lo = *reinterpret_cast<const bf16x8 *>(&Al[ao]);
+        b.hi = *reinterpret_cast<const bf16x8 *>(&sm.KF[bo]);
+        b.lo = *reinterpret_cast<const bf16x8 *>(&sm.KF[bo + LO]);
+        if (!diag_pair) {
+          // this lane's eight channels: 32u + 4j.. and 32u + 16 + 4j..
+          const f32x4 p0 = ld4(&Pv[32 * u + 4 * j]), p1 = ld4(&Pv[32 * u + 16 + 4 * j]);
+          const f32x4 x0 = (to_f32x4(half_lo(a.hi)) + to_f32x4(half_lo(a.lo))) * p0;
+          const f32x4 x1 = (to_f32x4(half_hi(a.hi)) + to_f32x4(half_hi(a.lo))) * p1;
+          a = split8(x0, x1);
+        }
+        acc = mma3(a, b, acc);
+      }
+      return acc;
+    };
+    // ---- Gram tiles, diagonal inverses; Q S, K S, R --------------------------
+    f32x4 jt[6];  // waves 1-3: their Gram tiles until the operand space is free
+    auto gram = [&](bool exact) __attribute__((always_inline)) {
+      if (w == 0) {
+        sm.beta[l] = beta_direct ? sm.et[l] : sm.et[l] / (sm.kk[l] + eps);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // diagonal tiles -> -Diag(beta) Ahat below the diagonal of each block
+        // (acc[i] = Ahat[16b + 4j + i][16b + c16])
+        if (exact) {
+#pragma unroll 1
+          for (int b = 0; b < 4; ++b) {
+            const f32x4 acc = exact_tile(false, b, b);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 4 * j + i;
+              sm.Ld[(b * 16 + c16) * 20 + r] = r > c16 ? -sm.beta[16 * b + r] * acc[i] : 0.f;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const f32x4 acc = bf_tile(false, b, b);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 4 * j + i;
+              sm.Ld[(b * 16 + c16) * 20 + r] = r > c16 ? -sm.beta[16 * b + r] * acc[i] : 0.f;
+            }
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // lane (block j, column c16): column c16 of (I + L_jj)^{-1}
+        float lc[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v4 = ld4(&sm.Ld[(j * 16 + c16) * 20 + 4 * q4]);
+          lc[4 * q4] = v4[0];
+          lc[4 * q4 + 1] = v4[1];
+          lc[4 * q4 + 2] = v4[2];
+          lc[4 * q4 + 3] = v4[3];
+        }
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (r == c16) ? 1.f : 0.f;
+        solve_steps(x, lc, std::make_integer_sequence<int, 15>{});
+        const float bc = sm.beta[16 * j + c16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.Yh[(j * 16 + r) * LDY + c16] = x[r] * bc;
+      } else {
+        // waves 1, 2, 3: jobs [0,5), [5,10), [10,16)
+        const int q0 = 5 * (w - 1);
+        const int nj = w == 3 ? 6 : 5;
+        if (exact) {
+#pragma unroll
+          for (int u = 0; u < 6; ++u) {
+            if (u < nj) {
+              const Job jb = job_of(q0 + u);
+              jt[u] = exact_tile(jb.qk, jb.bi, jb.bj);
+            }
+          }
+          return;
+        }
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+          if (u < nj) {
+            const Job jb = job_of(q0 + u);
+            jt[u] = bf_tile(jb.qk, jb.bi, jb.bj);
+          }
+        }
+      }
+    };
+    // fast path: operands, then the Gram tiles on the MFMA; exact path: the
+    // Gram tiles from the raw inputs, then the operands with absolute
+    // factors (Z = W = 1)
+    if (!deep) form(false);
+    lds_barrier();
+    gram(deep);
+    if (deep) {
+      lds_barrier();  // every read of the raw inputs is done
+      if (tid < D) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          sm.Z[b][tid] = 1.f;
+          sm.W[b][tid] = 1.f;
+        }
+      }
+      form(true);
+      lds_barrier();
+    }
+
+    // Q S and K S with the state rows scaled by 2^{ref_bi}: (q o 2^G) S =
+    // (q o E) (Diag(2^{ref}) S); the scaled state, split, is the B operand
+    f32x4 QS[4], R[4];
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NST / 2; ++kk) {
+        const Split8 Sf = split8(S[2 * kk] * ld4(&sm.Z[bi][32 * kk + 4 * j]),
+                                 S[2 * kk + 1] * ld4(&sm.Z[bi][32 * kk + 16 + 4 * j]));
+        const int ao = (16 * bi + c16) * LDB + 32 * kk + 8 * j;
+        Split8 qa, ka;
+        qa.hi = *reinterpret_cast<const bf16x8 *>(&QEh[ao]);
+        qa.lo = *reinterpret_cast<const bf16x8 *>(&QEl[ao]);
+        ka.hi = *reinterpret_cast<const bf16x8 *>(&KEh[ao]);
+        ka.lo = *reinterpret_cast<const bf16x8 *>(&KEl[ao]);
+        aq = mma3(qa, Sf, aq);
+        ak = mma3(ka, Sf, ak);
+      }
+      QS[bi] = aq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R[bi][i] = sm.Vs[(16 * bi + 4 * j + i) * LDV + 16 * w + c16] - ak[i];
+    }
+    lds_barrier();  // every read of k o E and q o E is done
+
+    // ---- planes over the operand space; k o F -> k o 2^{G_n - G} ------------
+    float *const Ahp = reinterpret_cast<float *>(sm.KE);
+    float *const Mhp = reinterpret_cast<float *>(sm.QE);
+    if (w != 0) {
+      const int q0 = 5 * (w - 1);
+      const int nj = w == 3 ? 6 : 5;
+#pragma unroll
+      for (int u = 0; u < 6; ++u) {
+        if (u < nj) {
+          const Job jb = job_of(q0 + u);
+          const int Sc = 16 * jb.bj + c16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int Rr = 16 * jb.bi + 4 * j + i;
+            if (jb.qk)
+              Mhp[Rr * LDP + Sc] = Rr >= Sc ? jt[u][i] : 0.f;  // M, lower incl. diagonal
+            else
+              Ahp[Rr * LDP + Sc] = -jt[u][i];                  // -Ahat, below the diagonal blocks
+          }
+        }
+      }
+    }
+    {
+      const int c4 = 4 * (tid % Q4);
+#pragma unroll
+      for (int r = tid / Q4; r < C; r += RPP) {
+        bf16x4 *ph = reinterpret_cast<bf16x4 *>(&sm.KF[r * LDR + pcol(c4)]);
+        bf16x4 *pl = reinterpret_cast<bf16x4 *>(&sm.KF[r * LDR + LO + pcol(c4)]);
+        const Split4 sp = split4((to_f32x4(*ph) + to_f32x4(*pl)) * ld4(&sm.W[r >> 4][c4]));
+        *ph = sp.hi;
+        *pl = sp.lo;
+      }
+    }
+    lds_barrier();
+
+    // ---- Delta by block substitution, output (fp32 MFMA) --------------------
+    f32x4 Dl[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      f32x4 acc = R[b];
+#pragma unroll
+      for (int m = 0; m < b; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mma(Ahp[(16 * b + c16) * LDP + 16 * m + 4 * j + i], Dl[m][i], acc);
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d = mma(sm.Yh[(b * 16 + c16) * LDY + 4 * j + i], acc[i], d);
+      Dl[b] = d;
+    }
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      f32x4 acc = QS[bi];
+#pragma unroll
+      for (int mt = 0; mt <= bi; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mma(Mhp[(16 * bi + c16) * LDP + 16 * mt + 4 * j + i], Dl[mt][i], acc);
+      QS[bi] = acc;  // now the output tile
+    }
+    {
+      const rsrc_t ro = make_rsrc(o + tok0 * H * (int64_t)D, (int64_t)n * H * D * 4);
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          buf_st4(ro, (uint32_t)(((16 * bi + 4 * j + i) * H + h) * D + col) * 4, QS[bi][i]);
+    }
+    // S' = Diag(2^{G_n}) S + (k o 2^{G_n - G})^T Delta on the bf16 MFMA: the
+    // A operand by transposing reads of the k o F' planes, Delta split
+#pragma unroll
+    for (int t = 0; t < NST; ++t) S[t] *= ld4(&sm.Zn[16 * t + 4 * j]);
+    const Split8 Hf[2] = {join(split4(Dl[0]), split4(Dl[1])), join(split4(Dl[2]), split4(Dl[3]))};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int t = 0; t < NST; ++t) {
+        const bf16 *base = &sm.KF[pcol(16 * t + 4 * (c16 & 3))];
+        const int r0 = (32 * kk + 4 * j + (c16 >> 2)) * LDR, r1 = (32 * kk + 16 + 4 * j + (c16 >> 2)) * LDR;
+        Split8 kt;
+        kt.hi = __builtin_shufflevector(ld_tr(base + r0), ld_tr(base + r1), 0, 1, 2, 3, 4, 5, 6, 7);
+        kt.lo = __builtin_shufflevector(ld_tr(base + LO + r0), ld_tr(base + LO + r1), 0, 1, 2, 3, 4, 5, 6, 7);
+        S[t] = mma3(kt, Hf[kk], S[t]);
+      }
+    lds_barrier();  // everyone is done with this chunk's LDS
+    stage(tok0 + C);
+  }
+
+  {
+    const rsrc_t rs = make_rsrc(Sfin ? Sfin + sh * DD : o, Sfin ? DD * 4 : 0);
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) buf_st4(rs, ((16 * t + 4 * j + i) * D + col) * 4, S[t][i]);
+  }
+}
+
+template <int D>
+hipError_t launch_kda_bf(const PrefillArgs &a, hipStream_t st) {
+  const int64_t grid = (int64_t)a.n_seqs * a.H * (D / DVB);
+  hipLaunchKernelGGL((prefill_kda_bf_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, st,
+                     static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
+                     static_cast<const bf16 *>(a.v), a.alpha, a.eta, a.cu_seqlens, a.seq_len_dense,
+                     a.H, a.eps, a.beta_direct, a.initial_state, a.o, a.final_state);
+  return hipGetLastError();
+}
+
 template <typename E, int D>
 hipError_t launch_kda(const PrefillArgs &a, hipStream_t st) {
   const int64_t grid = (int64_t)a.n_seqs * a.H * (D / DVB);
@@ -557,7 +1097,7 @@ hipError_t launch_kda(const PrefillArgs &a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_prefill_kda(const PrefillArgs &a, bool bf16_inputs, hipStream_t s) {
-  if (bf16_inputs) return a.D == 128 ? launch_kda<__bf16, 128>(a, s) : launch_kda<__bf16, 64>(a, s);
+  if (bf16_inputs) return a.D == 128 ? launch_kda_bf<128>(a, s) : launch_kda_bf<64>(a, s);
   return a.D == 128 ? launch_kda<float, 128>(a, s) : launch_kda<float, 64>(a, s);
 }
 

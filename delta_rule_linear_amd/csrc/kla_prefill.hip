@@ -101,16 +101,6 @@ __device__ inline bf16x8 lda_perm(const bf16 *row, int j) {
 }
 __device__ inline bf16x4 lda4(const bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
 
-// Column order of the bf16 K and Q rows (and of the M planes' token columns)
-// in the producer/consumer kernel's LDS: within each 32-column block the
-// 4-column groups sit in the order 0, 4, 1, 5, 2, 6, 3, 7.  A state
-// fragment pair (rows 4j..4j+3 of two 16-row tiles) then meets its eight
-// operand values in one 16-byte read, and a Gram tile, which contracts over
-// this index on both sides, is unchanged.  pcol maps a logical column (a
-// multiple of 4) to its place.
-__device__ constexpr int pcol(int c) { return (c & ~31) + ((c & 15) >> 2) * 8 + ((c >> 4) & 1) * 4; }
-static_assert(pcol(0) == 0 && pcol(4) == 8 && pcol(16) == 4 && pcol(20) == 12 && pcol(28) == 28 &&
-                  pcol(44) == 56, "column order");
 
 __device__ inline void store_split(bf16 *h, bf16 *l, int idx, float x) {
   const bf16 hv = static_cast<bf16>(x);
