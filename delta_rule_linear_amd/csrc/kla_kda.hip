@@ -744,35 +744,86 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     fetch(tok0 + C);
 
     // ---- scan: G per channel, block references and factor vectors ----------
-    if (tid < D) {
-      const int ch = tid;
-      float g = 0.f, rf[4];
+    // TPC adjacent lanes share a channel, each with 64 / TPC consecutive
+    // tokens: a running sum in registers, then the parts' totals by DPP
+    // (every lane forms the same prefix of them, in part order).
+    {
+      constexpr int TPC = kThreads / D;  // 2 (D = 128) or 4 (D = 64)
+      constexpr int BPT = 4 / TPC;       // 16-token blocks per lane
+      constexpr int NT = 16 * BPT;
+      static_assert(TPC == 2 || TPC == 4, "lanes per channel");
+      const int ch = tid / TPC, part = tid % TPC;
+      float x[NT];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        rf[b] = g;  // G just before block b
+      for (int tt = 0; tt < NT; ++tt) x[tt] = Gp[(NT * part + tt) * LDG + ch];
+      float run = 0.f;
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt) {
-          const int t = 16 * b + tt;
-          g += Gp[t * LDG + ch];
-          Gp[t * LDG + ch] = g;
-        }
+      for (int tt = 0; tt < NT; ++tt) {
+        run += x[tt];
+        x[tt] = run;
       }
+      // totals of the parts, T[p]; the own blocks' inner references
+      float T[TPC], inner = BPT == 2 ? x[15] : 0.f, in2[TPC];
+      if constexpr (TPC == 2) {
+        const float o = dpp<kQuadXor1>(run), oi = dpp<kQuadXor1>(inner);
+        T[0] = part ? o : run;
+        T[1] = part ? run : o;
+        in2[0] = part ? oi : inner;
+        in2[1] = part ? inner : oi;
+      } else {
+        T[0] = dpp<0x00>(run);
+        T[1] = dpp<0x55>(run);
+        T[2] = dpp<0xAA>(run);
+        T[3] = dpp<0xFF>(run);
+      }
+      float off[TPC];  // G before each part
+      off[0] = 0.f;
+#pragma unroll
+      for (int pp = 1; pp < TPC; ++pp) off[pp] = off[pp - 1] + T[pp - 1];
+      const float g = off[TPC - 1] + T[TPC - 1];  // G_n
+      float mine = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < TPC; ++pp) mine = part == pp ? off[pp] : mine;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) Gp[(NT * part + tt) * LDG + ch] = mine + x[tt];
+      // G just before each 16-token block
+      float rf[4];
+      if constexpr (TPC == 2) {
+        rf[0] = 0.f;
+        rf[1] = in2[0];
+        rf[2] = off[1];
+        rf[3] = off[1] + in2[1];
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) rf[b] = off[b];
+      }
+      // a block whose rates multiply below 2^-100 in this channel sends the
+      // chunk down the exact path
       bool deep = false;
 #pragma unroll
       for (int b = 0; b < 4; ++b) deep |= rf[b] - (b < 3 ? rf[b + 1] : g) > 100.f;
       if (deep) sm.deep = 1;
+      // the factor vectors, shared out over the channel's lanes
+      if (part == 0) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        sm.ref[b][ch] = rf[b];
-        sm.Z[b][ch] = fexp2(rf[b]);
-        sm.W[b][ch] = fexp2(g - rf[b]);
+        for (int b = 0; b < 4; ++b) sm.ref[b][ch] = rf[b];
+        sm.Gn[ch] = g;
       }
+      if (part == (TPC == 2 ? 0 : 1)) {
 #pragma unroll
-      for (int b = 1; b < 4; ++b)
+        for (int b = 0; b < 4; ++b) sm.Z[b][ch] = fexp2(rf[b]);
+      }
+      if (part == (TPC == 2 ? 1 : 2)) {
 #pragma unroll
-        for (int c = 0; c < b; ++c) sm.P[b * (b - 1) / 2 + c][ch] = fexp2(rf[b] - rf[c]);
-      sm.Zn[ch] = fexp2(g);
-      sm.Gn[ch] = g;
+        for (int b = 0; b < 4; ++b) sm.W[b][ch] = fexp2(g - rf[b]);
+        sm.Zn[ch] = fexp2(g);
+      }
+      if (part == TPC - 1) {
+#pragma unroll
+        for (int b = 1; b < 4; ++b)
+#pragma unroll
+          for (int c = 0; c < b; ++c) sm.P[b * (b - 1) / 2 + c][ch] = fexp2(rf[b] - rf[c]);
+      }
     }
     lds_barrier();
     const bool deep = __builtin_amdgcn_readfirstlane(sm.deep) != 0;
