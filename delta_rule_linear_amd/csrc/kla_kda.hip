@@ -567,14 +567,17 @@ struct KdaBfSmem {
   static constexpr int LO = D + 8;
   static constexpr int LDG = D + 8;       // the same rows as fp32 G
   static constexpr int LDV = DVB + 4;
-  static constexpr int LDP = C + 4;       // -Ahat and M planes (fp32), over the k o E and q o E space
-  static constexpr int LDY = 20;
-  static_assert(C * LDP * 4 <= 2 * C * LDB * 2, "planes must fit in the operand space");
-  alignas(16) bf16 KE[2 * C * LDB];  // hi plane then lo plane; raw k in the hi plane until formed
-  alignas(16) bf16 QE[2 * C * LDB];
+  static constexpr int LDA = 20;          // -Ahat blocks (bf16 hi, lo; 16 x 16 each, transposed)
+  static constexpr int LDP = C + 16;      // M planes (bf16 hi, lo; pcol order)
+  static constexpr int LDYT = 24;         // Y^T rows (bf16 hi, lo)
+  static_assert(2 * 6 * 16 * LDA <= 2 * C * LDB && 2 * C * LDP <= 2 * C * LDB,
+                "planes must fit in the operand space");
+  alignas(16) bf16 KE[2 * C * LDB];  // hi plane then lo plane; raw k in the hi plane until formed; -Ahat planes after the Gram phase
+  alignas(16) bf16 QE[2 * C * LDB];  // the same for q; M planes after the Gram phase
   alignas(16) bf16 KF[C * LDR];
   alignas(16) float Vs[C * LDV];
-  alignas(16) float Yh[4 * 16 * LDY];
+  alignas(16) bf16 Yh[4 * 16 * LDYT];  // Y_bb^T, Y_bb = (I + L_bb)^{-1} Diag(beta_b)
+  alignas(16) bf16 Yl[4 * 16 * LDYT];
   alignas(16) float Ld[4 * 16 * 20];
   alignas(16) float kk[C];
   alignas(16) float et[C];
@@ -613,7 +616,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
   constexpr int NB = D / DVB;
   constexpr int NST = D / 16;
   constexpr int LDB = SM::LDB, LDR = SM::LDR, LO = SM::LO, LDG = SM::LDG, LDV = SM::LDV,
-                LDP = SM::LDP, LDY = SM::LDY;
+                LDA = SM::LDA, LDP = SM::LDP, LDYT = SM::LDYT;
   constexpr int SEG_EL = 8;               // bf16 per 16-byte segment
   constexpr int SEG_ROW = D / SEG_EL;     // segments per K/Q row
   constexpr int SEG_VROW = DVB / SEG_EL;  // segments per V row (this block)
@@ -863,13 +866,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     };
     // exact Gram element: sum_i X_t[i] K_s[i] 2^{G_t[i] - G_s[i]} for t >= s
     // (raw X = Q or K in the hi planes, G still in LDS), else 0
-    auto exact_tile = [&](bool qk, int bi, int bj) __attribute__((always_inline)) {
+    // (transposed: element i of lane (j, c16) is row 16bi + c16, column
+    // 16bj + 4j + i; else row 16bi + 4j + i, column 16bj + c16)
+    auto exact_tile = [&](bool qk, int bi, int bj, bool tr) __attribute__((always_inline)) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const int sc = 16 * bj + c16;
       const bf16 *X = qk ? QEh : KEh;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = 16 * bi + 4 * j + i;
+        const int t = tr ? 16 * bi + c16 : 16 * bi + 4 * j + i;
+        const int sc = tr ? 16 * bj + 4 * j + i : 16 * bj + c16;
         if (t >= sc) {
           float a = 0.f;
 #pragma unroll 1
@@ -887,7 +892,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     };
     // Gram tile on the bf16 MFMA: rows 16bi.. of A (k o E or q o E), scaled
     // per channel by P (off-diagonal pairs), against rows 16bj.. of k o F
-    auto bf_tile = [&](bool qk, int bi, int bj) __attribute__((always_inline)) {
+    auto bf_tile = [&](bool qk, int bi, int bj, bool tr) __attribute__((always_inline)) {
       const bf16 *Ah = qk ? QEh : KEh, *Al = qk ? QEl : KEl;
       const bool diag_pair = bi == bj;
       const float *Pv = sm.P[diag_pair ? 0 : bi * (bi - 1) / 2 + bj];
@@ -908,7 +913,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
           const f32x4 x1 = (to_f32x4(half_hi(a.hi)) + to_f32x4(half_hi(a.lo))) * p1;
           a = split8(x0, x1);
         }
-        acc = mma3(a, b, acc);
+        acc = tr ? mma3(b, a, acc) : mma3(a, b, acc);
       }
       return acc;
     };
@@ -925,7 +930,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
         if (exact) {
 #pragma unroll 1
           for (int b = 0; b < 4; ++b) {
-            const f32x4 acc = exact_tile(false, b, b);
+            const f32x4 acc = exact_tile(false, b, b, false);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int r = 4 * j + i;
@@ -935,7 +940,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
         } else {
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
-            const f32x4 acc = bf_tile(false, b, b);
+            const f32x4 acc = bf_tile(false, b, b, false);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int r = 4 * j + i;
@@ -960,9 +965,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == c16) ? 1.f : 0.f;
         solve_steps(x, lc, std::make_integer_sequence<int, 15>{});
+        // column c16 of Y_jj, contiguous in Y^T: two 16-byte writes per plane
         const float bc = sm.beta[16 * j + c16];
+        Split4 yq[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sm.Yh[(j * 16 + r) * LDY + c16] = x[r] * bc;
+        for (int q4 = 0; q4 < 4; ++q4)
+          yq[q4] = split4(f32x4{x[4 * q4] * bc, x[4 * q4 + 1] * bc, x[4 * q4 + 2] * bc, x[4 * q4 + 3] * bc});
+        const int yo = (j * 16 + c16) * LDYT;
+        *reinterpret_cast<bf16x8 *>(&sm.Yh[yo]) = __builtin_shufflevector(yq[0].hi, yq[1].hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        *reinterpret_cast<bf16x8 *>(&sm.Yh[yo + 8]) = __builtin_shufflevector(yq[2].hi, yq[3].hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        *reinterpret_cast<bf16x8 *>(&sm.Yl[yo]) = __builtin_shufflevector(yq[0].lo, yq[1].lo, 0, 1, 2, 3, 4, 5, 6, 7);
+        *reinterpret_cast<bf16x8 *>(&sm.Yl[yo + 8]) = __builtin_shufflevector(yq[2].lo, yq[3].lo, 0, 1, 2, 3, 4, 5, 6, 7);
       } else {
         // waves 1, 2, 3: jobs [0,5), [5,10), [10,16)
         const int q0 = 5 * (w - 1);
@@ -972,7 +985,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
           for (int u = 0; u < 6; ++u) {
             if (u < nj) {
               const Job jb = job_of(q0 + u);
-              jt[u] = exact_tile(jb.qk, jb.bi, jb.bj);
+              jt[u] = exact_tile(jb.qk, jb.bi, jb.bj, true);
             }
           }
           return;
@@ -981,7 +994,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
         for (int u = 0; u < 6; ++u) {
           if (u < nj) {
             const Job jb = job_of(q0 + u);
-            jt[u] = bf_tile(jb.qk, jb.bi, jb.bj);
+            jt[u] = bf_tile(jb.qk, jb.bi, jb.bj, true);
           }
         }
       }
@@ -1031,8 +1044,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     lds_barrier();  // every read of k o E and q o E is done
 
     // ---- planes over the operand space; k o F -> k o 2^{G_n - G} ------------
-    float *const Ahp = reinterpret_cast<float *>(sm.KE);
-    float *const Mhp = reinterpret_cast<float *>(sm.QE);
+    // -Ahat blocks (b, m), m < b, transposed (row 16b + c16 of a lane holds
+    // columns 4j..4j+3), index b(b-1)/2 + m; M in the pcol column order,
+    // its two blocks above the diagonal that the 32-deep products read, (0, 1)
+    // and (2, 3), set to zero
+    bf16 *const Ah = sm.KE, *const Al = sm.KE + 6 * 16 * LDA;
+    bf16 *const Mh = sm.QE, *const Ml = sm.QE + C * LDP;
     if (w != 0) {
       const int q0 = 5 * (w - 1);
       const int nj = w == 3 ? 6 : 5;
@@ -1040,17 +1057,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
       for (int u = 0; u < 6; ++u) {
         if (u < nj) {
           const Job jb = job_of(q0 + u);
-          const int Sc = 16 * jb.bj + c16;
+          const int r = 16 * jb.bi + c16;  // this lane's row
+          f32x4 vals;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int Rr = 16 * jb.bi + 4 * j + i;
-            if (jb.qk)
-              Mhp[Rr * LDP + Sc] = Rr >= Sc ? jt[u][i] : 0.f;  // M, lower incl. diagonal
-            else
-              Ahp[Rr * LDP + Sc] = -jt[u][i];                  // -Ahat, below the diagonal blocks
+            const int sc = 16 * jb.bj + 4 * j + i;
+            vals[i] = jb.qk ? (r >= sc ? jt[u][i] : 0.f) : -jt[u][i];
+          }
+          const Split4 sp = split4(vals);
+          if (jb.qk) {
+            const int off = r * LDP + pcol(16 * jb.bj + 4 * j);
+            *reinterpret_cast<bf16x4 *>(&Mh[off]) = sp.hi;
+            *reinterpret_cast<bf16x4 *>(&Ml[off]) = sp.lo;
+          } else {
+            const int off = ((jb.bi * (jb.bi - 1) / 2 + jb.bj) * 16 + c16) * LDA + 4 * j;
+            *reinterpret_cast<bf16x4 *>(&Ah[off]) = sp.hi;
+            *reinterpret_cast<bf16x4 *>(&Al[off]) = sp.lo;
           }
         }
       }
+    }
+    {
+      // rows 0-15 x columns 16-31 and rows 32-47 x columns 48-63: one
+      // 4-column group of one row of one plane per thread
+      const int zr = (tid >> 3) & 15, zg = tid & 3, zs = (tid >> 2) & 1, zp = tid >> 7;
+      const int row = zs ? 32 + zr : zr, c = (zs ? 48 : 16) + 4 * zg;
+      *reinterpret_cast<bf16x4 *>(&(zp ? Ml : Mh)[row * LDP + pcol(c)]) = bf16x4{};
     }
     {
       const int c4 = 4 * (tid % Q4);
@@ -1065,27 +1097,53 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     }
     lds_barrier();
 
-    // ---- Delta by block substitution, output (fp32 MFMA) --------------------
-    f32x4 Dl[4];
+    // ---- Delta by block substitution, output ---------------------------------
+    // Delta_b = Y_bb (R_b - sum_{m<b} Ahat_bm Delta_m) on the 16-deep bf16 MFMA,
+    // every factor split; then O = Q S + M Delta and the state update on the
+    // 32-deep MFMA with the same split Delta
+    bf16x4 yh[4], yl[4], ah[6], al[6];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      f32x4 acc = R[b];
-#pragma unroll
-      for (int m = 0; m < b; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc = mma(Ahp[(16 * b + c16) * LDP + 16 * m + 4 * j + i], Dl[m][i], acc);
-      f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d = mma(sm.Yh[(b * 16 + c16) * LDY + 4 * j + i], acc[i], d);
-      Dl[b] = d;
+    for (int bb = 0; bb < 4; ++bb) {
+      const int yo = (bb * 16 + 4 * j + (c16 >> 2)) * LDYT + 4 * (c16 & 3);
+      yh[bb] = ld_tr(&sm.Yh[yo]);
+      yl[bb] = ld_tr(&sm.Yl[yo]);
     }
+#pragma unroll
+    for (int qb = 0; qb < 6; ++qb) {
+      const int off = (qb * 16 + c16) * LDA + 4 * j;
+      ah[qb] = *reinterpret_cast<const bf16x4 *>(&Ah[off]);
+      al[qb] = *reinterpret_cast<const bf16x4 *>(&Al[off]);
+    }
+    Split4 Ds[4];
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      f32x4 acc = R[bb];
+#pragma unroll
+      for (int m = 0; m < bb; ++m) {
+        const int qb = bb * (bb - 1) / 2 + m;
+        acc = mma(ah[qb], Ds[m].hi, acc);
+        acc = mma(ah[qb], Ds[m].lo, acc);
+        acc = mma(al[qb], Ds[m].hi, acc);
+      }
+      const Split4 as = split4(acc);
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+      d = mma(yh[bb], as.hi, d);
+      d = mma(yh[bb], as.lo, d);
+      d = mma(yl[bb], as.hi, d);
+      Ds[bb] = split4(d);
+    }
+    const Split8 Df[2] = {join(Ds[0], Ds[1]), join(Ds[2], Ds[3])};
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
       f32x4 acc = QS[bi];
 #pragma unroll
-      for (int mt = 0; mt <= bi; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc = mma(Mhp[(16 * bi + c16) * LDP + 16 * mt + 4 * j + i], Dl[mt][i], acc);
+      for (int kk = 0; kk <= bi / 2; ++kk) {
+        const int off = (16 * bi + c16) * LDP + 32 * kk + 8 * j;
+        Split8 m8;
+        m8.hi = *reinterpret_cast<const bf16x8 *>(&Mh[off]);
+        m8.lo = *reinterpret_cast<const bf16x8 *>(&Ml[off]);
+        acc = mma3(m8, Df[kk], acc);
+      }
       QS[bi] = acc;  // now the output tile
     }
     {
@@ -1096,11 +1154,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
         for (int i = 0; i < 4; ++i)
           buf_st4(ro, (uint32_t)(((16 * bi + 4 * j + i) * H + h) * D + col) * 4, QS[bi][i]);
     }
-    // S' = Diag(2^{G_n}) S + (k o 2^{G_n - G})^T Delta on the bf16 MFMA: the
-    // A operand by transposing reads of the k o F' planes, Delta split
+    // S' = Diag(2^{G_n}) S + (k o 2^{G_n - G})^T Delta: the A operand by
+    // transposing reads of the k o F' planes
 #pragma unroll
     for (int t = 0; t < NST; ++t) S[t] *= ld4(&sm.Zn[16 * t + 4 * j]);
-    const Split8 Hf[2] = {join(split4(Dl[0]), split4(Dl[1])), join(split4(Dl[2]), split4(Dl[3]))};
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -1110,7 +1167,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
         Split8 kt;
         kt.hi = __builtin_shufflevector(ld_tr(base + r0), ld_tr(base + r1), 0, 1, 2, 3, 4, 5, 6, 7);
         kt.lo = __builtin_shufflevector(ld_tr(base + LO + r0), ld_tr(base + LO + r1), 0, 1, 2, 3, 4, 5, 6, 7);
-        S[t] = mma3(kt, Hf[kk], S[t]);
+        S[t] = mma3(kt, Df[kk], S[t]);
       }
     lds_barrier();  // everyone is done with this chunk's LDS
     stage(tok0 + C);
