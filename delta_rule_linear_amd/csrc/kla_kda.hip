@@ -560,6 +560,26 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
 // rows with the log-decays: until the operands are formed, the same bytes
 // hold G as fp32 (D + 8 floats a row), and each row is formed by the one
 // wave that read it, G first.
+// Gram jobs of waves 1-3 in the bf16 kernel.  u = 0..3: the off-diagonal
+// block pairs 2(w-1) and 2(w-1)+1 of (1,0) (2,0) (2,1) (3,0) (3,1) (3,2),
+// each as its K K^T tile (-Ahat, u even) and its Q K^T tile (M, u odd),
+// which share the P-scaled k o F operand; u = 4, 5: the diagonal M blocks
+// (wave 1: blocks 0 and 1, wave 2: block 2, wave 3: block 3).
+__device__ inline Job kda_job(int w, int u) {
+  Job jb;
+  if (u < 4) {
+    const int pp = 2 * (w - 1) + (u >> 1);
+    jb.bi = pp == 0 ? 1 : pp < 3 ? 2 : 3;
+    jb.bj = pp - jb.bi * (jb.bi - 1) / 2;
+    jb.qk = (u & 1) != 0;
+  } else {
+    jb.qk = true;
+    jb.bi = jb.bj = w == 1 ? u - 4 : w;
+  }
+  return jb;
+}
+__device__ inline int kda_njobs(int w) { return w == 1 ? 6 : 5; }
+
 template <int D>
 struct KdaBfSmem {
   static constexpr int LDB = D + 16;      // k o E, q o E rows (bf16; 2 LDB bytes = 32 mod 128)
@@ -669,7 +689,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     const rsrc_t rk = make_rsrc(k + t0 * H * (int64_t)D, nn * rowb);
     const rsrc_t rq = make_rsrc(q + t0 * H * (int64_t)D, nn * rowb);
     const rsrc_t rv = make_rsrc(v + t0 * H * (int64_t)D, nn * rowb);
-    const rsrc_t ra = make_rsrc(alpha + t0 * H * (int64_t)D, nn * (int64_t)H * D * 4);
 #pragma unroll
     for (int u = 0; u < NSEG; ++u) {
       const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
@@ -682,14 +701,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
       const int sg = u * kThreads + tid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
       vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + nb * DVB + cs * SEG_EL) * 2);
     }
+    if (w == 0) {
+      const rsrc_t re = make_rsrc(eta + t0 * H, nn * H * 4);
+      ereg = buf_ld4(re, (uint32_t)(l * H + h) * 4);  // zero past the end
+    }
+  };
+  // the rates (the largest input) are fetched half a chunk later, so their
+  // registers are free during the Gram and Q S / K S phase
+  auto fetch_a = [&](int64_t t0) {
+    const int64_t nn = (eos - t0) < C ? (eos - t0) : C;
+    const rsrc_t ra = make_rsrc(alpha + t0 * H * (int64_t)D, nn * (int64_t)H * D * 4);
 #pragma unroll
     for (int u = 0; u < NASEG; ++u) {
       const int sg = u * kThreads + tid, r = sg / SEG_AROW, cs = sg % SEG_AROW;
       areg[u] = buf_ld16(ra, (uint32_t)((r * H + h) * D + 4 * cs) * 4);
-    }
-    if (w == 0) {
-      const rsrc_t re = make_rsrc(eta + t0 * H, nn * H * 4);
-      ereg = buf_ld4(re, (uint32_t)(l * H + h) * 4);  // zero past the end
     }
   };
   // registers -> LDS: raw K and Q (bf16, pcol order) in the hi planes, V as
@@ -740,6 +765,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
   };
 
   fetch(bos);
+  fetch_a(bos);
   stage(bos);
   for (int64_t tok0 = bos; tok0 < eos; tok0 += C) {
     const int n = (int)((eos - tok0) < C ? (eos - tok0) : C);
@@ -917,6 +943,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
       }
       return acc;
     };
+    // both transposed tiles of an off-diagonal pair (bi, bj): -Ahat from the
+    // k o E rows and M from the q o E rows against rows 16bj.. of k o F,
+    // which carry P_{bi,bj} (scaled once for both)
+    auto bf_pair = [&](int bi, int bj, f32x4 &tk, f32x4 &tq) __attribute__((always_inline)) {
+      const float *Pv = sm.P[bi * (bi - 1) / 2 + bj];
+      tk = f32x4{0.f, 0.f, 0.f, 0.f};
+      tq = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u) {
+        const int ao = (16 * bi + c16) * LDB + 32 * u + 8 * j;
+        const int bo = (16 * bj + c16) * LDR + 32 * u + 8 * j;
+        Split8 ka, qa, f;
+        ka.hi = *reinterpret_cast<const bf16x8 *>(&KEh[ao]);
+        ka.lo = *reinterpret_cast<const bf16x8 *>(&KEl[ao]);
+        qa.hi = *reinterpret_cast<const bf16x8 *>(&QEh[ao]);
+        qa.lo = *reinterpret_cast<const bf16x8 *>(&QEl[ao]);
+        f.hi = *reinterpret_cast<const bf16x8 *>(&sm.KF[bo]);
+        f.lo = *reinterpret_cast<const bf16x8 *>(&sm.KF[bo + LO]);
+        // this lane's eight channels: 32u + 4j.. and 32u + 16 + 4j..
+        const f32x4 p0 = ld4(&Pv[32 * u + 4 * j]), p1 = ld4(&Pv[32 * u + 16 + 4 * j]);
+        f = split8((to_f32x4(half_lo(f.hi)) + to_f32x4(half_lo(f.lo))) * p0,
+                   (to_f32x4(half_hi(f.hi)) + to_f32x4(half_hi(f.lo))) * p1);
+        tk = mma3(f, ka, tk);
+        tq = mma3(f, qa, tq);
+      }
+    };
     // ---- Gram tiles, diagonal inverses; Q S, K S, R --------------------------
     f32x4 jt[6];  // waves 1-3: their Gram tiles until the operand space is free
     auto gram = [&](bool exact) __attribute__((always_inline)) {
@@ -977,24 +1029,28 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
         *reinterpret_cast<bf16x8 *>(&sm.Yl[yo]) = __builtin_shufflevector(yq[0].lo, yq[1].lo, 0, 1, 2, 3, 4, 5, 6, 7);
         *reinterpret_cast<bf16x8 *>(&sm.Yl[yo + 8]) = __builtin_shufflevector(yq[2].lo, yq[3].lo, 0, 1, 2, 3, 4, 5, 6, 7);
       } else {
-        // waves 1, 2, 3: jobs [0,5), [5,10), [10,16)
-        const int q0 = 5 * (w - 1);
-        const int nj = w == 3 ? 6 : 5;
+        // waves 1, 2, 3: the jobs of kda_job
+        const int nj = kda_njobs(w);
         if (exact) {
 #pragma unroll
           for (int u = 0; u < 6; ++u) {
             if (u < nj) {
-              const Job jb = job_of(q0 + u);
+              const Job jb = kda_job(w, u);
               jt[u] = exact_tile(jb.qk, jb.bi, jb.bj, true);
             }
           }
           return;
         }
 #pragma unroll
-        for (int u = 0; u < 6; ++u) {
+        for (int u = 0; u < 4; u += 2) {
+          const Job jb = kda_job(w, u);
+          bf_pair(jb.bi, jb.bj, jt[u], jt[u + 1]);
+        }
+#pragma unroll
+        for (int u = 4; u < 6; ++u) {
           if (u < nj) {
-            const Job jb = job_of(q0 + u);
-            jt[u] = bf_tile(jb.qk, jb.bi, jb.bj, true);
+            const Job jb = kda_job(w, u);
+            jt[u] = bf_tile(true, jb.bi, jb.bj, true);
           }
         }
       }
@@ -1042,6 +1098,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
       for (int i = 0; i < 4; ++i) R[bi][i] = sm.Vs[(16 * bi + 4 * j + i) * LDV + 16 * w + c16] - ak[i];
     }
     lds_barrier();  // every read of k o E and q o E is done
+    fetch_a(tok0 + C);
 
     // ---- planes over the operand space; k o F -> k o 2^{G_n - G} ------------
     // -Ahat blocks (b, m), m < b, transposed (row 16b + c16 of a lane holds
@@ -1051,12 +1108,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     bf16 *const Ah = sm.KE, *const Al = sm.KE + 6 * 16 * LDA;
     bf16 *const Mh = sm.QE, *const Ml = sm.QE + C * LDP;
     if (w != 0) {
-      const int q0 = 5 * (w - 1);
-      const int nj = w == 3 ? 6 : 5;
+      const int nj = kda_njobs(w);
 #pragma unroll
       for (int u = 0; u < 6; ++u) {
         if (u < nj) {
-          const Job jb = job_of(q0 + u);
+          const Job jb = kda_job(w, u);
           const int r = 16 * jb.bi + c16;  // this lane's row
           f32x4 vals;
 #pragma unroll
