@@ -31,13 +31,15 @@ Algorithmic work counted per token-head (d = 128, C = 64):
   gate_variants  the layer prefill with the direct step (Gated DeltaNet) and
                  without decay (DeltaNet), same kernel
   ccq            the curvature-conditioned read: layer prefill (query-
-                 cleaning pass + bf16 prefill on the cleaned query's hi and
-                 lo parts + sum; algorithmic bytes as the prefill plus lambda
+                 cleaning pass + one bf16 prefill reading both planes of the
+                 cleaned query; algorithmic bytes as the prefill plus lambda
                  and the per-(sequence, head) sums) and the decode step
                  (state and running sums read and written once)
   per-channel decay (Kimi Delta Attention gate, `kda` object): the same
                  work with alpha fp32 [.., dk]: 1288 - 4 + 4*d = 1796 B per
-                 token-head; its prefill kernel computes in fp32 (fp32 MFMA)
+                 token-head; with bf16 inputs its prefill's contractions run
+                 on the bf16 MFMA (fp32 factors split hi/lo), so `mfma_frac`
+                 is against the bf16 peak
 
 Clock.  The GPU needs some tens of milliseconds of sustained work to reach
 its steady clock.  Every leg first runs its own launch back to back for at
@@ -63,7 +65,7 @@ FP32_MFMA_PEAK_TF = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
 
 PREFILL_KERNEL = "prefill_pc_kernel"  # the bf16 prefill kernel (producer/consumer waves)
 DECODE_KERNEL = "decode_kernel"
-KDA_KERNEL = "prefill_kda_kernel"      # per-channel decay prefill
+KDA_KERNEL = "prefill_kda_bf_kernel"   # per-channel decay prefill (bf16 inputs)
 BWD_KERNEL = "bwd_kernel"              # backward: the two-sweep kernel
 BWD_FINISH = "bwd_finish_kernel"       # backward: the sum over column slices
 BWD_STATES = "prefill_pc_kernel_states"  # backward (bf16): chunk-start states, no output
@@ -78,7 +80,7 @@ KERNEL_SOURCES = {PREFILL_KERNEL: "delta_rule_linear_amd/csrc/kla_prefill.hip",
 # (prefill_pc_kernel<D, OUT, QLO>: the plain prefill is <128, true, false>)
 KERNEL_MATCH = {PREFILL_KERNEL: "prefill_pc_kernelILi128ELb1ELb0E",
                 DECODE_KERNEL: "decode_kernelIDF16bLi128ELb0E",
-                KDA_KERNEL: "prefill_kda_kernelIDF16bLi128E",
+                KDA_KERNEL: "prefill_kda_bf_kernelILi128E",
                 BWD_KERNEL: "bwd_kernelIDF16bLi128E",
                 BWD_FINISH: "bwd_finish_kernelIDF16bLi128E",
                 BWD_STATES: "prefill_pc_kernelILi128ELb0ELb0E"}
@@ -374,9 +376,11 @@ def bench_kda(args, torch, kla, workloads, launches=50):
                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                         "traffic": measured_traffic(KDA_KERNEL), "kernel": KDA_KERNEL, "avg_launch_us": round(ev_ms * 1e3, 2),
                         "algorithmic_bytes_per_launch": nbytes,
-                        "fp32_mfma_tflops": round(tf, 2),
-                        "fp32_mfma_frac": round(tf / FP32_MFMA_PEAK_TF, 4),
-                        "algorithmic_flops_per_launch": flops},
+                        "mfma_tflops": round(tf, 2),
+                        "mfma_frac": round(tf / BF16_MFMA_PEAK_TF, 4),
+                        "mfma_peak": BF16_MFMA_PEAK_TF,
+                        "algorithmic_flops_per_launch": flops,
+                        "flops_convention": "full-tile 10Cd+6d^2 = 180,224 per token-head"},
            "clock_settle_ms": round(settle_ms, 1)}
     if not args.skip_decode:
         wl = workloads.decode(steps=args.decode_steps, channel_decay=True)
