@@ -92,7 +92,8 @@ def _tiny(a, case, d):
 
 @pytest.mark.parametrize("d,dtype,case", [
     (128, "bf16", "deep_channels"), (128, "bf16", "near_zero_run"), (128, "bf16", "subnormal"),
-    (128, "bf16", "past_bound"), (128, "bf16", "all"), (64, "f32", "all")])
+    (128, "bf16", "past_bound"), (128, "bf16", "all"), (64, "bf16", "all"), (64, "f32", "all"),
+    (64, "bf16", "deep_channels")])
 def test_kda_prefill_tiny_rates(kla, d, dtype, case):
     """Per-channel rates whose product inside a 16-token block falls far
     below 2^-126, mixed with ordinary rates: every output finite and within
