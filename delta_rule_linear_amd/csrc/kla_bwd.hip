@@ -34,9 +34,11 @@
 // inputs DV = 16.  A first
 // sweep runs the chunks forward and stores each chunk-start state slice in
 // the workspace; the reverse sweep then takes the chunks from last to first.
-// Products are fp32 MFMA (v_mfma_f32_16x16x4_f32); the two triangular solves
-// are 16 x 16 block substitutions whose diagonal blocks are inverted first,
-// one wave per block, so the substitution itself is MFMA only.  The column slices' contributions to dq,
+// Products are fp32 MFMA (v_mfma_f32_16x16x4_f32), except dq and dk with bf16
+// inputs, which run on the bf16 MFMA with every fp32 factor split hi/lo; the
+// two triangular solves are 16 x 16 block substitutions whose diagonal blocks
+// are inverted first, one wave per block, so the substitution itself is MFMA
+// only.  The column slices' contributions to dq,
 // dk, dbeta and c land in the workspace and a second kernel adds them in a
 // fixed order (deterministic, no atomics) and finishes dk, deta, dalpha.
 #include <hip/hip_runtime.h>
@@ -447,6 +449,120 @@ __device__ __attribute__((always_inline)) inline void dq_dk_tile(
   }
 }
 
+// The same tile for bf16 inputs on v_mfma_f32_32x32x16_bf16 (lane l supplies
+// contraction indices 16 s + 8 (l / 32) + 0..7 of its row or column); every
+// fp32 factor enters split hi/lo, products as hi*hi + hi*lo + lo*hi (K and Q
+// are bf16 and exact).  The contractions over rows take K and Q columns by
+// transposing LDS reads: in each 16-lane group, lane i addresses row
+// base + i / 4 at column group 4 (i % 4) and receives four rows of column i.
+__device__ inline f32x16 mma32b(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x16 mma32b3(const Split8 &a, const Split8 &b, f32x16 c) {
+  c = mma32b(a.hi, b.hi, c);
+  c = mma32b(a.hi, b.lo, c);
+  return mma32b(a.lo, b.hi, c);
+}
+__device__ inline Split8 split8f(const float (&x)[8]) {
+  return join(split4(f32x4{x[0], x[1], x[2], x[3]}), split4(f32x4{x[4], x[5], x[6], x[7]}));
+}
+template <int D>
+__device__ __attribute__((always_inline)) inline void dq_dk_tile_bf(
+    BwdSmem<__bf16, D> &sm, int T, int I, int l, float glast, rsrc_t r_dq, rsrc_t r_dk, int64_t HD) {
+  using CF = BwdCfg<__bf16, D>;
+  constexpr int LDK = CF::LDK, LDSL = CF::LDSL, DV = CF::DV;
+  const int r32 = l & 31, kh = l >> 5;
+  const int ta = 32 * T + r32;  // this lane's A row
+  const int ib = 32 * I + r32;  // this lane's B column
+  const float fe = fexp2(glast - sm.gl[ta]), fg = sm.gm[ta];
+  // transposing-read address of this lane for rows r0 + 8 kh.. of column block 32 I
+  const int gi = l >> 4, li = l & 15;
+  const int tr_row = 8 * (gi >> 1) + (li >> 2), tr_col = 32 * I + 16 * (gi & 1) + 4 * (li & 3);
+  auto col8 = [&](const __bf16 *X, int r0) __attribute__((always_inline)) {  // X[r0 + 8 kh + e][ib]
+    const bf16x4 a = ld_tr(&X[(r0 + tr_row) * LDK + tr_col]);
+    const bf16x4 b = ld_tr(&X[(r0 + tr_row + 4) * LDK + tr_col]);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto ld8 = [&](const float *X, float f, float (&v)[8]) __attribute__((always_inline)) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(X);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(X + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = f * a[i];
+      v[4 + i] = f * b[i];
+    }
+  };
+  // beta_s K[s][ib] for s = 16 st + 8 kh + e, split
+  auto bk8 = [&](int st) __attribute__((always_inline)) {
+    const bf16x8 k8 = col8(sm.K, 16 * st);
+    float kb[8];
+    ld8(&sm.beta[16 * st + 8 * kh], 1.f, kb);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kb[i] *= static_cast<float>(k8[i]);
+    return split8f(kb);
+  };
+  // dk (one accumulator live at a time keeps the tile within the register budget)
+  {
+    f32x16 ak = {};
+    // E Gend^T and -U S^T over the slice's columns
+#pragma unroll 1
+    for (int st = 0; st < DV / 16; ++st) {
+      const int c0 = 16 * st + 8 * kh;
+      float x[8], y[8];
+      ld8(&sm.Es[ta * LDSL + c0], fe, x);
+      ld8(&sm.Gd[ib * LDSL + c0], 1.f, y);
+      ak = mma32b3(split8f(x), split8f(y), ak);
+      ld8(&sm.Us[ta * LDSL + c0], -fg, x);
+      ld8(&sm.Sc[ib * LDSL + c0], 1.f, y);
+      ak = mma32b3(split8f(x), split8f(y), ak);
+    }
+    // Z^T Q over rows s >= 32 T: A[ta][s] = Xm[s][ta] (column reads), B = Q (exact)
+    for (int st = 2 * T; st < 4; ++st) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = sm.Xm[(16 * st + 8 * kh + e) * LDN + ta];
+      const Split8 xs = split8f(x);
+      const bf16x8 q8 = col8(sm.Q, 16 * st);
+      ak = mma32b(xs.hi, q8, ak);
+      ak = mma32b(xs.lo, q8, ak);
+    }
+    // - W B K over all s (A rows of Am)
+#pragma unroll 1
+    for (int st = 0; st < 4; ++st) {
+      float x[8];
+      ld8(&sm.Am[ta * LDN + 16 * st + 8 * kh], -1.f, x);
+      ak = mma32b3(split8f(x), bk8(st), ak);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * T + 8 * (r >> 2) + 4 * kh + (r & 3);
+      buf_st4(r_dk, (uint32_t)((t * HD + ib) * 4), sm.beta[t] * ak[r]);
+    }
+  }
+  // dq: dO S^T over the slice's columns, Z B K over s < 32 (T + 1) (A rows of Xm)
+  {
+    f32x16 aq = {};
+#pragma unroll
+    for (int st = 0; st < DV / 16; ++st) {
+      const int c0 = 16 * st + 8 * kh;
+      float x[8], y[8];
+      ld8(&sm.Ds[ta * LDSL + c0], fg, x);
+      ld8(&sm.Sc[ib * LDSL + c0], 1.f, y);
+      aq = mma32b3(split8f(x), split8f(y), aq);
+    }
+    for (int st = 0; st < 2 * (T + 1); ++st) {
+      float x[8];
+      ld8(&sm.Xm[ta * LDN + 16 * st + 8 * kh], 1.f, x);
+      aq = mma32b3(split8f(x), bk8(st), aq);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * T + 8 * (r >> 2) + 4 * kh + (r & 3);
+      buf_st4(r_dq, (uint32_t)((t * HD + ib) * 4), aq[r]);
+    }
+  }
+}
+
 template <typename E, int D>
 __device__ inline float block_sum(BwdSmem<E, D> &sm, float x, int w, int l) {
   x = group_sum<32>(x);
@@ -685,7 +801,12 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
     lds_barrier();
     // dq and dk contributions of these columns, as 32 x 32 tiles: wave w takes
     // row block w & 1 and column block w >> 1 of both (D = 64: waves 0-3)
-    if (w < D / 16) dq_dk_tile<E, D>(sm, w & 1, w >> 1, l, glast, r_dq, r_dk, HD);
+    if (w < D / 16) {
+      if constexpr (sizeof(E) == 2)
+        dq_dk_tile_bf<D>(sm, w & 1, w >> 1, l, glast, r_dq, r_dk, HD);
+      else
+        dq_dk_tile<E, D>(sm, w & 1, w >> 1, l, glast, r_dq, r_dk, HD);
+    }
     // Gend <- gamma_n Gend + Q^T Diag(gamma) dO - K^T Diag(gamma beta) U
     constexpr int NT = (NST + BW - 1) / BW;  // state tiles per wave
     f32x4 gnew[NT];
