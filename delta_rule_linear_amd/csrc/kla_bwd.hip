@@ -327,30 +327,44 @@ __device__ inline void residual_tile(BwdSmem<E, D> &sm, int tile, int j, int c16
   }
 }
 
-// Inverse of the unit triangular diagonal block b of Am (lower: the strict
-// lower part, upper: the strict upper part), one column per lane (lanes
-// 0..15 of the calling wave), by column substitution, into Y.
+// Inverses of the four unit triangular diagonal blocks of Am (lower: the
+// strict lower parts; upper: the strict upper parts) into Y, one block per
+// 16-lane row of the calling wave, by column substitution on the identity:
+// lane t of a row holds column t of its block's triangle and column t of the
+// result.  Each step broadcasts the pivot lane's triangle column across the
+// row (v_fmac_f32_dpp row_newbcast, its negation a source modifier).  The
+// triangle columns come straight from LDS, so no VALU write precedes their
+// DPP reads.
+template <int T, bool UPPER>
+__device__ inline void inv_step(float (&x)[16], const float (&lc)[16]) {
+#pragma unroll
+  for (int r = UPPER ? 0 : T + 1; r < (UPPER ? T : 16); ++r)
+    asm("v_fmac_f32_dpp %0, -%1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(x[r]) : "v"(lc[r]), "v"(x[T]), "n"(T));
+}
+template <bool UPPER, int... T>
+__device__ inline void inv_steps(float (&x)[16], const float (&lc)[16], std::integer_sequence<int, T...>) {
+  if constexpr (UPPER)
+    (inv_step<15 - T, true>(x, lc), ...);
+  else
+    (inv_step<T, false>(x, lc), ...);
+}
 template <bool UPPER>
-__device__ inline void invert_block(const float *Am, float *Y, int b, int l) {
-  if (l < 16) {
-    float y[16];
+__device__ inline void invert_blocks(const float *Am, float *Y, int l) {
+  const int b = l >> 4, t = l & 15;
+  const float *Lb = Am + 16 * b * LDN + 16 * b + t;
+  float lc[16], x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) y[r] = r == l ? 1.f : 0.f;
-    const float *L = Am + 16 * b * LDN + 16 * b;
-    if (UPPER) {
+  for (int r = 0; r < 16; ++r) lc[r] = Lb[r * LDN];
+  // a zero the compiler cannot hoist out of the caller's loop (the identity
+  // would otherwise stay live in 16 registers across it)
+  float zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
 #pragma unroll
-      for (int r = 14; r >= 0; --r)
+  for (int r = 0; r < 16; ++r) x[r] = r == t ? 1.f : zero;
+  inv_steps<UPPER>(x, lc, std::make_integer_sequence<int, 16>{});
 #pragma unroll
-        for (int s = r + 1; s < 16; ++s) y[r] = fmaf(-L[r * LDN + s], y[s], y[r]);
-    } else {
-#pragma unroll
-      for (int r = 1; r < 16; ++r)
-#pragma unroll
-        for (int s = 0; s < r; ++s) y[r] = fmaf(-L[r * LDN + s], y[s], y[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Y[b * 16 * LDY + r * LDY + l] = y[r];
-  }
+  for (int r = 0; r < 16; ++r) Y[b * 16 * LDY + r * LDY + t] = x[r];
 }
 
 // Block substitution on 16 columns (from c0) of X (64 rows, pitch LDSL, in
@@ -563,6 +577,50 @@ __device__ __attribute__((always_inline)) inline void dq_dk_tile_bf(
   }
 }
 
+// The state-gradient tiles of a wave for bf16 inputs (16x16x32 bf16 MFMA):
+// column block w & 1, row blocks (w >> 1) + 4 m.  The B operands
+// gamma_t dO[t][c] and -gamma_t beta_t U[t][c] (lane group j holding
+// t = 32 ks + 8 j + 0..7) are split hi/lo once and serve every row block;
+// the A operands Q^T and K^T come exact by transposing reads.
+template <int D, int NT>
+__device__ __attribute__((always_inline)) inline void gend_tiles_bf(BwdSmem<__bf16, D> &sm, int w, int j,
+                                                                   int c16, f32x4 (&gnew)[NT]) {
+  using CF = BwdCfg<__bf16, D>;
+  constexpr int LDK = CF::LDK, LDSL = CF::LDSL;
+  const int cc = 16 * (w & 1) + c16;
+  const float gn = sm.gm[C - 1];
+#pragma unroll
+  for (int m = 0; m < NT; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gnew[m][i] = gn * sm.Gd[(16 * ((w >> 1) + 4 * m) + 4 * j + i) * LDSL + cc];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int t0 = 32 * ks + 8 * j;
+    float xd[8], xu[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float g = sm.gm[t0 + e];
+      xd[e] = g * sm.Ds[(t0 + e) * LDSL + cc];
+      xu[e] = -g * sm.beta[t0 + e] * sm.Us[(t0 + e) * LDSL + cc];
+    }
+    const Split8 bd = split8f(xd), bu = split8f(xu);
+    // lane c16 of group j reads rows 32 ks + 8 j + c16 / 4 (and +4) at columns 16 ti + 4 (c16 % 4)..
+    const int r = t0 + (c16 >> 2);
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+      const int co = 16 * ((w >> 1) + 4 * m) + 4 * (c16 & 3);
+      const bf16x8 qa = __builtin_shufflevector(ld_tr(&sm.Q[r * LDK + co]), ld_tr(&sm.Q[(r + 4) * LDK + co]),
+                                                0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 ka = __builtin_shufflevector(ld_tr(&sm.K[r * LDK + co]), ld_tr(&sm.K[(r + 4) * LDK + co]),
+                                                0, 1, 2, 3, 4, 5, 6, 7);
+      gnew[m] = mma(qa, bd.hi, gnew[m]);
+      gnew[m] = mma(qa, bd.lo, gnew[m]);
+      gnew[m] = mma(ka, bu.hi, gnew[m]);
+      gnew[m] = mma(ka, bu.lo, gnew[m]);
+    }
+  }
+}
+
 template <typename E, int D>
 __device__ inline float block_sum(BwdSmem<E, D> &sm, float x, int w, int l) {
   x = group_sum<32>(x);
@@ -635,8 +693,8 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
     gram<E, D>(sm, false, w, j, c16);
     if (tid < C) sm.fc[tid] = sm.beta[tid] * fexp2(sm.gl[C - 1] - sm.gl[tid]);
     lds_barrier();
-    if (w < 4) invert_block<false>(sm.Am, sm.Yl, w, l);
-    else
+    if (w == 0) invert_blocks<false>(sm.Am, sm.Yl, l);
+    else if (w >= 4)
       for (int tile = w - 4; tile < 4 * NCB; tile += 4) residual_tile<E, D>(sm, tile, j, c16);
     lds_barrier();
     if (w < NCB) tri_solve_y<false, LDSL>(sm.Es, sm.Am, sm.Yl, 16 * w, j, c16);
@@ -703,8 +761,8 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
     if (w >= 4)
       for (int tile = w - 4; tile < 4 * NCB; tile += 4) residual_tile<E, D>(sm, tile, j, c16);
     lds_barrier();
-    if (w < 4) invert_block<false>(sm.Am, sm.Yl, w, l);
-    else invert_block<true>(sm.Am, sm.Yu, w - 4, l);
+    if (w == 0) invert_blocks<false>(sm.Am, sm.Yl, l);
+    else if (w == 4) invert_blocks<true>(sm.Am, sm.Yu, l);
     lds_barrier();
     const float glast = sm.gl[C - 1];
     if (w < NCB) {
@@ -809,14 +867,27 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
     }
     // Gend <- gamma_n Gend + Q^T Diag(gamma) dO - K^T Diag(gamma beta) U
     constexpr int NT = (NST + BW - 1) / BW;  // state tiles per wave
+    auto gtile = [&](int m, int &ti, int &cc) {
+      if constexpr (sizeof(E) == 2) {
+        ti = (w >> 1) + 4 * m;
+        cc = 16 * (w & 1) + c16;
+      } else {
+        const int tt = w + BW * m;
+        ti = tt % (D / 16);
+        cc = 16 * (tt / (D / 16)) + c16;
+      }
+    };
     f32x4 gnew[NT];
-    {
+    if constexpr (sizeof(E) == 2) {
+      static_assert(NT * BW == NST, "bf16 state tiling");
+      gend_tiles_bf<D, NT>(sm, w, j, c16, gnew);
+    } else {
       const float gn = sm.gm[C - 1];
 #pragma unroll
       for (int m = 0; m < NT; ++m) {
-        const int tt = w + BW * m;
-        if (tt >= NST) break;
-        const int ti = tt % (D / 16), cc = 16 * (tt / (D / 16)) + c16;
+        if (w + BW * m >= NST) break;
+        int ti, cc;
+        gtile(m, ti, cc);
         f32x4 acc;
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = gn * sm.Gd[(16 * ti + 4 * j + i) * LDSL + cc];
@@ -832,9 +903,9 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
       float x = 0.f;
 #pragma unroll
       for (int m = 0; m < NT; ++m) {
-        const int tt = w + BW * m;
-        if (tt >= NST) break;
-        const int ti = tt % (D / 16), cc = 16 * (tt / (D / 16)) + c16;
+        if (w + BW * m >= NST) break;
+        int ti, cc;
+        gtile(m, ti, cc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * ti + 4 * j + i;

@@ -13,7 +13,7 @@ import pytest
 import dpp_hazard
 from delta_rule_linear_amd import build as kbuild
 
-SOURCES = ["kla_prefill.hip", "kla_kda.hip"]
+SOURCES = ["kla_prefill.hip", "kla_kda.hip", "kla_bwd.hip"]
 
 
 def test_checker_finds_planted_hazards():
