@@ -121,6 +121,10 @@ __device__ __attribute__((always_inline)) inline f32x4 tile_mm(f32x4 acc, int k0
   return acc;
 }
 __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+// Eight fp32 values as hi/lo bf16 halves of an MFMA operand.
+__device__ inline Split8 split8f(const float (&x)[8]) {
+  return join(split4(f32x4{x[0], x[1], x[2], x[3]}), split4(f32x4{x[4], x[5], x[6], x[7]}));
+}
 
 // Lower tile p (0..9) of a 4x4 block grid, in row order.
 __device__ inline void lower_tile(int p, int &bt, int &bs) {
@@ -311,6 +315,34 @@ __device__ inline void gram(BwdSmem<E, D> &sm, bool with_q, int w, int j, int c1
   }
 }
 
+// A B for a 16-row block of a row-major input (K or Q) and one column of an
+// fp32 row-major plane B, contracted over D: for fp32 inputs on the fp32
+// MFMA; for bf16 inputs on the 16x16x32 bf16 MFMA, A exact (lane c16 of
+// group j reads row c16 at k = 32 ks + 8 j .. +7, one 16-byte read) and B
+// split hi/lo.  Result acc[i] is row 4 j + i of the block.
+template <typename E, int D>
+__device__ __attribute__((always_inline)) inline f32x4 rows_times_plane(const E *A, int lda, const float *B,
+                                                                       int ldb, int j, int c16) {
+  if constexpr (sizeof(E) == 2) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const int k0 = 32 * ks + 8 * j;
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&A[c16 * lda + k0]);
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = B[(k0 + e) * ldb];
+      const Split8 b = split8f(x);
+      acc = mma(a, b.hi, acc);
+      acc = mma(a, b.lo, acc);
+    }
+    return acc;
+  } else {
+    return tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return kf(A[c16 * lda + kx]); },
+                          [&](int kx) { return B[kx * ldb]; });
+  }
+}
+
 // Es <- V - Diag(gamma) K S for tile `tile` (rows 16 (tile % 4), columns
 // 16 (tile / 4) of the slice).
 template <typename E, int D>
@@ -318,8 +350,7 @@ __device__ inline void residual_tile(BwdSmem<E, D> &sm, int tile, int j, int c16
   using CF = BwdCfg<E, D>;
   constexpr int LDK = CF::LDK, LDSL = CF::LDSL;
   const int bt = tile & 3, cc = 16 * (tile >> 2) + c16;
-  f32x4 acc = tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return kf(sm.K[(16 * bt + c16) * LDK + kx]); },
-                             [&](int kx) { return sm.Sc[kx * LDSL + cc]; });
+  const f32x4 acc = rows_times_plane<E, D>(&sm.K[16 * bt * LDK], LDK, &sm.Sc[cc], LDSL, j, c16);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = 16 * bt + 4 * j + i;
@@ -476,9 +507,6 @@ __device__ inline f32x16 mma32b3(const Split8 &a, const Split8 &b, f32x16 c) {
   c = mma32b(a.hi, b.hi, c);
   c = mma32b(a.hi, b.lo, c);
   return mma32b(a.lo, b.hi, c);
-}
-__device__ inline Split8 split8f(const float (&x)[8]) {
-  return join(split4(f32x4{x[0], x[1], x[2], x[3]}), split4(f32x4{x[4], x[5], x[6], x[7]}));
 }
 template <int D>
 __device__ __attribute__((always_inline)) inline void dq_dk_tile_bf(
@@ -771,8 +799,7 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
       // U right-hand side: Diag(gamma_n/gamma) K Gend + Mq^T dO
       for (int tile = w - NCB; tile < 4 * NCB; tile += BW - NCB) {
         const int bt = tile & 3, cc = 16 * (tile >> 2) + c16;
-        f32x4 a1 = tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return kf(sm.K[(16 * bt + c16) * LDK + kx]); },
-                                  [&](int kx) { return sm.Gd[kx * LDSL + cc]; });
+        const f32x4 a1 = rows_times_plane<E, D>(&sm.K[16 * bt * LDK], LDK, &sm.Gd[cc], LDSL, j, c16);
         f32x4 a2 = zero4();
         for (int st = 4 * bt; st < 16; ++st) {
           const int kx = 4 * st + j;
@@ -792,8 +819,7 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
       // O = Diag(gamma) Q S + Mq B E, reduced at once to the rows' dO . o
       for (int tile = w - NCB; tile < 4 * NCB; tile += BW - NCB) {
         const int bt = tile & 3, cb = tile >> 2, cc = 16 * cb + c16;
-        f32x4 a1 = tile_mm<D / 4>(zero4(), 0, j, [&](int kx) { return kf(sm.Q[(16 * bt + c16) * LDK + kx]); },
-                                  [&](int kx) { return sm.Sc[kx * LDSL + cc]; });
+        const f32x4 a1 = rows_times_plane<E, D>(&sm.Q[16 * bt * LDK], LDK, &sm.Sc[cc], LDSL, j, c16);
         f32x4 a2 = zero4();
         for (int st = 0; st < 4 * (bt + 1); ++st) {
           const int kx = 4 * st + j;
