@@ -121,6 +121,14 @@ __device__ __attribute__((always_inline)) inline f32x4 tile_mm(f32x4 acc, int k0
   return acc;
 }
 __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+// A copy of a lane index that the compiler cannot hoist out of the chunk
+// loop: addresses derived from it are recomputed where they are used rather
+// than held (and spilled) across the loop, and every reload of a spill would
+// wait for the chunk's prefetch and stores to drain.
+__device__ inline int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 // Eight fp32 values as hi/lo bf16 halves of an MFMA operand.
 __device__ inline Split8 split8f(const float (&x)[8]) {
   return join(split4(f32x4{x[0], x[1], x[2], x[3]}), split4(f32x4{x[4], x[5], x[6], x[7]}));
@@ -155,9 +163,10 @@ struct Fetch {
 
 template <typename E, int D>
 __device__ inline void fetch(Fetch<E, D> &f, const BwdParams &p, int64_t t0, int n, int h,
-                             int col0, const float *ckslot, bool rev, int tid) {
+                             int col0, const float *ckslot, bool rev, int tid_) {
   using F = Fetch<E, D>;
   constexpr int esz = sizeof(E);
+  const int tid = fresh(tid_);
   const int64_t HD = (int64_t)p.H * D;
   const int64_t base = t0 * HD + (int64_t)h * D;
   const int64_t rows_kq = n > 0 ? ((int64_t)(n - 1) * HD + D) * esz : 0;
@@ -177,10 +186,11 @@ __device__ inline void fetch(Fetch<E, D> &f, const BwdParams &p, int64_t t0, int
     const rsrc_t rd = make_rsrc(p.d_o + base + col0, n > 0 ? ((int64_t)(n - 1) * HD + F::DV) * 4 : 0);
     if (tid < C * F::DSEG)
       f.d = buf_ld16(rd, (uint32_t)((tid / F::DSEG) * HD * 4 + (tid % F::DSEG) * 16));
+    const rsrc_t rs = make_rsrc(ckslot + col0, (int64_t)(D - 1) * D * 4 + F::DV * 4);
 #pragma unroll
     for (int m = 0; m < F::NSS; ++m) {
       const int sg = tid + BT * m, r = sg / F::DSEG, cs = sg % F::DSEG;
-      if (sg < F::NSSEG) f.s[m] = *reinterpret_cast<const uint4 *>(ckslot + (int64_t)r * D + col0 + 4 * cs);
+      if (sg < F::NSSEG) f.s[m] = buf_ld16(rs, (uint32_t)((r * D + 4 * cs) * 4));
     }
   }
   const rsrc_t rv = make_rsrc(static_cast<const E *>(p.v) + base + col0,
@@ -213,7 +223,8 @@ __device__ inline void st4(float *dst, const float *x) {
 // Registers -> LDS (K, Q in the input type, the rest fp32), with the row
 // norms |k|^2 and the raw gates.
 template <typename E, int D>
-__device__ inline void commit(BwdSmem<E, D> &sm, const Fetch<E, D> &f, int n, bool rev, int tid) {
+__device__ inline void commit(BwdSmem<E, D> &sm, const Fetch<E, D> &f, int n, bool rev, int tid_) {
+  const int tid = fresh(tid_);
   using F = Fetch<E, D>;
   using CF = BwdCfg<E, D>;
   constexpr int LDK = CF::LDK, LDSL = CF::LDSL;
@@ -381,8 +392,8 @@ __device__ inline void inv_steps(float (&x)[16], const float (&lc)[16], std::int
     (inv_step<T, false>(x, lc), ...);
 }
 template <bool UPPER>
-__device__ inline void invert_blocks(const float *Am, float *Y, int l) {
-  const int b = l >> 4, t = l & 15;
+__device__ inline void invert_blocks(const float *Am, float *Y, int l_) {
+  const int l = fresh(l_), b = l >> 4, t = l & 15;
   const float *Lb = Am + 16 * b * LDN + 16 * b + t;
   float lc[16], x[16];
 #pragma unroll
