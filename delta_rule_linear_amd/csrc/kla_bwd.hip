@@ -80,9 +80,9 @@ struct BwdSmem {
   alignas(16) float Xm[C * LDN];   // Mq, later Z (lower, diagonal included)
   alignas(16) float Yl[4 * 16 * LDY];  // (I + L_bb)^-1, unit lower, per diagonal block
   alignas(16) float Yu[4 * 16 * LDY];  // (I + Lu_bb)^-1, unit upper
-  float gl[C];    // cumulative log2 decay inside the chunk
-  float gm[C];    // 2^gl
-  float beta[C];
+  alignas(16) float gl[C];    // cumulative log2 decay inside the chunk
+  alignas(16) float gm[C];    // 2^gl
+  alignas(16) float beta[C];
   float kk[C];
   float fc[C];    // per-row factor of the state update
   float scan[C];
@@ -284,6 +284,41 @@ __device__ inline void row_scalars(BwdSmem<E, D> &sm, const BwdParams &p, int n,
   }
 }
 
+// Stores one 16x16 tile of a lower-triangular 64 x 64 plane P (rows
+// 16 bt + 4 j + i, column s = 16 bs + c16) scaled by the decay ratio
+// Gam_ts = 2^(gl_t - gl_s): P[t][s] for t >= s and its mirror P[s][t] for
+// t > s.  MODE 0: Lower(Gam o X) with zeros above; MODE 1: symmetric;
+// MODE 2: Gam o K K^T B below the diagonal (times beta_s), its reverse twin
+// above (times beta_t) and a zero diagonal.  The rows' decay logs come in
+// one read and no element waits on another's loads; lanes with t < s store
+// nothing (their clamped exponent cannot overflow).
+template <int MODE>
+__device__ __attribute__((always_inline)) inline void store_lower_tile(float *P, const float *gl, const float *beta,
+                                                                      f32x4 acc, int bt, int bs, int j, int c16) {
+  const int s = 16 * bs + c16, t0 = 16 * bt + 4 * j;
+  const f32x4 glt = *reinterpret_cast<const f32x4 *>(&gl[t0]);
+  const float gls = gl[s];
+  f32x4 bt4 = {};
+  float bss = 0.f;
+  if constexpr (MODE == 2) {
+    bt4 = *reinterpret_cast<const f32x4 *>(&beta[t0]);
+    bss = beta[s];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + i;
+    const float g = fexp2(fminf(glt[i] - gls, 0.f)) * acc[i];
+    float dv = g, mv = 0.f;
+    if constexpr (MODE == 1) mv = g;
+    if constexpr (MODE == 2) {
+      dv = t == s ? 0.f : g * bss;
+      mv = g * bt4[i];
+    }
+    if (t >= s) P[t * LDN + s] = dv;
+    if (t > s) P[s * LDN + t] = mv;
+  }
+}
+
 // Am <- Gam o K K^T B below the diagonal and its reverse twin
 // (Gam^T o K K^T B) above it; with_q: Xm <- Lower(Gam o Q K^T).  bf16 K and
 // Q go to the bf16 MFMA (exact products, fp32 accumulation); fp32 inputs use
@@ -308,21 +343,10 @@ __device__ inline void gram(BwdSmem<E, D> &sm, bool with_q, int w, int j, int c1
       acc = tile_mm<D / 4>(acc, 0, j, [&](int kx) { return X[(16 * bt + c16) * LDK + kx]; },
                            [&](int kx) { return sm.K[(16 * bs + c16) * LDK + kx]; });
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * bt + 4 * j + i, s = 16 * bs + c16;
-      if (t < s) continue;
-      const float G = fexp2(sm.gl[t] - sm.gl[s]);
-      if (qk) {
-        sm.Xm[t * LDN + s] = G * acc[i];
-        if (t != s) sm.Xm[s * LDN + t] = 0.f;
-      } else if (t == s) {
-        sm.Am[t * LDN + t] = 0.f;
-      } else {
-        sm.Am[t * LDN + s] = G * acc[i] * sm.beta[s];
-        sm.Am[s * LDN + t] = G * acc[i] * sm.beta[t];
-      }
-    }
+    if (qk)
+      store_lower_tile<0>(sm.Xm, sm.gl, sm.beta, acc, bt, bs, j, c16);
+    else
+      store_lower_tile<2>(sm.Am, sm.gl, sm.beta, acc, bt, bs, j, c16);
   }
 }
 
@@ -413,39 +437,40 @@ __device__ inline void invert_blocks(const float *Am, float *Y, int l_) {
 // place) with the unit triangle of Am, the diagonal blocks applied through
 // their inverses Y: for each block b (forward for the lower triangle,
 // backward for the upper one)  X_b <- Y_b (X_b - sum_c Am_bc X_c).  One
-// wave; MFMA only.
+// wave; MFMA only.  The solved blocks stay in registers, lane group j
+// holding rows 4 j .. 4 j + 3 of each: that is the B operand of a step whose
+// contraction index runs as 4 j + i, so the chain reads only the right-hand
+// sides, Am and Y from LDS (the Am and Y rows by 16-byte reads), all of them
+// independent of the chain.
 template <bool UPPER, int LDSL>
 __device__ inline void tri_solve_y(float *X, const float *Am, const float *Y, int c0, int j, int c16) {
   const int cc = c0 + c16;
+  f32x4 xs[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xs[b][i] = X[(16 * b + 4 * j + i) * LDSL + cc];
 #pragma unroll
   for (int bb = 0; bb < 4; ++bb) {
     const int b = UPPER ? 3 - bb : bb;
-    const int k0 = UPPER ? 16 * (b + 1) : 0;
-    const int steps = UPPER ? 4 * (3 - b) : 4 * b;
-    f32x4 r;
+    f32x4 acc = xs[b];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = X[(16 * b + 4 * j + i) * LDSL + cc];
-    if (steps > 0) {
-      f32x4 acc = zero4();
-#pragma unroll 4
-      for (int st = 0; st < steps; ++st) {
-        const int kx = k0 + 4 * st + j;
-        acc = mma(Am[(16 * b + c16) * LDN + kx], X[kx * LDSL + cc], acc);
-      }
+    for (int cb = 0; cb < bb; ++cb) {
+      const int c = UPPER ? 3 - cb : cb;
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(&Am[(16 * b + c16) * LDN + 16 * c + 4 * j]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) X[(16 * b + 4 * j + i) * LDSL + cc] = r[i] - acc[i];
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block's rows are in LDS
+      for (int i = 0; i < 4; ++i) acc = mma(-a[i], xs[c][i], acc);
     }
+    const f32x4 y = *reinterpret_cast<const f32x4 *>(&Y[b * 16 * LDY + c16 * LDY + 4 * j]);
     f32x4 x = zero4();
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int kx = 4 * st + j;
-      x = mma(Y[b * 16 * LDY + c16 * LDY + kx], X[(16 * b + kx) * LDSL + cc], x);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) X[(16 * b + 4 * j + i) * LDSL + cc] = x[i];
-    __builtin_amdgcn_s_waitcnt(0xc07f);
+    for (int i = 0; i < 4; ++i) x = mma(y[i], acc[i], x);
+    xs[b] = x;
   }
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) X[(16 * b + 4 * j + i) * LDSL + cc] = xs[b][i];
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -811,10 +836,18 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
       for (int tile = w - NCB; tile < 4 * NCB; tile += BW - NCB) {
         const int bt = tile & 3, cc = 16 * (tile >> 2) + c16;
         const f32x4 a1 = rows_times_plane<E, D>(&sm.K[16 * bt * LDK], LDK, &sm.Gd[cc], LDSL, j, c16);
+        // Mq^T dO over rows s >= 16 bt, 16 rows (eight loads in flight) per step
         f32x4 a2 = zero4();
-        for (int st = 4 * bt; st < 16; ++st) {
-          const int kx = 4 * st + j;
-          a2 = mma(sm.Xm[kx * LDN + 16 * bt + c16], sm.Ds[kx * LDSL + cc], a2);
+        for (int sb = bt; sb < 4; ++sb) {
+          float xa[4], xb[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kx = 16 * sb + 4 * j + i;
+            xa[i] = sm.Xm[kx * LDN + 16 * bt + c16];
+            xb[i] = sm.Ds[kx * LDSL + cc];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a2 = mma(xa[i], xb[i], a2);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -831,10 +864,16 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
       for (int tile = w - NCB; tile < 4 * NCB; tile += BW - NCB) {
         const int bt = tile & 3, cb = tile >> 2, cc = 16 * cb + c16;
         const f32x4 a1 = rows_times_plane<E, D>(&sm.Q[16 * bt * LDK], LDK, &sm.Sc[cc], LDSL, j, c16);
+        // Mq B E over rows s < 16 (bt + 1), 16 rows per step (Mq rows by 16-byte reads)
         f32x4 a2 = zero4();
-        for (int st = 0; st < 4 * (bt + 1); ++st) {
-          const int kx = 4 * st + j;
-          a2 = mma(sm.Xm[(16 * bt + c16) * LDN + kx], sm.beta[kx] * sm.Es[kx * LDSL + cc], a2);
+        for (int sb = 0; sb <= bt; ++sb) {
+          const f32x4 xa = *reinterpret_cast<const f32x4 *>(&sm.Xm[(16 * bt + c16) * LDN + 16 * sb + 4 * j]);
+          const f32x4 be = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * sb + 4 * j]);
+          float xb[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xb[i] = be[i] * sm.Es[(16 * sb + 4 * j + i) * LDSL + cc];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a2 = mma(xa[i], xb[i], a2);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -877,21 +916,26 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
       int bt, bs;
       lower_tile(zq ? jb - 10 : jb, bt, bs);
       const float *X = zq ? sm.Ds : sm.Us;
-      f32x4 acc = tile_mm<DV / 4>(zero4(), 0, j, [&](int kx) { return X[(16 * bt + c16) * LDSL + kx]; },
-                                  [&](int kx) { return sm.Es[(16 * bs + c16) * LDSL + kx]; });
+      // contraction over the slice's columns, lane group j taking columns
+      // DV / 4 j .. +DV / 4 - 1 of both rows (16-byte reads, all in flight at once)
+      f32x4 acc = zero4();
+      {
+        constexpr int NK = DV / 16;
+        f32x4 a[NK], b[NK];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * bt + 4 * j + i, s2 = 16 * bs + c16;
-        if (t < s2) continue;
-        const float val = fexp2(sm.gl[t] - sm.gl[s2]) * acc[i];
-        if (zq) {
-          sm.Xm[t * LDN + s2] = val;
-          if (t != s2) sm.Xm[s2 * LDN + t] = 0.f;
-        } else {
-          sm.Am[t * LDN + s2] = val;
-          sm.Am[s2 * LDN + t] = val;
+        for (int q = 0; q < NK; ++q) {
+          a[q] = *reinterpret_cast<const f32x4 *>(&X[(16 * bt + c16) * LDSL + (DV / 4) * j + 4 * q]);
+          b[q] = *reinterpret_cast<const f32x4 *>(&sm.Es[(16 * bs + c16) * LDSL + (DV / 4) * j + 4 * q]);
         }
+#pragma unroll
+        for (int q = 0; q < NK; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = mma(a[q][e], b[q][e], acc);
       }
+      if (zq)
+        store_lower_tile<0>(sm.Xm, sm.gl, sm.beta, acc, bt, bs, j, c16);
+      else
+        store_lower_tile<1>(sm.Am, sm.gl, sm.beta, acc, bt, bs, j, c16);
     }
     lds_barrier();
     // dq and dk contributions of these columns, as 32 x 32 tiles: wave w takes
