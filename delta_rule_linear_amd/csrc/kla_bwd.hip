@@ -570,74 +570,60 @@ __device__ __attribute__((always_inline)) inline void dq_dk_tile_bf(
       v[4 + i] = f * b[i];
     }
   };
-  // beta_s K[s][ib] for s = 16 st + 8 kh + e, split
-  auto bk8 = [&](int st) __attribute__((always_inline)) {
+  f32x16 ak = {}, aq = {};
+  // over the slice's columns: E Gend^T and -U S^T (dk), dO S^T (dq); the S
+  // split serves both
+#pragma unroll 1
+  for (int st = 0; st < DV / 16; ++st) {
+    const int c0 = 16 * st + 8 * kh;
+    float x[8], y[8];
+    ld8(&sm.Es[ta * LDSL + c0], fe, x);
+    ld8(&sm.Gd[ib * LDSL + c0], 1.f, y);
+    ak = mma32b3(split8f(x), split8f(y), ak);
+    ld8(&sm.Sc[ib * LDSL + c0], 1.f, y);
+    const Split8 bs = split8f(y);
+    ld8(&sm.Us[ta * LDSL + c0], -fg, x);
+    ak = mma32b3(split8f(x), bs, ak);
+    ld8(&sm.Ds[ta * LDSL + c0], fg, x);
+    aq = mma32b3(split8f(x), bs, aq);
+  }
+  // Z^T Q over rows s >= 32 T: A[ta][s] = Xm[s][ta] (column reads), B = Q (exact)
+  for (int st = 2 * T; st < 4; ++st) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = sm.Xm[(16 * st + 8 * kh + e) * LDN + ta];
+    const Split8 xs = split8f(x);
+    const bf16x8 q8 = col8(sm.Q, 16 * st);
+    ak = mma32b(xs.hi, q8, ak);
+    ak = mma32b(xs.lo, q8, ak);
+  }
+  // - W B K over all s and Z B K over s < 32 (T + 1): beta_s joins the A rows
+  // (Am, Xm), so the B operand is K itself (exact)
+#pragma unroll 1
+  for (int st = 0; st < 4; ++st) {
     const bf16x8 k8 = col8(sm.K, 16 * st);
-    float kb[8];
-    ld8(&sm.beta[16 * st + 8 * kh], 1.f, kb);
+    float be[8], x[8];
+    ld8(&sm.beta[16 * st + 8 * kh], 1.f, be);
+    ld8(&sm.Am[ta * LDN + 16 * st + 8 * kh], -1.f, x);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) kb[i] *= static_cast<float>(k8[i]);
-    return split8f(kb);
-  };
-  // dk (one accumulator live at a time keeps the tile within the register budget)
-  {
-    f32x16 ak = {};
-    // E Gend^T and -U S^T over the slice's columns
-#pragma unroll 1
-    for (int st = 0; st < DV / 16; ++st) {
-      const int c0 = 16 * st + 8 * kh;
-      float x[8], y[8];
-      ld8(&sm.Es[ta * LDSL + c0], fe, x);
-      ld8(&sm.Gd[ib * LDSL + c0], 1.f, y);
-      ak = mma32b3(split8f(x), split8f(y), ak);
-      ld8(&sm.Us[ta * LDSL + c0], -fg, x);
-      ld8(&sm.Sc[ib * LDSL + c0], 1.f, y);
-      ak = mma32b3(split8f(x), split8f(y), ak);
-    }
-    // Z^T Q over rows s >= 32 T: A[ta][s] = Xm[s][ta] (column reads), B = Q (exact)
-    for (int st = 2 * T; st < 4; ++st) {
-      float x[8];
+    for (int i = 0; i < 8; ++i) x[i] *= be[i];
+    const Split8 ws = split8f(x);
+    ak = mma32b(ws.hi, k8, ak);
+    ak = mma32b(ws.lo, k8, ak);
+    if (st < 2 * (T + 1)) {
+      ld8(&sm.Xm[ta * LDN + 16 * st + 8 * kh], 1.f, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = sm.Xm[(16 * st + 8 * kh + e) * LDN + ta];
-      const Split8 xs = split8f(x);
-      const bf16x8 q8 = col8(sm.Q, 16 * st);
-      ak = mma32b(xs.hi, q8, ak);
-      ak = mma32b(xs.lo, q8, ak);
-    }
-    // - W B K over all s (A rows of Am)
-#pragma unroll 1
-    for (int st = 0; st < 4; ++st) {
-      float x[8];
-      ld8(&sm.Am[ta * LDN + 16 * st + 8 * kh], -1.f, x);
-      ak = mma32b3(split8f(x), bk8(st), ak);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = 32 * T + 8 * (r >> 2) + 4 * kh + (r & 3);
-      buf_st4(r_dk, (uint32_t)((t * HD + ib) * 4), sm.beta[t] * ak[r]);
+      for (int i = 0; i < 8; ++i) x[i] *= be[i];
+      const Split8 zs = split8f(x);
+      aq = mma32b(zs.hi, k8, aq);
+      aq = mma32b(zs.lo, k8, aq);
     }
   }
-  // dq: dO S^T over the slice's columns, Z B K over s < 32 (T + 1) (A rows of Xm)
-  {
-    f32x16 aq = {};
 #pragma unroll
-    for (int st = 0; st < DV / 16; ++st) {
-      const int c0 = 16 * st + 8 * kh;
-      float x[8], y[8];
-      ld8(&sm.Ds[ta * LDSL + c0], fg, x);
-      ld8(&sm.Sc[ib * LDSL + c0], 1.f, y);
-      aq = mma32b3(split8f(x), split8f(y), aq);
-    }
-    for (int st = 0; st < 2 * (T + 1); ++st) {
-      float x[8];
-      ld8(&sm.Xm[ta * LDN + 16 * st + 8 * kh], 1.f, x);
-      aq = mma32b3(split8f(x), bk8(st), aq);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = 32 * T + 8 * (r >> 2) + 4 * kh + (r & 3);
-      buf_st4(r_dq, (uint32_t)((t * HD + ib) * 4), aq[r]);
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int t = 32 * T + 8 * (r >> 2) + 4 * kh + (r & 3);
+    buf_st4(r_dk, (uint32_t)((t * HD + ib) * 4), sm.beta[t] * ak[r]);
+    buf_st4(r_dq, (uint32_t)((t * HD + ib) * 4), aq[r]);
   }
 }
 
