@@ -1013,10 +1013,12 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdParams p) {
   const int i = (int)(g % D);
   f32x4 dq = zero4(), dk = zero4();
   float db = 0.f, c = 0.f;
+  // the partials are read once: non-temporal loads keep them from
+  // displacing the rest in the caches
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    dq += *reinterpret_cast<const f32x4 *>(p.ws_dq + (int64_t)s * TH * D + g);
-    dk += *reinterpret_cast<const f32x4 *>(p.ws_dk + (int64_t)s * TH * D + g);
+    dq += __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p.ws_dq + (int64_t)s * TH * D + g));
+    dk += __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p.ws_dk + (int64_t)s * TH * D + g));
     db += p.ws_db[(int64_t)s * TH + th];
     c += p.ws_c[(int64_t)s * TH + th];
   }
@@ -1032,9 +1034,10 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdParams p) {
     coef = beta * beta - 2.f * beta / den;
   }
   const float f = db * coef;
-  *reinterpret_cast<f32x4 *>(p.dq + g) = dq;
-  *reinterpret_cast<f32x4 *>(p.dk + g) =
-      f32x4{fmaf(f, kv[0], dk[0]), fmaf(f, kv[1], dk[1]), fmaf(f, kv[2], dk[2]), fmaf(f, kv[3], dk[3])};
+  __builtin_nontemporal_store(dq, reinterpret_cast<f32x4 *>(p.dq + g));
+  __builtin_nontemporal_store(
+      f32x4{fmaf(f, kv[0], dk[0]), fmaf(f, kv[1], dk[1]), fmaf(f, kv[2], dk[2]), fmaf(f, kv[3], dk[3])},
+      reinterpret_cast<f32x4 *>(p.dk + g));
   if (i == 0) {
     p.d_eta[th] = p.beta_direct ? db : db / (kk + p.eps);
     if (p.alpha) p.d_alpha[th] = c / p.alpha[th];
