@@ -985,7 +985,7 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
   }
   __syncthreads();
   if (p.d_initial) {
-    for (int idx = tid; idx < D * DV; idx += BT) {
+    for (int idx = fresh(tid); idx < D * DV; idx += BT) {
       const int i = idx / DV, c = idx % DV;
       p.d_initial[sh * DD + i * D + col0 + c] = sm.Gd[i * LDSL + c];
     }
