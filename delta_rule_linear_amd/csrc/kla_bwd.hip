@@ -671,6 +671,21 @@ __device__ __attribute__((always_inline)) inline void gend_tiles_bf(BwdSmem<__bf
   }
 }
 
+// Tile m (0, 1) of a wave's share of the U right-hand side or read-out
+// tiles (tile = bt + 4 cb), slot = wave - NCB, or -1.  With bf16 inputs the
+// 8 tiles go to 6 waves; the two waves that take two tiles take the cheapest
+// pairs: the U right-hand side's Mq^T dO part runs over 4 - bt row blocks,
+// the read-out's Mq B E part over bt + 1.
+template <int NCB>
+__device__ inline int side_tile(bool readout, int slot, int m) {
+  if constexpr (NCB == 2) {
+    if (m == 0) return ((readout ? 0x627310 : 0x514023) >> (4 * slot)) & 15;
+    return slot < 2 ? (readout ? 4 + slot : 7 - slot) : -1;
+  } else {
+    return m == 0 && slot < 4 * NCB ? slot : -1;
+  }
+}
+
 template <typename E, int D>
 __device__ inline float block_sum(BwdSmem<E, D> &sm, float x, int w, int l) {
   x = group_sum<32>(x);
@@ -819,7 +834,10 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
       tri_solve_y<false, LDSL>(sm.Es, sm.Am, sm.Yl, 16 * w, j, c16);
     } else {
       // U right-hand side: Diag(gamma_n/gamma) K Gend + Mq^T dO
-      for (int tile = w - NCB; tile < 4 * NCB; tile += BW - NCB) {
+#pragma unroll 1
+      for (int m = 0; m < 2; ++m) {
+        const int tile = side_tile<NCB>(false, w - NCB, m);
+        if (tile < 0) break;
         const int bt = tile & 3, cc = 16 * (tile >> 2) + c16;
         const f32x4 a1 = rows_times_plane<E, D>(&sm.K[16 * bt * LDK], LDK, &sm.Gd[cc], LDSL, j, c16);
         // Mq^T dO over rows s >= 16 bt, 16 rows (eight loads in flight) per step
@@ -847,7 +865,10 @@ __global__ __launch_bounds__(BT) void bwd_kernel(BwdParams p) {
       tri_solve_y<true, LDSL>(sm.Us, sm.Am, sm.Yu, 16 * w, j, c16);
     } else {
       // O = Diag(gamma) Q S + Mq B E, reduced at once to the rows' dO . o
-      for (int tile = w - NCB; tile < 4 * NCB; tile += BW - NCB) {
+#pragma unroll 1
+      for (int m = 0; m < 2; ++m) {
+        const int tile = side_tile<NCB>(true, w - NCB, m);
+        if (tile < 0) break;
         const int bt = tile & 3, cb = tile >> 2, cc = 16 * cb + c16;
         const f32x4 a1 = rows_times_plane<E, D>(&sm.Q[16 * bt * LDK], LDK, &sm.Sc[cc], LDSL, j, c16);
         // Mq B E over rows s < 16 (bt + 1), 16 rows per step (Mq rows by 16-byte reads)
