@@ -33,8 +33,10 @@ static __device__ __align__(256) float scratch[KLA_NOALLOC_SCRATCH_BYTES / sizeo
 namespace kla {
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kScanThreads = 256;
-constexpr int kCols = 64;  // state columns per scan workgroup
+constexpr int kCols = 16;  // state columns per scan workgroup
 
 // ws_a[m] <- I (D x D) for every m < count.
 template <int D>
@@ -53,9 +55,11 @@ __global__ __launch_bounds__(256) void identity_kernel(float *__restrict__ ws_a,
   }
 }
 
-// One workgroup per (sequence, head, block of 64 state columns).  The
-// running start state (D x 64) and the current A_p (D x D) live in LDS;
-// each thread owns CPT consecutive columns of one row of the next state.
+// One workgroup of four waves per (sequence, head, block of 16 state
+// columns).  The running start state (D x 16) and the current A_p (D x D)
+// live in LDS; each step S_{p+1} = A_p S_p + B_p runs on the fp32 MFMA
+// (v_mfma_f32_16x16x4_f32), wave w taking row blocks w, w + 4 (D = 128) of
+// the 16-column block, its accumulators started from B_p.
 template <int D>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const float *__restrict__ S0,
                                                              const float *__restrict__ ws_a,
@@ -63,15 +67,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const float *__restr
                                                              float *__restrict__ ws_s, int H,
                                                              int P) {
   constexpr int NCB = D / kCols;
-  constexpr int TPR = kScanThreads / D;  // threads per state row
-  constexpr int CPT = kCols / TPR;       // columns per thread
-  static_assert(TPR * D == kScanThreads && CPT * TPR == kCols, "scan tiling");
-  __shared__ float As[D * (D + 1)];
+  constexpr int LDA = D + 4;          // A rows: lanes of a 16 x 4 operand read hit distinct banks
+  constexpr int NRT = D / 64;         // row blocks per wave
+  __shared__ float As[D * LDA];
   __shared__ float Ss[D * kCols];
   const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, j = l >> 4, c16 = l & 15;
   const int cb = (int)(blockIdx.x % NCB);
   const int64_t sh = blockIdx.x / NCB;
-  const int r = tid / TPR, c0 = (tid % TPR) * CPT;
   constexpr int64_t DD = (int64_t)D * D;
   const int col0 = cb * kCols;
 
@@ -86,23 +89,36 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const float *__restr
   for (int p = 0; p + 1 < P; ++p) {
     const float *A = ws_a + (sh * (P - 1) + p) * DD;
     const float *B = ws_b + (sh * (P - 1) + p) * DD;
-    for (int i = tid; i < D * D; i += kScanThreads) As[(i / D) * (D + 1) + i % D] = A[i];
+    for (int i = tid; i < D * D / 4; i += kScanThreads) {
+      const int rr = (4 * i) / D, cc = (4 * i) % D;
+      *reinterpret_cast<float4 *>(&As[rr * LDA + cc]) = reinterpret_cast<const float4 *>(A)[i];
+    }
+    f32x4 acc[NRT];
+#pragma unroll
+    for (int m = 0; m < NRT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[m][i] = B[(int64_t)(16 * (w + 4 * m) + 4 * j + i) * D + col0 + c16];
     __syncthreads();
-    float acc[CPT];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) acc[c] = B[(int64_t)r * D + col0 + c0 + c];
-    for (int k = 0; k < D; ++k) {
-      const float a = As[r * (D + 1) + k];
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) acc[c] = fmaf(a, Ss[k * kCols + c0 + c], acc[c]);
+    for (int m = 0; m < NRT; ++m) {
+      const int r0 = 16 * (w + 4 * m);
+#pragma unroll 8
+      for (int st = 0; st < D / 4; ++st) {
+        const int kx = 4 * st + j;
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(As[(r0 + c16) * LDA + kx], Ss[kx * kCols + c16], acc[m],
+                                                       0, 0, 0);
+      }
     }
-    __syncthreads();  // every thread has read Ss and As
-    float *dst = ws_s + (sh * P + p + 1) * DD + (int64_t)r * D + col0 + c0;
+    __syncthreads();  // every wave has read Ss and As
+    float *dst = ws_s + (sh * P + p + 1) * DD + col0 + c16;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      Ss[r * kCols + c0 + c] = acc[c];
-      dst[c] = acc[c];
-    }
+    for (int m = 0; m < NRT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 16 * (w + 4 * m) + 4 * j + i;
+        Ss[rr * kCols + c16] = acc[m][i];
+        dst[(int64_t)rr * D] = acc[m][i];
+      }
     __syncthreads();
   }
 }
