@@ -16,9 +16,11 @@
 // "Metodologia e Estrutura") row r of the state decays by a[r]:
 //   x = S^T (a o k),  y = S^T (a o q),  e = v - x,  o = y + beta (k.q) e,
 //   S_new = Diag(a) S + beta k e^T.
-// The kernel is bound by HBM bandwidth (0.75 flop/byte): one workgroup of
-// 512 threads per (sequence, head), each thread holds RPT rows x 4 columns of
-// the state in registers between the read and the write.  The new state goes
+// The kernel is bound by HBM bandwidth (0.75 flop/byte).  Every column of
+// the state is independent given k and q (x and y are column sums over the
+// rows), so one workgroup of 512 threads takes one (sequence, head) and 64
+// state columns; each thread holds RPT = D / 32 rows x 4 columns of the state
+// in registers between the read and the write.  The new state goes
 // out with non-temporal stores: nothing reads it before the next step, and
 // the stores then keep the caches for the loads.
 #include <hip/hip_runtime.h>
@@ -29,29 +31,32 @@
 namespace kla {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kDecCols = 64;      // state columns per workgroup
+constexpr int kDecThreads = 512;
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 __device__ inline float to_f32(float x) { return x; }
 __device__ inline float to_f32(__bf16 x) { return static_cast<float>(x); }
 
-template <typename E, int D, bool CH>
-__global__ __launch_bounds__(kThreads) void decode_kernel(
+template <typename E, int D, bool CH, int COLS = kDecCols, int NT = kDecThreads>
+__global__ __launch_bounds__(NT) void decode_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ eta, float *__restrict__ state,
     float *__restrict__ o, float eps, int beta_direct) {
-  constexpr int NQ = D / 4;              // float4 column groups per row
-  constexpr int NRG = kThreads / NQ;     // row groups
+  constexpr int NQ = COLS / 4;           // float4 column groups per row (this block)
+  constexpr int NRG = NT / NQ;           // row groups
   constexpr int RPT = D / NRG;           // rows per thread
-  static_assert(NQ * NRG == kThreads && RPT * NRG == D, "decode tiling");
+  static_assert(NQ * NRG == NT && RPT * NRG == D, "decode tiling");
+  constexpr int NCB = D / COLS;
 
-  __shared__ float sq[D], sk[D], sv[D], se[D], sa[CH ? D : 1];
-  __shared__ float px[NRG][D], py[NRG][D];
+  __shared__ float sq[D], sk[D], sv[COLS], se[COLS], sa[CH ? D : 1];
+  __shared__ float px[NRG][COLS], py[NRG][COLS];
 
-  const int64_t sh = blockIdx.x;  // (sequence, head) pair
+  const int64_t sh = blockIdx.x / NCB;  // (sequence, head) pair
+  const int cb = (int)(blockIdx.x % NCB), c0 = cb * COLS;
   const int t = threadIdx.x;
   const int cq = t % NQ, rg = t / NQ;
-  float *Sg = state + sh * (int64_t)(D * D);
+  float *Sg = state + sh * (int64_t)(D * D) + c0;
 
   // Issue the state loads first: they carry all the bytes.
   float4 s[RPT];
@@ -59,12 +64,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   for (int i = 0; i < RPT; ++i)
     s[i] = *reinterpret_cast<const float4 *>(Sg + (rg + NRG * i) * D + 4 * cq);
 
-  if (t < D) {
-    sq[t] = to_f32(q[sh * D + t]);
-    sk[t] = to_f32(k[sh * D + t]);
-    sv[t] = to_f32(v[sh * D + t]);
-    if constexpr (CH) sa[t] = alpha[sh * D + t];
+  for (int i = t; i < D; i += NT) {
+    sq[i] = to_f32(q[sh * D + i]);
+    sk[i] = to_f32(k[sh * D + i]);
+    if constexpr (CH) sa[i] = alpha[sh * D + i];
   }
+  if (t < COLS) sv[t] = to_f32(v[sh * D + c0 + t]);
   const float a = CH ? 1.f : (alpha ? alpha[sh] : 1.f);  // scalar decay (CH: per row below)
   const float et = eta[sh];
   __syncthreads();
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   *reinterpret_cast<float4 *>(&py[rg][4 * cq]) = ys;
   __syncthreads();
 
-  if (t < D) {
+  if (t < COLS) {
     float x = 0.f, y = 0.f;
 #pragma unroll
     for (int r = 0; r < NRG; ++r) {
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     }
     const float e = sv[t] - a * x;
     se[t] = e;
-    o[sh * D + t] = a * y + beta * kq * e;
+    o[sh * D + c0 + t] = a * y + beta * kq * e;
   }
   __syncthreads();
 
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 
 template <typename E>
 hipError_t launch(const DecodeArgs &a, hipStream_t st) {
-  const dim3 grid((unsigned)((int64_t)a.n_seqs * a.H)), block(kThreads);
+  const dim3 grid((unsigned)((int64_t)a.n_seqs * a.H * (a.D / kDecCols))), block(kDecThreads);
   const E *q = static_cast<const E *>(a.q), *k = static_cast<const E *>(a.k),
           *v = static_cast<const E *>(a.v);
   auto kern = a.D == 128 ? (a.channel_decay ? decode_kernel<E, 128, true> : decode_kernel<E, 128, false>)
