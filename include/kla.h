@@ -285,8 +285,9 @@ kla_status kla_decode_step_ex(const void *q, const void *k, const void *v,
  *               channel's rates multiply below 2^-100 inside an aligned
  *               block of 16 tokens takes a slower exact path.)
  * Other arguments and errors as kla_fwd_chunked_ex (whole sequences only; no
- * workspace is needed).  The arithmetic is fp32 throughout (fp32 MFMA), for
- * bf16 and fp32 inputs alike.
+ * workspace is needed).  fp32 inputs run on the fp32 MFMA; bf16 inputs on
+ * the bf16 MFMA, every fp32 factor entering as a hi/lo pair of bf16 values
+ * (each product to about 2^-16 of its size), with fp32 accumulation.
  */
 kla_status kla_fwd_chunked_kda(const void *q, const void *k, const void *v,
                                const float *alpha, const float *eta,
@@ -392,7 +393,10 @@ kla_status kla_decode_step_ccq(const void *q, const void *k, const void *v,
  * chunkwise: a forward sweep stores each chunk-start state in the
  * workspace, a reverse sweep carries the state's gradient from the last
  * chunk to the first, and a second launch adds the column slices'
- * contributions in a fixed order (bitwise deterministic).
+ * contributions in a fixed order (bitwise deterministic).  With bf16
+ * inputs the large products run on the bf16 MFMA with the fp32 factors split
+ * into hi/lo bf16 pairs (each product to about 2^-16 of its size), with fp32
+ * accumulation; fp32 inputs run on the fp32 MFMA.
  *
  *   q, k, v, alpha, eta, cu_seqlens, n_seqs, total_tok, H, dk, dv, chunk,
  *   eps, dtype, beta_mode, initial_state
