@@ -560,25 +560,48 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
 // rows with the log-decays: until the operands are formed, the same bytes
 // hold G as fp32 (D + 8 floats a row), and each row is formed by the one
 // wave that read it, G first.
-// Gram jobs of waves 1-3 in the bf16 kernel.  u = 0..3: the off-diagonal
-// block pairs 2(w-1) and 2(w-1)+1 of (1,0) (2,0) (2,1) (3,0) (3,1) (3,2),
-// each as its K K^T tile (-Ahat, u even) and its Q K^T tile (M, u odd),
-// which share the P-scaled k o F operand; u = 4, 5: the diagonal M blocks
-// (wave 1: blocks 0 and 1, wave 2: block 2, wave 3: block 3).
+// Gram jobs of the bf16 kernel with NW waves (the first four own the state
+// columns).  The K K^T diagonal blocks and their inverses go to one wave
+// (kda_diag_wave); the off-diagonal block pairs of (1,0) (2,0) (2,1) (3,0)
+// (3,1) (3,2), each as its K K^T tile (-Ahat, u even) and its Q K^T tile (M,
+// u odd), which share the P-scaled k o F operand, and then the diagonal M
+// blocks go to the others:
+//   NW = 4: wave 0 the diagonal blocks; waves 1-3 two pairs each
+//           (2(w-1), 2(w-1)+1); diagonal M blocks: wave 1 blocks 0 and 1,
+//           wave 2 block 2, wave 3 block 3;
+//   NW = 8: wave 4 the diagonal blocks; waves 5-7 two pairs each
+//           (2(w-5), 2(w-5)+1); diagonal M block w on waves 0-3, which also
+//           form Q S and K S for their columns.
+template <int NW>
+constexpr int kda_diag_wave() { return NW == 4 ? 0 : 4; }
+template <int NW>
+__device__ inline int kda_npairs(int w) {
+  if constexpr (NW == 4) return w >= 1 ? 2 : 0;
+  else return w >= 5 ? 2 : 0;
+}
+template <int NW>
+__device__ inline int kda_njobs(int w) {
+  if constexpr (NW == 4) return w == 0 ? 0 : (w == 1 ? 6 : 5);
+  else return w >= 5 ? 4 : (w <= 3 ? 1 : 0);
+}
+template <int NW>
 __device__ inline Job kda_job(int w, int u) {
   Job jb;
-  if (u < 4) {
-    const int pp = 2 * (w - 1) + (u >> 1);
+  if (u < 2 * kda_npairs<NW>(w)) {
+    const int pp = (NW == 4 ? 2 * (w - 1) : 2 * (w - 5)) + (u >> 1);
     jb.bi = pp == 0 ? 1 : pp < 3 ? 2 : 3;
     jb.bj = pp - jb.bi * (jb.bi - 1) / 2;
     jb.qk = (u & 1) != 0;
   } else {
     jb.qk = true;
-    jb.bi = jb.bj = w == 1 ? u - 4 : w;
+    if constexpr (NW == 4) jb.bi = w == 1 ? u - 4 : w;
+    else jb.bi = w;
+    jb.bj = jb.bi;
   }
   return jb;
 }
-__device__ inline int kda_njobs(int w) { return w == 1 ? 6 : 5; }
+template <int NW>
+constexpr int kda_maxjobs() { return NW == 4 ? 6 : 4; }
 
 template <int D>
 struct KdaBfSmem {
@@ -625,14 +648,27 @@ __device__ inline f32x4 mma3(const Split8 &a, const Split8 &b, f32x4 c) {
   return mma(a.lo, b.hi, c);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
+// A copy of a lane index that the compiler cannot hoist out of the chunk
+// loop: the addresses derived from it are recomputed where they are used
+// instead of being held in registers across the loop.
+__device__ inline int fresh_lane(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ alpha, const float *__restrict__ eta,
     const int32_t *__restrict__ cu_seqlens, int64_t seq_len_dense, int H, float eps,
     int beta_direct, const float *__restrict__ S0, float *__restrict__ o,
     float *__restrict__ Sfin) {
   using SM = KdaBfSmem<D>;
+  // NW waves; the first NCW = 4 own 16 state columns each (DVB in all), the
+  // others (NW = 8) share only the chunk-wide phases: staging, scan, operand
+  // forming, the Gram tiles and their planes
+  constexpr int KT = 64 * NW, NCW = 4, DIAGW = kda_diag_wave<NW>();
+  static_assert(16 * NCW == DVB, "column waves");
   constexpr int NB = D / DVB;
   constexpr int NST = D / 16;
   constexpr int LDB = SM::LDB, LDR = SM::LDR, LO = SM::LO, LDG = SM::LDG, LDV = SM::LDV,
@@ -641,14 +677,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
   constexpr int SEG_ROW = D / SEG_EL;     // segments per K/Q row
   constexpr int SEG_VROW = DVB / SEG_EL;  // segments per V row (this block)
   constexpr int SEG_AROW = D / 4;         // fp32 segments per decay row
-  constexpr int NSEG = C * SEG_ROW / kThreads;
-  constexpr int NVSEG = C * SEG_VROW / kThreads;
-  constexpr int NASEG = C * SEG_AROW / kThreads;
-  static_assert(NSEG * kThreads == C * SEG_ROW && NVSEG * kThreads == C * SEG_VROW &&
-                    NASEG * kThreads == C * SEG_AROW, "staging tiling");
-  static_assert(kThreads % SEG_ROW == 0, "row segments must not straddle waves");
+  constexpr int NSEG = C * SEG_ROW / KT;
+  constexpr int NVSEG = C * SEG_VROW / KT;
+  constexpr int NASEG = C * SEG_AROW / KT;
+  static_assert(NSEG * KT == C * SEG_ROW && NVSEG * KT == C * SEG_VROW &&
+                    NASEG * KT == C * SEG_AROW, "staging tiling");
+  static_assert(KT % SEG_ROW == 0, "row segments must not straddle waves");
   constexpr int Q4 = D / 4;           // 4-column groups per row
-  constexpr int RPP = kThreads / Q4;  // rows per pass of the element-wise phases
+  constexpr int RPP = KT / Q4;  // rows per pass of the element-wise phases
   static_assert(64 % Q4 == 0, "a row of the element-wise phases stays inside one wave");
 
   __shared__ SM sm;
@@ -672,7 +708,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
   constexpr int64_t DD = (int64_t)D * D;
 
   f32x4 S[NST];
-  {
+  if (w < NCW) {
     const rsrc_t rs = make_rsrc(S0 ? S0 + sh * DD : o, S0 ? DD * 4 : 0);
 #pragma unroll
     for (int t = 0; t < NST; ++t)
@@ -684,6 +720,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
   uint4 kreg[NSEG], qreg[NSEG], vreg[NVSEG], areg[NASEG];
   float ereg = 0.f;
   auto fetch = [&](int64_t t0) {
+    const int tid = fresh_lane(threadIdx.x), l = tid & 63;
     const int64_t nn = (eos - t0) < C ? (eos - t0) : C;
     const int64_t rowb = (int64_t)H * D * 2;
     const rsrc_t rk = make_rsrc(k + t0 * H * (int64_t)D, nn * rowb);
@@ -691,14 +728,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     const rsrc_t rv = make_rsrc(v + t0 * H * (int64_t)D, nn * rowb);
 #pragma unroll
     for (int u = 0; u < NSEG; ++u) {
-      const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+      const int sg = u * KT + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
       const uint32_t off = (uint32_t)((r * H + h) * D + cs * SEG_EL) * 2;
       kreg[u] = buf_ld16(rk, off);
       qreg[u] = buf_ld16(rq, off);
     }
 #pragma unroll
     for (int u = 0; u < NVSEG; ++u) {
-      const int sg = u * kThreads + tid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
+      const int sg = u * KT + tid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
       vreg[u] = buf_ld16(rv, (uint32_t)((r * H + h) * D + nb * DVB + cs * SEG_EL) * 2);
     }
     if (w == 0) {
@@ -709,11 +746,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
   // the rates (the largest input) are fetched half a chunk later, so their
   // registers are free during the Gram and Q S / K S phase
   auto fetch_a = [&](int64_t t0) {
+    const int tid = fresh_lane(threadIdx.x);
     const int64_t nn = (eos - t0) < C ? (eos - t0) : C;
     const rsrc_t ra = make_rsrc(alpha + t0 * H * (int64_t)D, nn * (int64_t)H * D * 4);
 #pragma unroll
     for (int u = 0; u < NASEG; ++u) {
-      const int sg = u * kThreads + tid, r = sg / SEG_AROW, cs = sg % SEG_AROW;
+      const int sg = u * KT + tid, r = sg / SEG_AROW, cs = sg % SEG_AROW;
       areg[u] = buf_ld16(ra, (uint32_t)((r * H + h) * D + 4 * cs) * 4);
     }
   };
@@ -721,10 +759,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
   // fp32, log2 of the rates as G's input (0 past the end: rate 1), |k|^2,
   // eta
   auto stage = [&](int64_t t0) {
+    const int tid = fresh_lane(threadIdx.x), l = tid & 63;
     const int64_t n = (eos - t0) < C ? (eos - t0) : C;
 #pragma unroll
     for (int u = 0; u < NSEG; ++u) {
-      const int sg = u * kThreads + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
+      const int sg = u * KT + tid, r = sg / SEG_ROW, cs = sg % SEG_ROW;
       const uint4 kx = kreg[u], qx = qreg[u];
       *reinterpret_cast<uint2 *>(&KEh[r * LDB + pcol(cs * SEG_EL)]) = uint2{kx.x, kx.y};
       *reinterpret_cast<uint2 *>(&KEh[r * LDB + pcol(cs * SEG_EL + 4)]) = uint2{kx.z, kx.w};
@@ -742,7 +781,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     }
 #pragma unroll
     for (int u = 0; u < NVSEG; ++u) {
-      const int sg = u * kThreads + tid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
+      const int sg = u * KT + tid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
       const bf16x8 vb = __builtin_bit_cast(bf16x8, vreg[u]);
       st4(&sm.Vs[r * LDV + cs * SEG_EL], f32x4{static_cast<float>(vb[0]), static_cast<float>(vb[1]),
                                                static_cast<float>(vb[2]), static_cast<float>(vb[3])});
@@ -751,7 +790,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     }
 #pragma unroll
     for (int u = 0; u < NASEG; ++u) {
-      const int sg = u * kThreads + tid, r = sg / SEG_AROW, cs = sg % SEG_AROW;
+      const int sg = u * KT + tid, r = sg / SEG_AROW, cs = sg % SEG_AROW;
       const bool in = r < n;
       f32x4 g;
       g[0] = in ? flog2_rate(__uint_as_float(areg[u].x)) : 0.f;
@@ -768,6 +807,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
   fetch_a(bos);
   stage(bos);
   for (int64_t tok0 = bos; tok0 < eos; tok0 += C) {
+    // lane indices (and the addresses from them) recomputed in every chunk
+    const int tid = fresh_lane(threadIdx.x), l = tid & 63, j = l >> 4, c16 = l & 15;
+    const int col = nb * DVB + 16 * w + c16;
     const int n = (int)((eos - tok0) < C ? (eos - tok0) : C);
     lds_barrier();  // chunk tok0 is staged
     fetch(tok0 + C);
@@ -777,7 +819,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     // tokens: a running sum in registers, then the parts' totals by DPP
     // (every lane forms the same prefix of them, in part order).
     {
-      constexpr int TPC = kThreads / D;  // 2 (D = 128) or 4 (D = 64)
+      constexpr int TPC = KT / D;  // 4 (D = 128 with 8 waves, D = 64 with 4)
       constexpr int BPT = 4 / TPC;       // 16-token blocks per lane
       constexpr int NT = 16 * BPT;
       static_assert(TPC == 2 || TPC == 4, "lanes per channel");
@@ -970,9 +1012,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
       }
     };
     // ---- Gram tiles, diagonal inverses; Q S, K S, R --------------------------
-    f32x4 jt[6];  // waves 1-3: their Gram tiles until the operand space is free
+    f32x4 jt[kda_maxjobs<NW>()];  // a wave's Gram tiles until the operand space is free
     auto gram = [&](bool exact) __attribute__((always_inline)) {
-      if (w == 0) {
+      if (w == DIAGW) {
         sm.beta[l] = beta_direct ? sm.et[l] : sm.et[l] / (sm.kk[l] + eps);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -1029,13 +1071,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
         *reinterpret_cast<bf16x8 *>(&sm.Yl[yo]) = __builtin_shufflevector(yq[0].lo, yq[1].lo, 0, 1, 2, 3, 4, 5, 6, 7);
         *reinterpret_cast<bf16x8 *>(&sm.Yl[yo + 8]) = __builtin_shufflevector(yq[2].lo, yq[3].lo, 0, 1, 2, 3, 4, 5, 6, 7);
       } else {
-        // waves 1, 2, 3: the jobs of kda_job
-        const int nj = kda_njobs(w);
+        // the other waves: the jobs of kda_job
+        const int nj = kda_njobs<NW>(w), np = kda_npairs<NW>(w);
         if (exact) {
 #pragma unroll
-          for (int u = 0; u < 6; ++u) {
+          for (int u = 0; u < kda_maxjobs<NW>(); ++u) {
             if (u < nj) {
-              const Job jb = kda_job(w, u);
+              const Job jb = kda_job<NW>(w, u);
               jt[u] = exact_tile(jb.qk, jb.bi, jb.bj, true);
             }
           }
@@ -1043,13 +1085,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
         }
 #pragma unroll
         for (int u = 0; u < 4; u += 2) {
-          const Job jb = kda_job(w, u);
-          bf_pair(jb.bi, jb.bj, jt[u], jt[u + 1]);
+          if (u < 2 * np) {
+            const Job jb = kda_job<NW>(w, u);
+            bf_pair(jb.bi, jb.bj, jt[u], jt[u + 1]);
+          }
         }
 #pragma unroll
-        for (int u = 4; u < 6; ++u) {
-          if (u < nj) {
-            const Job jb = kda_job(w, u);
+        for (int u = 0; u < kda_maxjobs<NW>(); ++u) {
+          if (u >= 2 * np && u < nj) {
+            const Job jb = kda_job<NW>(w, u);
             jt[u] = bf_tile(true, jb.bi, jb.bj, true);
           }
         }
@@ -1079,6 +1123,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     f32x4 QS[4], R[4];
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
+      if (w >= NCW) break;
       f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NST / 2; ++kk) {
@@ -1107,12 +1152,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     // and (2, 3), set to zero
     bf16 *const Ah = sm.KE, *const Al = sm.KE + 6 * 16 * LDA;
     bf16 *const Mh = sm.QE, *const Ml = sm.QE + C * LDP;
-    if (w != 0) {
-      const int nj = kda_njobs(w);
+    if (w != DIAGW) {
+      const int nj = kda_njobs<NW>(w);
 #pragma unroll
-      for (int u = 0; u < 6; ++u) {
+      for (int u = 0; u < kda_maxjobs<NW>(); ++u) {
         if (u < nj) {
-          const Job jb = kda_job(w, u);
+          const Job jb = kda_job<NW>(w, u);
           const int r = 16 * jb.bi + c16;  // this lane's row
           f32x4 vals;
 #pragma unroll
@@ -1136,9 +1181,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     {
       // rows 0-15 x columns 16-31 and rows 32-47 x columns 48-63: one
       // 4-column group of one row of one plane per thread
-      const int zr = (tid >> 3) & 15, zg = tid & 3, zs = (tid >> 2) & 1, zp = tid >> 7;
+      const int zr = (tid >> 3) & 15, zg = tid & 3, zs = (tid >> 2) & 1, zp = (tid >> 7) & 1;
       const int row = zs ? 32 + zr : zr, c = (zs ? 48 : 16) + 4 * zg;
-      *reinterpret_cast<bf16x4 *>(&(zp ? Ml : Mh)[row * LDP + pcol(c)]) = bf16x4{};
+      if (tid < 256) *reinterpret_cast<bf16x4 *>(&(zp ? Ml : Mh)[row * LDP + pcol(c)]) = bf16x4{};
     }
     {
       const int c4 = 4 * (tid % Q4);
@@ -1153,6 +1198,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
     }
     lds_barrier();
 
+    if (w < NCW) {
     // ---- Delta by block substitution, output ---------------------------------
     // Delta_b = Y_bb (R_b - sum_{m<b} Ahat_bm Delta_m) on the 16-deep bf16 MFMA,
     // every factor split; then O = Q S + M Delta and the state update on the
@@ -1225,11 +1271,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
         kt.lo = __builtin_shufflevector(ld_tr(base + LO + r0), ld_tr(base + LO + r1), 0, 1, 2, 3, 4, 5, 6, 7);
         S[t] = mma3(kt, Df[kk], S[t]);
       }
+    }
     lds_barrier();  // everyone is done with this chunk's LDS
     stage(tok0 + C);
   }
 
-  {
+  if (w < NCW) {
     const rsrc_t rs = make_rsrc(Sfin ? Sfin + sh * DD : o, Sfin ? DD * 4 : 0);
 #pragma unroll
     for (int t = 0; t < NST; ++t)
@@ -1240,8 +1287,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_bf_kernel(
 
 template <int D>
 hipError_t launch_kda_bf(const PrefillArgs &a, hipStream_t st) {
+  // d = 128: four more waves for the chunk-wide phases
+  constexpr int NW = D == 128 ? 8 : 4;
   const int64_t grid = (int64_t)a.n_seqs * a.H * (D / DVB);
-  hipLaunchKernelGGL((prefill_kda_bf_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL((prefill_kda_bf_kernel<D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, st,
                      static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
                      static_cast<const bf16 *>(a.v), a.alpha, a.eta, a.cu_seqlens, a.seq_len_dense,
                      a.H, a.eps, a.beta_direct, a.initial_state, a.o, a.final_state);
