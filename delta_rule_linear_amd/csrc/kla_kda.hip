@@ -570,8 +570,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
 //           (2(w-1), 2(w-1)+1); diagonal M blocks: wave 1 blocks 0 and 1,
 //           wave 2 block 2, wave 3 block 3;
 //   NW = 8: wave 4 the diagonal blocks; waves 5-7 two pairs each
-//           (2(w-5), 2(w-5)+1); diagonal M block w on waves 0-3, which also
-//           form Q S and K S for their columns.
+//           (2(w-5), 2(w-5)+1); diagonal M blocks: wave 5 blocks 0 and 1,
+//           wave 6 block 2, wave 7 block 3 (waves 0-3 form Q S and K S for
+//           their columns meanwhile).
 template <int NW>
 constexpr int kda_diag_wave() { return NW == 4 ? 0 : 4; }
 template <int NW>
@@ -582,7 +583,7 @@ __device__ inline int kda_npairs(int w) {
 template <int NW>
 __device__ inline int kda_njobs(int w) {
   if constexpr (NW == 4) return w == 0 ? 0 : (w == 1 ? 6 : 5);
-  else return w >= 5 ? 4 : (w <= 3 ? 1 : 0);
+  else return w >= 5 ? (w == 5 ? 6 : 5) : 0;
 }
 template <int NW>
 __device__ inline Job kda_job(int w, int u) {
@@ -595,13 +596,13 @@ __device__ inline Job kda_job(int w, int u) {
   } else {
     jb.qk = true;
     if constexpr (NW == 4) jb.bi = w == 1 ? u - 4 : w;
-    else jb.bi = w;
+    else jb.bi = w == 5 ? u - 4 : w - 4;
     jb.bj = jb.bi;
   }
   return jb;
 }
 template <int NW>
-constexpr int kda_maxjobs() { return NW == 4 ? 6 : 4; }
+constexpr int kda_maxjobs() { return 6; }
 
 template <int D>
 struct KdaBfSmem {
