@@ -553,8 +553,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
 // factors is the three MFMAs hi*hi + hi*lo + lo*hi (the lo*lo term is below
 // 2^-16 of the product).  The operand planes are kept as bf16 hi and lo
 // planes in the pcol column order, so a state fragment pair or a Gram
-// operand is one 16-byte read.  The substitution and M Delta stay on the
-// fp32 MFMA.
+// operand is one 16-byte read.  The substitution and M Delta run on the
+// 16- and 32-deep bf16 MFMA with every factor split the same way.
 //
 // LDS: the k o E and q o E planes (hi, lo); the k o F planes share their
 // rows with the log-decays: until the operands are formed, the same bytes
