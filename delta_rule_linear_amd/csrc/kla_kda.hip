@@ -1186,19 +1186,40 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
       const int row = zs ? 32 + zr : zr, c = (zs ? 48 : 16) + 4 * zg;
       if (tid < 256) *reinterpret_cast<bf16x4 *>(&(zp ? Ml : Mh)[row * LDP + pcol(c)]) = bf16x4{};
     }
-    {
-      const int c4 = 4 * (tid % Q4);
+    // k o F -> k o F' over all rows: here with four waves; with helper
+    // waves, by them during the substitution (before the state update).
+    // Every row is read before any is written.
+    auto rescale_kf = [&](int t0) __attribute__((always_inline)) {
+      constexpr int NTH = NW == NCW ? KT : KT - 64 * NCW, RS = NTH / Q4, NR = C / RS;
+      static_assert(NR * RS == C, "rescale tiling");
+      const int c4 = 4 * (t0 % Q4), r0 = t0 / Q4;
+      bf16x4 xh[NR], xl[NR];
+      f32x4 wv[NR];
 #pragma unroll
-      for (int r = tid / Q4; r < C; r += RPP) {
-        bf16x4 *ph = reinterpret_cast<bf16x4 *>(&sm.KF[r * LDR + pcol(c4)]);
-        bf16x4 *pl = reinterpret_cast<bf16x4 *>(&sm.KF[r * LDR + LO + pcol(c4)]);
-        const Split4 sp = split4((to_f32x4(*ph) + to_f32x4(*pl)) * ld4(&sm.W[r >> 4][c4]));
-        *ph = sp.hi;
-        *pl = sp.lo;
+      for (int u = 0; u < NR; ++u) {
+        const int r = r0 + u * RS;
+        xh[u] = *reinterpret_cast<const bf16x4 *>(&sm.KF[r * LDR + pcol(c4)]);
+        xl[u] = *reinterpret_cast<const bf16x4 *>(&sm.KF[r * LDR + LO + pcol(c4)]);
+        wv[u] = ld4(&sm.W[r >> 4][c4]);
       }
-    }
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
+        const int r = r0 + u * RS;
+        const Split4 sp = split4((to_f32x4(xh[u]) + to_f32x4(xl[u])) * wv[u]);
+        *reinterpret_cast<bf16x4 *>(&sm.KF[r * LDR + pcol(c4)]) = sp.hi;
+        *reinterpret_cast<bf16x4 *>(&sm.KF[r * LDR + LO + pcol(c4)]) = sp.lo;
+      }
+    };
+    if constexpr (NW == NCW) rescale_kf(tid);
     lds_barrier();
 
+    if constexpr (NW != NCW) {
+      if (w >= NCW) {
+        rescale_kf(tid - 64 * NCW);
+        lds_barrier();  // k o F' is formed
+      }
+    }
     if (w < NCW) {
     // ---- Delta by block substitution, output ---------------------------------
     // Delta_b = Y_bb (R_b - sum_{m<b} Ahat_bm Delta_m) on the 16-deep bf16 MFMA,
@@ -1261,6 +1282,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
     // transposing reads of the k o F' planes
 #pragma unroll
     for (int t = 0; t < NST; ++t) S[t] *= ld4(&sm.Zn[16 * t + 4 * j]);
+    if constexpr (NW != NCW) lds_barrier();  // the helper waves' k o F'
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
