@@ -545,21 +545,24 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
 }
 
 // ---- bf16 inputs: the contractions on the bf16 MFMA ------------------------
-// The same chunk form, scan, exact path and substitution as above, with the
-// three large contraction groups moved to v_mfma_f32_16x16x32_bf16: the
-// Gram tiles (k o E or q o E against k o F), Q S and K S, and the state
-// update (k o 2^{G_n - G})^T Delta.  Every fp32 factor there enters as a
-// bf16 pair hi = bf16(x), lo = bf16(x - hi), and a product of two split
-// factors is the three MFMAs hi*hi + hi*lo + lo*hi (the lo*lo term is below
-// 2^-16 of the product).  The operand planes are kept as bf16 hi and lo
-// planes in the pcol column order, so a state fragment pair or a Gram
-// operand is one 16-byte read.  The substitution and M Delta run on the
-// 16- and 32-deep bf16 MFMA with every factor split the same way.
+// The same chunk form, exact path and substitution as above.  The fast path
+// takes its decay factors as products of the rates instead of exponentials
+// of summed log-rates (the same quantities: E_t = 2^{G_t - ref_b} is the
+// product of block b's rates up to t, F_t = 1 / E_t, and every factor vector
+// a product of block totals).  The contractions run on
+// v_mfma_f32_16x16x32_bf16: the Gram tiles (k o E or q o E against k o F),
+// Q S and K S, the substitution, M Delta and the state update
+// (k o 2^{G_n - G})^T Delta.  Every fp32 factor there enters as a bf16 pair
+// hi = bf16(x), lo = bf16(x - hi), and a product of two split factors is the
+// three MFMAs hi*hi + hi*lo + lo*hi (the lo*lo term is below 2^-16 of the
+// product).  The operand planes are kept as bf16 hi and lo planes in the
+// pcol column order, so a state fragment pair or a Gram operand is one
+// 16-byte read.
 //
 // LDS: the k o E and q o E planes (hi, lo); the k o F planes share their
-// rows with the log-decays: until the operands are formed, the same bytes
-// hold G as fp32 (D + 8 floats a row), and each row is formed by the one
-// wave that read it, G first.
+// rows with the decays: until the operands are formed, the same bytes hold
+// the rates, then E (or G on the exact path) as fp32 (D + 8 floats a row),
+// and each row is formed by the one wave that read it, E first.
 // Gram jobs of the bf16 kernel with NW waves (the first four own the state
 // columns).  The K K^T diagonal blocks and their inverses go to one wave
 // (kda_diag_wave); the off-diagonal block pairs of (1,0) (2,0) (2,1) (3,0)
@@ -626,7 +629,6 @@ struct KdaBfSmem {
   alignas(16) float kk[C];
   alignas(16) float et[C];
   alignas(16) float beta[C];
-  alignas(16) float ref[4][D];
   alignas(16) float Z[4][D];
   alignas(16) float W[4][D];
   alignas(16) float P[6][D];
@@ -757,8 +759,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
     }
   };
   // registers -> LDS: raw K and Q (bf16, pcol order) in the hi planes, V as
-  // fp32, log2 of the rates as G's input (0 past the end: rate 1), |k|^2,
-  // eta
+  // fp32, the rates (1 past the end), |k|^2, eta
   auto stage = [&](int64_t t0) {
     const int tid = fresh_lane(threadIdx.x), l = tid & 63;
     const int64_t n = (eos - t0) < C ? (eos - t0) : C;
@@ -794,10 +795,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
       const int sg = u * KT + tid, r = sg / SEG_AROW, cs = sg % SEG_AROW;
       const bool in = r < n;
       f32x4 g;
-      g[0] = in ? flog2_rate(__uint_as_float(areg[u].x)) : 0.f;
-      g[1] = in ? flog2_rate(__uint_as_float(areg[u].y)) : 0.f;
-      g[2] = in ? flog2_rate(__uint_as_float(areg[u].z)) : 0.f;
-      g[3] = in ? flog2_rate(__uint_as_float(areg[u].w)) : 0.f;
+      g[0] = in ? __uint_as_float(areg[u].x) : 1.f;
+      g[1] = in ? __uint_as_float(areg[u].y) : 1.f;
+      g[2] = in ? __uint_as_float(areg[u].z) : 1.f;
+      g[3] = in ? __uint_as_float(areg[u].w) : 1.f;
       st4(&Gp[r * LDG + 4 * cs], g);
     }
     if (w == 0) sm.et[l] = ereg;
@@ -815,90 +816,72 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
     lds_barrier();  // chunk tok0 is staged
     fetch(tok0 + C);
 
-    // ---- scan: G per channel, block references and factor vectors ----------
-    // TPC adjacent lanes share a channel, each with 64 / TPC consecutive
-    // tokens: a running sum in registers, then the parts' totals by DPP
-    // (every lane forms the same prefix of them, in part order).
+    // ---- scan: decay products per channel, block totals, factor vectors -----
+    // Four adjacent lanes share a channel, lane `part` with 16-token block
+    // `part`: E_t = the product of the block's rates up to t (= 2^{G_t -
+    // ref_b}), a running product in registers; the blocks' totals T_b by
+    // DPP, and from them every factor vector as a product of totals (no
+    // logarithms or exponentials on the fast path).  A block with T_b below
+    // 2^-100 sends the chunk down the exact path, which takes the log-decays
+    // G from the raw rates, still in this lane's registers.
+    static_assert(KT / D == 4, "one 16-token block of one channel per lane");
+    const int sch = tid >> 2, spart = tid & 3;
+    float xr[16];
     {
-      constexpr int TPC = KT / D;  // 4 (D = 128 with 8 waves, D = 64 with 4)
-      constexpr int BPT = 4 / TPC;       // 16-token blocks per lane
-      constexpr int NT = 16 * BPT;
-      static_assert(TPC == 2 || TPC == 4, "lanes per channel");
-      const int ch = tid / TPC, part = tid % TPC;
-      float x[NT];
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) x[tt] = Gp[(NT * part + tt) * LDG + ch];
-      float run = 0.f;
+      for (int tt = 0; tt < 16; ++tt) xr[tt] = Gp[(16 * spart + tt) * LDG + sch];
+      float e[16], run = 1.f;
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        run += x[tt];
-        x[tt] = run;
+      for (int tt = 0; tt < 16; ++tt) {
+        run *= xr[tt];
+        e[tt] = run;
       }
-      // totals of the parts, T[p]; the own blocks' inner references
-      float T[TPC], inner = BPT == 2 ? x[15] : 0.f, in2[TPC];
-      if constexpr (TPC == 2) {
-        const float o = dpp<kQuadXor1>(run), oi = dpp<kQuadXor1>(inner);
-        T[0] = part ? o : run;
-        T[1] = part ? run : o;
-        in2[0] = part ? oi : inner;
-        in2[1] = part ? inner : oi;
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt) Gp[(16 * spart + tt) * LDG + sch] = e[tt];
+      const float T0 = dpp<0x00>(run), T1 = dpp<0x55>(run), T2 = dpp<0xAA>(run),
+                  T3 = dpp<0xFF>(run);
+      if (T0 < 0x1p-100f || T1 < 0x1p-100f || T2 < 0x1p-100f || T3 < 0x1p-100f) sm.deep = 1;
+      const float T01 = T0 * T1, T12 = T1 * T2, T23 = T2 * T3;
+      if (spart == 0) {  // Z_b = 2^{ref_b}
+        sm.Z[0][sch] = 1.f;
+        sm.Z[1][sch] = T0;
+        sm.Z[2][sch] = T01;
+        sm.Z[3][sch] = T01 * T2;
+      } else if (spart == 1) {  // W_b = 2^{G_n - ref_b}, 2^{G_n}
+        sm.W[3][sch] = T3;
+        sm.W[2][sch] = T23;
+        sm.W[1][sch] = T1 * T23;
+        sm.W[0][sch] = T01 * T23;
+        sm.Zn[sch] = T01 * T23;
+      } else if (spart == 2) {  // P_bc = 2^{ref_b - ref_c}, index b(b-1)/2 + c
+        sm.P[0][sch] = T0;
+        sm.P[1][sch] = T01;
+        sm.P[2][sch] = T1;
       } else {
-        T[0] = dpp<0x00>(run);
-        T[1] = dpp<0x55>(run);
-        T[2] = dpp<0xAA>(run);
-        T[3] = dpp<0xFF>(run);
-      }
-      float off[TPC];  // G before each part
-      off[0] = 0.f;
-#pragma unroll
-      for (int pp = 1; pp < TPC; ++pp) off[pp] = off[pp - 1] + T[pp - 1];
-      const float g = off[TPC - 1] + T[TPC - 1];  // G_n
-      float mine = 0.f;
-#pragma unroll
-      for (int pp = 0; pp < TPC; ++pp) mine = part == pp ? off[pp] : mine;
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) Gp[(NT * part + tt) * LDG + ch] = mine + x[tt];
-      // G just before each 16-token block
-      float rf[4];
-      if constexpr (TPC == 2) {
-        rf[0] = 0.f;
-        rf[1] = in2[0];
-        rf[2] = off[1];
-        rf[3] = off[1] + in2[1];
-      } else {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) rf[b] = off[b];
-      }
-      // a block whose rates multiply below 2^-100 in this channel sends the
-      // chunk down the exact path
-      bool deep = false;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) deep |= rf[b] - (b < 3 ? rf[b + 1] : g) > 100.f;
-      if (deep) sm.deep = 1;
-      // the factor vectors, shared out over the channel's lanes
-      if (part == 0) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) sm.ref[b][ch] = rf[b];
-        sm.Gn[ch] = g;
-      }
-      if (part == (TPC == 2 ? 0 : 1)) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) sm.Z[b][ch] = fexp2(rf[b]);
-      }
-      if (part == (TPC == 2 ? 1 : 2)) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) sm.W[b][ch] = fexp2(g - rf[b]);
-        sm.Zn[ch] = fexp2(g);
-      }
-      if (part == TPC - 1) {
-#pragma unroll
-        for (int b = 1; b < 4; ++b)
-#pragma unroll
-          for (int c = 0; c < b; ++c) sm.P[b * (b - 1) / 2 + c][ch] = fexp2(rf[b] - rf[c]);
+        sm.P[3][sch] = T01 * T2;
+        sm.P[4][sch] = T12;
+        sm.P[5][sch] = T2;
       }
     }
     lds_barrier();
     const bool deep = __builtin_amdgcn_readfirstlane(sm.deep) != 0;
+    if (deep) {
+      // G_t = log2 of the product of the chunk's rates up to t (rates below
+      // 2^-126 taken as 2^-126, so every log is finite), and G_n
+      float run = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt) {
+        run += flog2_rate(xr[tt]);
+        xr[tt] = run;
+      }
+      const float T0 = dpp<0x00>(run), T1 = dpp<0x55>(run), T2 = dpp<0xAA>(run),
+                  T3 = dpp<0xFF>(run);
+      const float off = spart == 0 ? 0.f : spart == 1 ? T0 : spart == 2 ? T0 + T1 : (T0 + T1) + T2;
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt) Gp[(16 * spart + tt) * LDG + sch] = off + xr[tt];
+      if (spart == 0) sm.Gn[sch] = ((T0 + T1) + T2) + T3;
+      lds_barrier();
+    }
 
     // ---- form k o E, k o F, q o E as hi/lo planes --------------------------
     // (exact path: k o 2^G, q o 2^G and k o 2^{G_n - G}, with Z = W = 1).
@@ -908,8 +891,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
       const int c4 = 4 * (tid % Q4);
 #pragma unroll
       for (int r = tid / Q4; r < C; r += RPP) {
-        const f32x4 G = ld4(&Gp[r * LDG + c4]);
-        const f32x4 rf = ld4(&sm.ref[r >> 4][c4]);
+        const f32x4 G = ld4(&Gp[r * LDG + c4]);  // E (fast path) or G (exact path)
         const f32x4 gn = ld4(&sm.Gn[c4]);
         const f32x4 kx = to_f32x4(*reinterpret_cast<const bf16x4 *>(&KEh[r * LDB + pcol(c4)]));
         const f32x4 qx = to_f32x4(*reinterpret_cast<const bf16x4 *>(&QEh[r * LDB + pcol(c4)]));
@@ -917,8 +899,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
         f32x4 ke, kf, qe;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float Ev = exact ? fexp2(G[e]) : fexp2(G[e] - rf[e]);
-          const float Fv = exact ? fexp2(fminf(gn[e] - G[e], 0.f)) : fexp2(rf[e] - G[e]);
+          const float Ev = exact ? fexp2(G[e]) : G[e];
+          const float Fv = exact ? fexp2(fminf(gn[e] - G[e], 0.f)) : __builtin_amdgcn_rcpf(G[e]);
           ke[e] = kx[e] * Ev;
           kf[e] = kx[e] * Fv;
           qe[e] = qx[e] * Ev;
