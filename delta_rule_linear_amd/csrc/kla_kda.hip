@@ -635,6 +635,7 @@ struct KdaBfSmem {
   alignas(16) float Zn[D];
   alignas(16) float Gn[D];
   int deep;
+  int mode;  // 0: the chunk's decays are staged; 1: deep; 2: not scanned
 };
 
 __device__ inline f32x4 to_f32x4(bf16x4 x) {
@@ -671,6 +672,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
   // others (NW = 8) share only the chunk-wide phases: staging, scan, operand
   // forming, the Gram tiles and their planes
   constexpr int KT = 64 * NW, NCW = 4, DIAGW = kda_diag_wave<NW>();
+  // with helper waves, they scan the next chunk's rates during the
+  // substitution (from registers), and its decays are staged with it
+  constexpr bool AHEAD = NW != NCW;
   static_assert(16 * NCW == DVB, "column waves");
   constexpr int NB = D / DVB;
   constexpr int NST = D / 16;
@@ -694,6 +698,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
   bf16 *const KEh = sm.KE, *const KEl = sm.KE + C * LDB;
   bf16 *const QEh = sm.QE, *const QEl = sm.QE + C * LDB;
   float *const Gp = reinterpret_cast<float *>(sm.KF);
+  // E (the fast path's in-block decays) as fp32 in the lo planes of k o E
+  // (channels 0 .. D/2-1) and q o E (the others), row r in their row r; the
+  // lo planes are free from the Gram phase's last read to the next forming
+  auto eptr = [&](int r, int c) __attribute__((always_inline)) {
+    return reinterpret_cast<float *>(c < D / 2 ? KEl : QEl) + r * (LDB / 2) + (c & (D / 2 - 1));
+  };
+  static_assert(2 * D <= LDB * 2 * 2 && (LDB / 2) % 4 == 0, "E rows in the lo planes");
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -758,8 +769,24 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
       areg[u] = buf_ld16(ra, (uint32_t)((r * H + h) * D + 4 * cs) * 4);
     }
   };
+  // registers -> LDS: the rates (1 past the end)
+  auto stage_rates = [&](int64_t t0) {
+    const int tid = fresh_lane(threadIdx.x);
+    const int64_t n = (eos - t0) < C ? (eos - t0) : C;
+#pragma unroll
+    for (int u = 0; u < NASEG; ++u) {
+      const int sg = u * KT + tid, r = sg / SEG_AROW, cs = sg % SEG_AROW;
+      const bool in = r < n;
+      f32x4 g;
+      g[0] = in ? __uint_as_float(areg[u].x) : 1.f;
+      g[1] = in ? __uint_as_float(areg[u].y) : 1.f;
+      g[2] = in ? __uint_as_float(areg[u].z) : 1.f;
+      g[3] = in ? __uint_as_float(areg[u].w) : 1.f;
+      st4(&Gp[r * LDG + 4 * cs], g);
+    }
+  };
   // registers -> LDS: raw K and Q (bf16, pcol order) in the hi planes, V as
-  // fp32, the rates (1 past the end), |k|^2, eta
+  // fp32, the rates (without helper waves), |k|^2, eta
   auto stage = [&](int64_t t0) {
     const int tid = fresh_lane(threadIdx.x), l = tid & 63;
     const int64_t n = (eos - t0) < C ? (eos - t0) : C;
@@ -790,31 +817,33 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
       st4(&sm.Vs[r * LDV + cs * SEG_EL + 4], f32x4{static_cast<float>(vb[4]), static_cast<float>(vb[5]),
                                                    static_cast<float>(vb[6]), static_cast<float>(vb[7])});
     }
-#pragma unroll
-    for (int u = 0; u < NASEG; ++u) {
-      const int sg = u * KT + tid, r = sg / SEG_AROW, cs = sg % SEG_AROW;
-      const bool in = r < n;
-      f32x4 g;
-      g[0] = in ? __uint_as_float(areg[u].x) : 1.f;
-      g[1] = in ? __uint_as_float(areg[u].y) : 1.f;
-      g[2] = in ? __uint_as_float(areg[u].z) : 1.f;
-      g[3] = in ? __uint_as_float(areg[u].w) : 1.f;
-      st4(&Gp[r * LDG + 4 * cs], g);
-    }
+    if constexpr (!AHEAD) stage_rates(t0);
     if (w == 0) sm.et[l] = ereg;
     if (tid == 0) sm.deep = 0;
   };
 
   fetch(bos);
-  fetch_a(bos);
+  if constexpr (!AHEAD) fetch_a(bos);
   stage(bos);
+  if (tid == 0) sm.mode = 2;
   for (int64_t tok0 = bos; tok0 < eos; tok0 += C) {
     // lane indices (and the addresses from them) recomputed in every chunk
     const int tid = fresh_lane(threadIdx.x), l = tid & 63, j = l >> 4, c16 = l & 15;
     const int col = nb * DVB + 16 * w + c16;
     const int n = (int)((eos - tok0) < C ? (eos - tok0) : C);
     lds_barrier();  // chunk tok0 is staged
+    const int mode = AHEAD ? __builtin_amdgcn_readfirstlane(sm.mode) : 2;
     fetch(tok0 + C);
+    bool deep = false;
+    if (mode != 0) {
+    if constexpr (AHEAD) {
+      // the decays were not staged (first chunk) or the chunk is deep:
+      // the rates from memory, then the scan below
+      fetch_a(tok0);
+      stage_rates(tok0);
+      if (tid == 0) sm.deep = 0;
+      lds_barrier();
+    }
 
     // ---- scan: decay products per channel, block totals, factor vectors -----
     // Four adjacent lanes share a channel, lane `part` with 16-token block
@@ -837,7 +866,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
         e[tt] = run;
       }
 #pragma unroll
-      for (int tt = 0; tt < 16; ++tt) Gp[(16 * spart + tt) * LDG + sch] = e[tt];
+      for (int tt = 0; tt < 16; ++tt) *eptr(16 * spart + tt, sch) = e[tt];
       const float T0 = dpp<0x00>(run), T1 = dpp<0x55>(run), T2 = dpp<0xAA>(run),
                   T3 = dpp<0xFF>(run);
       if (T0 < 0x1p-100f || T1 < 0x1p-100f || T2 < 0x1p-100f || T3 < 0x1p-100f) sm.deep = 1;
@@ -864,7 +893,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
       }
     }
     lds_barrier();
-    const bool deep = __builtin_amdgcn_readfirstlane(sm.deep) != 0;
+    deep = __builtin_amdgcn_readfirstlane(sm.deep) != 0;
     if (deep) {
       // G_t = log2 of the product of the chunk's rates up to t (rates below
       // 2^-126 taken as 2^-126, so every log is finite), and G_n
@@ -882,6 +911,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
       if (spart == 0) sm.Gn[sch] = ((T0 + T1) + T2) + T3;
       lds_barrier();
     }
+    }  // mode != 0
 
     // ---- form k o E, k o F, q o E as hi/lo planes --------------------------
     // (exact path: k o 2^G, q o 2^G and k o 2^{G_n - G}, with Z = W = 1).
@@ -891,7 +921,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
       const int c4 = 4 * (tid % Q4);
 #pragma unroll
       for (int r = tid / Q4; r < C; r += RPP) {
-        const f32x4 G = ld4(&Gp[r * LDG + c4]);  // E (fast path) or G (exact path)
+        const f32x4 G = exact ? ld4(&Gp[r * LDG + c4]) : ld4(eptr(r, c4));  // G or E
         const f32x4 gn = ld4(&sm.Gn[c4]);
         const f32x4 kx = to_f32x4(*reinterpret_cast<const bf16x4 *>(&KEh[r * LDB + pcol(c4)]));
         const f32x4 qx = to_f32x4(*reinterpret_cast<const bf16x4 *>(&QEh[r * LDB + pcol(c4)]));
@@ -1126,7 +1156,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
       for (int i = 0; i < 4; ++i) R[bi][i] = sm.Vs[(16 * bi + 4 * j + i) * LDV + 16 * w + c16] - ak[i];
     }
     lds_barrier();  // every read of k o E and q o E is done
-    fetch_a(tok0 + C);
+    if constexpr (AHEAD) {
+      if (tid == 64 * NCW) sm.mode = 0;
+    } else {
+      fetch_a(tok0 + C);
+    }
 
     // ---- planes over the operand space; k o F -> k o 2^{G_n - G} ------------
     // -Ahat blocks (b, m), m < b, transposed (row 16b + c16 of a lane holds
@@ -1166,7 +1200,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
       // 4-column group of one row of one plane per thread
       const int zr = (tid >> 3) & 15, zg = tid & 3, zs = (tid >> 2) & 1, zp = (tid >> 7) & 1;
       const int row = zs ? 32 + zr : zr, c = (zs ? 48 : 16) + 4 * zg;
-      if (tid < 256) *reinterpret_cast<bf16x4 *>(&(zp ? Ml : Mh)[row * LDP + pcol(c)]) = bf16x4{};
+      if (tid < 256) {
+        uint32_t z;  // made here, not kept in a register over the loop
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+        *reinterpret_cast<uint2 *>(&(zp ? Ml : Mh)[row * LDP + pcol(c)]) = uint2{z, z};
+      }
     }
     // k o F -> k o F' over all rows: here with four waves; with helper
     // waves, by them during the substitution (before the state update).
@@ -1196,12 +1234,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
     if constexpr (NW == NCW) rescale_kf(tid);
     lds_barrier();
 
-    if constexpr (NW != NCW) {
-      if (w >= NCW) {
-        rescale_kf(tid - 64 * NCW);
-        lds_barrier();  // k o F' is formed
-      }
-    }
     if (w < NCW) {
     // ---- Delta by block substitution, output ---------------------------------
     // Delta_b = Y_bb (R_b - sum_{m<b} Ahat_bm Delta_m) on the 16-deep bf16 MFMA,
@@ -1275,6 +1307,58 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
         kt.hi = __builtin_shufflevector(ld_tr(base + r0), ld_tr(base + r1), 0, 1, 2, 3, 4, 5, 6, 7);
         kt.lo = __builtin_shufflevector(ld_tr(base + LO + r0), ld_tr(base + LO + r1), 0, 1, 2, 3, 4, 5, 6, 7);
         S[t] = mma3(kt, Df[kk], S[t]);
+      }
+    } else if constexpr (AHEAD) {
+      // the next chunk's rates: lane pair (2c, 2c + 1) holds tokens 0-31 and
+      // 32-63 of channel c (1 past the end)
+      const int hl = tid - 64 * NCW, ach = hl >> 1, apart = hl & 1;
+      const int64_t t1 = tok0 + C;
+      const int n1 = (int)((eos - t1) < C ? (eos - t1) : C);
+      float ra[32];
+      {
+        const rsrc_t rr = make_rsrc(alpha + t1 * H * (int64_t)D, (int64_t)n1 * H * D * 4);
+#pragma unroll
+        for (int tt = 0; tt < 32; ++tt)
+          ra[tt] = buf_ld4(rr, (uint32_t)(((32 * apart + tt) * H + h) * D + ach) * 4);
+      }
+      rescale_kf(tid - 64 * NCW);
+      lds_barrier();  // k o F' is formed
+      // the next chunk's scan (the products of the fast path): E and the
+      // factor vectors go to LDS now (this chunk's are read before the
+      // barrier above, and the lo planes are free)
+      float r0 = 1.f, r1 = 1.f;
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt) {
+        r0 *= 32 * apart + tt < n1 ? ra[tt] : 1.f;
+        *eptr(32 * apart + tt, ach) = r0;
+      }
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt) {
+        r1 *= 32 * apart + 16 + tt < n1 ? ra[16 + tt] : 1.f;
+        *eptr(32 * apart + 16 + tt, ach) = r1;
+      }
+      const float o0 = dpp<kQuadXor1>(r0), o1 = dpp<kQuadXor1>(r1);
+      const float T0 = apart ? o0 : r0, T1 = apart ? o1 : r1, T2 = apart ? r0 : o0,
+                  T3 = apart ? r1 : o1;
+      if (T0 < 0x1p-100f || T1 < 0x1p-100f || T2 < 0x1p-100f || T3 < 0x1p-100f) sm.mode = 1;
+      const float T01 = T0 * T1, T12 = T1 * T2, T23 = T2 * T3;
+      if (apart == 0) {
+        sm.Z[0][ach] = 1.f;
+        sm.Z[1][ach] = T0;
+        sm.Z[2][ach] = T01;
+        sm.Z[3][ach] = T01 * T2;
+        sm.W[3][ach] = T3;
+        sm.W[2][ach] = T23;
+        sm.W[1][ach] = T1 * T23;
+        sm.W[0][ach] = T01 * T23;
+      } else {
+        sm.Zn[ach] = T01 * T23;
+        sm.P[0][ach] = T0;
+        sm.P[1][ach] = T01;
+        sm.P[2][ach] = T1;
+        sm.P[3][ach] = T01 * T2;
+        sm.P[4][ach] = T12;
+        sm.P[5][ach] = T2;
       }
     }
     lds_barrier();  // everyone is done with this chunk's LDS
