@@ -545,29 +545,34 @@ __global__ __launch_bounds__(kThreads) void prefill_kda_kernel(
 }
 
 // ---- bf16 inputs: the contractions on the bf16 MFMA ------------------------
-// The same chunk form, exact path and substitution as above.  The fast path
-// takes its decay factors as products of the rates instead of exponentials
-// of summed log-rates (the same quantities: E_t = 2^{G_t - ref_b} is the
-// product of block b's rates up to t, F_t = 1 / E_t, and every factor vector
-// a product of block totals).  The contractions run on
-// v_mfma_f32_16x16x32_bf16: the Gram tiles (k o E or q o E against k o F),
-// Q S and K S, the substitution, M Delta and the state update
-// (k o 2^{G_n - G})^T Delta.  Every fp32 factor there enters as a bf16 pair
+// The same chunk form, exact path and substitution as above, with the fast
+// path's decays referenced per channel to the chunk's midpoint decay
+// r = G_n / 2 instead of per 16-token block: E'_t = 2^{G_t - r} and
+// F'_s = 2^{r - G_s} = 1 / E'_s, so every Gram tile is a plain product
+// (k o E' or q o E' against k o F'), Q S and K S take the state scaled by
+// 2^r (split once for all row blocks), and the state update is
+// S' = 2^r o (2^r o S + (k o F')^T Delta), with no rescaled copy of k o F.
+// E' and F' stay within 2^{+-100} when the chunk's decay in every channel is
+// at least 2^-200; a chunk below that, or with a 16-token block below
+// 2^-100, takes the exact path.  E'_t is the running product of the rates
+// in t's block times 2^{ref_b - r} (block totals in log2).  The contractions
+// run on v_mfma_f32_16x16x32_bf16: the Gram tiles, Q S and K S, the
+// substitution, M Delta and the state update.  Every fp32 factor there enters as a bf16 pair
 // hi = bf16(x), lo = bf16(x - hi), and a product of two split factors is the
 // three MFMAs hi*hi + hi*lo + lo*hi (the lo*lo term is below 2^-16 of the
 // product).  The operand planes are kept as bf16 hi and lo planes in the
 // pcol column order, so a state fragment pair or a Gram operand is one
 // 16-byte read.
 //
-// LDS: the k o E and q o E planes (hi, lo); the k o F planes share their
-// rows with the decays: until the operands are formed, the same bytes hold
-// the rates, then E (or G on the exact path) as fp32 (D + 8 floats a row),
-// and each row is formed by the one wave that read it, E first.
+// LDS: the k o E' and q o E' planes (hi, lo); the k o F' planes share their
+// rows with the raw rates and the exact path's log-decays G (D + 8 floats a
+// row); E' waits as fp32 in the lo planes, each row in that row's bytes, so
+// each row is formed by the one wave that read it, E' first.
 // Gram jobs of the bf16 kernel with NW waves (the first four own the state
 // columns).  The K K^T diagonal blocks and their inverses go to one wave
 // (kda_diag_wave); the off-diagonal block pairs of (1,0) (2,0) (2,1) (3,0)
 // (3,1) (3,2), each as its K K^T tile (-Ahat, u even) and its Q K^T tile (M,
-// u odd), which share the P-scaled k o F operand, and then the diagonal M
+// u odd), which share the k o F' operand, and then the diagonal M
 // blocks go to the others:
 //   NW = 4: wave 0 the diagonal blocks; waves 1-3 two pairs each
 //           (2(w-1), 2(w-1)+1); diagonal M blocks: wave 1 blocks 0 and 1,
@@ -619,6 +624,9 @@ struct KdaBfSmem {
   static constexpr int LDYT = 24;         // Y^T rows (bf16 hi, lo)
   static_assert(2 * 6 * 16 * LDA <= 2 * C * LDB && 2 * C * LDP <= 2 * C * LDB,
                 "planes must fit in the operand space");
+  // the M lo plane after the -Ahat planes in the k o E hi plane where it
+  // fits (d = 128), so both lo planes are free during the substitution
+  static constexpr bool ML_IN_KE = 2 * 6 * 16 * LDA + C * LDP <= C * LDB;
   alignas(16) bf16 KE[2 * C * LDB];  // hi plane then lo plane; raw k in the hi plane until formed; -Ahat planes after the Gram phase
   alignas(16) bf16 QE[2 * C * LDB];  // the same for q; M planes after the Gram phase
   alignas(16) bf16 KF[C * LDR];
@@ -629,10 +637,11 @@ struct KdaBfSmem {
   alignas(16) float kk[C];
   alignas(16) float et[C];
   alignas(16) float beta[C];
-  alignas(16) float Z[4][D];
-  alignas(16) float W[4][D];
-  alignas(16) float P[6][D];
-  alignas(16) float Zn[D];
+  // per channel, by chunk parity: the B-side scale of Q S and K S and the
+  // update's post-scale 2^{G_n / 2} (1 on the exact path), and the state's
+  // pre-scale 2^{G_n / 2} (2^{G_n} on the exact path)
+  alignas(16) float Zr[2][D];
+  alignas(16) float Yp[2][D];
   alignas(16) float Gn[D];
   int deep;
   int mode;  // 0: the chunk's decays are staged; 1: deep; 2: not scanned
@@ -675,6 +684,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
   // with helper waves, they scan the next chunk's rates during the
   // substitution (from registers), and its decays are staged with it
   constexpr bool AHEAD = NW != NCW;
+  static_assert(!AHEAD || SM::ML_IN_KE, "the lo planes must be free during the substitution");
   static_assert(16 * NCW == DVB, "column waves");
   constexpr int NB = D / DVB;
   constexpr int NST = D / 16;
@@ -833,6 +843,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
     const int n = (int)((eos - tok0) < C ? (eos - tok0) : C);
     lds_barrier();  // chunk tok0 is staged
     const int mode = AHEAD ? __builtin_amdgcn_readfirstlane(sm.mode) : 2;
+    const int cur = (int)(((tok0 - bos) / C) & 1);  // factor slot of this chunk
     fetch(tok0 + C);
     bool deep = false;
     if (mode != 0) {
@@ -845,14 +856,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
       lds_barrier();
     }
 
-    // ---- scan: decay products per channel, block totals, factor vectors -----
+    // ---- scan: decays per channel, E' and the scales ------------------------
     // Four adjacent lanes share a channel, lane `part` with 16-token block
-    // `part`: E_t = the product of the block's rates up to t (= 2^{G_t -
-    // ref_b}), a running product in registers; the blocks' totals T_b by
-    // DPP, and from them every factor vector as a product of totals (no
-    // logarithms or exponentials on the fast path).  A block with T_b below
-    // 2^-100 sends the chunk down the exact path, which takes the log-decays
-    // G from the raw rates, still in this lane's registers.
+    // `part`: the running product of the block's rates in registers, the
+    // blocks' totals in log2 by DPP, then E' = product * 2^{ref_b - r}.  A
+    // block below 2^-100 or a chunk below 2^-200 sends the chunk down the
+    // exact path, which takes the log-decays G from the raw rates, still in
+    // this lane's registers.
     static_assert(KT / D == 4, "one 16-token block of one channel per lane");
     const int sch = tid >> 2, spart = tid & 3;
     float xr[16];
@@ -865,31 +875,23 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
         run *= xr[tt];
         e[tt] = run;
       }
-#pragma unroll
-      for (int tt = 0; tt < 16; ++tt) *eptr(16 * spart + tt, sch) = e[tt];
+      // block totals in log2, the references ref_b (G before block b) and
+      // the midpoint r = G_n / 2
+      const float lt = __builtin_amdgcn_logf(run);
+      const float L0 = dpp<0x00>(lt), L1 = dpp<0x55>(lt), L2 = dpp<0xAA>(lt), L3 = dpp<0xFF>(lt);
+      const float ref = spart == 0 ? 0.f : spart == 1 ? L0 : spart == 2 ? L0 + L1 : (L0 + L1) + L2;
+      const float gn = ((L0 + L1) + L2) + L3, rm = 0.5f * gn;
       const float T0 = dpp<0x00>(run), T1 = dpp<0x55>(run), T2 = dpp<0xAA>(run),
                   T3 = dpp<0xFF>(run);
-      if (T0 < 0x1p-100f || T1 < 0x1p-100f || T2 < 0x1p-100f || T3 < 0x1p-100f) sm.deep = 1;
-      const float T01 = T0 * T1, T12 = T1 * T2, T23 = T2 * T3;
-      if (spart == 0) {  // Z_b = 2^{ref_b}
-        sm.Z[0][sch] = 1.f;
-        sm.Z[1][sch] = T0;
-        sm.Z[2][sch] = T01;
-        sm.Z[3][sch] = T01 * T2;
-      } else if (spart == 1) {  // W_b = 2^{G_n - ref_b}, 2^{G_n}
-        sm.W[3][sch] = T3;
-        sm.W[2][sch] = T23;
-        sm.W[1][sch] = T1 * T23;
-        sm.W[0][sch] = T01 * T23;
-        sm.Zn[sch] = T01 * T23;
-      } else if (spart == 2) {  // P_bc = 2^{ref_b - ref_c}, index b(b-1)/2 + c
-        sm.P[0][sch] = T0;
-        sm.P[1][sch] = T01;
-        sm.P[2][sch] = T1;
-      } else {
-        sm.P[3][sch] = T01 * T2;
-        sm.P[4][sch] = T12;
-        sm.P[5][sch] = T2;
+      if (T0 < 0x1p-100f || T1 < 0x1p-100f || T2 < 0x1p-100f || T3 < 0x1p-100f || !(gn >= -200.f))
+        sm.deep = 1;
+      const float fac = fexp2(ref - rm);
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt) *eptr(16 * spart + tt, sch) = e[tt] * fac;
+      if (spart == 0) {
+        const float zr = fexp2(rm);
+        sm.Zr[cur][sch] = zr;
+        sm.Yp[cur][sch] = zr;
       }
     }
     lds_barrier();
@@ -913,10 +915,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
     }
     }  // mode != 0
 
-    // ---- form k o E, k o F, q o E as hi/lo planes --------------------------
-    // (exact path: k o 2^G, q o 2^G and k o 2^{G_n - G}, with Z = W = 1).
-    // The k o F row overwrites that row's G: every G of the row is read
-    // (by this wave) before any of the row is written.
+    // ---- form k o E', k o F', q o E' as hi/lo planes ------------------------
+    // (exact path: k o 2^G, q o 2^G and k o 2^{G_n - G}, with the state
+    // scales set to match).  A row's E' (or G) is read by this wave before
+    // any of the row is written.
     auto form = [&](bool exact) __attribute__((always_inline)) {
       const int c4 = 4 * (tid % Q4);
 #pragma unroll
@@ -971,12 +973,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
       }
       return acc;
     };
-    // Gram tile on the bf16 MFMA: rows 16bi.. of A (k o E or q o E), scaled
-    // per channel by P (off-diagonal pairs), against rows 16bj.. of k o F
+    // Gram tile on the bf16 MFMA: rows 16bi.. of A (k o E' or q o E') against
+    // rows 16bj.. of k o F' (E'_t F'_s = 2^{G_t - G_s} for any block pair)
     auto bf_tile = [&](bool qk, int bi, int bj, bool tr) __attribute__((always_inline)) {
       const bf16 *Ah = qk ? QEh : KEh, *Al = qk ? QEl : KEl;
-      const bool diag_pair = bi == bj;
-      const float *Pv = sm.P[diag_pair ? 0 : bi * (bi - 1) / 2 + bj];
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < D / 32; ++u) {
@@ -987,22 +987,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
         a.lo = *reinterpret_cast<const bf16x8 *>(&Al[ao]);
         b.hi = *reinterpret_cast<const bf16x8 *>(&sm.KF[bo]);
         b.lo = *reinterpret_cast<const bf16x8 *>(&sm.KF[bo + LO]);
-        if (!diag_pair) {
-          // this lane's eight channels: 32u + 4j.. and 32u + 16 + 4j..
-          const f32x4 p0 = ld4(&Pv[32 * u + 4 * j]), p1 = ld4(&Pv[32 * u + 16 + 4 * j]);
-          const f32x4 x0 = (to_f32x4(half_lo(a.hi)) + to_f32x4(half_lo(a.lo))) * p0;
-          const f32x4 x1 = (to_f32x4(half_hi(a.hi)) + to_f32x4(half_hi(a.lo))) * p1;
-          a = split8(x0, x1);
-        }
         acc = tr ? mma3(b, a, acc) : mma3(a, b, acc);
       }
       return acc;
     };
     // both transposed tiles of an off-diagonal pair (bi, bj): -Ahat from the
-    // k o E rows and M from the q o E rows against rows 16bj.. of k o F,
-    // which carry P_{bi,bj} (scaled once for both)
+    // k o E' rows and M from the q o E' rows against rows 16bj.. of k o F'
+    // (read once for both)
     auto bf_pair = [&](int bi, int bj, f32x4 &tk, f32x4 &tq) __attribute__((always_inline)) {
-      const float *Pv = sm.P[bi * (bi - 1) / 2 + bj];
       tk = f32x4{0.f, 0.f, 0.f, 0.f};
       tq = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1016,10 +1008,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
         qa.lo = *reinterpret_cast<const bf16x8 *>(&QEl[ao]);
         f.hi = *reinterpret_cast<const bf16x8 *>(&sm.KF[bo]);
         f.lo = *reinterpret_cast<const bf16x8 *>(&sm.KF[bo + LO]);
-        // this lane's eight channels: 32u + 4j.. and 32u + 16 + 4j..
-        const f32x4 p0 = ld4(&Pv[32 * u + 4 * j]), p1 = ld4(&Pv[32 * u + 16 + 4 * j]);
-        f = split8((to_f32x4(half_lo(f.hi)) + to_f32x4(half_lo(f.lo))) * p0,
-                   (to_f32x4(half_hi(f.hi)) + to_f32x4(half_hi(f.lo))) * p1);
         tk = mma3(f, ka, tk);
         tq = mma3(f, qa, tq);
       }
@@ -1121,54 +1109,51 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
     if (deep) {
       lds_barrier();  // every read of the raw inputs is done
       if (tid < D) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          sm.Z[b][tid] = 1.f;
-          sm.W[b][tid] = 1.f;
-        }
+        sm.Zr[cur][tid] = 1.f;
+        sm.Yp[cur][tid] = fexp2(sm.Gn[tid]);
       }
       form(true);
       lds_barrier();
     }
 
-    // Q S and K S with the state rows scaled by 2^{ref_bi}: (q o 2^G) S =
-    // (q o E) (Diag(2^{ref}) S); the scaled state, split, is the B operand
+    // Q S and K S: (q o 2^G) S = (q o E') (Diag(2^{G_n / 2}) S), the scaled
+    // state split once for every row block (the B operand)
     f32x4 QS[4], R[4];
+    if (w < NCW) {
+      Split8 Sf[NST / 2];
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
-      if (w >= NCW) break;
-      f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < NST / 2; ++kk)
+        Sf[kk] = split8(S[2 * kk] * ld4(&sm.Zr[cur][32 * kk + 4 * j]),
+                        S[2 * kk + 1] * ld4(&sm.Zr[cur][32 * kk + 16 + 4 * j]));
 #pragma unroll
-      for (int kk = 0; kk < NST / 2; ++kk) {
-        const Split8 Sf = split8(S[2 * kk] * ld4(&sm.Z[bi][32 * kk + 4 * j]),
-                                 S[2 * kk + 1] * ld4(&sm.Z[bi][32 * kk + 16 + 4 * j]));
-        const int ao = (16 * bi + c16) * LDB + 32 * kk + 8 * j;
-        Split8 qa, ka;
-        qa.hi = *reinterpret_cast<const bf16x8 *>(&QEh[ao]);
-        qa.lo = *reinterpret_cast<const bf16x8 *>(&QEl[ao]);
-        ka.hi = *reinterpret_cast<const bf16x8 *>(&KEh[ao]);
-        ka.lo = *reinterpret_cast<const bf16x8 *>(&KEl[ao]);
-        aq = mma3(qa, Sf, aq);
-        ak = mma3(ka, Sf, ak);
+      for (int bi = 0; bi < 4; ++bi) {
+        f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NST / 2; ++kk) {
+          const int ao = (16 * bi + c16) * LDB + 32 * kk + 8 * j;
+          Split8 qa, ka;
+          qa.hi = *reinterpret_cast<const bf16x8 *>(&QEh[ao]);
+          qa.lo = *reinterpret_cast<const bf16x8 *>(&QEl[ao]);
+          ka.hi = *reinterpret_cast<const bf16x8 *>(&KEh[ao]);
+          ka.lo = *reinterpret_cast<const bf16x8 *>(&KEl[ao]);
+          aq = mma3(qa, Sf[kk], aq);
+          ak = mma3(ka, Sf[kk], ak);
+        }
+        QS[bi] = aq;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) R[bi][i] = sm.Vs[(16 * bi + 4 * j + i) * LDV + 16 * w + c16] - ak[i];
       }
-      QS[bi] = aq;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) R[bi][i] = sm.Vs[(16 * bi + 4 * j + i) * LDV + 16 * w + c16] - ak[i];
     }
     lds_barrier();  // every read of k o E and q o E is done
-    if constexpr (AHEAD) {
-      if (tid == 64 * NCW) sm.mode = 0;
-    } else {
-      fetch_a(tok0 + C);
-    }
+    if constexpr (!AHEAD) fetch_a(tok0 + C);
 
-    // ---- planes over the operand space; k o F -> k o 2^{G_n - G} ------------
+    // ---- planes over the operand space ---------------------------------------
     // -Ahat blocks (b, m), m < b, transposed (row 16b + c16 of a lane holds
     // columns 4j..4j+3), index b(b-1)/2 + m; M in the pcol column order,
     // its two blocks above the diagonal that the 32-deep products read, (0, 1)
     // and (2, 3), set to zero
     bf16 *const Ah = sm.KE, *const Al = sm.KE + 6 * 16 * LDA;
-    bf16 *const Mh = sm.QE, *const Ml = sm.QE + C * LDP;
+    bf16 *const Mh = sm.QE, *const Ml = SM::ML_IN_KE ? sm.KE + 2 * 6 * 16 * LDA : sm.QE + C * LDP;
     if (w != DIAGW) {
       const int nj = kda_njobs<NW>(w);
 #pragma unroll
@@ -1206,32 +1191,21 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
         *reinterpret_cast<uint2 *>(&(zp ? Ml : Mh)[row * LDP + pcol(c)]) = uint2{z, z};
       }
     }
-    // k o F -> k o F' over all rows: here with four waves; with helper
-    // waves, by them during the substitution (before the state update).
-    // Every row is read before any is written.
-    auto rescale_kf = [&](int t0) __attribute__((always_inline)) {
-      constexpr int NTH = NW == NCW ? KT : KT - 64 * NCW, RS = NTH / Q4, NR = C / RS;
-      static_assert(NR * RS == C, "rescale tiling");
-      const int c4 = 4 * (t0 % Q4), r0 = t0 / Q4;
-      bf16x4 xh[NR], xl[NR];
-      f32x4 wv[NR];
+    // the next chunk's rates (helper waves): lane pair (2c, 2c + 1) holds
+    // tokens 0-31 and 32-63 of channel c
+    float ra[32];
+    if constexpr (AHEAD) {
+      if (w >= NCW) {
+        const int hl = tid - 64 * NCW, ach = hl >> 1, apart = hl & 1;
+        const int64_t t1 = tok0 + C;
+        const int64_t n1 = (eos - t1) < C ? (eos - t1) : C;
+        const rsrc_t rr = make_rsrc(alpha + t1 * H * (int64_t)D, n1 * (int64_t)H * D * 4);
 #pragma unroll
-      for (int u = 0; u < NR; ++u) {
-        const int r = r0 + u * RS;
-        xh[u] = *reinterpret_cast<const bf16x4 *>(&sm.KF[r * LDR + pcol(c4)]);
-        xl[u] = *reinterpret_cast<const bf16x4 *>(&sm.KF[r * LDR + LO + pcol(c4)]);
-        wv[u] = ld4(&sm.W[r >> 4][c4]);
+        for (int tt = 0; tt < 32; ++tt)
+          ra[tt] = buf_ld4(rr, (uint32_t)(((32 * apart + tt) * H + h) * D + ach) * 4);
+        if (hl == 0) sm.mode = 0;
       }
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int u = 0; u < NR; ++u) {
-        const int r = r0 + u * RS;
-        const Split4 sp = split4((to_f32x4(xh[u]) + to_f32x4(xl[u])) * wv[u]);
-        *reinterpret_cast<bf16x4 *>(&sm.KF[r * LDR + pcol(c4)]) = sp.hi;
-        *reinterpret_cast<bf16x4 *>(&sm.KF[r * LDR + LO + pcol(c4)]) = sp.lo;
-      }
-    };
-    if constexpr (NW == NCW) rescale_kf(tid);
+    }
     lds_barrier();
 
     if (w < NCW) {
@@ -1292,11 +1266,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
         for (int i = 0; i < 4; ++i)
           buf_st4(ro, (uint32_t)(((16 * bi + 4 * j + i) * H + h) * D + col) * 4, QS[bi][i]);
     }
-    // S' = Diag(2^{G_n}) S + (k o 2^{G_n - G})^T Delta: the A operand by
-    // transposing reads of the k o F' planes
+    // S' = Diag(2^{G_n}) S + (k o 2^{G_n - G})^T Delta = Diag(2^{G_n / 2})
+    // (Diag(2^{G_n / 2}) S + (k o F')^T Delta) (exact path: pre-scale 2^{G_n},
+    // post-scale 1, k o F' = k o 2^{G_n - G}); the A operand by transposing
+    // reads of the k o F' planes
 #pragma unroll
-    for (int t = 0; t < NST; ++t) S[t] *= ld4(&sm.Zn[16 * t + 4 * j]);
-    if constexpr (NW != NCW) lds_barrier();  // the helper waves' k o F'
+    for (int t = 0; t < NST; ++t) S[t] *= ld4(&sm.Yp[cur][16 * t + 4 * j]);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -1308,57 +1283,43 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
         kt.lo = __builtin_shufflevector(ld_tr(base + LO + r0), ld_tr(base + LO + r1), 0, 1, 2, 3, 4, 5, 6, 7);
         S[t] = mma3(kt, Df[kk], S[t]);
       }
+#pragma unroll
+    for (int t = 0; t < NST; ++t) S[t] *= ld4(&sm.Zr[cur][16 * t + 4 * j]);
     } else if constexpr (AHEAD) {
-      // the next chunk's rates: lane pair (2c, 2c + 1) holds tokens 0-31 and
-      // 32-63 of channel c (1 past the end)
+      // the next chunk's scan (fast path): in-block products, block totals in
+      // log2, E' = product * 2^{ref_b - G_n / 2} to the lo planes (free now),
+      // the scales into the other chunk slot
       const int hl = tid - 64 * NCW, ach = hl >> 1, apart = hl & 1;
       const int64_t t1 = tok0 + C;
       const int n1 = (int)((eos - t1) < C ? (eos - t1) : C);
-      float ra[32];
-      {
-        const rsrc_t rr = make_rsrc(alpha + t1 * H * (int64_t)D, (int64_t)n1 * H * D * 4);
-#pragma unroll
-        for (int tt = 0; tt < 32; ++tt)
-          ra[tt] = buf_ld4(rr, (uint32_t)(((32 * apart + tt) * H + h) * D + ach) * 4);
-      }
-      rescale_kf(tid - 64 * NCW);
-      lds_barrier();  // k o F' is formed
-      // the next chunk's scan (the products of the fast path): E and the
-      // factor vectors go to LDS now (this chunk's are read before the
-      // barrier above, and the lo planes are free)
-      float r0 = 1.f, r1 = 1.f;
+      float e[32], r0 = 1.f, r1 = 1.f;
 #pragma unroll
       for (int tt = 0; tt < 16; ++tt) {
         r0 *= 32 * apart + tt < n1 ? ra[tt] : 1.f;
-        *eptr(32 * apart + tt, ach) = r0;
+        e[tt] = r0;
       }
 #pragma unroll
       for (int tt = 0; tt < 16; ++tt) {
         r1 *= 32 * apart + 16 + tt < n1 ? ra[16 + tt] : 1.f;
-        *eptr(32 * apart + 16 + tt, ach) = r1;
+        e[16 + tt] = r1;
       }
-      const float o0 = dpp<kQuadXor1>(r0), o1 = dpp<kQuadXor1>(r1);
-      const float T0 = apart ? o0 : r0, T1 = apart ? o1 : r1, T2 = apart ? r0 : o0,
-                  T3 = apart ? r1 : o1;
-      if (T0 < 0x1p-100f || T1 < 0x1p-100f || T2 < 0x1p-100f || T3 < 0x1p-100f) sm.mode = 1;
-      const float T01 = T0 * T1, T12 = T1 * T2, T23 = T2 * T3;
+      const float l0 = __builtin_amdgcn_logf(r0), l1 = __builtin_amdgcn_logf(r1);
+      const float o0 = dpp<kQuadXor1>(l0), o1 = dpp<kQuadXor1>(l1);
+      const float L0 = apart ? o0 : l0, L1 = apart ? o1 : l1, L2 = apart ? l0 : o0, L3 = apart ? l1 : o1;
+      const float gn = ((L0 + L1) + L2) + L3, rm = 0.5f * gn;
+      const float q0 = dpp<kQuadXor1>(r0), q1 = dpp<kQuadXor1>(r1);
+      if (r0 < 0x1p-100f || r1 < 0x1p-100f || q0 < 0x1p-100f || q1 < 0x1p-100f || !(gn >= -200.f))
+        sm.mode = 1;
+      const float fa = fexp2((apart ? L0 + L1 : 0.f) - rm);
+      const float fb = fexp2((apart ? (L0 + L1) + L2 : L0) - rm);
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt) *eptr(32 * apart + tt, ach) = e[tt] * fa;
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt) *eptr(32 * apart + 16 + tt, ach) = e[16 + tt] * fb;
       if (apart == 0) {
-        sm.Z[0][ach] = 1.f;
-        sm.Z[1][ach] = T0;
-        sm.Z[2][ach] = T01;
-        sm.Z[3][ach] = T01 * T2;
-        sm.W[3][ach] = T3;
-        sm.W[2][ach] = T23;
-        sm.W[1][ach] = T1 * T23;
-        sm.W[0][ach] = T01 * T23;
-      } else {
-        sm.Zn[ach] = T01 * T23;
-        sm.P[0][ach] = T0;
-        sm.P[1][ach] = T01;
-        sm.P[2][ach] = T1;
-        sm.P[3][ach] = T01 * T2;
-        sm.P[4][ach] = T12;
-        sm.P[5][ach] = T2;
+        const float zr = fexp2(rm);
+        sm.Zr[cur ^ 1][ach] = zr;
+        sm.Yp[cur ^ 1][ach] = zr;
       }
     }
     lds_barrier();  // everyone is done with this chunk's LDS

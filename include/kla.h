@@ -283,7 +283,8 @@ kla_status kla_decode_step_ex(const void *q, const void *k, const void *v,
  *   alpha       [total_tok, H, dk] fp32, required, 16-byte aligned; every
  *               rate in (0, 1], however small.  (A chunk in which one
  *               channel's rates multiply below 2^-100 inside an aligned
- *               block of 16 tokens takes a slower exact path.)
+ *               block of 16 tokens, or, with bf16 inputs, below 2^-200 over
+ *               the chunk, takes a slower exact path.)
  * Other arguments and errors as kla_fwd_chunked_ex (whole sequences only; no
  * workspace is needed).  fp32 inputs run on the fp32 MFMA; bf16 inputs on
  * the bf16 MFMA, every fp32 factor entering as a hi/lo pair of bf16 values

@@ -82,7 +82,14 @@ def chunked(q, k, v, alpha, eta, cu_seqlens, eps, C, initial_state=None):
 #   Ahat_ts = sum_i (k_t E_t)[i] P_b(t)b(s)[i] (k_s F_s)[i].
 
 def chunked_ch_seq(q, k, v, alpha, eta, eps, C, S0, factored=False, blk=16):
-    """One (sequence, head): q,k [L,dk], v [L,dv], alpha [L,dk], eta [L]."""
+    """One (sequence, head): q,k [L,dk], v [L,dv], alpha [L,dk], eta [L].
+
+    factored: False for the direct exponent differences; True for factors
+    referenced per block of `blk` rows (E = 2^{G - ref_b}, F = 1/E, P per
+    block pair); "mid" for factors referenced per channel to the chunk's
+    midpoint decay r = G_n / 2 (E' = 2^{G - r}, F' = 1/E'), with Q S and K S
+    on the state scaled by 2^r and the update 2^r (2^r S + (K F')^T Delta),
+    the operands of the bf16-input kernel."""
     L = q.shape[0]
     S = np.array(S0, dtype=np.float64, copy=True)
     o = np.zeros((L, v.shape[1]))
@@ -92,6 +99,19 @@ def chunked_ch_seq(q, k, v, alpha, eta, eps, C, S0, factored=False, blk=16):
         n = K.shape[0]
         G = np.cumsum(np.log(alpha[sl]), axis=0)          # [n, dk]
         beta = eta[sl] / (np.sum(K * K, axis=1) + eps)
+        if factored == "mid":
+            r = 0.5 * G[-1]                                   # [dk]
+            E, F = np.exp(G - r), np.exp(r - G)
+            KE, KF, QE = K * E, K * F, Q * E
+            Ah = np.tril(KE @ KF.T, -1)
+            M = np.tril(QE @ KF.T)
+            Sr = np.exp(r)[:, None] * S
+            Lm = np.tril(beta[:, None] * Ah, -1)
+            R = V - KE @ Sr
+            Delta = solve_triangular(np.eye(n) + Lm, beta[:, None] * R, lower=True)
+            o[sl] = QE @ Sr + M @ Delta
+            S = np.exp(r)[:, None] * (Sr + KF.T @ Delta)
+            continue
         if factored:
             ref = np.zeros_like(G)
             for t in range(n):

@@ -505,9 +505,10 @@ def pin_channel_untouched_channel(fwd, decode):
 
 
 def pin_channel_chunk_form(fwd, decode):
-    """The chunk form with per-channel decay factors (direct, and factored
-    per block of 16 rows as the GPU kernel forms it) gives the sequential
-    result for every chunk size, ragged last chunks included."""
+    """The chunk form with per-channel decay factors (direct; factored per
+    block of 16 rows as the fp32-input GPU kernel forms it; and referenced to
+    the chunk's midpoint decay as the bf16-input kernel forms it) gives the
+    sequential result for every chunk size, ragged last chunks included."""
     rng = np.random.default_rng(36)
     H, dk, dv = 2, 6, 5
     cu = np.array([0, 1, 17, 80, 143])
@@ -517,7 +518,7 @@ def pin_channel_chunk_form(fwd, decode):
     S0 = rng.standard_normal((len(cu) - 1, H, dk, dv))
     o, S = fwd(q, k, v, a, eta, cu_seqlens=cu, eps=1e-3, initial_state=S0, channel_decay=True)
     for C in (1, 7, 16, 64):
-        for fac in (False, True):
+        for fac in (False, True, "mid"):
             oc, Sc = chunked_ch(q, k, v, a, eta, cu, 1e-3, C, S0, factored=fac)
             assert rel(o, oc) < 1e-10 and rel(S, Sc) < 1e-10, (C, fac, rel(o, oc), rel(S, Sc))
 
