@@ -1191,18 +1191,18 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
         *reinterpret_cast<uint2 *>(&(zp ? Ml : Mh)[row * LDP + pcol(c)]) = uint2{z, z};
       }
     }
-    // the next chunk's rates (helper waves): lane pair (2c, 2c + 1) holds
-    // tokens 0-31 and 32-63 of channel c
-    float ra[32];
+    // the next chunk's rates (helper waves): lane (quad cq, part p) holds
+    // channels 4cq..4cq+3 of tokens 8p..8p+7
+    uint4 ra[8];
     if constexpr (AHEAD) {
       if (w >= NCW) {
-        const int hl = tid - 64 * NCW, ach = hl >> 1, apart = hl & 1;
+        const int hl = tid - 64 * NCW, cq = hl >> 3, p8 = hl & 7;
         const int64_t t1 = tok0 + C;
         const int64_t n1 = (eos - t1) < C ? (eos - t1) : C;
         const rsrc_t rr = make_rsrc(alpha + t1 * H * (int64_t)D, n1 * (int64_t)H * D * 4);
 #pragma unroll
-        for (int tt = 0; tt < 32; ++tt)
-          ra[tt] = buf_ld4(rr, (uint32_t)(((32 * apart + tt) * H + h) * D + ach) * 4);
+        for (int tt = 0; tt < 8; ++tt)
+          ra[tt] = buf_ld16(rr, (uint32_t)(((8 * p8 + tt) * H + h) * D + 4 * cq) * 4);
         if (hl == 0) sm.mode = 0;
       }
     }
@@ -1286,40 +1286,60 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
 #pragma unroll
     for (int t = 0; t < NST; ++t) S[t] *= ld4(&sm.Zr[cur][16 * t + 4 * j]);
     } else if constexpr (AHEAD) {
-      // the next chunk's scan (fast path): in-block products, block totals in
-      // log2, E' = product * 2^{ref_b - G_n / 2} to the lo planes (free now),
-      // the scales into the other chunk slot
-      const int hl = tid - 64 * NCW, ach = hl >> 1, apart = hl & 1;
+      // the next chunk's scan (fast path): running products over each lane's
+      // eight tokens, joined per 16-token block with the partner lane's, the
+      // block totals in log2 across the lane's group of eight, E' = product
+      // * 2^{ref_b - G_n / 2} to the lo planes (free now), the scales into
+      // the other chunk slot
+      static_assert(D == 128 && KT - 64 * NCW == 256, "helper scan layout");
+      const int hl = tid - 64 * NCW, cq = hl >> 3, p8 = hl & 7;
       const int64_t t1 = tok0 + C;
       const int n1 = (int)((eos - t1) < C ? (eos - t1) : C);
-      float e[32], r0 = 1.f, r1 = 1.f;
+      f32x4 e[8], run = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-      for (int tt = 0; tt < 16; ++tt) {
-        r0 *= 32 * apart + tt < n1 ? ra[tt] : 1.f;
-        e[tt] = r0;
+      for (int tt = 0; tt < 8; ++tt) {
+        const bool in = 8 * p8 + tt < n1;
+        const f32x4 x = {in ? __uint_as_float(ra[tt].x) : 1.f, in ? __uint_as_float(ra[tt].y) : 1.f,
+                         in ? __uint_as_float(ra[tt].z) : 1.f, in ? __uint_as_float(ra[tt].w) : 1.f};
+        run *= x;
+        e[tt] = run;
       }
+      f32x4 prev, L, Lq0, Lq1, O0, O1;
 #pragma unroll
-      for (int tt = 0; tt < 16; ++tt) {
-        r1 *= 32 * apart + 16 + tt < n1 ? ra[16 + tt] : 1.f;
-        e[16 + tt] = r1;
+      for (int i = 0; i < 4; ++i) prev[i] = dpp<kQuadXor1>(run[i]);  // the partner part's total
+      if (p8 & 1) {
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) e[tt] *= prev;
       }
-      const float l0 = __builtin_amdgcn_logf(r0), l1 = __builtin_amdgcn_logf(r1);
-      const float o0 = dpp<kQuadXor1>(l0), o1 = dpp<kQuadXor1>(l1);
-      const float L0 = apart ? o0 : l0, L1 = apart ? o1 : l1, L2 = apart ? l0 : o0, L3 = apart ? l1 : o1;
-      const float gn = ((L0 + L1) + L2) + L3, rm = 0.5f * gn;
-      const float q0 = dpp<kQuadXor1>(r0), q1 = dpp<kQuadXor1>(r1);
-      if (r0 < 0x1p-100f || r1 < 0x1p-100f || q0 < 0x1p-100f || q1 < 0x1p-100f || !(gn >= -200.f))
-        sm.mode = 1;
-      const float fa = fexp2((apart ? L0 + L1 : 0.f) - rm);
-      const float fb = fexp2((apart ? (L0 + L1) + L2 : L0) - rm);
+      const f32x4 tb = (p8 & 1) ? prev * run : run * prev;  // the block's total
+      bool deepb = false;
 #pragma unroll
-      for (int tt = 0; tt < 16; ++tt) *eptr(32 * apart + tt, ach) = e[tt] * fa;
+      for (int i = 0; i < 4; ++i) {
+        deepb |= tb[i] < 0x1p-100f;
+        L[i] = __builtin_amdgcn_logf(tb[i]);
+        Lq0[i] = dpp<0x00>(L[i]);  // blocks 2 (p8 >> 2) and 2 (p8 >> 2) + 1
+        Lq1[i] = dpp<0xAA>(L[i]);
+        O0[i] = dpp<kHalfMirror>(Lq0[i]);  // the other quad's two blocks
+        O1[i] = dpp<kHalfMirror>(Lq1[i]);
+      }
+      const bool hiq = (p8 & 4) != 0;
+      const f32x4 L0 = hiq ? O0 : Lq0, L1 = hiq ? O1 : Lq1, L2 = hiq ? Lq0 : O0, L3 = hiq ? Lq1 : O1;
+      const f32x4 gn = ((L0 + L1) + L2) + L3, rm = 0.5f * gn;
+      const int bk = p8 >> 1;
+      const f32x4 ref = bk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : bk == 1 ? L0 : bk == 2 ? L0 + L1 : (L0 + L1) + L2;
+      f32x4 fac, zr;
 #pragma unroll
-      for (int tt = 0; tt < 16; ++tt) *eptr(32 * apart + 16 + tt, ach) = e[16 + tt] * fb;
-      if (apart == 0) {
-        const float zr = fexp2(rm);
-        sm.Zr[cur ^ 1][ach] = zr;
-        sm.Yp[cur ^ 1][ach] = zr;
+      for (int i = 0; i < 4; ++i) {
+        deepb |= !(gn[i] >= -200.f);
+        fac[i] = fexp2(ref[i] - rm[i]);
+        zr[i] = fexp2(rm[i]);
+      }
+      if (deepb) sm.mode = 1;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) st4(eptr(8 * p8 + tt, 4 * cq), e[tt] * fac);
+      if (p8 == 0) {
+        st4(&sm.Zr[cur ^ 1][4 * cq], zr);
+        st4(&sm.Yp[cur ^ 1][4 * cq], zr);
       }
     }
     lds_barrier();  // everyone is done with this chunk's LDS
