@@ -708,11 +708,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
   bf16 *const KEh = sm.KE, *const KEl = sm.KE + C * LDB;
   bf16 *const QEh = sm.QE, *const QEl = sm.QE + C * LDB;
   float *const Gp = reinterpret_cast<float *>(sm.KF);
-  // E (the fast path's in-block decays) as fp32 in the lo planes of k o E
-  // (channels 0 .. D/2-1) and q o E (the others), row r in their row r; the
-  // lo planes are free from the Gram phase's last read to the next forming
+  // E' (the fast path's decays) as fp32 in the lo planes of k o E'
+  // (channels 0 .. D/2-1) and q o E' (the others), row r in their row r,
+  // rotated by 8 floats per group of 8 rows so that lanes writing rows 8
+  // apart use different banks; the lo planes are free from the Gram phase's
+  // last read to the next forming
   auto eptr = [&](int r, int c) __attribute__((always_inline)) {
-    return reinterpret_cast<float *>(c < D / 2 ? KEl : QEl) + r * (LDB / 2) + (c & (D / 2 - 1));
+    return reinterpret_cast<float *>(c < D / 2 ? KEl : QEl) + r * (LDB / 2) +
+           (((c & (D / 2 - 1)) + 8 * (r >> 3)) & (D / 2 - 1));
   };
   static_assert(2 * D <= LDB * 2 * 2 && (LDB / 2) % 4 == 0, "E rows in the lo planes");
 
