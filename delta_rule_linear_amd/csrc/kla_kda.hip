@@ -618,19 +618,18 @@ struct KdaBfSmem {
   static constexpr int LDR = 2 * D + 16;  // k o F rows (bf16): hi at 0, lo at LO; 2 LDR bytes = 32 mod 128
   static constexpr int LO = D + 8;
   static constexpr int LDG = D + 8;       // the same rows as fp32 G
-  static constexpr int LDV = DVB + 4;
+  static constexpr int LDV = DVB + 8;     // V rows (bf16)
   static constexpr int LDA = 20;          // -Ahat blocks (bf16 hi, lo; 16 x 16 each, transposed)
   static constexpr int LDP = C + 16;      // M planes (bf16 hi, lo; pcol order)
   static constexpr int LDYT = 24;         // Y^T rows (bf16 hi, lo)
   static_assert(2 * 6 * 16 * LDA <= 2 * C * LDB && 2 * C * LDP <= 2 * C * LDB,
                 "planes must fit in the operand space");
-  // the M lo plane after the -Ahat planes in the k o E hi plane where it
-  // fits (d = 128), so both lo planes are free during the substitution
-  static constexpr bool ML_IN_KE = 2 * 6 * 16 * LDA + C * LDP <= C * LDB;
   alignas(16) bf16 KE[2 * C * LDB];  // hi plane then lo plane; raw k in the hi plane until formed; -Ahat planes after the Gram phase
   alignas(16) bf16 QE[2 * C * LDB];  // the same for q; M planes after the Gram phase
   alignas(16) bf16 KF[C * LDR];
-  alignas(16) float Vs[C * LDV];
+  alignas(16) bf16 Vs[C * LDV];
+  alignas(16) bf16 AP[2 * 6 * 16 * LDA];  // -Ahat planes (hi, lo), written as the Gram jobs finish
+  alignas(16) bf16 MP[2 * C * LDP];       // M planes (hi, lo)
   alignas(16) bf16 Yh[4 * 16 * LDYT];  // Y_bb^T, Y_bb = (I + L_bb)^{-1} Diag(beta_b)
   alignas(16) bf16 Yl[4 * 16 * LDYT];
   alignas(16) float Ld[4 * 16 * 20];
@@ -684,7 +683,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
   // with helper waves, they scan the next chunk's rates during the
   // substitution (from registers), and its decays are staged with it
   constexpr bool AHEAD = NW != NCW;
-  static_assert(!AHEAD || SM::ML_IN_KE, "the lo planes must be free during the substitution");
   static_assert(16 * NCW == DVB, "column waves");
   constexpr int NB = D / DVB;
   constexpr int NST = D / 16;
@@ -824,16 +822,26 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
 #pragma unroll
     for (int u = 0; u < NVSEG; ++u) {
       const int sg = u * KT + tid, r = sg / SEG_VROW, cs = sg % SEG_VROW;
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, vreg[u]);
-      st4(&sm.Vs[r * LDV + cs * SEG_EL], f32x4{static_cast<float>(vb[0]), static_cast<float>(vb[1]),
-                                               static_cast<float>(vb[2]), static_cast<float>(vb[3])});
-      st4(&sm.Vs[r * LDV + cs * SEG_EL + 4], f32x4{static_cast<float>(vb[4]), static_cast<float>(vb[5]),
-                                                   static_cast<float>(vb[6]), static_cast<float>(vb[7])});
+      *reinterpret_cast<uint4 *>(&sm.Vs[r * LDV + cs * SEG_EL]) = vreg[u];
     }
     if constexpr (!AHEAD) stage_rates(t0);
     if (w == 0) sm.et[l] = ereg;
     if (tid == 0) sm.deep = 0;
   };
+
+  // -Ahat blocks (b, m), m < b, transposed (row 16b + c16 of a lane holds
+  // columns 4j..4j+3), index b(b-1)/2 + m; M in the pcol column order, its
+  // two blocks above the diagonal that the 32-deep products read, (0, 1) and
+  // (2, 3), zero (set once: no job writes them)
+  bf16 *const Ah = sm.AP, *const Al = sm.AP + 6 * 16 * LDA;
+  bf16 *const Mh = sm.MP, *const Ml = sm.MP + C * LDP;
+  for (int e = tid; e < 256; e += KT) {
+    // one 4-column group of one row of one plane per thread: rows 0-15 x
+    // columns 16-31 and rows 32-47 x columns 48-63
+    const int zr = (e >> 3) & 15, zg = e & 3, zs = (e >> 2) & 1, zp = (e >> 7) & 1;
+    const int row = zs ? 32 + zr : zr, c = (zs ? 48 : 16) + 4 * zg;
+    *reinterpret_cast<uint2 *>(&(zp ? Ml : Mh)[row * LDP + pcol(c)]) = uint2{0u, 0u};
+  }
 
   fetch(bos);
   if constexpr (!AHEAD) fetch_a(bos);
@@ -1103,12 +1111,55 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
         }
       }
     };
+    // the jobs' tiles as planes (-Ahat negated; M masked to t >= s)
+    auto write_planes = [&]() __attribute__((always_inline)) {
+      const int nj = kda_njobs<NW>(w);
+#pragma unroll
+      for (int u = 0; u < kda_maxjobs<NW>(); ++u) {
+        if (u < nj) {
+          const Job jb = kda_job<NW>(w, u);
+          const int r = 16 * jb.bi + c16;  // this lane's row
+          f32x4 vals;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int sc = 16 * jb.bj + 4 * j + i;
+            vals[i] = jb.qk ? (r >= sc ? jt[u][i] : 0.f) : -jt[u][i];
+          }
+          const Split4 sp = split4(vals);
+          if (jb.qk) {
+            const int off = r * LDP + pcol(16 * jb.bj + 4 * j);
+            *reinterpret_cast<bf16x4 *>(&Mh[off]) = sp.hi;
+            *reinterpret_cast<bf16x4 *>(&Ml[off]) = sp.lo;
+          } else {
+            const int off = ((jb.bi * (jb.bi - 1) / 2 + jb.bj) * 16 + c16) * LDA + 4 * j;
+            *reinterpret_cast<bf16x4 *>(&Ah[off]) = sp.hi;
+            *reinterpret_cast<bf16x4 *>(&Al[off]) = sp.lo;
+          }
+        }
+      }
+    };
     // fast path: operands, then the Gram tiles on the MFMA; exact path: the
     // Gram tiles from the raw inputs, then the operands with absolute
     // factors (Z = W = 1)
     if (!deep) form(false);
     lds_barrier();
+    // the next chunk's rates (helper waves), a phase ahead of their scan:
+    // lane (quad cq, part p) holds channels 4cq..4cq+3 of tokens 8p..8p+7
+    uint4 ra[8];
+    if constexpr (AHEAD) {
+      if (w >= NCW) {
+        const int hl = tid - 64 * NCW, cq = hl >> 3, p8 = hl & 7;
+        const int64_t t1 = tok0 + C;
+        const int64_t n1 = (eos - t1) < C ? (eos - t1) : C;
+        const rsrc_t rr = make_rsrc(alpha + t1 * H * (int64_t)D, n1 * (int64_t)H * D * 4);
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt)
+          ra[tt] = buf_ld16(rr, (uint32_t)(((8 * p8 + tt) * H + h) * D + 4 * cq) * 4);
+        if (hl == 0) sm.mode = 0;
+      }
+    }
     gram(deep);
+    write_planes();
     if (deep) {
       lds_barrier();  // every read of the raw inputs is done
       if (tid < D) {
@@ -1144,72 +1195,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
         }
         QS[bi] = aq;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) R[bi][i] = sm.Vs[(16 * bi + 4 * j + i) * LDV + 16 * w + c16] - ak[i];
+        for (int i = 0; i < 4; ++i)
+          R[bi][i] = static_cast<float>(sm.Vs[(16 * bi + 4 * j + i) * LDV + 16 * w + c16]) - ak[i];
       }
     }
     lds_barrier();  // every read of k o E and q o E is done
     if constexpr (!AHEAD) fetch_a(tok0 + C);
-
-    // ---- planes over the operand space ---------------------------------------
-    // -Ahat blocks (b, m), m < b, transposed (row 16b + c16 of a lane holds
-    // columns 4j..4j+3), index b(b-1)/2 + m; M in the pcol column order,
-    // its two blocks above the diagonal that the 32-deep products read, (0, 1)
-    // and (2, 3), set to zero
-    bf16 *const Ah = sm.KE, *const Al = sm.KE + 6 * 16 * LDA;
-    bf16 *const Mh = sm.QE, *const Ml = SM::ML_IN_KE ? sm.KE + 2 * 6 * 16 * LDA : sm.QE + C * LDP;
-    if (w != DIAGW) {
-      const int nj = kda_njobs<NW>(w);
-#pragma unroll
-      for (int u = 0; u < kda_maxjobs<NW>(); ++u) {
-        if (u < nj) {
-          const Job jb = kda_job<NW>(w, u);
-          const int r = 16 * jb.bi + c16;  // this lane's row
-          f32x4 vals;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int sc = 16 * jb.bj + 4 * j + i;
-            vals[i] = jb.qk ? (r >= sc ? jt[u][i] : 0.f) : -jt[u][i];
-          }
-          const Split4 sp = split4(vals);
-          if (jb.qk) {
-            const int off = r * LDP + pcol(16 * jb.bj + 4 * j);
-            *reinterpret_cast<bf16x4 *>(&Mh[off]) = sp.hi;
-            *reinterpret_cast<bf16x4 *>(&Ml[off]) = sp.lo;
-          } else {
-            const int off = ((jb.bi * (jb.bi - 1) / 2 + jb.bj) * 16 + c16) * LDA + 4 * j;
-            *reinterpret_cast<bf16x4 *>(&Ah[off]) = sp.hi;
-            *reinterpret_cast<bf16x4 *>(&Al[off]) = sp.lo;
-          }
-        }
-      }
-    }
-    {
-      // rows 0-15 x columns 16-31 and rows 32-47 x columns 48-63: one
-      // 4-column group of one row of one plane per thread
-      const int zr = (tid >> 3) & 15, zg = tid & 3, zs = (tid >> 2) & 1, zp = (tid >> 7) & 1;
-      const int row = zs ? 32 + zr : zr, c = (zs ? 48 : 16) + 4 * zg;
-      if (tid < 256) {
-        uint32_t z;  // made here, not kept in a register over the loop
-        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-        *reinterpret_cast<uint2 *>(&(zp ? Ml : Mh)[row * LDP + pcol(c)]) = uint2{z, z};
-      }
-    }
-    // the next chunk's rates (helper waves): lane (quad cq, part p) holds
-    // channels 4cq..4cq+3 of tokens 8p..8p+7
-    uint4 ra[8];
-    if constexpr (AHEAD) {
-      if (w >= NCW) {
-        const int hl = tid - 64 * NCW, cq = hl >> 3, p8 = hl & 7;
-        const int64_t t1 = tok0 + C;
-        const int64_t n1 = (eos - t1) < C ? (eos - t1) : C;
-        const rsrc_t rr = make_rsrc(alpha + t1 * H * (int64_t)D, n1 * (int64_t)H * D * 4);
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt)
-          ra[tt] = buf_ld16(rr, (uint32_t)(((8 * p8 + tt) * H + h) * D + 4 * cq) * 4);
-        if (hl == 0) sm.mode = 0;
-      }
-    }
-    lds_barrier();
 
     if (w < NCW) {
     // ---- Delta by block substitution, output ---------------------------------
