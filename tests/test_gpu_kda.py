@@ -84,6 +84,10 @@ def _tiny(a, case, d):
         a[70, 1, d // 2:] = 1e-38
     elif case == "past_bound":        # 0.004 per token: just past the fast path's bound
         a[150:160, :, 3 * d // 4:] = 0.004
+    elif case == "chunk_deep":        # 0.1 per token: 2^-53 per 16 tokens, 2^-213 per chunk
+        a[:, :, : d // 4] = 0.1
+    elif case == "near_chunk_bound":  # 0.116 per token: about 2^-199 per chunk
+        a[:, :, d // 4: d // 2] = 0.116
     elif case == "all":
         for c in ("deep_channels", "near_zero_run", "subnormal", "past_bound"):
             _tiny(a, c, d)
@@ -93,11 +97,14 @@ def _tiny(a, case, d):
 @pytest.mark.parametrize("d,dtype,case", [
     (128, "bf16", "deep_channels"), (128, "bf16", "near_zero_run"), (128, "bf16", "subnormal"),
     (128, "bf16", "past_bound"), (128, "bf16", "all"), (64, "bf16", "all"), (64, "f32", "all"),
-    (64, "bf16", "deep_channels")])
+    (64, "bf16", "deep_channels"), (128, "bf16", "chunk_deep"), (128, "bf16", "near_chunk_bound"),
+    (64, "bf16", "chunk_deep"), (64, "bf16", "near_chunk_bound")])
 def test_kda_prefill_tiny_rates(kla, d, dtype, case):
     """Per-channel rates whose product inside a 16-token block falls far
-    below 2^-126, mixed with ordinary rates: every output finite and within
-    the bar against the oracle."""
+    below 2^-126, or whose product over a chunk falls below or just above
+    2^-200 (the bf16 kernel's bound for its midpoint-referenced factors),
+    mixed with ordinary rates: every output finite and within the bar
+    against the oracle."""
     lengths = [200, 64, 1, 130]
     print(f"[case] per-channel prefill with tiny rates ({case}) d={d} {dtype} lengths={lengths} H=2",
           flush=True)
