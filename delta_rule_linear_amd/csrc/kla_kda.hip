@@ -931,14 +931,25 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
     // scales set to match).  A row's E' (or G) is read by this wave before
     // any of the row is written.
     auto form = [&](bool exact) __attribute__((always_inline)) {
-      const int c4 = 4 * (tid % Q4);
+      // this lane's rows r0 + u RPP: every read first (a row is read and
+      // written only by this wave), then the products, splits and writes
+      constexpr int NFR = C / RPP;
+      static_assert(NFR * RPP == C, "forming rows");
+      const int c4 = 4 * (tid % Q4), r0 = tid / Q4;
+      f32x4 Gv[NFR], kxv[NFR], qxv[NFR];
+      const f32x4 gn = ld4(&sm.Gn[c4]);
 #pragma unroll
-      for (int r = tid / Q4; r < C; r += RPP) {
-        const f32x4 G = exact ? ld4(&Gp[r * LDG + c4]) : ld4(eptr(r, c4));  // G or E
-        const f32x4 gn = ld4(&sm.Gn[c4]);
-        const f32x4 kx = to_f32x4(*reinterpret_cast<const bf16x4 *>(&KEh[r * LDB + pcol(c4)]));
-        const f32x4 qx = to_f32x4(*reinterpret_cast<const bf16x4 *>(&QEh[r * LDB + pcol(c4)]));
-        asm volatile("" ::: "memory");  // the row's reads above, its writes below
+      for (int u = 0; u < NFR; ++u) {
+        const int r = r0 + u * RPP;
+        Gv[u] = exact ? ld4(&Gp[r * LDG + c4]) : ld4(eptr(r, c4));  // G or E'
+        kxv[u] = to_f32x4(*reinterpret_cast<const bf16x4 *>(&KEh[r * LDB + pcol(c4)]));
+        qxv[u] = to_f32x4(*reinterpret_cast<const bf16x4 *>(&QEh[r * LDB + pcol(c4)]));
+      }
+      asm volatile("" ::: "memory");  // the reads above, the writes below
+#pragma unroll
+      for (int u = 0; u < NFR; ++u) {
+        const int r = r0 + u * RPP;
+        const f32x4 G = Gv[u], kx = kxv[u], qx = qxv[u];
         f32x4 ke, kf, qe;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -955,8 +966,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
         *reinterpret_cast<bf16x4 *>(&QEl[r * LDB + pcol(c4)]) = sq.lo;
         *reinterpret_cast<bf16x4 *>(&sm.KF[r * LDR + pcol(c4)]) = sf.hi;
         *reinterpret_cast<bf16x4 *>(&sm.KF[r * LDR + LO + pcol(c4)]) = sf.lo;
-        asm volatile("" ::: "memory");
       }
+      asm volatile("" ::: "memory");
     };
     // exact Gram element: sum_i X_t[i] K_s[i] 2^{G_t[i] - G_s[i]} for t >= s
     // (raw X = Q or K in the hi planes, G still in LDS), else 0
