@@ -1038,10 +1038,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
     f32x4 jt[kda_maxjobs<NW>()];  // a wave's Gram tiles until the operand space is free
     auto gram = [&](bool exact) __attribute__((always_inline)) {
       if (w == DIAGW) {
-        sm.beta[l] = beta_direct ? sm.et[l] : sm.et[l] / (sm.kk[l] + eps);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if constexpr (!AHEAD) {
+          sm.beta[l] = beta_direct ? sm.et[l] : sm.et[l] / (sm.kk[l] + eps);
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
         // diagonal tiles -> -Diag(beta) Ahat below the diagonal of each block
         // (acc[i] = Ahat[16b + 4j + i][16b + c16])
         if (exact) {
@@ -1153,6 +1155,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
     // Gram tiles from the raw inputs, then the operands with absolute
     // factors (Z = W = 1)
     if (!deep) form(false);
+    // with helper waves, beta on wave 0 (done forming first) for the
+    // diagonal wave
+    if constexpr (AHEAD) {
+      if (w == 0) sm.beta[l] = beta_direct ? sm.et[l] : sm.et[l] / (sm.kk[l] + eps);
+    }
     lds_barrier();
     // the next chunk's rates (helper waves), a phase ahead of their scan:
     // lane (quad cq, part p) holds channels 4cq..4cq+3 of tokens 8p..8p+7
