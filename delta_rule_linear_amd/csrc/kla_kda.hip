@@ -622,10 +622,8 @@ struct KdaBfSmem {
   static constexpr int LDA = 20;          // -Ahat blocks (bf16 hi, lo; 16 x 16 each, transposed)
   static constexpr int LDP = C + 16;      // M planes (bf16 hi, lo; pcol order)
   static constexpr int LDYT = 24;         // Y^T rows (bf16 hi, lo)
-  static_assert(2 * 6 * 16 * LDA <= 2 * C * LDB && 2 * C * LDP <= 2 * C * LDB,
-                "planes must fit in the operand space");
-  alignas(16) bf16 KE[2 * C * LDB];  // hi plane then lo plane; raw k in the hi plane until formed; -Ahat planes after the Gram phase
-  alignas(16) bf16 QE[2 * C * LDB];  // the same for q; M planes after the Gram phase
+  alignas(16) bf16 KE[2 * C * LDB];  // hi plane then lo plane; raw k in the hi plane until formed, E' in the lo plane
+  alignas(16) bf16 QE[2 * C * LDB];  // the same for q
   alignas(16) bf16 KF[C * LDR];
   alignas(16) bf16 Vs[C * LDV];
   alignas(16) bf16 AP[2 * 6 * 16 * LDA];  // -Ahat planes (hi, lo), written as the Gram jobs finish
@@ -768,8 +766,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
       ereg = buf_ld4(re, (uint32_t)(l * H + h) * 4);  // zero past the end
     }
   };
-  // the rates (the largest input) are fetched half a chunk later, so their
-  // registers are free during the Gram and Q S / K S phase
+  // the rates (the largest input): without helper waves fetched half a chunk
+  // later, so their registers are free during the Gram and Q S / K S phase;
+  // with them, only for a chunk the helpers have not scanned
   auto fetch_a = [&](int64_t t0) {
     const int tid = fresh_lane(threadIdx.x);
     const int64_t nn = (eos - t0) < C ? (eos - t0) : C;
@@ -1035,7 +1034,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
       }
     };
     // ---- Gram tiles, diagonal inverses; Q S, K S, R --------------------------
-    f32x4 jt[kda_maxjobs<NW>()];  // a wave's Gram tiles until the operand space is free
+    f32x4 jt[kda_maxjobs<NW>()];  // a wave's Gram tiles until they are written as planes
     auto gram = [&](bool exact) __attribute__((always_inline)) {
       if (w == DIAGW) {
         if constexpr (!AHEAD) {
@@ -1153,7 +1152,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kda_bf_kernel(
     };
     // fast path: operands, then the Gram tiles on the MFMA; exact path: the
     // Gram tiles from the raw inputs, then the operands with absolute
-    // factors (Z = W = 1)
+    // factors (and the state scales set to match)
     if (!deep) form(false);
     // with helper waves, beta on wave 0 (done forming first) for the
     // diagonal wave
