@@ -94,13 +94,18 @@ SHARED_HEADER = "delta_rule_linear_amd/csrc/kla_device.h"  # device helpers of t
 
 def source_hash(kernel):
     """sha256 of the kernel's source file (followed by the shared device
-    header for the prefill kernels, which include it)."""
+    header for the prefill kernels, which include it, and by the unit's own
+    extra build flags where it has any)."""
     import hashlib
+    from delta_rule_linear_amd import build as kbuild
     h = hashlib.sha256()
     paths = [KERNEL_SOURCES[kernel]] + ([SHARED_HEADER] if kernel != DECODE_KERNEL else [])
     for p in paths:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
+    extra = kbuild.EXTRA.get(os.path.basename(KERNEL_SOURCES[kernel]))
+    if extra:
+        h.update(" ".join(extra).encode())
     return h.hexdigest()
 
 

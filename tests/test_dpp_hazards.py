@@ -31,7 +31,7 @@ def test_checker_finds_planted_hazards():
 def test_no_dpp_read_after_valu_write(tmp_path):
     def asm(src):
         out = tmp_path / (src + ".s")
-        cmd = [kbuild.HIPCC] + kbuild.COMMON + ["-x", "hip", "--cuda-device-only", "-S",
+        cmd = [kbuild.HIPCC] + kbuild.flags(src) + ["-x", "hip", "--cuda-device-only", "-S",
                                                 os.path.join(kbuild.CSRC, src), "-o", str(out)]
         r = subprocess.run(cmd, capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
